@@ -1,0 +1,391 @@
+/*
+ * sgb_oracle.c -- CPU reference ("oracle") for the pooled embedding-bag
+ * backward with deduplication by sort + run-length encoding.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, obviously-correct
+ * definition that the GPU library is checked against.  Only the test suite,
+ * the smoke check and the benchmark's CPU-baseline leg may load it.  It shares
+ * no code, header, table or constant with the GPU library: every rule below is
+ * restated here from the pages, in plain single-threaded loops with double
+ * precision accumulation, rounded once to fp32 where an fp32 result is asked
+ * for.
+ *
+ * Sources (pages by title; sections named by the kernel or function they
+ * fall in):
+ *  [P1] "fbgemm_gpu/codegen/embedding_backward_split_template.cu" (FBGEMM):
+ *       host entry `..._exact_cuda`, kernels `grad_mean_kernel`,
+ *       `find_long_segments`, `..._kernel_cta_per_row_1`,
+ *       `..._kernel_warp_per_row_1`.
+ *  [P2] "tt_embeddings_cuda.cu" (FBTT-Embedding): `compute_rowidx_kernel`,
+ *       `cache_backward_dense_kernel`, `cache_backward_sgd_kernel`,
+ *       `cache_backward_rowwise_adagrad_approx_kernel`,
+ *       `update_tt_cores_adagrad_kernel`.
+ *  [P3] "Function _embedding_bwd_kernel" (tinygrad nn/__init__.py).
+ *
+ * Readings taken where the pages are silent are listed next to the code that
+ * takes them (marked "Reading").
+ *
+ * Every function here is pinned by the CPU test suite against something other
+ * than itself: hand-worked cases, a dense one-hot matrix product, the mass
+ * invariant, closed forms of the optimizer steps and brute-force run
+ * structure.  No function is "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Status codes of the oracle (its own; the test suite maps them by name). */
+enum {
+  ORC_OK = 0,
+  ORC_INVALID_ARGUMENT = 1,
+  ORC_UNSUPPORTED = 2,
+  ORC_INDEX_OUT_OF_RANGE = 4,
+  ORC_BAD_OFFSETS = 5
+};
+
+enum { ORC_POOL_SUM = 0, ORC_POOL_MEAN = 1, ORC_POOL_NONE = 2 };
+enum { ORC_DENSE = 0, ORC_SGD = 1, ORC_ROWWISE_ADAGRAD = 2 };
+
+/* One backward problem, all arrays on the host. */
+typedef struct {
+  int32_t T;                      /* number of tables, > 0                  */
+  int32_t B;                      /* bags per table (bag mode), > 0         */
+  int64_t N;                      /* number of lookups                      */
+  const int64_t* hash_size_cumsum;/* [T+1], [0]=0, strictly increasing      */
+  const int32_t* D_offsets;       /* [T+1], column start of table t in a bag
+                                     row of grad_output                     */
+  const int64_t* offsets;         /* [B*T+1], table-major (t*B+b); may be
+                                     NULL only for nobag with T == 1        */
+  const int64_t* indices;         /* [N], row index within the table        */
+  const float* per_sample_weights;/* [N] or NULL                            */
+  int32_t pooling;                /* ORC_POOL_*                             */
+  const void* grad_output;        /* bag: [B][D_offsets[T]]; nobag: [N][D]  */
+  int32_t grad_is_bf16;           /* 0: fp32, 1: bf16 bit patterns (uint16) */
+} orc_problem;
+
+/* ------------------------------------------------------------------------ */
+/* Small helpers                                                              */
+/* ------------------------------------------------------------------------ */
+
+/* bf16 -> fp32 is exact: the 16 bits are the top half of an fp32. */
+static double orc_bf16_to_double(uint16_t h) {
+  uint32_t bits = ((uint32_t)h) << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/* Element (row, col) of grad_output with `width` columns per row, widened. */
+static double orc_grad(const orc_problem* p, int64_t row, int64_t width,
+                       int64_t col) {
+  if (p->grad_is_bf16) {
+    const uint16_t* g = (const uint16_t*)p->grad_output;
+    return orc_bf16_to_double(g[row * width + col]);
+  }
+  const float* g = (const float*)p->grad_output;
+  return (double)g[row * width + col];
+}
+
+static int orc_table_D(const orc_problem* p, int32_t t) {
+  return p->D_offsets[t + 1] - p->D_offsets[t];
+}
+
+/* Bag (t, b) spans lookups [offsets[t*B+b], offsets[t*B+b+1]) -- table-major
+ * bag order [P1 `grad_mean_kernel` reads offsets[t * B + b]; P2
+ * `compute_rowidx_kernel` writes rowidx = bag % B, tableidx = bag / B].
+ * Nobag with no offsets array and a single table: every lookup is its own
+ * segment of table 0. */
+static void orc_bag_range(const orc_problem* p, int32_t t, int32_t b,
+                          int64_t* s, int64_t* e) {
+  if (p->offsets == NULL) {
+    *s = 0;
+    *e = p->N;
+    return;
+  }
+  *s = p->offsets[(int64_t)t * p->B + b];
+  *e = p->offsets[(int64_t)t * p->B + b + 1];
+}
+
+static int32_t orc_num_bags(const orc_problem* p) {
+  return p->offsets == NULL ? 1 : p->B;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Validation                                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* Checks the host entry makes or implies [P1 host entry `..._exact_cuda`:
+ * T > 0, B > 0, offsets has B*T+1 entries; P2 host wrappers: D % 4 == 0],
+ * plus the readings:
+ *  - Reading: offsets start at 0, never decrease and end at N (a bag is a
+ *    contiguous range of the indices array).
+ *  - Reading: an index outside [0, E_t) is an error.  The FBGEMM page does
+ *    not check; the tinygrad page clips.  We neither clip nor ignore.
+ *  - Reading: 4 <= D_t <= 8192 and D_t % 4 == 0 (the pages read rows in
+ *    groups of 4; 8192 is this library's stated maximum).
+ *  - Nobag exists only unweighted [P1: the nobag variant is generated only
+ *    when not weighted].  Nobag tables share one D [P1 nobag kernels take a
+ *    single D].
+ *  - hash_size_cumsum starts at 0 and strictly increases (no empty and no
+ *    shared tables).
+ */
+int orc_validate(const orc_problem* p) {
+  if (p->T <= 0 || p->N < 0 || p->hash_size_cumsum == NULL ||
+      p->D_offsets == NULL)
+    return ORC_INVALID_ARGUMENT;
+  if (p->pooling < ORC_POOL_SUM || p->pooling > ORC_POOL_NONE)
+    return ORC_INVALID_ARGUMENT;
+  const int nobag = p->pooling == ORC_POOL_NONE;
+  if (nobag && p->per_sample_weights != NULL) return ORC_UNSUPPORTED;
+  if (p->offsets == NULL && !(nobag && p->T == 1)) return ORC_INVALID_ARGUMENT;
+  if (p->offsets != NULL && p->B <= 0) return ORC_INVALID_ARGUMENT;
+  if (p->hash_size_cumsum[0] != 0) return ORC_INVALID_ARGUMENT;
+  if (p->D_offsets[0] != 0) return ORC_INVALID_ARGUMENT;
+  for (int32_t t = 0; t < p->T; ++t) {
+    if (p->hash_size_cumsum[t + 1] <= p->hash_size_cumsum[t])
+      return ORC_INVALID_ARGUMENT;
+    int D = orc_table_D(p, t);
+    if (D < 4 || D > 8192 || D % 4 != 0) return ORC_INVALID_ARGUMENT;
+    if (nobag && D != orc_table_D(p, 0)) return ORC_INVALID_ARGUMENT;
+  }
+  if (p->N > 0 && (p->indices == NULL || p->grad_output == NULL))
+    return ORC_INVALID_ARGUMENT;
+  if (p->offsets != NULL) {
+    int64_t nb = (int64_t)p->B * p->T;
+    if (p->offsets[0] != 0 || p->offsets[nb] != p->N) return ORC_BAD_OFFSETS;
+    for (int64_t k = 0; k < nb; ++k)
+      if (p->offsets[k + 1] < p->offsets[k]) return ORC_BAD_OFFSETS;
+  }
+  for (int32_t t = 0; t < p->T; ++t) {
+    int64_t E = p->hash_size_cumsum[t + 1] - p->hash_size_cumsum[t];
+    for (int32_t b = 0; b < orc_num_bags(p); ++b) {
+      int64_t s, e;
+      orc_bag_range(p, t, b, &s, &e);
+      for (int64_t i = s; i < e; ++i)
+        if (p->indices[i] < 0 || p->indices[i] >= E)
+          return ORC_INDEX_OUT_OF_RANGE;
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Per-lookup linear id, info and coefficient, in original order             */
+/* ------------------------------------------------------------------------ */
+
+/* For lookup i of bag (t, b):
+ *   key  = hash_size_cumsum[t] + indices[i]
+ *          (Reading: the inverse of the kernels' `idx = linear_index -
+ *          hash_size_cumsum[t_0]` [P1 `..._kernel_warp_per_row_1`]);
+ *   info = t*B + b in bag mode, i*T + t in nobag mode [P1 kernels decode
+ *          `b_t` into (t, b) with a divisor B, and nobag `l_t` into
+ *          l = l_t / T, t = l_t % T];
+ *   coef = (per-sample weight or 1) * (1/L under MEAN pooling, L > 0)
+ *          [P1 `grad_mean_kernel` scales the bag's output gradient by 1/L
+ *          and leaves empty bags alone; the weighted kernels multiply by the
+ *          sorted per-sample weight].  Reading: the two compose.
+ * Requires a valid problem (orc_validate == ORC_OK). */
+int orc_linearize(const orc_problem* p, int64_t* keys, int64_t* infos,
+                  double* coefs) {
+  int st = orc_validate(p);
+  if (st != ORC_OK) return st;
+  const int nobag = p->pooling == ORC_POOL_NONE;
+  for (int32_t t = 0; t < p->T; ++t) {
+    for (int32_t b = 0; b < orc_num_bags(p); ++b) {
+      int64_t s, e;
+      orc_bag_range(p, t, b, &s, &e);
+      int64_t L = e - s;
+      double scale = (p->pooling == ORC_POOL_MEAN && L > 0) ? 1.0 / (double)L
+                                                            : 1.0;
+      for (int64_t i = s; i < e; ++i) {
+        keys[i] = p->hash_size_cumsum[t] + p->indices[i];
+        infos[i] = nobag ? i * (int64_t)p->T + t : (int64_t)t * p->B + b;
+        double w = p->per_sample_weights ? (double)p->per_sample_weights[i]
+                                         : 1.0;
+        coefs[i] = w * scale;
+      }
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Run structure: stable sort, run-length encoding, long runs                 */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int64_t key;
+  int64_t pos;
+} orc_keypos;
+
+static int orc_cmp_keypos(const void* a, const void* b) {
+  const orc_keypos* x = (const orc_keypos*)a;
+  const orc_keypos* y = (const orc_keypos*)b;
+  if (x->key != y->key) return x->key < y->key ? -1 : 1;
+  if (x->pos != y->pos) return x->pos < y->pos ? -1 : 1;
+  return 0;
+}
+
+/* Sorts the lookups by linear id, keeping the original order among equal
+ * ids (Reading: the page re-sorts the per-sample weights by the same keys in
+ * a second pass and expects them to line up with the sorted infos, which
+ * only holds for a stable sort [P1 host entry, weighted branch]).  Then:
+ *   unique_ids[r]       the r-th distinct id, ascending;
+ *   cumulative[r]       position of its first lookup, cumulative[U] = N;
+ *   run_lengths[r]      cumulative[r+1] - cumulative[r];
+ *   long_run_ids        { r : run_lengths[r] >= thr }, ascending
+ *                       [P1 `find_long_segments` uses >=; the page emits the
+ *                       set in atomic-counter order, we list it ascending].
+ * Sorted keys/infos/positions are written in sorted order.  `thr` >= 1. */
+int orc_runs(int64_t N, const int64_t* keys, const int64_t* infos, int64_t thr,
+             int64_t* sorted_keys, int64_t* sorted_infos, int64_t* sorted_pos,
+             int64_t* unique_ids, int64_t* run_lengths, int64_t* cumulative,
+             int64_t* num_runs, int64_t* long_run_ids, int64_t* num_long) {
+  if (N < 0 || thr < 1) return ORC_INVALID_ARGUMENT;
+  orc_keypos* kp = (orc_keypos*)malloc(sizeof(orc_keypos) * (size_t)(N > 0 ? N : 1));
+  if (kp == NULL) return ORC_INVALID_ARGUMENT;
+  for (int64_t i = 0; i < N; ++i) {
+    kp[i].key = keys[i];
+    kp[i].pos = i;
+  }
+  qsort(kp, (size_t)N, sizeof(orc_keypos), orc_cmp_keypos);
+  int64_t U = 0;
+  for (int64_t i = 0; i < N; ++i) {
+    sorted_keys[i] = kp[i].key;
+    sorted_infos[i] = infos[kp[i].pos];
+    sorted_pos[i] = kp[i].pos;
+    if (i == 0 || kp[i].key != kp[i - 1].key) {
+      unique_ids[U] = kp[i].key;
+      cumulative[U] = i;
+      ++U;
+    }
+  }
+  cumulative[U] = N;
+  int64_t nl = 0;
+  for (int64_t r = 0; r < U; ++r) {
+    run_lengths[r] = cumulative[r + 1] - cumulative[r];
+    if (run_lengths[r] >= thr) long_run_ids[nl++] = r;
+  }
+  *num_runs = U;
+  *num_long = nl;
+  free(kp);
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Aggregated row gradients                                                   */
+/* ------------------------------------------------------------------------ */
+
+static int64_t orc_find(const int64_t* sorted, int64_t n, int64_t x) {
+  int64_t lo = 0, hi = n;
+  while (lo < hi) {
+    int64_t mid = lo + (hi - lo) / 2;
+    if (sorted[mid] < x)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  return (lo < n && sorted[lo] == x) ? lo : -1;
+}
+
+/* G[k][d] = sum over lookups i with linear id rows[k] of
+ *           coef_i * grad_output[b_i][D_offsets[t] + d]     (bag mode)
+ *           grad_output[i][d]                                (nobag)
+ * for d < D_t, accumulated in double; columns d >= D_t are left 0.
+ * This is the plain definition the pages' kernels compute: the dense
+ * gradient kernel adds every occurrence's output-gradient row into the
+ * table row [P2 `cache_backward_dense_kernel`; P3 `_embedding_bwd_kernel`,
+ * which also widens a 16-bit gradient to fp32 first], with the bag's mean
+ * scale [P1 `grad_mean_kernel`] and per-sample weight [P1 weighted kernels]
+ * folded in.  `rows` must be sorted ascending and distinct; `hits[k]` gets
+ * the number of lookups of rows[k]. */
+int orc_row_grads(const orc_problem* p, int64_t nreq, const int64_t* rows,
+                  int32_t ldg, double* G, int64_t* hits) {
+  int st = orc_validate(p);
+  if (st != ORC_OK) return st;
+  for (int64_t k = 1; k < nreq; ++k)
+    if (rows[k] <= rows[k - 1]) return ORC_INVALID_ARGUMENT;
+  memset(G, 0, sizeof(double) * (size_t)nreq * (size_t)ldg);
+  memset(hits, 0, sizeof(int64_t) * (size_t)nreq);
+  const int nobag = p->pooling == ORC_POOL_NONE;
+  const int64_t width = p->D_offsets[p->T];
+  for (int32_t t = 0; t < p->T; ++t) {
+    const int D = orc_table_D(p, t);
+    if (D > ldg) return ORC_INVALID_ARGUMENT;
+    for (int32_t b = 0; b < orc_num_bags(p); ++b) {
+      int64_t s, e;
+      orc_bag_range(p, t, b, &s, &e);
+      int64_t L = e - s;
+      double scale = (p->pooling == ORC_POOL_MEAN && L > 0) ? 1.0 / (double)L
+                                                            : 1.0;
+      for (int64_t i = s; i < e; ++i) {
+        int64_t k = orc_find(rows, nreq, p->hash_size_cumsum[t] + p->indices[i]);
+        if (k < 0) continue;
+        hits[k] += 1;
+        double* g = G + k * (int64_t)ldg;
+        if (nobag) {
+          for (int d = 0; d < D; ++d) g[d] += orc_grad(p, i, D, d);
+        } else {
+          double c = scale * (p->per_sample_weights
+                                  ? (double)p->per_sample_weights[i]
+                                  : 1.0);
+          for (int d = 0; d < D; ++d)
+            g[d] += c * orc_grad(p, b, width, p->D_offsets[t] + d);
+        }
+      }
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Row updates                                                                */
+/* ------------------------------------------------------------------------ */
+
+/* Applies the output step to `nrows` rows, once per distinct row, on the
+ * aggregated gradient G (row k has D[k] columns, leading dimension ldg):
+ *  ORC_DENSE, accumulate=0: out = G, the fresh dense gradient whose other
+ *        rows are zero [P1 host entry: grad_dev_weights = zeros_like(...),
+ *        kernels store grad_sum into the row].
+ *  ORC_DENSE, accumulate=1: out = out0 + G [P3 adds into grad_weight].
+ *  ORC_SGD: w = w0 - lr * G [P2 `cache_backward_sgd_kernel`,
+ *        `update_tt_cores_sgd_kernel`].
+ *  ORC_ROWWISE_ADAGRAD: m = m0 + (1/D) * sum_d G[d]^2;
+ *        w = w0 - lr * G / (sqrt(m) + eps)
+ *        [P2 `cache_backward_rowwise_adagrad_approx_kernel`: the state grows
+ *        by the mean square of the row gradient and the multiplier uses the
+ *        grown state, with eps outside the square root, as also in
+ *        `update_tt_cores_adagrad_kernel`].  Reading: applied once per
+ *        distinct row on the summed gradient (the "exact" method), not once
+ *        per occurrence as the approximate page kernel does.
+ * Everything is computed in double and rounded once to fp32.
+ * rows: in/out [nrows][ldg] (w0/out0 in, result out); mom: in/out [nrows]. */
+int orc_update_rows(int32_t mode, int32_t accumulate, int64_t nrows,
+                    const int32_t* D, int32_t ldg, const double* G, float lr,
+                    float eps, float* rows, float* mom) {
+  for (int64_t k = 0; k < nrows; ++k) {
+    const double* g = G + k * (int64_t)ldg;
+    float* w = rows + k * (int64_t)ldg;
+    const int Dk = D[k];
+    if (Dk <= 0 || Dk > ldg) return ORC_INVALID_ARGUMENT;
+    if (mode == ORC_DENSE) {
+      for (int d = 0; d < Dk; ++d)
+        w[d] = accumulate ? (float)((double)w[d] + g[d]) : (float)g[d];
+    } else if (mode == ORC_SGD) {
+      for (int d = 0; d < Dk; ++d)
+        w[d] = (float)((double)w[d] - (double)lr * g[d]);
+    } else if (mode == ORC_ROWWISE_ADAGRAD) {
+      double sumsq = 0.0;
+      for (int d = 0; d < Dk; ++d) sumsq += g[d] * g[d];
+      double m = (double)mom[k] + sumsq / (double)Dk;
+      double mult = (double)lr / (sqrt(m) + (double)eps);
+      for (int d = 0; d < Dk; ++d)
+        w[d] = (float)((double)w[d] - g[d] * mult);
+      mom[k] = (float)m;
+    } else {
+      return ORC_INVALID_ARGUMENT;
+    }
+  }
+  return ORC_OK;
+}
