@@ -1,0 +1,206 @@
+/*
+ * sgb.h -- C ABI of the MI355X (gfx950) pooled embedding-bag backward.
+ *
+ * The library computes the backward pass of pooled embedding bags: the
+ * per-bag output gradient grad_output[B][sum_t D_t] (sum, mean or
+ * per-sample-weighted pooling), or the per-token gradient [N][D] of the
+ * unpooled ("nobag") case, is scattered onto the table rows named by
+ * (indices, offsets).  The work is deduplicated: linear row ids are sorted,
+ * run-length encoded, and each run (one distinct row) is reduced once, then
+ * written once as a dense fp32 gradient row or as an in-place SGD or
+ * row-wise Adagrad update.
+ *
+ * Defining passages (pages by title, sections by kernel or function):
+ *  - "fbgemm_gpu/codegen/embedding_backward_split_template.cu" (FBGEMM):
+ *    host entry `split_embedding{_nobag}_backward_codegen_{opt}_{w}_exact_cuda`
+ *    (argument list, checks T > 0 and B > 0, empty-input early return,
+ *    table-major offsets of length B*T+1, `hash_size_cumsum`, `D_offsets`,
+ *    `max_segment_length_per_warp`), `find_long_segments`, `grad_mean_kernel`,
+ *    the cta-per-row and warp-per-row kernels (per-run reduction and the
+ *    dense-gradient store).
+ *  - "tt_embeddings_cuda.cu" (FBTT-Embedding): the three output modes
+ *    (SGD, Adagrad, dense) and the formulas of the dense, SGD and row-wise
+ *    Adagrad cache-backward kernels; D % 4 == 0 checks.
+ *  - "Function _embedding_bwd_kernel" (tinygrad): the nobag backward, fp32
+ *    accumulation of a 16-bit gradient into a dense grad_weight.
+ *
+ * Conventions for every entry point:
+ *  - All functions are plain C; no C++ or torch types cross the boundary.
+ *  - "device pointer" means memory on the GPU the plan was created on;
+ *    "host pointer" means ordinary CPU memory.  The caller owns every buffer
+ *    it passes (including the workspace) and keeps it alive until the work
+ *    enqueued on `stream` has finished.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *  - Work is enqueued asynchronously; functions return as soon as it is
+ *    enqueued.  Only sgb_device_status() synchronises.
+ *  - Argument errors are detected on the host before anything is enqueued;
+ *    nothing is written in that case.  Errors in the *contents* of device
+ *    arrays (an index outside its table, offsets that decrease or do not
+ *    start at 0 / end at N) are detected by the kernels, recorded in a
+ *    sticky status word in the workspace and reported by sgb_device_status();
+ *    the kernels never read or write outside the buffers, but the outputs are
+ *    then unspecified.
+ *  - Results are deterministic: the same inputs give bit-identical outputs.
+ *  - A plan is immutable after creation and may be used from several host
+ *    threads; concurrent calls need distinct workspaces.
+ */
+#ifndef SGB_H
+#define SGB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct sgb_plan_s* sgb_plan;
+
+typedef enum {
+  SGB_OK = 0,
+  SGB_ERR_INVALID_ARGUMENT = 1,   /* bad argument, detected on the host        */
+  SGB_ERR_UNSUPPORTED = 2,        /* valid request this library does not do    */
+  SGB_ERR_WORKSPACE_TOO_SMALL = 3,
+  SGB_ERR_INDEX_OUT_OF_RANGE = 4, /* device-detected: index outside [0, E_t)   */
+  SGB_ERR_BAD_OFFSETS = 5,        /* device-detected: offsets malformed        */
+  SGB_ERR_HIP = 6,                /* a HIP runtime call failed                 */
+  SGB_ERR_INTERNAL = 7            /* device-detected: a bounded wait expired   */
+} sgb_status;
+
+/* Pooling of the forward pass, FBGEMM page host entry `pooling_mode` and the
+ * nobag variant.  SGB_POOL_NONE is the nobag (per-token) case. */
+typedef enum { SGB_POOL_SUM = 0, SGB_POOL_MEAN = 1, SGB_POOL_NONE = 2 } sgb_pooling;
+
+/* Element type of grad_output. */
+typedef enum { SGB_F32 = 0, SGB_BF16 = 1 } sgb_dtype;
+
+/* Output mode, FBTT page OPTIM_{SGD, ADAGRAD, DENSE} (Adagrad is row-wise). */
+typedef enum { SGB_DENSE_GRAD = 0, SGB_SGD = 1, SGB_ROWWISE_ADAGRAD = 2 } sgb_mode;
+
+/*
+ * sgb_plan_create -- immutable table metadata for a set of T tables.
+ *  out                  receives the plan (host pointer to a handle).
+ *  T                    number of tables, 1 <= T <= 65536.
+ *  hash_size_cumsum     host, int64[T+1]: [0] = 0, strictly increasing;
+ *                       table t owns linear ids [hsc[t], hsc[t+1]), so
+ *                       E_t = hsc[t+1] - hsc[t] rows (FBGEMM host entry).
+ *  D_offsets            host, int32[T+1]: [0] = 0, D_t = D_offsets[t+1] -
+ *                       D_offsets[t] with D_t % 4 == 0 and 4 <= D_t <= 8192;
+ *                       D_offsets[t] is table t's first column in a bag row
+ *                       of grad_output.  Nobag plans need one common D_t.
+ *  pooling              an sgb_pooling value.
+ *  max_segment_length_per_warp
+ *                       >= 1.  Runs with at least this many lookups are
+ *                       "long" (FBGEMM `find_long_segments`, test `>=`) and
+ *                       are split across many wavefronts.
+ * The host arrays are copied; the plan allocates a few small device arrays on
+ * the device current at creation.  Returns SGB_ERR_INVALID_ARGUMENT on any
+ * violated rule, SGB_ERR_HIP if a device allocation fails.
+ */
+sgb_status sgb_plan_create(sgb_plan* out, int32_t T, const int64_t* hash_size_cumsum,
+                           const int32_t* D_offsets, int32_t pooling,
+                           int32_t max_segment_length_per_warp);
+
+/* Frees the plan and its device arrays.  NULL is ignored. */
+void sgb_plan_destroy(sgb_plan plan);
+
+/*
+ * sgb_workspace_bytes -- size of the device workspace needed by one
+ * sgb_backward() call with `num_indices` lookups and `B` bags per table
+ * (B is ignored for a nobag call without offsets; pass 0).  Also the size
+ * needed by sgb_device_status()/sgb_runs_view_get() on that workspace.
+ * Grows with num_indices and with 1 / max_segment_length_per_warp.
+ * Limits: 0 <= num_indices < 2^30, B * T < 2^31.
+ */
+sgb_status sgb_workspace_bytes(sgb_plan plan, int64_t num_indices, int32_t B, size_t* bytes);
+
+/* One batch of inputs; every pointer is a device pointer, read only. */
+typedef struct {
+  const void* grad_output;          /* bag: [B][D_offsets[T]] row-major;
+                                       nobag: [num_indices][D] row-major    */
+  int32_t grad_dtype;               /* an sgb_dtype value                   */
+  const int64_t* indices;           /* [num_indices], row within its table  */
+  int64_t num_indices;              /* N                                    */
+  const int64_t* offsets;           /* [B*T+1] table-major (bag t*B+b spans
+                                       [offsets[t*B+b], offsets[t*B+b+1]));
+                                       may be NULL only for nobag with T == 1 */
+  int32_t B;                        /* bags per table (0 if offsets NULL)   */
+  const float* per_sample_weights;  /* [num_indices] or NULL; must be NULL
+                                       for nobag (FBGEMM: nobag is generated
+                                       only unweighted)                     */
+} sgb_batch;
+
+/* Where and how the result is written; device pointers, caller-owned. */
+typedef struct {
+  int32_t mode;      /* an sgb_mode value                                        */
+  float* weights;    /* SGD / Adagrad: flat fp32 rows, table t row i at element
+                        woff[t] + i * D_t with woff[t] = sum_{t'<t} E_t' * D_t'  */
+  float* momentum;   /* Adagrad: fp32[sum_t E_t], one value per row, indexed by
+                        linear id hsc[t] + i                                      */
+  float* grad;       /* DENSE: fp32, same layout as weights                       */
+  int32_t accumulate;/* DENSE: 0 = the whole buffer is overwritten (zeros except
+                        touched rows, which get their gradient); 1 = touched rows
+                        get grad[row] += G_row, all others untouched             */
+  float lr;          /* SGD / Adagrad learning rate                               */
+  float eps;         /* Adagrad epsilon (added outside the square root)          */
+} sgb_update;
+
+/*
+ * sgb_backward -- enqueue one backward pass on `stream`.
+ *  For every distinct linear row r touched by the batch, with
+ *    G_r[d] = sum over lookups i of row r of coef_i * grad_output[b_i][D_offsets[t] + d]
+ *    (nobag: grad_output[i][d]); coef_i = per_sample_weight_i (or 1) times
+ *    1/L_b under MEAN pooling (FBGEMM `grad_mean_kernel`):
+ *   DENSE       grad[r] = G_r (accumulate=0, other rows zeroed) or
+ *               grad[r] += G_r (accumulate=1)          (FBGEMM dense store;
+ *                                                       tinygrad grad_weight add)
+ *   SGD         w_r -= lr * G_r                          (FBTT SGD kernel)
+ *   ROWWISE_ADAGRAD  m_r += mean_d G_r[d]^2; w_r -= lr * G_r / (sqrt(m_r) + eps)
+ *                                         (FBTT row-wise Adagrad kernel, once
+ *                                          per distinct row on the summed G)
+ *  Each touched row is read and written exactly once; untouched rows and
+ *  state are not written (except zeros in a fresh dense gradient).  Sums are
+ *  fp32 in a fixed order.  num_indices == 0 is a no-op (a fresh dense grad
+ *  is still zero-filled).  Allocates nothing.
+ */
+sgb_status sgb_backward(sgb_plan plan, const sgb_batch* batch, const sgb_update* update,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sgb_device_status -- synchronises `stream`, then stores in *out the first
+ * error the kernels recorded in `workspace` during the last sgb_backward()
+ * that used it (SGB_OK if none).  The return value reports failures of this
+ * call itself (SGB_ERR_HIP).
+ */
+sgb_status sgb_device_status(sgb_plan plan, const void* workspace, void* stream, int32_t* out);
+
+/*
+ * Introspection of the run structure the last sgb_backward() left in
+ * `workspace` (device pointers into it; valid until the workspace is reused).
+ * Same kernels, no second code path.  Sorted entries are packed 64-bit words
+ * (linear_id << info_bits) | info, info = t*B + b (bag) or i*T + t (nobag),
+ * in stable sorted order (FBGEMM `transpose_embedding_input` outputs, with the
+ * id and info carried in one word).  Counts live on the device.
+ */
+typedef struct {
+  const uint64_t* sorted_packed;    /* [N]                                     */
+  int32_t info_bits;
+  const int64_t* unique_ids;        /* [num_runs]   sorted distinct linear ids */
+  const int32_t* run_lengths;       /* [num_runs]                              */
+  const int32_t* cumulative;        /* [num_runs+1] start of each run, [U] = N */
+  const int32_t* num_runs;          /* [1]                                     */
+  const int32_t* long_run_ids;      /* [num_long]   ascending                  */
+  const int64_t* num_long_run_ids;  /* [1]                                     */
+} sgb_runs_view;
+
+sgb_status sgb_runs_view_get(sgb_plan plan, const void* workspace, int64_t num_indices,
+                             int32_t B, sgb_runs_view* out);
+
+/* Static string naming a status code. */
+const char* sgb_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGB_H */

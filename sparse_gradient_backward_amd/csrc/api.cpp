@@ -1,0 +1,464 @@
+// api.cpp -- the C ABI declared in include/sgb.h: plan creation, host-side
+// validation, workspace layout and the launch sequence of one backward pass.
+//
+// Host checks follow the FBGEMM page "embedding_backward_split_template.cu",
+// host entry `split_embedding{_nobag}_backward_codegen_..._exact_cuda`
+// (T > 0, B > 0, offsets of length B*T+1, early return when there are no
+// indices, the embedding-dimension bound), and the FBTT page
+// "tt_embeddings_cuda.cu" (D % 4 == 0).  Nothing here touches the data:
+// every step of the computation runs in the kernels of kernels.hip.
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "../../include/sgb.h"
+#include "internal.h"
+
+using namespace sgb;
+
+struct sgb_plan_s {
+  int device = 0;
+  int32_t T = 0;
+  int32_t pooling = 0;
+  int32_t thr = 1;
+  int32_t Dmax = 0;
+  int64_t total_rows = 0;   // sum of E_t
+  int64_t total_elems = 0;  // sum of E_t * D_t
+  int key_bits = 0;
+  std::vector<int64_t> hsc, woff;
+  std::vector<int32_t> doff;
+  int64_t* d_hsc = nullptr;
+  int32_t* d_doff = nullptr;
+  int64_t* d_woff = nullptr;
+  FillBlock* d_fill = nullptr;
+  int32_t n_fill = 0;
+  int num_cus = 1;
+  int red_grid[2] = {1, 1};
+};
+
+namespace {
+
+int bitlen(uint64_t v) {  // number of bits needed to hold v (0 for 0)
+  int b = 0;
+  while (v) {
+    ++b;
+    v >>= 1;
+  }
+  return b;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) return;
+    ok = (prev == dev) || (hipSetDevice(dev) == hipSuccess);
+  }
+  ~DeviceGuard() {
+    if (ok && prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+// Workspace layout of one call; every piece 256-byte aligned.
+struct Layout {
+  int info_bits = 0;
+  int npasses = 0;
+  int pass_bits[kMaxPasses] = {};
+  int pass_key_shift[kMaxPasses] = {};
+  int64_t sort_tiles = 0, scan_tiles = 0;
+  int64_t max_long = 0;   // bound on the number of long runs
+  int64_t max_items = 0;  // bound on the chunks over all long runs
+  int32_t ch_base = 0;
+  size_t hdr = 0, hist = 0, zero_begin = 0, sort_lb = 0, rle_lb = 0, post_lb = 0, bitmap = 0,
+         zero_end_nobitmap = 0, zero_end_bitmap = 0;
+  size_t kvA = 0, kvB = 0, coefA = 0, coefB = 0, uniq = 0, cum = 0, lens = 0, longs = 0,
+         chunkb = 0, runtk = 0, sctk = 0, part = 0, total = 0;
+};
+
+sgb_status make_layout(const sgb_plan_s* p, int64_t N, int32_t B, bool has_offsets, Layout* L) {
+  if (N < 0 || N >= (1ll << 30)) return SGB_ERR_INVALID_ARGUMENT;
+  const bool nobag = p->pooling == SGB_POOL_NONE;
+  uint64_t info_max = 0;
+  if (nobag) {
+    info_max = N > 0 ? (uint64_t)(N - 1) * (uint64_t)p->T + (uint64_t)(p->T - 1) : 0;
+  } else {
+    if (B <= 0) return SGB_ERR_INVALID_ARGUMENT;
+    if ((int64_t)B * p->T >= (1ll << 31)) return SGB_ERR_INVALID_ARGUMENT;
+    info_max = (uint64_t)B * (uint64_t)p->T - 1;
+  }
+  if (has_offsets && (int64_t)B * p->T >= (1ll << 31)) return SGB_ERR_INVALID_ARGUMENT;
+  if (info_max >= (1ull << 32)) return SGB_ERR_UNSUPPORTED;
+  L->info_bits = bitlen(info_max);
+  if (L->info_bits + p->key_bits > 64) return SGB_ERR_UNSUPPORTED;
+  L->npasses = (p->key_bits + 8) / 9;
+  int at = 0;
+  for (int i = 0; i < L->npasses; ++i) {
+    L->pass_bits[i] = p->key_bits / L->npasses + (i < p->key_bits % L->npasses ? 1 : 0);
+    L->pass_key_shift[i] = at;
+    at += L->pass_bits[i];
+  }
+  L->sort_tiles = (N + kSortTile - 1) / kSortTile;
+  L->scan_tiles = (N + kScanTile - 1) / kScanTile;
+  L->ch_base = std::max<int32_t>(p->thr, kChunkMin);
+  L->max_long = N / p->thr + 1;
+  L->max_items = N / L->ch_base + L->max_long + 1;
+
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    o = align_up(o, 256);
+    const size_t at_ = o;
+    o += bytes;
+    return at_;
+  };
+  L->hdr = take(sizeof(Header));
+  L->hist = take(sizeof(uint32_t) * kMaxPasses * kRadixMax);
+  L->zero_begin = align_up(o, 256);
+  L->sort_lb = take(sizeof(uint32_t) * (size_t)std::max(L->npasses, 1) * L->sort_tiles * kRadixMax);
+  L->rle_lb = take(sizeof(uint32_t) * (size_t)L->scan_tiles);
+  L->post_lb = take(sizeof(uint64_t) * (size_t)L->scan_tiles);
+  L->zero_end_nobitmap = align_up(o, 256);
+  L->bitmap = take(sizeof(uint32_t) * (size_t)((p->total_rows + 31) / 32));
+  L->zero_end_bitmap = align_up(o, 256);
+  L->kvA = take(sizeof(uint64_t) * (size_t)N);
+  L->kvB = take(sizeof(uint64_t) * (size_t)N);
+  L->coefA = take(sizeof(float) * (size_t)N);
+  L->coefB = take(sizeof(float) * (size_t)N);
+  L->uniq = take(sizeof(int64_t) * (size_t)N);
+  L->cum = take(sizeof(int32_t) * (size_t)(N + 1));
+  L->lens = take(sizeof(int32_t) * (size_t)N);
+  L->longs = take(sizeof(int32_t) * (size_t)L->max_long);
+  L->chunkb = take(sizeof(uint32_t) * (size_t)(L->max_long + 1));
+  L->runtk = take(sizeof(uint32_t) * (size_t)L->max_long);
+  L->sctk = take(sizeof(uint32_t) * (size_t)L->max_items);
+  L->part = take(sizeof(float) * (size_t)L->max_items * (size_t)p->Dmax);
+  L->total = align_up(o, 256);
+  return SGB_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* sgb_status_string(int32_t s) {
+  switch (s) {
+    case SGB_OK: return "SGB_OK";
+    case SGB_ERR_INVALID_ARGUMENT: return "SGB_ERR_INVALID_ARGUMENT";
+    case SGB_ERR_UNSUPPORTED: return "SGB_ERR_UNSUPPORTED";
+    case SGB_ERR_WORKSPACE_TOO_SMALL: return "SGB_ERR_WORKSPACE_TOO_SMALL";
+    case SGB_ERR_INDEX_OUT_OF_RANGE: return "SGB_ERR_INDEX_OUT_OF_RANGE";
+    case SGB_ERR_BAD_OFFSETS: return "SGB_ERR_BAD_OFFSETS";
+    case SGB_ERR_HIP: return "SGB_ERR_HIP";
+    case SGB_ERR_INTERNAL: return "SGB_ERR_INTERNAL";
+    default: return "SGB_UNKNOWN_STATUS";
+  }
+}
+
+sgb_status sgb_plan_create(sgb_plan* out, int32_t T, const int64_t* hsc, const int32_t* doff,
+                           int32_t pooling, int32_t thr) {
+  if (!out) return SGB_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  if (T < 1 || T > 65536 || !hsc || !doff || thr < 1) return SGB_ERR_INVALID_ARGUMENT;
+  if (pooling != SGB_POOL_SUM && pooling != SGB_POOL_MEAN && pooling != SGB_POOL_NONE)
+    return SGB_ERR_INVALID_ARGUMENT;
+  if (hsc[0] != 0 || doff[0] != 0) return SGB_ERR_INVALID_ARGUMENT;
+  for (int32_t t = 0; t < T; ++t) {
+    if (hsc[t + 1] <= hsc[t]) return SGB_ERR_INVALID_ARGUMENT;
+    const int32_t D = doff[t + 1] - doff[t];
+    if (D < 4 || D > kMaxD || D % 4 != 0) return SGB_ERR_INVALID_ARGUMENT;
+    if (pooling == SGB_POOL_NONE && D != doff[1] - doff[0]) return SGB_ERR_INVALID_ARGUMENT;
+  }
+  if (hsc[T] >= (1ll << 62)) return SGB_ERR_UNSUPPORTED;
+
+  sgb_plan_s* p = new (std::nothrow) sgb_plan_s();
+  if (!p) return SGB_ERR_HIP;
+  if (hipGetDevice(&p->device) != hipSuccess) {
+    delete p;
+    return SGB_ERR_HIP;
+  }
+  p->T = T;
+  p->pooling = pooling;
+  p->thr = thr;
+  p->hsc.assign(hsc, hsc + T + 1);
+  p->doff.assign(doff, doff + T + 1);
+  p->woff.assign(T + 1, 0);
+  std::vector<FillBlock> fill;
+  for (int32_t t = 0; t < T; ++t) {
+    const int64_t E = hsc[t + 1] - hsc[t];
+    const int32_t D = doff[t + 1] - doff[t];
+    p->Dmax = std::max(p->Dmax, D);
+    p->woff[t + 1] = p->woff[t] + E * D;
+    const int64_t rows_per = std::max<int64_t>(1, 16384 / D);
+    for (int64_t r0 = 0; r0 < E; r0 += rows_per)
+      fill.push_back(FillBlock{t, (int32_t)std::min<int64_t>(rows_per, E - r0), r0});
+  }
+  p->total_rows = hsc[T];
+  p->total_elems = p->woff[T];
+  p->key_bits = bitlen((uint64_t)(p->total_rows - 1));
+  p->n_fill = (int32_t)fill.size();
+
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, p->device) == hipSuccess && prop.multiProcessorCount > 0)
+    p->num_cus = prop.multiProcessorCount;
+  p->red_grid[0] = p->num_cus * reduce_blocks_per_cu(false);
+  p->red_grid[1] = p->num_cus * reduce_blocks_per_cu(true);
+
+  bool ok = hipMalloc(&p->d_hsc, sizeof(int64_t) * (T + 1)) == hipSuccess &&
+            hipMalloc(&p->d_doff, sizeof(int32_t) * (T + 1)) == hipSuccess &&
+            hipMalloc(&p->d_woff, sizeof(int64_t) * (T + 1)) == hipSuccess &&
+            hipMalloc(&p->d_fill, sizeof(FillBlock) * fill.size()) == hipSuccess;
+  ok = ok && hipMemcpy(p->d_hsc, p->hsc.data(), sizeof(int64_t) * (T + 1),
+                       hipMemcpyHostToDevice) == hipSuccess;
+  ok = ok && hipMemcpy(p->d_doff, p->doff.data(), sizeof(int32_t) * (T + 1),
+                       hipMemcpyHostToDevice) == hipSuccess;
+  ok = ok && hipMemcpy(p->d_woff, p->woff.data(), sizeof(int64_t) * (T + 1),
+                       hipMemcpyHostToDevice) == hipSuccess;
+  ok = ok && hipMemcpy(p->d_fill, fill.data(), sizeof(FillBlock) * fill.size(),
+                       hipMemcpyHostToDevice) == hipSuccess;
+  if (!ok) {
+    sgb_plan_destroy(p);
+    return SGB_ERR_HIP;
+  }
+  *out = p;
+  return SGB_OK;
+}
+
+void sgb_plan_destroy(sgb_plan p) {
+  if (!p) return;
+  DeviceGuard g(p->device);
+  if (p->d_hsc) (void)hipFree(p->d_hsc);
+  if (p->d_doff) (void)hipFree(p->d_doff);
+  if (p->d_woff) (void)hipFree(p->d_woff);
+  if (p->d_fill) (void)hipFree(p->d_fill);
+  delete p;
+}
+
+sgb_status sgb_workspace_bytes(sgb_plan p, int64_t N, int32_t B, size_t* bytes) {
+  if (!p || !bytes) return SGB_ERR_INVALID_ARGUMENT;
+  Layout L;
+  const bool nobag_no_off = p->pooling == SGB_POOL_NONE && B == 0;
+  if (nobag_no_off && p->T != 1) return SGB_ERR_INVALID_ARGUMENT;
+  sgb_status st = make_layout(p, N, B, !nobag_no_off, &L);
+  if (st != SGB_OK) return st;
+  *bytes = L.total;
+  return SGB_OK;
+}
+
+sgb_status sgb_backward(sgb_plan p, const sgb_batch* b, const sgb_update* u, void* ws,
+                        size_t ws_bytes, void* stream_) {
+  if (!p || !b || !u) return SGB_ERR_INVALID_ARGUMENT;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  const int64_t N = b->num_indices;
+  const bool nobag = p->pooling == SGB_POOL_NONE;
+  if (N < 0 || N >= (1ll << 30)) return SGB_ERR_INVALID_ARGUMENT;
+  if (b->grad_dtype != SGB_F32 && b->grad_dtype != SGB_BF16) return SGB_ERR_INVALID_ARGUMENT;
+  if (nobag && b->per_sample_weights) return SGB_ERR_UNSUPPORTED;
+  if (!b->offsets && !(nobag && p->T == 1)) return SGB_ERR_INVALID_ARGUMENT;
+  if (b->offsets && b->B <= 0) return SGB_ERR_INVALID_ARGUMENT;
+  if (u->mode != SGB_DENSE_GRAD && u->mode != SGB_SGD && u->mode != SGB_ROWWISE_ADAGRAD)
+    return SGB_ERR_INVALID_ARGUMENT;
+  if (u->mode == SGB_DENSE_GRAD && !u->grad) return SGB_ERR_INVALID_ARGUMENT;
+  if (u->mode == SGB_SGD && !u->weights) return SGB_ERR_INVALID_ARGUMENT;
+  if (u->mode == SGB_ROWWISE_ADAGRAD && (!u->weights || !u->momentum))
+    return SGB_ERR_INVALID_ARGUMENT;
+  if (u->mode == SGB_ROWWISE_ADAGRAD && p->Dmax > kMaxCb * kColBlock) return SGB_ERR_UNSUPPORTED;
+  float* out = u->mode == SGB_DENSE_GRAD ? u->grad : u->weights;
+  if (!aligned(out, 16)) return SGB_ERR_INVALID_ARGUMENT;
+  const bool fresh = u->mode == SGB_DENSE_GRAD && !u->accumulate;
+  DeviceGuard guard(p->device);
+  if (!guard.ok) return SGB_ERR_HIP;
+
+  if (N == 0) {  // FBGEMM host entry: no indices -> nothing to do (dense grad stays zero)
+    if (fresh && p->n_fill > 0) {
+      FillParams f{out, p->d_fill, p->d_hsc, p->d_doff, p->d_woff, nullptr};
+      if (launch_fill(f, p->n_fill, stream) != hipSuccess) return SGB_ERR_HIP;
+    }
+    return SGB_OK;
+  }
+  if (!b->indices || !b->grad_output) return SGB_ERR_INVALID_ARGUMENT;
+  if (!aligned(b->grad_output, b->grad_dtype == SGB_F32 ? 16 : 8)) return SGB_ERR_INVALID_ARGUMENT;
+  if (!ws || !aligned(ws, 256)) return SGB_ERR_INVALID_ARGUMENT;
+  Layout L;
+  sgb_status st = make_layout(p, N, b->offsets ? b->B : 0, b->offsets != nullptr, &L);
+  if (st != SGB_OK) return st;
+  if (ws_bytes < L.total) return SGB_ERR_WORKSPACE_TOO_SMALL;
+
+  Header* hdr = at<Header>(ws, L.hdr);
+  uint32_t* status = &hdr->status;
+  const bool has_coef = (p->pooling == SGB_POOL_MEAN) || (b->per_sample_weights != nullptr);
+  hipError_t e = launch_init(ws, L.zero_begin, stream);
+  if (e != hipSuccess) return SGB_ERR_HIP;
+
+  // linearise + digit histograms (+ clear look-back words and the bitmap)
+  LinParams lp{};
+  lp.indices = b->indices;
+  lp.offsets = b->offsets;
+  lp.psw = b->per_sample_weights;
+  lp.hsc = p->d_hsc;
+  lp.N = N;
+  lp.B = b->offsets ? b->B : 0;
+  lp.T = p->T;
+  lp.pooling = p->pooling;
+  lp.info_bits = L.info_bits;
+  lp.kv_out = at<uint64_t>(ws, L.kvA);
+  lp.coef_out = has_coef ? at<float>(ws, L.coefA) : nullptr;
+  lp.hist = at<uint32_t>(ws, L.hist);
+  lp.npasses = L.npasses;
+  for (int i = 0; i < L.npasses; ++i) {
+    lp.pass_shift[i] = L.pass_key_shift[i];
+    lp.pass_bits[i] = L.pass_bits[i];
+  }
+  lp.status = status;
+  lp.zero_begin = at<uint4>(ws, L.zero_begin);
+  lp.zero_vec4 = (int64_t)(((fresh ? L.zero_end_bitmap : L.zero_end_nobitmap) - L.zero_begin) / 16);
+  const int64_t lin_tiles = b->offsets ? ((int64_t)b->B * p->T + kLinBags - 1) / kLinBags
+                                       : (N + kLinLookups - 1) / kLinLookups;
+  const int lin_grid = (int)std::max<int64_t>(1, std::min<int64_t>(lin_tiles, 4ll * p->num_cus));
+  if (launch_linearize(lp, lin_grid, stream) != hipSuccess) return SGB_ERR_HIP;
+
+  // LSD radix passes, ping-pong between A and B
+  uint64_t* kv_in = at<uint64_t>(ws, L.kvA);
+  uint64_t* kv_out = at<uint64_t>(ws, L.kvB);
+  float* cf_in = has_coef ? at<float>(ws, L.coefA) : nullptr;
+  float* cf_out = has_coef ? at<float>(ws, L.coefB) : nullptr;
+  for (int ps = 0; ps < L.npasses; ++ps) {
+    SortParams sp{};
+    sp.kv_in = kv_in;
+    sp.coef_in = cf_in;
+    sp.kv_out = kv_out;
+    sp.coef_out = cf_out;
+    sp.N = N;
+    sp.shift = L.info_bits + L.pass_key_shift[ps];
+    sp.bits = L.pass_bits[ps];
+    sp.hist = at<uint32_t>(ws, L.hist) + ps * kRadixMax;
+    sp.lookback = at<uint32_t>(ws, L.sort_lb) + (size_t)ps * L.sort_tiles * kRadixMax;
+    sp.tile_ctr = &hdr->sort_tile_ctr[ps];
+    sp.status = status;
+    if (launch_sort_pass(sp, (int)L.sort_tiles, stream) != hipSuccess) return SGB_ERR_HIP;
+    std::swap(kv_in, kv_out);
+    std::swap(cf_in, cf_out);
+  }
+  const uint64_t* kv_sorted = kv_in;
+  const float* cf_sorted = cf_in;
+
+  RleParams rp{};
+  rp.kv = kv_sorted;
+  rp.N = N;
+  rp.info_bits = L.info_bits;
+  rp.unique_ids = at<int64_t>(ws, L.uniq);
+  rp.cum = at<int32_t>(ws, L.cum);
+  rp.num_runs = &hdr->num_runs;
+  rp.lookback = at<uint32_t>(ws, L.rle_lb);
+  rp.tile_ctr = &hdr->rle_tile_ctr;
+  rp.status = status;
+  if (launch_rle(rp, (int)L.scan_tiles, stream) != hipSuccess) return SGB_ERR_HIP;
+
+  PostParams pp{};
+  pp.cum = rp.cum;
+  pp.num_runs = rp.num_runs;
+  pp.unique_ids = rp.unique_ids;
+  pp.thr = p->thr;
+  pp.ch_base = L.ch_base;
+  pp.run_lengths = at<int32_t>(ws, L.lens);
+  pp.long_ids = at<int32_t>(ws, L.longs);
+  pp.chunk_begin = at<uint32_t>(ws, L.chunkb);
+  pp.sc_ticket = at<uint32_t>(ws, L.sctk);
+  pp.run_ticket = at<uint32_t>(ws, L.runtk);
+  pp.num_long = &hdr->num_long;
+  pp.total_items = &hdr->total_items;
+  pp.bitmap = fresh ? at<uint32_t>(ws, L.bitmap) : nullptr;
+  pp.total_rows = p->total_rows;
+  pp.lookback = at<uint64_t>(ws, L.post_lb);
+  pp.tile_ctr = &hdr->post_tile_ctr;
+  pp.status = status;
+  if (launch_post(pp, (int)L.scan_tiles, stream) != hipSuccess) return SGB_ERR_HIP;
+
+  if (fresh) {
+    FillParams f{out, p->d_fill, p->d_hsc, p->d_doff, p->d_woff, pp.bitmap};
+    if (launch_fill(f, p->n_fill, stream) != hipSuccess) return SGB_ERR_HIP;
+  }
+
+  RedParams q{};
+  q.grad = b->grad_output;
+  q.kv = kv_sorted;
+  q.coef = has_coef ? cf_sorted : nullptr;
+  q.hsc = p->d_hsc;
+  q.doff = p->d_doff;
+  q.woff = p->d_woff;
+  q.unique_ids = rp.unique_ids;
+  q.cum = rp.cum;
+  q.long_ids = pp.long_ids;
+  q.chunk_begin = pp.chunk_begin;
+  q.num_runs = rp.num_runs;
+  q.total_items = pp.total_items;
+  q.work_ctr = &hdr->work_ctr;
+  q.sc_ticket = pp.sc_ticket;
+  q.run_ticket = pp.run_ticket;
+  q.partials = at<float>(ws, L.part);
+  q.out = out;
+  q.mom = u->mode == SGB_ROWWISE_ADAGRAD ? u->momentum : nullptr;
+  q.status = status;
+  q.N = N;
+  q.row_stride = nobag ? (int64_t)p->doff[1] : (int64_t)p->doff[p->T];
+  q.slot_floats = p->Dmax;
+  q.info_bits = L.info_bits;
+  q.B = b->offsets ? b->B : 0;
+  q.T = p->T;
+  q.nobag = nobag ? 1 : 0;
+  q.thr = p->thr;
+  q.ch_base = L.ch_base;
+  q.mode = u->mode;
+  q.accumulate = u->accumulate ? 1 : 0;
+  q.lr = u->lr;
+  q.eps = u->eps;
+  const bool bf16 = b->grad_dtype == SGB_BF16;
+  if (launch_reduce(q, &hdr->num_long, bf16, p->red_grid[bf16 ? 1 : 0], stream) != hipSuccess)
+    return SGB_ERR_HIP;
+  return SGB_OK;
+}
+
+sgb_status sgb_device_status(sgb_plan p, const void* ws, void* stream_, int32_t* out) {
+  if (!p || !ws || !out) return SGB_ERR_INVALID_ARGUMENT;
+  DeviceGuard guard(p->device);
+  if (!guard.ok) return SGB_ERR_HIP;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  uint32_t v = 0;
+  if (hipMemcpyAsync(&v, ws, sizeof(v), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return SGB_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return SGB_ERR_HIP;
+  *out = (int32_t)v;
+  return SGB_OK;
+}
+
+sgb_status sgb_runs_view_get(sgb_plan p, const void* ws, int64_t N, int32_t B,
+                             sgb_runs_view* out) {
+  if (!p || !ws || !out) return SGB_ERR_INVALID_ARGUMENT;
+  Layout L;
+  const bool nobag_no_off = p->pooling == SGB_POOL_NONE && B == 0;
+  sgb_status st = make_layout(p, N, B, !nobag_no_off, &L);
+  if (st != SGB_OK) return st;
+  void* w = const_cast<void*>(ws);
+  Header* hdr = at<Header>(w, L.hdr);
+  out->sorted_packed = at<uint64_t>(w, (L.npasses % 2 == 0) ? L.kvA : L.kvB);
+  out->info_bits = L.info_bits;
+  out->unique_ids = at<int64_t>(w, L.uniq);
+  out->run_lengths = at<int32_t>(w, L.lens);
+  out->cumulative = at<int32_t>(w, L.cum);
+  out->num_runs = &hdr->num_runs;
+  out->long_run_ids = at<int32_t>(w, L.longs);
+  out->num_long_run_ids = &hdr->num_long;
+  return SGB_OK;
+}
+
+}  // extern "C"

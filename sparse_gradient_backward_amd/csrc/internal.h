@@ -1,0 +1,195 @@
+// internal.h -- definitions shared by the library's host code (api.cpp) and
+// its gfx950 kernels (kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sgb {
+
+// ---------------------------------------------------------------- limits
+constexpr int kMaxPasses = 7;         // LSD passes of <= 9 bits: up to 63 key bits
+constexpr int kRadixMax = 512;        // 9-bit digits
+constexpr int kMaxCb = 4;             // Adagrad rows held in registers: D <= 4 * 256
+constexpr int kColBlock = 256;        // columns one wave covers per pass (64 lanes x 4)
+constexpr int kMaxD = 8192;
+
+// sort pass tiling
+constexpr int kSortThreads = 256;
+constexpr int kSortItems = 16;
+constexpr int kSortTile = kSortThreads * kSortItems;
+
+// run-length encoding / run post-processing tiling
+constexpr int kScanThreads = 256;
+constexpr int kScanItems = 16;
+constexpr int kScanTile = kScanThreads * kScanItems;
+
+// linearisation: bags per tile, lookups per inner step
+constexpr int kLinThreads = 256;
+constexpr int kLinBags = 512;
+constexpr int kLinLookups = 4 * kLinThreads;
+
+// long runs: chunk sizing and two-level combine
+constexpr int kChunkMin = 64;         // a chunk has at least this many lookups
+constexpr int kMaxChunks = 2048;      // a run is cut into at most this many chunks
+constexpr int kSuperChunk = 32;       // chunks combined per first-level ticket
+
+// bounded waits (look-back): iterations of ~1 us before giving up
+constexpr uint32_t kSpinLimit = 1u << 21;
+
+// status codes written by kernels (values match sgb_status)
+constexpr uint32_t kStIndex = 4;
+constexpr uint32_t kStOffsets = 5;
+constexpr uint32_t kStInternal = 7;
+
+enum { kPoolSum = 0, kPoolMean = 1, kPoolNone = 2 };
+enum { kModeDense = 0, kModeSgd = 1, kModeAdagrad = 2 };
+
+// Workspace header (offset 0).
+struct Header {
+  uint32_t status;                    // first device-detected error, 0 = none
+  uint32_t sort_tile_ctr[kMaxPasses]; // dynamic tile ids of each sort pass
+  uint32_t rle_tile_ctr;
+  uint32_t post_tile_ctr;
+  uint32_t work_ctr;                  // reducer work queue
+  int32_t num_runs;                   // U
+  int64_t num_long;                   // number of long runs
+  uint32_t total_items;               // chunks over all long runs
+  uint32_t pad[15];
+};
+static_assert(sizeof(Header) <= 128, "header too large");
+
+// A block of rows of one table that the dense zero-fill covers.
+struct FillBlock {
+  int32_t t;
+  int32_t nrows;
+  int64_t row0;
+};
+
+// ---------------------------------------------------------------- kernel parameters
+
+struct LinParams {
+  const int64_t* indices;
+  const int64_t* offsets;   // NULL: nobag, single table, no bags
+  const float* psw;
+  const int64_t* hsc;       // [T+1]
+  int64_t N;
+  int32_t B;
+  int32_t T;
+  int32_t pooling;
+  int32_t info_bits;
+  uint64_t* kv_out;
+  float* coef_out;          // NULL when every coefficient is 1
+  uint32_t* hist;           // [kMaxPasses][kRadixMax]
+  int32_t npasses;
+  int32_t pass_shift[kMaxPasses];
+  int32_t pass_bits[kMaxPasses];
+  uint32_t* status;
+  uint4* zero_begin;        // region zeroed for the later kernels
+  int64_t zero_vec4;
+};
+
+struct SortParams {
+  const uint64_t* kv_in;
+  const float* coef_in;     // NULL when there are no coefficients
+  uint64_t* kv_out;
+  float* coef_out;
+  int64_t N;
+  int32_t shift;
+  int32_t bits;
+  const uint32_t* hist;     // this pass's digit counts [kRadixMax]
+  uint32_t* lookback;       // [tiles][kRadixMax]
+  uint32_t* tile_ctr;
+  uint32_t* status;
+};
+
+struct RleParams {
+  const uint64_t* kv;       // sorted
+  int64_t N;
+  int32_t info_bits;
+  int64_t* unique_ids;
+  int32_t* cum;
+  int32_t* num_runs;
+  uint32_t* lookback;       // [tiles]
+  uint32_t* tile_ctr;
+  uint32_t* status;
+};
+
+struct PostParams {
+  const int32_t* cum;
+  const int32_t* num_runs;
+  const int64_t* unique_ids;
+  int32_t thr;
+  int32_t ch_base;          // max(thr, kChunkMin)
+  int32_t* run_lengths;
+  int32_t* long_ids;
+  uint32_t* chunk_begin;    // [num_long + 1]
+  uint32_t* sc_ticket;      // [items]
+  uint32_t* run_ticket;     // [num_long]
+  int64_t* num_long;
+  uint32_t* total_items;
+  uint32_t* bitmap;         // touched-row bitmap (fresh dense grad) or NULL
+  int64_t total_rows;       // bitmap bits
+  uint64_t* lookback;       // [tiles]
+  uint32_t* tile_ctr;
+  uint32_t* status;
+};
+
+struct FillParams {
+  float* out;
+  const FillBlock* blocks;
+  const int64_t* hsc;
+  const int32_t* doff;
+  const int64_t* woff;
+  const uint32_t* bitmap;   // NULL: every row is zero-filled
+};
+
+struct RedParams {
+  const void* grad;
+  const uint64_t* kv;       // sorted packed (id << info_bits | info)
+  const float* coef;        // sorted coefficients or NULL
+  const int64_t* hsc;
+  const int32_t* doff;
+  const int64_t* woff;
+  const int64_t* unique_ids;
+  const int32_t* cum;
+  const int32_t* long_ids;
+  const uint32_t* chunk_begin;
+  const int32_t* num_runs;
+  const uint32_t* total_items;
+  uint32_t* work_ctr;
+  uint32_t* sc_ticket;
+  uint32_t* run_ticket;
+  float* partials;
+  float* out;               // weights (SGD/Adagrad) or dense grad
+  float* mom;               // Adagrad state
+  uint32_t* status;
+  int64_t N;
+  int64_t row_stride;       // elements per grad_output row
+  int64_t slot_floats;      // floats per partial slot
+  int32_t info_bits;
+  int32_t B;
+  int32_t T;
+  int32_t nobag;
+  int32_t thr;
+  int32_t ch_base;
+  int32_t mode;
+  int32_t accumulate;
+  float lr;
+  float eps;
+};
+
+// ---------------------------------------------------------------- launchers (kernels.hip)
+
+hipError_t launch_init(void* header_and_hist, size_t bytes, hipStream_t s);
+hipError_t launch_linearize(const LinParams& p, int grid, hipStream_t s);
+hipError_t launch_sort_pass(const SortParams& p, int grid, hipStream_t s);
+hipError_t launch_rle(const RleParams& p, int grid, hipStream_t s);
+hipError_t launch_post(const PostParams& p, int grid, hipStream_t s);
+hipError_t launch_fill(const FillParams& p, int nblocks, hipStream_t s);
+hipError_t launch_reduce(const RedParams& p, const int64_t* num_long, bool bf16, int grid,
+                         hipStream_t s);
+int reduce_blocks_per_cu(bool bf16);
+
+}  // namespace sgb

@@ -1,0 +1,1077 @@
+// kernels.hip -- gfx950 kernels of the pooled embedding-bag backward.
+//
+// Pipeline (one HIP stream, no host synchronisation):
+//   k_init       zero the workspace header and digit histograms
+//   k_linearize  bags -> per-lookup packed word (linear id << info_bits | info)
+//                and coefficient; digit histograms of every sort pass
+//   k_sort_pass  one stable LSD radix pass (<= 9-bit digits), single sweep
+//                with decoupled look-back, LDS-staged scatter
+//   k_rle        run heads of the sorted ids -> unique ids, run starts, count
+//   k_post       run lengths, ascending long-run list with chunk prefix
+//   k_fill       zeros for untouched rows of a fresh dense gradient
+//   k_reduce     persistent wave64 workers: short runs (one lane group per
+//                run) and chunks of long runs (whole wave, partials combined
+//                in a fixed order by the last arriving wave), each row
+//                finished by the fused dense / SGD / row-wise Adagrad step
+//
+// Method: "fbgemm_gpu/codegen/embedding_backward_split_template.cu" (FBGEMM),
+// host entry `..._exact_cuda` (linearise, sort, run-length encode, long
+// segments, per-run reduction, dense store or optimizer row update) and
+// "tt_embeddings_cuda.cu" (FBTT-Embedding) for the SGD / row-wise Adagrad
+// formulas.  The kernels here are designed for wave64 CDNA4; see the notes at
+// each kernel for where they depart from the pages' CUDA design.
+#include "internal.h"
+
+namespace sgb {
+namespace {
+
+constexpr uint32_t kFlagA32 = 1u << 30;   // look-back word: aggregate only
+constexpr uint32_t kFlagP32 = 2u << 30;   // look-back word: inclusive prefix
+constexpr uint32_t kVal32 = (1u << 30) - 1;
+constexpr uint64_t kFlagA64 = 1ull << 62;
+constexpr uint64_t kFlagP64 = 2ull << 62;
+constexpr uint64_t kVal64 = (1ull << 62) - 1;
+constexpr uint64_t kField = (1ull << 31) - 1;  // two 31-bit fields in a 64-bit word
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ uint32_t bits_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ void set_status(uint32_t* st, uint32_t code) {
+  atomicCAS(st, 0u, code);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_incl_scan(T x) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    T y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+// Exclusive scan over the 256 threads of a block (one value each).  `tmp`
+// holds 4 values of LDS.  Contains two barriers.
+template <typename T>
+__device__ __forceinline__ T block_excl_scan(T x, T* tmp, T& total) {
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  const T inc = wave_incl_scan(x);
+  if (lane == 63) tmp[w] = inc;
+  __syncthreads();
+  T before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const T v = tmp[i];
+    if (i < w) before += v;
+    all += v;
+  }
+  __syncthreads();
+  total = all;
+  return before + inc - x;
+}
+
+// Decoupled look-back over scalar per-tile values for one whole wave
+// (Merrill & Garland, "Single-pass Parallel Prefix Scan with Decoupled
+// Look-back", 2016): publish this tile's aggregate, inspect the 64 preceding
+// tiles at once, sum back to the nearest inclusive prefix, publish ours.
+// Tile ids come from an atomic counter, so every tile waited on belongs to a
+// workgroup that started earlier and is resident; the wait is still bounded
+// and records kStInternal if it ever expires.
+template <typename W>
+struct LB;
+template <>
+struct LB<uint32_t> {
+  static constexpr uint32_t A = kFlagA32, P = kFlagP32, V = kVal32;
+  static constexpr int S = 30;
+};
+template <>
+struct LB<uint64_t> {
+  static constexpr uint64_t A = kFlagA64, P = kFlagP64, V = kVal64;
+  static constexpr int S = 62;
+};
+
+template <typename W>
+__device__ W wave_lookback(W* lb, uint32_t tile, W agg, uint32_t* status) {
+  const int lane = lane_id();
+  if (lane == 0)
+    __hip_atomic_store(&lb[tile], (tile == 0 ? LB<W>::P : LB<W>::A) | agg, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  W excl = 0;
+  if (tile == 0) return excl;
+  int64_t top = (int64_t)tile - 1;
+  uint32_t spins = 0;
+  for (;;) {
+    const int64_t idx = top - lane;
+    const W v = idx >= 0 ? __hip_atomic_load(&lb[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : LB<W>::P;  // before tile 0: prefix 0
+    const uint32_t flag = (uint32_t)(v >> LB<W>::S);
+    const uint64_t pref = __ballot(flag == 2);
+    const uint64_t notready = __ballot(flag == 0);
+    const int first = pref ? __builtin_ctzll(pref) : 64;
+    const uint64_t upto = first >= 64 ? ~0ull : ((2ull << first) - 1ull);
+    if (notready & upto) {
+      if (++spins > kSpinLimit) {
+        if (lane == 0) set_status(status, kStInternal);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+      continue;
+    }
+    excl += wave_sum<W>(lane <= first ? (v & LB<W>::V) : (W)0);
+    if (first < 64) break;
+    top -= 64;
+  }
+  if (lane == 0)
+    __hip_atomic_store(&lb[tile], LB<W>::P | (excl + agg), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  return excl;
+}
+
+// Adds 1 for this lane's digit to an LDS histogram, aggregated over the lanes
+// of the wave holding the same digit (ballot match), so a hot Zipf digit costs
+// one LDS atomic per wave instead of 64 conflicting ones.  Wave-uniform call.
+__device__ __forceinline__ void hist_add(uint32_t* h, uint32_t digit, int bits, bool valid) {
+  uint64_t peers = __ballot(valid);
+  for (int b = 0; b < bits; ++b) {
+    const bool bit = (digit >> b) & 1u;
+    const uint64_t m = __ballot(bit);
+    peers &= bit ? m : ~m;
+  }
+  if (valid && bits_below(peers) == 0) atomicAdd(&h[digit], (uint32_t)__popcll(peers));
+}
+
+// ------------------------------------------------------------------ k_init
+
+__global__ void k_init(uint4* p, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// ------------------------------------------------------------------ k_linearize
+//
+// Bag (t, b) covers lookups [offsets[t*B+b], offsets[t*B+b+1]) in table-major
+// order (FBGEMM `grad_mean_kernel`; FBTT `compute_rowidx_kernel` expands the
+// same layout per lookup).  Each workgroup takes kLinBags consecutive bags,
+// stages their offsets in LDS and maps every lookup of the range to its bag
+// by binary search in LDS, so reads of `indices` and writes of the packed
+// words are fully coalesced whatever the bag lengths.  The linear id is
+// hash_size_cumsum[t] + index; the info is the bag number t*B + b (nobag:
+// i*T + t); the coefficient folds the per-sample weight and the 1/L of MEAN
+// pooling into one fp32 (the page instead writes a scaled copy of the whole
+// grad_output in `grad_mean_kernel` and sorts the weights a second time).
+// Malformed offsets are clamped and made non-decreasing per tile so that no
+// access leaves the arrays; the error is recorded.
+
+__global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
+  __shared__ int64_t s_off[kLinBags + 1];
+  __shared__ int32_t s_t[kLinBags];
+  __shared__ float s_scale[kLinBags];
+  __shared__ uint32_t s_hist[kMaxPasses * kRadixMax];
+  __shared__ int s_bad;
+  const int tid = threadIdx.x;
+
+  for (int64_t q = blockIdx.x * (int64_t)kLinThreads + tid; q < p.zero_vec4;
+       q += (int64_t)gridDim.x * kLinThreads)
+    p.zero_begin[q] = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = tid; i < p.npasses * kRadixMax; i += kLinThreads) s_hist[i] = 0u;
+  __syncthreads();
+
+  auto histogram = [&](uint64_t key, bool valid) {
+    for (int ps = 0; ps < p.npasses; ++ps) {
+      const uint32_t d = (uint32_t)(key >> p.pass_shift[ps]) & ((1u << p.pass_bits[ps]) - 1u);
+      hist_add(s_hist + ps * kRadixMax, d, p.pass_bits[ps], valid);
+    }
+  };
+
+  if (p.offsets == nullptr) {
+    // nobag with a single table and no offsets: lookup i is token i of table 0
+    const int64_t E = p.hsc[1];
+    const int64_t tiles = (p.N + kLinLookups - 1) / kLinLookups;
+    for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+      for (int k = 0; k < kLinLookups / kLinThreads; ++k) {
+        const int64_t i = tile * kLinLookups + k * kLinThreads + tid;
+        const bool valid = i < p.N;
+        uint64_t key = 0;
+        if (valid) {
+          int64_t idx = p.indices[i];
+          if (idx < 0 || idx >= E) {
+            set_status(p.status, kStIndex);
+            idx = idx < 0 ? 0 : E - 1;
+          }
+          key = (uint64_t)idx;
+          p.kv_out[i] = (key << p.info_bits) | (uint64_t)i;
+        }
+        histogram(key, valid);
+      }
+    }
+  } else {
+    const int64_t nbags = (int64_t)p.B * p.T;
+    const int64_t tiles = (nbags + kLinBags - 1) / kLinBags;
+    for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+      const int64_t b0 = tile * kLinBags;
+      const int nb = (int)min((int64_t)kLinBags, nbags - b0);
+      if (tid == 0) s_bad = 0;
+      __syncthreads();
+      for (int j = tid; j <= nb; j += kLinThreads) {
+        const int64_t v = p.offsets[b0 + j];
+        const bool bad = v < 0 || v > p.N || (b0 + j == 0 && v != 0) ||
+                         (b0 + j == nbags && v != p.N);
+        if (bad) s_bad = 1;
+        s_off[j] = v < 0 ? 0 : (v > p.N ? p.N : v);
+      }
+      __syncthreads();
+      for (int j = tid + 1; j <= nb; j += kLinThreads)
+        if (s_off[j] < s_off[j - 1]) s_bad = 1;
+      __syncthreads();
+      if (s_bad) {
+        if (tid == 0) {
+          set_status(p.status, kStOffsets);
+          for (int j = 1; j <= nb; ++j)
+            if (s_off[j] < s_off[j - 1]) s_off[j] = s_off[j - 1];
+        }
+        __syncthreads();
+      }
+      for (int j = tid; j < nb; j += kLinThreads) {
+        const int64_t bg = b0 + j;
+        int t = (int)(bg / p.B);
+        s_t[j] = t < p.T ? t : p.T - 1;
+        const int64_t L = s_off[j + 1] - s_off[j];
+        s_scale[j] = (p.pooling == kPoolMean && L > 0) ? 1.0f / (float)L : 1.0f;
+      }
+      __syncthreads();
+      const int64_t i0 = s_off[0], i1 = s_off[nb];
+      for (int64_t c = i0; c < i1; c += kLinLookups) {
+        for (int k = 0; k < kLinLookups / kLinThreads; ++k) {
+          const int64_t i = c + k * kLinThreads + tid;
+          const bool valid = i < i1;
+          uint64_t key = 0;
+          if (valid) {
+            int lo = 0, hi = nb;  // s_off[lo] <= i < s_off[hi]
+            while (hi - lo > 1) {
+              const int mid = (lo + hi) >> 1;
+              if (s_off[mid] <= i)
+                lo = mid;
+              else
+                hi = mid;
+            }
+            const int t = s_t[lo];
+            const int64_t h0 = p.hsc[t], E = p.hsc[t + 1] - h0;
+            int64_t idx = p.indices[i];
+            if (idx < 0 || idx >= E) {
+              set_status(p.status, kStIndex);
+              idx = idx < 0 ? 0 : E - 1;
+            }
+            key = (uint64_t)(h0 + idx);
+            const uint64_t info = p.pooling == kPoolNone ? (uint64_t)i * (uint64_t)p.T + (uint64_t)t
+                                                         : (uint64_t)(b0 + lo);
+            p.kv_out[i] = (key << p.info_bits) | info;
+            if (p.coef_out) p.coef_out[i] = s_scale[lo] * (p.psw ? p.psw[i] : 1.0f);
+          }
+          histogram(key, valid);
+        }
+      }
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < p.npasses * kRadixMax; i += kLinThreads) {
+    const uint32_t v = s_hist[i];
+    if (v) atomicAdd(&p.hist[i], v);
+  }
+}
+
+// ------------------------------------------------------------------ k_sort_pass
+//
+// One stable LSD pass over `bits` (<= 9) digit bits at `shift` of the packed
+// word (Adinets & Merrill, "Onesweep", 2022: digit counts of every pass come
+// from one upfront histogram; each tile ranks locally, looks back per digit
+// for its global offset and scatters once).  Ranking uses wave64 ballot
+// multisplit (match of equal digits across the 64 lanes), with a per-wave
+// LDS counter per digit, so skewed keys never contend on one LDS word.
+// Items are loaded wave-striped, which makes (wave, item, lane) order equal
+// to input order and keeps the pass stable.  The tile is then reordered by
+// digit in LDS so the global writes of each digit are contiguous.
+
+__global__ __launch_bounds__(kSortThreads) void k_sort_pass(SortParams p) {
+  __shared__ uint64_t s_kv[kSortTile];
+  __shared__ float s_coef[kSortTile];
+  __shared__ uint32_t s_wcnt[kSortThreads / 64][kRadixMax];
+  __shared__ uint32_t s_local[kRadixMax];
+  __shared__ int32_t s_gbase[kRadixMax];
+  __shared__ uint32_t s_dglob[kRadixMax];
+  __shared__ uint32_t s_tmp[4];
+  __shared__ uint32_t s_tile;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int radix = 1 << p.bits;
+  const uint64_t dmask = (uint64_t)(radix - 1);
+  const bool has_coef = p.coef_in != nullptr;
+  if (tid == 0) s_tile = __hip_atomic_fetch_add(p.tile_ctr, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+  // exclusive prefix of the global digit counts (two digits per thread)
+  {
+    const int d0 = 2 * tid;
+    const uint32_t a = d0 < radix ? p.hist[d0] : 0u;
+    const uint32_t b = d0 + 1 < radix ? p.hist[d0 + 1] : 0u;
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan<uint32_t>(a + b, s_tmp, tot);
+    if (d0 < radix) s_dglob[d0] = ex;
+    if (d0 + 1 < radix) s_dglob[d0 + 1] = ex + a;
+  }
+  for (int d = lane; d < radix; d += 64) s_wcnt[w][d] = 0u;
+  __syncthreads();
+  const uint32_t tile = s_tile;
+  const int64_t base = (int64_t)tile * kSortTile;
+  const int tile_n = (int)min((int64_t)kSortTile, p.N - base);
+
+  uint64_t kv[kSortItems];
+  float cf[kSortItems];
+  uint32_t rank[kSortItems];
+#pragma unroll
+  for (int k = 0; k < kSortItems; ++k) {
+    const int e = w * 64 * kSortItems + k * 64 + lane;
+    const bool valid = e < tile_n;
+    kv[k] = valid ? p.kv_in[base + e] : 0ull;
+    cf[k] = (valid && has_coef) ? p.coef_in[base + e] : 0.0f;
+  }
+#pragma unroll
+  for (int k = 0; k < kSortItems; ++k) {
+    const int e = w * 64 * kSortItems + k * 64 + lane;
+    const bool valid = e < tile_n;
+    const uint32_t d = (uint32_t)((kv[k] >> p.shift) & dmask);
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < p.bits; ++b) {
+      const bool bit = (d >> b) & 1u;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const uint32_t below = bits_below(peers);
+    const uint32_t before = valid ? s_wcnt[w][d] : 0u;
+    rank[k] = before + below;
+    if (valid && below == 0) s_wcnt[w][d] = before + (uint32_t)__popcll(peers);
+  }
+  __syncthreads();
+
+  // per digit: exclusive offsets of the waves, tile count, published early
+  uint32_t cnt[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int d = 2 * tid + h;
+    uint32_t acc = 0;
+    if (d < radix) {
+#pragma unroll
+      for (int ww = 0; ww < kSortThreads / 64; ++ww) {
+        const uint32_t c = s_wcnt[ww][d];
+        s_wcnt[ww][d] = acc;
+        acc += c;
+      }
+      __hip_atomic_store(&p.lookback[(size_t)tile * kRadixMax + d],
+                         (tile == 0 ? kFlagP32 : kFlagA32) | acc, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+    cnt[h] = acc;
+  }
+  {
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan<uint32_t>(cnt[0] + cnt[1], s_tmp, tot);
+    if (2 * tid < radix) s_local[2 * tid] = ex;
+    if (2 * tid + 1 < radix) s_local[2 * tid + 1] = ex + cnt[0];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kSortItems; ++k) {
+    const int e = w * 64 * kSortItems + k * 64 + lane;
+    if (e < tile_n) {
+      const uint32_t d = (uint32_t)((kv[k] >> p.shift) & dmask);
+      const uint32_t pos = s_local[d] + s_wcnt[w][d] + rank[k];
+      s_kv[pos] = kv[k];
+      if (has_coef) s_coef[pos] = cf[k];
+    }
+  }
+  // per digit look-back for the offset of this tile's digit group
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int d = 2 * tid + h;
+    if (d >= radix) continue;
+    uint32_t excl = 0;
+    if (tile > 0) {
+      int64_t j = (int64_t)tile - 1;
+      uint32_t spins = 0;
+      while (j >= 0) {
+        const uint32_t v = __hip_atomic_load(&p.lookback[(size_t)j * kRadixMax + d],
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t flag = v >> 30;
+        if (flag == 0) {
+          if (++spins > kSpinLimit) {
+            set_status(p.status, kStInternal);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+          continue;
+        }
+        excl += v & kVal32;
+        if (flag == 2) break;
+        --j;
+      }
+      __hip_atomic_store(&p.lookback[(size_t)tile * kRadixMax + d], kFlagP32 | (excl + cnt[h]),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    s_gbase[d] = (int32_t)(s_dglob[d] + excl) - (int32_t)s_local[d];
+  }
+  __syncthreads();
+  for (int q = tid; q < tile_n; q += kSortThreads) {
+    const uint64_t v = s_kv[q];
+    const uint32_t d = (uint32_t)((v >> p.shift) & dmask);
+    const int64_t pos = (int64_t)s_gbase[d] + q;
+    if (pos >= 0 && pos < p.N) {
+      p.kv_out[pos] = v;
+      if (has_coef) p.coef_out[pos] = s_coef[q];
+    } else {
+      set_status(p.status, kStInternal);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ k_rle
+//
+// Run-length encoding of the sorted ids: position i starts a run when its id
+// differs from position i-1.  Heads are counted per tile, the tile's run
+// offset comes from a wave-wide look-back, and each head writes its unique id
+// and its start (the exclusive scan of run lengths, FBGEMM
+// `sorted_linear_indices_cumulative_run_lengths`).  The last tile writes the
+// run count and the closing start N.
+
+__global__ __launch_bounds__(kScanThreads) void k_rle(RleParams p) {
+  __shared__ uint64_t s_key[kScanTile + 1];
+  __shared__ uint32_t s_tmp[4];
+  __shared__ uint32_t s_tile, s_excl;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_tile = __hip_atomic_fetch_add(p.tile_ctr, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const uint32_t tile = s_tile;
+  const int64_t base = (int64_t)tile * kScanTile;
+  const int n = (int)min((int64_t)kScanTile, p.N - base);
+  for (int q = tid; q < n; q += kScanThreads) s_key[q + 1] = p.kv[base + q] >> p.info_bits;
+  if (tid == 0) s_key[0] = base > 0 ? (p.kv[base - 1] >> p.info_bits) : ~0ull;
+  __syncthreads();
+  uint32_t heads = 0, cnt = 0;
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) {
+    const int q = tid * kScanItems + k;
+    if (q < n && (base + q == 0 || s_key[q + 1] != s_key[q])) {
+      heads |= 1u << k;
+      ++cnt;
+    }
+  }
+  uint32_t total;
+  const uint32_t before = block_excl_scan<uint32_t>(cnt, s_tmp, total);
+  if (tid < 64) {
+    const uint32_t ex = wave_lookback<uint32_t>(p.lookback, tile, total, p.status);
+    if (tid == 0) s_excl = ex;
+  }
+  __syncthreads();
+  uint32_t run = s_excl + before;
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) {
+    if (heads & (1u << k)) {
+      const int q = tid * kScanItems + k;
+      p.unique_ids[run] = (int64_t)s_key[q + 1];
+      p.cum[run] = (int32_t)(base + q);
+      ++run;
+    }
+  }
+  if (tid == 0 && base + n == p.N) {
+    const uint32_t U = s_excl + total;
+    p.cum[U] = (int32_t)p.N;
+    *p.num_runs = (int32_t)U;
+  }
+}
+
+// ------------------------------------------------------------------ k_post
+//
+// Run lengths, and the long runs -- length >= thr, FBGEMM `find_long_segments`
+// -- compacted in ascending run order (the page appends them through an
+// atomic counter in arbitrary order).  Each long run is cut into chunks of
+// chunk_len() lookups; a combined scan gives every long run its first chunk
+// number.  Also clears the combine tickets of those chunks and, for a fresh
+// dense gradient, marks touched rows in a bitmap.
+
+__device__ __forceinline__ int chunk_len(int len, int ch_base) {
+  const int c = (len + kMaxChunks - 1) / kMaxChunks;
+  return c > ch_base ? c : ch_base;
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_post(PostParams p) {
+  __shared__ uint64_t s_tmp[4];
+  __shared__ uint32_t s_tile;
+  __shared__ uint64_t s_excl;
+  const int tid = threadIdx.x;
+  const int U = *p.num_runs;
+  if (tid == 0) s_tile = __hip_atomic_fetch_add(p.tile_ctr, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const uint32_t tile = s_tile;
+  const int64_t base = (int64_t)tile * kScanTile;
+  if (base >= U) return;
+  const int n = (int)min((int64_t)kScanTile, (int64_t)U - base);
+  int len[kScanItems];
+  uint64_t sum = 0;
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) {
+    const int q = tid * kScanItems + k;
+    len[k] = 0;
+    if (q < n) {
+      const int64_t r = base + q;
+      len[k] = p.cum[r + 1] - p.cum[r];
+      p.run_lengths[r] = len[k];
+      if (len[k] >= p.thr) {
+        const int cl = chunk_len(len[k], p.ch_base);
+        sum += (1ull << 31) | (uint64_t)((len[k] + cl - 1) / cl);
+      }
+      if (p.bitmap) {
+        const uint64_t key = (uint64_t)p.unique_ids[r];
+        if (key < (uint64_t)p.total_rows) atomicOr(&p.bitmap[key >> 5], 1u << (key & 31));
+      }
+    }
+  }
+  uint64_t total;
+  const uint64_t before = block_excl_scan<uint64_t>(sum, s_tmp, total);
+  if (tid < 64) {
+    const uint64_t ex = wave_lookback<uint64_t>(p.lookback, tile, total, p.status);
+    if (tid == 0) s_excl = ex;
+  }
+  __syncthreads();
+  uint64_t at = s_excl + before;
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) {
+    const int q = tid * kScanItems + k;
+    if (q < n && len[k] >= p.thr) {
+      const uint32_t pos = (uint32_t)(at >> 31);
+      const uint32_t c0 = (uint32_t)(at & kField);
+      const int cl = chunk_len(len[k], p.ch_base);
+      const int nch = (len[k] + cl - 1) / cl;
+      p.long_ids[pos] = (int32_t)(base + q);
+      p.chunk_begin[pos] = c0;
+      p.run_ticket[pos] = 0u;
+      for (int s = 0; s < nch; s += kSuperChunk) p.sc_ticket[c0 + s] = 0u;
+      at += (1ull << 31) | (uint64_t)nch;
+    }
+  }
+  if (tid == 0 && base + n == U) {
+    const uint64_t all = s_excl + total;
+    const uint32_t nl = (uint32_t)(all >> 31);
+    *p.num_long = nl;
+    *p.total_items = (uint32_t)(all & kField);
+    p.chunk_begin[nl] = (uint32_t)(all & kField);
+  }
+}
+
+// ------------------------------------------------------------------ k_fill
+//
+// A fresh dense gradient is zero except on touched rows (FBGEMM host entry
+// starts from zeros_like(dev_weights)); rows marked in the bitmap are skipped
+// here because the reducer writes them, so every element is written once.
+
+__global__ __launch_bounds__(256) void k_fill(FillParams p) {
+  const FillBlock fb = p.blocks[blockIdx.x];
+  const int D = p.doff[fb.t + 1] - p.doff[fb.t];
+  const uint32_t d4 = (uint32_t)(D >> 2);
+  float4* out = reinterpret_cast<float4*>(p.out + p.woff[fb.t] + fb.row0 * (int64_t)D);
+  const int64_t lin0 = p.hsc[fb.t] + fb.row0;
+  const uint32_t total = (uint32_t)fb.nrows * d4;
+  // q / d4 by multiply-shift (Granlund & Montgomery), exact for q < 2^31
+  uint32_t s = 0;
+  while ((1u << s) < d4) ++s;
+  const uint64_t magic = ((1ull << (32 + s)) + d4 - 1) / d4;
+  for (uint32_t q = threadIdx.x; q < total; q += blockDim.x) {
+    const uint32_t row = (uint32_t)(((uint64_t)q * magic) >> (32 + s));
+    const int64_t lin = lin0 + row;
+    if (p.bitmap && ((p.bitmap[lin >> 5] >> (lin & 31)) & 1u)) continue;
+    out[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+// ------------------------------------------------------------------ k_reduce
+//
+// G_r[d] = sum over the lookups j of run r of coef_j * grad_output[row_j][col_t + d]
+// (FBGEMM warp-per-row / cta-per-row kernels), then the row is written once.
+//
+// Work items, fetched from one atomic queue by each wave (largest first):
+//  * chunks of long runs: the whole wave reads one chunk; for D < 256 the
+//    wave's lanes form 64/LPL groups of LPL lanes (4 columns per lane) that
+//    take interleaved lookups, and the groups are folded by a fixed xor tree.
+//    A run of several chunks writes one fp32 partial per chunk; the last
+//    wave of each group of kSuperChunk chunks (atomic ticket after a release
+//    fence) adds them in chunk order, and the last group adds the group sums
+//    in order and finishes the row -- a deterministic, atomic-free reduction
+//    across many workgroups (the page keeps a long run inside one block).
+//  * units of 64 consecutive runs: the short runs among them are served by
+//    lane groups, one run per group, so a wave carries 64/LPL rows at once.
+// Per-lookup metadata (packed word, coefficient) is read coalesced by the
+// group and broadcast lane to lane (readlane when the group is the wave).
+
+__device__ __forceinline__ int lpl_for(int D) {
+  const int need = (D + 3) >> 2;
+  int l = 4;
+  while (l < need && l < 64) l <<= 1;
+  return l;
+}
+
+template <int LPL>
+__device__ __forceinline__ int bcast_i(int v, int src) {
+  if constexpr (LPL == 64)
+    return __builtin_amdgcn_readlane(v, src);
+  else
+    return __shfl(v, src, 64);
+}
+
+template <int LPL>
+__device__ __forceinline__ float bcast_f(float v, int src) {
+  return __int_as_float(bcast_i<LPL>(__float_as_int(v), src));
+}
+
+template <bool BF16>
+__device__ __forceinline__ float4 load4(const void* base, int64_t elem) {
+  if constexpr (BF16) {
+    const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + elem);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+  } else {
+    return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + elem);
+  }
+}
+
+__device__ __forceinline__ int table_of(const RedParams& p, uint32_t info0) {
+  const int t = p.nobag ? (int)(info0 % (uint32_t)p.T) : (int)(info0 / (uint32_t)p.B);
+  return t < p.T ? t : p.T - 1;
+}
+
+// Row of grad_output that a lookup of table t reads.
+__device__ __forceinline__ int grad_row_of(const RedParams& p, uint32_t info, int t) {
+  if (p.nobag) {
+    const int64_t l = info / (uint32_t)p.T;
+    return (int)(l < p.N ? l : p.N - 1);
+  }
+  const int64_t b = (int64_t)info - (int64_t)t * p.B;
+  return (int)(b < 0 ? 0 : (b < p.B ? b : p.B - 1));
+}
+
+struct RowDst {
+  float* out;  // first element of the output row
+  float* mom;  // its Adagrad state
+};
+
+__device__ __forceinline__ RowDst row_dest(const RedParams& p, int t, int D, int64_t lin) {
+  const int64_t h0 = p.hsc[t], E = p.hsc[t + 1] - h0;
+  int64_t row = lin - h0;
+  row = row < 0 ? 0 : (row < E ? row : E - 1);
+  RowDst d;
+  d.out = p.out + p.woff[t] + row * (int64_t)D;
+  d.mom = p.mom ? p.mom + h0 + row : nullptr;
+  return d;
+}
+
+// Sum over lookups j = first, first+step, ... < last of coef_j * grad row_j
+// at elements [colofs, colofs+4).  first/last/step are uniform within each
+// group of LPL lanes; the wave must be converged at the call.
+template <int LPL, bool BF16>
+__device__ __forceinline__ float4 gather_sum(const RedParams& p, int first, int last, int step, int t,
+                             int64_t colofs, bool col_ok) {
+  constexpr int UNR = 8;
+  const int lane = lane_id();
+  const int gb = lane & ~(LPL - 1), lig = lane & (LPL - 1);
+  const uint64_t imask = p.info_bits >= 64 ? ~0ull : ((1ull << p.info_bits) - 1ull);
+  const bool has_coef = p.coef != nullptr;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j0 = first; j0 < last; j0 += LPL * step) {
+    const int jm = j0 + lig * step;
+    int rowi = 0;
+    float cf = 0.f;
+    if (jm < last) {
+      rowi = grad_row_of(p, (uint32_t)(p.kv[jm] & imask), t);
+      cf = has_coef ? p.coef[jm] : 1.0f;
+    }
+    const int cnt = min(LPL, (last - j0 + step - 1) / step);
+    for (int jj = 0; jj < cnt; jj += UNR) {
+      float4 v[UNR];
+      float c[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int src = (LPL == 64 ? 0 : gb) + min(jj + u, LPL - 1);
+        const int ro = bcast_i<LPL>(rowi, src);
+        c[u] = bcast_f<LPL>(cf, src);
+        const bool ok = (jj + u < cnt) && col_ok;
+        v[u] = ok ? load4<BF16>(p.grad, (int64_t)ro * p.row_stride + colofs)
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
+        if (jj + u >= cnt) c[u] = 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        acc.x = fmaf(c[u], v[u].x, acc.x);
+        acc.y = fmaf(c[u], v[u].y, acc.y);
+        acc.z = fmaf(c[u], v[u].z, acc.z);
+        acc.w = fmaf(c[u], v[u].w, acc.w);
+      }
+    }
+  }
+  return acc;
+}
+
+// Adds the 64/LPL lane groups of a wave (fixed xor tree; all groups get the sum).
+template <int LPL>
+__device__ __forceinline__ float4 fold_groups(float4 a) {
+#pragma unroll
+  for (int off = 32; off >= LPL; off >>= 1) {
+    a.x += __shfl_xor(a.x, off, 64);
+    a.y += __shfl_xor(a.y, off, 64);
+    a.z += __shfl_xor(a.z, off, 64);
+    a.w += __shfl_xor(a.w, off, 64);
+  }
+  return a;
+}
+
+// Sum over the LPL lanes of a group (fixed xor tree).
+template <int LPL>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int off = LPL / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+// Finishes one row whose gradient for column block cb is getG(cb) (this
+// lane's 4 columns).  getG is called by the whole wave.  The Adagrad state
+// grows by the mean square of the row gradient, then the step uses the grown
+// state with eps outside the root (FBTT `cache_backward_rowwise_adagrad_
+// approx_kernel`), here once per distinct row.  SGD: w -= lr * G (FBTT
+// `cache_backward_sgd_kernel`).  Dense: store, or add for an accumulating
+// grad_weight (tinygrad `_embedding_bwd_kernel`).
+template <int LPL, class F>
+__device__ __forceinline__ void finish_row(const RedParams& p, const RowDst& dst, int D, bool write,
+                                           F&& getG) {
+  const int lig = lane_id() & (LPL - 1);
+  const int ncb = LPL == 64 ? (D + kColBlock - 1) / kColBlock : 1;
+  if (p.mode == kModeAdagrad) {
+    // Column block 0 stays in registers; wider rows (D > 256) get their
+    // remaining blocks recomputed after the row's mean square is known.
+    const float4 g0 = getG(0);
+    float ss = 0.f;
+    if (4 * lig < D) ss = g0.x * g0.x + g0.y * g0.y + g0.z * g0.z + g0.w * g0.w;
+#pragma unroll 1
+    for (int cb = 1; cb < ncb; ++cb) {
+      const float4 g = getG(cb);
+      if (cb * kColBlock + 4 * lig < D) ss += g.x * g.x + g.y * g.y + g.z * g.z + g.w * g.w;
+    }
+    ss = group_sum<LPL>(ss);
+    float m = 0.f, mult = 0.f;
+    if (write) {
+      m = *dst.mom + ss / (float)D;
+      mult = p.lr / (sqrtf(m) + p.eps);
+    }
+#pragma unroll 1
+    for (int cb = 0; cb < ncb; ++cb) {
+      const float4 g = cb == 0 ? g0 : getG(cb);
+      const int col = cb * kColBlock + 4 * lig;
+      if (write && col < D) {
+        float4* o = reinterpret_cast<float4*>(dst.out + col);
+        float4 wv = *o;
+        wv.x -= mult * g.x;
+        wv.y -= mult * g.y;
+        wv.z -= mult * g.z;
+        wv.w -= mult * g.w;
+        *o = wv;
+      }
+    }
+    if (write && lig == 0) *dst.mom = m;
+    return;
+  }
+#pragma unroll 1
+  for (int cb = 0; cb < ncb; ++cb) {
+    const float4 g = getG(cb);
+    const int col = cb * kColBlock + 4 * lig;
+    if (!write || col >= D) continue;
+    float4* o = reinterpret_cast<float4*>(dst.out + col);
+    if (p.mode == kModeSgd) {
+      float4 wv = *o;
+      wv.x -= p.lr * g.x;
+      wv.y -= p.lr * g.y;
+      wv.z -= p.lr * g.z;
+      wv.w -= p.lr * g.w;
+      *o = wv;
+    } else if (p.accumulate) {
+      float4 wv = *o;
+      wv.x += g.x;
+      wv.y += g.y;
+      wv.z += g.z;
+      wv.w += g.w;
+      *o = wv;
+    } else {
+      *o = g;
+    }
+  }
+}
+
+// Last-arrival ticket: publishes this wave's prior global writes (release),
+// counts the arrival, and reports whether this wave completes the group; if
+// so its later reads see every member's writes (acquire).
+__device__ __forceinline__ bool ticket_last(uint32_t* ctr, uint32_t members) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  uint32_t old = 0;
+  if (lane_id() == 0)
+    old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = __shfl(old, 0, 64);
+  if (old + 1 != members) return false;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return true;
+}
+
+// Sum of `count` partial slots first, first+stride, ... (column block cb),
+// groups interleaved, folded in a fixed order.
+template <int LPL>
+__device__ __forceinline__ float4 sum_slots(const float* slot0, int64_t slot_floats, int first,
+                                            int count, int stride, int cb, int D) {
+  constexpr int G = 64 / LPL;
+  const int lane = lane_id(), g = lane / LPL, lig = lane & (LPL - 1);
+  const int col = cb * kColBlock + 4 * lig;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (col < D) {
+    for (int i = g; i < count; i += G) {
+      const float4 v = *reinterpret_cast<const float4*>(
+          slot0 + (int64_t)(first + i * stride) * slot_floats + col);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+  }
+  return fold_groups<LPL>(acc);
+}
+
+template <int LPL, bool BF16>
+__device__ __forceinline__ void long_item(const RedParams& p, int k, int c, int r, int start, int len, int t,
+                          int D) {
+  constexpr int G = 64 / LPL;
+  const int lane = lane_id(), g = lane / LPL, lig = lane & (LPL - 1);
+  const int chl = chunk_len(len, p.ch_base);
+  const int nch = (len + chl - 1) / chl;
+  const int lo = start + c * chl;
+  const int hi = min(lo + chl, start + len);
+  const int ncb = LPL == 64 ? (D + kColBlock - 1) / kColBlock : 1;
+  const int64_t gcol = p.nobag ? 0 : p.doff[t];
+  const RowDst dst = row_dest(p, t, D, p.unique_ids[r]);
+  auto chunkG = [&](int cb) {
+    const int col = cb * kColBlock + 4 * lig;
+    const float4 a = gather_sum<LPL, BF16>(p, lo + g, hi, G, t, gcol + col, col < D);
+    return fold_groups<LPL>(a);
+  };
+  if (nch == 1) {
+    finish_row<LPL>(p, dst, D, g == 0, chunkG);
+    return;
+  }
+  const uint32_t cbeg = p.chunk_begin[k];
+  float* slot0 = p.partials + (int64_t)cbeg * p.slot_floats;
+#pragma unroll 1
+  for (int cb = 0; cb < ncb; ++cb) {
+    const float4 a = chunkG(cb);
+    const int col = cb * kColBlock + 4 * lig;
+    if (g == 0 && col < D)
+      *reinterpret_cast<float4*>(slot0 + (int64_t)c * p.slot_floats + col) = a;
+  }
+  const int m0 = (c / kSuperChunk) * kSuperChunk;
+  const int members = min(kSuperChunk, nch - m0);
+  if (!ticket_last(p.sc_ticket + cbeg + m0, (uint32_t)members)) return;
+  const int nsc = (nch + kSuperChunk - 1) / kSuperChunk;
+  if (nsc == 1) {
+    finish_row<LPL>(p, dst, D, g == 0, [&](int cb) {
+      return sum_slots<LPL>(slot0, p.slot_floats, 0, nch, 1, cb, D);
+    });
+    return;
+  }
+#pragma unroll 1
+  for (int cb = 0; cb < ncb; ++cb) {
+    const float4 a = sum_slots<LPL>(slot0, p.slot_floats, m0, members, 1, cb, D);
+    const int col = cb * kColBlock + 4 * lig;
+    if (g == 0 && col < D)
+      *reinterpret_cast<float4*>(slot0 + (int64_t)m0 * p.slot_floats + col) = a;
+  }
+  if (!ticket_last(p.run_ticket + k, (uint32_t)nsc)) return;
+  finish_row<LPL>(p, dst, D, g == 0, [&](int cb) {
+    return sum_slots<LPL>(slot0, p.slot_floats, 0, nsc, kSuperChunk, cb, D);
+  });
+}
+
+template <int LPL, bool BF16>
+__device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, int r, int start, int len, int t,
+                            int D) {
+  const int lane = lane_id(), g = lane / LPL, lig = lane & (LPL - 1);
+  uint64_t m = sel;
+  for (int i = 0; i < g; ++i) m &= m - 1;
+  const bool active = m != 0;
+  const int src = active ? __builtin_ctzll(m) : 0;
+  const int s = __shfl(start, src, 64);
+  const int n = active ? __shfl(len, src, 64) : 0;
+  const int rr = __shfl(r, src, 64);
+  RowDst dst{nullptr, nullptr};
+  if (active) dst = row_dest(p, t, D, p.unique_ids[rr]);
+  const int64_t gcol = p.nobag ? 0 : p.doff[t];
+  finish_row<LPL>(p, dst, D, active, [&](int cb) {
+    const int col = cb * kColBlock + 4 * lig;
+    return gather_sum<LPL, BF16>(p, s, s + n, 1, t, gcol + col, col < D);
+  });
+}
+
+template <bool BF16>
+__device__ __forceinline__ void do_long(const RedParams& p, uint32_t w, int nlong) {
+  int lo = 0, hi = nlong;  // chunk_begin[lo] <= w < chunk_begin[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.chunk_begin[mid] <= w)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  const int k = __builtin_amdgcn_readfirstlane(lo);
+  const int c = (int)(w - p.chunk_begin[k]);
+  const int r = p.long_ids[k];
+  const int start = p.cum[r], len = p.cum[r + 1] - start;
+  const uint64_t imask = p.info_bits >= 64 ? ~0ull : ((1ull << p.info_bits) - 1ull);
+  const int t = table_of(p, (uint32_t)(p.kv[start] & imask));
+  const int D = p.doff[t + 1] - p.doff[t];
+  switch (lpl_for(D)) {
+    case 4: long_item<4, BF16>(p, k, c, r, start, len, t, D); break;
+    case 8: long_item<8, BF16>(p, k, c, r, start, len, t, D); break;
+    case 16: long_item<16, BF16>(p, k, c, r, start, len, t, D); break;
+    case 32: long_item<32, BF16>(p, k, c, r, start, len, t, D); break;
+    default: long_item<64, BF16>(p, k, c, r, start, len, t, D); break;
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void do_short(const RedParams& p, uint32_t u, int U) {
+  const int lane = lane_id();
+  const int r = (int)u * 64 + lane;
+  int start = 0, len = 0, t = 0;
+  bool todo = false;
+  if (r < U) {
+    start = p.cum[r];
+    len = p.cum[r + 1] - start;
+    todo = len < p.thr;
+  }
+  if (todo) {
+    const uint64_t imask = p.info_bits >= 64 ? ~0ull : ((1ull << p.info_bits) - 1ull);
+    t = table_of(p, (uint32_t)(p.kv[start] & imask));
+  }
+  uint64_t pending = __ballot(todo);
+  while (pending) {
+    const int lead = __builtin_ctzll(pending);
+    const int t0 = __builtin_amdgcn_readfirstlane(__shfl(t, lead, 64));
+    const uint64_t same = __ballot(todo && t == t0) & pending;
+    const int D = p.doff[t0 + 1] - p.doff[t0];
+    const int lpl = lpl_for(D);
+    uint64_t sel = 0, rest = same;
+    for (int i = 0; i < 64 / lpl && rest; ++i) {
+      const uint64_t low = rest & (~rest + 1ull);
+      sel |= low;
+      rest ^= low;
+    }
+    pending &= ~sel;
+    switch (lpl) {
+      case 4: short_batch<4, BF16>(p, sel, r, start, len, t0, D); break;
+      case 8: short_batch<8, BF16>(p, sel, r, start, len, t0, D); break;
+      case 16: short_batch<16, BF16>(p, sel, r, start, len, t0, D); break;
+      case 32: short_batch<32, BF16>(p, sel, r, start, len, t0, D); break;
+      default: short_batch<64, BF16>(p, sel, r, start, len, t0, D); break;
+    }
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_reduce(RedParams p, const int64_t* num_long) {
+  const int lane = lane_id();
+  const int U = *p.num_runs;
+  const uint32_t n_items = *p.total_items;
+  const int nlong = (int)*num_long;
+  const uint32_t n_units = (uint32_t)((U + 63) / 64);
+  const uint32_t total = n_items + n_units;
+  for (;;) {
+    uint32_t w = 0;
+    if (lane == 0)
+      w = __hip_atomic_fetch_add(p.work_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    w = __builtin_amdgcn_readfirstlane(__shfl(w, 0, 64));
+    if (w >= total) break;
+    if (w < n_items)
+      do_long<BF16>(p, w, nlong);
+    else
+      do_short<BF16>(p, w - n_items, U);
+  }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ launchers
+
+hipError_t launch_init(void* p, size_t bytes, hipStream_t s) {
+  const int64_t n = (int64_t)(bytes / 16);
+  const int64_t want = (n + 255) / 256;
+  const int grid = (int)(want < 1024 ? want : 1024);
+  hipLaunchKernelGGL(k_init, dim3(grid > 0 ? grid : 1), dim3(256), 0, s,
+                     reinterpret_cast<uint4*>(p), n);
+  return hipGetLastError();
+}
+
+hipError_t launch_linearize(const LinParams& p, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(k_linearize, dim3(grid), dim3(kLinThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_sort_pass(const SortParams& p, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(k_sort_pass, dim3(grid), dim3(kSortThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_rle(const RleParams& p, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(k_rle, dim3(grid), dim3(kScanThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_post(const PostParams& p, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(k_post, dim3(grid), dim3(kScanThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill(const FillParams& p, int nblocks, hipStream_t s) {
+  hipLaunchKernelGGL(k_fill, dim3(nblocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce(const RedParams& p, const int64_t* num_long, bool bf16, int grid,
+                         hipStream_t s) {
+  if (bf16)
+    hipLaunchKernelGGL(k_reduce<true>, dim3(grid), dim3(256), 0, s, p, num_long);
+  else
+    hipLaunchKernelGGL(k_reduce<false>, dim3(grid), dim3(256), 0, s, p, num_long);
+  return hipGetLastError();
+}
+
+int reduce_blocks_per_cu(bool bf16) {
+  int n = 0;
+  hipError_t e = bf16 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_reduce<true>, 256, 0)
+                      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_reduce<false>, 256, 0);
+  return (e == hipSuccess && n > 0) ? n : 2;
+}
+
+}  // namespace sgb

@@ -1,0 +1,271 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+fp32 results: |gpu - oracle| <= 1e-4 + 1e-5 |oracle| per element; integer
+run structure (sorted ids and infos, unique ids, run lengths, starts, long
+runs): bit-exact; untouched rows: bit-unchanged (zero for a fresh dense grad).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from harness import assert_close, check_case, check_runs, initial_buffers, run_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sgb():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_gradient_backward_amd as m
+    return m
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def small_spec(cfg, **kw):
+    """A configuration's shape and distributions at a size the oracle finishes quickly."""
+    return synth.spec(cfg, **kw)
+
+
+# configuration-shaped cases at reduced size (several tiles + ragged tails)
+CASES = {
+    "c1": (1, dict()),
+    "c2": (2, dict(T=3, E=(20000,) * 3, B=700)),
+    "c3": (3, dict(T=6, E=(30000,) * 6, B=900)),
+    "c4": (4, dict(E=(9000,), D=(512,), nobag_tokens=6000)),
+    "c5": (5, dict(E=(200000,), B=1500)),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_config_shaped(sgb, name):
+    cfg, kw = CASES[name]
+    s = small_spec(cfg, **kw)
+    inp = synth.generate(s)
+    _say(f"[parity] {name} N={inp.N} T={inp.T} B={inp.B} mode={s.mode}")
+    check_case(sgb, inp, s.mode, s.thr, accumulate=s.accumulate, lr=s.lr or 0.01,
+               eps=s.eps or 1e-8)
+
+
+@pytest.mark.parametrize("thr", [1, 2, 63, 64, 65, 2**31 - 1])
+def test_thresholds(sgb, thr):
+    s = synth.Spec("thr", 2, (300, 50), (64, 16), 40, ("uniform", 0, 70), ("zipf", 1.5), "sum",
+                   True, "f32", "rowwise_adagrad", lr=0.05, eps=1e-6, seed=500 + thr % 97)
+    inp = synth.generate(s)
+    _say(f"[parity] thr={thr} N={inp.N}")
+    check_case(sgb, inp, "rowwise_adagrad", thr, lr=0.05, eps=1e-6)
+
+
+SWEEP = []
+for T in (1, 3):
+    for B in (1, 7, 64):
+        for pooling, weighted in (("sum", False), ("sum", True), ("mean", False), ("mean", True)):
+            for mode in ("dense", "sgd", "rowwise_adagrad"):
+                SWEEP.append((T, B, pooling, weighted, mode))
+
+
+@pytest.mark.parametrize("T,B,pooling,weighted,mode", SWEEP)
+def test_sweep(sgb, T, B, pooling, weighted, mode):
+    Ds = (4, 12, 64, 132, 256)
+    D = tuple(Ds[(t + B + (3 if weighted else 0)) % len(Ds)] for t in range(T))
+    E = tuple(5 + 37 * (t + 1) for t in range(T))
+    seed = hash((T, B, pooling, weighted, mode)) % 100000
+    s = synth.Spec("sweep", T, E, D, B, ("uniform", 0, 70), ("zipf", 1.1), pooling, weighted,
+                   "f32", mode, seed=seed)
+    inp = synth.generate(s)
+    acc = mode == "dense" and B % 2 == 1
+    check_case(sgb, inp, mode, 16, accumulate=acc, lr=0.03, eps=1e-7)
+
+
+@pytest.mark.parametrize("grad_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [4, 64, 256, 1024, 4096])
+def test_nobag(sgb, grad_dtype, D):
+    s = synth.Spec("nobag", 1, (3000,), (D,), 0, ("fixed", 1), ("zipf", 1.1), "none", False,
+                   grad_dtype, "dense", accumulate=True, nobag_tokens=2500, seed=D)
+    inp = synth.generate(s)
+    check_case(sgb, inp, "dense", 128, accumulate=True)
+
+
+def test_nobag_multi_table_offsets(sgb):
+    s = synth.Spec("nobag2", 3, (500, 70, 900), (32, 32, 32), 50, ("uniform", 0, 9),
+                   ("uniform",), "none", False, "bf16", "dense", seed=31)
+    inp = synth.generate(s, with_grad=False)
+    inp.grad_output = synth.bf16_bits(
+        inp.rngs["grad_output"].standard_normal((inp.N, 32), dtype=np.float32))
+    check_case(sgb, inp, "dense", 8, accumulate=False)
+
+
+def test_wide_rows_adagrad_and_sgd(sgb):
+    for mode in ("rowwise_adagrad", "sgd", "dense"):
+        s = synth.Spec("wide", 2, (400, 300), (1024, 516), 33, ("uniform", 0, 40), ("zipf", 1.3),
+                       "mean", True, "f32", mode, seed=77)
+        check_case(sgb, synth.generate(s), mode, 32, lr=0.02, eps=1e-6)
+
+
+# ------------------------------------------------------------------ edge cases
+
+def test_empty_input(sgb):
+    s = synth.Spec("empty", 2, (10, 20), (8, 16), 5, ("fixed", 0), ("uniform",), "sum", False,
+                   "f32", "dense", seed=1)
+    inp = synth.generate(s)
+    assert inp.N == 0
+    for mode, acc in (("dense", False), ("dense", True), ("sgd", False), ("rowwise_adagrad", False)):
+        check_case(sgb, inp, mode, 4, accumulate=acc, runs=False)
+
+
+def test_all_empty_but_one(sgb):
+    s = synth.Spec("one", 2, (50, 60), (16, 32), 100, ("fixed", 0), ("uniform",), "mean", True,
+                   "f32", "sgd", seed=2)
+    inp = synth.generate(s, with_grad=True)
+    lens = np.zeros(200, np.int64)
+    lens[137] = 9
+    inp.offsets = np.concatenate([[0], np.cumsum(lens)])
+    inp.indices = np.array([3, 3, 59, 0, 3, 7, 7, 1, 3])
+    inp.per_sample_weights = np.linspace(0.5, 2.0, 9).astype(np.float32)
+    check_case(sgb, inp, "sgd", 2)
+
+
+def test_one_hot_row(sgb):
+    """Every lookup on one row: one run of length N, long path only."""
+    s = synth.Spec("hot", 1, (1000,), (128,), 3000, ("uniform", 1, 40), ("uniform",), "sum", True,
+                   "f32", "rowwise_adagrad", seed=3)
+    inp = synth.generate(s)
+    inp.indices[:] = 417
+    _say(f"[parity] one row N={inp.N}")
+    check_case(sgb, inp, "rowwise_adagrad", 64, lr=0.01, eps=1e-8)
+    check_case(sgb, inp, "dense", 64)
+
+
+def test_all_distinct(sgb):
+    """U = N, short path only."""
+    B = 5000
+    s = synth.Spec("distinct", 1, (B,), (64,), B, ("fixed", 1), ("uniform",), "mean", False, "f32",
+                   "dense", seed=4)
+    inp = synth.generate(s)
+    inp.indices = np.random.default_rng(5).permutation(B).astype(np.int64)
+    check_case(sgb, inp, "dense", 2)
+
+
+@pytest.mark.parametrize("delta", [-1, 0, 1])
+def test_run_lengths_around_threshold(sgb, delta):
+    thr = 64
+    L = thr + delta
+    s = synth.Spec("around", 1, (50,), (16,), 3 * L, ("fixed", 1), ("uniform",), "sum", False,
+                   "f32", "sgd", seed=6)
+    inp = synth.generate(s)
+    inp.indices = np.repeat(np.array([5, 9, 40]), L).astype(np.int64)
+    check_case(sgb, inp, "sgd", thr)
+
+
+def test_mixed_dims_and_bf16_bags(sgb):
+    s = synth.Spec("mixed", 4, (700, 20, 1500, 90), (8, 200, 48, 132), 300, ("poisson", 6.0),
+                   ("zipf", 1.2), "mean", True, "bf16", "rowwise_adagrad", lr=0.1, eps=1e-5,
+                   seed=8)
+    check_case(sgb, synth.generate(s), "rowwise_adagrad", 24, lr=0.1, eps=1e-5)
+
+
+def test_huge_run_two_level_combine(sgb):
+    """A run long enough for several first-level groups of chunks."""
+    s = synth.Spec("huge", 1, (100,), (64,), 8000, ("uniform", 20, 40), ("zipf", 3.0), "sum",
+                   True, "f32", "rowwise_adagrad", lr=0.01, eps=1e-8, seed=9)
+    inp = synth.generate(s)
+    _say(f"[parity] huge run N={inp.N}")
+    check_case(sgb, inp, "rowwise_adagrad", 64, lr=0.01, eps=1e-8)
+
+
+# ------------------------------------------------------------------ properties
+
+def test_deterministic(sgb):
+    s = synth.spec(5, E=(50000,), B=3000)
+    inp = synth.generate(s)
+    out0, mom0 = initial_buffers(inp, s.mode, False)
+    d0, m0 = torch.from_numpy(out0).cuda(), torch.from_numpy(mom0).cuda()
+    dev = to_dev(inp)
+    r1 = run_gpu(sgb, inp, s.mode, 64, d0, m0, lr=s.lr, eps=s.eps, dev=dev)
+    r2 = run_gpu(sgb, inp, s.mode, 64, d0, m0, lr=s.lr, eps=s.eps, dev=dev, plan=r1.plan)
+    assert torch.equal(r1.out.view(torch.int32), r2.out.view(torch.int32))
+    assert torch.equal(r1.mom.view(torch.int32), r2.mom.view(torch.int32))
+
+
+def test_workspace_reuse_smaller_second_call(sgb):
+    """The same workspace serves a big call and then a smaller one."""
+    s1 = synth.spec(3, T=3, E=(5000,) * 3, B=600)
+    s2 = synth.spec(3, T=3, E=(5000,) * 3, B=200, seed=77)
+    plan = sgb.Plan(synth.generate(s1).hash_size_cumsum, synth.generate(s1).D_offsets, "sum", 32)
+    inp1, inp2 = synth.generate(s1), synth.generate(s2)
+    ws = plan.workspace(max(inp1.N, inp2.N), 600)
+    for inp in (inp1, inp2):
+        out0, mom0 = initial_buffers(inp, "rowwise_adagrad", False)
+        run = run_gpu(sgb, inp, "rowwise_adagrad", 32, torch.from_numpy(out0).cuda(),
+                      torch.from_numpy(mom0).cuda(), lr=0.01, eps=1e-8, plan=plan, ws=ws)
+        assert run.status == "SGB_OK"
+        check_runs(sgb, run, inp, 32)
+
+
+# ------------------------------------------------------------------ errors
+
+def test_device_detected_errors(sgb):
+    s = synth.Spec("err", 2, (30, 40), (8, 8), 20, ("uniform", 1, 5), ("uniform",), "sum", False,
+                   "f32", "dense", seed=10)
+    inp = synth.generate(s)
+    out0 = torch.zeros(int(inp.weights_offsets[-1]), device="cuda")
+    bad = synth.generate(s)
+    bad.indices = bad.indices.copy()
+    bad.indices[inp.offsets[20] + 1] = 40          # table 1 has E = 40: out of range
+    r = run_gpu(sgb, bad, "dense", 4, out0, None)
+    assert r.status == "SGB_ERR_INDEX_OUT_OF_RANGE"
+    bad = synth.generate(s)
+    bad.indices = bad.indices.copy()
+    bad.indices[0] = -3
+    assert run_gpu(sgb, bad, "dense", 4, out0, None).status == "SGB_ERR_INDEX_OUT_OF_RANGE"
+    bad = synth.generate(s)
+    bad.offsets = bad.offsets.copy()
+    bad.offsets[5], bad.offsets[6] = bad.offsets[6], bad.offsets[5] - 1
+    assert run_gpu(sgb, bad, "dense", 4, out0, None).status == "SGB_ERR_BAD_OFFSETS"
+    bad = synth.generate(s)
+    bad.offsets = bad.offsets.copy()
+    bad.offsets[-1] -= 1
+    assert run_gpu(sgb, bad, "dense", 4, out0, None).status == "SGB_ERR_BAD_OFFSETS"
+    # a clean call on the same plan afterwards is fine again
+    assert run_gpu(sgb, inp, "dense", 4, out0, None).status == "SGB_OK"
+
+
+def test_host_detected_errors(sgb):
+    s = synth.Spec("herr", 1, (30,), (8,), 4, ("uniform", 1, 5), ("uniform",), "none", False,
+                   "f32", "dense", seed=11)
+    with pytest.raises(sgb.SgbError) as e:
+        sgb.Plan(np.array([0, 10]), np.array([0, 6]), "sum", 4)
+    assert e.value.name == "SGB_ERR_INVALID_ARGUMENT"
+    with pytest.raises(sgb.SgbError):
+        sgb.Plan(np.array([0, 10, 10]), np.array([0, 8, 16]), "sum", 4)
+    with pytest.raises(sgb.SgbError):
+        sgb.Plan(np.array([0, 10]), np.array([0, 8]), "sum", 0)
+    plan = sgb.Plan(np.array([0, 10]), np.array([0, 8]), "none", 4)
+    idx = torch.zeros(4, dtype=torch.int64, device="cuda")
+    g = torch.zeros(4, 8, device="cuda")
+    grad = torch.zeros(80, device="cuda")
+    ws = plan.workspace(4, 0)
+    with pytest.raises(sgb.SgbError) as e:   # nobag is unweighted only
+        plan.backward(g, idx, None, 0, torch.ones(4, device="cuda"), "dense", grad=grad,
+                      workspace=ws)
+    assert e.value.name == "SGB_ERR_UNSUPPORTED"
+    with pytest.raises(sgb.SgbError) as e:
+        plan.backward(g, idx, None, 0, None, "dense", grad=grad, workspace=ws[:16])
+    assert e.value.name == "SGB_ERR_WORKSPACE_TOO_SMALL"
+    with pytest.raises(sgb.SgbError) as e:
+        plan.backward(g, idx, None, 0, None, "sgd", workspace=ws)   # no weights
+    assert e.value.name == "SGB_ERR_INVALID_ARGUMENT"
+    wide = sgb.Plan(np.array([0, 10]), np.array([0, 2048]), "sum", 4)
+    with pytest.raises(sgb.SgbError) as e:
+        wide.backward(torch.zeros(1, 2048, device="cuda"), idx[:1], torch.tensor([0, 1],
+                      device="cuda"), 1, None, "rowwise_adagrad", weights=torch.zeros(20480,
+                      device="cuda"), momentum=torch.zeros(10, device="cuda"),
+                      workspace=wide.workspace(1, 1))
+    assert e.value.name == "SGB_ERR_UNSUPPORTED"
