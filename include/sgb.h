@@ -166,6 +166,30 @@ typedef struct {
 sgb_status sgb_backward(sgb_plan plan, const sgb_batch* batch, const sgb_update* update,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* Stages of sgb_backward() in launch order (see sgb_backward_timed). */
+typedef enum {
+  SGB_STAGE_INIT = 0,       /* clear workspace header and digit histograms        */
+  SGB_STAGE_LINEARIZE = 1,  /* bags -> packed (linear id, info) words + histograms */
+  SGB_STAGE_SORT = 2,       /* all stable radix passes                            */
+  SGB_STAGE_RLE = 3,        /* run heads -> unique ids, run starts, run count      */
+  SGB_STAGE_RUNS = 4,       /* run lengths, long-run list, chunk prefix           */
+  SGB_STAGE_FILL = 5,       /* zeros of untouched rows (fresh dense grad only)    */
+  SGB_STAGE_REDUCE = 6,     /* per-run reduction and the fused row write          */
+  SGB_NUM_STAGES = 7
+} sgb_stage;
+
+/*
+ * sgb_backward_timed -- sgb_backward() that also records HIP events on
+ * `stream` around each stage: events[2k] just before stage k's first kernel
+ * and events[2k+1] just after its last (hipEvent_t passed as void*).  NULL
+ * entries, and stages that do not run in this call, are skipped.  `events`
+ * has 2 * SGB_NUM_STAGES entries or is NULL.  For measurement only: the
+ * kernels and results are those of sgb_backward().
+ */
+sgb_status sgb_backward_timed(sgb_plan plan, const sgb_batch* batch, const sgb_update* update,
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              void* const* events);
+
 /*
  * sgb_device_status -- synchronises `stream`, then stores in *out the first
  * error the kernels recorded in `workspace` during the last sgb_backward()

@@ -24,7 +24,23 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "sgb.h")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
                       "`python -m sparse_gradient_backward_amd.build` (hipcc, gfx950)")
+
+# torch ships its own HIP runtime.  Load it first so that libsgb.so binds to
+# that same runtime (by soname): device pointers and streams come from torch,
+# and two HIP runtimes in one process do not share streams or contexts.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
+
+
+def _hip_runtimes() -> list:
+    with open("/proc/self/maps") as f:
+        return sorted(set(re.findall(r"(/\S*libamdhip64\S*)", f.read())))
+
+
+if len(_hip_runtimes()) > 1:
+    raise ImportError("more than one HIP runtime is loaded in this process: "
+                      f"{_hip_runtimes()}; import torch before any other HIP library")
 
 # ------------------------------------------------------------------ enums
 
@@ -62,12 +78,14 @@ _lib.sgb_plan_destroy.restype = None
 _lib.sgb_workspace_bytes.argtypes = [_vp, _i64, _i32, ctypes.POINTER(ctypes.c_size_t)]
 _lib.sgb_backward.argtypes = [_vp, ctypes.POINTER(_Batch), ctypes.POINTER(_Update), _vp,
                               ctypes.c_size_t, _vp]
+_lib.sgb_backward_timed.argtypes = [_vp, ctypes.POINTER(_Batch), ctypes.POINTER(_Update), _vp,
+                                    ctypes.c_size_t, _vp, ctypes.POINTER(_vp)]
 _lib.sgb_device_status.argtypes = [_vp, _vp, _vp, ctypes.POINTER(_i32)]
 _lib.sgb_runs_view_get.argtypes = [_vp, _vp, _i64, _i32, ctypes.POINTER(_RunsView)]
 _lib.sgb_status_string.argtypes = [_i32]
 _lib.sgb_status_string.restype = ctypes.c_char_p
-for _f in ("sgb_plan_create", "sgb_workspace_bytes", "sgb_backward", "sgb_device_status",
-           "sgb_runs_view_get"):
+for _f in ("sgb_plan_create", "sgb_workspace_bytes", "sgb_backward", "sgb_backward_timed",
+           "sgb_device_status", "sgb_runs_view_get"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -135,11 +153,18 @@ def _stream(stream) -> Optional[int]:
     return int(s.cuda_stream)
 
 
+STAGES = ("init", "linearize", "sort", "rle", "runs", "fill", "reduce")
+
+
 def sgb_backward(plan: int, grad_output, indices, offsets, B: int, per_sample_weights,
                  mode: str, weights=None, momentum=None, grad=None, accumulate: bool = False,
-                 lr: float = 0.0, eps: float = 0.0, workspace=None, stream=None) -> None:
+                 lr: float = 0.0, eps: float = 0.0, workspace=None, stream=None,
+                 events=None) -> None:
     """Enqueue one backward pass.  Tensors are device tensors; grad_output is
-    float32 or bfloat16, indices/offsets int64, per_sample_weights float32."""
+    float32 or bfloat16, indices/offsets int64, per_sample_weights float32.
+    `events`, if given, is a list of 2 * len(STAGES) recorded-once
+    torch.cuda.Event(enable_timing=True) objects (or None entries) that the
+    library records around each stage (sgb_backward_timed)."""
     import torch
     gd = {torch.float32: "f32", torch.bfloat16: "bf16"}[grad_output.dtype]
     for name, t, dt in (("indices", indices, torch.int64), ("offsets", offsets, torch.int64),
@@ -156,8 +181,14 @@ def sgb_backward(plan: int, grad_output, indices, offsets, B: int, per_sample_we
                   float(lr), float(eps))
     ws_ptr = _ptr(workspace)
     ws_bytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
-    _check(_lib.sgb_backward(plan, ctypes.byref(batch), ctypes.byref(upd), ws_ptr, ws_bytes,
-                             _stream(stream)), "sgb_backward")
+    if events is None:
+        _check(_lib.sgb_backward(plan, ctypes.byref(batch), ctypes.byref(upd), ws_ptr, ws_bytes,
+                                 _stream(stream)), "sgb_backward")
+    else:
+        arr = (_vp * (2 * len(STAGES)))(*[None if e is None else int(e.cuda_event)
+                                          for e in events])
+        _check(_lib.sgb_backward_timed(plan, ctypes.byref(batch), ctypes.byref(upd), ws_ptr,
+                                       ws_bytes, _stream(stream), arr), "sgb_backward_timed")
 
 
 def sgb_device_status(plan: int, workspace, stream=None) -> int:

@@ -1,6 +1,8 @@
 """Build libsgb.so (gfx950 HIP kernels + C ABI) in-tree with hipcc.
 
-    python -m sparse_gradient_backward_amd.build
+    python sparse_gradient_backward_amd/build.py
+
+(run as a script: importing the package itself needs the built library)
 """
 from __future__ import annotations
 

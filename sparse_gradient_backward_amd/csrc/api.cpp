@@ -208,9 +208,11 @@ sgb_status sgb_plan_create(sgb_plan* out, int32_t T, const int64_t* hsc, const i
   p->key_bits = bitlen((uint64_t)(p->total_rows - 1));
   p->n_fill = (int32_t)fill.size();
 
-  hipDeviceProp_t prop;
-  if (hipGetDeviceProperties(&prop, p->device) == hipSuccess && prop.multiProcessorCount > 0)
-    p->num_cus = prop.multiProcessorCount;
+  int cus = 0;  // a scalar attribute: no versioned property struct crosses the runtime
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device) ==
+          hipSuccess &&
+      cus > 0)
+    p->num_cus = cus;
   p->red_grid[0] = p->num_cus * reduce_blocks_per_cu(false);
   p->red_grid[1] = p->num_cus * reduce_blocks_per_cu(true);
 
@@ -257,6 +259,11 @@ sgb_status sgb_workspace_bytes(sgb_plan p, int64_t N, int32_t B, size_t* bytes) 
 
 sgb_status sgb_backward(sgb_plan p, const sgb_batch* b, const sgb_update* u, void* ws,
                         size_t ws_bytes, void* stream_) {
+  return sgb_backward_timed(p, b, u, ws, ws_bytes, stream_, nullptr);
+}
+
+sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* u, void* ws,
+                              size_t ws_bytes, void* stream_, void* const* events) {
   if (!p || !b || !u) return SGB_ERR_INVALID_ARGUMENT;
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
   const int64_t N = b->num_indices;
@@ -278,8 +285,16 @@ sgb_status sgb_backward(sgb_plan p, const sgb_batch* b, const sgb_update* u, voi
   const bool fresh = u->mode == SGB_DENSE_GRAD && !u->accumulate;
   DeviceGuard guard(p->device);
   if (!guard.ok) return SGB_ERR_HIP;
+  auto mark = [&](int stage, int end) {
+    void* ev = events ? events[2 * stage + end] : nullptr;
+    if (ev) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev), stream);
+  };
 
   if (N == 0) {  // FBGEMM host entry: no indices -> nothing to do (dense grad stays zero)
+    // clear the status word so sgb_device_status() reports this call
+    if (ws && aligned(ws, 256) && ws_bytes >= sizeof(Header) &&
+        launch_init(ws, sizeof(Header), stream) != hipSuccess)
+      return SGB_ERR_HIP;
     if (fresh && p->n_fill > 0) {
       FillParams f{out, p->d_fill, p->d_hsc, p->d_doff, p->d_woff, nullptr};
       if (launch_fill(f, p->n_fill, stream) != hipSuccess) return SGB_ERR_HIP;
@@ -297,8 +312,10 @@ sgb_status sgb_backward(sgb_plan p, const sgb_batch* b, const sgb_update* u, voi
   Header* hdr = at<Header>(ws, L.hdr);
   uint32_t* status = &hdr->status;
   const bool has_coef = (p->pooling == SGB_POOL_MEAN) || (b->per_sample_weights != nullptr);
+  mark(SGB_STAGE_INIT, 0);
   hipError_t e = launch_init(ws, L.zero_begin, stream);
   if (e != hipSuccess) return SGB_ERR_HIP;
+  mark(SGB_STAGE_INIT, 1);
 
   // linearise + digit histograms (+ clear look-back words and the bitmap)
   LinParams lp{};
@@ -325,13 +342,16 @@ sgb_status sgb_backward(sgb_plan p, const sgb_batch* b, const sgb_update* u, voi
   const int64_t lin_tiles = b->offsets ? ((int64_t)b->B * p->T + kLinBags - 1) / kLinBags
                                        : (N + kLinLookups - 1) / kLinLookups;
   const int lin_grid = (int)std::max<int64_t>(1, std::min<int64_t>(lin_tiles, 4ll * p->num_cus));
+  mark(SGB_STAGE_LINEARIZE, 0);
   if (launch_linearize(lp, lin_grid, stream) != hipSuccess) return SGB_ERR_HIP;
+  mark(SGB_STAGE_LINEARIZE, 1);
 
   // LSD radix passes, ping-pong between A and B
   uint64_t* kv_in = at<uint64_t>(ws, L.kvA);
   uint64_t* kv_out = at<uint64_t>(ws, L.kvB);
   float* cf_in = has_coef ? at<float>(ws, L.coefA) : nullptr;
   float* cf_out = has_coef ? at<float>(ws, L.coefB) : nullptr;
+  if (L.npasses > 0) mark(SGB_STAGE_SORT, 0);
   for (int ps = 0; ps < L.npasses; ++ps) {
     SortParams sp{};
     sp.kv_in = kv_in;
@@ -349,6 +369,7 @@ sgb_status sgb_backward(sgb_plan p, const sgb_batch* b, const sgb_update* u, voi
     std::swap(kv_in, kv_out);
     std::swap(cf_in, cf_out);
   }
+  if (L.npasses > 0) mark(SGB_STAGE_SORT, 1);
   const uint64_t* kv_sorted = kv_in;
   const float* cf_sorted = cf_in;
 
@@ -362,7 +383,9 @@ sgb_status sgb_backward(sgb_plan p, const sgb_batch* b, const sgb_update* u, voi
   rp.lookback = at<uint32_t>(ws, L.rle_lb);
   rp.tile_ctr = &hdr->rle_tile_ctr;
   rp.status = status;
+  mark(SGB_STAGE_RLE, 0);
   if (launch_rle(rp, (int)L.scan_tiles, stream) != hipSuccess) return SGB_ERR_HIP;
+  mark(SGB_STAGE_RLE, 1);
 
   PostParams pp{};
   pp.cum = rp.cum;
@@ -382,11 +405,15 @@ sgb_status sgb_backward(sgb_plan p, const sgb_batch* b, const sgb_update* u, voi
   pp.lookback = at<uint64_t>(ws, L.post_lb);
   pp.tile_ctr = &hdr->post_tile_ctr;
   pp.status = status;
+  mark(SGB_STAGE_RUNS, 0);
   if (launch_post(pp, (int)L.scan_tiles, stream) != hipSuccess) return SGB_ERR_HIP;
+  mark(SGB_STAGE_RUNS, 1);
 
   if (fresh) {
     FillParams f{out, p->d_fill, p->d_hsc, p->d_doff, p->d_woff, pp.bitmap};
+    mark(SGB_STAGE_FILL, 0);
     if (launch_fill(f, p->n_fill, stream) != hipSuccess) return SGB_ERR_HIP;
+    mark(SGB_STAGE_FILL, 1);
   }
 
   RedParams q{};
@@ -423,8 +450,10 @@ sgb_status sgb_backward(sgb_plan p, const sgb_batch* b, const sgb_update* u, voi
   q.lr = u->lr;
   q.eps = u->eps;
   const bool bf16 = b->grad_dtype == SGB_BF16;
+  mark(SGB_STAGE_REDUCE, 0);
   if (launch_reduce(q, &hdr->num_long, bf16, p->red_grid[bf16 ? 1 : 0], stream) != hipSuccess)
     return SGB_ERR_HIP;
+  mark(SGB_STAGE_REDUCE, 1);
   return SGB_OK;
 }
 

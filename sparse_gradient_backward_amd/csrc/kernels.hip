@@ -922,9 +922,12 @@ __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, in
   for (int i = 0; i < g; ++i) m &= m - 1;
   const bool active = m != 0;
   const int src = active ? __builtin_ctzll(m) : 0;
+  // Shuffles run with the whole wave active: a source lane can sit in a group
+  // that has no run of its own, and a masked-off source would read as 0.
   const int s = __shfl(start, src, 64);
-  const int n = active ? __shfl(len, src, 64) : 0;
+  const int nn = __shfl(len, src, 64);
   const int rr = __shfl(r, src, 64);
+  const int n = active ? nn : 0;
   RowDst dst{nullptr, nullptr};
   if (active) dst = row_dest(p, t, D, p.unique_ids[rr]);
   const int64_t gcol = p.nobag ? 0 : p.doff[t];
