@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Benchmark of the pooled embedding-bag backward on one MI355X.
+
+One step = one sgb_backward() call -- the whole path: linearise, radix sort,
+run-length encode, long-run split, segmented reduce and the fused row write
+-- over one synthetic batch already resident in HBM.  Default workload: the
+T=8 x E=100k x D=128 dense-gradient configuration (mean pooling with
+per-sample weights, Zipf 1.05, B=2048); --config selects another one.
+
+Prints ONE JSON line on stdout (progress goes to stderr):
+  value        lookups/s of the whole step (wall clock, synchronised)
+  roofline     the dominant kernel: algorithmic bytes per launch / its average
+               duration from HIP events recorded on the library's stream
+  cpu_baseline the CPU oracle (plain C, one thread) on the same batch
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402  (first: the library binds to torch's HIP runtime)
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+
+METRIC = "embedding-bwd lookups/sec + achieved HBM GB/s (% of MI355X peak), 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+STAGES = ("init", "linearize", "sort", "rle", "runs", "fill", "reduce_long", "reduce_short")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def stage_bytes(inp: synth.Inputs, spec: synth.Spec, U: int, run_D: np.ndarray,
+                run_len: np.ndarray, thr: int, npasses: int):
+    """Algorithmic bytes each stage must move (one call), by the byte model of
+    the design doc: every input read once, every output written once, the sorted
+    stream written and read once per radix pass, each run's gather and row
+    update once."""
+    N = inp.N
+    c = 1 if (spec.pooling == "mean" or spec.weighted) else 0
+    sg = 2 if spec.grad_dtype == "bf16" else 4
+    BT = inp.B * inp.T if inp.offsets is not None else 0
+    rec = 8 + 4 * c                       # packed word (+ coefficient) per lookup
+    fresh = spec.mode == "dense" and not spec.accumulate
+    Ds = np.diff(inp.D_offsets).astype(np.int64)
+    Es = np.diff(inp.hash_size_cumsum).astype(np.int64)
+    touched_elems = int(run_D.sum())
+
+    def update(D):
+        if spec.mode == "dense":
+            return int(D.sum()) * 4 * (2 if spec.accumulate else 1)
+        if spec.mode == "sgd":
+            return int(D.sum()) * 8
+        return int(D.sum()) * 8 + D.shape[0] * 8
+
+    lg = run_len >= thr
+    gather_long = int((run_len[lg] * run_D[lg]).sum()) * sg
+    gather_short = int((run_len[~lg] * run_D[~lg]).sum()) * sg
+    b = {
+        "init": 0,
+        "linearize": N * (8 + 8 + 4 * c + (4 if spec.weighted else 0)) + (BT + 1) * 8 * (BT > 0),
+        "sort": npasses * N * rec * 2,
+        "rle": N * 8 + U * (8 + 4 + 4),
+        "runs": U * (4 * 2 + 4 + (8 if fresh else 0)),
+        "fill": ((int((Es * Ds).sum()) - touched_elems) * 4 + int(Es.sum()) // 8) if fresh else 0,
+        "reduce_long": gather_long + int(run_len[lg].sum()) * rec + int(lg.sum()) * 16
+        + update(run_D[lg]),
+        "reduce_short": gather_short + N * 8 + int(run_len[~lg].sum()) * 4 * c
+        + int((~lg).sum()) * 8 + update(run_D[~lg]),
+    }
+    # whole path, counted as the contract's byte model: indices read, the
+    # sorted stream (8-byte id + 4-byte info + coefficient) written and read
+    # once, the gather, offsets, 24 bytes per run, the row update
+    b_path = N * (8 + 2 * (8 + 4 + 4 * c)) + gather_long + gather_short \
+        + (BT + 1) * 8 * (BT > 0) + U * 24 + update(run_D)
+    if fresh:
+        b_path += (int((Es * Ds).sum()) - touched_elems) * 4
+    return b, b_path
+
+
+def cpu_baseline(inp: synth.Inputs, spec: synth.Spec, thr: int, min_s: float, max_reps: int):
+    """The CPU oracle as it stands (plain C, single thread) on the same batch."""
+    import oracle
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from harness import oracle_problem
+    prob = oracle_problem(inp)
+    reps, total = 0, 0.0
+    while reps < max_reps and (reps == 0 or total < min_s):
+        t0 = time.perf_counter()
+        keys, infos, _ = oracle.linearize(prob)
+        r = oracle.runs(keys, infos, thr)
+        G, _ = oracle.row_grads(prob, r["unique_ids"])
+        D = np.diff(inp.D_offsets)[np.searchsorted(inp.hash_size_cumsum, r["unique_ids"],
+                                                   side="right") - 1]
+        rows0 = None if (spec.mode == "dense" and not spec.accumulate) else \
+            np.zeros(G.shape, np.float32)
+        mom0 = np.zeros(G.shape[0], np.float32) if spec.mode == "rowwise_adagrad" else None
+        oracle.update_rows(spec.mode, G, D, rows0, mom0, lr=spec.lr, eps=spec.eps,
+                           accumulate=spec.accumulate)
+        total += time.perf_counter() - t0
+        reps += 1
+        log(f"cpu oracle rep {reps}: {total:.1f} s so far")
+    return dict(value=inp.N * reps / total, unit="lookups/s", cores=1, kind="oracle",
+                sample=f"the full batch ({inp.N} lookups) x {reps} repetition(s), "
+                       f"{total:.1f} s, one thread (plain C loops, fp64)")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--thr", type=int, default=None,
+                    help="max_segment_length_per_warp (default: the workload's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-min-s", type=float, default=10.0)
+    ap.add_argument("--cpu-max-reps", type=int, default=20)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import sparse_gradient_backward_amd as sgb
+    spec = synth.spec(args.config)
+    thr = args.thr or spec.thr
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    log(f"config {args.config} ({spec.name}): generating inputs")
+    inp = synth.generate(spec)
+    g = torch.from_numpy(inp.grad_output)
+    if inp.grad_output.dtype == np.uint16:
+        g = g.view(torch.bfloat16)
+    grad_output = g.to(dev)
+    indices = torch.from_numpy(inp.indices).to(dev)
+    offsets = None if inp.offsets is None else torch.from_numpy(inp.offsets).to(dev)
+    psw = None if inp.per_sample_weights is None else torch.from_numpy(inp.per_sample_weights).to(dev)
+    B = inp.B if inp.offsets is not None else 0
+    n_elems = int(inp.weights_offsets[-1])
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(spec.seed)
+    out = torch.empty(n_elems, dtype=torch.float32, device=dev)
+    mom = None
+    if spec.mode == "dense" and not spec.accumulate:
+        out.zero_()
+    elif spec.mode == "dense":
+        out.normal_(0.0, spec.dense_init_std, generator=gen)
+    else:
+        out.normal_(0.0, spec.weights_std, generator=gen)
+    if spec.mode == "rowwise_adagrad":
+        mom = torch.zeros(inp.total_rows, dtype=torch.float32, device=dev)   # measurement: state 0
+    plan = sgb.Plan(inp.hash_size_cumsum, inp.D_offsets, spec.pooling, thr)
+    ws = plan.workspace(inp.N, B)
+    kw = dict(grad=out) if spec.mode == "dense" else dict(weights=out, momentum=mom)
+    log(f"N={inp.N} T={inp.T} B={B} workspace={ws.numel() / 2**20:.1f} MiB; warmup {args.warmup}")
+
+    def step(events=None):
+        plan.backward(grad_output, indices, offsets, B, psw, spec.mode, accumulate=spec.accumulate,
+                      lr=spec.lr, eps=spec.eps, workspace=ws, events=events, **kw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    status = plan.device_status(ws)
+    if status != "SGB_OK":
+        raise SystemExit(f"device status after warm-up: {status}")
+
+    # timed region 1: plain steps (the reported value)
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    # timed region 2: the same steps with HIP events around each stage,
+    # recorded by the library on its stream
+    evs = []
+    for _ in range(args.steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(STAGES))]
+        for x in e:
+            x.record()          # creates the event handle
+        evs.append(e)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    ms_timed = (time.perf_counter() - t1) * 1e3 / args.steps
+    stage_ms = {}
+    view = plan.runs_view(ws, inp.N, B)
+    for k, name in enumerate(STAGES):
+        if name == "fill" and not (spec.mode == "dense" and not spec.accumulate):
+            continue
+        if name == "sort" and plan_npasses(inp) == 0:
+            continue
+        d = [e[2 * k].elapsed_time(e[2 * k + 1]) for e in evs]
+        stage_ms[name] = float(np.mean(d))
+    status = plan.device_status(ws)
+
+    # run statistics for the byte model (from the library's own run view)
+    U = view["num_runs"]
+    uniq = view["unique_ids"].cpu().numpy()
+    lens = view["run_lengths"].cpu().numpy().astype(np.int64)
+    run_t = np.searchsorted(inp.hash_size_cumsum, uniq, side="right") - 1
+    run_D = np.diff(inp.D_offsets).astype(np.int64)[run_t]
+    nlong = view["num_long"]
+    npasses = plan_npasses(inp)
+    sb, b_path = stage_bytes(inp, spec, U, run_D, lens, thr, npasses)
+    dom = max(stage_ms, key=lambda k: stage_ms[k])
+    launches = npasses if dom == "sort" else 1
+    per_launch_bytes = sb[dom] / launches
+    per_launch_ms = stage_ms[dom] / launches
+    achieved = per_launch_bytes / (per_launch_ms * 1e-3) / 1e9
+    gbps_path = b_path / (ms_per_step * 1e-3) / 1e9
+    log(f"stages (ms): " + ", ".join(f"{k}={v:.4f}" for k, v in stage_ms.items()))
+    log(f"step {ms_per_step:.4f} ms (instrumented {ms_timed:.4f} ms); path {gbps_path:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        cpu = cpu_baseline(inp, spec, thr, args.cpu_min_s, args.cpu_max_reps)
+
+    kernel_names = {"reduce_long": "k_reduce_long", "reduce_short": "k_reduce_short",
+                    "sort": "k_sort_pass", "fill": "k_fill", "linearize": "k_linearize",
+                    "rle": "k_rle", "runs": "k_post", "init": "k_init"}
+    res = {
+        "metric": METRIC,
+        "value": inp.N / (ms_per_step * 1e-3),
+        "unit": "lookups/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "T": inp.T, "B": B, "N": inp.N, "U": int(U),
+                   "num_long_runs": int(nlong), "max_segment_length_per_warp": thr,
+                   "grad_dtype": spec.grad_dtype, "mode": spec.mode,
+                   "accumulate": bool(spec.accumulate), "pooling": spec.pooling,
+                   "weighted": bool(spec.weighted), "radix_passes": npasses},
+        "achieved_GBps_path": gbps_path,
+        "hbm_pct_path": 100.0 * gbps_path / HBM_PEAK_GBPS,
+        "bytes_alg_path": int(b_path),
+        "stage_ms": stage_ms,
+        "stage_bytes": {k: int(v) for k, v in sb.items()},
+        "ms_per_step_instrumented": ms_timed,
+        "roofline": {"bound": "hbm", "kernel": kernel_names[dom], "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": None, "bytes_per_launch": int(per_launch_bytes),
+                     "launch_ms": per_launch_ms},
+        "cpu_baseline": cpu,
+        "device_status": status,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def plan_npasses(inp: synth.Inputs) -> int:
+    rows = int(inp.hash_size_cumsum[-1])
+    bits = int(rows - 1).bit_length()
+    return (bits + 8) // 9
+
+
+if __name__ == "__main__":
+    main()

@@ -174,8 +174,9 @@ typedef enum {
   SGB_STAGE_RLE = 3,        /* run heads -> unique ids, run starts, run count      */
   SGB_STAGE_RUNS = 4,       /* run lengths, long-run list, chunk prefix           */
   SGB_STAGE_FILL = 5,       /* zeros of untouched rows (fresh dense grad only)    */
-  SGB_STAGE_REDUCE = 6,     /* per-run reduction and the fused row write          */
-  SGB_NUM_STAGES = 7
+  SGB_STAGE_REDUCE_LONG = 6,  /* long runs: chunked reduction + fused row write   */
+  SGB_STAGE_REDUCE_SHORT = 7, /* short runs: reduction + fused row write          */
+  SGB_NUM_STAGES = 8
 } sgb_stage;
 
 /*

@@ -153,7 +153,7 @@ def _stream(stream) -> Optional[int]:
     return int(s.cuda_stream)
 
 
-STAGES = ("init", "linearize", "sort", "rle", "runs", "fill", "reduce")
+STAGES = ("init", "linearize", "sort", "rle", "runs", "fill", "reduce_long", "reduce_short")
 
 
 def sgb_backward(plan: int, grad_output, indices, offsets, B: int, per_sample_weights,

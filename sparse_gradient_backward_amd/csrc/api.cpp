@@ -36,7 +36,7 @@ struct sgb_plan_s {
   FillBlock* d_fill = nullptr;
   int32_t n_fill = 0;
   int num_cus = 1;
-  int red_grid[2] = {1, 1};
+  int red_grid[2] = {1, 1};  // persistent grid of the long-run reducer (f32, bf16)
 };
 
 namespace {
@@ -72,11 +72,11 @@ struct Layout {
   int pass_key_shift[kMaxPasses] = {};
   int64_t sort_tiles = 0, scan_tiles = 0;
   int64_t max_long = 0;   // bound on the number of long runs
-  int64_t max_items = 0;  // bound on the chunks over all long runs
+  int64_t max_items = 0;  // bound on the (chunk, column block) items over all long runs
   int32_t ch_base = 0;
   size_t hdr = 0, hist = 0, zero_begin = 0, sort_lb = 0, rle_lb = 0, post_lb = 0, bitmap = 0,
          zero_end_nobitmap = 0, zero_end_bitmap = 0;
-  size_t kvA = 0, kvB = 0, coefA = 0, coefB = 0, uniq = 0, cum = 0, lens = 0, longs = 0,
+  size_t kvA = 0, kvB = 0, coefA = 0, coefB = 0, uniq = 0, cum = 0, headrun = 0, lens = 0, longs = 0,
          chunkb = 0, runtk = 0, sctk = 0, part = 0, total = 0;
 };
 
@@ -106,7 +106,9 @@ sgb_status make_layout(const sgb_plan_s* p, int64_t N, int32_t B, bool has_offse
   L->scan_tiles = (N + kScanTile - 1) / kScanTile;
   L->ch_base = std::max<int32_t>(p->thr, kChunkMin);
   L->max_long = N / p->thr + 1;
-  L->max_items = N / L->ch_base + L->max_long + 1;
+  // chunks over long runs <= N / ch_base + number of long runs; each chunk
+  // spans at most ceil(Dmax / 256) column blocks
+  L->max_items = (N / L->ch_base + L->max_long + 1) * ((p->Dmax + kColBlock - 1) / kColBlock);
 
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -130,12 +132,13 @@ sgb_status make_layout(const sgb_plan_s* p, int64_t N, int32_t B, bool has_offse
   L->coefB = take(sizeof(float) * (size_t)N);
   L->uniq = take(sizeof(int64_t) * (size_t)N);
   L->cum = take(sizeof(int32_t) * (size_t)(N + 1));
+  L->headrun = take(sizeof(int32_t) * (size_t)N);
   L->lens = take(sizeof(int32_t) * (size_t)N);
   L->longs = take(sizeof(int32_t) * (size_t)L->max_long);
   L->chunkb = take(sizeof(uint32_t) * (size_t)(L->max_long + 1));
-  L->runtk = take(sizeof(uint32_t) * (size_t)L->max_long);
+  L->runtk = take(sizeof(uint32_t) * (size_t)L->max_items);
   L->sctk = take(sizeof(uint32_t) * (size_t)L->max_items);
-  L->part = take(sizeof(float) * (size_t)L->max_items * (size_t)p->Dmax);
+  L->part = take(sizeof(float) * (size_t)L->max_items * (size_t)kColBlock);
   L->total = align_up(o, 256);
   return SGB_OK;
 }
@@ -213,8 +216,8 @@ sgb_status sgb_plan_create(sgb_plan* out, int32_t T, const int64_t* hsc, const i
           hipSuccess &&
       cus > 0)
     p->num_cus = cus;
-  p->red_grid[0] = p->num_cus * reduce_blocks_per_cu(false);
-  p->red_grid[1] = p->num_cus * reduce_blocks_per_cu(true);
+  p->red_grid[0] = p->num_cus * reduce_long_blocks_per_cu(false);
+  p->red_grid[1] = p->num_cus * reduce_long_blocks_per_cu(true);
 
   bool ok = hipMalloc(&p->d_hsc, sizeof(int64_t) * (T + 1)) == hipSuccess &&
             hipMalloc(&p->d_doff, sizeof(int32_t) * (T + 1)) == hipSuccess &&
@@ -379,6 +382,7 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   rp.info_bits = L.info_bits;
   rp.unique_ids = at<int64_t>(ws, L.uniq);
   rp.cum = at<int32_t>(ws, L.cum);
+  rp.head_run = at<int32_t>(ws, L.headrun);
   rp.num_runs = &hdr->num_runs;
   rp.lookback = at<uint32_t>(ws, L.rle_lb);
   rp.tile_ctr = &hdr->rle_tile_ctr;
@@ -391,6 +395,9 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   pp.cum = rp.cum;
   pp.num_runs = rp.num_runs;
   pp.unique_ids = rp.unique_ids;
+  pp.hsc = p->d_hsc;
+  pp.doff = p->d_doff;
+  pp.T = p->T;
   pp.thr = p->thr;
   pp.ch_base = L.ch_base;
   pp.run_lengths = at<int32_t>(ws, L.lens);
@@ -425,10 +432,12 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   q.woff = p->d_woff;
   q.unique_ids = rp.unique_ids;
   q.cum = rp.cum;
+  q.head_run = rp.head_run;
   q.long_ids = pp.long_ids;
   q.chunk_begin = pp.chunk_begin;
   q.num_runs = rp.num_runs;
   q.total_items = pp.total_items;
+  q.num_long = &hdr->num_long;
   q.work_ctr = &hdr->work_ctr;
   q.sc_ticket = pp.sc_ticket;
   q.run_ticket = pp.run_ticket;
@@ -438,7 +447,6 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   q.status = status;
   q.N = N;
   q.row_stride = nobag ? (int64_t)p->doff[1] : (int64_t)p->doff[p->T];
-  q.slot_floats = p->Dmax;
   q.info_bits = L.info_bits;
   q.B = b->offsets ? b->B : 0;
   q.T = p->T;
@@ -450,10 +458,15 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   q.lr = u->lr;
   q.eps = u->eps;
   const bool bf16 = b->grad_dtype == SGB_BF16;
-  mark(SGB_STAGE_REDUCE, 0);
-  if (launch_reduce(q, &hdr->num_long, bf16, p->red_grid[bf16 ? 1 : 0], stream) != hipSuccess)
+  mark(SGB_STAGE_REDUCE_LONG, 0);
+  if (launch_reduce_long(q, bf16, p->red_grid[bf16 ? 1 : 0], stream) != hipSuccess)
     return SGB_ERR_HIP;
-  mark(SGB_STAGE_REDUCE, 1);
+  mark(SGB_STAGE_REDUCE_LONG, 1);
+  // dense and SGD rows are independent per 256-column block: one grid row per block
+  const int ysplit = u->mode == SGB_ROWWISE_ADAGRAD ? 1 : (p->Dmax + kColBlock - 1) / kColBlock;
+  mark(SGB_STAGE_REDUCE_SHORT, 0);
+  if (launch_reduce_short(q, bf16, ysplit, stream) != hipSuccess) return SGB_ERR_HIP;
+  mark(SGB_STAGE_REDUCE_SHORT, 1);
   return SGB_OK;
 }
 

@@ -27,8 +27,11 @@ constexpr int kScanTile = kScanThreads * kScanItems;
 
 // linearisation: bags per tile, lookups per inner step
 constexpr int kLinThreads = 256;
-constexpr int kLinBags = 512;
+constexpr int kLinBags = 64;
 constexpr int kLinLookups = 4 * kLinThreads;
+
+// short runs: sorted positions per wave of the short-run reducer
+constexpr int kShortSpan = 64;
 
 // long runs: chunk sizing and two-level combine
 constexpr int kChunkMin = 64;         // a chunk has at least this many lookups
@@ -110,6 +113,7 @@ struct RleParams {
   int32_t info_bits;
   int64_t* unique_ids;
   int32_t* cum;
+  int32_t* head_run;        // [N]: run index at each run's first position
   int32_t* num_runs;
   uint32_t* lookback;       // [tiles]
   uint32_t* tile_ctr;
@@ -120,13 +124,16 @@ struct PostParams {
   const int32_t* cum;
   const int32_t* num_runs;
   const int64_t* unique_ids;
+  const int64_t* hsc;
+  const int32_t* doff;
+  int32_t T;
   int32_t thr;
   int32_t ch_base;          // max(thr, kChunkMin)
   int32_t* run_lengths;
   int32_t* long_ids;
-  uint32_t* chunk_begin;    // [num_long + 1]
+  uint32_t* chunk_begin;    // [num_long + 1]: first (chunk, column block) item of each long run
   uint32_t* sc_ticket;      // [items]
-  uint32_t* run_ticket;     // [num_long]
+  uint32_t* run_ticket;     // [items]
   int64_t* num_long;
   uint32_t* total_items;
   uint32_t* bitmap;         // touched-row bitmap (fresh dense grad) or NULL
@@ -154,10 +161,12 @@ struct RedParams {
   const int64_t* woff;
   const int64_t* unique_ids;
   const int32_t* cum;
+  const int32_t* head_run;
   const int32_t* long_ids;
   const uint32_t* chunk_begin;
   const int32_t* num_runs;
   const uint32_t* total_items;
+  const int64_t* num_long;
   uint32_t* work_ctr;
   uint32_t* sc_ticket;
   uint32_t* run_ticket;
@@ -167,7 +176,6 @@ struct RedParams {
   uint32_t* status;
   int64_t N;
   int64_t row_stride;       // elements per grad_output row
-  int64_t slot_floats;      // floats per partial slot
   int32_t info_bits;
   int32_t B;
   int32_t T;
@@ -188,8 +196,8 @@ hipError_t launch_sort_pass(const SortParams& p, int grid, hipStream_t s);
 hipError_t launch_rle(const RleParams& p, int grid, hipStream_t s);
 hipError_t launch_post(const PostParams& p, int grid, hipStream_t s);
 hipError_t launch_fill(const FillParams& p, int nblocks, hipStream_t s);
-hipError_t launch_reduce(const RedParams& p, const int64_t* num_long, bool bf16, int grid,
-                         hipStream_t s);
-int reduce_blocks_per_cu(bool bf16);
+hipError_t launch_reduce_long(const RedParams& p, bool bf16, int grid, hipStream_t s);
+hipError_t launch_reduce_short(const RedParams& p, bool bf16, int ysplit, hipStream_t s);
+int reduce_long_blocks_per_cu(bool bf16);
 
 }  // namespace sgb

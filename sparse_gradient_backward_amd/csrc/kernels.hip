@@ -9,10 +9,11 @@
 //   k_rle        run heads of the sorted ids -> unique ids, run starts, count
 //   k_post       run lengths, ascending long-run list with chunk prefix
 //   k_fill       zeros for untouched rows of a fresh dense gradient
-//   k_reduce     persistent wave64 workers: short runs (one lane group per
-//                run) and chunks of long runs (whole wave, partials combined
-//                in a fixed order by the last arriving wave), each row
-//                finished by the fused dense / SGD / row-wise Adagrad step
+//   k_reduce_long   (chunk, column block) items of long runs from an atomic
+//                queue, partials combined in a fixed order by the last wave
+//   k_reduce_short  one wave per 64 sorted positions, short runs served one
+//                per lane group; both finish each row with the fused dense /
+//                SGD / row-wise Adagrad step
 //
 // Method: "fbgemm_gpu/codegen/embedding_backward_split_template.cu" (FBGEMM),
 // host entry `..._exact_cuda` (linearise, sort, run-length encode, long
@@ -492,6 +493,7 @@ __global__ __launch_bounds__(kScanThreads) void k_rle(RleParams p) {
       const int q = tid * kScanItems + k;
       p.unique_ids[run] = (int64_t)s_key[q + 1];
       p.cum[run] = (int32_t)(base + q);
+      p.head_run[base + q] = (int32_t)run;
       ++run;
     }
   }
@@ -507,13 +509,30 @@ __global__ __launch_bounds__(kScanThreads) void k_rle(RleParams p) {
 // Run lengths, and the long runs -- length >= thr, FBGEMM `find_long_segments`
 // -- compacted in ascending run order (the page appends them through an
 // atomic counter in arbitrary order).  Each long run is cut into chunks of
-// chunk_len() lookups; a combined scan gives every long run its first chunk
-// number.  Also clears the combine tickets of those chunks and, for a fresh
-// dense gradient, marks touched rows in a bitmap.
+// chunk_len() lookups times the 256-column blocks of its row; a combined scan
+// gives every long run its first work item.  Also clears the combine tickets
+// of those items and, for a fresh dense gradient, marks touched rows in a
+// bitmap.
 
 __device__ __forceinline__ int chunk_len(int len, int ch_base) {
   const int c = (len + kMaxChunks - 1) / kMaxChunks;
   return c > ch_base ? c : ch_base;
+}
+
+// Column blocks of 256 a row of D columns spans.
+__device__ __forceinline__ int col_blocks(int D) { return (D + kColBlock - 1) / kColBlock; }
+
+// Table of a linear id (binary search of hash_size_cumsum).
+__device__ __forceinline__ int table_of_id(const int64_t* hsc, int T, int64_t id) {
+  int lo = 0, hi = T;  // hsc[lo] <= id < hsc[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (hsc[mid] <= id)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return lo;
 }
 
 __global__ __launch_bounds__(kScanThreads) void k_post(PostParams p) {
@@ -530,18 +549,23 @@ __global__ __launch_bounds__(kScanThreads) void k_post(PostParams p) {
   if (base >= U) return;
   const int n = (int)min((int64_t)kScanTile, (int64_t)U - base);
   int len[kScanItems];
+  int ncb[kScanItems];
   uint64_t sum = 0;
 #pragma unroll
   for (int k = 0; k < kScanItems; ++k) {
     const int q = tid * kScanItems + k;
     len[k] = 0;
+    ncb[k] = 1;
     if (q < n) {
       const int64_t r = base + q;
       len[k] = p.cum[r + 1] - p.cum[r];
       p.run_lengths[r] = len[k];
       if (len[k] >= p.thr) {
+        // a long run becomes nch chunks x ncb column blocks of work items
+        const int t = table_of_id(p.hsc, p.T, p.unique_ids[r]);
+        ncb[k] = col_blocks(p.doff[t + 1] - p.doff[t]);
         const int cl = chunk_len(len[k], p.ch_base);
-        sum += (1ull << 31) | (uint64_t)((len[k] + cl - 1) / cl);
+        sum += (1ull << 31) | (uint64_t)(((len[k] + cl - 1) / cl) * ncb[k]);
       }
       if (p.bitmap) {
         const uint64_t key = (uint64_t)p.unique_ids[r];
@@ -567,9 +591,10 @@ __global__ __launch_bounds__(kScanThreads) void k_post(PostParams p) {
       const int nch = (len[k] + cl - 1) / cl;
       p.long_ids[pos] = (int32_t)(base + q);
       p.chunk_begin[pos] = c0;
-      p.run_ticket[pos] = 0u;
-      for (int s = 0; s < nch; s += kSuperChunk) p.sc_ticket[c0 + s] = 0u;
-      at += (1ull << 31) | (uint64_t)nch;
+      for (int cb = 0; cb < ncb[k]; ++cb) p.run_ticket[c0 + cb] = 0u;
+      for (int sc = 0; sc < nch; sc += kSuperChunk)
+        for (int cb = 0; cb < ncb[k]; ++cb) p.sc_ticket[c0 + sc * ncb[k] + cb] = 0u;
+      at += (1ull << 31) | (uint64_t)(nch * ncb[k]);
     }
   }
   if (tid == 0 && base + n == U) {
@@ -606,24 +631,30 @@ __global__ __launch_bounds__(256) void k_fill(FillParams p) {
   }
 }
 
-// ------------------------------------------------------------------ k_reduce
+// ------------------------------------------------------------------ reducers
 //
 // G_r[d] = sum over the lookups j of run r of coef_j * grad_output[row_j][col_t + d]
 // (FBGEMM warp-per-row / cta-per-row kernels), then the row is written once.
+// Lanes form groups of LPL lanes with 4 columns per lane (LPL = 4..64, the
+// power of two covering D/4, capped at one wave); a row wider than 256
+// columns is covered in column blocks of 256.
 //
-// Work items, fetched from one atomic queue by each wave (largest first):
-//  * chunks of long runs: the whole wave reads one chunk; for D < 256 the
-//    wave's lanes form 64/LPL groups of LPL lanes (4 columns per lane) that
-//    take interleaved lookups, and the groups are folded by a fixed xor tree.
-//    A run of several chunks writes one fp32 partial per chunk; the last
-//    wave of each group of kSuperChunk chunks (atomic ticket after a release
-//    fence) adds them in chunk order, and the last group adds the group sums
-//    in order and finishes the row -- a deterministic, atomic-free reduction
-//    across many workgroups (the page keeps a long run inside one block).
-//  * units of 64 consecutive runs: the short runs among them are served by
-//    lane groups, one run per group, so a wave carries 64/LPL rows at once.
-// Per-lookup metadata (packed word, coefficient) is read coalesced by the
-// group and broadcast lane to lane (readlane when the group is the wave).
+// k_reduce_short: one wave per 64 consecutive sorted positions.  The wave
+//   reads the packed words of its window once, finds the run heads in it
+//   (id differs from the previous position), takes each run's length from the
+//   run starts, and serves the short runs (length < thr) that start in the
+//   window, one run per lane group, so a wave carries 64/LPL rows at a time.
+//   Metadata of the window is broadcast lane to lane with the whole wave
+//   active; the row's old value is fetched before the gather so the two
+//   overlap.  Balanced by lookups, and the grid is fixed on the host.
+// k_reduce_long: persistent waves take (chunk, column block) items of the
+//   long runs from an atomic queue.  For D < 256 the wave's groups take
+//   interleaved lookups of the chunk and are folded by a fixed xor tree.  A
+//   run of several chunks writes one fp32 partial per item; the last wave of
+//   each group of kSuperChunk chunks (ticket after a release fence) adds them
+//   in chunk order, and the last group adds the group sums in order and
+//   finishes the row: a deterministic, atomic-free reduction across many
+//   workgroups (the page keeps a long run inside one block).
 
 __device__ __forceinline__ int lpl_for(int D) {
   const int need = (D + 3) >> 2;
@@ -656,8 +687,12 @@ __device__ __forceinline__ float4 load4(const void* base, int64_t elem) {
   }
 }
 
-__device__ __forceinline__ int table_of(const RedParams& p, uint32_t info0) {
-  const int t = p.nobag ? (int)(info0 % (uint32_t)p.T) : (int)(info0 / (uint32_t)p.B);
+__device__ __forceinline__ uint64_t info_mask(const RedParams& p) {
+  return p.info_bits >= 64 ? ~0ull : ((1ull << p.info_bits) - 1ull);
+}
+
+__device__ __forceinline__ int table_of(const RedParams& p, uint32_t info) {
+  const int t = p.nobag ? (int)(info % (uint32_t)p.T) : (int)(info / (uint32_t)p.B);
   return t < p.T ? t : p.T - 1;
 }
 
@@ -688,24 +723,30 @@ __device__ __forceinline__ RowDst row_dest(const RedParams& p, int t, int D, int
 
 // Sum over lookups j = first, first+step, ... < last of coef_j * grad row_j
 // at elements [colofs, colofs+4).  first/last/step are uniform within each
-// group of LPL lanes; the wave must be converged at the call.
-template <int LPL, bool BF16>
-__device__ __forceinline__ float4 gather_sum(const RedParams& p, int first, int last, int step, int t,
-                             int64_t colofs, bool col_ok) {
-  constexpr int UNR = 8;
+// group of LPL lanes.  For the first batch a lane may bring its lookup's
+// (row, coefficient) already (pre_ok); otherwise they are read here.
+template <int LPL, int UNR, bool BF16>
+__device__ __forceinline__ float4 gather_sum(const RedParams& p, int first, int last, int step,
+                                             int t, int64_t colofs, bool col_ok, int pre_row,
+                                             float pre_cf, bool pre_ok) {
   const int lane = lane_id();
   const int gb = lane & ~(LPL - 1), lig = lane & (LPL - 1);
-  const uint64_t imask = p.info_bits >= 64 ? ~0ull : ((1ull << p.info_bits) - 1ull);
+  const uint64_t imask = info_mask(p);
   const bool has_coef = p.coef != nullptr;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  bool firstb = true;
   for (int j0 = first; j0 < last; j0 += LPL * step) {
     const int jm = j0 + lig * step;
     int rowi = 0;
     float cf = 0.f;
-    if (jm < last) {
+    if (firstb && pre_ok) {
+      rowi = pre_row;
+      cf = pre_cf;
+    } else if (jm < last) {
       rowi = grad_row_of(p, (uint32_t)(p.kv[jm] & imask), t);
       cf = has_coef ? p.coef[jm] : 1.0f;
     }
+    firstb = false;
     const int cnt = min(LPL, (last - j0 + step - 1) / step);
     for (int jj = 0; jj < cnt; jj += UNR) {
       float4 v[UNR];
@@ -753,21 +794,28 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-// Finishes one row whose gradient for column block cb is getG(cb) (this
-// lane's 4 columns).  getG is called by the whole wave.  The Adagrad state
-// grows by the mean square of the row gradient, then the step uses the grown
-// state with eps outside the root (FBTT `cache_backward_rowwise_adagrad_
-// approx_kernel`), here once per distinct row.  SGD: w -= lr * G (FBTT
+__device__ __forceinline__ float4 ld4(const float* q) { return *reinterpret_cast<const float4*>(q); }
+__device__ __forceinline__ void st4(float* q, float4 v) { *reinterpret_cast<float4*>(q) = v; }
+
+// Finishes column blocks [cb_lo, cb_hi) of one row whose gradient for block
+// cb is getG(cb) (this lane's 4 columns).  getG is called by the whole wave.
+// Row-wise Adagrad: the state grows by the mean square of the row gradient,
+// then the step uses the grown state with eps outside the root (FBTT
+// `cache_backward_rowwise_adagrad_approx_kernel`), here once per distinct row
+// on the summed gradient; a row wider than 256 columns recomputes blocks
+// after its mean square is known.  SGD: w -= lr * G (FBTT
 // `cache_backward_sgd_kernel`).  Dense: store, or add for an accumulating
-// grad_weight (tinygrad `_embedding_bwd_kernel`).
+// grad_weight (tinygrad `_embedding_bwd_kernel`).  The old row value is read
+// before getG so that the read overlaps the gather.
 template <int LPL, class F>
 __device__ __forceinline__ void finish_row(const RedParams& p, const RowDst& dst, int D, bool write,
-                                           F&& getG) {
+                                           int cb_lo, int cb_hi, F&& getG) {
   const int lig = lane_id() & (LPL - 1);
-  const int ncb = LPL == 64 ? (D + kColBlock - 1) / kColBlock : 1;
   if (p.mode == kModeAdagrad) {
-    // Column block 0 stays in registers; wider rows (D > 256) get their
-    // remaining blocks recomputed after the row's mean square is known.
+    const bool w0ok = write && 4 * lig < D;
+    const float4 w0 = w0ok ? ld4(dst.out + 4 * lig) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float m0 = write ? *dst.mom : 0.f;
+    const int ncb = col_blocks(D);
     const float4 g0 = getG(0);
     float ss = 0.f;
     if (4 * lig < D) ss = g0.x * g0.x + g0.y * g0.y + g0.z * g0.z + g0.w * g0.w;
@@ -777,51 +825,55 @@ __device__ __forceinline__ void finish_row(const RedParams& p, const RowDst& dst
       if (cb * kColBlock + 4 * lig < D) ss += g.x * g.x + g.y * g.y + g.z * g.z + g.w * g.w;
     }
     ss = group_sum<LPL>(ss);
-    float m = 0.f, mult = 0.f;
-    if (write) {
-      m = *dst.mom + ss / (float)D;
-      mult = p.lr / (sqrtf(m) + p.eps);
+    const float m = m0 + ss / (float)D;
+    const float mult = p.lr / (sqrtf(m) + p.eps);
+    if (w0ok) {
+      float4 wv = w0;
+      wv.x -= mult * g0.x;
+      wv.y -= mult * g0.y;
+      wv.z -= mult * g0.z;
+      wv.w -= mult * g0.w;
+      st4(dst.out + 4 * lig, wv);
     }
 #pragma unroll 1
-    for (int cb = 0; cb < ncb; ++cb) {
-      const float4 g = cb == 0 ? g0 : getG(cb);
+    for (int cb = 1; cb < ncb; ++cb) {
+      const float4 g = getG(cb);
       const int col = cb * kColBlock + 4 * lig;
       if (write && col < D) {
-        float4* o = reinterpret_cast<float4*>(dst.out + col);
-        float4 wv = *o;
+        float4 wv = ld4(dst.out + col);
         wv.x -= mult * g.x;
         wv.y -= mult * g.y;
         wv.z -= mult * g.z;
         wv.w -= mult * g.w;
-        *o = wv;
+        st4(dst.out + col, wv);
       }
     }
     if (write && lig == 0) *dst.mom = m;
     return;
   }
+  const bool needs_old = p.mode == kModeSgd || p.accumulate;
 #pragma unroll 1
-  for (int cb = 0; cb < ncb; ++cb) {
-    const float4 g = getG(cb);
+  for (int cb = cb_lo; cb < cb_hi; ++cb) {
     const int col = cb * kColBlock + 4 * lig;
-    if (!write || col >= D) continue;
-    float4* o = reinterpret_cast<float4*>(dst.out + col);
+    const bool ok = write && col < D;
+    const float4 old = (ok && needs_old) ? ld4(dst.out + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 g = getG(cb);
+    if (!ok) continue;
+    float4 wv;
     if (p.mode == kModeSgd) {
-      float4 wv = *o;
-      wv.x -= p.lr * g.x;
-      wv.y -= p.lr * g.y;
-      wv.z -= p.lr * g.z;
-      wv.w -= p.lr * g.w;
-      *o = wv;
+      wv.x = old.x - p.lr * g.x;
+      wv.y = old.y - p.lr * g.y;
+      wv.z = old.z - p.lr * g.z;
+      wv.w = old.w - p.lr * g.w;
     } else if (p.accumulate) {
-      float4 wv = *o;
-      wv.x += g.x;
-      wv.y += g.y;
-      wv.z += g.z;
-      wv.w += g.w;
-      *o = wv;
+      wv.x = old.x + g.x;
+      wv.y = old.y + g.y;
+      wv.z = old.z + g.z;
+      wv.w = old.w + g.w;
     } else {
-      *o = g;
+      wv = g;
     }
+    st4(dst.out + col, wv);
   }
 }
 
@@ -839,19 +891,25 @@ __device__ __forceinline__ bool ticket_last(uint32_t* ctr, uint32_t members) {
   return true;
 }
 
-// Sum of `count` partial slots first, first+stride, ... (column block cb),
-// groups interleaved, folded in a fixed order.
+// Partial slot of chunk c, column block cb, of a long run whose items start
+// at slot `cbeg`: kColBlock floats each, chunk-major.
+__device__ __forceinline__ float* slot_of(const RedParams& p, uint32_t cbeg, int c, int ncb,
+                                          int cb) {
+  return p.partials + ((int64_t)cbeg + (int64_t)c * ncb + cb) * kColBlock;
+}
+
+// Sum of the partials of chunks first, first+stride, ... (count of them) for
+// column block cb, groups interleaved, folded in a fixed order.
 template <int LPL>
-__device__ __forceinline__ float4 sum_slots(const float* slot0, int64_t slot_floats, int first,
+__device__ __forceinline__ float4 sum_slots(const RedParams& p, uint32_t cbeg, int ncb, int first,
                                             int count, int stride, int cb, int D) {
   constexpr int G = 64 / LPL;
   const int lane = lane_id(), g = lane / LPL, lig = lane & (LPL - 1);
-  const int col = cb * kColBlock + 4 * lig;
+  const int col = 4 * lig;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (col < D) {
+  if (cb * kColBlock + col < D) {
     for (int i = g; i < count; i += G) {
-      const float4 v = *reinterpret_cast<const float4*>(
-          slot0 + (int64_t)(first + i * stride) * slot_floats + col);
+      const float4 v = ld4(slot_of(p, cbeg, first + i * stride, ncb, cb) + col);
       acc.x += v.x;
       acc.y += v.y;
       acc.z += v.z;
@@ -862,122 +920,153 @@ __device__ __forceinline__ float4 sum_slots(const float* slot0, int64_t slot_flo
 }
 
 template <int LPL, bool BF16>
-__device__ __forceinline__ void long_item(const RedParams& p, int k, int c, int r, int start, int len, int t,
-                          int D) {
+__device__ __forceinline__ void long_item(const RedParams& p, int k, int c, int cb, int r,
+                                          int start, int len, int t, int D) {
   constexpr int G = 64 / LPL;
   const int lane = lane_id(), g = lane / LPL, lig = lane & (LPL - 1);
+  const int ncb = col_blocks(D);
   const int chl = chunk_len(len, p.ch_base);
   const int nch = (len + chl - 1) / chl;
   const int lo = start + c * chl;
   const int hi = min(lo + chl, start + len);
-  const int ncb = LPL == 64 ? (D + kColBlock - 1) / kColBlock : 1;
+  // Adagrad needs the whole row in one wave: item cb 0 covers every block
+  const int cb_lo = p.mode == kModeAdagrad ? 0 : cb;
+  const int cb_hi = p.mode == kModeAdagrad ? ncb : cb + 1;
   const int64_t gcol = p.nobag ? 0 : p.doff[t];
   const RowDst dst = row_dest(p, t, D, p.unique_ids[r]);
-  auto chunkG = [&](int cb) {
-    const int col = cb * kColBlock + 4 * lig;
-    const float4 a = gather_sum<LPL, BF16>(p, lo + g, hi, G, t, gcol + col, col < D);
+  auto chunkG = [&](int cbx) {
+    const int col = cbx * kColBlock + 4 * lig;
+    const float4 a = gather_sum<LPL, 16, BF16>(p, lo + g, hi, G, t, gcol + col, col < D, 0, 0.f,
+                                               false);
     return fold_groups<LPL>(a);
   };
   if (nch == 1) {
-    finish_row<LPL>(p, dst, D, g == 0, chunkG);
+    finish_row<LPL>(p, dst, D, g == 0, cb_lo, cb_hi, chunkG);
     return;
   }
   const uint32_t cbeg = p.chunk_begin[k];
-  float* slot0 = p.partials + (int64_t)cbeg * p.slot_floats;
 #pragma unroll 1
-  for (int cb = 0; cb < ncb; ++cb) {
-    const float4 a = chunkG(cb);
-    const int col = cb * kColBlock + 4 * lig;
-    if (g == 0 && col < D)
-      *reinterpret_cast<float4*>(slot0 + (int64_t)c * p.slot_floats + col) = a;
+  for (int cbx = cb_lo; cbx < cb_hi; ++cbx) {
+    const float4 a = chunkG(cbx);
+    if (g == 0 && cbx * kColBlock + 4 * lig < D) st4(slot_of(p, cbeg, c, ncb, cbx) + 4 * lig, a);
   }
   const int m0 = (c / kSuperChunk) * kSuperChunk;
   const int members = min(kSuperChunk, nch - m0);
-  if (!ticket_last(p.sc_ticket + cbeg + m0, (uint32_t)members)) return;
+  if (!ticket_last(p.sc_ticket + cbeg + (int64_t)m0 * ncb + cb_lo, (uint32_t)members)) return;
   const int nsc = (nch + kSuperChunk - 1) / kSuperChunk;
   if (nsc == 1) {
-    finish_row<LPL>(p, dst, D, g == 0, [&](int cb) {
-      return sum_slots<LPL>(slot0, p.slot_floats, 0, nch, 1, cb, D);
+    finish_row<LPL>(p, dst, D, g == 0, cb_lo, cb_hi, [&](int cbx) {
+      return sum_slots<LPL>(p, cbeg, ncb, 0, nch, 1, cbx, D);
     });
     return;
   }
 #pragma unroll 1
-  for (int cb = 0; cb < ncb; ++cb) {
-    const float4 a = sum_slots<LPL>(slot0, p.slot_floats, m0, members, 1, cb, D);
-    const int col = cb * kColBlock + 4 * lig;
-    if (g == 0 && col < D)
-      *reinterpret_cast<float4*>(slot0 + (int64_t)m0 * p.slot_floats + col) = a;
+  for (int cbx = cb_lo; cbx < cb_hi; ++cbx) {
+    const float4 a = sum_slots<LPL>(p, cbeg, ncb, m0, members, 1, cbx, D);
+    if (g == 0 && cbx * kColBlock + 4 * lig < D) st4(slot_of(p, cbeg, m0, ncb, cbx) + 4 * lig, a);
   }
-  if (!ticket_last(p.run_ticket + k, (uint32_t)nsc)) return;
-  finish_row<LPL>(p, dst, D, g == 0, [&](int cb) {
-    return sum_slots<LPL>(slot0, p.slot_floats, 0, nsc, kSuperChunk, cb, D);
+  if (!ticket_last(p.run_ticket + cbeg + cb_lo, (uint32_t)nsc)) return;
+  finish_row<LPL>(p, dst, D, g == 0, cb_lo, cb_hi, [&](int cbx) {
+    return sum_slots<LPL>(p, cbeg, ncb, 0, nsc, kSuperChunk, cbx, D);
   });
 }
 
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_reduce_long(RedParams p) {
+  const int lane = lane_id();
+  const uint32_t n_items = *p.total_items;
+  const int nlong = (int)*p.num_long;
+  const uint64_t imask = info_mask(p);
+  for (;;) {
+    uint32_t w = 0;
+    if (lane == 0)
+      w = __hip_atomic_fetch_add(p.work_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    w = __builtin_amdgcn_readfirstlane(__shfl(w, 0, 64));
+    if (w >= n_items) break;
+    int lo = 0, hi = nlong;  // chunk_begin[lo] <= w < chunk_begin[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.chunk_begin[mid] <= w)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    const int k = __builtin_amdgcn_readfirstlane(lo);
+    const int r = p.long_ids[k];
+    const int start = p.cum[r], len = p.cum[r + 1] - start;
+    const int t = table_of(p, (uint32_t)(p.kv[start] & imask));
+    const int D = p.doff[t + 1] - p.doff[t];
+    const int ncb = col_blocks(D);
+    const int local = (int)(w - p.chunk_begin[k]);
+    const int c = local / ncb, cb = local % ncb;
+    if (p.mode == kModeAdagrad && cb != 0) continue;
+    switch (lpl_for(D)) {
+      case 4: long_item<4, BF16>(p, k, c, cb, r, start, len, t, D); break;
+      case 8: long_item<8, BF16>(p, k, c, cb, r, start, len, t, D); break;
+      case 16: long_item<16, BF16>(p, k, c, cb, r, start, len, t, D); break;
+      case 32: long_item<32, BF16>(p, k, c, cb, r, start, len, t, D); break;
+      default: long_item<64, BF16>(p, k, c, cb, r, start, len, t, D); break;
+    }
+  }
+}
+
+// One batch of short runs of table t: the g-th set bit of `sel` (a window
+// lane holding a run head) is served by lane group g.  Called with the whole
+// wave active.
 template <int LPL, bool BF16>
-__device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, int r, int start, int len, int t,
-                            int D) {
+__device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, int64_t base,
+                                            int len, uint64_t key, int rowi, float cf, int t,
+                                            int D, int cb) {
   const int lane = lane_id(), g = lane / LPL, lig = lane & (LPL - 1);
   uint64_t m = sel;
   for (int i = 0; i < g; ++i) m &= m - 1;
   const bool active = m != 0;
   const int src = active ? __builtin_ctzll(m) : 0;
-  // Shuffles run with the whole wave active: a source lane can sit in a group
-  // that has no run of its own, and a masked-off source would read as 0.
-  const int s = __shfl(start, src, 64);
+  // every shuffle below runs with the whole wave active: a masked-off source
+  // lane would read as 0
   const int nn = __shfl(len, src, 64);
-  const int rr = __shfl(r, src, 64);
+  const uint64_t id = __shfl(key, src, 64);
+  const int wl = src + lig;                      // window lane of this lane's first lookup
+  const int prow = __shfl(rowi, wl < 64 ? wl : 63, 64);
+  const float pcf = __shfl(cf, wl < 64 ? wl : 63, 64);
   const int n = active ? nn : 0;
+  const int s = (int)base + src;
   RowDst dst{nullptr, nullptr};
-  if (active) dst = row_dest(p, t, D, p.unique_ids[rr]);
+  if (active) dst = row_dest(p, t, D, (int64_t)id);
   const int64_t gcol = p.nobag ? 0 : p.doff[t];
-  finish_row<LPL>(p, dst, D, active, [&](int cb) {
-    const int col = cb * kColBlock + 4 * lig;
-    return gather_sum<LPL, BF16>(p, s, s + n, 1, t, gcol + col, col < D);
+  const int cb_lo = p.mode == kModeAdagrad ? 0 : cb;
+  finish_row<LPL>(p, dst, D, active, cb_lo, cb_lo + 1, [&](int cbx) {
+    const int col = cbx * kColBlock + 4 * lig;
+    return gather_sum<LPL, 4, BF16>(p, s, s + n, 1, t, gcol + col, col < D, prow, pcf,
+                                    wl < 64);
   });
 }
 
 template <bool BF16>
-__device__ __forceinline__ void do_long(const RedParams& p, uint32_t w, int nlong) {
-  int lo = 0, hi = nlong;  // chunk_begin[lo] <= w < chunk_begin[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (p.chunk_begin[mid] <= w)
-      lo = mid;
-    else
-      hi = mid;
-  }
-  const int k = __builtin_amdgcn_readfirstlane(lo);
-  const int c = (int)(w - p.chunk_begin[k]);
-  const int r = p.long_ids[k];
-  const int start = p.cum[r], len = p.cum[r + 1] - start;
-  const uint64_t imask = p.info_bits >= 64 ? ~0ull : ((1ull << p.info_bits) - 1ull);
-  const int t = table_of(p, (uint32_t)(p.kv[start] & imask));
-  const int D = p.doff[t + 1] - p.doff[t];
-  switch (lpl_for(D)) {
-    case 4: long_item<4, BF16>(p, k, c, r, start, len, t, D); break;
-    case 8: long_item<8, BF16>(p, k, c, r, start, len, t, D); break;
-    case 16: long_item<16, BF16>(p, k, c, r, start, len, t, D); break;
-    case 32: long_item<32, BF16>(p, k, c, r, start, len, t, D); break;
-    default: long_item<64, BF16>(p, k, c, r, start, len, t, D); break;
-  }
-}
-
-template <bool BF16>
-__device__ __forceinline__ void do_short(const RedParams& p, uint32_t u, int U) {
+__global__ __launch_bounds__(256) void k_reduce_short(RedParams p) {
   const int lane = lane_id();
-  const int r = (int)u * 64 + lane;
-  int start = 0, len = 0, t = 0;
-  bool todo = false;
-  if (r < U) {
-    start = p.cum[r];
-    len = p.cum[r + 1] - start;
-    todo = len < p.thr;
+  const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int cb = blockIdx.y;
+  const int64_t base = unit * kShortSpan;
+  if (base >= p.N) return;
+  const uint64_t imask = info_mask(p);
+  const int64_t pos = base + lane;
+  const bool in = pos < p.N;
+  const uint64_t kv = in ? p.kv[pos] : 0ull;
+  const uint64_t key = kv >> p.info_bits;
+  uint64_t prev = __shfl_up(key, 1, 64);
+  if (lane == 0) prev = base > 0 ? (p.kv[base - 1] >> p.info_bits) : ~0ull;
+  const bool head = in && (pos == 0 || key != prev);
+  const uint32_t info = (uint32_t)(kv & imask);
+  const int t = in ? table_of(p, info) : 0;
+  const int rowi = in ? grad_row_of(p, info, t) : 0;
+  const float cf = (in && p.coef) ? p.coef[pos] : 1.0f;
+  int len = 0;
+  if (head) {
+    const int r = p.head_run[pos];
+    len = p.cum[r + 1] - (int)pos;
   }
-  if (todo) {
-    const uint64_t imask = p.info_bits >= 64 ? ~0ull : ((1ull << p.info_bits) - 1ull);
-    t = table_of(p, (uint32_t)(p.kv[start] & imask));
-  }
+  const bool todo = head && len < p.thr;
   uint64_t pending = __ballot(todo);
   while (pending) {
     const int lead = __builtin_ctzll(pending);
@@ -992,34 +1081,15 @@ __device__ __forceinline__ void do_short(const RedParams& p, uint32_t u, int U) 
       rest ^= low;
     }
     pending &= ~sel;
+    // column block cb of this grid row; Adagrad rows are finished whole by cb 0
+    if ((p.mode == kModeAdagrad && cb != 0) || cb >= col_blocks(D)) continue;
     switch (lpl) {
-      case 4: short_batch<4, BF16>(p, sel, r, start, len, t0, D); break;
-      case 8: short_batch<8, BF16>(p, sel, r, start, len, t0, D); break;
-      case 16: short_batch<16, BF16>(p, sel, r, start, len, t0, D); break;
-      case 32: short_batch<32, BF16>(p, sel, r, start, len, t0, D); break;
-      default: short_batch<64, BF16>(p, sel, r, start, len, t0, D); break;
+      case 4: short_batch<4, BF16>(p, sel, base, len, key, rowi, cf, t0, D, cb); break;
+      case 8: short_batch<8, BF16>(p, sel, base, len, key, rowi, cf, t0, D, cb); break;
+      case 16: short_batch<16, BF16>(p, sel, base, len, key, rowi, cf, t0, D, cb); break;
+      case 32: short_batch<32, BF16>(p, sel, base, len, key, rowi, cf, t0, D, cb); break;
+      default: short_batch<64, BF16>(p, sel, base, len, key, rowi, cf, t0, D, cb); break;
     }
-  }
-}
-
-template <bool BF16>
-__global__ __launch_bounds__(256) void k_reduce(RedParams p, const int64_t* num_long) {
-  const int lane = lane_id();
-  const int U = *p.num_runs;
-  const uint32_t n_items = *p.total_items;
-  const int nlong = (int)*num_long;
-  const uint32_t n_units = (uint32_t)((U + 63) / 64);
-  const uint32_t total = n_items + n_units;
-  for (;;) {
-    uint32_t w = 0;
-    if (lane == 0)
-      w = __hip_atomic_fetch_add(p.work_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    w = __builtin_amdgcn_readfirstlane(__shfl(w, 0, 64));
-    if (w >= total) break;
-    if (w < n_items)
-      do_long<BF16>(p, w, nlong);
-    else
-      do_short<BF16>(p, w - n_items, U);
   }
 }
 
@@ -1061,19 +1131,28 @@ hipError_t launch_fill(const FillParams& p, int nblocks, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_reduce(const RedParams& p, const int64_t* num_long, bool bf16, int grid,
-                         hipStream_t s) {
+hipError_t launch_reduce_long(const RedParams& p, bool bf16, int grid, hipStream_t s) {
   if (bf16)
-    hipLaunchKernelGGL(k_reduce<true>, dim3(grid), dim3(256), 0, s, p, num_long);
+    hipLaunchKernelGGL(k_reduce_long<true>, dim3(grid), dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL(k_reduce<false>, dim3(grid), dim3(256), 0, s, p, num_long);
+    hipLaunchKernelGGL(k_reduce_long<false>, dim3(grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
-int reduce_blocks_per_cu(bool bf16) {
+hipError_t launch_reduce_short(const RedParams& p, bool bf16, int ysplit, hipStream_t s) {
+  const int64_t units = (p.N + kShortSpan - 1) / kShortSpan;
+  const dim3 grid((unsigned)((units + 3) / 4), (unsigned)ysplit);
+  if (bf16)
+    hipLaunchKernelGGL(k_reduce_short<true>, grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(k_reduce_short<false>, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+int reduce_long_blocks_per_cu(bool bf16) {
   int n = 0;
-  hipError_t e = bf16 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_reduce<true>, 256, 0)
-                      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_reduce<false>, 256, 0);
+  hipError_t e = bf16 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_reduce_long<true>, 256, 0)
+                      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_reduce_long<false>, 256, 0);
   return (e == hipSuccess && n > 0) ? n : 2;
 }
 
