@@ -18,7 +18,8 @@ from typing import Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsgb.so")
+# SGB_LIBRARY selects another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("SGB_LIBRARY") or os.path.join(_HERE, "libsgb.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "sgb.h")
 
 if not os.path.exists(LIB_PATH):

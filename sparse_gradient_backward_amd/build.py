@@ -33,10 +33,11 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libsgb.so (always recompiles)."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *FLAGS, *SOURCES, "-o", tmp]
+def build(verbose: bool = False, out: str = LIB, defines: tuple = ()) -> str:
+    """Compile every source into libsgb.so (always recompiles).  `defines`
+    (e.g. ("SGB_SHORT_UNR=2",)) override the tuning knobs of internal.h."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *FLAGS, *[f"-D{d}" for d in defines], *SOURCES, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -47,9 +48,14 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("-o", "--out", default=LIB)
+    ap.add_argument("-D", dest="defines", action="append", default=[])
+    a = ap.parse_args()
+    print(build(verbose=True, out=a.out, defines=tuple(a.defines)))

@@ -77,7 +77,7 @@ struct Layout {
   size_t hdr = 0, hist = 0, zero_begin = 0, sort_lb = 0, rle_lb = 0, post_lb = 0, bitmap = 0,
          zero_end_nobitmap = 0, zero_end_bitmap = 0;
   size_t kvA = 0, kvB = 0, coefA = 0, coefB = 0, uniq = 0, cum = 0, headrun = 0, lens = 0, longs = 0,
-         chunkb = 0, runtk = 0, sctk = 0, part = 0, total = 0;
+         chunkb = 0, longrec = 0, runtk = 0, sctk = 0, part = 0, total = 0;
 };
 
 sgb_status make_layout(const sgb_plan_s* p, int64_t N, int32_t B, bool has_offsets, Layout* L) {
@@ -135,6 +135,7 @@ sgb_status make_layout(const sgb_plan_s* p, int64_t N, int32_t B, bool has_offse
   L->headrun = take(sizeof(int32_t) * (size_t)N);
   L->lens = take(sizeof(int32_t) * (size_t)N);
   L->longs = take(sizeof(int32_t) * (size_t)L->max_long);
+  L->longrec = take(sizeof(LongRun) * (size_t)L->max_long);
   L->chunkb = take(sizeof(uint32_t) * (size_t)(L->max_long + 1));
   L->runtk = take(sizeof(uint32_t) * (size_t)L->max_items);
   L->sctk = take(sizeof(uint32_t) * (size_t)L->max_items);
@@ -403,6 +404,7 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   pp.run_lengths = at<int32_t>(ws, L.lens);
   pp.long_ids = at<int32_t>(ws, L.longs);
   pp.chunk_begin = at<uint32_t>(ws, L.chunkb);
+  pp.long_recs = at<LongRun>(ws, L.longrec);
   pp.sc_ticket = at<uint32_t>(ws, L.sctk);
   pp.run_ticket = at<uint32_t>(ws, L.runtk);
   pp.num_long = &hdr->num_long;
@@ -435,6 +437,7 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   q.head_run = rp.head_run;
   q.long_ids = pp.long_ids;
   q.chunk_begin = pp.chunk_begin;
+  q.long_recs = pp.long_recs;
   q.num_runs = rp.num_runs;
   q.total_items = pp.total_items;
   q.num_long = &hdr->num_long;
@@ -462,8 +465,8 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   if (launch_reduce_long(q, bf16, p->red_grid[bf16 ? 1 : 0], stream) != hipSuccess)
     return SGB_ERR_HIP;
   mark(SGB_STAGE_REDUCE_LONG, 1);
-  // dense and SGD rows are independent per 256-column block: one grid row per block
-  const int ysplit = u->mode == SGB_ROWWISE_ADAGRAD ? 1 : (p->Dmax + kColBlock - 1) / kColBlock;
+  // short rows wider than 1024 columns (dense / SGD only): one grid row per block
+  const int ysplit = (p->Dmax + kShortBlock - 1) / kShortBlock;
   mark(SGB_STAGE_REDUCE_SHORT, 0);
   if (launch_reduce_short(q, bf16, ysplit, stream) != hipSuccess) return SGB_ERR_HIP;
   mark(SGB_STAGE_REDUCE_SHORT, 1);

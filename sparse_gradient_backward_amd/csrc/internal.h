@@ -15,9 +15,23 @@ constexpr int kMaxCb = 4;             // Adagrad rows held in registers: D <= 4 
 constexpr int kColBlock = 256;        // columns one wave covers per pass (64 lanes x 4)
 constexpr int kMaxD = 8192;
 
+// Tuning knobs (compile-time; the defaults are the measured best).
+#ifndef SGB_SORT_ITEMS
+#define SGB_SORT_ITEMS 16
+#endif
+#ifndef SGB_SHORT_UNR
+#define SGB_SHORT_UNR 2
+#endif
+#ifndef SGB_LONG_UNR
+#define SGB_LONG_UNR 8
+#endif
+#ifndef SGB_CHUNK_MIN
+#define SGB_CHUNK_MIN 64
+#endif
+
 // sort pass tiling
 constexpr int kSortThreads = 256;
-constexpr int kSortItems = 16;
+constexpr int kSortItems = SGB_SORT_ITEMS;
 constexpr int kSortTile = kSortThreads * kSortItems;
 
 // run-length encoding / run post-processing tiling
@@ -34,7 +48,7 @@ constexpr int kLinLookups = 4 * kLinThreads;
 constexpr int kShortSpan = 64;
 
 // long runs: chunk sizing and two-level combine
-constexpr int kChunkMin = 64;         // a chunk has at least this many lookups
+constexpr int kChunkMin = SGB_CHUNK_MIN;  // a chunk has at least this many lookups
 constexpr int kMaxChunks = 2048;      // a run is cut into at most this many chunks
 constexpr int kSuperChunk = 32;       // chunks combined per first-level ticket
 
@@ -62,6 +76,21 @@ struct Header {
   uint32_t pad[15];
 };
 static_assert(sizeof(Header) <= 128, "header too large");
+
+// A long run as the long-run reducer needs it (written by k_post).
+struct LongRun {
+  int32_t start;   // first sorted position
+  int32_t len;     // lookups
+  int32_t t;       // table
+  int32_t ncb;     // 256-column blocks of its row
+  uint32_t cbeg;   // first work item / partial slot
+  int32_t nch;     // chunks
+  int64_t id;      // linear row id
+};
+
+// Columns per lane in the short-run reducer, and the row width one wave covers.
+constexpr int kShortCpl = 16;
+constexpr int kShortBlock = 64 * kShortCpl;
 
 // A block of rows of one table that the dense zero-fill covers.
 struct FillBlock {
@@ -132,6 +161,7 @@ struct PostParams {
   int32_t* run_lengths;
   int32_t* long_ids;
   uint32_t* chunk_begin;    // [num_long + 1]: first (chunk, column block) item of each long run
+  LongRun* long_recs;       // [num_long]
   uint32_t* sc_ticket;      // [items]
   uint32_t* run_ticket;     // [items]
   int64_t* num_long;
@@ -164,6 +194,7 @@ struct RedParams {
   const int32_t* head_run;
   const int32_t* long_ids;
   const uint32_t* chunk_begin;
+  const LongRun* long_recs;
   const int32_t* num_runs;
   const uint32_t* total_items;
   const int64_t* num_long;

@@ -591,6 +591,15 @@ __global__ __launch_bounds__(kScanThreads) void k_post(PostParams p) {
       const int nch = (len[k] + cl - 1) / cl;
       p.long_ids[pos] = (int32_t)(base + q);
       p.chunk_begin[pos] = c0;
+      LongRun rec;
+      rec.start = p.cum[base + q];
+      rec.len = len[k];
+      rec.t = table_of_id(p.hsc, p.T, p.unique_ids[base + q]);
+      rec.ncb = ncb[k];
+      rec.cbeg = c0;
+      rec.nch = nch;
+      rec.id = p.unique_ids[base + q];
+      p.long_recs[pos] = rec;
       for (int cb = 0; cb < ncb[k]; ++cb) p.run_ticket[c0 + cb] = 0u;
       for (int sc = 0; sc < nch; sc += kSuperChunk)
         for (int cb = 0; cb < ncb[k]; ++cb) p.sc_ticket[c0 + sc * ncb[k] + cb] = 0u;
@@ -651,10 +660,10 @@ __global__ __launch_bounds__(256) void k_fill(FillParams p) {
 //   long runs from an atomic queue.  For D < 256 the wave's groups take
 //   interleaved lookups of the chunk and are folded by a fixed xor tree.  A
 //   run of several chunks writes one fp32 partial per item; the last wave of
-//   each group of kSuperChunk chunks (ticket after a release fence) adds them
-//   in chunk order, and the last group adds the group sums in order and
-//   finishes the row: a deterministic, atomic-free reduction across many
-//   workgroups (the page keeps a long run inside one block).
+//   each group of kSuperChunk chunks (arrival ticket) adds them in chunk
+//   order, and the last group adds the group sums in order and finishes the
+//   row: a deterministic reduction across many workgroups without float
+//   atomics (the page keeps a long run inside one block).
 
 __device__ __forceinline__ int lpl_for(int D) {
   const int need = (D + 3) >> 2;
@@ -877,18 +886,40 @@ __device__ __forceinline__ void finish_row(const RedParams& p, const RowDst& dst
   }
 }
 
-// Last-arrival ticket: publishes this wave's prior global writes (release),
-// counts the arrival, and reports whether this wave completes the group; if
-// so its later reads see every member's writes (acquire).
+// Partials travel between waves on different XCDs.  They are written and read
+// with device-scope (agent) atomic accesses, which the hardware keeps coherent
+// across the XCDs' L2 caches by themselves; an agent-scope release/acquire
+// fence pair would instead write back and invalidate a whole L2 per ticket,
+// which measured as most of the long-run kernel's time.
+__device__ __forceinline__ void store_partial(float* q, float4 v) {
+  const uint64_t lo = (uint64_t)__float_as_uint(v.x) | ((uint64_t)__float_as_uint(v.y) << 32);
+  const uint64_t hi = (uint64_t)__float_as_uint(v.z) | ((uint64_t)__float_as_uint(v.w) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(q), lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(q) + 1, hi, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float4 load_partial(const float* q) {
+  uint64_t* u = reinterpret_cast<uint64_t*>(const_cast<float*>(q));
+  const uint64_t lo = __hip_atomic_load(u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t hi = __hip_atomic_load(u + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float4(__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+                     __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32)));
+}
+
+// Last-arrival ticket: waits until this wave's partial stores have completed
+// (s_waitcnt vmcnt(0): on this architecture the vector-memory counter also
+// covers stores), counts the arrival with a device-scope atomic, and reports
+// whether this wave completes the group.  The caller reads the members'
+// partials only after this returns true, i.e. after the atomic's result came
+// back, with device-scope loads.
 __device__ __forceinline__ bool ticket_last(uint32_t* ctr, uint32_t members) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) expcnt(7) lgkmcnt(15)
   uint32_t old = 0;
   if (lane_id() == 0)
     old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   old = __shfl(old, 0, 64);
-  if (old + 1 != members) return false;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return true;
+  return old + 1 == members;
 }
 
 // Partial slot of chunk c, column block cb, of a long run whose items start
@@ -909,7 +940,7 @@ __device__ __forceinline__ float4 sum_slots(const RedParams& p, uint32_t cbeg, i
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (cb * kColBlock + col < D) {
     for (int i = g; i < count; i += G) {
-      const float4 v = ld4(slot_of(p, cbeg, first + i * stride, ncb, cb) + col);
+      const float4 v = load_partial(slot_of(p, cbeg, first + i * stride, ncb, cb) + col);
       acc.x += v.x;
       acc.y += v.y;
       acc.z += v.z;
@@ -920,23 +951,24 @@ __device__ __forceinline__ float4 sum_slots(const RedParams& p, uint32_t cbeg, i
 }
 
 template <int LPL, bool BF16>
-__device__ __forceinline__ void long_item(const RedParams& p, int k, int c, int cb, int r,
-                                          int start, int len, int t, int D) {
+__device__ __forceinline__ void long_item(const RedParams& p, const LongRun& rec, int c, int cb,
+                                          int D) {
   constexpr int G = 64 / LPL;
   const int lane = lane_id(), g = lane / LPL, lig = lane & (LPL - 1);
-  const int ncb = col_blocks(D);
+  const int t = rec.t, start = rec.start, len = rec.len;
+  const int ncb = rec.ncb;
   const int chl = chunk_len(len, p.ch_base);
-  const int nch = (len + chl - 1) / chl;
+  const int nch = rec.nch;
   const int lo = start + c * chl;
   const int hi = min(lo + chl, start + len);
   // Adagrad needs the whole row in one wave: item cb 0 covers every block
   const int cb_lo = p.mode == kModeAdagrad ? 0 : cb;
   const int cb_hi = p.mode == kModeAdagrad ? ncb : cb + 1;
   const int64_t gcol = p.nobag ? 0 : p.doff[t];
-  const RowDst dst = row_dest(p, t, D, p.unique_ids[r]);
+  const RowDst dst = row_dest(p, t, D, rec.id);
   auto chunkG = [&](int cbx) {
     const int col = cbx * kColBlock + 4 * lig;
-    const float4 a = gather_sum<LPL, 16, BF16>(p, lo + g, hi, G, t, gcol + col, col < D, 0, 0.f,
+    const float4 a = gather_sum<LPL, SGB_LONG_UNR, BF16>(p, lo + g, hi, G, t, gcol + col, col < D, 0, 0.f,
                                                false);
     return fold_groups<LPL>(a);
   };
@@ -944,11 +976,11 @@ __device__ __forceinline__ void long_item(const RedParams& p, int k, int c, int 
     finish_row<LPL>(p, dst, D, g == 0, cb_lo, cb_hi, chunkG);
     return;
   }
-  const uint32_t cbeg = p.chunk_begin[k];
+  const uint32_t cbeg = rec.cbeg;
 #pragma unroll 1
   for (int cbx = cb_lo; cbx < cb_hi; ++cbx) {
     const float4 a = chunkG(cbx);
-    if (g == 0 && cbx * kColBlock + 4 * lig < D) st4(slot_of(p, cbeg, c, ncb, cbx) + 4 * lig, a);
+    if (g == 0 && cbx * kColBlock + 4 * lig < D) store_partial(slot_of(p, cbeg, c, ncb, cbx) + 4 * lig, a);
   }
   const int m0 = (c / kSuperChunk) * kSuperChunk;
   const int members = min(kSuperChunk, nch - m0);
@@ -963,7 +995,8 @@ __device__ __forceinline__ void long_item(const RedParams& p, int k, int c, int 
 #pragma unroll 1
   for (int cbx = cb_lo; cbx < cb_hi; ++cbx) {
     const float4 a = sum_slots<LPL>(p, cbeg, ncb, m0, members, 1, cbx, D);
-    if (g == 0 && cbx * kColBlock + 4 * lig < D) st4(slot_of(p, cbeg, m0, ncb, cbx) + 4 * lig, a);
+    if (g == 0 && cbx * kColBlock + 4 * lig < D)
+      store_partial(slot_of(p, cbeg, m0, ncb, cbx) + 4 * lig, a);
   }
   if (!ticket_last(p.run_ticket + cbeg + cb_lo, (uint32_t)nsc)) return;
   finish_row<LPL>(p, dst, D, g == 0, cb_lo, cb_hi, [&](int cbx) {
@@ -971,48 +1004,117 @@ __device__ __forceinline__ void long_item(const RedParams& p, int k, int c, int 
   });
 }
 
+// Index k of the long run holding work item w: chunk_begin[k] <= w <
+// chunk_begin[k+1].  A 64-way search: every lane probes one point of the
+// interval, so each round shrinks it 64-fold (2 rounds for 4096 runs).
+__device__ __forceinline__ int find_long_run(const uint32_t* cbeg, int nlong, uint32_t w) {
+  const int lane = lane_id();
+  int lo = 0, hi = nlong;
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 63) / 64;
+    const int probe = lo + lane * step;
+    const bool le = probe < hi && cbeg[probe] <= w;
+    const uint64_t m = __ballot(le);
+    const int last = 63 - __builtin_clzll(m);  // lane 0 always qualifies
+    lo = lo + last * step;
+    hi = min(lo + step, hi);
+  }
+  return __builtin_amdgcn_readfirstlane(lo);
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_reduce_long(RedParams p) {
-  const int lane = lane_id();
   const uint32_t n_items = *p.total_items;
   const int nlong = (int)*p.num_long;
-  const uint64_t imask = info_mask(p);
-  for (;;) {
-    uint32_t w = 0;
-    if (lane == 0)
-      w = __hip_atomic_fetch_add(p.work_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    w = __builtin_amdgcn_readfirstlane(__shfl(w, 0, 64));
-    if (w >= n_items) break;
-    int lo = 0, hi = nlong;  // chunk_begin[lo] <= w < chunk_begin[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (p.chunk_begin[mid] <= w)
-        lo = mid;
-      else
-        hi = mid;
-    }
-    const int k = __builtin_amdgcn_readfirstlane(lo);
-    const int r = p.long_ids[k];
-    const int start = p.cum[r], len = p.cum[r + 1] - start;
-    const int t = table_of(p, (uint32_t)(p.kv[start] & imask));
+  // items are dealt round-robin: consecutive chunks of a hot run go to
+  // different waves, and no shared counter is contended
+  const uint32_t nw = gridDim.x * (blockDim.x / 64);
+  for (uint32_t w = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6); w < n_items; w += nw) {
+    const int k = find_long_run(p.chunk_begin, nlong, w);
+    const LongRun rec = p.long_recs[k];
+    const int t = rec.t;
     const int D = p.doff[t + 1] - p.doff[t];
-    const int ncb = col_blocks(D);
-    const int local = (int)(w - p.chunk_begin[k]);
-    const int c = local / ncb, cb = local % ncb;
+    const int local = (int)(w - rec.cbeg);
+    const int c = local / rec.ncb, cb = local % rec.ncb;
     if (p.mode == kModeAdagrad && cb != 0) continue;
     switch (lpl_for(D)) {
-      case 4: long_item<4, BF16>(p, k, c, cb, r, start, len, t, D); break;
-      case 8: long_item<8, BF16>(p, k, c, cb, r, start, len, t, D); break;
-      case 16: long_item<16, BF16>(p, k, c, cb, r, start, len, t, D); break;
-      case 32: long_item<32, BF16>(p, k, c, cb, r, start, len, t, D); break;
-      default: long_item<64, BF16>(p, k, c, cb, r, start, len, t, D); break;
+      case 4: long_item<4, BF16>(p, rec, c, cb, D); break;
+      case 8: long_item<8, BF16>(p, rec, c, cb, D); break;
+      case 16: long_item<16, BF16>(p, rec, c, cb, D); break;
+      case 32: long_item<32, BF16>(p, rec, c, cb, D); break;
+      default: long_item<64, BF16>(p, rec, c, cb, D); break;
+    }
+  }
+}
+
+// Lanes per group for a short row: 16 columns per lane, a power of two, at
+// most one wave (1024 columns); wider rows are done in 1024-column blocks.
+__device__ __forceinline__ int lpl16_for(int D) {
+  const int need = (D + kShortCpl - 1) / kShortCpl;
+  int l = 1;
+  while (l < need && l < 64) l <<= 1;
+  return l;
+}
+
+// Sum over lookups first .. last-1 of coef_j * grad row_j at this lane's 16
+// columns: 4-column piece i sits at element colofs + 4 * LPL * i, so each load
+// instruction of a group reads one contiguous span (valid pieces: vmask).
+// Uniform within each group of LPL lanes.  The first batch's metadata may
+// come from the window (pre_ok).
+template <int LPL, int UNR, bool BF16>
+__device__ __forceinline__ void gather16(const RedParams& p, int first, int last, int t,
+                                         int64_t colofs, int vmask, int pre_row, float pre_cf,
+                                         bool pre_ok, float4 (&acc)[4]) {
+  const int lane = lane_id();
+  const int gb = lane & ~(LPL - 1), lig = lane & (LPL - 1);
+  const uint64_t imask = info_mask(p);
+  const bool has_coef = p.coef != nullptr;
+  bool firstb = true;
+  for (int j0 = first; j0 < last; j0 += LPL) {
+    const int jm = j0 + lig;
+    int rowi = 0;
+    float cf = 0.f;
+    if (firstb && pre_ok) {
+      rowi = pre_row;
+      cf = pre_cf;
+    } else if (jm < last) {
+      rowi = grad_row_of(p, (uint32_t)(p.kv[jm] & imask), t);
+      cf = has_coef ? p.coef[jm] : 1.0f;
+    }
+    firstb = false;
+    const int cnt = min(LPL, last - j0);
+    for (int jj = 0; jj < cnt; jj += UNR) {
+      float4 v[UNR][4];
+      float c[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int src = (LPL == 64 ? 0 : gb) + min(jj + u, LPL - 1);
+        const int ro = bcast_i<LPL>(rowi, src);
+        c[u] = jj + u < cnt ? bcast_f<LPL>(cf, src) : 0.f;
+        const bool ok = jj + u < cnt;
+        const int64_t e = (int64_t)ro * p.row_stride + colofs;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v[u][i] = (ok && ((vmask >> i) & 1)) ? load4<BF16>(p.grad, e + 4 * LPL * i)
+                                               : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[i].x = fmaf(c[u], v[u][i].x, acc[i].x);
+          acc[i].y = fmaf(c[u], v[u][i].y, acc[i].y);
+          acc[i].z = fmaf(c[u], v[u][i].z, acc[i].z);
+          acc[i].w = fmaf(c[u], v[u][i].w, acc[i].w);
+        }
     }
   }
 }
 
 // One batch of short runs of table t: the g-th set bit of `sel` (a window
-// lane holding a run head) is served by lane group g.  Called with the whole
-// wave active.
+// lane holding a run head) is served by lane group g, 16 columns per lane, in
+// 1024-column block cb.  Called with the whole wave active.  The row's old
+// value (and Adagrad state) is read before the gather so the reads overlap.
 template <int LPL, bool BF16>
 __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, int64_t base,
                                             int len, uint64_t key, int rowi, float cf, int t,
@@ -1026,20 +1128,71 @@ __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, in
   // lane would read as 0
   const int nn = __shfl(len, src, 64);
   const uint64_t id = __shfl(key, src, 64);
-  const int wl = src + lig;                      // window lane of this lane's first lookup
+  const int wl = src + lig;  // window lane of this lane's first lookup
   const int prow = __shfl(rowi, wl < 64 ? wl : 63, 64);
   const float pcf = __shfl(cf, wl < 64 ? wl : 63, 64);
   const int n = active ? nn : 0;
   const int s = (int)base + src;
+  // this lane's columns: col + 4 * LPL * i for pieces i = 0..3 (striped)
+  const int col = cb * kShortBlock + 4 * lig;
+  int vmask = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (active && col + 4 * LPL * i < D) vmask |= 1 << i;
   RowDst dst{nullptr, nullptr};
   if (active) dst = row_dest(p, t, D, (int64_t)id);
-  const int64_t gcol = p.nobag ? 0 : p.doff[t];
-  const int cb_lo = p.mode == kModeAdagrad ? 0 : cb;
-  finish_row<LPL>(p, dst, D, active, cb_lo, cb_lo + 1, [&](int cbx) {
-    const int col = cbx * kColBlock + 4 * lig;
-    return gather_sum<LPL, 4, BF16>(p, s, s + n, 1, t, gcol + col, col < D, prow, pcf,
-                                    wl < 64);
-  });
+  const bool needs_old = p.mode != kModeDense || p.accumulate;
+  float4 old[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    old[i] = (needs_old && ((vmask >> i) & 1)) ? ld4(dst.out + col + 4 * LPL * i)
+                                              : make_float4(0.f, 0.f, 0.f, 0.f);
+  const float m0 = (p.mode == kModeAdagrad && active) ? *dst.mom : 0.f;
+  float4 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int64_t gcol = (p.nobag ? 0 : p.doff[t]) + col;
+  gather16<LPL, SGB_SHORT_UNR, BF16>(p, s, s + n, t, gcol, vmask, prow, pcf, wl < 64, acc);
+  if (p.mode == kModeAdagrad) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      ss += acc[i].x * acc[i].x + acc[i].y * acc[i].y + acc[i].z * acc[i].z + acc[i].w * acc[i].w;
+    ss = group_sum<LPL>(ss);
+    const float mm = m0 + ss / (float)D;
+    const float mult = p.lr / (sqrtf(mm) + p.eps);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if ((vmask >> i) & 1) {
+        float4 w = old[i];
+        w.x -= mult * acc[i].x;
+        w.y -= mult * acc[i].y;
+        w.z -= mult * acc[i].z;
+        w.w -= mult * acc[i].w;
+        st4(dst.out + col + 4 * LPL * i, w);
+      }
+    if (active && lig == 0) *dst.mom = mm;
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (!((vmask >> i) & 1)) continue;
+    float4 w;
+    if (p.mode == kModeSgd) {
+      w.x = old[i].x - p.lr * acc[i].x;
+      w.y = old[i].y - p.lr * acc[i].y;
+      w.z = old[i].z - p.lr * acc[i].z;
+      w.w = old[i].w - p.lr * acc[i].w;
+    } else if (p.accumulate) {
+      w.x = old[i].x + acc[i].x;
+      w.y = old[i].y + acc[i].y;
+      w.z = old[i].z + acc[i].z;
+      w.w = old[i].w + acc[i].w;
+    } else {
+      w = acc[i];
+    }
+    st4(dst.out + col + 4 * LPL * i, w);
+  }
 }
 
 template <bool BF16>
@@ -1073,7 +1226,7 @@ __global__ __launch_bounds__(256) void k_reduce_short(RedParams p) {
     const int t0 = __builtin_amdgcn_readfirstlane(__shfl(t, lead, 64));
     const uint64_t same = __ballot(todo && t == t0) & pending;
     const int D = p.doff[t0 + 1] - p.doff[t0];
-    const int lpl = lpl_for(D);
+    const int lpl = lpl16_for(D);
     uint64_t sel = 0, rest = same;
     for (int i = 0; i < 64 / lpl && rest; ++i) {
       const uint64_t low = rest & (~rest + 1ull);
@@ -1081,9 +1234,10 @@ __global__ __launch_bounds__(256) void k_reduce_short(RedParams p) {
       rest ^= low;
     }
     pending &= ~sel;
-    // column block cb of this grid row; Adagrad rows are finished whole by cb 0
-    if ((p.mode == kModeAdagrad && cb != 0) || cb >= col_blocks(D)) continue;
+    if (cb * kShortBlock >= D) continue;  // this grid row's column block is past the row
     switch (lpl) {
+      case 1: short_batch<1, BF16>(p, sel, base, len, key, rowi, cf, t0, D, cb); break;
+      case 2: short_batch<2, BF16>(p, sel, base, len, key, rowi, cf, t0, D, cb); break;
       case 4: short_batch<4, BF16>(p, sel, base, len, key, rowi, cf, t0, D, cb); break;
       case 8: short_batch<8, BF16>(p, sel, base, len, key, rowi, cf, t0, D, cb); break;
       case 16: short_batch<16, BF16>(p, sel, base, len, key, rowi, cf, t0, D, cb); break;
