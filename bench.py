@@ -243,7 +243,7 @@ def main():
         log("timing the CPU oracle")
         cpu = cpu_baseline(inp, spec, thr, args.cpu_min_s, args.cpu_max_reps)
 
-    kernel_names = {"reduce_long": "k_reduce_long", "reduce_short": "k_reduce_short",
+    kernel_names = {"reduce_long": "k_reduce_long", "reduce_short": "k_reduce_short8/16",
                     "sort": "k_sort_pass", "fill": "k_fill", "linearize": "k_linearize",
                     "rle": "k_rle", "runs": "k_post", "init": "k_init"}
     res = {

@@ -465,10 +465,8 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   if (launch_reduce_long(q, bf16, p->red_grid[bf16 ? 1 : 0], stream) != hipSuccess)
     return SGB_ERR_HIP;
   mark(SGB_STAGE_REDUCE_LONG, 1);
-  // short rows wider than 1024 columns (dense / SGD only): one grid row per block
-  const int ysplit = (p->Dmax + kShortBlock - 1) / kShortBlock;
   mark(SGB_STAGE_REDUCE_SHORT, 0);
-  if (launch_reduce_short(q, bf16, ysplit, stream) != hipSuccess) return SGB_ERR_HIP;
+  if (launch_reduce_short(q, bf16, p->Dmax, stream) != hipSuccess) return SGB_ERR_HIP;
   mark(SGB_STAGE_REDUCE_SHORT, 1);
   return SGB_OK;
 }

@@ -88,10 +88,6 @@ struct LongRun {
   int64_t id;      // linear row id
 };
 
-// Columns per lane in the short-run reducer, and the row width one wave covers.
-constexpr int kShortCpl = 16;
-constexpr int kShortBlock = 64 * kShortCpl;
-
 // A block of rows of one table that the dense zero-fill covers.
 struct FillBlock {
   int32_t t;
@@ -228,7 +224,7 @@ hipError_t launch_rle(const RleParams& p, int grid, hipStream_t s);
 hipError_t launch_post(const PostParams& p, int grid, hipStream_t s);
 hipError_t launch_fill(const FillParams& p, int nblocks, hipStream_t s);
 hipError_t launch_reduce_long(const RedParams& p, bool bf16, int grid, hipStream_t s);
-hipError_t launch_reduce_short(const RedParams& p, bool bf16, int ysplit, hipStream_t s);
+hipError_t launch_reduce_short(const RedParams& p, bool bf16, int dmax, hipStream_t s);
 int reduce_long_blocks_per_cu(bool bf16);
 
 }  // namespace sgb

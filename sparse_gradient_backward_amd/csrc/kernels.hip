@@ -1047,84 +1047,36 @@ __global__ __launch_bounds__(256) void k_reduce_long(RedParams p) {
   }
 }
 
-// Lanes per group for a short row: 16 columns per lane, a power of two, at
-// most one wave (1024 columns); wider rows are done in 1024-column blocks.
-__device__ __forceinline__ int lpl16_for(int D) {
-  const int need = (D + kShortCpl - 1) / kShortCpl;
+// Short runs, CPL columns per lane (8, or 16 for rows wider than 512): lane
+// groups of lpl lanes, lpl = the power of two covering D / CPL, at most one
+// wave.  The group width is a runtime value so that one code path (and one
+// register budget) serves every row width.
+template <int CPL>
+__device__ __forceinline__ int short_lpl(int D) {
+  const int need = (D + CPL - 1) / CPL;
   int l = 1;
   while (l < need && l < 64) l <<= 1;
   return l;
 }
 
-// Sum over lookups first .. last-1 of coef_j * grad row_j at this lane's 16
-// columns: 4-column piece i sits at element colofs + 4 * LPL * i, so each load
-// instruction of a group reads one contiguous span (valid pieces: vmask).
-// Uniform within each group of LPL lanes.  The first batch's metadata may
-// come from the window (pre_ok).
-template <int LPL, int UNR, bool BF16>
-__device__ __forceinline__ void gather16(const RedParams& p, int first, int last, int t,
-                                         int64_t colofs, int vmask, int pre_row, float pre_cf,
-                                         bool pre_ok, float4 (&acc)[4]) {
-  const int lane = lane_id();
-  const int gb = lane & ~(LPL - 1), lig = lane & (LPL - 1);
-  const uint64_t imask = info_mask(p);
-  const bool has_coef = p.coef != nullptr;
-  bool firstb = true;
-  for (int j0 = first; j0 < last; j0 += LPL) {
-    const int jm = j0 + lig;
-    int rowi = 0;
-    float cf = 0.f;
-    if (firstb && pre_ok) {
-      rowi = pre_row;
-      cf = pre_cf;
-    } else if (jm < last) {
-      rowi = grad_row_of(p, (uint32_t)(p.kv[jm] & imask), t);
-      cf = has_coef ? p.coef[jm] : 1.0f;
-    }
-    firstb = false;
-    const int cnt = min(LPL, last - j0);
-    for (int jj = 0; jj < cnt; jj += UNR) {
-      float4 v[UNR][4];
-      float c[UNR];
-#pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        const int src = (LPL == 64 ? 0 : gb) + min(jj + u, LPL - 1);
-        const int ro = bcast_i<LPL>(rowi, src);
-        c[u] = jj + u < cnt ? bcast_f<LPL>(cf, src) : 0.f;
-        const bool ok = jj + u < cnt;
-        const int64_t e = (int64_t)ro * p.row_stride + colofs;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          v[u][i] = (ok && ((vmask >> i) & 1)) ? load4<BF16>(p.grad, e + 4 * LPL * i)
-                                               : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int u = 0; u < UNR; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[i].x = fmaf(c[u], v[u][i].x, acc[i].x);
-          acc[i].y = fmaf(c[u], v[u][i].y, acc[i].y);
-          acc[i].z = fmaf(c[u], v[u][i].z, acc[i].z);
-          acc[i].w = fmaf(c[u], v[u][i].w, acc[i].w);
-        }
-    }
-  }
-}
-
 // One batch of short runs of table t: the g-th set bit of `sel` (a window
-// lane holding a run head) is served by lane group g, 16 columns per lane, in
-// 1024-column block cb.  Called with the whole wave active.  The row's old
-// value (and Adagrad state) is read before the gather so the reads overlap.
-template <int LPL, bool BF16>
-__device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, int64_t base,
+// lane holding a run head) is served by lane group g (lpl lanes), CPL columns
+// per lane in pieces of 4 striped across the group (piece i at column
+// col + 4 * lpl * i), in the CPL*64-column block cb.  Called with the whole
+// wave active.  The row's old value and Adagrad state are read before the
+// gather so that the reads overlap.
+template <int CPL, bool BF16>
+__device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, int lpl, int64_t base,
                                             int len, uint64_t key, int rowi, float cf, int t,
                                             int D, int cb) {
-  const int lane = lane_id(), g = lane / LPL, lig = lane & (LPL - 1);
+  constexpr int NP = CPL / 4;
+  const int lg = __builtin_ctz(lpl);
+  const int lane = lane_id(), g = lane >> lg, lig = lane & (lpl - 1), gb = g << lg;
   uint64_t m = sel;
   for (int i = 0; i < g; ++i) m &= m - 1;
   const bool active = m != 0;
   const int src = active ? __builtin_ctzll(m) : 0;
-  // every shuffle below runs with the whole wave active: a masked-off source
+  // every shuffle here runs with the whole wave active: a masked-off source
   // lane would read as 0
   const int nn = __shfl(len, src, 64);
   const uint64_t id = __shfl(key, src, 64);
@@ -1133,49 +1085,90 @@ __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, in
   const float pcf = __shfl(cf, wl < 64 ? wl : 63, 64);
   const int n = active ? nn : 0;
   const int s = (int)base + src;
-  // this lane's columns: col + 4 * LPL * i for pieces i = 0..3 (striped)
-  const int col = cb * kShortBlock + 4 * lig;
+  const int col = cb * 64 * CPL + 4 * lig;
   int vmask = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (active && col + 4 * LPL * i < D) vmask |= 1 << i;
+  for (int i = 0; i < NP; ++i)
+    if (active && col + 4 * lpl * i < D) vmask |= 1 << i;
   RowDst dst{nullptr, nullptr};
   if (active) dst = row_dest(p, t, D, (int64_t)id);
   const bool needs_old = p.mode != kModeDense || p.accumulate;
-  float4 old[4];
+  float4 old[NP], acc[NP];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    old[i] = (needs_old && ((vmask >> i) & 1)) ? ld4(dst.out + col + 4 * LPL * i)
+  for (int i = 0; i < NP; ++i) {
+    old[i] = (needs_old && ((vmask >> i) & 1)) ? ld4(dst.out + col + 4 * lpl * i)
                                               : make_float4(0.f, 0.f, 0.f, 0.f);
+    acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   const float m0 = (p.mode == kModeAdagrad && active) ? *dst.mom : 0.f;
-  float4 acc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   const int64_t gcol = (p.nobag ? 0 : p.doff[t]) + col;
-  gather16<LPL, SGB_SHORT_UNR, BF16>(p, s, s + n, t, gcol, vmask, prow, pcf, wl < 64, acc);
+  const uint64_t imask = info_mask(p);
+  const bool has_coef = p.coef != nullptr;
+  // lookups s .. s+n-1 of this group's run, lpl at a time; the first lpl
+  // lookups' metadata comes from the window when it lies inside it
+  bool firstb = true;
+  for (int j0 = s; j0 < s + n; j0 += lpl) {
+    const int jm = j0 + lig;
+    int ri = 0;
+    float ci = 0.f;
+    if (firstb && wl < 64) {
+      ri = prow;
+      ci = pcf;
+    } else if (jm < s + n) {
+      ri = grad_row_of(p, (uint32_t)(p.kv[jm] & imask), t);
+      ci = has_coef ? p.coef[jm] : 1.0f;
+    }
+    firstb = false;
+    const int cnt = min(lpl, s + n - j0);
+    for (int jj = 0; jj < cnt; jj += SGB_SHORT_UNR) {
+      float4 v[SGB_SHORT_UNR][NP];
+      float c[SGB_SHORT_UNR];
+#pragma unroll
+      for (int u = 0; u < SGB_SHORT_UNR; ++u) {
+        const int srcl = gb + min(jj + u, lpl - 1);
+        const bool ok = jj + u < cnt;
+        const int ro = __shfl(ri, srcl, 64);
+        c[u] = ok ? __shfl(ci, srcl, 64) : 0.f;
+        const int64_t e = (int64_t)ro * p.row_stride + gcol;
+#pragma unroll
+        for (int i = 0; i < NP; ++i)
+          v[u][i] = (ok && ((vmask >> i) & 1)) ? load4<BF16>(p.grad, e + 4 * lpl * i)
+                                               : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < SGB_SHORT_UNR; ++u)
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          acc[i].x = fmaf(c[u], v[u][i].x, acc[i].x);
+          acc[i].y = fmaf(c[u], v[u][i].y, acc[i].y);
+          acc[i].z = fmaf(c[u], v[u][i].z, acc[i].z);
+          acc[i].w = fmaf(c[u], v[u][i].w, acc[i].w);
+        }
+    }
+  }
   if (p.mode == kModeAdagrad) {
     float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NP; ++i)
       ss += acc[i].x * acc[i].x + acc[i].y * acc[i].y + acc[i].z * acc[i].z + acc[i].w * acc[i].w;
-    ss = group_sum<LPL>(ss);
+    for (int off = lpl >> 1; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
     const float mm = m0 + ss / (float)D;
     const float mult = p.lr / (sqrtf(mm) + p.eps);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NP; ++i)
       if ((vmask >> i) & 1) {
         float4 w = old[i];
         w.x -= mult * acc[i].x;
         w.y -= mult * acc[i].y;
         w.z -= mult * acc[i].z;
         w.w -= mult * acc[i].w;
-        st4(dst.out + col + 4 * LPL * i, w);
+        st4(dst.out + col + 4 * lpl * i, w);
       }
     if (active && lig == 0) *dst.mom = mm;
     return;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NP; ++i) {
     if (!((vmask >> i) & 1)) continue;
     float4 w;
     if (p.mode == kModeSgd) {
@@ -1191,12 +1184,19 @@ __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, in
     } else {
       w = acc[i];
     }
-    st4(dst.out + col + 4 * LPL * i, w);
+    st4(dst.out + col + 4 * lpl * i, w);
   }
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(256) void k_reduce_short(RedParams p) {
+// One wave per 64 sorted positions.  Run heads are where the id changes; a
+// run's length is the distance to the next head in the window, and only a run
+// that reaches the window's end looks its length up (run index at the head,
+// run starts).  Short runs (length < thr) starting in the window are served
+// in batches of 64/lpl runs of one table.  Rows wider than 512 columns are
+// served by the CPL = 16 instance; the CPL = 8 instance skips them, and the
+// reverse.
+template <int CPL, bool BF16>
+__device__ __forceinline__ void reduce_short(const RedParams& p) {
   const int lane = lane_id();
   const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int cb = blockIdx.y;
@@ -1210,14 +1210,22 @@ __global__ __launch_bounds__(256) void k_reduce_short(RedParams p) {
   uint64_t prev = __shfl_up(key, 1, 64);
   if (lane == 0) prev = base > 0 ? (p.kv[base - 1] >> p.info_bits) : ~0ull;
   const bool head = in && (pos == 0 || key != prev);
+  const uint64_t heads = __ballot(head);
+  if (heads == 0) return;
   const uint32_t info = (uint32_t)(kv & imask);
   const int t = in ? table_of(p, info) : 0;
   const int rowi = in ? grad_row_of(p, info, t) : 0;
   const float cf = (in && p.coef) ? p.coef[pos] : 1.0f;
+  // length to the next head in the window; the run of the last head may go on
+  const uint64_t after = lane < 63 ? (heads & (~0ull << (lane + 1))) : 0ull;
   int len = 0;
   if (head) {
-    const int r = p.head_run[pos];
-    len = p.cum[r + 1] - (int)pos;
+    if (after) {
+      len = __builtin_ctzll(after) - lane;
+    } else {
+      const int r = p.head_run[pos];
+      len = p.cum[r + 1] - (int)pos;
+    }
   }
   const bool todo = head && len < p.thr;
   uint64_t pending = __ballot(todo);
@@ -1226,7 +1234,7 @@ __global__ __launch_bounds__(256) void k_reduce_short(RedParams p) {
     const int t0 = __builtin_amdgcn_readfirstlane(__shfl(t, lead, 64));
     const uint64_t same = __ballot(todo && t == t0) & pending;
     const int D = p.doff[t0 + 1] - p.doff[t0];
-    const int lpl = lpl16_for(D);
+    const int lpl = short_lpl<CPL>(D);
     uint64_t sel = 0, rest = same;
     for (int i = 0; i < 64 / lpl && rest; ++i) {
       const uint64_t low = rest & (~rest + 1ull);
@@ -1234,17 +1242,23 @@ __global__ __launch_bounds__(256) void k_reduce_short(RedParams p) {
       rest ^= low;
     }
     pending &= ~sel;
-    if (cb * kShortBlock >= D) continue;  // this grid row's column block is past the row
-    switch (lpl) {
-      case 1: short_batch<1, BF16>(p, sel, base, len, key, rowi, cf, t0, D, cb); break;
-      case 2: short_batch<2, BF16>(p, sel, base, len, key, rowi, cf, t0, D, cb); break;
-      case 4: short_batch<4, BF16>(p, sel, base, len, key, rowi, cf, t0, D, cb); break;
-      case 8: short_batch<8, BF16>(p, sel, base, len, key, rowi, cf, t0, D, cb); break;
-      case 16: short_batch<16, BF16>(p, sel, base, len, key, rowi, cf, t0, D, cb); break;
-      case 32: short_batch<32, BF16>(p, sel, base, len, key, rowi, cf, t0, D, cb); break;
-      default: short_batch<64, BF16>(p, sel, base, len, key, rowi, cf, t0, D, cb); break;
-    }
+    const bool mine = CPL == 16 ? D > 512 : D <= 512;  // rows of the other instance
+    if (!mine || cb * 64 * CPL >= D) continue;
+    short_batch<CPL, BF16>(p, sel, lpl, base, len, key, rowi, cf, t0, D, cb);
   }
+}
+
+// 8 columns per lane fits 64 VGPRs: 8 waves per SIMD to overlap the runs'
+// dependent memory steps.
+template <bool BF16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void k_reduce_short8(RedParams p) {
+  reduce_short<8, BF16>(p);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_reduce_short16(RedParams p) {
+  reduce_short<16, BF16>(p);
 }
 
 }  // namespace
@@ -1293,13 +1307,26 @@ hipError_t launch_reduce_long(const RedParams& p, bool bf16, int grid, hipStream
   return hipGetLastError();
 }
 
-hipError_t launch_reduce_short(const RedParams& p, bool bf16, int ysplit, hipStream_t s) {
+hipError_t launch_reduce_short(const RedParams& p, bool bf16, int dmax, hipStream_t s) {
   const int64_t units = (p.N + kShortSpan - 1) / kShortSpan;
-  const dim3 grid((unsigned)((units + 3) / 4), (unsigned)ysplit);
-  if (bf16)
-    hipLaunchKernelGGL(k_reduce_short<true>, grid, dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(k_reduce_short<false>, grid, dim3(256), 0, s, p);
+  const unsigned gx = (unsigned)((units + 3) / 4);
+  {
+    // rows up to 512 columns: 8 columns per lane, one wave per row at most
+    const dim3 grid(gx, 1);
+    if (bf16)
+      hipLaunchKernelGGL(k_reduce_short8<true>, grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL(k_reduce_short8<false>, grid, dim3(256), 0, s, p);
+  }
+  if (dmax > 512) {
+    // wider rows: 16 columns per lane in 1024-column blocks (dense / SGD may
+    // have several; Adagrad rows are at most 1024 wide)
+    const dim3 grid(gx, (unsigned)((dmax + 1023) / 1024));
+    if (bf16)
+      hipLaunchKernelGGL(k_reduce_short16<true>, grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL(k_reduce_short16<false>, grid, dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 
