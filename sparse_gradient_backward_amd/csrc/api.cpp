@@ -96,6 +96,7 @@ sgb_status make_layout(const sgb_plan_s* p, int64_t N, int32_t B, bool has_offse
   L->info_bits = bitlen(info_max);
   if (L->info_bits + p->key_bits > 64) return SGB_ERR_UNSUPPORTED;
   L->npasses = (p->key_bits + 8) / 9;
+  if (L->npasses > kMaxPasses) return SGB_ERR_UNSUPPORTED;  // linear ids >= 2^36
   int at = 0;
   for (int i = 0; i < L->npasses; ++i) {
     L->pass_bits[i] = p->key_bits / L->npasses + (i < p->key_bits % L->npasses ? 1 : 0);
@@ -183,7 +184,7 @@ sgb_status sgb_plan_create(sgb_plan* out, int32_t T, const int64_t* hsc, const i
     if (D < 4 || D > kMaxD || D % 4 != 0) return SGB_ERR_INVALID_ARGUMENT;
     if (pooling == SGB_POOL_NONE && D != doff[1] - doff[0]) return SGB_ERR_INVALID_ARGUMENT;
   }
-  if (hsc[T] >= (1ll << 62)) return SGB_ERR_UNSUPPORTED;
+  if (hsc[T] > (1ll << 36)) return SGB_ERR_UNSUPPORTED;  // linear ids must fit 4 radix passes
 
   sgb_plan_s* p = new (std::nothrow) sgb_plan_s();
   if (!p) return SGB_ERR_HIP;

@@ -9,7 +9,8 @@
 namespace sgb {
 
 // ---------------------------------------------------------------- limits
-constexpr int kMaxPasses = 7;         // LSD passes of <= 9 bits: up to 63 key bits
+constexpr int kMaxPasses = 4;         // LSD passes of <= 9 bits: linear ids below 2^36
+constexpr int kHistPasses = kMaxPasses;
 constexpr int kRadixMax = 512;        // 9-bit digits
 constexpr int kMaxCb = 4;             // Adagrad rows held in registers: D <= 4 * 256
 constexpr int kColBlock = 256;        // columns one wave covers per pass (64 lanes x 4)

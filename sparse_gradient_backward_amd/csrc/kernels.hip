@@ -46,6 +46,14 @@ __device__ __forceinline__ void set_status(uint32_t* st, uint32_t code) {
   atomicCAS(st, 0u, code);
 }
 
+// Records `code` if any lane of the wave has `bad`, with one atomic per wave
+// (an error path must not turn into millions of same-address atomics).
+// Wave-uniform call.
+__device__ __forceinline__ void set_status_wave(uint32_t* st, uint32_t code, bool bad) {
+  const uint64_t m = __ballot(bad);
+  if (m && lane_id() == __builtin_ctzll(m)) set_status(st, code);
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_incl_scan(T x) {
   const int lane = lane_id();
@@ -141,19 +149,6 @@ __device__ W wave_lookback(W* lb, uint32_t tile, W agg, uint32_t* status) {
   return excl;
 }
 
-// Adds 1 for this lane's digit to an LDS histogram, aggregated over the lanes
-// of the wave holding the same digit (ballot match), so a hot Zipf digit costs
-// one LDS atomic per wave instead of 64 conflicting ones.  Wave-uniform call.
-__device__ __forceinline__ void hist_add(uint32_t* h, uint32_t digit, int bits, bool valid) {
-  uint64_t peers = __ballot(valid);
-  for (int b = 0; b < bits; ++b) {
-    const bool bit = (digit >> b) & 1u;
-    const uint64_t m = __ballot(bit);
-    peers &= bit ? m : ~m;
-  }
-  if (valid && bits_below(peers) == 0) atomicAdd(&h[digit], (uint32_t)__popcll(peers));
-}
-
 // ------------------------------------------------------------------ k_init
 
 __global__ void k_init(uint4* p, int64_t n) {
@@ -181,20 +176,24 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
   __shared__ int64_t s_off[kLinBags + 1];
   __shared__ int32_t s_t[kLinBags];
   __shared__ float s_scale[kLinBags];
-  __shared__ uint32_t s_hist[kMaxPasses * kRadixMax];
+  // one digit histogram per wave and pass (conflicting LDS atomics stay
+  // within a wave), summed when the block is done
+  __shared__ uint32_t s_hist[kLinThreads / 64][kHistPasses * kRadixMax];
   __shared__ int s_bad;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wv = tid >> 6;
 
   for (int64_t q = blockIdx.x * (int64_t)kLinThreads + tid; q < p.zero_vec4;
        q += (int64_t)gridDim.x * kLinThreads)
     p.zero_begin[q] = make_uint4(0u, 0u, 0u, 0u);
-  for (int i = tid; i < p.npasses * kRadixMax; i += kLinThreads) s_hist[i] = 0u;
+  for (int i = tid; i < (kLinThreads / 64) * kHistPasses * kRadixMax; i += kLinThreads)
+    (&s_hist[0][0])[i] = 0u;
   __syncthreads();
 
   auto histogram = [&](uint64_t key, bool valid) {
+    if (!valid) return;
     for (int ps = 0; ps < p.npasses; ++ps) {
       const uint32_t d = (uint32_t)(key >> p.pass_shift[ps]) & ((1u << p.pass_bits[ps]) - 1u);
-      hist_add(s_hist + ps * kRadixMax, d, p.pass_bits[ps], valid);
+      atomicAdd(&s_hist[wv][ps * kRadixMax + d], 1u);
     }
   };
 
@@ -207,15 +206,17 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
         const int64_t i = tile * kLinLookups + k * kLinThreads + tid;
         const bool valid = i < p.N;
         uint64_t key = 0;
+        bool bad = false;
         if (valid) {
           int64_t idx = p.indices[i];
           if (idx < 0 || idx >= E) {
-            set_status(p.status, kStIndex);
+            bad = true;
             idx = idx < 0 ? 0 : E - 1;
           }
           key = (uint64_t)idx;
           p.kv_out[i] = (key << p.info_bits) | (uint64_t)i;
         }
+        set_status_wave(p.status, kStIndex, bad);
         histogram(key, valid);
       }
     }
@@ -260,6 +261,7 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
           const int64_t i = c + k * kLinThreads + tid;
           const bool valid = i < i1;
           uint64_t key = 0;
+          bool bad = false;
           if (valid) {
             int lo = 0, hi = nb;  // s_off[lo] <= i < s_off[hi]
             while (hi - lo > 1) {
@@ -273,7 +275,7 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
             const int64_t h0 = p.hsc[t], E = p.hsc[t + 1] - h0;
             int64_t idx = p.indices[i];
             if (idx < 0 || idx >= E) {
-              set_status(p.status, kStIndex);
+              bad = true;
               idx = idx < 0 ? 0 : E - 1;
             }
             key = (uint64_t)(h0 + idx);
@@ -282,6 +284,7 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
             p.kv_out[i] = (key << p.info_bits) | info;
             if (p.coef_out) p.coef_out[i] = s_scale[lo] * (p.psw ? p.psw[i] : 1.0f);
           }
+          set_status_wave(p.status, kStIndex, bad);
           histogram(key, valid);
         }
       }
@@ -290,7 +293,9 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
   }
   __syncthreads();
   for (int i = tid; i < p.npasses * kRadixMax; i += kLinThreads) {
-    const uint32_t v = s_hist[i];
+    uint32_t v = 0;
+#pragma unroll
+    for (int w = 0; w < kLinThreads / 64; ++w) v += s_hist[w][i];
     if (v) atomicAdd(&p.hist[i], v);
   }
 }
@@ -403,47 +408,95 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_pass(SortParams p) {
       if (has_coef) s_coef[pos] = cf[k];
     }
   }
-  // per digit look-back for the offset of this tile's digit group
+  // per digit look-back for the offset of this tile's digit group: each
+  // round reads kLookAhead preceding tiles for both of this thread's digits
+  // at once, sums aggregates back to the nearest inclusive prefix, and only
+  // waits when one of the tiles it needs has published nothing yet
+  {
+    constexpr int kLookAhead = 4;
+    uint32_t excl[2] = {0u, 0u};
+    bool done[2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int d = 2 * tid + h;
-    if (d >= radix) continue;
-    uint32_t excl = 0;
-    if (tile > 0) {
-      int64_t j = (int64_t)tile - 1;
-      uint32_t spins = 0;
-      while (j >= 0) {
-        const uint32_t v = __hip_atomic_load(&p.lookback[(size_t)j * kRadixMax + d],
-                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t flag = v >> 30;
-        if (flag == 0) {
-          if (++spins > kSpinLimit) {
-            set_status(p.status, kStInternal);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-          continue;
+    for (int h = 0; h < 2; ++h) done[h] = (2 * tid + h >= radix) || tile == 0;
+    int64_t top[2] = {(int64_t)tile - 1, (int64_t)tile - 1};
+    uint32_t spins = 0;
+    while (!(done[0] && done[1])) {
+      uint32_t v[2][kLookAhead];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int k = 0; k < kLookAhead; ++k) {
+          const int64_t j = top[h] - k;
+          v[h][k] = (!done[h] && j >= 0)
+                        ? __hip_atomic_load(&p.lookback[(size_t)j * kRadixMax + 2 * tid + h],
+                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                        : kFlagP32;  // before tile 0: prefix 0
         }
-        excl += v & kVal32;
-        if (flag == 2) break;
-        --j;
+      bool waiting = false;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (done[h]) continue;
+        uint32_t sum = 0;
+        int used = kLookAhead;
+        bool found = false, notready = false;
+#pragma unroll
+        for (int k = 0; k < kLookAhead; ++k) {
+          if (found || notready) continue;
+          const uint32_t flag = v[h][k] >> 30;
+          if (flag == 0) {
+            notready = true;
+            used = k;
+          } else {
+            sum += v[h][k] & kVal32;
+            if (flag == 2) found = true;
+          }
+        }
+        // tiles before the first not-ready one are consumed either way
+        if (found) {
+          excl[h] += sum;
+          done[h] = true;
+        } else if (!notready) {
+          excl[h] += sum;
+          top[h] -= kLookAhead;
+        } else {
+          uint32_t part = 0;
+#pragma unroll
+          for (int k = 0; k < kLookAhead; ++k)
+            if (k < used) part += v[h][k] & kVal32;
+          excl[h] += part;
+          top[h] -= used;
+          waiting = true;
+        }
       }
-      __hip_atomic_store(&p.lookback[(size_t)tile * kRadixMax + d], kFlagP32 | (excl + cnt[h]),
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (waiting) {
+        if (++spins > kSpinLimit) {
+          set_status(p.status, kStInternal);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
     }
-    s_gbase[d] = (int32_t)(s_dglob[d] + excl) - (int32_t)s_local[d];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int d = 2 * tid + h;
+      if (d >= radix) continue;
+      if (tile > 0)
+        __hip_atomic_store(&p.lookback[(size_t)tile * kRadixMax + d], kFlagP32 | (excl[h] + cnt[h]),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_gbase[d] = (int32_t)(s_dglob[d] + excl[h]) - (int32_t)s_local[d];
+    }
   }
   __syncthreads();
   for (int q = tid; q < tile_n; q += kSortThreads) {
     const uint64_t v = s_kv[q];
     const uint32_t d = (uint32_t)((v >> p.shift) & dmask);
     const int64_t pos = (int64_t)s_gbase[d] + q;
-    if (pos >= 0 && pos < p.N) {
+    const bool okp = pos >= 0 && pos < p.N;
+    if (okp) {
       p.kv_out[pos] = v;
       if (has_coef) p.coef_out[pos] = s_coef[q];
-    } else {
-      set_status(p.status, kStInternal);
     }
+    set_status_wave(p.status, kStInternal, !okp);
   }
 }
 
