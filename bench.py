@@ -32,6 +32,10 @@ import synth  # noqa: E402
 METRIC = "embedding-bwd lookups/sec + achieved HBM GB/s (% of MI355X peak), 1 GPU"
 HBM_PEAK_GBPS = 8000.0
 STAGES = ("init", "linearize", "sort", "rle", "runs", "fill", "reduce_long", "reduce_short")
+KERNEL_SOURCES = ("sparse_gradient_backward_amd/csrc/kernels.hip",
+                  "sparse_gradient_backward_amd/csrc/internal.h",
+                  "sparse_gradient_backward_amd/csrc/api.cpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
 
 
 def log(*a):
@@ -40,10 +44,9 @@ def log(*a):
 
 def stage_bytes(inp: synth.Inputs, spec: synth.Spec, U: int, run_D: np.ndarray,
                 run_len: np.ndarray, thr: int, npasses: int):
-    """Algorithmic bytes each stage must move (one call), by the byte model of
-    the design doc: every input read once, every output written once, the sorted
-    stream written and read once per radix pass, each run's gather and row
-    update once."""
+    """Algorithmic bytes each stage must move (one call): every input read
+    once, every output written once, the sorted stream written and read once
+    per radix pass, each run's gather and row update once."""
     N = inp.N
     c = 1 if (spec.pooling == "mean" or spec.weighted) else 0
     sg = 2 if spec.grad_dtype == "bf16" else 4
@@ -86,6 +89,35 @@ def stage_bytes(inp: synth.Inputs, spec: synth.Spec, U: int, run_D: np.ndarray,
     return b, b_path
 
 
+def kernel_digest() -> str:
+    """Short hash of the kernel and launch sources: counter figures taken on
+    other sources no longer describe these kernels."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:12]
+
+
+def measured_traffic(workload: str, stage: str):
+    """HBM bytes per launch of one stage's kernel(s), from the FETCH_SIZE and
+    WRITE_SIZE counter runs recorded in profiles/pmc_traffic.txt (already
+    scaled by the copy-kernel calibration), or None when no figure exists for
+    the current kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    src = kernel_digest()
+    for line in open(TRAFFIC_FILE):
+        f = line.split()
+        if len(f) < 4 or f[0] != "traffic" or f[1] != workload or f[2] != stage:
+            continue
+        kv = dict(x.split("=", 1) for x in f[3:])
+        if kv.get("src") == src:
+            return float(kv["fetch_bytes"]) + float(kv["write_bytes"])
+    return None
+
+
 def cpu_baseline(inp: synth.Inputs, spec: synth.Spec, thr: int, min_s: float, max_reps: int):
     """The CPU oracle as it stands (plain C, single thread) on the same batch."""
     import oracle
@@ -123,7 +155,7 @@ def main():
                     help="max_segment_length_per_warp (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-min-s", type=float, default=10.0)
-    ap.add_argument("--cpu-max-reps", type=int, default=20)
+    ap.add_argument("--cpu-max-reps", type=int, default=2000)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (the reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -272,10 +304,11 @@ def main():
         "ms_per_step_instrumented": ms_timed,
         "roofline": {"bound": "hbm", "kernel": kernel_names[dom], "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None, "bytes_per_launch": int(per_launch_bytes),
+                     "traffic": measured_traffic(spec.name, dom), "bytes_per_launch": int(per_launch_bytes),
                      "launch_ms": per_launch_ms},
         "cpu_baseline": cpu,
         "device_status": status,
+        "kernel_src": kernel_digest(),
     }
     print(json.dumps(res), flush=True)
 

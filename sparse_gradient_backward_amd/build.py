@@ -20,7 +20,7 @@ ARCH = os.environ.get("SGB_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-    # packed fp32 VALU ops disabled on this target (build notes)
+    # packed fp32 VALU ops are kept out of the generated code on this target
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
