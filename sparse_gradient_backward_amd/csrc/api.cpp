@@ -25,6 +25,10 @@ struct sgb_plan_s {
   int32_t pooling = 0;
   int32_t thr = 1;
   int32_t Dmax = 0;
+  int32_t Dmin = 0;
+  // bound on (chunk, column block) items per lookup of a long run:
+  // max over tables of col_blocks(D) / chunk_min(D), as a fraction
+  int64_t items_num = 0, items_den = 1;
   int64_t total_rows = 0;   // sum of E_t
   int64_t total_elems = 0;  // sum of E_t * D_t
   int key_bits = 0;
@@ -73,7 +77,6 @@ struct Layout {
   int64_t sort_tiles = 0, scan_tiles = 0;
   int64_t max_long = 0;   // bound on the number of long runs
   int64_t max_items = 0;  // bound on the (chunk, column block) items over all long runs
-  int32_t ch_base = 0;
   size_t hdr = 0, hist = 0, zero_begin = 0, sort_lb = 0, rle_lb = 0, post_lb = 0, bitmap = 0,
          zero_end_nobitmap = 0, zero_end_bitmap = 0;
   size_t kvA = 0, kvB = 0, coefA = 0, coefB = 0, uniq = 0, cum = 0, headrun = 0, lens = 0, longs = 0,
@@ -105,11 +108,11 @@ sgb_status make_layout(const sgb_plan_s* p, int64_t N, int32_t B, bool has_offse
   }
   L->sort_tiles = (N + kSortTile - 1) / kSortTile;
   L->scan_tiles = (N + kScanTile - 1) / kScanTile;
-  L->ch_base = std::max<int32_t>(p->thr, kChunkMin);
   L->max_long = N / p->thr + 1;
-  // chunks over long runs <= N / ch_base + number of long runs; each chunk
-  // spans at most ceil(Dmax / 256) column blocks
-  L->max_items = (N / L->ch_base + L->max_long + 1) * ((p->Dmax + kColBlock - 1) / kColBlock);
+  // a long run of len lookups in a table of width D has ceil(len / chunk_len)
+  // <= len / chunk_min(D) + 1 chunks of col_blocks(D) items each
+  L->max_items = (N * p->items_num + p->items_den - 1) / p->items_den +
+                 (L->max_long + 1) * col_blocks(p->Dmax);
 
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -140,7 +143,7 @@ sgb_status make_layout(const sgb_plan_s* p, int64_t N, int32_t B, bool has_offse
   L->chunkb = take(sizeof(uint32_t) * (size_t)(L->max_long + 1));
   L->runtk = take(sizeof(uint32_t) * (size_t)L->max_items);
   L->sctk = take(sizeof(uint32_t) * (size_t)L->max_items);
-  L->part = take(sizeof(float) * (size_t)L->max_items * (size_t)kColBlock);
+  L->part = take(sizeof(double) * (size_t)L->max_items * (size_t)kColBlock);
   L->total = align_up(o, 256);
   return SGB_OK;
 }
@@ -203,6 +206,12 @@ sgb_status sgb_plan_create(sgb_plan* out, int32_t T, const int64_t* hsc, const i
     const int64_t E = hsc[t + 1] - hsc[t];
     const int32_t D = doff[t + 1] - doff[t];
     p->Dmax = std::max(p->Dmax, D);
+    p->Dmin = t == 0 ? D : std::min(p->Dmin, D);
+    const int64_t num = col_blocks(D), den = chunk_min(D);
+    if (num * p->items_den > p->items_num * den) {
+      p->items_num = num;
+      p->items_den = den;
+    }
     p->woff[t + 1] = p->woff[t] + E * D;
     const int64_t rows_per = std::max<int64_t>(1, 16384 / D);
     for (int64_t r0 = 0; r0 < E; r0 += rows_per)
@@ -401,7 +410,6 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   pp.doff = p->d_doff;
   pp.T = p->T;
   pp.thr = p->thr;
-  pp.ch_base = L.ch_base;
   pp.run_lengths = at<int32_t>(ws, L.lens);
   pp.long_ids = at<int32_t>(ws, L.longs);
   pp.chunk_begin = at<uint32_t>(ws, L.chunkb);
@@ -445,7 +453,7 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   q.work_ctr = &hdr->work_ctr;
   q.sc_ticket = pp.sc_ticket;
   q.run_ticket = pp.run_ticket;
-  q.partials = at<float>(ws, L.part);
+  q.partials = at<double>(ws, L.part);
   q.out = out;
   q.mom = u->mode == SGB_ROWWISE_ADAGRAD ? u->momentum : nullptr;
   q.status = status;
@@ -456,7 +464,6 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   q.T = p->T;
   q.nobag = nobag ? 1 : 0;
   q.thr = p->thr;
-  q.ch_base = L.ch_base;
   q.mode = u->mode;
   q.accumulate = u->accumulate ? 1 : 0;
   q.lr = u->lr;
@@ -467,7 +474,7 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
     return SGB_ERR_HIP;
   mark(SGB_STAGE_REDUCE_LONG, 1);
   mark(SGB_STAGE_REDUCE_SHORT, 0);
-  if (launch_reduce_short(q, bf16, p->Dmax, stream) != hipSuccess) return SGB_ERR_HIP;
+  if (launch_reduce_short(q, bf16, p->Dmin, p->Dmax, stream) != hipSuccess) return SGB_ERR_HIP;
   mark(SGB_STAGE_REDUCE_SHORT, 1);
   return SGB_OK;
 }

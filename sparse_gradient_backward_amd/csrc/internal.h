@@ -26,8 +26,20 @@ constexpr int kMaxD = 8192;
 #ifndef SGB_LONG_UNR
 #define SGB_LONG_UNR 8
 #endif
-#ifndef SGB_CHUNK_MIN
-#define SGB_CHUNK_MIN 64
+#ifndef SGB_CHUNK_BASE
+#define SGB_CHUNK_BASE 256
+#endif
+#ifndef SGB_CHUNK_FLOOR
+#define SGB_CHUNK_FLOOR 128
+#endif
+#ifndef SGB_SHORT_SUB8
+#define SGB_SHORT_SUB8 1
+#endif
+#ifndef SGB_SHORT_SUB16
+#define SGB_SHORT_SUB16 2
+#endif
+#ifndef SGB_SHORT8_WAVES
+#define SGB_SHORT8_WAVES 6
 #endif
 
 // sort pass tiling
@@ -45,13 +57,45 @@ constexpr int kLinThreads = 256;
 constexpr int kLinBags = 64;
 constexpr int kLinLookups = 4 * kLinThreads;
 
-// short runs: sorted positions per wave of the short-run reducer
+// short runs: sorted positions of one window of the short-run reducer, and
+// log2 of the waves sharing a window (each serves the runs starting in its
+// part), for rows up to 512 columns and for wider rows
 constexpr int kShortSpan = 64;
+constexpr int kShortSub8 = SGB_SHORT_SUB8;
+constexpr int kShortSub16 = SGB_SHORT_SUB16;
+static_assert(kShortSub8 >= 0 && kShortSub8 <= 6 && kShortSub16 >= 0 && kShortSub16 <= 6,
+              "a window of 64 positions splits into at most 64 parts");
 
 // long runs: chunk sizing and two-level combine
-constexpr int kChunkMin = SGB_CHUNK_MIN;  // a chunk has at least this many lookups
 constexpr int kMaxChunks = 2048;      // a run is cut into at most this many chunks
 constexpr int kSuperChunk = 32;       // chunks combined per first-level ticket
+
+// Lanes that cover a row of D columns at 4 columns per lane: the power of two
+// covering D / 4, between 4 and 64 (wider rows take several 256-column blocks).
+__host__ __device__ inline int lanes_per_row(int D) {
+  const int need = (D + 3) >> 2;
+  int l = 4;
+  while (l < need && l < 64) l <<= 1;
+  return l;
+}
+
+// 256-column blocks a row of D columns spans.
+__host__ __device__ inline int col_blocks(int D) { return (D + kColBlock - 1) / kColBlock; }
+
+// Fewest lookups in one chunk of a long run.  A work item is one chunk times
+// one 256-column block; a row of several blocks already spreads a chunk over
+// several waves, so its chunks are proportionally shorter (down to a floor).
+__host__ __device__ inline int chunk_min(int D) {
+  const int c = SGB_CHUNK_BASE / col_blocks(D);
+  return c > SGB_CHUNK_FLOOR ? c : SGB_CHUNK_FLOOR;
+}
+
+// Lookups per chunk of a long run of `len` lookups in a table of width D.
+__host__ __device__ inline int chunk_len(int len, int D) {
+  const int c = (len + kMaxChunks - 1) / kMaxChunks;
+  const int m = chunk_min(D);
+  return c > m ? c : m;
+}
 
 // bounded waits (look-back): iterations of ~1 us before giving up
 constexpr uint32_t kSpinLimit = 1u << 21;
@@ -154,7 +198,6 @@ struct PostParams {
   const int32_t* doff;
   int32_t T;
   int32_t thr;
-  int32_t ch_base;          // max(thr, kChunkMin)
   int32_t* run_lengths;
   int32_t* long_ids;
   uint32_t* chunk_begin;    // [num_long + 1]: first (chunk, column block) item of each long run
@@ -198,7 +241,7 @@ struct RedParams {
   uint32_t* work_ctr;
   uint32_t* sc_ticket;
   uint32_t* run_ticket;
-  float* partials;
+  double* partials;         // fp64 partial sums of long-run work items
   float* out;               // weights (SGD/Adagrad) or dense grad
   float* mom;               // Adagrad state
   uint32_t* status;
@@ -209,7 +252,7 @@ struct RedParams {
   int32_t T;
   int32_t nobag;
   int32_t thr;
-  int32_t ch_base;
+  int32_t sub_log;          // short-run reducer: log2 of the waves per window
   int32_t mode;
   int32_t accumulate;
   float lr;
@@ -225,7 +268,7 @@ hipError_t launch_rle(const RleParams& p, int grid, hipStream_t s);
 hipError_t launch_post(const PostParams& p, int grid, hipStream_t s);
 hipError_t launch_fill(const FillParams& p, int nblocks, hipStream_t s);
 hipError_t launch_reduce_long(const RedParams& p, bool bf16, int grid, hipStream_t s);
-hipError_t launch_reduce_short(const RedParams& p, bool bf16, int dmax, hipStream_t s);
+hipError_t launch_reduce_short(const RedParams& p, bool bf16, int dmin, int dmax, hipStream_t s);
 int reduce_long_blocks_per_cu(bool bf16);
 
 }  // namespace sgb

@@ -562,18 +562,10 @@ __global__ __launch_bounds__(kScanThreads) void k_rle(RleParams p) {
 // Run lengths, and the long runs -- length >= thr, FBGEMM `find_long_segments`
 // -- compacted in ascending run order (the page appends them through an
 // atomic counter in arbitrary order).  Each long run is cut into chunks of
-// chunk_len() lookups times the 256-column blocks of its row; a combined scan
-// gives every long run its first work item.  Also clears the combine tickets
-// of those items and, for a fresh dense gradient, marks touched rows in a
-// bitmap.
-
-__device__ __forceinline__ int chunk_len(int len, int ch_base) {
-  const int c = (len + kMaxChunks - 1) / kMaxChunks;
-  return c > ch_base ? c : ch_base;
-}
-
-// Column blocks of 256 a row of D columns spans.
-__device__ __forceinline__ int col_blocks(int D) { return (D + kColBlock - 1) / kColBlock; }
+// chunk_len() lookups (set by the row width) times the 256-column blocks of
+// its row; a combined scan gives every long run its first work item.  Also
+// clears the combine tickets of those items and, for a fresh dense gradient,
+// marks touched rows in a bitmap.
 
 // Table of a linear id (binary search of hash_size_cumsum).
 __device__ __forceinline__ int table_of_id(const int64_t* hsc, int T, int64_t id) {
@@ -603,12 +595,14 @@ __global__ __launch_bounds__(kScanThreads) void k_post(PostParams p) {
   const int n = (int)min((int64_t)kScanTile, (int64_t)U - base);
   int len[kScanItems];
   int ncb[kScanItems];
+  int Dk[kScanItems];
   uint64_t sum = 0;
 #pragma unroll
   for (int k = 0; k < kScanItems; ++k) {
     const int q = tid * kScanItems + k;
     len[k] = 0;
     ncb[k] = 1;
+    Dk[k] = 4;
     if (q < n) {
       const int64_t r = base + q;
       len[k] = p.cum[r + 1] - p.cum[r];
@@ -616,8 +610,9 @@ __global__ __launch_bounds__(kScanThreads) void k_post(PostParams p) {
       if (len[k] >= p.thr) {
         // a long run becomes nch chunks x ncb column blocks of work items
         const int t = table_of_id(p.hsc, p.T, p.unique_ids[r]);
-        ncb[k] = col_blocks(p.doff[t + 1] - p.doff[t]);
-        const int cl = chunk_len(len[k], p.ch_base);
+        Dk[k] = p.doff[t + 1] - p.doff[t];
+        ncb[k] = col_blocks(Dk[k]);
+        const int cl = chunk_len(len[k], Dk[k]);
         sum += (1ull << 31) | (uint64_t)(((len[k] + cl - 1) / cl) * ncb[k]);
       }
       if (p.bitmap) {
@@ -640,7 +635,7 @@ __global__ __launch_bounds__(kScanThreads) void k_post(PostParams p) {
     if (q < n && len[k] >= p.thr) {
       const uint32_t pos = (uint32_t)(at >> 31);
       const uint32_t c0 = (uint32_t)(at & kField);
-      const int cl = chunk_len(len[k], p.ch_base);
+      const int cl = chunk_len(len[k], Dk[k]);
       const int nch = (len[k] + cl - 1) / cl;
       p.long_ids[pos] = (int32_t)(base + q);
       p.chunk_begin[pos] = c0;
@@ -718,13 +713,6 @@ __global__ __launch_bounds__(256) void k_fill(FillParams p) {
 //   row: a deterministic reduction across many workgroups without float
 //   atomics (the page keeps a long run inside one block).
 
-__device__ __forceinline__ int lpl_for(int D) {
-  const int need = (D + 3) >> 2;
-  int l = 4;
-  while (l < need && l < 64) l <<= 1;
-  return l;
-}
-
 template <int LPL>
 __device__ __forceinline__ int bcast_i(int v, int src) {
   if constexpr (LPL == 64)
@@ -738,15 +726,81 @@ __device__ __forceinline__ float bcast_f(float v, int src) {
   return __int_as_float(bcast_i<LPL>(__float_as_int(v), src));
 }
 
+// Four grad_output elements as stored (4 x bf16 or 4 x fp32) and their fp32
+// values.  Gathers load the raw bits under their condition and widen them
+// only after every load of a round has been issued: widening inside the
+// conditional block would make each load wait for its data before the next
+// one starts.
 template <bool BF16>
-__device__ __forceinline__ float4 load4(const void* base, int64_t elem) {
-  if constexpr (BF16) {
-    const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + elem);
-    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
-  } else {
-    return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + elem);
-  }
+struct Raw4;
+template <>
+struct Raw4<true> {
+  uint2 u;
+};
+template <>
+struct Raw4<false> {
+  float4 f;
+};
+
+template <bool BF16>
+__device__ __forceinline__ Raw4<BF16> load_raw4(const void* base, int64_t elem) {
+  if constexpr (BF16)
+    return {*reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + elem)};
+  else
+    return {*reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + elem)};
+}
+
+template <bool BF16>
+__device__ __forceinline__ Raw4<BF16> zero_raw4() {
+  if constexpr (BF16)
+    return {make_uint2(0u, 0u)};
+  else
+    return {make_float4(0.f, 0.f, 0.f, 0.f)};
+}
+
+// bf16 -> fp32 is exact: the 16 bits become the high half of the fp32 word.
+template <bool BF16>
+__device__ __forceinline__ float4 widen4(const Raw4<BF16>& r) {
+  if constexpr (BF16)
+    return make_float4(__uint_as_float(r.u.x << 16), __uint_as_float(r.u.x & 0xffff0000u),
+                       __uint_as_float(r.u.y << 16), __uint_as_float(r.u.y & 0xffff0000u));
+  else
+    return r.f;
+}
+
+// Four fp64 accumulators.  Every product coef * value of fp32 (or widened
+// bf16) operands is exact in fp64, and the sums of a row stay in fp64 until
+// the row is written, where they are rounded once to fp32 -- so the result
+// does not depend on the order in which lookups are summed beyond fp64
+// rounding, however long or cancelling the run.
+struct d4 {
+  double x, y, z, w;
+};
+
+__device__ __forceinline__ d4 d4_zero() { return d4{0.0, 0.0, 0.0, 0.0}; }
+
+__device__ __forceinline__ void d4_fma(d4& a, float c, const float4& v) {
+  const double cd = (double)c;
+  a.x = fma(cd, (double)v.x, a.x);
+  a.y = fma(cd, (double)v.y, a.y);
+  a.z = fma(cd, (double)v.z, a.z);
+  a.w = fma(cd, (double)v.w, a.w);
+}
+
+__device__ __forceinline__ void d4_add(d4& a, const d4& b) {
+  a.x += b.x;
+  a.y += b.y;
+  a.z += b.z;
+  a.w += b.w;
+}
+
+__device__ __forceinline__ d4 d4_xor(const d4& a, int off) {
+  return d4{__shfl_xor(a.x, off, 64), __shfl_xor(a.y, off, 64), __shfl_xor(a.z, off, 64),
+            __shfl_xor(a.w, off, 64)};
+}
+
+__device__ __forceinline__ double d4_sumsq(const d4& a) {
+  return a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
 }
 
 __device__ __forceinline__ uint64_t info_mask(const RedParams& p) {
@@ -788,14 +842,14 @@ __device__ __forceinline__ RowDst row_dest(const RedParams& p, int t, int D, int
 // group of LPL lanes.  For the first batch a lane may bring its lookup's
 // (row, coefficient) already (pre_ok); otherwise they are read here.
 template <int LPL, int UNR, bool BF16>
-__device__ __forceinline__ float4 gather_sum(const RedParams& p, int first, int last, int step,
+__device__ __forceinline__ d4 gather_sum(const RedParams& p, int first, int last, int step,
                                              int t, int64_t colofs, bool col_ok, int pre_row,
                                              float pre_cf, bool pre_ok) {
   const int lane = lane_id();
   const int gb = lane & ~(LPL - 1), lig = lane & (LPL - 1);
   const uint64_t imask = info_mask(p);
   const bool has_coef = p.coef != nullptr;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  d4 acc = d4_zero();
   bool firstb = true;
   for (int j0 = first; j0 < last; j0 += LPL * step) {
     const int jm = j0 + lig * step;
@@ -811,7 +865,7 @@ __device__ __forceinline__ float4 gather_sum(const RedParams& p, int first, int 
     firstb = false;
     const int cnt = min(LPL, (last - j0 + step - 1) / step);
     for (int jj = 0; jj < cnt; jj += UNR) {
-      float4 v[UNR];
+      Raw4<BF16> r[UNR];
       float c[UNR];
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
@@ -819,17 +873,11 @@ __device__ __forceinline__ float4 gather_sum(const RedParams& p, int first, int 
         const int ro = bcast_i<LPL>(rowi, src);
         c[u] = bcast_f<LPL>(cf, src);
         const bool ok = (jj + u < cnt) && col_ok;
-        v[u] = ok ? load4<BF16>(p.grad, (int64_t)ro * p.row_stride + colofs)
-                  : make_float4(0.f, 0.f, 0.f, 0.f);
+        r[u] = ok ? load_raw4<BF16>(p.grad, (int64_t)ro * p.row_stride + colofs) : zero_raw4<BF16>();
         if (jj + u >= cnt) c[u] = 0.f;
       }
 #pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        acc.x = fmaf(c[u], v[u].x, acc.x);
-        acc.y = fmaf(c[u], v[u].y, acc.y);
-        acc.z = fmaf(c[u], v[u].z, acc.z);
-        acc.w = fmaf(c[u], v[u].w, acc.w);
-      }
+      for (int u = 0; u < UNR; ++u) d4_fma(acc, c[u], widen4<BF16>(r[u]));
     }
   }
   return acc;
@@ -837,20 +885,15 @@ __device__ __forceinline__ float4 gather_sum(const RedParams& p, int first, int 
 
 // Adds the 64/LPL lane groups of a wave (fixed xor tree; all groups get the sum).
 template <int LPL>
-__device__ __forceinline__ float4 fold_groups(float4 a) {
+__device__ __forceinline__ d4 fold_groups(d4 a) {
 #pragma unroll
-  for (int off = 32; off >= LPL; off >>= 1) {
-    a.x += __shfl_xor(a.x, off, 64);
-    a.y += __shfl_xor(a.y, off, 64);
-    a.z += __shfl_xor(a.z, off, 64);
-    a.w += __shfl_xor(a.w, off, 64);
-  }
+  for (int off = 32; off >= LPL; off >>= 1) d4_add(a, d4_xor(a, off));
   return a;
 }
 
 // Sum over the LPL lanes of a group (fixed xor tree).
 template <int LPL>
-__device__ __forceinline__ float group_sum(float x) {
+__device__ __forceinline__ double group_sum(double x) {
 #pragma unroll
   for (int off = LPL / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
   return x;
@@ -869,6 +912,11 @@ __device__ __forceinline__ void st4(float* q, float4 v) { *reinterpret_cast<floa
 // `cache_backward_sgd_kernel`).  Dense: store, or add for an accumulating
 // grad_weight (tinygrad `_embedding_bwd_kernel`).  The old row value is read
 // before getG so that the read overlaps the gather.
+// One fp32 result from an fp64 value, rounded once.
+__device__ __forceinline__ float4 round4(double x, double y, double z, double w) {
+  return make_float4((float)x, (float)y, (float)z, (float)w);
+}
+
 template <int LPL, class F>
 __device__ __forceinline__ void finish_row(const RedParams& p, const RowDst& dst, int D, bool write,
                                            int cb_lo, int cb_hi, F&& getG) {
@@ -878,63 +926,51 @@ __device__ __forceinline__ void finish_row(const RedParams& p, const RowDst& dst
     const float4 w0 = w0ok ? ld4(dst.out + 4 * lig) : make_float4(0.f, 0.f, 0.f, 0.f);
     const float m0 = write ? *dst.mom : 0.f;
     const int ncb = col_blocks(D);
-    const float4 g0 = getG(0);
-    float ss = 0.f;
-    if (4 * lig < D) ss = g0.x * g0.x + g0.y * g0.y + g0.z * g0.z + g0.w * g0.w;
+    const d4 g0 = getG(0);
+    double ss = 0.0;
+    if (4 * lig < D) ss = d4_sumsq(g0);
 #pragma unroll 1
     for (int cb = 1; cb < ncb; ++cb) {
-      const float4 g = getG(cb);
-      if (cb * kColBlock + 4 * lig < D) ss += g.x * g.x + g.y * g.y + g.z * g.z + g.w * g.w;
+      const d4 g = getG(cb);
+      if (cb * kColBlock + 4 * lig < D) ss += d4_sumsq(g);
     }
     ss = group_sum<LPL>(ss);
-    const float m = m0 + ss / (float)D;
-    const float mult = p.lr / (sqrtf(m) + p.eps);
-    if (w0ok) {
-      float4 wv = w0;
-      wv.x -= mult * g0.x;
-      wv.y -= mult * g0.y;
-      wv.z -= mult * g0.z;
-      wv.w -= mult * g0.w;
-      st4(dst.out + 4 * lig, wv);
-    }
+    const double m = (double)m0 + ss / (double)D;
+    const double mult = (double)p.lr / (sqrt(m) + (double)p.eps);
+    if (w0ok)
+      st4(dst.out + 4 * lig, round4((double)w0.x - g0.x * mult, (double)w0.y - g0.y * mult,
+                                    (double)w0.z - g0.z * mult, (double)w0.w - g0.w * mult));
 #pragma unroll 1
     for (int cb = 1; cb < ncb; ++cb) {
-      const float4 g = getG(cb);
+      const d4 g = getG(cb);
       const int col = cb * kColBlock + 4 * lig;
       if (write && col < D) {
-        float4 wv = ld4(dst.out + col);
-        wv.x -= mult * g.x;
-        wv.y -= mult * g.y;
-        wv.z -= mult * g.z;
-        wv.w -= mult * g.w;
-        st4(dst.out + col, wv);
+        const float4 wv = ld4(dst.out + col);
+        st4(dst.out + col, round4((double)wv.x - g.x * mult, (double)wv.y - g.y * mult,
+                                  (double)wv.z - g.z * mult, (double)wv.w - g.w * mult));
       }
     }
-    if (write && lig == 0) *dst.mom = m;
+    if (write && lig == 0) *dst.mom = (float)m;
     return;
   }
   const bool needs_old = p.mode == kModeSgd || p.accumulate;
+  const double lr = (double)p.lr;
 #pragma unroll 1
   for (int cb = cb_lo; cb < cb_hi; ++cb) {
     const int col = cb * kColBlock + 4 * lig;
     const bool ok = write && col < D;
     const float4 old = (ok && needs_old) ? ld4(dst.out + col) : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4 g = getG(cb);
+    const d4 g = getG(cb);
     if (!ok) continue;
     float4 wv;
-    if (p.mode == kModeSgd) {
-      wv.x = old.x - p.lr * g.x;
-      wv.y = old.y - p.lr * g.y;
-      wv.z = old.z - p.lr * g.z;
-      wv.w = old.w - p.lr * g.w;
-    } else if (p.accumulate) {
-      wv.x = old.x + g.x;
-      wv.y = old.y + g.y;
-      wv.z = old.z + g.z;
-      wv.w = old.w + g.w;
-    } else {
-      wv = g;
-    }
+    if (p.mode == kModeSgd)
+      wv = round4((double)old.x - lr * g.x, (double)old.y - lr * g.y, (double)old.z - lr * g.z,
+                  (double)old.w - lr * g.w);
+    else if (p.accumulate)
+      wv = round4((double)old.x + g.x, (double)old.y + g.y, (double)old.z + g.z,
+                  (double)old.w + g.w);
+    else
+      wv = round4(g.x, g.y, g.z, g.w);
     st4(dst.out + col, wv);
   }
 }
@@ -944,20 +980,28 @@ __device__ __forceinline__ void finish_row(const RedParams& p, const RowDst& dst
 // across the XCDs' L2 caches by themselves; an agent-scope release/acquire
 // fence pair would instead write back and invalidate a whole L2 per ticket,
 // which measured as most of the long-run kernel's time.
-__device__ __forceinline__ void store_partial(float* q, float4 v) {
-  const uint64_t lo = (uint64_t)__float_as_uint(v.x) | ((uint64_t)__float_as_uint(v.y) << 32);
-  const uint64_t hi = (uint64_t)__float_as_uint(v.z) | ((uint64_t)__float_as_uint(v.w) << 32);
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(q), lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(q) + 1, hi, __ATOMIC_RELAXED,
+__device__ __forceinline__ void store_partial(double* q, const d4& v) {
+  uint64_t* u = reinterpret_cast<uint64_t*>(q);
+  __hip_atomic_store(u, (uint64_t)__double_as_longlong(v.x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(u + 1, (uint64_t)__double_as_longlong(v.y), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(u + 2, (uint64_t)__double_as_longlong(v.z), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(u + 3, (uint64_t)__double_as_longlong(v.w), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ float4 load_partial(const float* q) {
-  uint64_t* u = reinterpret_cast<uint64_t*>(const_cast<float*>(q));
-  const uint64_t lo = __hip_atomic_load(u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint64_t hi = __hip_atomic_load(u + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return make_float4(__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
-                     __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32)));
+__device__ __forceinline__ d4 load_partial(const double* q) {
+  uint64_t* u = reinterpret_cast<uint64_t*>(const_cast<double*>(q));
+  d4 r;
+  r.x = __longlong_as_double((long long)__hip_atomic_load(u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  r.y = __longlong_as_double(
+      (long long)__hip_atomic_load(u + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  r.z = __longlong_as_double(
+      (long long)__hip_atomic_load(u + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  r.w = __longlong_as_double(
+      (long long)__hip_atomic_load(u + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  return r;
 }
 
 // Last-arrival ticket: waits until this wave's partial stores have completed
@@ -976,29 +1020,24 @@ __device__ __forceinline__ bool ticket_last(uint32_t* ctr, uint32_t members) {
 }
 
 // Partial slot of chunk c, column block cb, of a long run whose items start
-// at slot `cbeg`: kColBlock floats each, chunk-major.
-__device__ __forceinline__ float* slot_of(const RedParams& p, uint32_t cbeg, int c, int ncb,
-                                          int cb) {
+// at slot `cbeg`: kColBlock fp64 values each, chunk-major.
+__device__ __forceinline__ double* slot_of(const RedParams& p, uint32_t cbeg, int c, int ncb,
+                                           int cb) {
   return p.partials + ((int64_t)cbeg + (int64_t)c * ncb + cb) * kColBlock;
 }
 
 // Sum of the partials of chunks first, first+stride, ... (count of them) for
 // column block cb, groups interleaved, folded in a fixed order.
 template <int LPL>
-__device__ __forceinline__ float4 sum_slots(const RedParams& p, uint32_t cbeg, int ncb, int first,
-                                            int count, int stride, int cb, int D) {
+__device__ __forceinline__ d4 sum_slots(const RedParams& p, uint32_t cbeg, int ncb, int first,
+                                        int count, int stride, int cb, int D) {
   constexpr int G = 64 / LPL;
   const int lane = lane_id(), g = lane / LPL, lig = lane & (LPL - 1);
   const int col = 4 * lig;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  d4 acc = d4_zero();
   if (cb * kColBlock + col < D) {
-    for (int i = g; i < count; i += G) {
-      const float4 v = load_partial(slot_of(p, cbeg, first + i * stride, ncb, cb) + col);
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
-    }
+    for (int i = g; i < count; i += G)
+      d4_add(acc, load_partial(slot_of(p, cbeg, first + i * stride, ncb, cb) + col));
   }
   return fold_groups<LPL>(acc);
 }
@@ -1010,7 +1049,7 @@ __device__ __forceinline__ void long_item(const RedParams& p, const LongRun& rec
   const int lane = lane_id(), g = lane / LPL, lig = lane & (LPL - 1);
   const int t = rec.t, start = rec.start, len = rec.len;
   const int ncb = rec.ncb;
-  const int chl = chunk_len(len, p.ch_base);
+  const int chl = chunk_len(len, D);
   const int nch = rec.nch;
   const int lo = start + c * chl;
   const int hi = min(lo + chl, start + len);
@@ -1021,8 +1060,8 @@ __device__ __forceinline__ void long_item(const RedParams& p, const LongRun& rec
   const RowDst dst = row_dest(p, t, D, rec.id);
   auto chunkG = [&](int cbx) {
     const int col = cbx * kColBlock + 4 * lig;
-    const float4 a = gather_sum<LPL, SGB_LONG_UNR, BF16>(p, lo + g, hi, G, t, gcol + col, col < D, 0, 0.f,
-                                               false);
+    const d4 a = gather_sum<LPL, SGB_LONG_UNR, BF16>(p, lo + g, hi, G, t, gcol + col, col < D, 0,
+                                                     0.f, false);
     return fold_groups<LPL>(a);
   };
   if (nch == 1) {
@@ -1032,7 +1071,7 @@ __device__ __forceinline__ void long_item(const RedParams& p, const LongRun& rec
   const uint32_t cbeg = rec.cbeg;
 #pragma unroll 1
   for (int cbx = cb_lo; cbx < cb_hi; ++cbx) {
-    const float4 a = chunkG(cbx);
+    const d4 a = chunkG(cbx);
     if (g == 0 && cbx * kColBlock + 4 * lig < D) store_partial(slot_of(p, cbeg, c, ncb, cbx) + 4 * lig, a);
   }
   const int m0 = (c / kSuperChunk) * kSuperChunk;
@@ -1047,7 +1086,7 @@ __device__ __forceinline__ void long_item(const RedParams& p, const LongRun& rec
   }
 #pragma unroll 1
   for (int cbx = cb_lo; cbx < cb_hi; ++cbx) {
-    const float4 a = sum_slots<LPL>(p, cbeg, ncb, m0, members, 1, cbx, D);
+    const d4 a = sum_slots<LPL>(p, cbeg, ncb, m0, members, 1, cbx, D);
     if (g == 0 && cbx * kColBlock + 4 * lig < D)
       store_partial(slot_of(p, cbeg, m0, ncb, cbx) + 4 * lig, a);
   }
@@ -1090,7 +1129,7 @@ __global__ __launch_bounds__(256) void k_reduce_long(RedParams p) {
     const int local = (int)(w - rec.cbeg);
     const int c = local / rec.ncb, cb = local % rec.ncb;
     if (p.mode == kModeAdagrad && cb != 0) continue;
-    switch (lpl_for(D)) {
+    switch (lanes_per_row(D)) {
       case 4: long_item<4, BF16>(p, rec, c, cb, D); break;
       case 8: long_item<8, BF16>(p, rec, c, cb, D); break;
       case 16: long_item<16, BF16>(p, rec, c, cb, D); break;
@@ -1112,12 +1151,15 @@ __device__ __forceinline__ int short_lpl(int D) {
   return l;
 }
 
-// One batch of short runs of table t: the g-th set bit of `sel` (a window
-// lane holding a run head) is served by lane group g (lpl lanes), CPL columns
-// per lane in pieces of 4 striped across the group (piece i at column
-// col + 4 * lpl * i), in the CPL*64-column block cb.  Called with the whole
-// wave active.  The row's old value and Adagrad state are read before the
-// gather so that the reads overlap.
+// One batch of short runs of table t, CPL columns per lane in pieces of 4
+// striped across a lane group of lpl lanes (piece i at column
+// col + 4 * lpl * i), in the CPL*64-column block cb.  With k runs in the
+// batch (the set bits of `sel`, window lanes holding run heads) and 64 / lpl
+// groups, each run gets the largest power-of-two number of groups that fits:
+// its groups take interleaved slices of lpl lookups and are folded by a fixed
+// xor tree, and the first of them writes the row.  Called with the whole wave
+// active.  The row's old value and Adagrad state are read before the gather
+// so that the reads overlap.
 template <int CPL, bool BF16>
 __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, int lpl, int64_t base,
                                             int len, uint64_t key, int rowi, float cf, int t,
@@ -1125,15 +1167,21 @@ __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, in
   constexpr int NP = CPL / 4;
   const int lg = __builtin_ctz(lpl);
   const int lane = lane_id(), g = lane >> lg, lig = lane & (lpl - 1), gb = g << lg;
+  const int ng = 64 >> lg;
+  const int k = __popcll(sel);
+  int glg = 0;  // log2 of the groups per run
+  while ((k << (glg + 1)) <= ng) ++glg;
+  const int rg = g >> glg, q = g & ((1 << glg) - 1);
   uint64_t m = sel;
-  for (int i = 0; i < g; ++i) m &= m - 1;
+  for (int i = 0; i < rg; ++i) m &= m - 1;
   const bool active = m != 0;
+  const bool lead = active && q == 0;
   const int src = active ? __builtin_ctzll(m) : 0;
   // every shuffle here runs with the whole wave active: a masked-off source
   // lane would read as 0
   const int nn = __shfl(len, src, 64);
   const uint64_t id = __shfl(key, src, 64);
-  const int wl = src + lig;  // window lane of this lane's first lookup
+  const int wl = src + (q << lg) + lig;  // window lane of this lane's first lookup
   const int prow = __shfl(rowi, wl < 64 ? wl : 63, 64);
   const float pcf = __shfl(cf, wl < 64 ? wl : 63, 64);
   const int n = active ? nn : 0;
@@ -1143,24 +1191,26 @@ __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, in
 #pragma unroll
   for (int i = 0; i < NP; ++i)
     if (active && col + 4 * lpl * i < D) vmask |= 1 << i;
+  const int wmask = lead ? vmask : 0;
   RowDst dst{nullptr, nullptr};
-  if (active) dst = row_dest(p, t, D, (int64_t)id);
+  if (lead) dst = row_dest(p, t, D, (int64_t)id);
   const bool needs_old = p.mode != kModeDense || p.accumulate;
-  float4 old[NP], acc[NP];
+  float4 old[NP];
+  d4 acc[NP];
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
-    old[i] = (needs_old && ((vmask >> i) & 1)) ? ld4(dst.out + col + 4 * lpl * i)
+    old[i] = (needs_old && ((wmask >> i) & 1)) ? ld4(dst.out + col + 4 * lpl * i)
                                               : make_float4(0.f, 0.f, 0.f, 0.f);
-    acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    acc[i] = d4_zero();
   }
-  const float m0 = (p.mode == kModeAdagrad && active) ? *dst.mom : 0.f;
+  const float m0 = (p.mode == kModeAdagrad && lead) ? *dst.mom : 0.f;
   const int64_t gcol = (p.nobag ? 0 : p.doff[t]) + col;
   const uint64_t imask = info_mask(p);
   const bool has_coef = p.coef != nullptr;
-  // lookups s .. s+n-1 of this group's run, lpl at a time; the first lpl
-  // lookups' metadata comes from the window when it lies inside it
+  // slices of lpl lookups of this group's run, every (1 << glg)-th one; the
+  // first slice's metadata comes from the window when it lies inside it
   bool firstb = true;
-  for (int j0 = s; j0 < s + n; j0 += lpl) {
+  for (int j0 = s + (q << lg); j0 < s + n; j0 += lpl << glg) {
     const int jm = j0 + lig;
     int ri = 0;
     float ci = 0.f;
@@ -1174,7 +1224,7 @@ __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, in
     firstb = false;
     const int cnt = min(lpl, s + n - j0);
     for (int jj = 0; jj < cnt; jj += SGB_SHORT_UNR) {
-      float4 v[SGB_SHORT_UNR][NP];
+      Raw4<BF16> r[SGB_SHORT_UNR][NP];
       float c[SGB_SHORT_UNR];
 #pragma unroll
       for (int u = 0; u < SGB_SHORT_UNR; ++u) {
@@ -1185,67 +1235,71 @@ __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, in
         const int64_t e = (int64_t)ro * p.row_stride + gcol;
 #pragma unroll
         for (int i = 0; i < NP; ++i)
-          v[u][i] = (ok && ((vmask >> i) & 1)) ? load4<BF16>(p.grad, e + 4 * lpl * i)
-                                               : make_float4(0.f, 0.f, 0.f, 0.f);
+          r[u][i] = (ok && ((vmask >> i) & 1)) ? load_raw4<BF16>(p.grad, e + 4 * lpl * i)
+                                               : zero_raw4<BF16>();
       }
 #pragma unroll
-      for (int u = 0; u < SGB_SHORT_UNR; ++u)
+      for (int i = 0; i < NP; ++i) {
+        // the round's few products are summed in fp32, the run's sum in fp64
+        float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int i = 0; i < NP; ++i) {
-          acc[i].x = fmaf(c[u], v[u][i].x, acc[i].x);
-          acc[i].y = fmaf(c[u], v[u][i].y, acc[i].y);
-          acc[i].z = fmaf(c[u], v[u][i].z, acc[i].z);
-          acc[i].w = fmaf(c[u], v[u][i].w, acc[i].w);
+        for (int u = 0; u < SGB_SHORT_UNR; ++u) {
+          const float4 v = widen4<BF16>(r[u][i]);
+          t.x = fmaf(c[u], v.x, t.x);
+          t.y = fmaf(c[u], v.y, t.y);
+          t.z = fmaf(c[u], v.z, t.z);
+          t.w = fmaf(c[u], v.w, t.w);
         }
+        d4_add(acc[i], d4{(double)t.x, (double)t.y, (double)t.z, (double)t.w});
+      }
     }
   }
+  // fold the groups of each run (uniform trip count: the whole wave takes part)
+  for (int off = lpl; off < (lpl << glg); off <<= 1) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) d4_add(acc[i], d4_xor(acc[i], off));
+  }
   if (p.mode == kModeAdagrad) {
-    float ss = 0.f;
+    double ss = 0.0;
 #pragma unroll
     for (int i = 0; i < NP; ++i)
-      ss += acc[i].x * acc[i].x + acc[i].y * acc[i].y + acc[i].z * acc[i].z + acc[i].w * acc[i].w;
+      if ((vmask >> i) & 1) ss += d4_sumsq(acc[i]);
     for (int off = lpl >> 1; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-    const float mm = m0 + ss / (float)D;
-    const float mult = p.lr / (sqrtf(mm) + p.eps);
+    const double mm = (double)m0 + ss / (double)D;
+    const double mult = (double)p.lr / (sqrt(mm) + (double)p.eps);
 #pragma unroll
     for (int i = 0; i < NP; ++i)
-      if ((vmask >> i) & 1) {
-        float4 w = old[i];
-        w.x -= mult * acc[i].x;
-        w.y -= mult * acc[i].y;
-        w.z -= mult * acc[i].z;
-        w.w -= mult * acc[i].w;
-        st4(dst.out + col + 4 * lpl * i, w);
-      }
-    if (active && lig == 0) *dst.mom = mm;
+      if ((wmask >> i) & 1)
+        st4(dst.out + col + 4 * lpl * i,
+            round4((double)old[i].x - acc[i].x * mult, (double)old[i].y - acc[i].y * mult,
+                   (double)old[i].z - acc[i].z * mult, (double)old[i].w - acc[i].w * mult));
+    if (lead && lig == 0) *dst.mom = (float)mm;
     return;
   }
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
-    if (!((vmask >> i) & 1)) continue;
+    if (!((wmask >> i) & 1)) continue;
+    const d4& a = acc[i];
+    const double lr = (double)p.lr;
     float4 w;
-    if (p.mode == kModeSgd) {
-      w.x = old[i].x - p.lr * acc[i].x;
-      w.y = old[i].y - p.lr * acc[i].y;
-      w.z = old[i].z - p.lr * acc[i].z;
-      w.w = old[i].w - p.lr * acc[i].w;
-    } else if (p.accumulate) {
-      w.x = old[i].x + acc[i].x;
-      w.y = old[i].y + acc[i].y;
-      w.z = old[i].z + acc[i].z;
-      w.w = old[i].w + acc[i].w;
-    } else {
-      w = acc[i];
-    }
+    if (p.mode == kModeSgd)
+      w = round4((double)old[i].x - lr * a.x, (double)old[i].y - lr * a.y,
+                 (double)old[i].z - lr * a.z, (double)old[i].w - lr * a.w);
+    else if (p.accumulate)
+      w = round4((double)old[i].x + a.x, (double)old[i].y + a.y, (double)old[i].z + a.z,
+                 (double)old[i].w + a.w);
+    else
+      w = round4(a.x, a.y, a.z, a.w);
     st4(dst.out + col + 4 * lpl * i, w);
   }
 }
 
-// One wave per 64 sorted positions.  Run heads are where the id changes; a
-// run's length is the distance to the next head in the window, and only a run
-// that reaches the window's end looks its length up (run index at the head,
-// run starts).  Short runs (length < thr) starting in the window are served
-// in batches of 64/lpl runs of one table.  Rows wider than 512 columns are
+// Windows of 64 sorted positions, each shared by 2^sub_log waves.  Run heads
+// are where the id changes; a run's length is the distance to the next head
+// in the window, and only a run that reaches the window's end looks its
+// length up (run index at the head, run starts).  A wave serves the short
+// runs (length < thr) that start in its 64 >> sub_log positions, in batches
+// of at most 64/lpl runs of one table.  Rows wider than 512 columns are
 // served by the CPL = 16 instance; the CPL = 8 instance skips them, and the
 // reverse.
 template <int CPL, bool BF16>
@@ -1253,7 +1307,8 @@ __device__ __forceinline__ void reduce_short(const RedParams& p) {
   const int lane = lane_id();
   const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int cb = blockIdx.y;
-  const int64_t base = unit * kShortSpan;
+  const int64_t base = (unit >> p.sub_log) * kShortSpan;
+  const int part = (int)(unit & ((1 << p.sub_log) - 1));
   if (base >= p.N) return;
   const uint64_t imask = info_mask(p);
   const int64_t pos = base + lane;
@@ -1280,7 +1335,7 @@ __device__ __forceinline__ void reduce_short(const RedParams& p) {
       len = p.cum[r + 1] - (int)pos;
     }
   }
-  const bool todo = head && len < p.thr;
+  const bool todo = head && len < p.thr && (lane >> (6 - p.sub_log)) == part;
   uint64_t pending = __ballot(todo);
   while (pending) {
     const int lead = __builtin_ctzll(pending);
@@ -1301,10 +1356,10 @@ __device__ __forceinline__ void reduce_short(const RedParams& p) {
   }
 }
 
-// 8 columns per lane fits 64 VGPRs: 8 waves per SIMD to overlap the runs'
-// dependent memory steps.
+// 8 columns per lane with fp64 sums fits about 80 VGPRs: 6 waves per SIMD overlap
+// the runs' dependent memory steps.
 template <bool BF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SGB_SHORT8_WAVES, SGB_SHORT8_WAVES)))
 void k_reduce_short8(RedParams p) {
   reduce_short<8, BF16>(p);
 }
@@ -1360,25 +1415,35 @@ hipError_t launch_reduce_long(const RedParams& p, bool bf16, int grid, hipStream
   return hipGetLastError();
 }
 
-hipError_t launch_reduce_short(const RedParams& p, bool bf16, int dmax, hipStream_t s) {
-  const int64_t units = (p.N + kShortSpan - 1) / kShortSpan;
-  const unsigned gx = (unsigned)((units + 3) / 4);
-  {
+hipError_t launch_reduce_short(const RedParams& p, bool bf16, int dmin, int dmax, hipStream_t s) {
+  const int64_t windows = (p.N + kShortSpan - 1) / kShortSpan;
+  // waves per window, reduced when the grid would pass 2^32 threads
+  auto sub_for = [&](int want) {
+    int sub = want;
+    while (sub > 0 && (windows << sub) > (1ll << 25)) --sub;
+    return sub;
+  };
+  if (dmin <= 512) {
     // rows up to 512 columns: 8 columns per lane, one wave per row at most
-    const dim3 grid(gx, 1);
+    RedParams q = p;
+    q.sub_log = sub_for(kShortSub8);
+    const dim3 grid((unsigned)(((windows << q.sub_log) + 3) / 4), 1);
     if (bf16)
-      hipLaunchKernelGGL(k_reduce_short8<true>, grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL(k_reduce_short8<true>, grid, dim3(256), 0, s, q);
     else
-      hipLaunchKernelGGL(k_reduce_short8<false>, grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL(k_reduce_short8<false>, grid, dim3(256), 0, s, q);
   }
   if (dmax > 512) {
     // wider rows: 16 columns per lane in 1024-column blocks (dense / SGD may
     // have several; Adagrad rows are at most 1024 wide)
-    const dim3 grid(gx, (unsigned)((dmax + 1023) / 1024));
+    RedParams q = p;
+    q.sub_log = sub_for(kShortSub16);
+    const dim3 grid((unsigned)(((windows << q.sub_log) + 3) / 4),
+                    (unsigned)((dmax + 1023) / 1024));
     if (bf16)
-      hipLaunchKernelGGL(k_reduce_short16<true>, grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL(k_reduce_short16<true>, grid, dim3(256), 0, s, q);
     else
-      hipLaunchKernelGGL(k_reduce_short16<false>, grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL(k_reduce_short16<false>, grid, dim3(256), 0, s, q);
   }
   return hipGetLastError();
 }
