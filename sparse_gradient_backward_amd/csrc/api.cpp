@@ -77,7 +77,7 @@ struct Layout {
   int64_t sort_tiles = 0, scan_tiles = 0;
   int64_t max_long = 0;   // bound on the number of long runs
   int64_t max_items = 0;  // bound on the (chunk, column block) items over all long runs
-  size_t hdr = 0, hist = 0, zero_begin = 0, sort_lb = 0, rle_lb = 0, post_lb = 0, bitmap = 0,
+  size_t hdr = 0, hist = 0, counts = 0, zero_begin = 0, rle_lb = 0, post_lb = 0, bitmap = 0,
          zero_end_nobitmap = 0, zero_end_bitmap = 0;
   size_t kvA = 0, kvB = 0, coefA = 0, coefB = 0, uniq = 0, cum = 0, headrun = 0, lens = 0, longs = 0,
          chunkb = 0, longrec = 0, runtk = 0, sctk = 0, part = 0, total = 0;
@@ -122,14 +122,14 @@ sgb_status make_layout(const sgb_plan_s* p, int64_t N, int32_t B, bool has_offse
     return at_;
   };
   L->hdr = take(sizeof(Header));
-  L->hist = take(sizeof(uint32_t) * kMaxPasses * kRadixMax);
+  L->hist = take(sizeof(uint32_t) * kMaxPasses * kRadixMax);  // digit bases of each pass
   L->zero_begin = align_up(o, 256);
-  L->sort_lb = take(sizeof(uint32_t) * (size_t)std::max(L->npasses, 1) * L->sort_tiles * kRadixMax);
   L->rle_lb = take(sizeof(uint32_t) * (size_t)L->scan_tiles);
   L->post_lb = take(sizeof(uint64_t) * (size_t)L->scan_tiles);
   L->zero_end_nobitmap = align_up(o, 256);
   L->bitmap = take(sizeof(uint32_t) * (size_t)((p->total_rows + 31) / 32));
   L->zero_end_bitmap = align_up(o, 256);
+  L->counts = take(sizeof(uint32_t) * (size_t)L->sort_tiles * kRadixMax);
   L->kvA = take(sizeof(uint64_t) * (size_t)N);
   L->kvB = take(sizeof(uint64_t) * (size_t)N);
   L->coefA = take(sizeof(float) * (size_t)N);
@@ -331,7 +331,7 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   if (e != hipSuccess) return SGB_ERR_HIP;
   mark(SGB_STAGE_INIT, 1);
 
-  // linearise + digit histograms (+ clear look-back words and the bitmap)
+  // linearise (+ clear look-back words and the bitmap)
   LinParams lp{};
   lp.indices = b->indices;
   lp.offsets = b->offsets;
@@ -344,18 +344,12 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   lp.info_bits = L.info_bits;
   lp.kv_out = at<uint64_t>(ws, L.kvA);
   lp.coef_out = has_coef ? at<float>(ws, L.coefA) : nullptr;
-  lp.hist = at<uint32_t>(ws, L.hist);
-  lp.npasses = L.npasses;
-  for (int i = 0; i < L.npasses; ++i) {
-    lp.pass_shift[i] = L.pass_key_shift[i];
-    lp.pass_bits[i] = L.pass_bits[i];
-  }
   lp.status = status;
   lp.zero_begin = at<uint4>(ws, L.zero_begin);
   lp.zero_vec4 = (int64_t)(((fresh ? L.zero_end_bitmap : L.zero_end_nobitmap) - L.zero_begin) / 16);
   const int64_t lin_tiles = b->offsets ? ((int64_t)b->B * p->T + kLinBags - 1) / kLinBags
                                        : (N + kLinLookups - 1) / kLinLookups;
-  const int lin_grid = (int)std::max<int64_t>(1, std::min<int64_t>(lin_tiles, 4ll * p->num_cus));
+  const int lin_grid = (int)std::max<int64_t>(1, std::min<int64_t>(lin_tiles, 16ll * p->num_cus));
   mark(SGB_STAGE_LINEARIZE, 0);
   if (launch_linearize(lp, lin_grid, stream) != hipSuccess) return SGB_ERR_HIP;
   mark(SGB_STAGE_LINEARIZE, 1);
@@ -373,13 +367,14 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
     sp.kv_out = kv_out;
     sp.coef_out = cf_out;
     sp.N = N;
+    sp.tiles = L.sort_tiles;
     sp.shift = L.info_bits + L.pass_key_shift[ps];
     sp.bits = L.pass_bits[ps];
-    sp.hist = at<uint32_t>(ws, L.hist) + ps * kRadixMax;
-    sp.lookback = at<uint32_t>(ws, L.sort_lb) + (size_t)ps * L.sort_tiles * kRadixMax;
-    sp.tile_ctr = &hdr->sort_tile_ctr[ps];
+    sp.counts = at<uint32_t>(ws, L.counts);
+    sp.bases = at<uint32_t>(ws, L.hist) + ps * kRadixMax;
+    sp.ticket = &hdr->sort_ticket[ps];
     sp.status = status;
-    if (launch_sort_pass(sp, (int)L.sort_tiles, stream) != hipSuccess) return SGB_ERR_HIP;
+    if (launch_sort_pass(sp, stream) != hipSuccess) return SGB_ERR_HIP;
     std::swap(kv_in, kv_out);
     std::swap(cf_in, cf_out);
   }
@@ -406,9 +401,12 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   pp.cum = rp.cum;
   pp.num_runs = rp.num_runs;
   pp.unique_ids = rp.unique_ids;
-  pp.hsc = p->d_hsc;
+  pp.kv = kv_sorted;
   pp.doff = p->d_doff;
+  pp.info_bits = L.info_bits;
+  pp.B = b->offsets ? b->B : 0;
   pp.T = p->T;
+  pp.nobag = nobag ? 1 : 0;
   pp.thr = p->thr;
   pp.run_lengths = at<int32_t>(ws, L.lens);
   pp.long_ids = at<int32_t>(ws, L.longs);

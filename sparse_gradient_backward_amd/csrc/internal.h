@@ -10,7 +10,6 @@ namespace sgb {
 
 // ---------------------------------------------------------------- limits
 constexpr int kMaxPasses = 4;         // LSD passes of <= 9 bits: linear ids below 2^36
-constexpr int kHistPasses = kMaxPasses;
 constexpr int kRadixMax = 512;        // 9-bit digits
 constexpr int kMaxCb = 4;             // Adagrad rows held in registers: D <= 4 * 256
 constexpr int kColBlock = 256;        // columns one wave covers per pass (64 lanes x 4)
@@ -56,6 +55,8 @@ constexpr int kScanTile = kScanThreads * kScanItems;
 constexpr int kLinThreads = 256;
 constexpr int kLinBags = 64;
 constexpr int kLinLookups = 4 * kLinThreads;
+constexpr int kLinPer = 8;            // lookups per thread whose loads are issued together
+static_assert(kLinBags < kLinThreads, "one thread per bag offset of a tile");
 
 // short runs: sorted positions of one window of the short-run reducer, and
 // log2 of the waves sharing a window (each serves the runs starting in its
@@ -111,7 +112,7 @@ enum { kModeDense = 0, kModeSgd = 1, kModeAdagrad = 2 };
 // Workspace header (offset 0).
 struct Header {
   uint32_t status;                    // first device-detected error, 0 = none
-  uint32_t sort_tile_ctr[kMaxPasses]; // dynamic tile ids of each sort pass
+  uint32_t sort_ticket[kMaxPasses];   // last-arrival counters of the sort passes
   uint32_t rle_tile_ctr;
   uint32_t post_tile_ctr;
   uint32_t work_ctr;                  // reducer work queue
@@ -154,10 +155,6 @@ struct LinParams {
   int32_t info_bits;
   uint64_t* kv_out;
   float* coef_out;          // NULL when every coefficient is 1
-  uint32_t* hist;           // [kMaxPasses][kRadixMax]
-  int32_t npasses;
-  int32_t pass_shift[kMaxPasses];
-  int32_t pass_bits[kMaxPasses];
   uint32_t* status;
   uint4* zero_begin;        // region zeroed for the later kernels
   int64_t zero_vec4;
@@ -169,11 +166,12 @@ struct SortParams {
   uint64_t* kv_out;
   float* coef_out;
   int64_t N;
+  int64_t tiles;            // tiles of kSortTile items
   int32_t shift;
   int32_t bits;
-  const uint32_t* hist;     // this pass's digit counts [kRadixMax]
-  uint32_t* lookback;       // [tiles][kRadixMax]
-  uint32_t* tile_ctr;
+  uint32_t* counts;         // [radix][tiles]: tile digit counts, then their offsets
+  uint32_t* bases;          // [radix]: digit totals, then the digits' first positions
+  uint32_t* ticket;         // arrival counter of k_sort_offsets (zero at launch)
   uint32_t* status;
 };
 
@@ -194,9 +192,12 @@ struct PostParams {
   const int32_t* cum;
   const int32_t* num_runs;
   const int64_t* unique_ids;
-  const int64_t* hsc;
+  const uint64_t* kv;       // sorted packed words (table of a run from its info)
   const int32_t* doff;
+  int32_t info_bits;
+  int32_t B;
   int32_t T;
+  int32_t nobag;
   int32_t thr;
   int32_t* run_lengths;
   int32_t* long_ids;
@@ -263,7 +264,7 @@ struct RedParams {
 
 hipError_t launch_init(void* header_and_hist, size_t bytes, hipStream_t s);
 hipError_t launch_linearize(const LinParams& p, int grid, hipStream_t s);
-hipError_t launch_sort_pass(const SortParams& p, int grid, hipStream_t s);
+hipError_t launch_sort_pass(const SortParams& p, hipStream_t s);
 hipError_t launch_rle(const RleParams& p, int grid, hipStream_t s);
 hipError_t launch_post(const PostParams& p, int grid, hipStream_t s);
 hipError_t launch_fill(const FillParams& p, int nblocks, hipStream_t s);

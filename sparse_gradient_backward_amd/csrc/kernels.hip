@@ -174,28 +174,16 @@ __global__ void k_init(uint4* p, int64_t n) {
 
 __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
   __shared__ int64_t s_off[kLinBags + 1];
+  __shared__ int64_t s_h0[kLinBags];
+  __shared__ int64_t s_E[kLinBags];
   __shared__ int32_t s_t[kLinBags];
   __shared__ float s_scale[kLinBags];
-  // one digit histogram per wave and pass (conflicting LDS atomics stay
-  // within a wave), summed when the block is done
-  __shared__ uint32_t s_hist[kLinThreads / 64][kHistPasses * kRadixMax];
   __shared__ int s_bad;
-  const int tid = threadIdx.x, wv = tid >> 6;
+  const int tid = threadIdx.x;
 
   for (int64_t q = blockIdx.x * (int64_t)kLinThreads + tid; q < p.zero_vec4;
        q += (int64_t)gridDim.x * kLinThreads)
     p.zero_begin[q] = make_uint4(0u, 0u, 0u, 0u);
-  for (int i = tid; i < (kLinThreads / 64) * kHistPasses * kRadixMax; i += kLinThreads)
-    (&s_hist[0][0])[i] = 0u;
-  __syncthreads();
-
-  auto histogram = [&](uint64_t key, bool valid) {
-    if (!valid) return;
-    for (int ps = 0; ps < p.npasses; ++ps) {
-      const uint32_t d = (uint32_t)(key >> p.pass_shift[ps]) & ((1u << p.pass_bits[ps]) - 1u);
-      atomicAdd(&s_hist[wv][ps * kRadixMax + d], 1u);
-    }
-  };
 
   if (p.offsets == nullptr) {
     // nobag with a single table and no offsets: lookup i is token i of table 0
@@ -217,7 +205,6 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
           p.kv_out[i] = (key << p.info_bits) | (uint64_t)i;
         }
         set_status_wave(p.status, kStIndex, bad);
-        histogram(key, valid);
       }
     }
   } else {
@@ -227,17 +214,30 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
       const int64_t b0 = tile * kLinBags;
       const int nb = (int)min((int64_t)kLinBags, nbags - b0);
       if (tid == 0) s_bad = 0;
-      __syncthreads();
-      for (int j = tid; j <= nb; j += kLinThreads) {
-        const int64_t v = p.offsets[b0 + j];
-        const bool bad = v < 0 || v > p.N || (b0 + j == 0 && v != 0) ||
-                         (b0 + j == nbags && v != p.N);
-        if (bad) s_bad = 1;
-        s_off[j] = v < 0 ? 0 : (v > p.N ? p.N : v);
+      // offsets of the tile's bags and the row range of each bag's table,
+      // loaded together (the table of bag t*B+b is known without offsets)
+      int64_t ov = 0, h0 = 0, h1 = 0;
+      if (tid <= nb) ov = p.offsets[b0 + tid];
+      if (tid < nb) {
+        int t = (int)((b0 + tid) / p.B);
+        t = t < p.T ? t : p.T - 1;
+        s_t[tid] = t;
+        h0 = p.hsc[t];
+        h1 = p.hsc[t + 1];
       }
       __syncthreads();
-      for (int j = tid + 1; j <= nb; j += kLinThreads)
-        if (s_off[j] < s_off[j - 1]) s_bad = 1;
+      if (tid <= nb) {
+        const bool bad = ov < 0 || ov > p.N || (b0 + tid == 0 && ov != 0) ||
+                         (b0 + tid == nbags && ov != p.N);
+        if (bad) s_bad = 1;
+        s_off[tid] = ov < 0 ? 0 : (ov > p.N ? p.N : ov);
+      }
+      if (tid < nb) {
+        s_h0[tid] = h0;
+        s_E[tid] = h1 - h0;
+      }
+      __syncthreads();
+      if (tid >= 1 && tid <= nb && s_off[tid] < s_off[tid - 1]) s_bad = 1;
       __syncthreads();
       if (s_bad) {
         if (tid == 0) {
@@ -247,17 +247,24 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
         }
         __syncthreads();
       }
-      for (int j = tid; j < nb; j += kLinThreads) {
-        const int64_t bg = b0 + j;
-        int t = (int)(bg / p.B);
-        s_t[j] = t < p.T ? t : p.T - 1;
-        const int64_t L = s_off[j + 1] - s_off[j];
-        s_scale[j] = (p.pooling == kPoolMean && L > 0) ? 1.0f / (float)L : 1.0f;
+      if (tid < nb) {
+        const int64_t L = s_off[tid + 1] - s_off[tid];
+        s_scale[tid] = (p.pooling == kPoolMean && L > 0) ? 1.0f / (float)L : 1.0f;
       }
       __syncthreads();
       const int64_t i0 = s_off[0], i1 = s_off[nb];
-      for (int64_t c = i0; c < i1; c += kLinLookups) {
-        for (int k = 0; k < kLinLookups / kLinThreads; ++k) {
+      for (int64_t c = i0; c < i1; c += kLinThreads * kLinPer) {
+        // every load of the chunk first, then the work
+        int64_t idx[kLinPer];
+        float w[kLinPer];
+#pragma unroll
+        for (int k = 0; k < kLinPer; ++k) {
+          const int64_t i = c + k * kLinThreads + tid;
+          idx[k] = i < i1 ? p.indices[i] : 0;
+          w[k] = (i < i1 && p.psw) ? p.psw[i] : 1.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < kLinPer; ++k) {
           const int64_t i = c + k * kLinThreads + tid;
           const bool valid = i < i1;
           uint64_t key = 0;
@@ -272,77 +279,167 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
                 hi = mid;
             }
             const int t = s_t[lo];
-            const int64_t h0 = p.hsc[t], E = p.hsc[t + 1] - h0;
-            int64_t idx = p.indices[i];
-            if (idx < 0 || idx >= E) {
+            const int64_t E = s_E[lo];
+            int64_t x = idx[k];
+            if (x < 0 || x >= E) {
               bad = true;
-              idx = idx < 0 ? 0 : E - 1;
+              x = x < 0 ? 0 : E - 1;
             }
-            key = (uint64_t)(h0 + idx);
+            key = (uint64_t)(s_h0[lo] + x);
             const uint64_t info = p.pooling == kPoolNone ? (uint64_t)i * (uint64_t)p.T + (uint64_t)t
                                                          : (uint64_t)(b0 + lo);
             p.kv_out[i] = (key << p.info_bits) | info;
-            if (p.coef_out) p.coef_out[i] = s_scale[lo] * (p.psw ? p.psw[i] : 1.0f);
+            if (p.coef_out) p.coef_out[i] = s_scale[lo] * w[k];
           }
           set_status_wave(p.status, kStIndex, bad);
-          histogram(key, valid);
         }
       }
       __syncthreads();
     }
   }
-  __syncthreads();
-  for (int i = tid; i < p.npasses * kRadixMax; i += kLinThreads) {
-    uint32_t v = 0;
+}
+
+// ------------------------------------------------------------------ radix sort
+//
+// One stable LSD pass over `bits` (<= 9) digit bits at `shift` of the packed
+// word, as reduce-then-scan in three kernels (no workgroup waits for another):
+//   k_sort_count    digit counts of every tile, stored digit-major
+//   k_sort_offsets  one workgroup per digit: exclusive scan of its counts over
+//                   the tiles; the last one to finish also scans the digit
+//                   totals into the digits' global bases
+//   k_sort_scatter  ranks each tile's items by digit, stably, and writes each
+//                   digit group to its offset
+// Ranking (the multisplit of Adinets & Merrill, "Onesweep", 2022, done per
+// wave64): the lanes of one item round find their same-digit peers with one
+// ballot per digit bit -- a lane's peers are the lanes that agree with it on
+// every bit.  Its cost does not depend on the data; LDS atomics would
+// serialise on the hot digits of skewed keys.  Rank = per-wave running count
+// of the digit + peers in lower lanes.  Items are loaded wave-striped, so
+// (wave, item, lane) order is input order and the pass is stable.  The tile
+// is reordered by digit in LDS so the global writes of each digit group are
+// contiguous; keys, then coefficients, pass through the same LDS buffer.
+
+__device__ __forceinline__ uint32_t digit_of(uint64_t kv, int shift, uint32_t dmask) {
+  return (uint32_t)(kv >> shift) & dmask;
+}
+
+// Lanes of a wave that share a sub-histogram in k_sort_count: 4 copies per
+// wave cut same-address conflicts of skewed keys fourfold.
+constexpr int kCountCopies = (kSortThreads / 64) * 4;
+
+__global__ __launch_bounds__(kSortThreads) void k_sort_count(SortParams p) {
+  __shared__ uint32_t s_h[kCountCopies][kRadixMax];
+  const int tid = threadIdx.x, w = (tid >> 6) * 4 + (tid & 3);
+  const uint32_t tile = blockIdx.x;
+  const int radix = 1 << p.bits;
+  const uint32_t dmask = (uint32_t)radix - 1u;
+  for (int d = tid; d < kCountCopies * kRadixMax; d += kSortThreads) (&s_h[0][0])[d] = 0u;
+  const int64_t base = (int64_t)tile * kSortTile;
+  const int n = (int)min((int64_t)kSortTile, p.N - base);
+  uint64_t kv[kSortItems];
 #pragma unroll
-    for (int w = 0; w < kLinThreads / 64; ++w) v += s_hist[w][i];
-    if (v) atomicAdd(&p.hist[i], v);
+  for (int k = 0; k < kSortItems; ++k) {
+    const int q = k * kSortThreads + tid;
+    kv[k] = q < n ? p.kv_in[base + q] : 0ull;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kSortItems; ++k)
+    if (k * kSortThreads + tid < n) atomicAdd(&s_h[w][digit_of(kv[k], p.shift, dmask)], 1u);
+  __syncthreads();
+  for (int d = tid; d < radix; d += kSortThreads) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int ww = 0; ww < kCountCopies; ++ww) c += s_h[ww][d];
+    p.counts[(size_t)d * p.tiles + tile] = c;
   }
 }
 
-// ------------------------------------------------------------------ k_sort_pass
-//
-// One stable LSD pass over `bits` (<= 9) digit bits at `shift` of the packed
-// word (Adinets & Merrill, "Onesweep", 2022: digit counts of every pass come
-// from one upfront histogram; each tile ranks locally, looks back per digit
-// for its global offset and scatters once).  Ranking uses wave64 ballot
-// multisplit (match of equal digits across the 64 lanes), with a per-wave
-// LDS counter per digit, so skewed keys never contend on one LDS word.
-// Items are loaded wave-striped, which makes (wave, item, lane) order equal
-// to input order and keeps the pass stable.  The tile is then reordered by
-// digit in LDS so the global writes of each digit are contiguous.
+// Workgroup d: offsets[d][j] = items of digit d in tiles < j, in place over
+// the counts, and the row total.  The last workgroup to finish (arrival
+// ticket) turns the row totals into the digits' global bases.
+__global__ __launch_bounds__(kScanThreads) void k_sort_offsets(SortParams p) {
+  __shared__ uint32_t s_tmp[4];
+  __shared__ uint32_t s_last;
+  const int tid = threadIdx.x;
+  const int d = blockIdx.x;
+  uint32_t* row = p.counts + (size_t)d * p.tiles;
+  uint32_t carry = 0;
+  for (int64_t c0 = 0; c0 < p.tiles; c0 += (int64_t)kScanThreads * kScanItems) {
+    uint32_t v[kScanItems];
+    uint32_t sum = 0;
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) {
+      const int64_t j = c0 + (int64_t)tid * kScanItems + k;
+      v[k] = j < p.tiles ? row[j] : 0u;
+      sum += v[k];
+    }
+    uint32_t total;
+    uint32_t run = carry + block_excl_scan<uint32_t>(sum, s_tmp, total);
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) {
+      const int64_t j = c0 + (int64_t)tid * kScanItems + k;
+      if (j < p.tiles) row[j] = run;
+      run += v[k];
+    }
+    carry += total;
+  }
+  // publish the row total (device scope: the last workgroup may run on
+  // another XCD), wait for the store, then count the arrival
+  if (tid == 0) {
+    __hip_atomic_store(&p.bases[d], carry, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    s_last = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u ==
+             gridDim.x;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  const int radix = (int)gridDim.x;
+  uint32_t t2[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int e = 2 * tid + h;
+    t2[h] = e < radix ? __hip_atomic_load(&p.bases[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                      : 0u;
+  }
+  uint32_t tot;
+  const uint32_t ex = block_excl_scan<uint32_t>(t2[0] + t2[1], s_tmp, tot);
+  if (2 * tid < radix) p.bases[2 * tid] = ex;
+  if (2 * tid + 1 < radix) p.bases[2 * tid + 1] = ex + t2[0];
+}
 
-__global__ __launch_bounds__(kSortThreads) void k_sort_pass(SortParams p) {
-  __shared__ uint64_t s_kv[kSortTile];
-  __shared__ float s_coef[kSortTile];
+// Same-digit peers of this lane among the valid lanes: the lanes that agree
+// with it on each of the `bits` low bits of d.  Wave-uniform call.
+__device__ __forceinline__ uint64_t digit_peers(uint32_t d, int bits, bool valid) {
+  uint32_t mlo = 0, mhi = 0;  // lanes that differ from this one on some bit
+#pragma unroll
+  for (int b = 0; b < 9; ++b) {
+    if (b < bits) {  // uniform
+      const int32_t sx = -(int32_t)((d >> b) & 1u);  // 0 or all ones
+      const uint64_t m = __ballot(sx != 0);
+      mlo |= (uint32_t)m ^ (uint32_t)sx;
+      mhi |= (uint32_t)(m >> 32) ^ (uint32_t)sx;
+    }
+  }
+  const uint64_t live = __ballot(valid);
+  return valid ? (~(((uint64_t)mhi << 32) | mlo) & live) : 0ull;
+}
+
+__global__ __launch_bounds__(kSortThreads) void k_sort_scatter(SortParams p) {
+  __shared__ uint64_t s_kv[kSortTile];  // keys, then coefficients, in tile order by digit
   __shared__ uint32_t s_wcnt[kSortThreads / 64][kRadixMax];
   __shared__ uint32_t s_local[kRadixMax];
   __shared__ int32_t s_gbase[kRadixMax];
-  __shared__ uint32_t s_dglob[kRadixMax];
   __shared__ uint32_t s_tmp[4];
-  __shared__ uint32_t s_tile;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int radix = 1 << p.bits;
-  const uint64_t dmask = (uint64_t)(radix - 1);
+  const uint32_t dmask = (uint32_t)radix - 1u;
   const bool has_coef = p.coef_in != nullptr;
-  if (tid == 0) s_tile = __hip_atomic_fetch_add(p.tile_ctr, 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-  // exclusive prefix of the global digit counts (two digits per thread)
-  {
-    const int d0 = 2 * tid;
-    const uint32_t a = d0 < radix ? p.hist[d0] : 0u;
-    const uint32_t b = d0 + 1 < radix ? p.hist[d0 + 1] : 0u;
-    uint32_t tot;
-    const uint32_t ex = block_excl_scan<uint32_t>(a + b, s_tmp, tot);
-    if (d0 < radix) s_dglob[d0] = ex;
-    if (d0 + 1 < radix) s_dglob[d0 + 1] = ex + a;
-  }
-  for (int d = lane; d < radix; d += 64) s_wcnt[w][d] = 0u;
-  __syncthreads();
-  const uint32_t tile = s_tile;
+  const uint32_t tile = blockIdx.x;
   const int64_t base = (int64_t)tile * kSortTile;
   const int tile_n = (int)min((int64_t)kSortTile, p.N - base);
+  for (int d = lane; d < radix; d += 64) s_wcnt[w][d] = 0u;
 
   uint64_t kv[kSortItems];
   float cf[kSortItems];
@@ -354,17 +451,19 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_pass(SortParams p) {
     kv[k] = valid ? p.kv_in[base + e] : 0ull;
     cf[k] = (valid && has_coef) ? p.coef_in[base + e] : 0.0f;
   }
+  // global offsets of this tile's digit groups (independent of the ranking)
+  uint32_t goff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int d = 2 * tid + h;
+    goff[h] = d < radix ? p.bases[d] + p.counts[(size_t)d * p.tiles + tile] : 0u;
+  }
 #pragma unroll
   for (int k = 0; k < kSortItems; ++k) {
     const int e = w * 64 * kSortItems + k * 64 + lane;
     const bool valid = e < tile_n;
-    const uint32_t d = (uint32_t)((kv[k] >> p.shift) & dmask);
-    uint64_t peers = __ballot(valid);
-    for (int b = 0; b < p.bits; ++b) {
-      const bool bit = (d >> b) & 1u;
-      const uint64_t m = __ballot(bit);
-      peers &= bit ? m : ~m;
-    }
+    const uint32_t d = digit_of(kv[k], p.shift, dmask);
+    const uint64_t peers = digit_peers(d, p.bits, valid);
     const uint32_t below = bits_below(peers);
     const uint32_t before = valid ? s_wcnt[w][d] : 0u;
     rank[k] = before + below;
@@ -372,7 +471,7 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_pass(SortParams p) {
   }
   __syncthreads();
 
-  // per digit: exclusive offsets of the waves, tile count, published early
+  // per digit: exclusive offsets of the waves and the tile's count
   uint32_t cnt[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -385,118 +484,64 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_pass(SortParams p) {
         s_wcnt[ww][d] = acc;
         acc += c;
       }
-      __hip_atomic_store(&p.lookback[(size_t)tile * kRadixMax + d],
-                         (tile == 0 ? kFlagP32 : kFlagA32) | acc, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
     }
     cnt[h] = acc;
   }
   {
     uint32_t tot;
     const uint32_t ex = block_excl_scan<uint32_t>(cnt[0] + cnt[1], s_tmp, tot);
-    if (2 * tid < radix) s_local[2 * tid] = ex;
-    if (2 * tid + 1 < radix) s_local[2 * tid + 1] = ex + cnt[0];
+    if (2 * tid < radix) {
+      s_local[2 * tid] = ex;
+      s_gbase[2 * tid] = (int32_t)goff[0] - (int32_t)ex;
+    }
+    if (2 * tid + 1 < radix) {
+      s_local[2 * tid + 1] = ex + cnt[0];
+      s_gbase[2 * tid + 1] = (int32_t)goff[1] - (int32_t)(ex + cnt[0]);
+    }
   }
   __syncthreads();
+  // tile position of every item, then keys through LDS to their groups
 #pragma unroll
   for (int k = 0; k < kSortItems; ++k) {
     const int e = w * 64 * kSortItems + k * 64 + lane;
     if (e < tile_n) {
-      const uint32_t d = (uint32_t)((kv[k] >> p.shift) & dmask);
-      const uint32_t pos = s_local[d] + s_wcnt[w][d] + rank[k];
-      s_kv[pos] = kv[k];
-      if (has_coef) s_coef[pos] = cf[k];
-    }
-  }
-  // per digit look-back for the offset of this tile's digit group: each
-  // round reads kLookAhead preceding tiles for both of this thread's digits
-  // at once, sums aggregates back to the nearest inclusive prefix, and only
-  // waits when one of the tiles it needs has published nothing yet
-  {
-    constexpr int kLookAhead = 4;
-    uint32_t excl[2] = {0u, 0u};
-    bool done[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) done[h] = (2 * tid + h >= radix) || tile == 0;
-    int64_t top[2] = {(int64_t)tile - 1, (int64_t)tile - 1};
-    uint32_t spins = 0;
-    while (!(done[0] && done[1])) {
-      uint32_t v[2][kLookAhead];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int k = 0; k < kLookAhead; ++k) {
-          const int64_t j = top[h] - k;
-          v[h][k] = (!done[h] && j >= 0)
-                        ? __hip_atomic_load(&p.lookback[(size_t)j * kRadixMax + 2 * tid + h],
-                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                        : kFlagP32;  // before tile 0: prefix 0
-        }
-      bool waiting = false;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (done[h]) continue;
-        uint32_t sum = 0;
-        int used = kLookAhead;
-        bool found = false, notready = false;
-#pragma unroll
-        for (int k = 0; k < kLookAhead; ++k) {
-          if (found || notready) continue;
-          const uint32_t flag = v[h][k] >> 30;
-          if (flag == 0) {
-            notready = true;
-            used = k;
-          } else {
-            sum += v[h][k] & kVal32;
-            if (flag == 2) found = true;
-          }
-        }
-        // tiles before the first not-ready one are consumed either way
-        if (found) {
-          excl[h] += sum;
-          done[h] = true;
-        } else if (!notready) {
-          excl[h] += sum;
-          top[h] -= kLookAhead;
-        } else {
-          uint32_t part = 0;
-#pragma unroll
-          for (int k = 0; k < kLookAhead; ++k)
-            if (k < used) part += v[h][k] & kVal32;
-          excl[h] += part;
-          top[h] -= used;
-          waiting = true;
-        }
-      }
-      if (waiting) {
-        if (++spins > kSpinLimit) {
-          set_status(p.status, kStInternal);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int d = 2 * tid + h;
-      if (d >= radix) continue;
-      if (tile > 0)
-        __hip_atomic_store(&p.lookback[(size_t)tile * kRadixMax + d], kFlagP32 | (excl[h] + cnt[h]),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_gbase[d] = (int32_t)(s_dglob[d] + excl[h]) - (int32_t)s_local[d];
+      const uint32_t d = digit_of(kv[k], p.shift, dmask);
+      rank[k] += s_local[d] + s_wcnt[w][d];
+      s_kv[rank[k]] = kv[k];
     }
   }
   __syncthreads();
   for (int q = tid; q < tile_n; q += kSortThreads) {
     const uint64_t v = s_kv[q];
-    const uint32_t d = (uint32_t)((v >> p.shift) & dmask);
-    const int64_t pos = (int64_t)s_gbase[d] + q;
+    const int64_t pos = (int64_t)s_gbase[digit_of(v, p.shift, dmask)] + q;
     const bool okp = pos >= 0 && pos < p.N;
-    if (okp) {
-      p.kv_out[pos] = v;
-      if (has_coef) p.coef_out[pos] = s_coef[q];
-    }
+    if (okp) p.kv_out[pos] = v;
     set_status_wave(p.status, kStInternal, !okp);
+  }
+  if (!has_coef) return;
+  // coefficients the same way; the digit of each tile slot is read back from
+  // the keys before the buffer is reused
+  uint32_t slot_d[kSortItems];
+#pragma unroll
+  for (int k = 0; k < kSortItems; ++k) {
+    const int q = k * kSortThreads + tid;
+    slot_d[k] = q < tile_n ? digit_of(s_kv[q], p.shift, dmask) : 0u;
+  }
+  __syncthreads();
+  float* s_cf = reinterpret_cast<float*>(s_kv);
+#pragma unroll
+  for (int k = 0; k < kSortItems; ++k) {
+    const int e = w * 64 * kSortItems + k * 64 + lane;
+    if (e < tile_n) s_cf[rank[k]] = cf[k];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kSortItems; ++k) {
+    const int q = k * kSortThreads + tid;
+    if (q < tile_n) {
+      const int64_t pos = (int64_t)s_gbase[slot_d[k]] + q;
+      if (pos >= 0 && pos < p.N) p.coef_out[pos] = s_cf[q];
+    }
   }
 }
 
@@ -520,8 +565,22 @@ __global__ __launch_bounds__(kScanThreads) void k_rle(RleParams p) {
   const uint32_t tile = s_tile;
   const int64_t base = (int64_t)tile * kScanTile;
   const int n = (int)min((int64_t)kScanTile, p.N - base);
-  for (int q = tid; q < n; q += kScanThreads) s_key[q + 1] = p.kv[base + q] >> p.info_bits;
-  if (tid == 0) s_key[0] = base > 0 ? (p.kv[base - 1] >> p.info_bits) : ~0ull;
+  {
+    // all loads of the tile in flight at once, then into LDS
+    uint64_t v[kScanItems];
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) {
+      const int q = k * kScanThreads + tid;
+      v[k] = q < n ? p.kv[base + q] : 0ull;
+    }
+    const uint64_t before_tile = (tid == 0 && base > 0) ? p.kv[base - 1] : 0ull;
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) {
+      const int q = k * kScanThreads + tid;
+      if (q < n) s_key[q + 1] = v[k] >> p.info_bits;
+    }
+    if (tid == 0) s_key[0] = base > 0 ? (before_tile >> p.info_bits) : ~0ull;
+  }
   __syncthreads();
   uint32_t heads = 0, cnt = 0;
 #pragma unroll
@@ -567,59 +626,83 @@ __global__ __launch_bounds__(kScanThreads) void k_rle(RleParams p) {
 // clears the combine tickets of those items and, for a fresh dense gradient,
 // marks touched rows in a bitmap.
 
-// Table of a linear id (binary search of hash_size_cumsum).
-__device__ __forceinline__ int table_of_id(const int64_t* hsc, int T, int64_t id) {
-  int lo = 0, hi = T;  // hsc[lo] <= id < hsc[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (hsc[mid] <= id)
-      lo = mid;
-    else
-      hi = mid;
-  }
-  return lo;
+// Table of a run from the info of one of its lookups (bag t*B+b, or token
+// l*T+t without bags).
+__device__ __forceinline__ int table_of_info(const PostParams& p, uint32_t info) {
+  const int t = p.nobag ? (int)(info % (uint32_t)p.T) : (int)(info / (uint32_t)p.B);
+  return t < p.T ? t : p.T - 1;
 }
 
 __global__ __launch_bounds__(kScanThreads) void k_post(PostParams p) {
+  __shared__ int32_t s_cum[kScanTile + 1];
   __shared__ uint64_t s_tmp[4];
   __shared__ uint32_t s_tile;
   __shared__ uint64_t s_excl;
   const int tid = threadIdx.x;
   const int U = *p.num_runs;
+  // the grid is sized for N runs; workgroups past the last run leave before
+  // taking a tile id, so the ids handed out are exactly the tiles of U runs
+  if ((int64_t)blockIdx.x * kScanTile >= U) return;
   if (tid == 0) s_tile = __hip_atomic_fetch_add(p.tile_ctr, 1u, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const uint32_t tile = s_tile;
   const int64_t base = (int64_t)tile * kScanTile;
-  if (base >= U) return;
   const int n = (int)min((int64_t)kScanTile, (int64_t)U - base);
-  int len[kScanItems];
-  int ncb[kScanItems];
-  int Dk[kScanItems];
-  uint64_t sum = 0;
+  const uint64_t imask = p.info_bits >= 64 ? ~0ull : ((1ull << p.info_bits) - 1ull);
+  {
+    // run starts base .. base+n (n+1 values) into LDS, all loads in flight
+    int32_t v[kScanItems];
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) {
+      const int q = k * kScanThreads + tid;
+      v[k] = q < n ? p.cum[base + q] : 0;
+    }
+    const int32_t last = tid == 0 ? p.cum[base + n] : 0;
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) {
+      const int q = k * kScanThreads + tid;
+      if (q < n) s_cum[q] = v[k];
+    }
+    if (tid == 0) s_cum[n] = last;
+  }
+  __syncthreads();
+  // this thread's kScanItems consecutive runs: lengths and long-run items.
+  // A long run's table comes from the info of its first lookup; all these
+  // loads are issued together, then the row widths.
+  uint32_t longmask = 0;
 #pragma unroll
   for (int k = 0; k < kScanItems; ++k) {
     const int q = tid * kScanItems + k;
-    len[k] = 0;
-    ncb[k] = 1;
-    Dk[k] = 4;
-    if (q < n) {
-      const int64_t r = base + q;
-      len[k] = p.cum[r + 1] - p.cum[r];
-      p.run_lengths[r] = len[k];
-      if (len[k] >= p.thr) {
-        // a long run becomes nch chunks x ncb column blocks of work items
-        const int t = table_of_id(p.hsc, p.T, p.unique_ids[r]);
-        Dk[k] = p.doff[t + 1] - p.doff[t];
-        ncb[k] = col_blocks(Dk[k]);
-        const int cl = chunk_len(len[k], Dk[k]);
-        sum += (1ull << 31) | (uint64_t)(((len[k] + cl - 1) / cl) * ncb[k]);
-      }
-      if (p.bitmap) {
-        const uint64_t key = (uint64_t)p.unique_ids[r];
-        if (key < (uint64_t)p.total_rows) atomicOr(&p.bitmap[key >> 5], 1u << (key & 31));
-      }
+    if (q < n && s_cum[q + 1] - s_cum[q] >= p.thr) longmask |= 1u << k;
+  }
+  // (the loads are unconditional, from index 0 where there is nothing to
+  // read, so that none of them waits behind a branch for the one before)
+  int tq[kScanItems], Dq[kScanItems];
+  if (longmask) {
+    uint64_t raw[kScanItems];
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k)
+      raw[k] = p.kv[((longmask >> k) & 1u) ? s_cum[tid * kScanItems + k] : 0];
+    int dlo[kScanItems], dhi[kScanItems];
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) {
+      tq[k] = ((longmask >> k) & 1u) ? table_of_info(p, (uint32_t)(raw[k] & imask)) : 0;
+      dlo[k] = p.doff[tq[k]];
+      dhi[k] = p.doff[tq[k] + 1];
     }
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) Dq[k] = ((longmask >> k) & 1u) ? dhi[k] - dlo[k] : 4;
+  }
+  uint64_t sum = 0;
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) {
+    if (!((longmask >> k) & 1u)) continue;
+    // a long run becomes nch chunks x ncb column blocks of work items
+    const int q = tid * kScanItems + k;
+    const int len = s_cum[q + 1] - s_cum[q];
+    const int cl = chunk_len(len, Dq[k]);
+    sum += (1ull << 31) | (uint64_t)(((len + cl - 1) / cl) * col_blocks(Dq[k]));
   }
   uint64_t total;
   const uint64_t before = block_excl_scan<uint64_t>(sum, s_tmp, total);
@@ -627,32 +710,69 @@ __global__ __launch_bounds__(kScanThreads) void k_post(PostParams p) {
     const uint64_t ex = wave_lookback<uint64_t>(p.lookback, tile, total, p.status);
     if (tid == 0) s_excl = ex;
   }
+  // run lengths, coalesced
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) {
+    const int q = k * kScanThreads + tid;
+    if (q < n) p.run_lengths[base + q] = s_cum[q + 1] - s_cum[q];
+  }
+  if (p.bitmap) {
+    // touched rows: lanes holding ids of the same 32-bit word (ids ascend
+    // along the lanes) OR their bits together; the first lane of each such
+    // segment does the one atomic
+    const int lane = tid & 63;
+#pragma unroll 1
+    for (int k = 0; k < kScanItems; ++k) {
+      const int q = k * kScanThreads + tid;
+      const bool ok = q < n;
+      const uint64_t key = ok ? (uint64_t)p.unique_ids[base + q] : ~0ull;
+      const bool in = ok && key < (uint64_t)p.total_rows;
+      const uint64_t word = in ? key >> 5 : ~0ull;
+      uint32_t bits = in ? 1u << (key & 31) : 0u;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t ob = __shfl_down(bits, off, 64);
+        const uint64_t ow = __shfl_down(word, off, 64);
+        if (lane + off < 64 && ow == word) bits |= ob;
+      }
+      const uint64_t pw = __shfl_up(word, 1, 64);
+      if (in && (lane == 0 || pw != word)) atomicOr(&p.bitmap[word], bits);
+    }
+  }
+  int64_t ids[kScanItems];
+  if (longmask) {
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k)
+      ids[k] = p.unique_ids[base + (((longmask >> k) & 1u) ? tid * kScanItems + k : 0)];
+  }
   __syncthreads();
   uint64_t at = s_excl + before;
 #pragma unroll
   for (int k = 0; k < kScanItems; ++k) {
+    if (!((longmask >> k) & 1u)) continue;
     const int q = tid * kScanItems + k;
-    if (q < n && len[k] >= p.thr) {
-      const uint32_t pos = (uint32_t)(at >> 31);
-      const uint32_t c0 = (uint32_t)(at & kField);
-      const int cl = chunk_len(len[k], Dk[k]);
-      const int nch = (len[k] + cl - 1) / cl;
-      p.long_ids[pos] = (int32_t)(base + q);
-      p.chunk_begin[pos] = c0;
-      LongRun rec;
-      rec.start = p.cum[base + q];
-      rec.len = len[k];
-      rec.t = table_of_id(p.hsc, p.T, p.unique_ids[base + q]);
-      rec.ncb = ncb[k];
-      rec.cbeg = c0;
-      rec.nch = nch;
-      rec.id = p.unique_ids[base + q];
-      p.long_recs[pos] = rec;
-      for (int cb = 0; cb < ncb[k]; ++cb) p.run_ticket[c0 + cb] = 0u;
-      for (int sc = 0; sc < nch; sc += kSuperChunk)
-        for (int cb = 0; cb < ncb[k]; ++cb) p.sc_ticket[c0 + sc * ncb[k] + cb] = 0u;
-      at += (1ull << 31) | (uint64_t)(nch * ncb[k]);
-    }
+    const int len = s_cum[q + 1] - s_cum[q];
+    const int D = Dq[k];
+    const int ncb = col_blocks(D);
+    const int cl = chunk_len(len, D);
+    const int nch = (len + cl - 1) / cl;
+    const uint32_t pos = (uint32_t)(at >> 31);
+    const uint32_t c0 = (uint32_t)(at & kField);
+    p.long_ids[pos] = (int32_t)(base + q);
+    p.chunk_begin[pos] = c0;
+    LongRun rec;
+    rec.start = s_cum[q];
+    rec.len = len;
+    rec.t = tq[k];
+    rec.ncb = ncb;
+    rec.cbeg = c0;
+    rec.nch = nch;
+    rec.id = ids[k];
+    p.long_recs[pos] = rec;
+    for (int cb = 0; cb < ncb; ++cb) p.run_ticket[c0 + cb] = 0u;
+    for (int sc = 0; sc < nch; sc += kSuperChunk)
+      for (int cb = 0; cb < ncb; ++cb) p.sc_ticket[c0 + sc * ncb + cb] = 0u;
+    at += (1ull << 31) | (uint64_t)(nch * ncb);
   }
   if (tid == 0 && base + n == U) {
     const uint64_t all = s_excl + total;
@@ -1387,8 +1507,11 @@ hipError_t launch_linearize(const LinParams& p, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_sort_pass(const SortParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(k_sort_pass, dim3(grid), dim3(kSortThreads), 0, s, p);
+hipError_t launch_sort_pass(const SortParams& p, hipStream_t s) {
+  const unsigned tiles = (unsigned)p.tiles;
+  hipLaunchKernelGGL(k_sort_count, dim3(tiles), dim3(kSortThreads), 0, s, p);
+  hipLaunchKernelGGL(k_sort_offsets, dim3(1u << p.bits), dim3(kScanThreads), 0, s, p);
+  hipLaunchKernelGGL(k_sort_scatter, dim3(tiles), dim3(kSortThreads), 0, s, p);
   return hipGetLastError();
 }
 
