@@ -77,7 +77,7 @@ struct Layout {
   int64_t sort_tiles = 0, scan_tiles = 0;
   int64_t max_long = 0;   // bound on the number of long runs
   int64_t max_items = 0;  // bound on the (chunk, column block) items over all long runs
-  size_t hdr = 0, hist = 0, counts = 0, zero_begin = 0, rle_lb = 0, post_lb = 0, bitmap = 0,
+  size_t hdr = 0, hist = 0, counts = 0, zero_begin = 0, tile_runs = 0, post_lb = 0, bitmap = 0,
          zero_end_nobitmap = 0, zero_end_bitmap = 0;
   size_t kvA = 0, kvB = 0, coefA = 0, coefB = 0, uniq = 0, cum = 0, headrun = 0, lens = 0, longs = 0,
          chunkb = 0, longrec = 0, runtk = 0, sctk = 0, part = 0, total = 0;
@@ -124,12 +124,12 @@ sgb_status make_layout(const sgb_plan_s* p, int64_t N, int32_t B, bool has_offse
   L->hdr = take(sizeof(Header));
   L->hist = take(sizeof(uint32_t) * kMaxPasses * kRadixMax);  // digit bases of each pass
   L->zero_begin = align_up(o, 256);
-  L->rle_lb = take(sizeof(uint32_t) * (size_t)L->scan_tiles);
   L->post_lb = take(sizeof(uint64_t) * (size_t)L->scan_tiles);
   L->zero_end_nobitmap = align_up(o, 256);
   L->bitmap = take(sizeof(uint32_t) * (size_t)((p->total_rows + 31) / 32));
   L->zero_end_bitmap = align_up(o, 256);
   L->counts = take(sizeof(uint32_t) * (size_t)L->sort_tiles * kRadixMax);
+  L->tile_runs = take(sizeof(uint32_t) * (size_t)L->scan_tiles);
   L->kvA = take(sizeof(uint64_t) * (size_t)N);
   L->kvB = take(sizeof(uint64_t) * (size_t)N);
   L->coefA = take(sizeof(float) * (size_t)N);
@@ -390,11 +390,10 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   rp.cum = at<int32_t>(ws, L.cum);
   rp.head_run = at<int32_t>(ws, L.headrun);
   rp.num_runs = &hdr->num_runs;
-  rp.lookback = at<uint32_t>(ws, L.rle_lb);
-  rp.tile_ctr = &hdr->rle_tile_ctr;
-  rp.status = status;
+  rp.tiles = L.scan_tiles;
+  rp.tile_runs = at<uint32_t>(ws, L.tile_runs);
   mark(SGB_STAGE_RLE, 0);
-  if (launch_rle(rp, (int)L.scan_tiles, stream) != hipSuccess) return SGB_ERR_HIP;
+  if (launch_rle(rp, stream) != hipSuccess) return SGB_ERR_HIP;
   mark(SGB_STAGE_RLE, 1);
 
   PostParams pp{};

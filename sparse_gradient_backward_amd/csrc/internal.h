@@ -113,7 +113,7 @@ enum { kModeDense = 0, kModeSgd = 1, kModeAdagrad = 2 };
 struct Header {
   uint32_t status;                    // first device-detected error, 0 = none
   uint32_t sort_ticket[kMaxPasses];   // last-arrival counters of the sort passes
-  uint32_t rle_tile_ctr;
+  uint32_t unused0;
   uint32_t post_tile_ctr;
   uint32_t work_ctr;                  // reducer work queue
   int32_t num_runs;                   // U
@@ -178,14 +178,13 @@ struct SortParams {
 struct RleParams {
   const uint64_t* kv;       // sorted
   int64_t N;
+  int64_t tiles;            // tiles of kScanTile positions
   int32_t info_bits;
   int64_t* unique_ids;
   int32_t* cum;
   int32_t* head_run;        // [N]: run index at each run's first position
   int32_t* num_runs;
-  uint32_t* lookback;       // [tiles]
-  uint32_t* tile_ctr;
-  uint32_t* status;
+  uint32_t* tile_runs;      // [tiles]: runs starting in each tile, then the first run index
 };
 
 struct PostParams {
@@ -265,7 +264,7 @@ struct RedParams {
 hipError_t launch_init(void* header_and_hist, size_t bytes, hipStream_t s);
 hipError_t launch_linearize(const LinParams& p, int grid, hipStream_t s);
 hipError_t launch_sort_pass(const SortParams& p, hipStream_t s);
-hipError_t launch_rle(const RleParams& p, int grid, hipStream_t s);
+hipError_t launch_rle(const RleParams& p, hipStream_t s);
 hipError_t launch_post(const PostParams& p, int grid, hipStream_t s);
 hipError_t launch_fill(const FillParams& p, int nblocks, hipStream_t s);
 hipError_t launch_reduce_long(const RedParams& p, bool bf16, int grid, hipStream_t s);

@@ -6,7 +6,7 @@
 //                and coefficient; digit histograms of every sort pass
 //   k_sort_pass  one stable LSD radix pass (<= 9-bit digits), single sweep
 //                with decoupled look-back, LDS-staged scatter
-//   k_rle        run heads of the sorted ids -> unique ids, run starts, count
+//   k_rle_*      run heads of the sorted ids -> unique ids, run starts, count
 //   k_post       run lengths, ascending long-run list with chunk prefix
 //   k_fill       zeros for untouched rows of a fresh dense gradient
 //   k_reduce_long   (chunk, column block) items of long runs from an atomic
@@ -545,74 +545,143 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(SortParams p) {
   }
 }
 
-// ------------------------------------------------------------------ k_rle
+// ------------------------------------------------------------------ run-length encoding
 //
 // Run-length encoding of the sorted ids: position i starts a run when its id
-// differs from position i-1.  Heads are counted per tile, the tile's run
-// offset comes from a wave-wide look-back, and each head writes its unique id
-// and its start (the exclusive scan of run lengths, FBGEMM
-// `sorted_linear_indices_cumulative_run_lengths`).  The last tile writes the
-// run count and the closing start N.
+// differs from position i-1.  Reduce-then-scan in three kernels:
+//   k_rle_count  run heads of every tile
+//   k_rle_scan   one workgroup: exclusive scan of the tile counts (each
+//                tile's first run index), the run count U and the closing
+//                run start N
+//   k_rle_write  each head writes its unique id and its start (the exclusive
+//                scan of run lengths, FBGEMM
+//                `sorted_linear_indices_cumulative_run_lengths`), and its run
+//                index at its position
+// Items are read coalesced (item k of thread t is position k*256 + t); a
+// position's predecessor is the previous lane, or for lane 0 the last lane of
+// the wave before it in that order (through LDS).
 
-__global__ __launch_bounds__(kScanThreads) void k_rle(RleParams p) {
-  __shared__ uint64_t s_key[kScanTile + 1];
-  __shared__ uint32_t s_tmp[4];
-  __shared__ uint32_t s_tile, s_excl;
-  const int tid = threadIdx.x;
-  if (tid == 0) s_tile = __hip_atomic_fetch_add(p.tile_ctr, 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
+// Ids of this thread's kScanItems positions and which of them start a run.
+// Returns the head bits; ids land in key[].
+__device__ __forceinline__ uint32_t rle_heads(const RleParams& p, int64_t base, int n,
+                                              uint64_t* key, uint64_t (*s_edge)[kScanThreads / 64]) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) {
+    const int q = k * kScanThreads + tid;
+    key[k] = (q < n ? p.kv[base + q] : 0ull) >> p.info_bits;
+  }
+  const uint64_t before_tile =
+      (tid == 0 && base > 0) ? (p.kv[base - 1] >> p.info_bits) : ~0ull;
+  if (lane == 63) {
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) s_edge[k][w] = key[k];
+  }
   __syncthreads();
-  const uint32_t tile = s_tile;
-  const int64_t base = (int64_t)tile * kScanTile;
+  uint32_t heads = 0;
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) {
+    const int q = k * kScanThreads + tid;
+    uint64_t prev = __shfl_up(key[k], 1, 64);
+    if (lane == 0) {
+      if (w > 0)
+        prev = s_edge[k][w - 1];
+      else if (k > 0)
+        prev = s_edge[k - 1][kScanThreads / 64 - 1];
+      else
+        prev = before_tile;
+    }
+    if (q < n && (base + q == 0 || key[k] != prev)) heads |= 1u << k;
+  }
+  return heads;
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_rle_count(RleParams p) {
+  __shared__ uint64_t s_edge[kScanItems][kScanThreads / 64];
+  __shared__ uint32_t s_w[kScanThreads / 64];
+  const int64_t base = (int64_t)blockIdx.x * kScanTile;
   const int n = (int)min((int64_t)kScanTile, p.N - base);
-  {
-    // all loads of the tile in flight at once, then into LDS
-    uint64_t v[kScanItems];
+  uint64_t key[kScanItems];
+  const uint32_t heads = rle_heads(p, base, n, key, s_edge);
+  uint32_t c = 0;
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) c += (uint32_t)__popcll(__ballot((heads >> k) & 1u));
+  if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+#pragma unroll
+    for (int ww = 0; ww < kScanThreads / 64; ++ww) t += s_w[ww];
+    p.tile_runs[blockIdx.x] = t;
+  }
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_rle_scan(RleParams p) {
+  __shared__ uint32_t s_tmp[4];
+  const int tid = threadIdx.x;
+  uint32_t carry = 0;
+  for (int64_t c0 = 0; c0 < p.tiles; c0 += (int64_t)kScanThreads * kScanItems) {
+    uint32_t v[kScanItems];
+    uint32_t sum = 0;
 #pragma unroll
     for (int k = 0; k < kScanItems; ++k) {
-      const int q = k * kScanThreads + tid;
-      v[k] = q < n ? p.kv[base + q] : 0ull;
+      const int64_t j = c0 + (int64_t)tid * kScanItems + k;
+      v[k] = j < p.tiles ? p.tile_runs[j] : 0u;
+      sum += v[k];
     }
-    const uint64_t before_tile = (tid == 0 && base > 0) ? p.kv[base - 1] : 0ull;
+    uint32_t total;
+    uint32_t run = carry + block_excl_scan<uint32_t>(sum, s_tmp, total);
 #pragma unroll
     for (int k = 0; k < kScanItems; ++k) {
-      const int q = k * kScanThreads + tid;
-      if (q < n) s_key[q + 1] = v[k] >> p.info_bits;
+      const int64_t j = c0 + (int64_t)tid * kScanItems + k;
+      if (j < p.tiles) p.tile_runs[j] = run;
+      run += v[k];
     }
-    if (tid == 0) s_key[0] = base > 0 ? (before_tile >> p.info_bits) : ~0ull;
+    carry += total;
   }
-  __syncthreads();
-  uint32_t heads = 0, cnt = 0;
+  if (tid == 0) {
+    p.cum[carry] = (int32_t)p.N;
+    *p.num_runs = (int32_t)carry;
+  }
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_rle_write(RleParams p) {
+  __shared__ uint64_t s_edge[kScanItems][kScanThreads / 64];
+  __shared__ uint32_t s_off[kScanItems * (kScanThreads / 64)];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t base = (int64_t)blockIdx.x * kScanTile;
+  const int n = (int)min((int64_t)kScanTile, p.N - base);
+  uint64_t key[kScanItems];
+  const uint32_t heads = rle_heads(p, base, n, key, s_edge);
+  const uint32_t first = p.tile_runs[blockIdx.x];
+  // heads of every (item round, wave) in tile order, then their exclusive scan
+  uint64_t bal[kScanItems];
 #pragma unroll
   for (int k = 0; k < kScanItems; ++k) {
-    const int q = tid * kScanItems + k;
-    if (q < n && (base + q == 0 || s_key[q + 1] != s_key[q])) {
-      heads |= 1u << k;
-      ++cnt;
-    }
-  }
-  uint32_t total;
-  const uint32_t before = block_excl_scan<uint32_t>(cnt, s_tmp, total);
-  if (tid < 64) {
-    const uint32_t ex = wave_lookback<uint32_t>(p.lookback, tile, total, p.status);
-    if (tid == 0) s_excl = ex;
+    bal[k] = __ballot((heads >> k) & 1u);
+    if (lane == 0) s_off[k * (kScanThreads / 64) + w] = (uint32_t)__popcll(bal[k]);
   }
   __syncthreads();
-  uint32_t run = s_excl + before;
+  if (w == 0) {
+    static_assert(kScanItems * (kScanThreads / 64) == 64, "one lane per (item round, wave)");
+    const uint32_t c = s_off[lane];
+    uint32_t incl = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    s_off[lane] = incl - c;
+  }
+  __syncthreads();
 #pragma unroll
   for (int k = 0; k < kScanItems; ++k) {
-    if (heads & (1u << k)) {
-      const int q = tid * kScanItems + k;
-      p.unique_ids[run] = (int64_t)s_key[q + 1];
-      p.cum[run] = (int32_t)(base + q);
-      p.head_run[base + q] = (int32_t)run;
-      ++run;
-    }
-  }
-  if (tid == 0 && base + n == p.N) {
-    const uint32_t U = s_excl + total;
-    p.cum[U] = (int32_t)p.N;
-    *p.num_runs = (int32_t)U;
+    if (!((heads >> k) & 1u)) continue;
+    const int q = k * kScanThreads + tid;
+    const uint32_t run = first + s_off[k * (kScanThreads / 64) + w] + bits_below(bal[k]);
+    p.unique_ids[run] = (int64_t)key[k];
+    p.cum[run] = (int32_t)(base + q);
+    p.head_run[base + q] = (int32_t)run;
   }
 }
 
@@ -1515,8 +1584,11 @@ hipError_t launch_sort_pass(const SortParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_rle(const RleParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(k_rle, dim3(grid), dim3(kScanThreads), 0, s, p);
+hipError_t launch_rle(const RleParams& p, hipStream_t s) {
+  const unsigned tiles = (unsigned)p.tiles;
+  hipLaunchKernelGGL(k_rle_count, dim3(tiles), dim3(kScanThreads), 0, s, p);
+  hipLaunchKernelGGL(k_rle_scan, dim3(1), dim3(kScanThreads), 0, s, p);
+  hipLaunchKernelGGL(k_rle_write, dim3(tiles), dim3(kScanThreads), 0, s, p);
   return hipGetLastError();
 }
 
