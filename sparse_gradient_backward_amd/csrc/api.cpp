@@ -372,7 +372,6 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
     sp.bits = L.pass_bits[ps];
     sp.counts = at<uint32_t>(ws, L.counts);
     sp.bases = at<uint32_t>(ws, L.hist) + ps * kRadixMax;
-    sp.ticket = &hdr->sort_ticket[ps];
     sp.status = status;
     if (launch_sort_pass(sp, stream) != hipSuccess) return SGB_ERR_HIP;
     std::swap(kv_in, kv_out);

@@ -112,7 +112,7 @@ enum { kModeDense = 0, kModeSgd = 1, kModeAdagrad = 2 };
 // Workspace header (offset 0).
 struct Header {
   uint32_t status;                    // first device-detected error, 0 = none
-  uint32_t sort_ticket[kMaxPasses];   // last-arrival counters of the sort passes
+  uint32_t unused1[kMaxPasses];
   uint32_t unused0;
   uint32_t post_tile_ctr;
   uint32_t work_ctr;                  // reducer work queue
@@ -170,8 +170,7 @@ struct SortParams {
   int32_t shift;
   int32_t bits;
   uint32_t* counts;         // [radix][tiles]: tile digit counts, then their offsets
-  uint32_t* bases;          // [radix]: digit totals, then the digits' first positions
-  uint32_t* ticket;         // arrival counter of k_sort_offsets (zero at launch)
+  uint32_t* bases;          // [radix]: digit totals
   uint32_t* status;
 };
 

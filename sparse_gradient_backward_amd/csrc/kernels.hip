@@ -305,8 +305,8 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
 // word, as reduce-then-scan in three kernels (no workgroup waits for another):
 //   k_sort_count    digit counts of every tile, stored digit-major
 //   k_sort_offsets  one workgroup per digit: exclusive scan of its counts over
-//                   the tiles; the last one to finish also scans the digit
-//                   totals into the digits' global bases
+//                   the tiles, and the digit's total (each scatter workgroup
+//                   scans the totals into the digits' first positions)
 //   k_sort_scatter  ranks each tile's items by digit, stably, and writes each
 //                   digit group to its offset
 // Ranking (the multisplit of Adinets & Merrill, "Onesweep", 2022, done per
@@ -343,9 +343,22 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_count(SortParams p) {
     kv[k] = q < n ? p.kv_in[base + q] : 0ull;
   }
   __syncthreads();
+  // the lanes that share the first lane's digit (on skewed keys usually the
+  // hot one) are counted with one atomic by their first lane; the others
+  // add one each into their lane group's copy
+  const int lane = tid & 63;
 #pragma unroll
-  for (int k = 0; k < kSortItems; ++k)
-    if (k * kSortThreads + tid < n) atomicAdd(&s_h[w][digit_of(kv[k], p.shift, dmask)], 1u);
+  for (int k = 0; k < kSortItems; ++k) {
+    const bool valid = k * kSortThreads + tid < n;
+    const uint32_t d = digit_of(kv[k], p.shift, dmask);
+    const uint32_t d0 = __builtin_amdgcn_readfirstlane(d);
+    const uint64_t same = __ballot(valid && d == d0);
+    if (valid && d == d0) {
+      if (lane == __builtin_ctzll(same)) atomicAdd(&s_h[w][d0], (uint32_t)__popcll(same));
+    } else if (valid) {
+      atomicAdd(&s_h[w][d], 1u);
+    }
+  }
   __syncthreads();
   for (int d = tid; d < radix; d += kSortThreads) {
     uint32_t c = 0;
@@ -356,11 +369,9 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_count(SortParams p) {
 }
 
 // Workgroup d: offsets[d][j] = items of digit d in tiles < j, in place over
-// the counts, and the row total.  The last workgroup to finish (arrival
-// ticket) turns the row totals into the digits' global bases.
+// the counts, and the row total of digit d.
 __global__ __launch_bounds__(kScanThreads) void k_sort_offsets(SortParams p) {
   __shared__ uint32_t s_tmp[4];
-  __shared__ uint32_t s_last;
   const int tid = threadIdx.x;
   const int d = blockIdx.x;
   uint32_t* row = p.counts + (size_t)d * p.tiles;
@@ -384,28 +395,7 @@ __global__ __launch_bounds__(kScanThreads) void k_sort_offsets(SortParams p) {
     }
     carry += total;
   }
-  // publish the row total (device scope: the last workgroup may run on
-  // another XCD), wait for the store, then count the arrival
-  if (tid == 0) {
-    __hip_atomic_store(&p.bases[d], carry, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    s_last = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u ==
-             gridDim.x;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  const int radix = (int)gridDim.x;
-  uint32_t t2[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int e = 2 * tid + h;
-    t2[h] = e < radix ? __hip_atomic_load(&p.bases[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                      : 0u;
-  }
-  uint32_t tot;
-  const uint32_t ex = block_excl_scan<uint32_t>(t2[0] + t2[1], s_tmp, tot);
-  if (2 * tid < radix) p.bases[2 * tid] = ex;
-  if (2 * tid + 1 < radix) p.bases[2 * tid + 1] = ex + t2[0];
+  if (tid == 0) p.bases[d] = carry;
 }
 
 // Same-digit peers of this lane among the valid lanes: the lanes that agree
@@ -451,12 +441,17 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(SortParams p) {
     kv[k] = valid ? p.kv_in[base + e] : 0ull;
     cf[k] = (valid && has_coef) ? p.coef_in[base + e] : 0.0f;
   }
-  // global offsets of this tile's digit groups (independent of the ranking)
-  uint32_t goff[2];
+  // global offsets of this tile's digit groups (independent of the ranking):
+  // the digit's base (exclusive scan of the digit totals, done below) plus
+  // the tile's offset within the digit
+  uint32_t goff[2], dtot[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int d = 2 * tid + h;
-    goff[h] = d < radix ? p.bases[d] + p.counts[(size_t)d * p.tiles + tile] : 0u;
+    const int dc = d < radix ? d : 0;  // unconditional loads: none waits behind a branch
+    goff[h] = p.counts[(size_t)dc * p.tiles + tile];
+    dtot[h] = p.bases[dc];
+    if (d >= radix) dtot[h] = 0u;
   }
 #pragma unroll
   for (int k = 0; k < kSortItems; ++k) {
@@ -489,6 +484,9 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(SortParams p) {
   }
   {
     uint32_t tot;
+    const uint32_t dbase = block_excl_scan<uint32_t>(dtot[0] + dtot[1], s_tmp, tot);
+    goff[0] += dbase;
+    goff[1] += dbase + dtot[0];
     const uint32_t ex = block_excl_scan<uint32_t>(cnt[0] + cnt[1], s_tmp, tot);
     if (2 * tid < radix) {
       s_local[2 * tid] = ex;
