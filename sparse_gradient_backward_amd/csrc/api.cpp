@@ -125,6 +125,8 @@ sgb_status make_layout(const sgb_plan_s* p, int64_t N, int32_t B, bool has_offse
   L->hist = take(sizeof(uint32_t) * kMaxPasses * kRadixMax);  // digit bases of each pass
   L->zero_begin = align_up(o, 256);
   L->post_lb = take(sizeof(uint64_t) * (size_t)L->scan_tiles);
+  L->runtk = take(sizeof(uint32_t) * (size_t)L->max_items);
+  L->sctk = take(sizeof(uint32_t) * (size_t)L->max_items);
   L->zero_end_nobitmap = align_up(o, 256);
   L->bitmap = take(sizeof(uint32_t) * (size_t)((p->total_rows + 31) / 32));
   L->zero_end_bitmap = align_up(o, 256);
@@ -141,8 +143,6 @@ sgb_status make_layout(const sgb_plan_s* p, int64_t N, int32_t B, bool has_offse
   L->longs = take(sizeof(int32_t) * (size_t)L->max_long);
   L->longrec = take(sizeof(LongRun) * (size_t)L->max_long);
   L->chunkb = take(sizeof(uint32_t) * (size_t)(L->max_long + 1));
-  L->runtk = take(sizeof(uint32_t) * (size_t)L->max_items);
-  L->sctk = take(sizeof(uint32_t) * (size_t)L->max_items);
   L->part = take(sizeof(double) * (size_t)L->max_items * (size_t)kColBlock);
   L->total = align_up(o, 256);
   return SGB_OK;
@@ -410,8 +410,6 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   pp.long_ids = at<int32_t>(ws, L.longs);
   pp.chunk_begin = at<uint32_t>(ws, L.chunkb);
   pp.long_recs = at<LongRun>(ws, L.longrec);
-  pp.sc_ticket = at<uint32_t>(ws, L.sctk);
-  pp.run_ticket = at<uint32_t>(ws, L.runtk);
   pp.num_long = &hdr->num_long;
   pp.total_items = &hdr->total_items;
   pp.bitmap = fresh ? at<uint32_t>(ws, L.bitmap) : nullptr;
@@ -447,8 +445,8 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   q.total_items = pp.total_items;
   q.num_long = &hdr->num_long;
   q.work_ctr = &hdr->work_ctr;
-  q.sc_ticket = pp.sc_ticket;
-  q.run_ticket = pp.run_ticket;
+  q.sc_ticket = at<uint32_t>(ws, L.sctk);
+  q.run_ticket = at<uint32_t>(ws, L.runtk);
   q.partials = at<double>(ws, L.part);
   q.out = out;
   q.mom = u->mode == SGB_ROWWISE_ADAGRAD ? u->momentum : nullptr;

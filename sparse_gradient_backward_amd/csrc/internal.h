@@ -201,8 +201,6 @@ struct PostParams {
   int32_t* long_ids;
   uint32_t* chunk_begin;    // [num_long + 1]: first (chunk, column block) item of each long run
   LongRun* long_recs;       // [num_long]
-  uint32_t* sc_ticket;      // [items]
-  uint32_t* run_ticket;     // [items]
   int64_t* num_long;
   uint32_t* total_items;
   uint32_t* bitmap;         // touched-row bitmap (fresh dense grad) or NULL

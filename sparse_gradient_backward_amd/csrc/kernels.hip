@@ -689,9 +689,9 @@ __global__ __launch_bounds__(kScanThreads) void k_rle_write(RleParams p) {
 // -- compacted in ascending run order (the page appends them through an
 // atomic counter in arbitrary order).  Each long run is cut into chunks of
 // chunk_len() lookups (set by the row width) times the 256-column blocks of
-// its row; a combined scan gives every long run its first work item.  Also
-// clears the combine tickets of those items and, for a fresh dense gradient,
-// marks touched rows in a bitmap.
+// its row; a combined scan gives every long run its first work item.  For a
+// fresh dense gradient it also marks touched rows in a bitmap.  (The combine
+// tickets of the work items are cleared with the workspace's zeroed region.)
 
 // Table of a run from the info of one of its lookups (bag t*B+b, or token
 // l*T+t without bags).
@@ -702,6 +702,8 @@ __device__ __forceinline__ int table_of_info(const PostParams& p, uint32_t info)
 
 __global__ __launch_bounds__(kScanThreads) void k_post(PostParams p) {
   __shared__ int32_t s_cum[kScanTile + 1];
+  __shared__ int32_t s_lq[kScanTile];   // tile positions of the tile's long runs
+  __shared__ uint32_t s_lc[kScanTile];  // their first work items
   __shared__ uint64_t s_tmp[4];
   __shared__ uint32_t s_tile;
   __shared__ uint64_t s_excl;
@@ -745,7 +747,7 @@ __global__ __launch_bounds__(kScanThreads) void k_post(PostParams p) {
   }
   // (the loads are unconditional, from index 0 where there is nothing to
   // read, so that none of them waits behind a branch for the one before)
-  int tq[kScanItems], Dq[kScanItems];
+  int Dq[kScanItems];
   if (longmask) {
     uint64_t raw[kScanItems];
 #pragma unroll
@@ -754,9 +756,9 @@ __global__ __launch_bounds__(kScanThreads) void k_post(PostParams p) {
     int dlo[kScanItems], dhi[kScanItems];
 #pragma unroll
     for (int k = 0; k < kScanItems; ++k) {
-      tq[k] = ((longmask >> k) & 1u) ? table_of_info(p, (uint32_t)(raw[k] & imask)) : 0;
-      dlo[k] = p.doff[tq[k]];
-      dhi[k] = p.doff[tq[k] + 1];
+      const int t = ((longmask >> k) & 1u) ? table_of_info(p, (uint32_t)(raw[k] & imask)) : 0;
+      dlo[k] = p.doff[t];
+      dhi[k] = p.doff[t + 1];
     }
 #pragma unroll
     for (int k = 0; k < kScanItems; ++k) Dq[k] = ((longmask >> k) & 1u) ? dhi[k] - dlo[k] : 4;
@@ -806,40 +808,48 @@ __global__ __launch_bounds__(kScanThreads) void k_post(PostParams p) {
       if (in && (lane == 0 || pw != word)) atomicOr(&p.bitmap[word], bits);
     }
   }
-  int64_t ids[kScanItems];
-  if (longmask) {
+  __syncthreads();
+  // the tile's long runs in order: tile-local slot -> position and first work
+  // item (this thread's runs, cheap arithmetic), then their records written
+  // by all threads in parallel
+  {
+    uint64_t at = s_excl + before;
+    uint32_t li = (uint32_t)(before >> 31);
 #pragma unroll
-    for (int k = 0; k < kScanItems; ++k)
-      ids[k] = p.unique_ids[base + (((longmask >> k) & 1u) ? tid * kScanItems + k : 0)];
+    for (int k = 0; k < kScanItems; ++k) {
+      if (!((longmask >> k) & 1u)) continue;
+      const int q = tid * kScanItems + k;
+      const int len = s_cum[q + 1] - s_cum[q];
+      const int cl = chunk_len(len, Dq[k]);
+      s_lq[li] = q;
+      s_lc[li] = (uint32_t)(at & kField);
+      at += (1ull << 31) | (uint64_t)(((len + cl - 1) / cl) * col_blocks(Dq[k]));
+      ++li;
+    }
   }
   __syncthreads();
-  uint64_t at = s_excl + before;
-#pragma unroll
-  for (int k = 0; k < kScanItems; ++k) {
-    if (!((longmask >> k) & 1u)) continue;
-    const int q = tid * kScanItems + k;
-    const int len = s_cum[q + 1] - s_cum[q];
-    const int D = Dq[k];
-    const int ncb = col_blocks(D);
+  const uint32_t g0 = (uint32_t)(s_excl >> 31);
+  const uint32_t nl_tile = (uint32_t)(total >> 31);
+  for (uint32_t i = tid; i < nl_tile; i += kScanThreads) {
+    const int q = s_lq[i];
+    const int start = s_cum[q];
+    const int len = s_cum[q + 1] - start;
+    const uint64_t w0 = p.kv[start];
+    const int64_t id = p.unique_ids[base + q];
+    const int t = table_of_info(p, (uint32_t)(w0 & imask));
+    const int D = p.doff[t + 1] - p.doff[t];
     const int cl = chunk_len(len, D);
-    const int nch = (len + cl - 1) / cl;
-    const uint32_t pos = (uint32_t)(at >> 31);
-    const uint32_t c0 = (uint32_t)(at & kField);
-    p.long_ids[pos] = (int32_t)(base + q);
-    p.chunk_begin[pos] = c0;
     LongRun rec;
-    rec.start = s_cum[q];
+    rec.start = start;
     rec.len = len;
-    rec.t = tq[k];
-    rec.ncb = ncb;
-    rec.cbeg = c0;
-    rec.nch = nch;
-    rec.id = ids[k];
-    p.long_recs[pos] = rec;
-    for (int cb = 0; cb < ncb; ++cb) p.run_ticket[c0 + cb] = 0u;
-    for (int sc = 0; sc < nch; sc += kSuperChunk)
-      for (int cb = 0; cb < ncb; ++cb) p.sc_ticket[c0 + sc * ncb + cb] = 0u;
-    at += (1ull << 31) | (uint64_t)(nch * ncb);
+    rec.t = t;
+    rec.ncb = col_blocks(D);
+    rec.cbeg = s_lc[i];
+    rec.nch = (len + cl - 1) / cl;
+    rec.id = id;
+    p.long_ids[g0 + i] = (int32_t)(base + q);
+    p.chunk_begin[g0 + i] = s_lc[i];
+    p.long_recs[g0 + i] = rec;
   }
   if (tid == 0 && base + n == U) {
     const uint64_t all = s_excl + total;
