@@ -25,6 +25,9 @@ constexpr int kMaxD = 8192;
 #ifndef SGB_LONG_UNR
 #define SGB_LONG_UNR 8
 #endif
+#ifndef SGB_MAX_CHUNKS
+#define SGB_MAX_CHUNKS 2048
+#endif
 #ifndef SGB_CHUNK_BASE
 #define SGB_CHUNK_BASE 256
 #endif
@@ -68,7 +71,7 @@ static_assert(kShortSub8 >= 0 && kShortSub8 <= 6 && kShortSub16 >= 0 && kShortSu
               "a window of 64 positions splits into at most 64 parts");
 
 // long runs: chunk sizing and two-level combine
-constexpr int kMaxChunks = 2048;      // a run is cut into at most this many chunks
+constexpr int kMaxChunks = SGB_MAX_CHUNKS;  // a run is cut into at most this many chunks
 constexpr int kSuperChunk = 32;       // chunks combined per first-level ticket
 
 // Lanes that cover a row of D columns at 4 columns per lane: the power of two

@@ -910,19 +910,6 @@ __global__ __launch_bounds__(256) void k_fill(FillParams p) {
 //   row: a deterministic reduction across many workgroups without float
 //   atomics (the page keeps a long run inside one block).
 
-template <int LPL>
-__device__ __forceinline__ int bcast_i(int v, int src) {
-  if constexpr (LPL == 64)
-    return __builtin_amdgcn_readlane(v, src);
-  else
-    return __shfl(v, src, 64);
-}
-
-template <int LPL>
-__device__ __forceinline__ float bcast_f(float v, int src) {
-  return __int_as_float(bcast_i<LPL>(__float_as_int(v), src));
-}
-
 // Four grad_output elements as stored (4 x bf16 or 4 x fp32) and their fp32
 // values.  Gathers load the raw bits under their condition and widen them
 // only after every load of a round has been issued: widening inside the
@@ -1034,48 +1021,86 @@ __device__ __forceinline__ RowDst row_dest(const RedParams& p, int t, int D, int
   return d;
 }
 
-// Sum over lookups j = first, first+step, ... < last of coef_j * grad row_j
-// at elements [colofs, colofs+4).  first/last/step are uniform within each
-// group of LPL lanes.  For the first batch a lane may bring its lookup's
-// (row, coefficient) already (pre_ok); otherwise they are read here.
+// One gathered grad_output row of a long run: the row and the sum of the
+// coefficients of the run's consecutive lookups that read it.
+struct MergedRow {
+  int32_t row;
+  int32_t pad;
+  double coef;
+};
+
+// Sum over lookups j in [first, last) of coef_j * grad row_j at elements
+// [colofs, colofs+4), where each group of LPL lanes passes its own range
+// (uniform within the group; the ranges of a wave differ by at most LPL).
+// Within a run the lookups are ordered by bag, so lookups of one bag -- one
+// grad_output row -- are adjacent: each slice of LPL lookups is merged into
+// (row, summed coefficient) entries first (segmented sum across the lanes,
+// fp64), the entries are compacted into the wave's LDS list `q`, and only
+// they are gathered.  The next slice's metadata is loaded while the current
+// one is gathered.  Called with the whole wave active.
 template <int LPL, int UNR, bool BF16>
-__device__ __forceinline__ d4 gather_sum(const RedParams& p, int first, int last, int step,
-                                             int t, int64_t colofs, bool col_ok, int pre_row,
-                                             float pre_cf, bool pre_ok) {
+__device__ __forceinline__ d4 gather_merged(const RedParams& p, int first, int last, int slices,
+                                            int t, int64_t colofs, bool col_ok, MergedRow* q) {
   const int lane = lane_id();
   const int gb = lane & ~(LPL - 1), lig = lane & (LPL - 1);
   const uint64_t imask = info_mask(p);
   const bool has_coef = p.coef != nullptr;
+  const uint64_t gmask = (LPL == 64) ? ~0ull : (((1ull << LPL) - 1ull) << gb);
+  auto clampj = [&](int j) { return j < last ? j : (last > first ? last - 1 : first); };
   d4 acc = d4_zero();
-  bool firstb = true;
-  for (int j0 = first; j0 < last; j0 += LPL * step) {
-    const int jm = j0 + lig * step;
-    int rowi = 0;
-    float cf = 0.f;
-    if (firstb && pre_ok) {
-      rowi = pre_row;
-      cf = pre_cf;
-    } else if (jm < last) {
-      rowi = grad_row_of(p, (uint32_t)(p.kv[jm] & imask), t);
-      cf = has_coef ? p.coef[jm] : 1.0f;
+  // metadata of this lane's lookup in slice 0 (loads from a valid index even
+  // when there is nothing to read, so no branch holds them up)
+  int j = first + lig;
+  uint64_t w = p.kv[clampj(j)];
+  float c = has_coef ? p.coef[clampj(j)] : 1.0f;
+  for (int s = 0; s < slices; ++s) {
+    const bool ok = j < last;
+    const int jn = j + LPL;
+    const uint64_t wn = p.kv[clampj(jn)];
+    const float cn = has_coef ? p.coef[clampj(jn)] : 1.0f;
+    const int row = ok ? grad_row_of(p, (uint32_t)(w & imask), t) : -1 - lane;
+    // segments of equal rows (adjacent lanes of the group) summed into their
+    // first lane
+    double cs = ok ? (double)c : 0.0;
+    const int prow = __shfl_up(row, 1, 64);
+    const bool head = ok && (lig == 0 || prow != row);
+#pragma unroll
+    for (int off = 1; off < LPL; off <<= 1) {
+      const double o = __shfl_down(cs, off, 64);
+      const int orow = __shfl_down(row, off, 64);
+      if (lig + off < LPL && orow == row) cs += o;
     }
-    firstb = false;
-    const int cnt = min(LPL, (last - j0 + step - 1) / step);
+    const uint64_t hm = __ballot(head) & gmask;
+    const int cnt = __popcll(hm);
+    if (head) {
+      const int at = __popcll(hm & ((1ull << lane) - 1ull));
+      q[gb + at] = MergedRow{row, 0, cs};
+    }
+    // (a wave's LDS accesses are performed in order: the list is complete
+    // for the reads below)
     for (int jj = 0; jj < cnt; jj += UNR) {
       Raw4<BF16> r[UNR];
-      float c[UNR];
+      double cf[UNR];
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
-        const int src = (LPL == 64 ? 0 : gb) + min(jj + u, LPL - 1);
-        const int ro = bcast_i<LPL>(rowi, src);
-        c[u] = bcast_f<LPL>(cf, src);
-        const bool ok = (jj + u < cnt) && col_ok;
-        r[u] = ok ? load_raw4<BF16>(p.grad, (int64_t)ro * p.row_stride + colofs) : zero_raw4<BF16>();
-        if (jj + u >= cnt) c[u] = 0.f;
+        const bool okk = (jj + u < cnt) && col_ok;
+        const MergedRow e = q[gb + min(jj + u, LPL - 1)];
+        cf[u] = okk ? e.coef : 0.0;
+        r[u] = okk ? load_raw4<BF16>(p.grad, (int64_t)e.row * p.row_stride + colofs)
+                   : zero_raw4<BF16>();
       }
 #pragma unroll
-      for (int u = 0; u < UNR; ++u) d4_fma(acc, c[u], widen4<BF16>(r[u]));
+      for (int u = 0; u < UNR; ++u) {
+        const float4 v = widen4<BF16>(r[u]);
+        acc.x = fma(cf[u], (double)v.x, acc.x);
+        acc.y = fma(cf[u], (double)v.y, acc.y);
+        acc.z = fma(cf[u], (double)v.z, acc.z);
+        acc.w = fma(cf[u], (double)v.w, acc.w);
+      }
     }
+    j = jn;
+    w = wn;
+    c = cn;
   }
   return acc;
 }
@@ -1255,10 +1280,17 @@ __device__ __forceinline__ void long_item(const RedParams& p, const LongRun& rec
   const int cb_hi = p.mode == kModeAdagrad ? ncb : cb + 1;
   const int64_t gcol = p.nobag ? 0 : p.doff[t];
   const RowDst dst = row_dest(p, t, D, rec.id);
+  // each lane group takes a contiguous share of the chunk, so that the
+  // adjacent lookups of one bag stay together for merging
+  const int per = (hi - lo + G - 1) / G;
+  const int glo = min(lo + g * per, hi), ghi = min(glo + per, hi);
+  const int slices = (per + LPL - 1) / LPL;
+  __shared__ MergedRow s_rows[4][64];
+  MergedRow* q = s_rows[threadIdx.x >> 6];
   auto chunkG = [&](int cbx) {
     const int col = cbx * kColBlock + 4 * lig;
-    const d4 a = gather_sum<LPL, SGB_LONG_UNR, BF16>(p, lo + g, hi, G, t, gcol + col, col < D, 0,
-                                                     0.f, false);
+    const d4 a =
+        gather_merged<LPL, SGB_LONG_UNR, BF16>(p, glo, ghi, slices, t, gcol + col, col < D, q);
     return fold_groups<LPL>(a);
   };
   if (nch == 1) {
