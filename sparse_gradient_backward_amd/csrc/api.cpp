@@ -110,7 +110,8 @@ sgb_status make_layout(const sgb_plan_s* p, int64_t N, int32_t B, bool has_offse
   L->scan_tiles = (N + kScanTile - 1) / kScanTile;
   L->max_long = N / p->thr + 1;
   // a long run of len lookups in a table of width D has ceil(len / chunk_len)
-  // <= len / chunk_min(D) + 1 chunks of col_blocks(D) items each
+  // <= len / chunk_min(D, base) + 1 chunks of col_blocks(D) items each, for
+  // any chunk base >= kChunkBaseMin
   L->max_items = (N * p->items_num + p->items_den - 1) / p->items_den +
                  (L->max_long + 1) * col_blocks(p->Dmax);
 
@@ -207,7 +208,7 @@ sgb_status sgb_plan_create(sgb_plan* out, int32_t T, const int64_t* hsc, const i
     const int32_t D = doff[t + 1] - doff[t];
     p->Dmax = std::max(p->Dmax, D);
     p->Dmin = t == 0 ? D : std::min(p->Dmin, D);
-    const int64_t num = col_blocks(D), den = chunk_min(D);
+    const int64_t num = col_blocks(D), den = chunk_min(D, kChunkBaseMin);
     if (num * p->items_den > p->items_num * den) {
       p->items_num = num;
       p->items_den = den;
@@ -405,6 +406,9 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   pp.B = b->offsets ? b->B : 0;
   pp.T = p->T;
   pp.nobag = nobag ? 1 : 0;
+  pp.chunk_base = chunk_base_for(N);
+  pp.hsc = p->d_hsc;
+  pp.woff = p->d_woff;
   pp.thr = p->thr;
   pp.run_lengths = at<int32_t>(ws, L.lens);
   pp.long_ids = at<int32_t>(ws, L.longs);
@@ -458,6 +462,7 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   q.T = p->T;
   q.nobag = nobag ? 1 : 0;
   q.thr = p->thr;
+  q.chunk_base = pp.chunk_base;
   q.mode = u->mode;
   q.accumulate = u->accumulate ? 1 : 0;
   q.lr = u->lr;

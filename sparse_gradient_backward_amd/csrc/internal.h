@@ -28,8 +28,8 @@ constexpr int kMaxD = 8192;
 #ifndef SGB_MAX_CHUNKS
 #define SGB_MAX_CHUNKS 2048
 #endif
-#ifndef SGB_CHUNK_BASE
-#define SGB_CHUNK_BASE 256
+#ifndef SGB_CHUNK_DIV
+#define SGB_CHUNK_DIV 8192
 #endif
 #ifndef SGB_CHUNK_FLOOR
 #define SGB_CHUNK_FLOOR 128
@@ -86,18 +86,30 @@ __host__ __device__ inline int lanes_per_row(int D) {
 // 256-column blocks a row of D columns spans.
 __host__ __device__ inline int col_blocks(int D) { return (D + kColBlock - 1) / kColBlock; }
 
+// Chunk base of one call: lookups per chunk of a long run in a one-block row.
+// Larger batches have more long-run work, so their chunks are larger (fewer
+// items, less fixed cost each); small batches need more, shorter items to
+// fill the GPU.  A power of two in [kChunkBaseMin, kChunkBaseMax].
+constexpr int kChunkBaseMin = 128;
+constexpr int kChunkBaseMax = 512;
+__host__ __device__ inline int chunk_base_for(int64_t N) {
+  int b = kChunkBaseMin;
+  while (b < kChunkBaseMax && (int64_t)b * 2 * SGB_CHUNK_DIV <= N) b *= 2;
+  return b;
+}
+
 // Fewest lookups in one chunk of a long run.  A work item is one chunk times
 // one 256-column block; a row of several blocks already spreads a chunk over
 // several waves, so its chunks are proportionally shorter (down to a floor).
-__host__ __device__ inline int chunk_min(int D) {
-  const int c = SGB_CHUNK_BASE / col_blocks(D);
+__host__ __device__ inline int chunk_min(int D, int base) {
+  const int c = base / col_blocks(D);
   return c > SGB_CHUNK_FLOOR ? c : SGB_CHUNK_FLOOR;
 }
 
 // Lookups per chunk of a long run of `len` lookups in a table of width D.
-__host__ __device__ inline int chunk_len(int len, int D) {
+__host__ __device__ inline int chunk_len(int len, int D, int base) {
   const int c = (len + kMaxChunks - 1) / kMaxChunks;
-  const int m = chunk_min(D);
+  const int m = chunk_min(D, base);
   return c > m ? c : m;
 }
 
@@ -135,6 +147,10 @@ struct LongRun {
   uint32_t cbeg;   // first work item / partial slot
   int32_t nch;     // chunks
   int64_t id;      // linear row id
+  int32_t D;       // row width
+  int32_t gcol;    // first grad_output column of its table (0 without bags)
+  int64_t out;     // element offset of its row in the weights / dense grad
+  int64_t mom;     // its Adagrad state index (its row among all tables)
 };
 
 // A block of rows of one table that the dense zero-fill covers.
@@ -200,6 +216,9 @@ struct PostParams {
   int32_t T;
   int32_t nobag;
   int32_t thr;
+  int32_t chunk_base;       // chunk_base_for(N)
+  const int64_t* hsc;       // [T+1]
+  const int64_t* woff;      // [T+1]
   int32_t* run_lengths;
   int32_t* long_ids;
   uint32_t* chunk_begin;    // [num_long + 1]: first (chunk, column block) item of each long run
@@ -252,6 +271,7 @@ struct RedParams {
   int32_t T;
   int32_t nobag;
   int32_t thr;
+  int32_t chunk_base;       // chunk_base_for(N)
   int32_t sub_log;          // short-run reducer: log2 of the waves per window
   int32_t mode;
   int32_t accumulate;

@@ -770,7 +770,7 @@ __global__ __launch_bounds__(kScanThreads) void k_post(PostParams p) {
     // a long run becomes nch chunks x ncb column blocks of work items
     const int q = tid * kScanItems + k;
     const int len = s_cum[q + 1] - s_cum[q];
-    const int cl = chunk_len(len, Dq[k]);
+    const int cl = chunk_len(len, Dq[k], p.chunk_base);
     sum += (1ull << 31) | (uint64_t)(((len + cl - 1) / cl) * col_blocks(Dq[k]));
   }
   uint64_t total;
@@ -820,7 +820,7 @@ __global__ __launch_bounds__(kScanThreads) void k_post(PostParams p) {
       if (!((longmask >> k) & 1u)) continue;
       const int q = tid * kScanItems + k;
       const int len = s_cum[q + 1] - s_cum[q];
-      const int cl = chunk_len(len, Dq[k]);
+      const int cl = chunk_len(len, Dq[k], p.chunk_base);
       s_lq[li] = q;
       s_lc[li] = (uint32_t)(at & kField);
       at += (1ull << 31) | (uint64_t)(((len + cl - 1) / cl) * col_blocks(Dq[k]));
@@ -837,8 +837,12 @@ __global__ __launch_bounds__(kScanThreads) void k_post(PostParams p) {
     const uint64_t w0 = p.kv[start];
     const int64_t id = p.unique_ids[base + q];
     const int t = table_of_info(p, (uint32_t)(w0 & imask));
-    const int D = p.doff[t + 1] - p.doff[t];
-    const int cl = chunk_len(len, D);
+    const int d0 = p.doff[t], D = p.doff[t + 1] - d0;
+    const int64_t h0 = p.hsc[t], E = p.hsc[t + 1] - h0;
+    const int64_t wo = p.woff[t];
+    const int cl = chunk_len(len, D, p.chunk_base);
+    int64_t row = id - h0;
+    row = row < 0 ? 0 : (row < E ? row : E - 1);
     LongRun rec;
     rec.start = start;
     rec.len = len;
@@ -847,6 +851,10 @@ __global__ __launch_bounds__(kScanThreads) void k_post(PostParams p) {
     rec.cbeg = s_lc[i];
     rec.nch = (len + cl - 1) / cl;
     rec.id = id;
+    rec.D = D;
+    rec.gcol = p.nobag ? 0 : d0;
+    rec.out = wo + row * (int64_t)D;
+    rec.mom = h0 + row;
     p.long_ids[g0 + i] = (int32_t)(base + q);
     p.chunk_begin[g0 + i] = s_lc[i];
     p.long_recs[g0 + i] = rec;
@@ -901,14 +909,15 @@ __global__ __launch_bounds__(256) void k_fill(FillParams p) {
 //   Metadata of the window is broadcast lane to lane with the whole wave
 //   active; the row's old value is fetched before the gather so the two
 //   overlap.  Balanced by lookups, and the grid is fixed on the host.
-// k_reduce_long: persistent waves take (chunk, column block) items of the
-//   long runs from an atomic queue.  For D < 256 the wave's groups take
-//   interleaved lookups of the chunk and are folded by a fixed xor tree.  A
-//   run of several chunks writes one fp32 partial per item; the last wave of
-//   each group of kSuperChunk chunks (arrival ticket) adds them in chunk
-//   order, and the last group adds the group sums in order and finishes the
-//   row: a deterministic reduction across many workgroups without float
-//   atomics (the page keeps a long run inside one block).
+// k_reduce_long: persistent waves take the long runs' (chunk, column block)
+//   items round-robin.  For D < 256 the wave's lane groups take
+//   contiguous shares of the chunk, merge adjacent lookups of one bag, and
+//   are folded by a fixed xor tree.  A run of several chunks writes one fp64
+//   partial per item; the last wave of each group of kSuperChunk chunks
+//   (arrival ticket) adds them in chunk order, and the last group adds the
+//   group sums in order and finishes the row: a deterministic reduction
+//   across many workgroups without float atomics (the page keeps a long run
+//   inside one block).
 
 // Four grad_output elements as stored (4 x bf16 or 4 x fp32) and their fp32
 // values.  Gathers load the raw bits under their condition and widen them
@@ -1265,21 +1274,20 @@ __device__ __forceinline__ d4 sum_slots(const RedParams& p, uint32_t cbeg, int n
 }
 
 template <int LPL, bool BF16>
-__device__ __forceinline__ void long_item(const RedParams& p, const LongRun& rec, int c, int cb,
-                                          int D) {
+__device__ __forceinline__ void long_item(const RedParams& p, const LongRun& rec, int c, int cb) {
   constexpr int G = 64 / LPL;
   const int lane = lane_id(), g = lane / LPL, lig = lane & (LPL - 1);
-  const int t = rec.t, start = rec.start, len = rec.len;
+  const int t = rec.t, start = rec.start, len = rec.len, D = rec.D;
   const int ncb = rec.ncb;
-  const int chl = chunk_len(len, D);
+  const int chl = chunk_len(len, D, p.chunk_base);
   const int nch = rec.nch;
   const int lo = start + c * chl;
   const int hi = min(lo + chl, start + len);
   // Adagrad needs the whole row in one wave: item cb 0 covers every block
   const int cb_lo = p.mode == kModeAdagrad ? 0 : cb;
   const int cb_hi = p.mode == kModeAdagrad ? ncb : cb + 1;
-  const int64_t gcol = p.nobag ? 0 : p.doff[t];
-  const RowDst dst = row_dest(p, t, D, rec.id);
+  const int64_t gcol = rec.gcol;
+  const RowDst dst{p.out + rec.out, p.mom ? p.mom + rec.mom : nullptr};
   // each lane group takes a contiguous share of the chunk, so that the
   // adjacent lookups of one bag stay together for merging
   const int per = (hi - lo + G - 1) / G;
@@ -1348,22 +1356,21 @@ __global__ __launch_bounds__(256) void k_reduce_long(RedParams p) {
   const uint32_t n_items = *p.total_items;
   const int nlong = (int)*p.num_long;
   // items are dealt round-robin: consecutive chunks of a hot run go to
-  // different waves, and no shared counter is contended
+  // different waves, tables of different row widths mix on every wave, and no
+  // shared counter is contended
   const uint32_t nw = gridDim.x * (blockDim.x / 64);
   for (uint32_t w = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6); w < n_items; w += nw) {
     const int k = find_long_run(p.chunk_begin, nlong, w);
     const LongRun rec = p.long_recs[k];
-    const int t = rec.t;
-    const int D = p.doff[t + 1] - p.doff[t];
     const int local = (int)(w - rec.cbeg);
     const int c = local / rec.ncb, cb = local % rec.ncb;
     if (p.mode == kModeAdagrad && cb != 0) continue;
-    switch (lanes_per_row(D)) {
-      case 4: long_item<4, BF16>(p, rec, c, cb, D); break;
-      case 8: long_item<8, BF16>(p, rec, c, cb, D); break;
-      case 16: long_item<16, BF16>(p, rec, c, cb, D); break;
-      case 32: long_item<32, BF16>(p, rec, c, cb, D); break;
-      default: long_item<64, BF16>(p, rec, c, cb, D); break;
+    switch (lanes_per_row(rec.D)) {
+      case 4: long_item<4, BF16>(p, rec, c, cb); break;
+      case 8: long_item<8, BF16>(p, rec, c, cb); break;
+      case 16: long_item<16, BF16>(p, rec, c, cb); break;
+      case 32: long_item<32, BF16>(p, rec, c, cb); break;
+      default: long_item<64, BF16>(p, rec, c, cb); break;
     }
   }
 }
