@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <new>
 #include <vector>
 
@@ -55,6 +56,16 @@ int bitlen(uint64_t v) {  // number of bits needed to hold v (0 for 0)
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// A fresh 24-bit tag per call (never 0): device-detected errors carry the tag
+// of the call that found them, so the status word needs no clearing.
+uint32_t next_epoch() {
+  static std::atomic<uint32_t> counter{0};
+  for (;;) {
+    const uint32_t e = (counter.fetch_add(1, std::memory_order_relaxed) + 1u) & 0xFFFFFFu;
+    if (e) return e;
+  }
+}
 
 struct DeviceGuard {
   int prev = -1;
@@ -326,10 +337,10 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
 
   Header* hdr = at<Header>(ws, L.hdr);
   uint32_t* status = &hdr->status;
+  const uint32_t epoch = next_epoch();
   const bool has_coef = (p->pooling == SGB_POOL_MEAN) || (b->per_sample_weights != nullptr);
+  // (no separate clearing step: linearisation resets the header's counters)
   mark(SGB_STAGE_INIT, 0);
-  hipError_t e = launch_init(ws, L.zero_begin, stream);
-  if (e != hipSuccess) return SGB_ERR_HIP;
   mark(SGB_STAGE_INIT, 1);
 
   // linearise (+ clear look-back words and the bitmap)
@@ -346,6 +357,8 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   lp.kv_out = at<uint64_t>(ws, L.kvA);
   lp.coef_out = has_coef ? at<float>(ws, L.coefA) : nullptr;
   lp.status = status;
+  lp.epoch = epoch;
+  lp.header = hdr;
   lp.zero_begin = at<uint4>(ws, L.zero_begin);
   lp.zero_vec4 = (int64_t)(((fresh ? L.zero_end_bitmap : L.zero_end_nobitmap) - L.zero_begin) / 16);
   const int64_t lin_tiles = b->offsets ? ((int64_t)b->B * p->T + kLinBags - 1) / kLinBags
@@ -374,6 +387,7 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
     sp.counts = at<uint32_t>(ws, L.counts);
     sp.bases = at<uint32_t>(ws, L.hist) + ps * kRadixMax;
     sp.status = status;
+    sp.epoch = epoch;
     if (launch_sort_pass(sp, stream) != hipSuccess) return SGB_ERR_HIP;
     std::swap(kv_in, kv_out);
     std::swap(cf_in, cf_out);
@@ -421,6 +435,7 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   pp.lookback = at<uint64_t>(ws, L.post_lb);
   pp.tile_ctr = &hdr->post_tile_ctr;
   pp.status = status;
+  pp.epoch = epoch;
   mark(SGB_STAGE_RUNS, 0);
   if (launch_post(pp, (int)L.scan_tiles, stream) != hipSuccess) return SGB_ERR_HIP;
   mark(SGB_STAGE_RUNS, 1);
@@ -448,7 +463,6 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   q.num_runs = rp.num_runs;
   q.total_items = pp.total_items;
   q.num_long = &hdr->num_long;
-  q.work_ctr = &hdr->work_ctr;
   q.sc_ticket = at<uint32_t>(ws, L.sctk);
   q.run_ticket = at<uint32_t>(ws, L.runtk);
   q.partials = at<double>(ws, L.part);
@@ -483,11 +497,12 @@ sgb_status sgb_device_status(sgb_plan p, const void* ws, void* stream_, int32_t*
   DeviceGuard guard(p->device);
   if (!guard.ok) return SGB_ERR_HIP;
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
-  uint32_t v = 0;
-  if (hipMemcpyAsync(&v, ws, sizeof(v), hipMemcpyDeviceToHost, stream) != hipSuccess)
+  uint32_t v[2] = {0, 0};  // status word, epoch of the last call
+  static_assert(offsetof(Header, status) == 0 && offsetof(Header, epoch) == 4, "header layout");
+  if (hipMemcpyAsync(v, ws, sizeof(v), hipMemcpyDeviceToHost, stream) != hipSuccess)
     return SGB_ERR_HIP;
   if (hipStreamSynchronize(stream) != hipSuccess) return SGB_ERR_HIP;
-  *out = (int32_t)v;
+  *out = (v[0] >> 8) == v[1] ? (int32_t)(v[0] & 0xFFu) : (int32_t)SGB_OK;
   return SGB_OK;
 }
 

@@ -125,16 +125,18 @@ enum { kPoolSum = 0, kPoolMean = 1, kPoolNone = 2 };
 enum { kModeDense = 0, kModeSgd = 1, kModeAdagrad = 2 };
 
 // Workspace header (offset 0).
+// Nothing in it needs clearing between calls: errors are tagged with the
+// call's epoch (a call reads as error-free unless its own epoch is in the
+// status word), and linearisation resets the tile counter.
 struct Header {
-  uint32_t status;                    // first device-detected error, 0 = none
-  uint32_t unused1[kMaxPasses];
-  uint32_t unused0;
-  uint32_t post_tile_ctr;
-  uint32_t work_ctr;                  // reducer work queue
+  uint32_t status;                    // epoch << 8 | first device-detected error of that call
+  uint32_t epoch;                     // epoch of the last call (set while linearising)
+  uint32_t post_tile_ctr;             // dynamic tile ids of the run post-processing
+  uint32_t unused;
   int32_t num_runs;                   // U
-  int64_t num_long;                   // number of long runs
   uint32_t total_items;               // chunks over all long runs
-  uint32_t pad[15];
+  int64_t num_long;                   // number of long runs
+  uint32_t pad[24];
 };
 static_assert(sizeof(Header) <= 128, "header too large");
 
@@ -175,6 +177,8 @@ struct LinParams {
   uint64_t* kv_out;
   float* coef_out;          // NULL when every coefficient is 1
   uint32_t* status;
+  uint32_t epoch;
+  Header* header;           // epoch and counters reset by the first workgroup
   uint4* zero_begin;        // region zeroed for the later kernels
   int64_t zero_vec4;
 };
@@ -191,6 +195,7 @@ struct SortParams {
   uint32_t* counts;         // [radix][tiles]: tile digit counts, then their offsets
   uint32_t* bases;          // [radix]: digit totals
   uint32_t* status;
+  uint32_t epoch;
 };
 
 struct RleParams {
@@ -230,6 +235,7 @@ struct PostParams {
   uint64_t* lookback;       // [tiles]
   uint32_t* tile_ctr;
   uint32_t* status;
+  uint32_t epoch;
 };
 
 struct FillParams {
@@ -257,7 +263,6 @@ struct RedParams {
   const int32_t* num_runs;
   const uint32_t* total_items;
   const int64_t* num_long;
-  uint32_t* work_ctr;
   uint32_t* sc_ticket;
   uint32_t* run_ticket;
   double* partials;         // fp64 partial sums of long-run work items

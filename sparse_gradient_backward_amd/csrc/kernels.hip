@@ -42,16 +42,26 @@ __device__ __forceinline__ uint32_t bits_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-__device__ __forceinline__ void set_status(uint32_t* st, uint32_t code) {
-  atomicCAS(st, 0u, code);
+// Records `code` as this call's error unless the call already has one: the
+// status word holds epoch << 8 | code, and a word from an earlier epoch counts
+// as no error.
+__device__ __forceinline__ void set_status(uint32_t* st, uint32_t epoch, uint32_t code) {
+  const uint32_t mine = (epoch << 8) | code;
+  uint32_t old = __hip_atomic_load(st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  while ((old >> 8) != epoch) {
+    const uint32_t seen = atomicCAS(st, old, mine);
+    if (seen == old) break;
+    old = seen;
+  }
 }
 
 // Records `code` if any lane of the wave has `bad`, with one atomic per wave
 // (an error path must not turn into millions of same-address atomics).
 // Wave-uniform call.
-__device__ __forceinline__ void set_status_wave(uint32_t* st, uint32_t code, bool bad) {
+__device__ __forceinline__ void set_status_wave(uint32_t* st, uint32_t epoch, uint32_t code,
+                                                bool bad) {
   const uint64_t m = __ballot(bad);
-  if (m && lane_id() == __builtin_ctzll(m)) set_status(st, code);
+  if (m && lane_id() == __builtin_ctzll(m)) set_status(st, epoch, code);
 }
 
 template <typename T>
@@ -113,7 +123,7 @@ struct LB<uint64_t> {
 };
 
 template <typename W>
-__device__ W wave_lookback(W* lb, uint32_t tile, W agg, uint32_t* status) {
+__device__ W wave_lookback(W* lb, uint32_t tile, W agg, uint32_t* status, uint32_t epoch) {
   const int lane = lane_id();
   if (lane == 0)
     __hip_atomic_store(&lb[tile], (tile == 0 ? LB<W>::P : LB<W>::A) | agg, __ATOMIC_RELAXED,
@@ -133,7 +143,7 @@ __device__ W wave_lookback(W* lb, uint32_t tile, W agg, uint32_t* status) {
     const uint64_t upto = first >= 64 ? ~0ull : ((2ull << first) - 1ull);
     if (notready & upto) {
       if (++spins > kSpinLimit) {
-        if (lane == 0) set_status(status, kStInternal);
+        if (lane == 0) set_status(status, epoch, kStInternal);
         break;
       }
       __builtin_amdgcn_s_sleep(2);
@@ -180,6 +190,10 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
   __shared__ float s_scale[kLinBags];
   __shared__ int s_bad;
   const int tid = threadIdx.x;
+  if (blockIdx.x == 0 && tid == 0) {
+    p.header->epoch = p.epoch;
+    p.header->post_tile_ctr = 0u;
+  }
 
   for (int64_t q = blockIdx.x * (int64_t)kLinThreads + tid; q < p.zero_vec4;
        q += (int64_t)gridDim.x * kLinThreads)
@@ -204,7 +218,7 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
           key = (uint64_t)idx;
           p.kv_out[i] = (key << p.info_bits) | (uint64_t)i;
         }
-        set_status_wave(p.status, kStIndex, bad);
+        set_status_wave(p.status, p.epoch, kStIndex, bad);
       }
     }
   } else {
@@ -241,7 +255,7 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
       __syncthreads();
       if (s_bad) {
         if (tid == 0) {
-          set_status(p.status, kStOffsets);
+          set_status(p.status, p.epoch, kStOffsets);
           for (int j = 1; j <= nb; ++j)
             if (s_off[j] < s_off[j - 1]) s_off[j] = s_off[j - 1];
         }
@@ -291,7 +305,7 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
             p.kv_out[i] = (key << p.info_bits) | info;
             if (p.coef_out) p.coef_out[i] = s_scale[lo] * w[k];
           }
-          set_status_wave(p.status, kStIndex, bad);
+          set_status_wave(p.status, p.epoch, kStIndex, bad);
         }
       }
       __syncthreads();
@@ -514,7 +528,7 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(SortParams p) {
     const int64_t pos = (int64_t)s_gbase[digit_of(v, p.shift, dmask)] + q;
     const bool okp = pos >= 0 && pos < p.N;
     if (okp) p.kv_out[pos] = v;
-    set_status_wave(p.status, kStInternal, !okp);
+    set_status_wave(p.status, p.epoch, kStInternal, !okp);
   }
   if (!has_coef) return;
   // coefficients the same way; the digit of each tile slot is read back from
@@ -776,7 +790,7 @@ __global__ __launch_bounds__(kScanThreads) void k_post(PostParams p) {
   uint64_t total;
   const uint64_t before = block_excl_scan<uint64_t>(sum, s_tmp, total);
   if (tid < 64) {
-    const uint64_t ex = wave_lookback<uint64_t>(p.lookback, tile, total, p.status);
+    const uint64_t ex = wave_lookback<uint64_t>(p.lookback, tile, total, p.status, p.epoch);
     if (tid == 0) s_excl = ex;
   }
   // run lengths, coalesced
