@@ -31,7 +31,9 @@ import synth  # noqa: E402
 
 METRIC = "embedding-bwd lookups/sec + achieved HBM GB/s (% of MI355X peak), 1 GPU"
 HBM_PEAK_GBPS = 8000.0
-STAGES = ("init", "linearize", "sort", "rle", "runs", "fill", "reduce_long", "reduce_short")
+STAGES = ("linearize", "sort_count", "sort_offsets", "sort_scatter", "sort", "rle_count",
+          "rle_scan", "rle_write", "runs", "fill", "reduce_long", "reduce_short")
+SORT_KERNELS = ("sort_count", "sort_offsets", "sort_scatter")  # timed on the first pass
 KERNEL_SOURCES = ("sparse_gradient_backward_amd/csrc/kernels.hip",
                   "sparse_gradient_backward_amd/csrc/internal.h",
                   "sparse_gradient_backward_amd/csrc/api.cpp")
@@ -43,10 +45,10 @@ def log(*a):
 
 
 def stage_bytes(inp: synth.Inputs, spec: synth.Spec, U: int, run_D: np.ndarray,
-                run_len: np.ndarray, thr: int, npasses: int):
-    """Algorithmic bytes each stage must move (one call): every input read
-    once, every output written once, the sorted stream written and read once
-    per radix pass, each run's gather and row update once."""
+                run_len: np.ndarray, thr: int, npasses: int, radix0: int):
+    """Algorithmic bytes of one launch of each kernel: every input read once,
+    every output written once; a radix pass reads and writes the packed words
+    (and coefficients) once; each run's gather and row update once."""
     N = inp.N
     c = 1 if (spec.pooling == "mean" or spec.weighted) else 0
     sg = 2 if spec.grad_dtype == "bf16" else 4
@@ -56,6 +58,7 @@ def stage_bytes(inp: synth.Inputs, spec: synth.Spec, U: int, run_D: np.ndarray,
     Ds = np.diff(inp.D_offsets).astype(np.int64)
     Es = np.diff(inp.hash_size_cumsum).astype(np.int64)
     touched_elems = int(run_D.sum())
+    tiles = (N + 4095) // 4096
 
     def update(D):
         if spec.mode == "dense":
@@ -68,17 +71,21 @@ def stage_bytes(inp: synth.Inputs, spec: synth.Spec, U: int, run_D: np.ndarray,
     gather_long = int((run_len[lg] * run_D[lg]).sum()) * sg
     gather_short = int((run_len[~lg] * run_D[~lg]).sum()) * sg
     b = {
-        "init": 0,
         "linearize": N * (8 + 8 + 4 * c + (4 if spec.weighted else 0)) + (BT + 1) * 8 * (BT > 0),
-        "sort": npasses * N * rec * 2,
-        "rle": N * 8 + U * (8 + 4 + 4),
-        "runs": U * (4 * 2 + 4 + (8 if fresh else 0)),
+        "sort_count": N * 8 + tiles * radix0 * 4,
+        "sort_offsets": tiles * radix0 * 4 * 2 + radix0 * 4,
+        "sort_scatter": N * rec * 2 + tiles * radix0 * 4 + radix0 * 4,
+        "rle_count": N * 8 + tiles * 4,
+        "rle_scan": tiles * 4 * 2 + 8,
+        "rle_write": N * 8 + tiles * 4 + U * (8 + 4 + 4),
+        "runs": U * (4 + 4 + (8 if fresh else 0)),
         "fill": ((int((Es * Ds).sum()) - touched_elems) * 4 + int(Es.sum()) // 8) if fresh else 0,
-        "reduce_long": gather_long + int(run_len[lg].sum()) * rec + int(lg.sum()) * 16
+        "reduce_long": gather_long + int(run_len[lg].sum()) * rec + int(lg.sum()) * 48
         + update(run_D[lg]),
         "reduce_short": gather_short + N * 8 + int(run_len[~lg].sum()) * 4 * c
         + int((~lg).sum()) * 8 + update(run_D[~lg]),
     }
+    b["sort"] = npasses * (b["sort_count"] + b["sort_offsets"] + b["sort_scatter"])
     # whole path, counted as the contract's byte model: indices read, the
     # sorted stream (8-byte id + 4-byte info + coefficient) written and read
     # once, the gather, offsets, 24 bytes per run, the row update
@@ -100,17 +107,17 @@ def kernel_digest() -> str:
     return h.hexdigest()[:12]
 
 
-def measured_traffic(workload: str, stage: str):
-    """HBM bytes per launch of one stage's kernel(s), from the FETCH_SIZE and
-    WRITE_SIZE counter runs recorded in profiles/pmc_traffic.txt (already
-    scaled by the copy-kernel calibration), or None when no figure exists for
-    the current kernel sources."""
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of one kernel, from the FETCH_SIZE and WRITE_SIZE
+    counter runs recorded in profiles/pmc_traffic.txt (already scaled by the
+    copy-kernel calibration), or None when no figure exists for the current
+    kernel sources."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     src = kernel_digest()
     for line in open(TRAFFIC_FILE):
         f = line.split()
-        if len(f) < 4 or f[0] != "traffic" or f[1] != workload or f[2] != stage:
+        if len(f) < 4 or f[0] != "kernel" or f[1] != workload or f[2] != kernel:
             continue
         kv = dict(x.split("=", 1) for x in f[3:])
         if kv.get("src") == src:
@@ -241,12 +248,12 @@ def main():
         step(e)
     torch.cuda.synchronize()
     ms_timed = (time.perf_counter() - t1) * 1e3 / args.steps
-    stage_ms = {}
+    stage_ms = {}  # mean duration of one launch of each kernel ("sort": all passes)
     view = plan.runs_view(ws, inp.N, B)
     for k, name in enumerate(STAGES):
         if name == "fill" and not (spec.mode == "dense" and not spec.accumulate):
             continue
-        if name == "sort" and plan_npasses(inp) == 0:
+        if name.startswith("sort") and plan_npasses(inp) == 0:
             continue
         d = [e[2 * k].elapsed_time(e[2 * k + 1]) for e in evs]
         stage_ms[name] = float(np.mean(d))
@@ -260,11 +267,14 @@ def main():
     run_D = np.diff(inp.D_offsets).astype(np.int64)[run_t]
     nlong = view["num_long"]
     npasses = plan_npasses(inp)
-    sb, b_path = stage_bytes(inp, spec, U, run_D, lens, thr, npasses)
-    dom = max(stage_ms, key=lambda k: stage_ms[k])
-    launches = npasses if dom == "sort" else 1
-    per_launch_bytes = sb[dom] / launches
-    per_launch_ms = stage_ms[dom] / launches
+    radix0 = 1 << pass_bits0(inp)
+    sb, b_path = stage_bytes(inp, spec, U, run_D, lens, thr, npasses, radix0)
+    # dominant kernel: the largest time per step (a sort kernel runs once per pass)
+    per_step = {k: v * (npasses if k in SORT_KERNELS else 1)
+                for k, v in stage_ms.items() if k != "sort"}
+    dom = max(per_step, key=lambda k: per_step[k])
+    per_launch_bytes = sb[dom]
+    per_launch_ms = stage_ms[dom]
     achieved = per_launch_bytes / (per_launch_ms * 1e-3) / 1e9
     gbps_path = b_path / (ms_per_step * 1e-3) / 1e9
     log(f"stages (ms): " + ", ".join(f"{k}={v:.4f}" for k, v in stage_ms.items()))
@@ -275,9 +285,12 @@ def main():
         log("timing the CPU oracle")
         cpu = cpu_baseline(inp, spec, thr, args.cpu_min_s, args.cpu_max_reps)
 
-    kernel_names = {"reduce_long": "k_reduce_long", "reduce_short": "k_reduce_short8/16",
-                    "sort": "k_sort_pass", "fill": "k_fill", "linearize": "k_linearize",
-                    "rle": "k_rle", "runs": "k_post", "init": "k_init"}
+    kernel_names = {"reduce_long": "k_reduce_long", "fill": "k_fill", "linearize": "k_linearize",
+                    "sort_count": "k_sort_count", "sort_offsets": "k_sort_offsets",
+                    "sort_scatter": "k_sort_scatter", "rle_count": "k_rle_count",
+                    "rle_scan": "k_rle_scan", "rle_write": "k_rle_write", "runs": "k_post",
+                    "reduce_short": "k_reduce_short8" if int(np.diff(inp.D_offsets).max()) <= 512
+                    else "k_reduce_short16"}
     res = {
         "metric": METRIC,
         "value": inp.N / (ms_per_step * 1e-3),
@@ -304,7 +317,7 @@ def main():
         "ms_per_step_instrumented": ms_timed,
         "roofline": {"bound": "hbm", "kernel": kernel_names[dom], "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(spec.name, dom), "bytes_per_launch": int(per_launch_bytes),
+                     "traffic": measured_traffic(spec.name, kernel_names[dom]), "bytes_per_launch": int(per_launch_bytes),
                      "launch_ms": per_launch_ms},
         "cpu_baseline": cpu,
         "device_status": status,
@@ -317,6 +330,14 @@ def plan_npasses(inp: synth.Inputs) -> int:
     rows = int(inp.hash_size_cumsum[-1])
     bits = int(rows - 1).bit_length()
     return (bits + 8) // 9
+
+
+def pass_bits0(inp: synth.Inputs) -> int:
+    """Digit bits of the first radix pass (the library splits the id bits evenly)."""
+    rows = int(inp.hash_size_cumsum[-1])
+    bits = int(rows - 1).bit_length()
+    n = plan_npasses(inp)
+    return bits // n + (1 if bits % n else 0) if n else 0
 
 
 if __name__ == "__main__":

@@ -159,31 +159,43 @@ typedef struct {
  *   ROWWISE_ADAGRAD  m_r += mean_d G_r[d]^2; w_r -= lr * G_r / (sqrt(m_r) + eps)
  *                                         (FBTT row-wise Adagrad kernel, once
  *                                          per distinct row on the summed G)
- *  Each touched row is read and written exactly once; untouched rows and
- *  state are not written (except zeros in a fresh dense gradient).  Sums are
- *  fp32 in a fixed order.  num_indices == 0 is a no-op (a fresh dense grad
- *  is still zero-filled).  Allocates nothing.
+ *  Each touched row is read and written once; untouched rows and state are
+ *  not written (a fresh dense gradient is zeroed whole first, then its
+ *  touched rows are written).  A row's sum is accumulated in fp64 in a fixed
+ *  order and rounded once to fp32.  num_indices == 0 is a no-op (a fresh
+ *  dense grad is still zero-filled).  Allocates nothing.
+ *  Part of the work runs on two side streams the plan owns (the zero fill of
+ *  a fresh dense gradient, and the short-run reduction); they start after
+ *  everything enqueued on `stream` before the call, and `stream` waits for
+ *  them before any work enqueued after the call, so the call behaves as if
+ *  it ran on `stream` alone.  Calls with one plan share its side streams.
  */
 sgb_status sgb_backward(sgb_plan plan, const sgb_batch* batch, const sgb_update* update,
                         void* workspace, size_t workspace_bytes, void* stream);
 
-/* Stages of sgb_backward() in launch order (see sgb_backward_timed). */
+/* Timed regions of sgb_backward() (see sgb_backward_timed): one per kernel,
+ * in launch order, plus SGB_STAGE_SORT spanning every radix pass.  The three
+ * sort-pass kernels are timed on the first pass. */
 typedef enum {
-  SGB_STAGE_INIT = 0,       /* clear workspace header and digit histograms        */
-  SGB_STAGE_LINEARIZE = 1,  /* bags -> packed (linear id, info) words + histograms */
-  SGB_STAGE_SORT = 2,       /* all stable radix passes                            */
-  SGB_STAGE_RLE = 3,        /* run heads -> unique ids, run starts, run count      */
-  SGB_STAGE_RUNS = 4,       /* run lengths, long-run list, chunk prefix           */
-  SGB_STAGE_FILL = 5,       /* zeros of untouched rows (fresh dense grad only)    */
-  SGB_STAGE_REDUCE_LONG = 6,  /* long runs: chunked reduction + fused row write   */
-  SGB_STAGE_REDUCE_SHORT = 7, /* short runs: reduction + fused row write          */
-  SGB_NUM_STAGES = 8
+  SGB_STAGE_LINEARIZE = 0,     /* bags -> packed (linear id, info) words         */
+  SGB_STAGE_SORT_COUNT = 1,    /* radix pass: digit counts of every tile          */
+  SGB_STAGE_SORT_OFFSETS = 2,  /* radix pass: digit offsets of every tile         */
+  SGB_STAGE_SORT_SCATTER = 3,  /* radix pass: stable rank and scatter             */
+  SGB_STAGE_SORT = 4,          /* all radix passes                                */
+  SGB_STAGE_RLE_COUNT = 5,     /* run heads of every tile                         */
+  SGB_STAGE_RLE_SCAN = 6,      /* first run index of every tile, run count        */
+  SGB_STAGE_RLE_WRITE = 7,     /* unique ids, run starts                          */
+  SGB_STAGE_RUNS = 8,          /* run lengths, long-run list, chunk prefix        */
+  SGB_STAGE_FILL = 9,          /* zeros of untouched rows (fresh dense grad only) */
+  SGB_STAGE_REDUCE_LONG = 10,  /* long runs: chunked reduction + fused row write  */
+  SGB_STAGE_REDUCE_SHORT = 11, /* short runs: reduction + fused row write         */
+  SGB_NUM_STAGES = 12
 } sgb_stage;
 
 /*
  * sgb_backward_timed -- sgb_backward() that also records HIP events on
- * `stream` around each stage: events[2k] just before stage k's first kernel
- * and events[2k+1] just after its last (hipEvent_t passed as void*).  NULL
+ * `stream` around each timed region: events[2k] just before region k's first
+ * kernel and events[2k+1] just after its last (hipEvent_t passed as void*).  NULL
  * entries, and stages that do not run in this call, are skipped.  `events`
  * has 2 * SGB_NUM_STAGES entries or is NULL.  For measurement only: the
  * kernels and results are those of sgb_backward().

@@ -12,6 +12,8 @@
 
 #include <algorithm>
 #include <atomic>
+#include <functional>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -42,6 +44,13 @@ struct sgb_plan_s {
   int32_t n_fill = 0;
   int num_cus = 1;
   int red_grid[2] = {1, 1};  // persistent grid of the long-run reducer (f32, bf16)
+  // side streams (default priority): [0] clears a fresh dense gradient while
+  // the ids are sorted, [1] reduces the short runs while the long-run list is
+  // built and the long runs are reduced; the events fork and join them.  The
+  // mutex keeps one call's fork/join sequence from interleaving with another's.
+  hipStream_t aux[2] = {nullptr, nullptr};
+  hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};  // fork, fill done, rle done, short done
+  std::mutex mu;
 };
 
 namespace {
@@ -88,8 +97,7 @@ struct Layout {
   int64_t sort_tiles = 0, scan_tiles = 0;
   int64_t max_long = 0;   // bound on the number of long runs
   int64_t max_items = 0;  // bound on the (chunk, column block) items over all long runs
-  size_t hdr = 0, hist = 0, counts = 0, zero_begin = 0, tile_runs = 0, post_lb = 0, bitmap = 0,
-         zero_end_nobitmap = 0, zero_end_bitmap = 0;
+  size_t hdr = 0, hist = 0, counts = 0, zero_begin = 0, tile_runs = 0, post_lb = 0, zero_end = 0;
   size_t kvA = 0, kvB = 0, coefA = 0, coefB = 0, uniq = 0, cum = 0, headrun = 0, lens = 0, longs = 0,
          chunkb = 0, longrec = 0, runtk = 0, sctk = 0, part = 0, total = 0;
 };
@@ -139,9 +147,7 @@ sgb_status make_layout(const sgb_plan_s* p, int64_t N, int32_t B, bool has_offse
   L->post_lb = take(sizeof(uint64_t) * (size_t)L->scan_tiles);
   L->runtk = take(sizeof(uint32_t) * (size_t)L->max_items);
   L->sctk = take(sizeof(uint32_t) * (size_t)L->max_items);
-  L->zero_end_nobitmap = align_up(o, 256);
-  L->bitmap = take(sizeof(uint32_t) * (size_t)((p->total_rows + 31) / 32));
-  L->zero_end_bitmap = align_up(o, 256);
+  L->zero_end = align_up(o, 256);
   L->counts = take(sizeof(uint32_t) * (size_t)L->sort_tiles * kRadixMax);
   L->tile_runs = take(sizeof(uint32_t) * (size_t)L->scan_tiles);
   L->kvA = take(sizeof(uint64_t) * (size_t)N);
@@ -242,7 +248,11 @@ sgb_status sgb_plan_create(sgb_plan* out, int32_t T, const int64_t* hsc, const i
   p->red_grid[0] = p->num_cus * reduce_long_blocks_per_cu(false);
   p->red_grid[1] = p->num_cus * reduce_long_blocks_per_cu(true);
 
-  bool ok = hipMalloc(&p->d_hsc, sizeof(int64_t) * (T + 1)) == hipSuccess &&
+  bool ok = hipStreamCreateWithFlags(&p->aux[0], hipStreamNonBlocking) == hipSuccess &&
+            hipStreamCreateWithFlags(&p->aux[1], hipStreamNonBlocking) == hipSuccess;
+  for (int i = 0; i < 4 && ok; ++i)
+    ok = hipEventCreateWithFlags(&p->ev[i], hipEventDisableTiming) == hipSuccess;
+  ok = ok && hipMalloc(&p->d_hsc, sizeof(int64_t) * (T + 1)) == hipSuccess &&
             hipMalloc(&p->d_doff, sizeof(int32_t) * (T + 1)) == hipSuccess &&
             hipMalloc(&p->d_woff, sizeof(int64_t) * (T + 1)) == hipSuccess &&
             hipMalloc(&p->d_fill, sizeof(FillBlock) * fill.size()) == hipSuccess;
@@ -269,6 +279,10 @@ void sgb_plan_destroy(sgb_plan p) {
   if (p->d_doff) (void)hipFree(p->d_doff);
   if (p->d_woff) (void)hipFree(p->d_woff);
   if (p->d_fill) (void)hipFree(p->d_fill);
+  for (hipEvent_t e : p->ev)
+    if (e) (void)hipEventDestroy(e);
+  for (hipStream_t s : p->aux)
+    if (s) (void)hipStreamDestroy(s);
   delete p;
 }
 
@@ -311,10 +325,11 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   const bool fresh = u->mode == SGB_DENSE_GRAD && !u->accumulate;
   DeviceGuard guard(p->device);
   if (!guard.ok) return SGB_ERR_HIP;
-  auto mark = [&](int stage, int end) {
+  auto mark_on = [&](hipStream_t s, int stage, int end) {
     void* ev = events ? events[2 * stage + end] : nullptr;
-    if (ev) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev), stream);
+    if (ev) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev), s);
   };
+  auto mark = [&](int stage, int end) { mark_on(stream, stage, end); };
 
   if (N == 0) {  // FBGEMM host entry: no indices -> nothing to do (dense grad stays zero)
     // clear the status word so sgb_device_status() reports this call
@@ -322,7 +337,7 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
         launch_init(ws, sizeof(Header), stream) != hipSuccess)
       return SGB_ERR_HIP;
     if (fresh && p->n_fill > 0) {
-      FillParams f{out, p->d_fill, p->d_hsc, p->d_doff, p->d_woff, nullptr};
+      FillParams f{out, p->d_fill, p->d_doff, p->d_woff};
       if (launch_fill(f, p->n_fill, stream) != hipSuccess) return SGB_ERR_HIP;
     }
     return SGB_OK;
@@ -340,10 +355,24 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   const uint32_t epoch = next_epoch();
   const bool has_coef = (p->pooling == SGB_POOL_MEAN) || (b->per_sample_weights != nullptr);
   // (no separate clearing step: linearisation resets the header's counters)
-  mark(SGB_STAGE_INIT, 0);
-  mark(SGB_STAGE_INIT, 1);
 
-  // linearise (+ clear look-back words and the bitmap)
+  // the plan's side streams and fork/join events: one call's sequence at a time
+  std::lock_guard<std::mutex> lock(p->mu);
+  hipStream_t fill_s = p->aux[0], short_s = p->aux[1];
+  if (fresh) {
+    // fork: the fresh gradient is cleared on a side stream, overlapping the
+    // steps up to run-length encoding
+    if (hipEventRecord(p->ev[0], stream) != hipSuccess ||
+        hipStreamWaitEvent(fill_s, p->ev[0], 0) != hipSuccess)
+      return SGB_ERR_HIP;
+    FillParams f{out, p->d_fill, p->d_doff, p->d_woff};
+    mark_on(fill_s, SGB_STAGE_FILL, 0);
+    if (launch_fill(f, p->n_fill, fill_s) != hipSuccess) return SGB_ERR_HIP;
+    mark_on(fill_s, SGB_STAGE_FILL, 1);
+    if (hipEventRecord(p->ev[1], fill_s) != hipSuccess) return SGB_ERR_HIP;
+  }
+
+  // linearise (+ clear look-back words and combine tickets)
   LinParams lp{};
   lp.indices = b->indices;
   lp.offsets = b->offsets;
@@ -360,7 +389,7 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   lp.epoch = epoch;
   lp.header = hdr;
   lp.zero_begin = at<uint4>(ws, L.zero_begin);
-  lp.zero_vec4 = (int64_t)(((fresh ? L.zero_end_bitmap : L.zero_end_nobitmap) - L.zero_begin) / 16);
+  lp.zero_vec4 = (int64_t)((L.zero_end - L.zero_begin) / 16);
   const int64_t lin_tiles = b->offsets ? ((int64_t)b->B * p->T + kLinBags - 1) / kLinBags
                                        : (N + kLinLookups - 1) / kLinLookups;
   const int lin_grid = (int)std::max<int64_t>(1, std::min<int64_t>(lin_tiles, 16ll * p->num_cus));
@@ -388,7 +417,10 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
     sp.bases = at<uint32_t>(ws, L.hist) + ps * kRadixMax;
     sp.status = status;
     sp.epoch = epoch;
-    if (launch_sort_pass(sp, stream) != hipSuccess) return SGB_ERR_HIP;
+    // the kernels of the first pass are timed one by one
+    const std::function<void(int, int)> pass_mark =
+        ps == 0 ? std::function<void(int, int)>(mark) : std::function<void(int, int)>();
+    if (launch_sort_pass(sp, stream, pass_mark) != hipSuccess) return SGB_ERR_HIP;
     std::swap(kv_in, kv_out);
     std::swap(cf_in, cf_out);
   }
@@ -406,9 +438,7 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   rp.num_runs = &hdr->num_runs;
   rp.tiles = L.scan_tiles;
   rp.tile_runs = at<uint32_t>(ws, L.tile_runs);
-  mark(SGB_STAGE_RLE, 0);
-  if (launch_rle(rp, stream) != hipSuccess) return SGB_ERR_HIP;
-  mark(SGB_STAGE_RLE, 1);
+  if (launch_rle(rp, stream, mark) != hipSuccess) return SGB_ERR_HIP;
 
   PostParams pp{};
   pp.cum = rp.cum;
@@ -430,22 +460,10 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   pp.long_recs = at<LongRun>(ws, L.longrec);
   pp.num_long = &hdr->num_long;
   pp.total_items = &hdr->total_items;
-  pp.bitmap = fresh ? at<uint32_t>(ws, L.bitmap) : nullptr;
-  pp.total_rows = p->total_rows;
   pp.lookback = at<uint64_t>(ws, L.post_lb);
   pp.tile_ctr = &hdr->post_tile_ctr;
   pp.status = status;
   pp.epoch = epoch;
-  mark(SGB_STAGE_RUNS, 0);
-  if (launch_post(pp, (int)L.scan_tiles, stream) != hipSuccess) return SGB_ERR_HIP;
-  mark(SGB_STAGE_RUNS, 1);
-
-  if (fresh) {
-    FillParams f{out, p->d_fill, p->d_hsc, p->d_doff, p->d_woff, pp.bitmap};
-    mark(SGB_STAGE_FILL, 0);
-    if (launch_fill(f, p->n_fill, stream) != hipSuccess) return SGB_ERR_HIP;
-    mark(SGB_STAGE_FILL, 1);
-  }
 
   RedParams q{};
   q.grad = b->grad_output;
@@ -482,13 +500,27 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   q.lr = u->lr;
   q.eps = u->eps;
   const bool bf16 = b->grad_dtype == SGB_BF16;
+  // short runs need only the sorted words and run starts: side stream from
+  // here on (after the zero fill), while the long-run list is built and the
+  // long runs are reduced here; the two write disjoint rows
+  if (hipEventRecord(p->ev[2], stream) != hipSuccess ||
+      hipStreamWaitEvent(short_s, p->ev[2], 0) != hipSuccess ||
+      (fresh && hipStreamWaitEvent(short_s, p->ev[1], 0) != hipSuccess))
+    return SGB_ERR_HIP;
+  mark_on(short_s, SGB_STAGE_REDUCE_SHORT, 0);
+  if (launch_reduce_short(q, bf16, p->Dmin, p->Dmax, short_s) != hipSuccess) return SGB_ERR_HIP;
+  mark_on(short_s, SGB_STAGE_REDUCE_SHORT, 1);
+  if (hipEventRecord(p->ev[3], short_s) != hipSuccess) return SGB_ERR_HIP;
+  mark(SGB_STAGE_RUNS, 0);
+  if (launch_post(pp, (int)L.scan_tiles, stream) != hipSuccess) return SGB_ERR_HIP;
+  mark(SGB_STAGE_RUNS, 1);
+  if (fresh && hipStreamWaitEvent(stream, p->ev[1], 0) != hipSuccess) return SGB_ERR_HIP;
   mark(SGB_STAGE_REDUCE_LONG, 0);
   if (launch_reduce_long(q, bf16, p->red_grid[bf16 ? 1 : 0], stream) != hipSuccess)
     return SGB_ERR_HIP;
   mark(SGB_STAGE_REDUCE_LONG, 1);
-  mark(SGB_STAGE_REDUCE_SHORT, 0);
-  if (launch_reduce_short(q, bf16, p->Dmin, p->Dmax, stream) != hipSuccess) return SGB_ERR_HIP;
-  mark(SGB_STAGE_REDUCE_SHORT, 1);
+  // join: the call's work is complete when `stream` reaches this point
+  if (hipStreamWaitEvent(stream, p->ev[3], 0) != hipSuccess) return SGB_ERR_HIP;
   return SGB_OK;
 }
 

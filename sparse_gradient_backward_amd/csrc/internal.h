@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <functional>
+
 namespace sgb {
 
 // ---------------------------------------------------------------- limits
@@ -230,8 +232,6 @@ struct PostParams {
   LongRun* long_recs;       // [num_long]
   int64_t* num_long;
   uint32_t* total_items;
-  uint32_t* bitmap;         // touched-row bitmap (fresh dense grad) or NULL
-  int64_t total_rows;       // bitmap bits
   uint64_t* lookback;       // [tiles]
   uint32_t* tile_ctr;
   uint32_t* status;
@@ -241,10 +241,8 @@ struct PostParams {
 struct FillParams {
   float* out;
   const FillBlock* blocks;
-  const int64_t* hsc;
   const int32_t* doff;
   const int64_t* woff;
-  const uint32_t* bitmap;   // NULL: every row is zero-filled
 };
 
 struct RedParams {
@@ -288,8 +286,11 @@ struct RedParams {
 
 hipError_t launch_init(void* header_and_hist, size_t bytes, hipStream_t s);
 hipError_t launch_linearize(const LinParams& p, int grid, hipStream_t s);
-hipError_t launch_sort_pass(const SortParams& p, hipStream_t s);
-hipError_t launch_rle(const RleParams& p, hipStream_t s);
+// `mark(stage, end)` (if set) records the timing events of a kernel's
+// timed region just before (end = 0) and after (end = 1) its launch.
+hipError_t launch_sort_pass(const SortParams& p, hipStream_t s,
+                            const std::function<void(int, int)>& mark);
+hipError_t launch_rle(const RleParams& p, hipStream_t s, const std::function<void(int, int)>& mark);
 hipError_t launch_post(const PostParams& p, int grid, hipStream_t s);
 hipError_t launch_fill(const FillParams& p, int nblocks, hipStream_t s);
 hipError_t launch_reduce_long(const RedParams& p, bool bf16, int grid, hipStream_t s);

@@ -8,7 +8,8 @@
 //                with decoupled look-back, LDS-staged scatter
 //   k_rle_*      run heads of the sorted ids -> unique ids, run starts, count
 //   k_post       run lengths, ascending long-run list with chunk prefix
-//   k_fill       zeros for untouched rows of a fresh dense gradient
+//   k_fill       zeros of a fresh dense gradient (side stream, overlapping
+//                the steps up to run-length encoding)
 //   k_reduce_long   (chunk, column block) items of long runs from an atomic
 //                queue, partials combined in a fixed order by the last wave
 //   k_reduce_short  one wave per 64 sorted positions, short runs served one
@@ -22,6 +23,7 @@
 // formulas.  The kernels here are designed for wave64 CDNA4; see the notes at
 // each kernel for where they depart from the pages' CUDA design.
 #include "internal.h"
+#include "sgb.h"
 
 namespace sgb {
 namespace {
@@ -703,9 +705,9 @@ __global__ __launch_bounds__(kScanThreads) void k_rle_write(RleParams p) {
 // -- compacted in ascending run order (the page appends them through an
 // atomic counter in arbitrary order).  Each long run is cut into chunks of
 // chunk_len() lookups (set by the row width) times the 256-column blocks of
-// its row; a combined scan gives every long run its first work item.  For a
-// fresh dense gradient it also marks touched rows in a bitmap.  (The combine
-// tickets of the work items are cleared with the workspace's zeroed region.)
+// its row; a combined scan gives every long run its first work item.  (The
+// combine tickets of the work items are cleared with the workspace's zeroed
+// region.)
 
 // Table of a run from the info of one of its lookups (bag t*B+b, or token
 // l*T+t without bags).
@@ -799,29 +801,6 @@ __global__ __launch_bounds__(kScanThreads) void k_post(PostParams p) {
     const int q = k * kScanThreads + tid;
     if (q < n) p.run_lengths[base + q] = s_cum[q + 1] - s_cum[q];
   }
-  if (p.bitmap) {
-    // touched rows: lanes holding ids of the same 32-bit word (ids ascend
-    // along the lanes) OR their bits together; the first lane of each such
-    // segment does the one atomic
-    const int lane = tid & 63;
-#pragma unroll 1
-    for (int k = 0; k < kScanItems; ++k) {
-      const int q = k * kScanThreads + tid;
-      const bool ok = q < n;
-      const uint64_t key = ok ? (uint64_t)p.unique_ids[base + q] : ~0ull;
-      const bool in = ok && key < (uint64_t)p.total_rows;
-      const uint64_t word = in ? key >> 5 : ~0ull;
-      uint32_t bits = in ? 1u << (key & 31) : 0u;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t ob = __shfl_down(bits, off, 64);
-        const uint64_t ow = __shfl_down(word, off, 64);
-        if (lane + off < 64 && ow == word) bits |= ob;
-      }
-      const uint64_t pw = __shfl_up(word, 1, 64);
-      if (in && (lane == 0 || pw != word)) atomicOr(&p.bitmap[word], bits);
-    }
-  }
   __syncthreads();
   // the tile's long runs in order: tile-local slot -> position and first work
   // item (this thread's runs, cheap arithmetic), then their records written
@@ -884,27 +863,17 @@ __global__ __launch_bounds__(kScanThreads) void k_post(PostParams p) {
 
 // ------------------------------------------------------------------ k_fill
 //
-// A fresh dense gradient is zero except on touched rows (FBGEMM host entry
-// starts from zeros_like(dev_weights)); rows marked in the bitmap are skipped
-// here because the reducer writes them, so every element is written once.
+// A fresh dense gradient starts from zeros (FBGEMM host entry starts from
+// zeros_like(dev_weights)).  The whole buffer is cleared on a side stream
+// while the ids are linearised and sorted; the reducers write the touched
+// rows after it.
 
 __global__ __launch_bounds__(256) void k_fill(FillParams p) {
   const FillBlock fb = p.blocks[blockIdx.x];
   const int D = p.doff[fb.t + 1] - p.doff[fb.t];
-  const uint32_t d4 = (uint32_t)(D >> 2);
   float4* out = reinterpret_cast<float4*>(p.out + p.woff[fb.t] + fb.row0 * (int64_t)D);
-  const int64_t lin0 = p.hsc[fb.t] + fb.row0;
-  const uint32_t total = (uint32_t)fb.nrows * d4;
-  // q / d4 by multiply-shift (Granlund & Montgomery), exact for q < 2^31
-  uint32_t s = 0;
-  while ((1u << s) < d4) ++s;
-  const uint64_t magic = ((1ull << (32 + s)) + d4 - 1) / d4;
-  for (uint32_t q = threadIdx.x; q < total; q += blockDim.x) {
-    const uint32_t row = (uint32_t)(((uint64_t)q * magic) >> (32 + s));
-    const int64_t lin = lin0 + row;
-    if (p.bitmap && ((p.bitmap[lin >> 5] >> (lin & 31)) & 1u)) continue;
-    out[q] = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  const uint32_t total = (uint32_t)fb.nrows * (uint32_t)(D >> 2);
+  for (uint32_t q = threadIdx.x; q < total; q += blockDim.x) out[q] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 // ------------------------------------------------------------------ reducers
@@ -1637,19 +1606,35 @@ hipError_t launch_linearize(const LinParams& p, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_sort_pass(const SortParams& p, hipStream_t s) {
+hipError_t launch_sort_pass(const SortParams& p, hipStream_t s,
+                            const std::function<void(int, int)>& mark) {
   const unsigned tiles = (unsigned)p.tiles;
+  auto m = [&](int stage, int end) {
+    if (mark) mark(stage, end);
+  };
+  m(SGB_STAGE_SORT_COUNT, 0);
   hipLaunchKernelGGL(k_sort_count, dim3(tiles), dim3(kSortThreads), 0, s, p);
+  m(SGB_STAGE_SORT_COUNT, 1);
+  m(SGB_STAGE_SORT_OFFSETS, 0);
   hipLaunchKernelGGL(k_sort_offsets, dim3(1u << p.bits), dim3(kScanThreads), 0, s, p);
+  m(SGB_STAGE_SORT_OFFSETS, 1);
+  m(SGB_STAGE_SORT_SCATTER, 0);
   hipLaunchKernelGGL(k_sort_scatter, dim3(tiles), dim3(kSortThreads), 0, s, p);
+  m(SGB_STAGE_SORT_SCATTER, 1);
   return hipGetLastError();
 }
 
-hipError_t launch_rle(const RleParams& p, hipStream_t s) {
+hipError_t launch_rle(const RleParams& p, hipStream_t s, const std::function<void(int, int)>& mark) {
   const unsigned tiles = (unsigned)p.tiles;
+  mark(SGB_STAGE_RLE_COUNT, 0);
   hipLaunchKernelGGL(k_rle_count, dim3(tiles), dim3(kScanThreads), 0, s, p);
+  mark(SGB_STAGE_RLE_COUNT, 1);
+  mark(SGB_STAGE_RLE_SCAN, 0);
   hipLaunchKernelGGL(k_rle_scan, dim3(1), dim3(kScanThreads), 0, s, p);
+  mark(SGB_STAGE_RLE_SCAN, 1);
+  mark(SGB_STAGE_RLE_WRITE, 0);
   hipLaunchKernelGGL(k_rle_write, dim3(tiles), dim3(kScanThreads), 0, s, p);
+  mark(SGB_STAGE_RLE_WRITE, 1);
   return hipGetLastError();
 }
 
