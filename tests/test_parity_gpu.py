@@ -12,7 +12,9 @@ import pytest
 import torch
 
 import synth
-from harness import assert_close, check_case, check_runs, initial_buffers, run_gpu, to_dev
+import oracle
+from harness import (assert_close, check_case, check_runs, expected_rows, initial_buffers,
+                     oracle_problem, row_elements, run_gpu, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -270,3 +272,54 @@ def test_host_detected_errors(sgb):
                       device="cuda"), momentum=torch.zeros(10, device="cuda"),
                       workspace=wide.workspace(1, 1))
     assert e.value.name == "SGB_ERR_UNSUPPORTED"
+
+
+@pytest.mark.parametrize("cfg", [2, 5])
+def test_own_stream_and_timed(sgb, cfg):
+    """The call on a stream of the caller's own, completed by synchronising that
+    stream alone (the side streams are joined back into it), matches the
+    oracle; the timed entry point (events around every kernel) gives
+    bit-identical outputs."""
+    s = synth.spec(2, T=2, E=(4000, 3000), B=300) if cfg == 2 else \
+        synth.spec(5, E=(60000,), B=2000)
+    inp = synth.generate(s)
+    _say(f"[parity] own stream config {cfg} N={inp.N}")
+    dev = to_dev(inp)
+    plan = sgb.Plan(inp.hash_size_cumsum, inp.D_offsets, s.pooling, 64)
+    B = inp.B
+    ws = plan.workspace(inp.N, B)
+    o0, m0h = initial_buffers(inp, s.mode, s.accumulate)
+    out0 = torch.from_numpy(o0).cuda()
+    mom0 = None if m0h is None else torch.from_numpy(m0h).cuda()
+    outs = []
+    for timed in (False, True):
+        out = out0.clone()
+        mom = None if mom0 is None else mom0.clone()
+        kw = dict(weights=out, momentum=mom) if s.mode != "dense" else dict(grad=out)
+        st = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        events = None
+        if timed:
+            events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(sgb.STAGES))]
+            with torch.cuda.stream(st):
+                for e in events:
+                    e.record()
+        with torch.cuda.stream(st):
+            plan.backward(dev["grad"], dev["indices"], dev["offsets"], B, dev["psw"], s.mode,
+                          accumulate=s.accumulate, lr=s.lr, eps=s.eps, workspace=ws,
+                          stream=st, events=events, **kw)
+        st.synchronize()  # only this stream
+        host = out.cpu().numpy()
+        outs.append((host, None if mom is None else mom.cpu().numpy()))
+        assert plan.device_status(ws, st) == "SGB_OK"
+    assert np.array_equal(outs[0][0].view(np.uint32), outs[1][0].view(np.uint32))
+    if outs[0][1] is not None:
+        assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
+    # and the values are the oracle's
+    keys, _, _ = oracle.linearize(oracle_problem(inp))
+    rows = np.unique(keys)
+    elems, valid, _ = row_elements(inp, rows)
+    m0 = None if m0h is None else m0h[rows]
+    exp, emom, _ = expected_rows(inp, rows, s.mode, o0[elems], m0, accumulate=s.accumulate,
+                                 lr=s.lr, eps=s.eps)
+    assert_close(outs[0][0][elems], exp, valid, "rows on the caller's stream")
