@@ -9,8 +9,8 @@ per-sample weights, Zipf 1.05, B=2048); --config selects another one.
 
 Prints ONE JSON line on stdout (progress goes to stderr):
   value        lookups/s of the whole step (wall clock, synchronised)
-  roofline     the dominant kernel: algorithmic bytes per launch / its average
-               duration from HIP events recorded on the library's stream
+  roofline     the dominant kernel (largest time per step): algorithmic bytes
+               per launch / its mean launch duration from HIP events around it
   cpu_baseline the CPU oracle (plain C, one thread) on the same batch
 """
 from __future__ import annotations
@@ -234,8 +234,10 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
 
-    # timed region 2: the same steps with HIP events around each stage,
-    # recorded by the library on its stream
+    # timed region 2: the same steps with HIP events around each kernel,
+    # recorded by the library on the stream the kernel runs on (the timed
+    # entry point runs the kernels one after another on one stream, so each
+    # pair of events brackets one kernel alone)
     evs = []
     for _ in range(args.steps):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(STAGES))]

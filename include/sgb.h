@@ -198,7 +198,9 @@ typedef enum {
  * kernel and events[2k+1] just after its last (hipEvent_t passed as void*).  NULL
  * entries, and stages that do not run in this call, are skipped.  `events`
  * has 2 * SGB_NUM_STAGES entries or is NULL.  For measurement only: the
- * kernels and results are those of sgb_backward().
+ * kernels and results are those of sgb_backward(), but with events given all
+ * of them run one after another on `stream` (no side streams), so that each
+ * timed region holds its kernel alone.
  */
 sgb_status sgb_backward_timed(sgb_plan plan, const sgb_batch* batch, const sgb_update* update,
                               void* workspace, size_t workspace_bytes, void* stream,

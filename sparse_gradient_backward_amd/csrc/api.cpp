@@ -358,7 +358,10 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
 
   // the plan's side streams and fork/join events: one call's sequence at a time
   std::lock_guard<std::mutex> lock(p->mu);
-  hipStream_t fill_s = p->aux[0], short_s = p->aux[1];
+  // the timed variant runs every kernel in order on `stream`, so that each
+  // kernel's events bracket that kernel alone
+  const bool overlap = events == nullptr;
+  hipStream_t fill_s = overlap ? p->aux[0] : stream, short_s = overlap ? p->aux[1] : stream;
   if (fresh) {
     // fork: the fresh gradient is cleared on a side stream, overlapping the
     // steps up to run-length encoding
