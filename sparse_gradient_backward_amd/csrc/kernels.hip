@@ -1,20 +1,25 @@
 // kernels.hip -- gfx950 kernels of the pooled embedding-bag backward.
 //
-// Pipeline (one HIP stream, no host synchronisation):
-//   k_init       zero the workspace header and digit histograms
-//   k_linearize  bags -> per-lookup packed word (linear id << info_bits | info)
-//                and coefficient; digit histograms of every sort pass
-//   k_sort_pass  one stable LSD radix pass (<= 9-bit digits), single sweep
-//                with decoupled look-back, LDS-staged scatter
-//   k_rle_*      run heads of the sorted ids -> unique ids, run starts, count
-//   k_post       run lengths, ascending long-run list with chunk prefix
-//   k_fill       zeros of a fresh dense gradient (side stream, overlapping
-//                the steps up to run-length encoding)
-//   k_reduce_long   (chunk, column block) items of long runs from an atomic
-//                queue, partials combined in a fixed order by the last wave
-//   k_reduce_short  one wave per 64 sorted positions, short runs served one
-//                per lane group; both finish each row with the fused dense /
-//                SGD / row-wise Adagrad step
+// Pipeline (no host synchronisation; the caller's stream unless noted):
+//   k_init         zero the workspace header (empty batches only)
+//   k_linearize    bags -> per-lookup packed word (linear id << info_bits | info)
+//                  and coefficient; range and offset checks; zeroes the
+//                  region the later kernels count in
+//   k_sort_count / k_sort_offsets / k_sort_scatter
+//                  one stable LSD radix pass (<= 9-bit digits) as
+//                  reduce-then-scan: tile digit counts, their scan per digit,
+//                  ballot-ranked LDS-staged scatter
+//   k_rle_count / k_rle_scan / k_rle_write
+//                  run heads of the sorted ids -> unique ids, run starts, count
+//   k_post         run lengths, ascending long-run list and records
+//   k_fill         zeros of a fresh dense gradient (side stream, from the start)
+//   k_reduce_short short runs (side stream, after run-length encoding): the
+//                  runs starting in a part of a 64-position window, one per
+//                  lane group
+//   k_reduce_long  (chunk, column block) items of long runs, fp64 partials
+//                  combined in a fixed order by the last-arriving workgroup
+//   Both reducers finish each row with the fused dense / SGD / row-wise
+//   Adagrad step.
 //
 // Method: "fbgemm_gpu/codegen/embedding_backward_split_template.cu" (FBGEMM),
 // host entry `..._exact_cuda` (linearise, sort, run-length encode, long
