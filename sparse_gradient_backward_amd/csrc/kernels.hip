@@ -1018,31 +1018,56 @@ __device__ __forceinline__ RowDst row_dest(const RedParams& p, int t, int D, int
   return d;
 }
 
-// One gathered grad_output row of a long run: the row and the sum of the
-// coefficients of the run's consecutive lookups that read it.
+// Lane groups of a long-run item: lpl lanes per group (the power of two
+// covering D/4, 4..64), 64/lpl groups per wave.  lpl is a wave-uniform
+// runtime value, so one code path -- and one register budget -- serves every
+// row width.
+struct Groups {
+  int lpl;         // lanes per group
+  int g;           // this lane's group
+  int lig;         // this lane's index in its group
+  int gb;          // first lane of its group
+  uint64_t gmask;  // the lanes of its group
+};
+
+__device__ __forceinline__ Groups groups_of(int lpl) {
+  const int lane = lane_id();
+  Groups q;
+  q.lpl = lpl;
+  q.lig = lane & (lpl - 1);
+  q.gb = lane - q.lig;
+  q.g = lane >> __builtin_ctz((unsigned)lpl);
+  q.gmask = lpl == 64 ? ~0ull : (((1ull << lpl) - 1ull) << q.gb);
+  return q;
+}
+
+// One gathered grad_output row of a long run: the element offset of the row
+// and the sum of the coefficients of the run's consecutive lookups that read
+// it.
 struct MergedRow {
-  int32_t row;
-  int32_t pad;
+  int64_t base;
   double coef;
 };
 
 // Sum over lookups j in [first, last) of coef_j * grad row_j at elements
-// [colofs, colofs+4), where each group of LPL lanes passes its own range
-// (uniform within the group; the ranges of a wave differ by at most LPL).
-// Within a run the lookups are ordered by bag, so lookups of one bag -- one
-// grad_output row -- are adjacent: each slice of LPL lookups is merged into
+// [colofs, colofs+4), where each lane group passes its own range (uniform
+// within the group; the ranges of a wave differ by at most lpl).  Within a
+// run the lookups are ordered by bag, so lookups of one bag -- one
+// grad_output row -- are adjacent: each slice of lpl lookups is merged into
 // (row, summed coefficient) entries first (segmented sum across the lanes,
 // fp64), the entries are compacted into the wave's LDS list `q`, and only
-// they are gathered.  The next slice's metadata is loaded while the current
-// one is gathered.  Called with the whole wave active.
-template <int LPL, int UNR, bool BF16>
-__device__ __forceinline__ d4 gather_merged(const RedParams& p, int first, int last, int slices,
-                                            int t, int64_t colofs, bool col_ok, MergedRow* q) {
+// they are gathered, UNR rows per lane at a time: the row offsets are read
+// from the list first, then every load of the round is issued before any
+// value is used.  The next slice's metadata is loaded while the current one
+// is gathered.  Called with the whole wave active.
+template <int UNR, bool BF16>
+__device__ __forceinline__ d4 gather_merged(const RedParams& p, const Groups& G, int first, int last,
+                                            int slices, int t, int64_t colofs, bool col_ok,
+                                            MergedRow* q) {
   const int lane = lane_id();
-  const int gb = lane & ~(LPL - 1), lig = lane & (LPL - 1);
+  const int lpl = G.lpl, lig = G.lig, gb = G.gb;
   const uint64_t imask = info_mask(p);
   const bool has_coef = p.coef != nullptr;
-  const uint64_t gmask = (LPL == 64) ? ~0ull : (((1ull << LPL) - 1ull) << gb);
   auto clampj = [&](int j) { return j < last ? j : (last > first ? last - 1 : first); };
   d4 acc = d4_zero();
   // metadata of this lane's lookup in slice 0 (loads from a valid index even
@@ -1052,7 +1077,7 @@ __device__ __forceinline__ d4 gather_merged(const RedParams& p, int first, int l
   float c = has_coef ? p.coef[clampj(j)] : 1.0f;
   for (int s = 0; s < slices; ++s) {
     const bool ok = j < last;
-    const int jn = j + LPL;
+    const int jn = j + lpl;
     const uint64_t wn = p.kv[clampj(jn)];
     const float cn = has_coef ? p.coef[clampj(jn)] : 1.0f;
     const int row = ok ? grad_row_of(p, (uint32_t)(w & imask), t) : -1 - lane;
@@ -1061,38 +1086,35 @@ __device__ __forceinline__ d4 gather_merged(const RedParams& p, int first, int l
     double cs = ok ? (double)c : 0.0;
     const int prow = __shfl_up(row, 1, 64);
     const bool head = ok && (lig == 0 || prow != row);
-#pragma unroll
-    for (int off = 1; off < LPL; off <<= 1) {
+    for (int off = 1; off < lpl; off <<= 1) {
       const double o = __shfl_down(cs, off, 64);
       const int orow = __shfl_down(row, off, 64);
-      if (lig + off < LPL && orow == row) cs += o;
+      if (lig + off < lpl && orow == row) cs += o;
     }
-    const uint64_t hm = __ballot(head) & gmask;
+    const uint64_t hm = __ballot(head) & G.gmask;
     const int cnt = __popcll(hm);
     if (head) {
       const int at = __popcll(hm & ((1ull << lane) - 1ull));
-      q[gb + at] = MergedRow{row, 0, cs};
+      q[gb + at] = MergedRow{(int64_t)row * p.row_stride, cs};
     }
     // (a wave's LDS accesses are performed in order: the list is complete
     // for the reads below)
     for (int jj = 0; jj < cnt; jj += UNR) {
+      int64_t eb[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) eb[u] = q[gb + min(jj + u, lpl - 1)].base;
       Raw4<BF16> r[UNR];
-      double cf[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u)
+        r[u] = (jj + u < cnt && col_ok) ? load_raw4<BF16>(p.grad, eb[u] + colofs) : zero_raw4<BF16>();
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
-        const bool okk = (jj + u < cnt) && col_ok;
-        const MergedRow e = q[gb + min(jj + u, LPL - 1)];
-        cf[u] = okk ? e.coef : 0.0;
-        r[u] = okk ? load_raw4<BF16>(p.grad, (int64_t)e.row * p.row_stride + colofs)
-                   : zero_raw4<BF16>();
-      }
-#pragma unroll
-      for (int u = 0; u < UNR; ++u) {
+        const double cf = (jj + u < cnt && col_ok) ? q[gb + min(jj + u, lpl - 1)].coef : 0.0;
         const float4 v = widen4<BF16>(r[u]);
-        acc.x = fma(cf[u], (double)v.x, acc.x);
-        acc.y = fma(cf[u], (double)v.y, acc.y);
-        acc.z = fma(cf[u], (double)v.z, acc.z);
-        acc.w = fma(cf[u], (double)v.w, acc.w);
+        acc.x = fma(cf, (double)v.x, acc.x);
+        acc.y = fma(cf, (double)v.y, acc.y);
+        acc.z = fma(cf, (double)v.z, acc.z);
+        acc.w = fma(cf, (double)v.w, acc.w);
       }
     }
     j = jn;
@@ -1102,24 +1124,25 @@ __device__ __forceinline__ d4 gather_merged(const RedParams& p, int first, int l
   return acc;
 }
 
-// Adds the 64/LPL lane groups of a wave (fixed xor tree; all groups get the sum).
-template <int LPL>
-__device__ __forceinline__ d4 fold_groups(d4 a) {
-#pragma unroll
-  for (int off = 32; off >= LPL; off >>= 1) d4_add(a, d4_xor(a, off));
+// Adds the lane groups of a wave (fixed xor tree; all groups get the sum).
+__device__ __forceinline__ d4 fold_groups(d4 a, int lpl) {
+  for (int off = 32; off >= lpl; off >>= 1) d4_add(a, d4_xor(a, off));
   return a;
 }
 
-// Sum over the LPL lanes of a group (fixed xor tree).
-template <int LPL>
-__device__ __forceinline__ double group_sum(double x) {
-#pragma unroll
-  for (int off = LPL / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+// Sum over the lanes of a group (fixed xor tree).
+__device__ __forceinline__ double group_sum(double x, int lpl) {
+  for (int off = lpl / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
   return x;
 }
 
 __device__ __forceinline__ float4 ld4(const float* q) { return *reinterpret_cast<const float4*>(q); }
 __device__ __forceinline__ void st4(float* q, float4 v) { *reinterpret_cast<float4*>(q) = v; }
+
+// One fp32 result from an fp64 value, rounded once.
+__device__ __forceinline__ float4 round4(double x, double y, double z, double w) {
+  return make_float4((float)x, (float)y, (float)z, (float)w);
+}
 
 // Finishes column blocks [cb_lo, cb_hi) of one row whose gradient for block
 // cb is getG(cb) (this lane's 4 columns).  getG is called by the whole wave.
@@ -1131,15 +1154,10 @@ __device__ __forceinline__ void st4(float* q, float4 v) { *reinterpret_cast<floa
 // `cache_backward_sgd_kernel`).  Dense: store, or add for an accumulating
 // grad_weight (tinygrad `_embedding_bwd_kernel`).  The old row value is read
 // before getG so that the read overlaps the gather.
-// One fp32 result from an fp64 value, rounded once.
-__device__ __forceinline__ float4 round4(double x, double y, double z, double w) {
-  return make_float4((float)x, (float)y, (float)z, (float)w);
-}
-
-template <int LPL, class F>
-__device__ __forceinline__ void finish_row(const RedParams& p, const RowDst& dst, int D, bool write,
-                                           int cb_lo, int cb_hi, F&& getG) {
-  const int lig = lane_id() & (LPL - 1);
+template <class F>
+__device__ __forceinline__ void finish_row(const RedParams& p, const Groups& G, const RowDst& dst,
+                                           int D, bool write, int cb_lo, int cb_hi, F&& getG) {
+  const int lig = G.lig;
   if (p.mode == kModeAdagrad) {
     const bool w0ok = write && 4 * lig < D;
     const float4 w0 = w0ok ? ld4(dst.out + 4 * lig) : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1153,7 +1171,7 @@ __device__ __forceinline__ void finish_row(const RedParams& p, const RowDst& dst
       const d4 g = getG(cb);
       if (cb * kColBlock + 4 * lig < D) ss += d4_sumsq(g);
     }
-    ss = group_sum<LPL>(ss);
+    ss = group_sum(ss, G.lpl);
     const double m = (double)m0 + ss / (double)D;
     const double mult = (double)p.lr / (sqrt(m) + (double)p.eps);
     if (w0ok)
@@ -1194,6 +1212,39 @@ __device__ __forceinline__ void finish_row(const RedParams& p, const RowDst& dst
   }
 }
 
+// Update of one 256-column block cb of a row whose gradient g (this lane's 4
+// columns, fp64) is complete, from the old values `old` (and Adagrad state
+// m0) read before g was gathered.  Row-wise Adagrad here covers a row of one
+// block; wider rows take finish_row.
+__device__ __forceinline__ void update_block(const RedParams& p, const Groups& G, const RowDst& dst,
+                                             int D, bool write, int cb, const float4& old, float m0,
+                                             const d4& g) {
+  const int lig = G.lig;
+  const int col = cb * kColBlock + 4 * lig;
+  const bool ok = write && col < D;
+  if (p.mode == kModeAdagrad) {
+    const double ss = group_sum(col < D ? d4_sumsq(g) : 0.0, G.lpl);
+    const double m = (double)m0 + ss / (double)D;
+    const double mult = (double)p.lr / (sqrt(m) + (double)p.eps);
+    if (ok)
+      st4(dst.out + col, round4((double)old.x - g.x * mult, (double)old.y - g.y * mult,
+                                (double)old.z - g.z * mult, (double)old.w - g.w * mult));
+    if (write && lig == 0) *dst.mom = (float)m;
+    return;
+  }
+  if (!ok) return;
+  float4 wv;
+  if (p.mode == kModeSgd) {
+    const double lr = (double)p.lr;
+    wv = round4((double)old.x - lr * g.x, (double)old.y - lr * g.y, (double)old.z - lr * g.z,
+                (double)old.w - lr * g.w);
+  } else if (p.accumulate) {
+    wv = round4((double)old.x + g.x, (double)old.y + g.y, (double)old.z + g.z, (double)old.w + g.w);
+  } else {
+    wv = round4(g.x, g.y, g.z, g.w);
+  }
+  st4(dst.out + col, wv);
+}
 // Partials travel between waves on different XCDs.  They are written and read
 // with device-scope (agent) atomic accesses, which the hardware keeps coherent
 // across the XCDs' L2 caches by themselves; an agent-scope release/acquire
@@ -1245,79 +1296,98 @@ __device__ __forceinline__ double* slot_of(const RedParams& p, uint32_t cbeg, in
   return p.partials + ((int64_t)cbeg + (int64_t)c * ncb + cb) * kColBlock;
 }
 
+
 // Sum of the partials of chunks first, first+stride, ... (count of them) for
-// column block cb, groups interleaved, folded in a fixed order.
-template <int LPL>
-__device__ __forceinline__ d4 sum_slots(const RedParams& p, uint32_t cbeg, int ncb, int first,
-                                        int count, int stride, int cb, int D) {
-  constexpr int G = 64 / LPL;
-  const int lane = lane_id(), g = lane / LPL, lig = lane & (LPL - 1);
-  const int col = 4 * lig;
+// column block cb, groups interleaved, each group adding its partials in
+// order and the groups folded by a fixed tree.  Four partials per lane are in
+// flight at a time.
+__device__ __forceinline__ d4 sum_slots(const RedParams& p, const Groups& G, uint32_t cbeg, int ncb,
+                                        int first, int count, int stride, int cb, int D) {
+  const int ng = 64 / G.lpl;
+  const int col = 4 * G.lig;
   d4 acc = d4_zero();
   if (cb * kColBlock + col < D) {
-    for (int i = g; i < count; i += G)
-      d4_add(acc, load_partial(slot_of(p, cbeg, first + i * stride, ncb, cb) + col));
+    int i = G.g;
+    for (; i + 3 * ng < count; i += 4 * ng) {
+      const d4 a0 = load_partial(slot_of(p, cbeg, first + i * stride, ncb, cb) + col);
+      const d4 a1 = load_partial(slot_of(p, cbeg, first + (i + ng) * stride, ncb, cb) + col);
+      const d4 a2 = load_partial(slot_of(p, cbeg, first + (i + 2 * ng) * stride, ncb, cb) + col);
+      const d4 a3 = load_partial(slot_of(p, cbeg, first + (i + 3 * ng) * stride, ncb, cb) + col);
+      d4_add(acc, a0);
+      d4_add(acc, a1);
+      d4_add(acc, a2);
+      d4_add(acc, a3);
+    }
+    for (; i < count; i += ng) d4_add(acc, load_partial(slot_of(p, cbeg, first + i * stride, ncb, cb) + col));
   }
-  return fold_groups<LPL>(acc);
+  return fold_groups(acc, G.lpl);
 }
 
-template <int LPL, bool BF16>
+template <bool BF16>
 __device__ __forceinline__ void long_item(const RedParams& p, const LongRun& rec, int c, int cb) {
-  constexpr int G = 64 / LPL;
-  const int lane = lane_id(), g = lane / LPL, lig = lane & (LPL - 1);
   const int t = rec.t, start = rec.start, len = rec.len, D = rec.D;
+  const Groups G = groups_of(lanes_per_row(D));
+  const int ng = 64 / G.lpl, g = G.g, lig = G.lig;
   const int ncb = rec.ncb;
   const int chl = chunk_len(len, D, p.chunk_base);
   const int nch = rec.nch;
   const int lo = start + c * chl;
   const int hi = min(lo + chl, start + len);
   // Adagrad needs the whole row in one wave: item cb 0 covers every block
-  const int cb_lo = p.mode == kModeAdagrad ? 0 : cb;
-  const int cb_hi = p.mode == kModeAdagrad ? ncb : cb + 1;
+  const bool adagrad = p.mode == kModeAdagrad;
+  const int cb_lo = adagrad ? 0 : cb;
+  const int cb_hi = adagrad ? ncb : cb + 1;
   const int64_t gcol = rec.gcol;
   const RowDst dst{p.out + rec.out, p.mom ? p.mom + rec.mom : nullptr};
   // each lane group takes a contiguous share of the chunk, so that the
   // adjacent lookups of one bag stay together for merging
-  const int per = (hi - lo + G - 1) / G;
+  const int per = (hi - lo + ng - 1) / ng;
   const int glo = min(lo + g * per, hi), ghi = min(glo + per, hi);
-  const int slices = (per + LPL - 1) / LPL;
+  const int slices = (per + G.lpl - 1) / G.lpl;
   __shared__ MergedRow s_rows[4][64];
   MergedRow* q = s_rows[threadIdx.x >> 6];
-  auto chunkG = [&](int cbx) {
-    const int col = cbx * kColBlock + 4 * lig;
-    const d4 a =
-        gather_merged<LPL, SGB_LONG_UNR, BF16>(p, glo, ghi, slices, t, gcol + col, col < D, q);
-    return fold_groups<LPL>(a);
-  };
-  if (nch == 1) {
-    finish_row<LPL>(p, dst, D, g == 0, cb_lo, cb_hi, chunkG);
-    return;
-  }
+  // The only chunk of a row that needs nothing beyond this item (Adagrad: a
+  // row of one block) updates the row itself; otherwise each block's sum is
+  // this item's partial.  One gather site keeps the register budget that of
+  // a single gather loop.
+  const bool direct = nch == 1 && (!adagrad || ncb == 1);
+  const bool needs_old = p.mode != kModeDense || p.accumulate;
   const uint32_t cbeg = rec.cbeg;
 #pragma unroll 1
   for (int cbx = cb_lo; cbx < cb_hi; ++cbx) {
-    const d4 a = chunkG(cbx);
-    if (g == 0 && cbx * kColBlock + 4 * lig < D) store_partial(slot_of(p, cbeg, c, ncb, cbx) + 4 * lig, a);
+    const int col = cbx * kColBlock + 4 * lig;
+    const bool col_ok = col < D;
+    // the old row (and state) is read before the gather so the two overlap
+    const bool rd = direct && g == 0 && col_ok && needs_old;
+    const float4 old = rd ? ld4(dst.out + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float mom0 = (direct && adagrad && g == 0) ? *dst.mom : 0.f;
+    const d4 a = fold_groups(
+        gather_merged<SGB_LONG_UNR, BF16>(p, G, glo, ghi, slices, t, gcol + col, col_ok, q), G.lpl);
+    if (direct)
+      update_block(p, G, dst, D, g == 0, cbx, old, mom0, a);
+    else if (g == 0 && col_ok)
+      store_partial(slot_of(p, cbeg, c, ncb, cbx) + 4 * lig, a);
   }
+  if (direct) return;
   const int m0 = (c / kSuperChunk) * kSuperChunk;
   const int members = min(kSuperChunk, nch - m0);
   if (!ticket_last(p.sc_ticket + cbeg + (int64_t)m0 * ncb + cb_lo, (uint32_t)members)) return;
   const int nsc = (nch + kSuperChunk - 1) / kSuperChunk;
   if (nsc == 1) {
-    finish_row<LPL>(p, dst, D, g == 0, cb_lo, cb_hi, [&](int cbx) {
-      return sum_slots<LPL>(p, cbeg, ncb, 0, nch, 1, cbx, D);
+    finish_row(p, G, dst, D, g == 0, cb_lo, cb_hi, [&](int cbx) {
+      return sum_slots(p, G, cbeg, ncb, 0, nch, 1, cbx, D);
     });
     return;
   }
 #pragma unroll 1
   for (int cbx = cb_lo; cbx < cb_hi; ++cbx) {
-    const d4 a = sum_slots<LPL>(p, cbeg, ncb, m0, members, 1, cbx, D);
+    const d4 a = sum_slots(p, G, cbeg, ncb, m0, members, 1, cbx, D);
     if (g == 0 && cbx * kColBlock + 4 * lig < D)
       store_partial(slot_of(p, cbeg, m0, ncb, cbx) + 4 * lig, a);
   }
   if (!ticket_last(p.run_ticket + cbeg + cb_lo, (uint32_t)nsc)) return;
-  finish_row<LPL>(p, dst, D, g == 0, cb_lo, cb_hi, [&](int cbx) {
-    return sum_slots<LPL>(p, cbeg, ncb, 0, nsc, kSuperChunk, cbx, D);
+  finish_row(p, G, dst, D, g == 0, cb_lo, cb_hi, [&](int cbx) {
+    return sum_slots(p, G, cbeg, ncb, 0, nsc, kSuperChunk, cbx, D);
   });
 }
 
@@ -1339,6 +1409,31 @@ __device__ __forceinline__ int find_long_run(const uint32_t* cbeg, int nlong, ui
   return __builtin_amdgcn_readfirstlane(lo);
 }
 
+// A wave-uniform copy of a long-run record (its fields steer the wave's
+// control flow).
+__device__ __forceinline__ int32_t uni32(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uni64(int64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ LongRun uniform_rec(const LongRun& r) {
+  LongRun u;
+  u.start = uni32(r.start);
+  u.len = uni32(r.len);
+  u.t = uni32(r.t);
+  u.ncb = uni32(r.ncb);
+  u.cbeg = (uint32_t)uni32((int32_t)r.cbeg);
+  u.nch = uni32(r.nch);
+  u.id = uni64(r.id);
+  u.D = uni32(r.D);
+  u.gcol = uni32(r.gcol);
+  u.out = uni64(r.out);
+  u.mom = uni64(r.mom);
+  return u;
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_reduce_long(RedParams p) {
   const uint32_t n_items = *p.total_items;
@@ -1349,17 +1444,11 @@ __global__ __launch_bounds__(256) void k_reduce_long(RedParams p) {
   const uint32_t nw = gridDim.x * (blockDim.x / 64);
   for (uint32_t w = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6); w < n_items; w += nw) {
     const int k = find_long_run(p.chunk_begin, nlong, w);
-    const LongRun rec = p.long_recs[k];
+    const LongRun rec = uniform_rec(p.long_recs[k]);
     const int local = (int)(w - rec.cbeg);
     const int c = local / rec.ncb, cb = local % rec.ncb;
     if (p.mode == kModeAdagrad && cb != 0) continue;
-    switch (lanes_per_row(rec.D)) {
-      case 4: long_item<4, BF16>(p, rec, c, cb); break;
-      case 8: long_item<8, BF16>(p, rec, c, cb); break;
-      case 16: long_item<16, BF16>(p, rec, c, cb); break;
-      case 32: long_item<32, BF16>(p, rec, c, cb); break;
-      default: long_item<64, BF16>(p, rec, c, cb); break;
-    }
+    long_item<BF16>(p, rec, c, cb);
   }
 }
 
