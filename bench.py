@@ -58,7 +58,10 @@ def stage_bytes(inp: synth.Inputs, spec: synth.Spec, U: int, run_D: np.ndarray,
     Ds = np.diff(inp.D_offsets).astype(np.int64)
     Es = np.diff(inp.hash_size_cumsum).astype(np.int64)
     touched_elems = int(run_D.sum())
-    tiles = (N + 4095) // 4096
+    # sort tiles: 256 threads x 8 items for batches up to 2^20 lookups, x 12 above
+    sort_tile = 256 * (8 if N <= (1 << 20) else 12)
+    tiles = (N + sort_tile - 1) // sort_tile
+    scan_tiles = (N + 4095) // 4096
 
     def update(D):
         if spec.mode == "dense":
@@ -75,11 +78,11 @@ def stage_bytes(inp: synth.Inputs, spec: synth.Spec, U: int, run_D: np.ndarray,
         "sort_count": N * 8 + tiles * radix0 * 4,
         "sort_offsets": tiles * radix0 * 4 * 2 + radix0 * 4,
         "sort_scatter": N * rec * 2 + tiles * radix0 * 4 + radix0 * 4,
-        "rle_count": N * 8 + tiles * 4,
-        "rle_scan": tiles * 4 * 2 + 8,
-        "rle_write": N * 8 + tiles * 4 + U * (8 + 4 + 4),
-        "runs": U * (4 + 4 + (8 if fresh else 0)),
-        "fill": ((int((Es * Ds).sum()) - touched_elems) * 4 + int(Es.sum()) // 8) if fresh else 0,
+        "rle_count": N * 8 + scan_tiles * 4,
+        "rle_scan": scan_tiles * 4 * 2 + 8,
+        "rle_write": N * 8 + scan_tiles * 4 + U * (8 + 4 + 4),
+        "runs": U * (4 + 4) + int(lg.sum()) * (48 + 4 + 4),
+        "fill": int((Es * Ds).sum()) * 4 if fresh else 0,
         "reduce_long": gather_long + int(run_len[lg].sum()) * rec + int(lg.sum()) * 48
         + update(run_D[lg]),
         "reduce_short": gather_short + N * 8 + int(run_len[~lg].sum()) * 4 * c

@@ -125,7 +125,11 @@ sgb_status make_layout(const sgb_plan_s* p, int64_t N, int32_t B, bool has_offse
     L->pass_key_shift[i] = at;
     at += L->pass_bits[i];
   }
-  L->sort_tiles = (N + kSortTile - 1) / kSortTile;
+  const int64_t sort_tile = (int64_t)kSortThreads * sort_items_for(N);
+  L->sort_tiles = (N + sort_tile - 1) / sort_tile;
+  // the tile counts are sized for the smallest tiles, so a workspace sized
+  // for N also fits every smaller batch
+  const int64_t max_sort_tiles = (N + kSortThreads * kSortItemsSmall - 1) / (kSortThreads * kSortItemsSmall);
   L->scan_tiles = (N + kScanTile - 1) / kScanTile;
   L->max_long = N / p->thr + 1;
   // a long run of len lookups in a table of width D has ceil(len / chunk_len)
@@ -148,7 +152,7 @@ sgb_status make_layout(const sgb_plan_s* p, int64_t N, int32_t B, bool has_offse
   L->runtk = take(sizeof(uint32_t) * (size_t)L->max_items);
   L->sctk = take(sizeof(uint32_t) * (size_t)L->max_items);
   L->zero_end = align_up(o, 256);
-  L->counts = take(sizeof(uint32_t) * (size_t)L->sort_tiles * kRadixMax);
+  L->counts = take(sizeof(uint32_t) * (size_t)max_sort_tiles * kRadixMax);
   L->tile_runs = take(sizeof(uint32_t) * (size_t)L->scan_tiles);
   L->kvA = take(sizeof(uint64_t) * (size_t)N);
   L->kvB = take(sizeof(uint64_t) * (size_t)N);
@@ -414,6 +418,7 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
     sp.coef_out = cf_out;
     sp.N = N;
     sp.tiles = L.sort_tiles;
+    sp.items = sort_items_for(N);
     sp.shift = L.info_bits + L.pass_key_shift[ps];
     sp.bits = L.pass_bits[ps];
     sp.counts = at<uint32_t>(ws, L.counts);

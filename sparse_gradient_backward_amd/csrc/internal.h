@@ -18,8 +18,14 @@ constexpr int kColBlock = 256;        // columns one wave covers per pass (64 la
 constexpr int kMaxD = 8192;
 
 // Tuning knobs (compile-time; the defaults are the measured best).
-#ifndef SGB_SORT_ITEMS
-#define SGB_SORT_ITEMS 16
+#ifndef SGB_SORT_ITEMS_SMALL
+#define SGB_SORT_ITEMS_SMALL 8
+#endif
+#ifndef SGB_SORT_ITEMS_LARGE
+#define SGB_SORT_ITEMS_LARGE 12
+#endif
+#ifndef SGB_SORT_SMALL_N
+#define SGB_SORT_SMALL_N (1 << 20)
 #endif
 #ifndef SGB_SHORT_UNR
 #define SGB_SHORT_UNR 2
@@ -46,10 +52,15 @@ constexpr int kMaxD = 8192;
 #define SGB_SHORT8_WAVES 6
 #endif
 
-// sort pass tiling
+// sort pass tiling: items per thread of a tile, fewer for small batches
+// (more, shorter tiles fill the GPU and finish sooner) than for large ones
 constexpr int kSortThreads = 256;
-constexpr int kSortItems = SGB_SORT_ITEMS;
-constexpr int kSortTile = kSortThreads * kSortItems;
+constexpr int kSortItemsSmall = SGB_SORT_ITEMS_SMALL;
+constexpr int kSortItemsLarge = SGB_SORT_ITEMS_LARGE;
+static_assert(kSortItemsSmall <= kSortItemsLarge, "small batches take the smaller tiles");
+__host__ __device__ inline int sort_items_for(int64_t N) {
+  return N <= (int64_t)SGB_SORT_SMALL_N ? kSortItemsSmall : kSortItemsLarge;
+}
 
 // run-length encoding / run post-processing tiling
 constexpr int kScanThreads = 256;
@@ -191,7 +202,8 @@ struct SortParams {
   uint64_t* kv_out;
   float* coef_out;
   int64_t N;
-  int64_t tiles;            // tiles of kSortTile items
+  int64_t tiles;            // tiles of kSortThreads * items lookups
+  int32_t items;            // sort_items_for(N)
   int32_t shift;
   int32_t bits;
   uint32_t* counts;         // [radix][tiles]: tile digit counts, then their offsets

@@ -348,7 +348,9 @@ __device__ __forceinline__ uint32_t digit_of(uint64_t kv, int shift, uint32_t dm
 // wave cut same-address conflicts of skewed keys fourfold.
 constexpr int kCountCopies = (kSortThreads / 64) * 4;
 
+template <int kSortItems>
 __global__ __launch_bounds__(kSortThreads) void k_sort_count(SortParams p) {
+  constexpr int kSortTile = kSortThreads * kSortItems;
   __shared__ uint32_t s_h[kCountCopies][kRadixMax];
   const int tid = threadIdx.x, w = (tid >> 6) * 4 + (tid & 3);
   const uint32_t tile = blockIdx.x;
@@ -436,7 +438,9 @@ __device__ __forceinline__ uint64_t digit_peers(uint32_t d, int bits, bool valid
   return valid ? (~(((uint64_t)mhi << 32) | mlo) & live) : 0ull;
 }
 
+template <int kSortItems>
 __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(SortParams p) {
+  constexpr int kSortTile = kSortThreads * kSortItems;
   __shared__ uint64_t s_kv[kSortTile];  // keys, then coefficients, in tile order by digit
   __shared__ uint32_t s_wcnt[kSortThreads / 64][kRadixMax];
   __shared__ uint32_t s_local[kRadixMax];
@@ -530,22 +534,36 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(SortParams p) {
     }
   }
   __syncthreads();
-  for (int q = tid; q < tile_n; q += kSortThreads) {
-    const uint64_t v = s_kv[q];
-    const int64_t pos = (int64_t)s_gbase[digit_of(v, p.shift, dmask)] + q;
-    const bool okp = pos >= 0 && pos < p.N;
-    if (okp) p.kv_out[pos] = v;
-    set_status_wave(p.status, p.epoch, kStInternal, !okp);
-  }
-  if (!has_coef) return;
-  // coefficients the same way; the digit of each tile slot is read back from
-  // the keys before the buffer is reused
-  uint32_t slot_d[kSortItems];
+  // every slot's key and destination first (all LDS reads in flight), then
+  // the stores; slot q of the tile goes to s_gbase[its digit] + q
+  uint64_t v[kSortItems];
+  int64_t pos[kSortItems];
 #pragma unroll
   for (int k = 0; k < kSortItems; ++k) {
     const int q = k * kSortThreads + tid;
-    slot_d[k] = q < tile_n ? digit_of(s_kv[q], p.shift, dmask) : 0u;
+    v[k] = s_kv[q < tile_n ? q : 0];
   }
+#pragma unroll
+  for (int k = 0; k < kSortItems; ++k) {
+    const int q = k * kSortThreads + tid;
+    pos[k] = (int64_t)s_gbase[digit_of(v[k], p.shift, dmask)] + q;
+  }
+  bool bad = false;
+#pragma unroll
+  for (int k = 0; k < kSortItems; ++k) {
+    const int q = k * kSortThreads + tid;
+    const bool okp = pos[k] >= 0 && pos[k] < p.N;
+    if (q < tile_n) {
+      if (okp)
+        p.kv_out[pos[k]] = v[k];
+      else
+        bad = true;
+    }
+  }
+  set_status_wave(p.status, p.epoch, kStInternal, bad);
+  if (!has_coef) return;
+  // coefficients the same way, through the same buffer once every key has
+  // been read from it
   __syncthreads();
   float* s_cf = reinterpret_cast<float*>(s_kv);
 #pragma unroll
@@ -557,10 +575,7 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(SortParams p) {
 #pragma unroll
   for (int k = 0; k < kSortItems; ++k) {
     const int q = k * kSortThreads + tid;
-    if (q < tile_n) {
-      const int64_t pos = (int64_t)s_gbase[slot_d[k]] + q;
-      if (pos >= 0 && pos < p.N) p.coef_out[pos] = s_cf[q];
-    }
+    if (q < tile_n && pos[k] >= 0 && pos[k] < p.N) p.coef_out[pos[k]] = s_cf[q];
   }
 }
 
@@ -1702,18 +1717,25 @@ hipError_t launch_linearize(const LinParams& p, int grid, hipStream_t s) {
 
 hipError_t launch_sort_pass(const SortParams& p, hipStream_t s,
                             const std::function<void(int, int)>& mark) {
+  if (p.items != kSortItemsSmall && p.items != kSortItemsLarge) return hipErrorInvalidValue;
   const unsigned tiles = (unsigned)p.tiles;
   auto m = [&](int stage, int end) {
     if (mark) mark(stage, end);
   };
   m(SGB_STAGE_SORT_COUNT, 0);
-  hipLaunchKernelGGL(k_sort_count, dim3(tiles), dim3(kSortThreads), 0, s, p);
+  if (p.items == kSortItemsSmall)
+    hipLaunchKernelGGL(k_sort_count<kSortItemsSmall>, dim3(tiles), dim3(kSortThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(k_sort_count<kSortItemsLarge>, dim3(tiles), dim3(kSortThreads), 0, s, p);
   m(SGB_STAGE_SORT_COUNT, 1);
   m(SGB_STAGE_SORT_OFFSETS, 0);
   hipLaunchKernelGGL(k_sort_offsets, dim3(1u << p.bits), dim3(kScanThreads), 0, s, p);
   m(SGB_STAGE_SORT_OFFSETS, 1);
   m(SGB_STAGE_SORT_SCATTER, 0);
-  hipLaunchKernelGGL(k_sort_scatter, dim3(tiles), dim3(kSortThreads), 0, s, p);
+  if (p.items == kSortItemsSmall)
+    hipLaunchKernelGGL(k_sort_scatter<kSortItemsSmall>, dim3(tiles), dim3(kSortThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(k_sort_scatter<kSortItemsLarge>, dim3(tiles), dim3(kSortThreads), 0, s, p);
   m(SGB_STAGE_SORT_SCATTER, 1);
   return hipGetLastError();
 }
