@@ -334,7 +334,7 @@ def main():
 def plan_npasses(inp: synth.Inputs) -> int:
     rows = int(inp.hash_size_cumsum[-1])
     bits = int(rows - 1).bit_length()
-    return (bits + 8) // 9
+    return (bits + 9) // 10
 
 
 def pass_bits0(inp: synth.Inputs) -> int:

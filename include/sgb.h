@@ -84,7 +84,7 @@ typedef enum { SGB_DENSE_GRAD = 0, SGB_SGD = 1, SGB_ROWWISE_ADAGRAD = 2 } sgb_mo
  *  hash_size_cumsum     host, int64[T+1]: [0] = 0, strictly increasing;
  *                       table t owns linear ids [hsc[t], hsc[t+1]), so
  *                       E_t = hsc[t+1] - hsc[t] rows (FBGEMM host entry).
- *                       hsc[T] <= 2^36 (SGB_ERR_UNSUPPORTED above).
+ *                       hsc[T] <= 2^40 (SGB_ERR_UNSUPPORTED above).
  *  D_offsets            host, int32[T+1]: [0] = 0, D_t = D_offsets[t+1] -
  *                       D_offsets[t] with D_t % 4 == 0 and 4 <= D_t <= 8192;
  *                       D_offsets[t] is table t's first column in a bag row

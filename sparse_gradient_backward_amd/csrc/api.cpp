@@ -117,8 +117,8 @@ sgb_status make_layout(const sgb_plan_s* p, int64_t N, int32_t B, bool has_offse
   if (info_max >= (1ull << 32)) return SGB_ERR_UNSUPPORTED;
   L->info_bits = bitlen(info_max);
   if (L->info_bits + p->key_bits > 64) return SGB_ERR_UNSUPPORTED;
-  L->npasses = (p->key_bits + 8) / 9;
-  if (L->npasses > kMaxPasses) return SGB_ERR_UNSUPPORTED;  // linear ids >= 2^36
+  L->npasses = (p->key_bits + kMaxDigitBits - 1) / kMaxDigitBits;
+  if (L->npasses > kMaxPasses) return SGB_ERR_UNSUPPORTED;  // linear ids >= 2^40
   int at = 0;
   for (int i = 0; i < L->npasses; ++i) {
     L->pass_bits[i] = p->key_bits / L->npasses + (i < p->key_bits % L->npasses ? 1 : 0);

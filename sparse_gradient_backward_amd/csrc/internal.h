@@ -11,8 +11,9 @@
 namespace sgb {
 
 // ---------------------------------------------------------------- limits
-constexpr int kMaxPasses = 4;         // LSD passes of <= 9 bits: linear ids below 2^36
-constexpr int kRadixMax = 512;        // 9-bit digits
+constexpr int kMaxDigitBits = 10;     // LSD digits of <= 10 bits
+constexpr int kMaxPasses = 4;         // linear ids below 2^40
+constexpr int kRadixMax = 1 << kMaxDigitBits;
 constexpr int kMaxCb = 4;             // Adagrad rows held in registers: D <= 4 * 256
 constexpr int kColBlock = 256;        // columns one wave covers per pass (64 lanes x 4)
 constexpr int kMaxD = 8192;

@@ -6,7 +6,7 @@
 //                  and coefficient; range and offset checks; zeroes the
 //                  region the later kernels count in
 //   k_sort_count / k_sort_offsets / k_sort_scatter
-//                  one stable LSD radix pass (<= 9-bit digits) as
+//                  one stable LSD radix pass (<= 10-bit digits) as
 //                  reduce-then-scan: tile digit counts, their scan per digit,
 //                  ballot-ranked LDS-staged scatter
 //   k_rle_count / k_rle_scan / k_rle_write
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
 
 // ------------------------------------------------------------------ radix sort
 //
-// One stable LSD pass over `bits` (<= 9) digit bits at `shift` of the packed
+// One stable LSD pass over `bits` (<= 10) digit bits at `shift` of the packed
 // word, as reduce-then-scan in three kernels (no workgroup waits for another):
 //   k_sort_count    digit counts of every tile, stored digit-major
 //   k_sort_offsets  one workgroup per digit: exclusive scan of its counts over
@@ -344,15 +344,18 @@ __device__ __forceinline__ uint32_t digit_of(uint64_t kv, int shift, uint32_t dm
   return (uint32_t)(kv >> shift) & dmask;
 }
 
-// Lanes of a wave that share a sub-histogram in k_sort_count: 4 copies per
-// wave cut same-address conflicts of skewed keys fourfold.
-constexpr int kCountCopies = (kSortThreads / 64) * 4;
+// Lanes of a wave that share a sub-histogram in k_sort_count: 2 copies per
+// wave halve same-address conflicts of skewed keys.
+constexpr int kCopiesPerWave = 2;
+constexpr int kCountCopies = (kSortThreads / 64) * kCopiesPerWave;
+// digits of the radix per thread in the scatter's per-digit steps
+constexpr int kDigitsPerThread = kRadixMax / kSortThreads;
 
 template <int kSortItems>
 __global__ __launch_bounds__(kSortThreads) void k_sort_count(SortParams p) {
   constexpr int kSortTile = kSortThreads * kSortItems;
   __shared__ uint32_t s_h[kCountCopies][kRadixMax];
-  const int tid = threadIdx.x, w = (tid >> 6) * 4 + (tid & 3);
+  const int tid = threadIdx.x, w = (tid >> 6) * kCopiesPerWave + (tid & (kCopiesPerWave - 1));
   const uint32_t tile = blockIdx.x;
   const int radix = 1 << p.bits;
   const uint32_t dmask = (uint32_t)radix - 1u;
@@ -426,7 +429,7 @@ __global__ __launch_bounds__(kScanThreads) void k_sort_offsets(SortParams p) {
 __device__ __forceinline__ uint64_t digit_peers(uint32_t d, int bits, bool valid) {
   uint32_t mlo = 0, mhi = 0;  // lanes that differ from this one on some bit
 #pragma unroll
-  for (int b = 0; b < 9; ++b) {
+  for (int b = 0; b < kMaxDigitBits; ++b) {
     if (b < bits) {  // uniform
       const int32_t sx = -(int32_t)((d >> b) & 1u);  // 0 or all ones
       const uint64_t m = __ballot(sx != 0);
@@ -469,10 +472,11 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(SortParams p) {
   // global offsets of this tile's digit groups (independent of the ranking):
   // the digit's base (exclusive scan of the digit totals, done below) plus
   // the tile's offset within the digit
-  uint32_t goff[2], dtot[2];
+  // (thread tid owns digits kDigitsPerThread * tid + h, h < kDigitsPerThread)
+  uint32_t goff[kDigitsPerThread], dtot[kDigitsPerThread];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int d = 2 * tid + h;
+  for (int h = 0; h < kDigitsPerThread; ++h) {
+    const int d = kDigitsPerThread * tid + h;
     const int dc = d < radix ? d : 0;  // unconditional loads: none waits behind a branch
     goff[h] = p.counts[(size_t)dc * p.tiles + tile];
     dtot[h] = p.bases[dc];
@@ -492,10 +496,10 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(SortParams p) {
   __syncthreads();
 
   // per digit: exclusive offsets of the waves and the tile's count
-  uint32_t cnt[2];
+  uint32_t cnt[kDigitsPerThread];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int d = 2 * tid + h;
+  for (int h = 0; h < kDigitsPerThread; ++h) {
+    const int d = kDigitsPerThread * tid + h;
     uint32_t acc = 0;
     if (d < radix) {
 #pragma unroll
@@ -508,18 +512,23 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(SortParams p) {
     cnt[h] = acc;
   }
   {
-    uint32_t tot;
-    const uint32_t dbase = block_excl_scan<uint32_t>(dtot[0] + dtot[1], s_tmp, tot);
-    goff[0] += dbase;
-    goff[1] += dbase + dtot[0];
-    const uint32_t ex = block_excl_scan<uint32_t>(cnt[0] + cnt[1], s_tmp, tot);
-    if (2 * tid < radix) {
-      s_local[2 * tid] = ex;
-      s_gbase[2 * tid] = (int32_t)goff[0] - (int32_t)ex;
+    uint32_t tot, dsum = 0, csum = 0;
+#pragma unroll
+    for (int h = 0; h < kDigitsPerThread; ++h) {
+      dsum += dtot[h];
+      csum += cnt[h];
     }
-    if (2 * tid + 1 < radix) {
-      s_local[2 * tid + 1] = ex + cnt[0];
-      s_gbase[2 * tid + 1] = (int32_t)goff[1] - (int32_t)(ex + cnt[0]);
+    uint32_t g = block_excl_scan<uint32_t>(dsum, s_tmp, tot);
+    uint32_t ex = block_excl_scan<uint32_t>(csum, s_tmp, tot);
+#pragma unroll
+    for (int h = 0; h < kDigitsPerThread; ++h) {
+      const int d = kDigitsPerThread * tid + h;
+      if (d < radix) {
+        s_local[d] = ex;
+        s_gbase[d] = (int32_t)(goff[h] + g) - (int32_t)ex;
+      }
+      g += dtot[h];
+      ex += cnt[h];
     }
   }
   __syncthreads();
