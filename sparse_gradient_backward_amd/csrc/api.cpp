@@ -209,7 +209,7 @@ sgb_status sgb_plan_create(sgb_plan* out, int32_t T, const int64_t* hsc, const i
     if (D < 4 || D > kMaxD || D % 4 != 0) return SGB_ERR_INVALID_ARGUMENT;
     if (pooling == SGB_POOL_NONE && D != doff[1] - doff[0]) return SGB_ERR_INVALID_ARGUMENT;
   }
-  if (hsc[T] > (1ll << 36)) return SGB_ERR_UNSUPPORTED;  // linear ids must fit 4 radix passes
+  if (hsc[T] > (1ll << 40)) return SGB_ERR_UNSUPPORTED;  // linear ids must fit 4 radix passes
 
   sgb_plan_s* p = new (std::nothrow) sgb_plan_s();
   if (!p) return SGB_ERR_HIP;

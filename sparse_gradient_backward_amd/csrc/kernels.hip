@@ -738,85 +738,137 @@ __global__ __launch_bounds__(kScanThreads) void k_rle_write(RleParams p) {
 // combine tickets of the work items are cleared with the workspace's zeroed
 // region.)
 
-// Table of a run from the info of one of its lookups (bag t*B+b, or token
-// l*T+t without bags).
-__device__ __forceinline__ int table_of_info(const PostParams& p, uint32_t info) {
-  const int t = p.nobag ? (int)(info % (uint32_t)p.T) : (int)(info / (uint32_t)p.B);
-  return t < p.T ? t : p.T - 1;
+// Table metadata staged in LDS for up to kMetaT tables (read from global
+// memory beyond that).  The loads are issued with the tile's first loads, so
+// staging adds no memory round trip.
+constexpr int kMetaT = 512;
+constexpr int kMetaPer = (kMetaT + 1 + kScanThreads - 1) / kScanThreads;
+
+struct MetaLds {
+  int32_t doff[kMetaT + 1];
+  int64_t hsc[kMetaT + 1];
+  int64_t woff[kMetaT + 1];
+};
+
+// Table of linear id `id`: the last t with hsc[t] <= id (binary search over
+// hsc[0..T), in LDS or global memory).
+template <typename H>
+__device__ __forceinline__ int table_of_id(const H* hsc, int T, int64_t id) {
+  int lo = 0, hi = T;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (hsc[mid] <= id)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+// Work items of a long run of `len` lookups in a row of width D: nch
+// chunks x ncb column blocks.
+__device__ __forceinline__ uint32_t long_items(int len, int D, int base) {
+  const int cl = chunk_len(len, D, base);
+  return (uint32_t)(((len + cl - 1) / cl) * col_blocks(D));
 }
 
 __global__ __launch_bounds__(kScanThreads) void k_post(PostParams p) {
   __shared__ int32_t s_cum[kScanTile + 1];
-  __shared__ int32_t s_lq[kScanTile];   // tile positions of the tile's long runs
+  __shared__ uint32_t s_items[kScanTile];  // work items of each run (0: short)
+  __shared__ int16_t s_lq[kScanTile];   // tile positions of the tile's long runs
   __shared__ uint32_t s_lc[kScanTile];  // their first work items
   __shared__ uint64_t s_tmp[4];
   __shared__ uint32_t s_tile;
   __shared__ uint64_t s_excl;
+  __shared__ MetaLds s_meta;
   const int tid = threadIdx.x;
   const int U = *p.num_runs;
   // the grid is sized for N runs; workgroups past the last run leave before
   // taking a tile id, so the ids handed out are exactly the tiles of U runs
   if ((int64_t)blockIdx.x * kScanTile >= U) return;
+  // table metadata loads first, so that they are in flight with the tile id
+  const bool staged = p.T <= kMetaT;
+  int32_t md[kMetaPer];
+  int64_t mh[kMetaPer], mo[kMetaPer];
+  if (staged) {
+#pragma unroll
+    for (int i = 0; i < kMetaPer; ++i) {
+      const int j = min(i * kScanThreads + tid, p.T);
+      md[i] = p.doff[j];
+      mh[i] = p.hsc[j];
+      mo[i] = p.woff[j];
+    }
+  }
   if (tid == 0) s_tile = __hip_atomic_fetch_add(p.tile_ctr, 1u, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const uint32_t tile = s_tile;
   const int64_t base = (int64_t)tile * kScanTile;
   const int n = (int)min((int64_t)kScanTile, (int64_t)U - base);
-  const uint64_t imask = p.info_bits >= 64 ? ~0ull : ((1ull << p.info_bits) - 1ull);
-  {
-    // run starts base .. base+n (n+1 values) into LDS, all loads in flight
-    int32_t v[kScanItems];
-#pragma unroll
-    for (int k = 0; k < kScanItems; ++k) {
-      const int q = k * kScanThreads + tid;
-      v[k] = q < n ? p.cum[base + q] : 0;
-    }
-    const int32_t last = tid == 0 ? p.cum[base + n] : 0;
-#pragma unroll
-    for (int k = 0; k < kScanItems; ++k) {
-      const int q = k * kScanThreads + tid;
-      if (q < n) s_cum[q] = v[k];
-    }
-    if (tid == 0) s_cum[n] = last;
-  }
-  __syncthreads();
-  // this thread's kScanItems consecutive runs: lengths and long-run items.
-  // A long run's table comes from the info of its first lookup; all these
-  // loads are issued together, then the row widths.
-  uint32_t longmask = 0;
+  // run starts base .. base+n (n+1 values) and the run ids (used by long
+  // runs only; loaded with the starts, from indices clamped into the tile,
+  // so that no load waits for another)
+  int32_t v[kScanItems];
+  int64_t idv[kScanItems];
 #pragma unroll
   for (int k = 0; k < kScanItems; ++k) {
-    const int q = tid * kScanItems + k;
-    if (q < n && s_cum[q + 1] - s_cum[q] >= p.thr) longmask |= 1u << k;
+    const int q = k * kScanThreads + tid;
+    v[k] = p.cum[base + (q < n ? q : 0)];
+    idv[k] = p.unique_ids[base + (q < n ? q : 0)];
   }
-  // (the loads are unconditional, from index 0 where there is nothing to
-  // read, so that none of them waits behind a branch for the one before)
-  int Dq[kScanItems];
-  if (longmask) {
-    uint64_t raw[kScanItems];
+  const int32_t last = p.cum[base + n];
 #pragma unroll
-    for (int k = 0; k < kScanItems; ++k)
-      raw[k] = p.kv[((longmask >> k) & 1u) ? s_cum[tid * kScanItems + k] : 0];
-    int dlo[kScanItems], dhi[kScanItems];
+  for (int k = 0; k < kScanItems; ++k) {
+    const int q = k * kScanThreads + tid;
+    if (q < n) s_cum[q] = v[k];
+  }
+  if (tid == 0) s_cum[n] = last;
+  if (staged) {
 #pragma unroll
-    for (int k = 0; k < kScanItems; ++k) {
-      const int t = ((longmask >> k) & 1u) ? table_of_info(p, (uint32_t)(raw[k] & imask)) : 0;
-      dlo[k] = p.doff[t];
-      dhi[k] = p.doff[t + 1];
+    for (int i = 0; i < kMetaPer; ++i) {
+      const int j = i * kScanThreads + tid;
+      if (j <= p.T) {
+        s_meta.doff[j] = md[i];
+        s_meta.hsc[j] = mh[i];
+        s_meta.woff[j] = mo[i];
+      }
     }
-#pragma unroll
-    for (int k = 0; k < kScanItems; ++k) Dq[k] = ((longmask >> k) & 1u) ? dhi[k] - dlo[k] : 4;
   }
+  __syncthreads();
+  auto doff_at = [&](int t) { return staged ? s_meta.doff[t] : p.doff[t]; };
+  // work items of every run (0 for a short one), runs spread over the
+  // threads: the long runs are usually a few adjacent ones
+  uint32_t tmask = 0;  // runs of this thread (position k * kScanThreads + tid) that are long
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) {
+    const int q = k * kScanThreads + tid;
+    if (q < n) {
+      const bool lg = s_cum[q + 1] - s_cum[q] >= p.thr;
+      int32_t D = 0;
+      if (lg) {
+        tmask |= 1u << k;
+        const int t = staged ? table_of_id(s_meta.hsc, p.T, idv[k]) : table_of_id(p.hsc, p.T, idv[k]);
+        D = doff_at(t + 1) - doff_at(t);
+      }
+      s_items[q] = (uint32_t)D;  // (the width for now)
+    }
+  }
+#pragma unroll 1
+  for (uint32_t m = tmask; m; m &= m - 1u) {
+    const int q = __builtin_ctz(m) * kScanThreads + tid;
+    s_items[q] = long_items(s_cum[q + 1] - s_cum[q], (int)s_items[q], p.chunk_base);
+  }
+  __syncthreads();
+  // this thread's kScanItems consecutive runs: which are long, and their items
+  uint32_t longmask = 0;
   uint64_t sum = 0;
 #pragma unroll
   for (int k = 0; k < kScanItems; ++k) {
-    if (!((longmask >> k) & 1u)) continue;
-    // a long run becomes nch chunks x ncb column blocks of work items
     const int q = tid * kScanItems + k;
-    const int len = s_cum[q + 1] - s_cum[q];
-    const int cl = chunk_len(len, Dq[k], p.chunk_base);
-    sum += (1ull << 31) | (uint64_t)(((len + cl - 1) / cl) * col_blocks(Dq[k]));
+    if (q < n && s_cum[q + 1] - s_cum[q] >= p.thr) {
+      longmask |= 1u << k;
+      sum += (1ull << 31) | s_items[q];
+    }
   }
   uint64_t total;
   const uint64_t before = block_excl_scan<uint64_t>(sum, s_tmp, total);
@@ -832,36 +884,34 @@ __global__ __launch_bounds__(kScanThreads) void k_post(PostParams p) {
   }
   __syncthreads();
   // the tile's long runs in order: tile-local slot -> position and first work
-  // item (this thread's runs, cheap arithmetic), then their records written
-  // by all threads in parallel
+  // item (this thread's runs), then their records written by all threads in
+  // parallel
   {
     uint64_t at = s_excl + before;
     uint32_t li = (uint32_t)(before >> 31);
-#pragma unroll
-    for (int k = 0; k < kScanItems; ++k) {
-      if (!((longmask >> k) & 1u)) continue;
-      const int q = tid * kScanItems + k;
-      const int len = s_cum[q + 1] - s_cum[q];
-      const int cl = chunk_len(len, Dq[k], p.chunk_base);
-      s_lq[li] = q;
+#pragma unroll 1
+    for (uint32_t m = longmask; m; m &= m - 1u) {
+      const int q = tid * kScanItems + __builtin_ctz(m);
+      s_lq[li] = (int16_t)q;
       s_lc[li] = (uint32_t)(at & kField);
-      at += (1ull << 31) | (uint64_t)(((len + cl - 1) / cl) * col_blocks(Dq[k]));
+      at += (1ull << 31) | s_items[q];
       ++li;
     }
   }
   __syncthreads();
   const uint32_t g0 = (uint32_t)(s_excl >> 31);
   const uint32_t nl_tile = (uint32_t)(total >> 31);
+#pragma unroll 1
   for (uint32_t i = tid; i < nl_tile; i += kScanThreads) {
     const int q = s_lq[i];
     const int start = s_cum[q];
     const int len = s_cum[q + 1] - start;
-    const uint64_t w0 = p.kv[start];
     const int64_t id = p.unique_ids[base + q];
-    const int t = table_of_info(p, (uint32_t)(w0 & imask));
-    const int d0 = p.doff[t], D = p.doff[t + 1] - d0;
-    const int64_t h0 = p.hsc[t], E = p.hsc[t + 1] - h0;
-    const int64_t wo = p.woff[t];
+    const int t = staged ? table_of_id(s_meta.hsc, p.T, id) : table_of_id(p.hsc, p.T, id);
+    const int d0 = doff_at(t), D = doff_at(t + 1) - d0;
+    const int64_t h0 = staged ? s_meta.hsc[t] : p.hsc[t];
+    const int64_t E = (staged ? s_meta.hsc[t + 1] : p.hsc[t + 1]) - h0;
+    const int64_t wo = staged ? s_meta.woff[t] : p.woff[t];
     const int cl = chunk_len(len, D, p.chunk_base);
     int64_t row = id - h0;
     row = row < 0 ? 0 : (row < E ? row : E - 1);
