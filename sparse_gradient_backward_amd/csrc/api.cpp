@@ -170,6 +170,14 @@ sgb_status make_layout(const sgb_plan_s* p, int64_t N, int32_t B, bool has_offse
   return SGB_OK;
 }
 
+// Workgroups of the zero fill: one per SGB_FILL_CUS_PER_WG compute units.
+// The fill overlaps latency-bound kernels on other streams; a small grid
+// still saturates HBM with stores and leaves them the CU slots.
+int fill_grid(const sgb_plan_s* p) {
+  const int g = std::max(1, p->num_cus / std::max(1, (int)SGB_FILL_CUS_PER_WG));
+  return std::max(1, std::min(p->n_fill, g));
+}
+
 template <typename T>
 T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
@@ -341,8 +349,8 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
         launch_init(ws, sizeof(Header), stream) != hipSuccess)
       return SGB_ERR_HIP;
     if (fresh && p->n_fill > 0) {
-      FillParams f{out, p->d_fill, p->d_doff, p->d_woff};
-      if (launch_fill(f, p->n_fill, stream) != hipSuccess) return SGB_ERR_HIP;
+      FillParams f{out, p->d_fill, p->n_fill, p->d_doff, p->d_woff};
+      if (launch_fill(f, fill_grid(p), stream) != hipSuccess) return SGB_ERR_HIP;
     }
     return SGB_OK;
   }
@@ -372,9 +380,9 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
     if (hipEventRecord(p->ev[0], stream) != hipSuccess ||
         hipStreamWaitEvent(fill_s, p->ev[0], 0) != hipSuccess)
       return SGB_ERR_HIP;
-    FillParams f{out, p->d_fill, p->d_doff, p->d_woff};
+    FillParams f{out, p->d_fill, p->n_fill, p->d_doff, p->d_woff};
     mark_on(fill_s, SGB_STAGE_FILL, 0);
-    if (launch_fill(f, p->n_fill, fill_s) != hipSuccess) return SGB_ERR_HIP;
+    if (launch_fill(f, fill_grid(p), fill_s) != hipSuccess) return SGB_ERR_HIP;
     mark_on(fill_s, SGB_STAGE_FILL, 1);
     if (hipEventRecord(p->ev[1], fill_s) != hipSuccess) return SGB_ERR_HIP;
   }

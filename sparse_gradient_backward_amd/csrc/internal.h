@@ -52,6 +52,9 @@ constexpr int kMaxD = 8192;
 #ifndef SGB_SHORT8_WAVES
 #define SGB_SHORT8_WAVES 6
 #endif
+#ifndef SGB_FILL_CUS_PER_WG
+#define SGB_FILL_CUS_PER_WG 1
+#endif
 
 // sort pass tiling: items per thread of a tile, fewer for small batches
 // (more, shorter tiles fill the GPU and finish sooner) than for large ones
@@ -254,6 +257,7 @@ struct PostParams {
 struct FillParams {
   float* out;
   const FillBlock* blocks;
+  int32_t nblocks;
   const int32_t* doff;
   const int64_t* woff;
 };
@@ -305,7 +309,7 @@ hipError_t launch_sort_pass(const SortParams& p, hipStream_t s,
                             const std::function<void(int, int)>& mark);
 hipError_t launch_rle(const RleParams& p, hipStream_t s, const std::function<void(int, int)>& mark);
 hipError_t launch_post(const PostParams& p, int grid, hipStream_t s);
-hipError_t launch_fill(const FillParams& p, int nblocks, hipStream_t s);
+hipError_t launch_fill(const FillParams& p, int grid, hipStream_t s);
 hipError_t launch_reduce_long(const RedParams& p, bool bf16, int grid, hipStream_t s);
 hipError_t launch_reduce_short(const RedParams& p, bool bf16, int dmin, int dmax, hipStream_t s);
 int reduce_long_blocks_per_cu(bool bf16);

@@ -948,11 +948,15 @@ __global__ __launch_bounds__(kScanThreads) void k_post(PostParams p) {
 // rows after it.
 
 __global__ __launch_bounds__(256) void k_fill(FillParams p) {
-  const FillBlock fb = p.blocks[blockIdx.x];
-  const int D = p.doff[fb.t + 1] - p.doff[fb.t];
-  float4* out = reinterpret_cast<float4*>(p.out + p.woff[fb.t] + fb.row0 * (int64_t)D);
-  const uint32_t total = (uint32_t)fb.nrows * (uint32_t)(D >> 2);
-  for (uint32_t q = threadIdx.x; q < total; q += blockDim.x) out[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+  // few workgroups, each looping over fill blocks: the fill saturates HBM
+  // without holding the CU slots that the concurrent latency-bound kernels need
+  for (int b = blockIdx.x; b < p.nblocks; b += gridDim.x) {
+    const FillBlock fb = p.blocks[b];
+    const int D = p.doff[fb.t + 1] - p.doff[fb.t];
+    float4* out = reinterpret_cast<float4*>(p.out + p.woff[fb.t] + fb.row0 * (int64_t)D);
+    const uint32_t total = (uint32_t)fb.nrows * (uint32_t)(D >> 2);
+    for (uint32_t q = threadIdx.x; q < total; q += blockDim.x) out[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
 }
 
 // ------------------------------------------------------------------ reducers
@@ -1818,8 +1822,8 @@ hipError_t launch_post(const PostParams& p, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_fill(const FillParams& p, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL(k_fill, dim3(nblocks), dim3(256), 0, s, p);
+hipError_t launch_fill(const FillParams& p, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(k_fill, dim3(grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
