@@ -96,7 +96,12 @@ def stage_bytes(inp: synth.Inputs, spec: synth.Spec, U: int, run_D: np.ndarray,
         + (BT + 1) * 8 * (BT > 0) + U * 24 + update(run_D)
     if fresh:
         b_path += (int((Es * Ds).sum()) - touched_elems) * 4
-    return b, b_path
+    # compulsory bytes: grad_output, indices, offsets and weights read once,
+    # the rows updated once (a fresh dense gradient written whole)
+    b_comp = int(inp.grad_output.nbytes) + N * 8 + (BT + 1) * 8 * (BT > 0) \
+        + (N * 4 if spec.weighted else 0) \
+        + (int((Es * Ds).sum()) * 4 if fresh else update(run_D))
+    return b, b_path, b_comp
 
 
 def kernel_digest() -> str:
@@ -262,6 +267,20 @@ def main():
             continue
         d = [e[2 * k].elapsed_time(e[2 * k + 1]) for e in evs]
         stage_ms[name] = float(np.mean(d))
+    # cold caches: each call after a 512 MiB write (larger than the L2 caches
+    # and the 256 MB MALL), timed by events around the call alone
+    flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device=dev)
+    cold_ev = []
+    for _ in range(min(args.steps, 20)):
+        flush.fill_(1.0)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        step()
+        c1.record()
+        cold_ev.append((c0, c1))
+    torch.cuda.synchronize()
+    cold_ms = float(np.median([c0.elapsed_time(c1) for c0, c1 in cold_ev]))
+    del flush
     status = plan.device_status(ws)
 
     # run statistics for the byte model (from the library's own run view)
@@ -273,7 +292,7 @@ def main():
     nlong = view["num_long"]
     npasses = plan_npasses(inp)
     radix0 = 1 << pass_bits0(inp)
-    sb, b_path = stage_bytes(inp, spec, U, run_D, lens, thr, npasses, radix0)
+    sb, b_path, b_comp = stage_bytes(inp, spec, U, run_D, lens, thr, npasses, radix0)
     # dominant kernel: the largest time per step (a sort kernel runs once per pass)
     per_step = {k: v * (npasses if k in SORT_KERNELS else 1)
                 for k, v in stage_ms.items() if k != "sort"}
@@ -317,6 +336,10 @@ def main():
         "achieved_GBps_path": gbps_path,
         "hbm_pct_path": 100.0 * gbps_path / HBM_PEAK_GBPS,
         "bytes_alg_path": int(b_path),
+        "bytes_compulsory": int(b_comp),
+        "achieved_GBps_compulsory": b_comp / (ms_per_step * 1e-3) / 1e9,
+        "cold": {"ms_per_call_median": cold_ms, "value": inp.N / (cold_ms * 1e-3),
+                 "calls": len(cold_ev), "flush_bytes": 512 << 20},
         "stage_ms": stage_ms,
         "stage_bytes": {k: int(v) for k, v in sb.items()},
         "ms_per_step_instrumented": ms_timed,
