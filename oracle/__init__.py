@@ -1,4 +1,5 @@
-"""CPU oracle for the pooled embedding-bag backward (test infrastructure).
+"""CPU oracle for the pooled embedding-bag backward, and the pooled forward it
+differentiates (test infrastructure).
 
 Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The GPU library never does, and this
@@ -64,8 +65,9 @@ def _lib(path: Optional[str] = None):
         lib.orc_runs.argtypes = [i64, vp, vp, i64] + [vp] * 9
         lib.orc_row_grads.argtypes = [P, i64, vp, i32, vp, vp]
         lib.orc_update_rows.argtypes = [i32, i32, i64, vp, i32, vp, f32, f32, vp, vp]
+        lib.orc_forward.argtypes = [P, vp, vp]
         for f in (lib.orc_validate, lib.orc_linearize, lib.orc_runs,
-                  lib.orc_row_grads, lib.orc_update_rows):
+                  lib.orc_row_grads, lib.orc_update_rows, lib.orc_forward):
             f.restype = ctypes.c_int
         _libs[path] = lib
     return _libs[path]
@@ -79,8 +81,9 @@ def _ptr(a: Optional[np.ndarray]):
 class Problem:
     """Host-side description of one backward call (numpy arrays).
 
-    grad_output is float32, or uint16 holding bf16 bit patterns.
-    offsets may be None only for nobag ('none' pooling) with T == 1.
+    grad_output is float32, or uint16 holding bf16 bit patterns (None for
+    the forward).  offsets may be None only for nobag ('none' pooling) with
+    T == 1.
     """
     T: int
     B: int
@@ -101,14 +104,14 @@ class Problem:
             np.ascontiguousarray(self.indices, dtype=np.int64),
             None if self.per_sample_weights is None
             else np.ascontiguousarray(self.per_sample_weights, dtype=np.float32),
-            np.ascontiguousarray(self.grad_output),
+            None if self.grad_output is None else np.ascontiguousarray(self.grad_output),
         ]
         hsc, doff, off, idx, psw, g = self._keep
-        if g.dtype not in (np.float32, np.uint16):
+        if g is not None and g.dtype not in (np.float32, np.uint16):
             raise TypeError("grad_output must be float32 or uint16 (bf16 bits)")
         return _Problem(int(self.T), int(self.B), int(idx.shape[0]), _ptr(hsc), _ptr(doff),
                         _ptr(off), _ptr(idx), _ptr(psw), POOL[self.pooling], _ptr(g),
-                        1 if g.dtype == np.uint16 else 0)
+                        1 if g is not None and g.dtype == np.uint16 else 0)
 
 
 def _check(st: int, what: str):
@@ -186,3 +189,18 @@ def update_rows(mode: str, G: np.ndarray, D: np.ndarray, rows0: Optional[np.ndar
     _check(_lib(lib).orc_update_rows(MODE[mode], 1 if accumulate else 0, n, _ptr(D), ldg, _ptr(G),
                                      float(lr), float(eps), _ptr(rows), _ptr(mom)), "update_rows")
     return rows, mom
+
+
+def forward(p: Problem, weights: np.ndarray, lib: Optional[str] = None) -> np.ndarray:
+    """Pooled forward: [B][D_offsets[T]] (bag) or [N][D] (nobag) float32, from
+    the flat float32 weights (table t at sum_{t'<t} E_t' * D_t', row-major)."""
+    c = p._c()
+    W = np.ascontiguousarray(weights, np.float32)
+    doff = np.asarray(p.D_offsets, np.int64)
+    if p.pooling == "none":
+        out = np.zeros((c.N, int(doff[1] - doff[0])), np.float32)
+    else:
+        out = np.zeros((int(p.B) if p.offsets is not None else 1, int(doff[-1])), np.float32)
+    _check(_lib(lib).orc_forward(ctypes.byref(c), _ptr(W), _ptr(out)), "forward")
+    return out
+

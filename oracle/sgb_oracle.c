@@ -130,7 +130,15 @@ static int32_t orc_num_bags(const orc_problem* p) {
  *  - hash_size_cumsum starts at 0 and strictly increases (no empty and no
  *    shared tables).
  */
+static int orc_validate_lookups(const orc_problem* p);
+
 int orc_validate(const orc_problem* p) {
+  if (p->N > 0 && p->grad_output == NULL) return ORC_INVALID_ARGUMENT;
+  return orc_validate_lookups(p);
+}
+
+/* The rules above except the gradient buffer (the forward reads weights). */
+static int orc_validate_lookups(const orc_problem* p) {
   if (p->T <= 0 || p->N < 0 || p->hash_size_cumsum == NULL ||
       p->D_offsets == NULL)
     return ORC_INVALID_ARGUMENT;
@@ -149,8 +157,7 @@ int orc_validate(const orc_problem* p) {
     if (D < 4 || D > 8192 || D % 4 != 0) return ORC_INVALID_ARGUMENT;
     if (nobag && D != orc_table_D(p, 0)) return ORC_INVALID_ARGUMENT;
   }
-  if (p->N > 0 && (p->indices == NULL || p->grad_output == NULL))
-    return ORC_INVALID_ARGUMENT;
+  if (p->N > 0 && p->indices == NULL) return ORC_INVALID_ARGUMENT;
   if (p->offsets != NULL) {
     int64_t nb = (int64_t)p->B * p->T;
     if (p->offsets[0] != 0 || p->offsets[nb] != p->N) return ORC_BAD_OFFSETS;
@@ -389,3 +396,59 @@ int orc_update_rows(int32_t mode, int32_t accumulate, int64_t nrows,
   }
   return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Pooled forward                                                             */
+/* ------------------------------------------------------------------------ */
+
+/* The pooled lookup that the backward above differentiates:
+ *   out[b][D_offsets[t] + d] = sum over lookups i of bag (t, b) of
+ *                              coef_i * W_t[indices[i]][d]        (bag mode)
+ *   out[i][d]                = W_t[indices[i]][d]                 (nobag)
+ * for d < D_t, with coef_i = per_sample_weights[i] (or 1) times 1/L for a
+ * mean bag of L lookups; an empty bag gives a zero row.  The FBTT cache
+ * forward sums the weight rows of a segment's lookups into the segment's
+ * output row [P2 `cache_forward_kernel`]; the mean scale and the per-sample
+ * weight are the factors the backward applies [P1 `grad_mean_kernel`,
+ * weighted kernels], so forward and backward are adjoint.
+ * W is one flat fp32 array, table t from woff[t] = sum_{t'<t} E_t' * D_t',
+ * row-major.  out is [B][D_offsets[T]] (bag) or [N][D] (nobag).  Sums in
+ * double, rounded once to fp32. */
+int orc_forward(const orc_problem* p, const float* W, float* out) {
+  int st = orc_validate_lookups(p);
+  if (st != ORC_OK) return st;
+  if (W == NULL || out == NULL) return ORC_INVALID_ARGUMENT;
+  const int nobag = p->pooling == ORC_POOL_NONE;
+  const int64_t width = nobag ? (int64_t)orc_table_D(p, 0) : (int64_t)p->D_offsets[p->T];
+  const int64_t rows = nobag ? p->N : (int64_t)orc_num_bags(p);
+  memset(out, 0, sizeof(float) * (size_t)(rows * width));
+  double* acc = (double*)malloc(sizeof(double) * 8192);
+  if (acc == NULL) return ORC_INVALID_ARGUMENT;
+  int64_t woff = 0;
+  for (int32_t t = 0; t < p->T; ++t) {
+    const int D = orc_table_D(p, t);
+    const int64_t E = p->hash_size_cumsum[t + 1] - p->hash_size_cumsum[t];
+    for (int32_t b = 0; b < orc_num_bags(p); ++b) {
+      int64_t s, e;
+      orc_bag_range(p, t, b, &s, &e);
+      const int64_t L = e - s;
+      const double scale = (p->pooling == ORC_POOL_MEAN && L > 0) ? 1.0 / (double)L : 1.0;
+      for (int d = 0; d < D; ++d) acc[d] = 0.0;
+      for (int64_t i = s; i < e; ++i) {
+        const float* wr = W + woff + p->indices[i] * (int64_t)D;
+        if (nobag) {
+          for (int d = 0; d < D; ++d) out[i * width + d] = wr[d];
+          continue;
+        }
+        const double c = scale * (p->per_sample_weights ? (double)p->per_sample_weights[i] : 1.0);
+        for (int d = 0; d < D; ++d) acc[d] += c * (double)wr[d];
+      }
+      if (!nobag)
+        for (int d = 0; d < D; ++d) out[(int64_t)b * width + p->D_offsets[t] + d] = (float)acc[d];
+    }
+    woff += E * (int64_t)D;
+  }
+  free(acc);
+  return ORC_OK;
+}
+
