@@ -236,6 +236,43 @@ typedef struct {
 sgb_status sgb_runs_view_get(sgb_plan plan, const void* workspace, int64_t num_indices,
                              int32_t B, sgb_runs_view* out);
 
+/* Lookups of a forward call; every pointer is a device pointer, read only.
+ * The fields mean what they mean in sgb_batch. */
+typedef struct {
+  const int64_t* indices;           /* [num_indices], row within its table  */
+  int64_t num_indices;              /* N                                    */
+  const int64_t* offsets;           /* [B*T+1] table-major, or NULL only for
+                                       nobag with T == 1                    */
+  int32_t B;                        /* bags per table (0 if offsets NULL)   */
+  const float* per_sample_weights;  /* [num_indices] or NULL (bag only)     */
+} sgb_lookups;
+
+/*
+ * sgb_forward -- enqueue the pooled forward on `stream`: the operation that
+ * sgb_backward() differentiates.  With coef_i = per_sample_weight_i (or 1)
+ * times 1/L under MEAN pooling (FBGEMM `grad_mean_kernel`), for bag (t, b)
+ * and d < D_t:
+ *     output[b][D_offsets[t] + d] = sum over lookups i of the bag of
+ *                                   coef_i * W_t[indices[i]][d]
+ * (an empty bag gives zeros), and for nobag output[i][d] = W_t[indices[i]][d]
+ * (FBTT `cache_forward_kernel` sums the weight rows of a segment's lookups
+ * into its output row).
+ *  weights  device fp32, the layout of sgb_update.weights (table t row i at
+ *           woff[t] + i * D_t), 16-byte aligned; read only.
+ *  output   device fp32, caller-owned, 16-byte aligned: [B][D_offsets[T]]
+ *           (bag) or [num_indices][D] (nobag); every element is written.
+ *  Sums are accumulated in fp64 and rounded once.  Allocates nothing.
+ *  workspace: device, 256-byte aligned, at least 128 bytes (any size that
+ *  sgb_workspace_bytes() returns); only its status header is used, so
+ *  sgb_device_status() reports this call's device-detected errors
+ *  (SGB_ERR_INDEX_OUT_OF_RANGE, SGB_ERR_BAD_OFFSETS; output unspecified
+ *  then).  Host-detected errors (SGB_ERR_INVALID_ARGUMENT for NULL or
+ *  misaligned buffers and inconsistent sizes, SGB_ERR_UNSUPPORTED for
+ *  weighted nobag) return before anything is enqueued.
+ */
+sgb_status sgb_forward(sgb_plan plan, const sgb_lookups* lookups, const float* weights,
+                       float* output, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static string naming a status code. */
 const char* sgb_status_string(int32_t status);
 

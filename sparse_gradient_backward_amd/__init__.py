@@ -59,6 +59,12 @@ class _Batch(ctypes.Structure):
                 ("per_sample_weights", ctypes.c_void_p)]
 
 
+class _Lookups(ctypes.Structure):
+    _fields_ = [("indices", ctypes.c_void_p), ("num_indices", ctypes.c_int64),
+                ("offsets", ctypes.c_void_p), ("B", ctypes.c_int32),
+                ("per_sample_weights", ctypes.c_void_p)]
+
+
 class _Update(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("weights", ctypes.c_void_p),
                 ("momentum", ctypes.c_void_p), ("grad", ctypes.c_void_p),
@@ -82,11 +88,12 @@ _lib.sgb_backward.argtypes = [_vp, ctypes.POINTER(_Batch), ctypes.POINTER(_Updat
 _lib.sgb_backward_timed.argtypes = [_vp, ctypes.POINTER(_Batch), ctypes.POINTER(_Update), _vp,
                                     ctypes.c_size_t, _vp, ctypes.POINTER(_vp)]
 _lib.sgb_device_status.argtypes = [_vp, _vp, _vp, ctypes.POINTER(_i32)]
+_lib.sgb_forward.argtypes = [_vp, ctypes.POINTER(_Lookups), _vp, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.sgb_runs_view_get.argtypes = [_vp, _vp, _i64, _i32, ctypes.POINTER(_RunsView)]
 _lib.sgb_status_string.argtypes = [_i32]
 _lib.sgb_status_string.restype = ctypes.c_char_p
 for _f in ("sgb_plan_create", "sgb_workspace_bytes", "sgb_backward", "sgb_backward_timed",
-           "sgb_device_status", "sgb_runs_view_get"):
+           "sgb_device_status", "sgb_runs_view_get", "sgb_forward"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -193,6 +200,24 @@ def sgb_backward(plan: int, grad_output, indices, offsets, B: int, per_sample_we
                                        ws_bytes, _stream(stream), arr), "sgb_backward_timed")
 
 
+def sgb_forward(plan: int, indices, offsets, B: int, per_sample_weights, weights, output,
+                workspace, stream=None) -> None:
+    """Enqueue the pooled forward (sgb_forward): output [B][sum D] (bag) or
+    [N][D] (nobag) float32, from the flat float32 weights.  Device tensors;
+    indices/offsets int64, per_sample_weights float32 or None."""
+    import torch
+    for name, t, dt in (("indices", indices, torch.int64), ("offsets", offsets, torch.int64),
+                        ("per_sample_weights", per_sample_weights, torch.float32),
+                        ("weights", weights, torch.float32), ("output", output, torch.float32)):
+        if t is not None and (t.dtype != dt or not t.is_contiguous()):
+            raise SgbError(SGB_ERR_INVALID_ARGUMENT, f"sgb_forward: {name} must be contiguous {dt}")
+    lk = _Lookups(_ptr(indices), int(indices.numel()), _ptr(offsets), int(B),
+                  _ptr(per_sample_weights))
+    ws_bytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
+    _check(_lib.sgb_forward(plan, ctypes.byref(lk), _ptr(weights), _ptr(output), _ptr(workspace),
+                            ws_bytes, _stream(stream)), "sgb_forward")
+
+
 def sgb_device_status(plan: int, workspace, stream=None) -> int:
     out = _i32()
     _check(_lib.sgb_device_status(plan, _ptr(workspace), _stream(stream), ctypes.byref(out)),
@@ -244,6 +269,9 @@ class Plan:
 
     def backward(self, *args, **kw):
         return sgb_backward(self.handle, *args, **kw)
+
+    def forward(self, *args, **kw):
+        return sgb_forward(self.handle, *args, **kw)
 
     def device_status(self, workspace, stream=None) -> str:
         return sgb_status_string(sgb_device_status(self.handle, workspace, stream))

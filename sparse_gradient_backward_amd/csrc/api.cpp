@@ -540,6 +540,49 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   return SGB_OK;
 }
 
+sgb_status sgb_forward(sgb_plan p, const sgb_lookups* lk, const float* weights, float* output,
+                       void* ws, size_t ws_bytes, void* stream_) {
+  if (!p || !lk || !output) return SGB_ERR_INVALID_ARGUMENT;
+  const int64_t N = lk->num_indices;
+  const bool nobag = p->pooling == SGB_POOL_NONE;
+  if (N < 0 || N >= (1ll << 30)) return SGB_ERR_INVALID_ARGUMENT;
+  if (nobag && lk->per_sample_weights) return SGB_ERR_UNSUPPORTED;
+  if (!lk->offsets && !(nobag && p->T == 1)) return SGB_ERR_INVALID_ARGUMENT;
+  if (lk->offsets && (lk->B <= 0 || (int64_t)lk->B * p->T >= (1ll << 31)))
+    return SGB_ERR_INVALID_ARGUMENT;
+  if (N > 0 && (!lk->indices || !weights)) return SGB_ERR_INVALID_ARGUMENT;
+  if (!aligned(output, 16) || (weights && !aligned(weights, 16))) return SGB_ERR_INVALID_ARGUMENT;
+  if (!ws || !aligned(ws, 256) || ws_bytes < sizeof(Header)) return SGB_ERR_INVALID_ARGUMENT;
+  DeviceGuard guard(p->device);
+  if (!guard.ok) return SGB_ERR_HIP;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  Header* hdr = at<Header>(ws, 0);
+  FwdParams f{};
+  f.indices = lk->indices;
+  f.offsets = lk->offsets;
+  f.psw = lk->per_sample_weights;
+  f.weights = weights;
+  f.out = output;
+  f.hsc = p->d_hsc;
+  f.doff = p->d_doff;
+  f.woff = p->d_woff;
+  f.N = N;
+  f.B = lk->offsets ? lk->B : 0;
+  f.T = p->T;
+  f.pooling = p->pooling;
+  f.lpl = lanes_per_row(p->Dmin);
+  f.segs_per_table = lk->offsets ? (int64_t)lk->B : N;
+  f.waves_per_table = (f.segs_per_table + (64 / f.lpl) - 1) / (64 / f.lpl);
+  f.out_stride = nobag ? (int64_t)p->doff[1] : (int64_t)p->doff[p->T];
+  f.status = &hdr->status;
+  f.epoch = next_epoch();
+  f.header = hdr;
+  if (f.waves_per_table == 0) {  // no segments: nothing to write; report this call clean
+    return launch_init(ws, sizeof(Header), stream) == hipSuccess ? SGB_OK : SGB_ERR_HIP;
+  }
+  return launch_forward(f, stream) == hipSuccess ? SGB_OK : SGB_ERR_HIP;
+}
+
 sgb_status sgb_device_status(sgb_plan p, const void* ws, void* stream_, int32_t* out) {
   if (!p || !ws || !out) return SGB_ERR_INVALID_ARGUMENT;
   DeviceGuard guard(p->device);

@@ -299,6 +299,28 @@ struct RedParams {
   float eps;
 };
 
+struct FwdParams {
+  const int64_t* indices;
+  const int64_t* offsets;   // NULL: nobag, one table, every lookup its own segment
+  const float* psw;
+  const float* weights;
+  float* out;
+  const int64_t* hsc;       // [T+1]
+  const int32_t* doff;      // [T+1]
+  const int64_t* woff;      // [T+1]
+  int64_t N;
+  int32_t B;
+  int32_t T;
+  int32_t pooling;
+  int32_t lpl;              // lanes per segment: lanes_per_row(narrowest D)
+  int64_t segs_per_table;   // B, or N without offsets
+  int64_t waves_per_table;  // ceil(segs_per_table / (64 / lpl))
+  int64_t out_stride;       // elements per output row
+  uint32_t* status;
+  uint32_t epoch;
+  Header* header;
+};
+
 // ---------------------------------------------------------------- launchers (kernels.hip)
 
 hipError_t launch_init(void* header_and_hist, size_t bytes, hipStream_t s);
@@ -313,5 +335,6 @@ hipError_t launch_fill(const FillParams& p, int grid, hipStream_t s);
 hipError_t launch_reduce_long(const RedParams& p, bool bf16, int grid, hipStream_t s);
 hipError_t launch_reduce_short(const RedParams& p, bool bf16, int dmin, int dmax, hipStream_t s);
 int reduce_long_blocks_per_cu(bool bf16);
+hipError_t launch_forward(const FwdParams& p, hipStream_t s);
 
 }  // namespace sgb

@@ -1760,6 +1760,115 @@ __global__ __launch_bounds__(256) void k_reduce_short16(RedParams p) {
   reduce_short<16, BF16>(p);
 }
 
+
+// ------------------------------------------------------------------ k_forward
+//
+// Pooled forward, the operation the backward differentiates: the output row
+// of bag (t, b) is the sum over its lookups of coef * weight row (FBTT
+// `cache_forward_kernel` sums the weight rows of a segment's lookups into
+// the segment's output row); coef is the backward's, the per-sample weight
+// times 1/L for a mean bag.  Nobag: a lookup's output row is its weight row.
+// A lane group of lpl lanes (4 columns per lane; one width for all tables,
+// that of the narrowest) takes one bag and a wave 64/lpl bags of one table;
+// wider rows take several column blocks.  A slice of lpl lookups has its
+// indices and coefficients loaded one per lane, then broadcast by shuffles
+// while UNR weight rows per lane are in flight.  Sums in fp64, rounded once.
+constexpr int kFwdUnr = 4;
+
+__global__ __launch_bounds__(256) void k_forward(FwdParams p) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) p.header->epoch = p.epoch;
+  const int lane = lane_id();
+  const int lpl = p.lpl, lg = __builtin_ctz((unsigned)lpl), G = 64 >> lg;
+  const int g = lane >> lg, lig = lane & (lpl - 1), gb = g << lg;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t tw = wave / p.waves_per_table;
+  if (tw >= p.T) return;  // (wave-uniform)
+  const int t = (int)tw;
+  const int64_t seg = (wave - tw * p.waves_per_table) * G + g;
+  const bool live = seg < p.segs_per_table;
+  const int D = p.doff[t + 1] - p.doff[t];
+  const int64_t E = p.hsc[t + 1] - p.hsc[t];
+  const float* W = p.weights + p.woff[t];
+  const bool nobag = p.pooling == kPoolNone;
+  // the segment's lookups [s, e): a bag, or one lookup without offsets
+  int64_t s = 0, e = 0;
+  bool bad_off = false;
+  if (live) {
+    if (p.offsets) {
+      const int64_t bag = (int64_t)t * p.B + seg;
+      s = p.offsets[bag];
+      e = p.offsets[bag + 1];
+      bad_off = s < 0 || e < s || e > p.N || (bag == 0 && s != 0) ||
+                (bag == (int64_t)p.T * p.B - 1 && e != p.N);
+      if (bad_off) {
+        s = min(max(s, (int64_t)0), p.N);
+        e = s;
+      }
+    } else {
+      s = seg;
+      e = seg + 1;
+    }
+  }
+  set_status_wave(p.status, p.epoch, kStOffsets, bad_off);
+  const float scale = (p.pooling == kPoolMean && e > s) ? 1.0f / (float)(e - s) : 1.0f;
+  // slices of the wave's longest bag (a uniform trip count: shuffles below
+  // need the whole wave)
+  int64_t maxlen = e - s;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) maxlen = max(maxlen, __shfl_xor(maxlen, off, 64));
+  const int64_t nslices = (maxlen + lpl - 1) / lpl;
+  bool bad_idx = false;
+#pragma unroll 1
+  for (int c0 = 0; c0 < D; c0 += 4 * lpl) {
+    const int col = c0 + 4 * lig;
+    const bool cok = live && col < D;
+    d4 acc = d4_zero();
+#pragma unroll 1
+    for (int64_t sl = 0; sl < nslices; ++sl) {
+      const int64_t j0 = s + sl * lpl;
+      const int64_t j = j0 + lig;
+      const bool jok = live && j < e;
+      // (indices are loaded only when this group has a lookup left; the
+      // index is always inside [s, e) then)
+      int64_t x = 0;
+      float cf = 0.f;
+      if (jok) {
+        x = p.indices[j];
+        cf = (p.psw ? p.psw[j] : 1.0f) * scale;
+        if (x < 0 || x >= E) {
+          bad_idx = true;
+          x = x < 0 ? 0 : E - 1;
+        }
+      }
+      const int64_t cnt = live ? min((int64_t)lpl, e - j0) : 0;
+#pragma unroll 1
+      for (int jj = 0; jj < lpl; jj += kFwdUnr) {
+        if (!__ballot(jj < cnt)) break;
+        float4 v[kFwdUnr];
+        float co[kFwdUnr];
+#pragma unroll
+        for (int u = 0; u < kFwdUnr; ++u) {
+          const int src = gb + min(jj + u, lpl - 1);
+          const int64_t ro = __shfl(x, src, 64);
+          co[u] = __shfl(cf, src, 64);
+          const bool ok = cok && jj + u < cnt;
+          v[u] = ok ? ld4(W + ro * D + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        if (nobag) {
+#pragma unroll
+          for (int u = 0; u < kFwdUnr; ++u)
+            if (cok && jj + u < cnt) st4(p.out + (j0 + jj + u) * p.out_stride + col, v[u]);
+        } else {
+#pragma unroll
+          for (int u = 0; u < kFwdUnr; ++u) d4_fma(acc, co[u], v[u]);
+        }
+      }
+    }
+    if (!nobag && cok)
+      st4(p.out + seg * p.out_stride + p.doff[t] + col, round4(acc.x, acc.y, acc.z, acc.w));
+  }
+  set_status_wave(p.status, p.epoch, kStIndex, bad_idx);
+}
 }  // namespace
 
 // ------------------------------------------------------------------ launchers
@@ -1865,6 +1974,16 @@ hipError_t launch_reduce_short(const RedParams& p, bool bf16, int dmin, int dmax
     else
       hipLaunchKernelGGL(k_reduce_short16<false>, grid, dim3(256), 0, s, q);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_forward(const FwdParams& p, hipStream_t s) {
+  const int G = 64 / p.lpl;
+  (void)G;
+  const int64_t waves = p.waves_per_table * p.T;
+  const int64_t blocks = (waves + 3) / 4;
+  if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_forward, dim3((unsigned)blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -18,7 +18,7 @@ def test_every_declared_function_is_exported():
     declared = sgb.header_functions()
     assert set(declared) == {"sgb_plan_create", "sgb_plan_destroy", "sgb_workspace_bytes",
                              "sgb_backward", "sgb_backward_timed", "sgb_device_status",
-                             "sgb_runs_view_get", "sgb_status_string"}
+                             "sgb_runs_view_get", "sgb_status_string", "sgb_forward"}
     lib = ctypes.CDLL(sgb.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
@@ -46,6 +46,9 @@ int main(void) {
   F(sgb_runs_view, sorted_packed); F(sgb_runs_view, info_bits); F(sgb_runs_view, unique_ids);
   F(sgb_runs_view, run_lengths); F(sgb_runs_view, cumulative); F(sgb_runs_view, num_runs);
   F(sgb_runs_view, long_run_ids); F(sgb_runs_view, num_long_run_ids);
+  printf("sgb_lookups %zu\n", sizeof(sgb_lookups));
+  F(sgb_lookups, indices); F(sgb_lookups, num_indices); F(sgb_lookups, offsets);
+  F(sgb_lookups, B); F(sgb_lookups, per_sample_weights);
   return 0;
 }
 """
@@ -57,7 +60,7 @@ int main(void) {
         lines = subprocess.check_output([exe], text=True).split("\n")
     c_layout = dict(l.rsplit(" ", 1) for l in lines if l)
     for name, cls in (("sgb_batch", sgb._Batch), ("sgb_update", sgb._Update),
-                      ("sgb_runs_view", sgb._RunsView)):
+                      ("sgb_runs_view", sgb._RunsView), ("sgb_lookups", sgb._Lookups)):
         assert int(c_layout[name]) == ctypes.sizeof(cls), name
         for field, _ in cls._fields_:
             assert int(c_layout[f"{name}.{field}"]) == getattr(cls, field).offset, (name, field)
