@@ -282,6 +282,7 @@ def main():
     cold_ms = float(np.median([c0.elapsed_time(c1) for c0, c1 in cold_ev]))
     del flush
     status = plan.device_status(ws)
+    fwd = forward_measure(plan, inp, spec, indices, offsets, psw, out, ws, args.steps)
 
     # run statistics for the byte model (from the library's own run view)
     U = view["num_runs"]
@@ -347,11 +348,55 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(spec.name, kernel_names[dom]), "bytes_per_launch": int(per_launch_bytes),
                      "launch_ms": per_launch_ms},
+        "forward": fwd,
         "cpu_baseline": cpu,
         "device_status": status,
         "kernel_src": kernel_digest(),
     }
     print(json.dumps(res), flush=True)
+
+
+def forward_measure(plan, inp, spec, indices, offsets, psw, table, ws, steps) -> dict:
+    """The pooled forward (sgb_forward) on the same lookups, reading `table`
+    (the workload's weights, or for a dense-gradient workload its gradient
+    buffer, which has the weights' shape), timed by HIP events around
+    `steps` back-to-back calls.  Algorithmic bytes per call: each lookup's
+    weight row, index (and weight), the offsets, and the output written."""
+    B = inp.B if inp.offsets is not None else 0
+    doff = inp.D_offsets
+    Ds = np.diff(doff).astype(np.int64)
+    if spec.pooling == "none":
+        shape = (inp.N, int(Ds[0]))
+    else:
+        shape = (inp.B, int(doff[-1]))
+    res = torch.empty(shape, dtype=torch.float32, device=table.device)
+    if inp.offsets is not None:
+        per_table = np.diff(inp.offsets[::inp.B]) if inp.B > 0 else np.zeros(inp.T, np.int64)
+        gather = int((per_table * Ds).sum()) * 4
+    else:
+        gather = inp.N * int(Ds[0]) * 4
+    bytes_alg = gather + inp.N * (8 + (4 if inp.per_sample_weights is not None else 0)) \
+        + ((B * inp.T + 1) * 8 if inp.offsets is not None else 0) + int(np.prod(shape)) * 4
+
+    def call():
+        plan.forward(indices, offsets, B, psw, table, res, ws)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    status = plan.device_status(ws)
+    gbps = bytes_alg / (ms * 1e-3) / 1e9
+    return {"ms_per_call": ms, "lookups_per_s": inp.N / (ms * 1e-3), "bytes_alg": int(bytes_alg),
+            "device_status": status,
+            "roofline": {"bound": "hbm", "kernel": "k_forward", "achieved": gbps,
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS}}
 
 
 def plan_npasses(inp: synth.Inputs) -> int:

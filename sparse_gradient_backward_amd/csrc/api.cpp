@@ -571,6 +571,7 @@ sgb_status sgb_forward(sgb_plan p, const sgb_lookups* lk, const float* weights, 
   f.T = p->T;
   f.pooling = p->pooling;
   f.lpl = lanes_per_row(p->Dmin);
+  f.Dmax = p->Dmax;
   f.segs_per_table = lk->offsets ? (int64_t)lk->B : N;
   f.waves_per_table = (f.segs_per_table + (64 / f.lpl) - 1) / (64 / f.lpl);
   f.out_stride = nobag ? (int64_t)p->doff[1] : (int64_t)p->doff[p->T];

@@ -313,6 +313,7 @@ struct FwdParams {
   int32_t T;
   int32_t pooling;
   int32_t lpl;              // lanes per segment: lanes_per_row(narrowest D)
+  int32_t Dmax;             // widest D
   int64_t segs_per_table;   // B, or N without offsets
   int64_t waves_per_table;  // ceil(segs_per_table / (64 / lpl))
   int64_t out_stride;       // elements per output row

@@ -1773,8 +1773,10 @@ __global__ __launch_bounds__(256) void k_reduce_short16(RedParams p) {
 // wider rows take several column blocks.  A slice of lpl lookups has its
 // indices and coefficients loaded one per lane, then broadcast by shuffles
 // while UNR weight rows per lane are in flight.  Sums in fp64, rounded once.
-constexpr int kFwdUnr = 4;
-
+// UNR lookups x NB column blocks of weight rows are in flight per lane: the
+// launcher takes NB = 1 when every row fits one block, more for wider rows
+// (and for nobag, whose segments are single lookups, UNR = 1).
+template <int UNR, int NB, bool NOBAG>
 __global__ __launch_bounds__(256) void k_forward(FwdParams p) {
   if (blockIdx.x == 0 && threadIdx.x == 0) p.header->epoch = p.epoch;
   const int lane = lane_id();
@@ -1789,7 +1791,6 @@ __global__ __launch_bounds__(256) void k_forward(FwdParams p) {
   const int D = p.doff[t + 1] - p.doff[t];
   const int64_t E = p.hsc[t + 1] - p.hsc[t];
   const float* W = p.weights + p.woff[t];
-  const bool nobag = p.pooling == kPoolNone;
   // the segment's lookups [s, e): a bag, or one lookup without offsets
   int64_t s = 0, e = 0;
   bool bad_off = false;
@@ -1817,22 +1818,25 @@ __global__ __launch_bounds__(256) void k_forward(FwdParams p) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) maxlen = max(maxlen, __shfl_xor(maxlen, off, 64));
   const int64_t nslices = (maxlen + lpl - 1) / lpl;
+  const int span = 4 * lpl;  // columns of one block
   bool bad_idx = false;
 #pragma unroll 1
-  for (int c0 = 0; c0 < D; c0 += 4 * lpl) {
-    const int col = c0 + 4 * lig;
-    const bool cok = live && col < D;
-    d4 acc = d4_zero();
+  for (int c0 = 0; c0 < D; c0 += span * NB) {
+    bool cok[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) cok[k] = live && c0 + k * span + 4 * lig < D;
+    d4 acc[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) acc[k] = d4_zero();
 #pragma unroll 1
     for (int64_t sl = 0; sl < nslices; ++sl) {
       const int64_t j0 = s + sl * lpl;
       const int64_t j = j0 + lig;
-      const bool jok = live && j < e;
-      // (indices are loaded only when this group has a lookup left; the
-      // index is always inside [s, e) then)
+      // this lane's lookup of the slice (loaded only when the group has one
+      // left; the index is inside [s, e) then)
       int64_t x = 0;
       float cf = 0.f;
-      if (jok) {
+      if (live && j < e) {
         x = p.indices[j];
         cf = (p.psw ? p.psw[j] : 1.0f) * scale;
         if (x < 0 || x >= E) {
@@ -1842,33 +1846,47 @@ __global__ __launch_bounds__(256) void k_forward(FwdParams p) {
       }
       const int64_t cnt = live ? min((int64_t)lpl, e - j0) : 0;
 #pragma unroll 1
-      for (int jj = 0; jj < lpl; jj += kFwdUnr) {
+      for (int jj = 0; jj < lpl; jj += UNR) {
         if (!__ballot(jj < cnt)) break;
-        float4 v[kFwdUnr];
-        float co[kFwdUnr];
+        float4 v[UNR][NB];
+        float co[UNR];
 #pragma unroll
-        for (int u = 0; u < kFwdUnr; ++u) {
+        for (int u = 0; u < UNR; ++u) {
           const int src = gb + min(jj + u, lpl - 1);
           const int64_t ro = __shfl(x, src, 64);
           co[u] = __shfl(cf, src, 64);
-          const bool ok = cok && jj + u < cnt;
-          v[u] = ok ? ld4(W + ro * D + col) : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        if (nobag) {
 #pragma unroll
-          for (int u = 0; u < kFwdUnr; ++u)
-            if (cok && jj + u < cnt) st4(p.out + (j0 + jj + u) * p.out_stride + col, v[u]);
+          for (int k = 0; k < NB; ++k) {
+            const bool ok = cok[k] && jj + u < cnt;
+            v[u][k] = ok ? ld4(W + ro * D + c0 + k * span + 4 * lig) : make_float4(0.f, 0.f, 0.f, 0.f);
+          }
+        }
+        if constexpr (NOBAG) {
+#pragma unroll
+          for (int u = 0; u < UNR; ++u)
+#pragma unroll
+            for (int k = 0; k < NB; ++k)
+              if (cok[k] && jj + u < cnt)
+                st4(p.out + (j0 + jj + u) * p.out_stride + c0 + k * span + 4 * lig, v[u][k]);
         } else {
 #pragma unroll
-          for (int u = 0; u < kFwdUnr; ++u) d4_fma(acc, co[u], v[u]);
+          for (int u = 0; u < UNR; ++u)
+#pragma unroll
+            for (int k = 0; k < NB; ++k) d4_fma(acc[k], co[u], v[u][k]);
         }
       }
     }
-    if (!nobag && cok)
-      st4(p.out + seg * p.out_stride + p.doff[t] + col, round4(acc.x, acc.y, acc.z, acc.w));
+    if constexpr (!NOBAG) {
+#pragma unroll
+      for (int k = 0; k < NB; ++k)
+        if (cok[k])
+          st4(p.out + seg * p.out_stride + p.doff[t] + c0 + k * span + 4 * lig,
+              round4(acc[k].x, acc[k].y, acc[k].z, acc[k].w));
+    }
   }
   set_status_wave(p.status, p.epoch, kStIndex, bad_idx);
 }
+
 }  // namespace
 
 // ------------------------------------------------------------------ launchers
@@ -1978,12 +1996,16 @@ hipError_t launch_reduce_short(const RedParams& p, bool bf16, int dmin, int dmax
 }
 
 hipError_t launch_forward(const FwdParams& p, hipStream_t s) {
-  const int G = 64 / p.lpl;
-  (void)G;
   const int64_t waves = p.waves_per_table * p.T;
   const int64_t blocks = (waves + 3) / 4;
   if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_forward, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  const int span = 4 * p.lpl;
+  if (p.pooling == kPoolNone)
+    hipLaunchKernelGGL((k_forward<1, 8, true>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+  else if (p.Dmax <= span)
+    hipLaunchKernelGGL((k_forward<4, 1, false>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((k_forward<2, 4, false>), dim3((unsigned)blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
