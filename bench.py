@@ -104,6 +104,17 @@ def stage_bytes(inp: synth.Inputs, spec: synth.Spec, U: int, run_D: np.ndarray,
     return b, b_path, b_comp
 
 
+def short_kernels(dims) -> str:
+    """Kernels of the short-run stage: rows up to 512 columns go to the window
+    reducer, wider rows to the wide-row reducer."""
+    names = []
+    if int(np.min(dims)) <= 512:
+        names.append("k_reduce_short8")
+    if int(np.max(dims)) > 512:
+        names.append("k_reduce_wide")
+    return "+".join(names)
+
+
 def kernel_digest() -> str:
     """Short hash of the kernel and launch sources: counter figures taken on
     other sources no longer describe these kernels."""
@@ -314,8 +325,7 @@ def main():
                     "sort_count": "k_sort_count", "sort_offsets": "k_sort_offsets",
                     "sort_scatter": "k_sort_scatter", "rle_count": "k_rle_count",
                     "rle_scan": "k_rle_scan", "rle_write": "k_rle_write", "runs": "k_post",
-                    "reduce_short": "k_reduce_short8" if int(np.diff(inp.D_offsets).max()) <= 512
-                    else "k_reduce_short16"}
+                    "reduce_short": short_kernels(np.diff(inp.D_offsets))}
     res = {
         "metric": METRIC,
         "value": inp.N / (ms_per_step * 1e-3),

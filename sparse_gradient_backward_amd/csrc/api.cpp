@@ -44,6 +44,7 @@ struct sgb_plan_s {
   int32_t n_fill = 0;
   int num_cus = 1;
   int red_grid[2] = {1, 1};  // persistent grid of the long-run reducer (f32, bf16)
+  int wide_grid[4] = {1, 1, 1, 1};  // persistent grid of the wide-row reducer (see launch_reduce_short)
   // side streams (default priority): [0] clears a fresh dense gradient while
   // the ids are sorted, [1] reduces the short runs while the long-run list is
   // built and the long runs are reduced; the events fork and join them.  The
@@ -259,6 +260,8 @@ sgb_status sgb_plan_create(sgb_plan* out, int32_t T, const int64_t* hsc, const i
     p->num_cus = cus;
   p->red_grid[0] = p->num_cus * reduce_long_blocks_per_cu(false);
   p->red_grid[1] = p->num_cus * reduce_long_blocks_per_cu(true);
+  reduce_wide_blocks_per_cu(p->wide_grid);
+  for (int i = 0; i < 4; ++i) p->wide_grid[i] *= p->num_cus;
 
   bool ok = hipStreamCreateWithFlags(&p->aux[0], hipStreamNonBlocking) == hipSuccess &&
             hipStreamCreateWithFlags(&p->aux[1], hipStreamNonBlocking) == hipSuccess;
@@ -524,7 +527,7 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
       (fresh && hipStreamWaitEvent(short_s, p->ev[1], 0) != hipSuccess))
     return SGB_ERR_HIP;
   mark_on(short_s, SGB_STAGE_REDUCE_SHORT, 0);
-  if (launch_reduce_short(q, bf16, p->Dmin, p->Dmax, short_s) != hipSuccess) return SGB_ERR_HIP;
+  if (launch_reduce_short(q, bf16, p->Dmin, p->Dmax, p->wide_grid, short_s) != hipSuccess) return SGB_ERR_HIP;
   mark_on(short_s, SGB_STAGE_REDUCE_SHORT, 1);
   if (hipEventRecord(p->ev[3], short_s) != hipSuccess) return SGB_ERR_HIP;
   mark(SGB_STAGE_RUNS, 0);

@@ -49,6 +49,21 @@ constexpr int kMaxD = 8192;
 #ifndef SGB_SHORT_SUB16
 #define SGB_SHORT_SUB16 2
 #endif
+#ifndef SGB_WIDE_CPL
+#define SGB_WIDE_CPL 8
+#endif
+#ifndef SGB_WIDE_UNR
+#define SGB_WIDE_UNR 4
+#endif
+#ifndef SGB_WIDE_UNR16
+#define SGB_WIDE_UNR16 4
+#endif
+#ifndef SGB_WIDE_NT
+#define SGB_WIDE_NT 0
+#endif
+#ifndef SGB_WIDE_WAVES
+#define SGB_WIDE_WAVES 8
+#endif
 #ifndef SGB_SHORT8_WAVES
 #define SGB_SHORT8_WAVES 6
 #endif
@@ -86,6 +101,14 @@ constexpr int kShortSub8 = SGB_SHORT_SUB8;
 constexpr int kShortSub16 = SGB_SHORT_SUB16;
 static_assert(kShortSub8 >= 0 && kShortSub8 <= 6 && kShortSub16 >= 0 && kShortSub16 <= 6,
               "a window of 64 positions splits into at most 64 parts");
+
+// short runs of rows wider than 512 columns: columns per lane (4, 8 or 16) of
+// a dense / SGD item and lookups gathered per round; row-wise Adagrad items
+// always take 16 columns per lane (a whole row of up to 1024)
+constexpr int kWideCpl = SGB_WIDE_CPL;
+constexpr int kWideUnr = SGB_WIDE_UNR;
+constexpr int kWideUnr16 = SGB_WIDE_UNR16;
+static_assert(kWideCpl == 4 || kWideCpl == 8 || kWideCpl == 16, "pieces of 4 columns, 256 apart");
 
 // long runs: chunk sizing and two-level combine
 constexpr int kMaxChunks = SGB_MAX_CHUNKS;  // a run is cut into at most this many chunks
@@ -293,6 +316,7 @@ struct RedParams {
   int32_t thr;
   int32_t chunk_base;       // chunk_base_for(N)
   int32_t sub_log;          // short-run reducer: log2 of the waves per window
+  int32_t wide_ncb;         // wide-row reducer: column blocks per run
   int32_t mode;
   int32_t accumulate;
   float lr;
@@ -334,7 +358,10 @@ hipError_t launch_rle(const RleParams& p, hipStream_t s, const std::function<voi
 hipError_t launch_post(const PostParams& p, int grid, hipStream_t s);
 hipError_t launch_fill(const FillParams& p, int grid, hipStream_t s);
 hipError_t launch_reduce_long(const RedParams& p, bool bf16, int grid, hipStream_t s);
-hipError_t launch_reduce_short(const RedParams& p, bool bf16, int dmin, int dmax, hipStream_t s);
+// wide_grid: blocks of the wide-row reducer, {fp32 Adagrad, fp32 other, bf16 Adagrad, bf16 other}
+hipError_t launch_reduce_short(const RedParams& p, bool bf16, int dmin, int dmax,
+                               const int* wide_grid, hipStream_t s);
+void reduce_wide_blocks_per_cu(int out[4]);
 int reduce_long_blocks_per_cu(bool bf16);
 hipError_t launch_forward(const FwdParams& p, hipStream_t s);
 

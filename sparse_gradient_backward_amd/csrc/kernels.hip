@@ -1530,8 +1530,8 @@ __global__ __launch_bounds__(256) void k_reduce_long(RedParams p) {
   }
 }
 
-// Short runs, CPL columns per lane (8, or 16 for rows wider than 512): lane
-// groups of lpl lanes, lpl = the power of two covering D / CPL, at most one
+// Short runs, CPL columns per lane (8; rows wider than 512 go to
+// k_reduce_wide): lane groups of lpl lanes, lpl = the power of two covering D / CPL, at most one
 // wave.  The group width is a runtime value so that one code path (and one
 // register budget) serves every row width.
 template <int CPL>
@@ -1691,8 +1691,7 @@ __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, in
 // length up (run index at the head, run starts).  A wave serves the short
 // runs (length < thr) that start in its 64 >> sub_log positions, in batches
 // of at most 64/lpl runs of one table.  Rows wider than 512 columns are
-// served by the CPL = 16 instance; the CPL = 8 instance skips them, and the
-// reverse.
+// skipped here (k_reduce_wide serves them).
 template <int CPL, bool BF16>
 __device__ __forceinline__ void reduce_short(const RedParams& p) {
   const int lane = lane_id();
@@ -1741,8 +1740,7 @@ __device__ __forceinline__ void reduce_short(const RedParams& p) {
       rest ^= low;
     }
     pending &= ~sel;
-    const bool mine = CPL == 16 ? D > 512 : D <= 512;  // rows of the other instance
-    if (!mine || cb * 64 * CPL >= D) continue;
+    if (D > 512 || cb * 64 * CPL >= D) continue;  // wider rows: k_reduce_wide
     short_batch<CPL, BF16>(p, sel, lpl, base, len, key, rowi, cf, t0, D, cb);
   }
 }
@@ -1755,9 +1753,183 @@ void k_reduce_short8(RedParams p) {
   reduce_short<8, BF16>(p);
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(256) void k_reduce_short16(RedParams p) {
-  reduce_short<16, BF16>(p);
+
+// ------------------------------------------------------------ k_reduce_wide
+//
+// Short runs of rows wider than 512 columns.  The row update of such a run
+// (read and write of the old row, 8 bytes per column) outweighs the gather of
+// its few lookups, and a wave that served every run of a 64-position window
+// in turn paid two memory round trips per run.  Here the work is dealt by
+// run: items (run, column block of 64*CPL columns) go round-robin to
+// persistent waves, the whole wave serves one item (each lane CPL columns,
+// pieces of 4 columns 256 apart), and before a wave gathers its current item
+// it has issued the loads of the next item's first sorted words and of the
+// run starts of the item after that, so an item costs about one round trip.
+// Lookups are gathered UNR at a time from wave-uniform row offsets (readlane),
+// accumulated with fp64 FMAs.  Runs of length >= thr belong to the long-run
+// reducer, rows of 512 columns or fewer to k_reduce_short8.
+
+// Start and end of the run of an item (end = next run's start; zero length
+// past the last item).
+struct WideRun {
+  int s, e;
+};
+
+__device__ __forceinline__ WideRun wide_run(const RedParams& p, int64_t item, int64_t items,
+                                            int ncb) {
+  WideRun m{0, 0};
+  if (item < items) {
+    const int r = (int)(item / ncb);
+    m.s = uni32(p.cum[r]);
+    m.e = uni32(p.cum[r + 1]);
+  }
+  return m;
+}
+
+// This lane's sorted word and coefficient of lookup s + j0 + lane of a run.
+struct WideLane {
+  uint64_t kv;
+  float cf;
+};
+
+__device__ __forceinline__ WideLane wide_lane(const RedParams& p, const WideRun& m, int j0) {
+  const int j = m.s + j0 + lane_id();
+  WideLane d{0ull, 1.0f};
+  if (j < m.e) {
+    d.kv = p.kv[j];
+    if (p.coef) d.cf = p.coef[j];
+  }
+  return d;
+}
+
+__device__ __forceinline__ int rl32(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+__device__ __forceinline__ float rlf(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ __forceinline__ uint64_t rl64(uint64_t x, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int32_t)(uint32_t)x, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int32_t)(x >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ void wide_st4(float* q, float4 v) {
+#if SGB_WIDE_NT
+  __builtin_nontemporal_store(v.x, q);
+  __builtin_nontemporal_store(v.y, q + 1);
+  __builtin_nontemporal_store(v.z, q + 2);
+  __builtin_nontemporal_store(v.w, q + 3);
+#else
+  st4(q, v);
+#endif
+}
+
+template <int CPL, int UNR, bool BF16>
+__device__ __forceinline__ void wide_item(const RedParams& p, const WideRun& m, const WideLane& d0,
+                                          int cb) {
+  constexpr int NP = CPL / 4;
+  const int len = m.e - m.s;
+  if (len <= 0 || len >= p.thr) return;
+  const uint64_t imask = info_mask(p);
+  const uint64_t kv0 = rl64(d0.kv, 0);
+  const int t = uni32(table_of(p, (uint32_t)(kv0 & imask)));
+  const int D = uni32(p.doff[t + 1] - p.doff[t]);
+  if (D <= 512 || cb * 64 * CPL >= D) return;
+  const int col = cb * 64 * CPL + 4 * lane_id();
+  int vmask = 0;
+#pragma unroll
+  for (int i = 0; i < NP; ++i)
+    if (col + 256 * i < D) vmask |= 1 << i;
+  const RowDst dst = row_dest(p, t, D, (int64_t)(kv0 >> p.info_bits));
+  const bool needs_old = p.mode != kModeDense || p.accumulate;
+  float4 old[NP];
+  d4 acc[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    old[i] = (needs_old && ((vmask >> i) & 1)) ? ld4(dst.out + col + 256 * i)
+                                              : make_float4(0.f, 0.f, 0.f, 0.f);
+    acc[i] = d4_zero();
+  }
+  const float m0 = p.mode == kModeAdagrad ? *dst.mom : 0.f;
+  const int64_t gcol = (p.nobag ? 0 : p.doff[t]) + col;
+  for (int j0 = 0; j0 < len; j0 += 64) {
+    const WideLane dl = j0 == 0 ? d0 : wide_lane(p, m, j0);
+    const int rowi = grad_row_of(p, (uint32_t)(dl.kv & imask), t);
+    const int cnt = min(64, len - j0);
+    for (int u0 = 0; u0 < cnt; u0 += UNR) {
+      Raw4<BF16> r[UNR][NP];
+      float c[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const bool ok = u0 + u < cnt;
+        const int src = ok ? u0 + u : cnt - 1;
+        const int64_t e = (int64_t)rl32(rowi, src) * p.row_stride + gcol;
+        c[u] = ok ? rlf(dl.cf, src) : 0.f;
+#pragma unroll
+        for (int i = 0; i < NP; ++i)
+          r[u][i] = (ok && ((vmask >> i) & 1)) ? load_raw4<BF16>(p.grad, e + 256 * i)
+                                               : zero_raw4<BF16>();
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u)
+#pragma unroll
+        for (int i = 0; i < NP; ++i) d4_fma(acc[i], c[u], widen4<BF16>(r[u][i]));
+    }
+  }
+  if (p.mode == kModeAdagrad) {
+    // one item holds the whole row (row-wise Adagrad rows are at most 1024 wide)
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < NP; ++i)
+      if ((vmask >> i) & 1) ss += d4_sumsq(acc[i]);
+    ss = group_sum(ss, 64);
+    const double mm = (double)m0 + ss / (double)D;
+    const double mult = (double)p.lr / (sqrt(mm) + (double)p.eps);
+#pragma unroll
+    for (int i = 0; i < NP; ++i)
+      if ((vmask >> i) & 1)
+        st4(dst.out + col + 256 * i,
+            round4((double)old[i].x - acc[i].x * mult, (double)old[i].y - acc[i].y * mult,
+                   (double)old[i].z - acc[i].z * mult, (double)old[i].w - acc[i].w * mult));
+    if (lane_id() == 0) *dst.mom = (float)mm;
+    return;
+  }
+  const double lr = (double)p.lr;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    if (!((vmask >> i) & 1)) continue;
+    const d4& a = acc[i];
+    float4 w;
+    if (p.mode == kModeSgd)
+      w = round4((double)old[i].x - lr * a.x, (double)old[i].y - lr * a.y,
+                 (double)old[i].z - lr * a.z, (double)old[i].w - lr * a.w);
+    else if (p.accumulate)
+      w = round4((double)old[i].x + a.x, (double)old[i].y + a.y, (double)old[i].z + a.z,
+                 (double)old[i].w + a.w);
+    else
+      w = round4(a.x, a.y, a.z, a.w);
+    wide_st4(dst.out + col + 256 * i, w);
+  }
+}
+
+template <int CPL, int UNR, bool BF16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, SGB_WIDE_WAVES)))
+void k_reduce_wide(RedParams p) {
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int ncb = p.wide_ncb;
+  const int64_t items = (int64_t)(*p.num_runs) * ncb;
+  if (item >= items) return;
+  WideRun m0 = wide_run(p, item, items, ncb);
+  WideLane d0 = wide_lane(p, m0, 0);
+  WideRun m1 = wide_run(p, item + nw, items, ncb);
+  for (; item < items; item += nw) {
+    const WideRun m2 = wide_run(p, item + 2 * nw, items, ncb);
+    const WideLane d1 = wide_lane(p, m1, 0);
+    wide_item<CPL, UNR, BF16>(p, m0, d0, (int)(item % ncb));
+    m0 = m1;
+    d0 = d1;
+    m1 = m2;
+  }
 }
 
 
@@ -1962,7 +2134,45 @@ hipError_t launch_reduce_long(const RedParams& p, bool bf16, int grid, hipStream
   return hipGetLastError();
 }
 
-hipError_t launch_reduce_short(const RedParams& p, bool bf16, int dmin, int dmax, hipStream_t s) {
+// Row-wise Adagrad needs a whole row in one item: 16 columns per lane (rows
+// up to 1024); dense and SGD rows take SGB_WIDE_CPL columns per lane.
+template <bool BF16>
+void launch_wide_t(RedParams q, bool adagrad, int dmax, const int* grid, hipStream_t s) {
+  if (adagrad) {
+    q.wide_ncb = (dmax + 1023) / 1024;
+    hipLaunchKernelGGL((k_reduce_wide<16, kWideUnr16, BF16>), dim3(grid[0]), dim3(256), 0, s, q);
+  } else {
+    q.wide_ncb = (dmax + 64 * kWideCpl - 1) / (64 * kWideCpl);
+    hipLaunchKernelGGL((k_reduce_wide<kWideCpl, kWideUnr, BF16>), dim3(grid[1]), dim3(256), 0, s,
+                       q);
+  }
+}
+
+void launch_reduce_wide(const RedParams& p, bool bf16, int dmax, const int* grid, hipStream_t s) {
+  const bool adagrad = p.mode == kModeAdagrad;
+  if (bf16)
+    launch_wide_t<true>(p, adagrad, dmax, grid + 2, s);
+  else
+    launch_wide_t<false>(p, adagrad, dmax, grid, s);
+}
+
+// Blocks per CU of the wide-row reducer instances, in the order
+// {fp32 Adagrad, fp32 other, bf16 Adagrad, bf16 other}.
+void reduce_wide_blocks_per_cu(int out[4]) {
+  const void* k[4] = {reinterpret_cast<const void*>(k_reduce_wide<16, kWideUnr16, false>),
+                      reinterpret_cast<const void*>(k_reduce_wide<kWideCpl, kWideUnr, false>),
+                      reinterpret_cast<const void*>(k_reduce_wide<16, kWideUnr16, true>),
+                      reinterpret_cast<const void*>(k_reduce_wide<kWideCpl, kWideUnr, true>)};
+  for (int i = 0; i < 4; ++i) {
+    int n = 0;
+    out[i] = (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k[i], 256, 0) == hipSuccess && n > 0)
+                 ? n
+                 : 2;
+  }
+}
+
+hipError_t launch_reduce_short(const RedParams& p, bool bf16, int dmin, int dmax,
+                               const int* wide_grid, hipStream_t s) {
   const int64_t windows = (p.N + kShortSpan - 1) / kShortSpan;
   // waves per window, reduced when the grid would pass 2^32 threads
   auto sub_for = [&](int want) {
@@ -1980,18 +2190,7 @@ hipError_t launch_reduce_short(const RedParams& p, bool bf16, int dmin, int dmax
     else
       hipLaunchKernelGGL(k_reduce_short8<false>, grid, dim3(256), 0, s, q);
   }
-  if (dmax > 512) {
-    // wider rows: 16 columns per lane in 1024-column blocks (dense / SGD may
-    // have several; Adagrad rows are at most 1024 wide)
-    RedParams q = p;
-    q.sub_log = sub_for(kShortSub16);
-    const dim3 grid((unsigned)(((windows << q.sub_log) + 3) / 4),
-                    (unsigned)((dmax + 1023) / 1024));
-    if (bf16)
-      hipLaunchKernelGGL(k_reduce_short16<true>, grid, dim3(256), 0, s, q);
-    else
-      hipLaunchKernelGGL(k_reduce_short16<false>, grid, dim3(256), 0, s, q);
-  }
+  if (dmax > 512) launch_reduce_wide(p, bf16, dmax, wide_grid, s);
   return hipGetLastError();
 }
 

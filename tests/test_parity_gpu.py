@@ -112,6 +112,18 @@ def test_wide_rows_adagrad_and_sgd(sgb):
         check_case(sgb, synth.generate(s), mode, 32, lr=0.02, eps=1e-6)
 
 
+def test_wide_and_narrow_tables_all_short(sgb):
+    """Rows wider than 512 columns beside narrow ones; a threshold above every
+    run length sends even the hottest runs (hundreds of lookups, several
+    64-lookup slices) through the short-run reducers."""
+    s = synth.Spec("widemix", 3, (700, 500, 300), (64, 2048, 772), 257, ("uniform", 0, 30),
+                   ("zipf", 1.2), "sum", True, "bf16", "dense", seed=91)
+    inp = synth.generate(s)
+    check_case(sgb, inp, "dense", 2**31 - 1, accumulate=False)
+    check_case(sgb, inp, "sgd", 2**31 - 1, lr=0.05)
+    check_case(sgb, inp, "dense", 40, accumulate=True)
+
+
 # ------------------------------------------------------------------ edge cases
 
 def test_empty_input(sgb):
