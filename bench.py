@@ -294,6 +294,8 @@ def main():
     del flush
     status = plan.device_status(ws)
     fwd = forward_measure(plan, inp, spec, indices, offsets, psw, out, ws, args.steps)
+    atomic = atomic_measure(inp, spec, grad_output, indices, offsets, psw, out,
+                            min(args.steps, 20), ms_per_step)
 
     # run statistics for the byte model (from the library's own run view)
     U = view["num_runs"]
@@ -359,6 +361,7 @@ def main():
                      "traffic": measured_traffic(spec.name, kernel_names[dom]), "bytes_per_launch": int(per_launch_bytes),
                      "launch_ms": per_launch_ms},
         "forward": fwd,
+        "atomic_scatter": atomic,
         "cpu_baseline": cpu,
         "device_status": status,
         "kernel_src": kernel_digest(),
@@ -407,6 +410,45 @@ def forward_measure(plan, inp, spec, indices, offsets, psw, table, ws, steps) ->
             "device_status": status,
             "roofline": {"bound": "hbm", "kernel": "k_forward", "achieved": gbps,
                          "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS}}
+
+
+def atomic_measure(inp, spec, grad_output, indices, offsets, psw, out, calls, ms_path) -> dict:
+    """The atomic scatter-add baseline (libsgb_atomic.so: every lookup adds
+    its bag's gradient row into the looked-up row with fp32 atomics, no
+    deduplication) on the same lookups, timed by HIP events around `calls`
+    back-to-back calls.  Dense workloads produce the same dense gradient
+    (fresh or accumulated); SGD and row-wise Adagrad workloads are run as
+    atomic SGD on the same weights (row-wise Adagrad has no atomic form).
+    Runs after every other measurement: it changes `out`."""
+    import sparse_gradient_backward_amd.atomic as atomic
+    tables = atomic.AtomicTables(inp.hash_size_cumsum, inp.D_offsets, spec.pooling)
+    B = inp.B if inp.offsets is not None else 0
+    dense = spec.mode == "dense"
+    mode = "dense" if dense else "sgd"
+    scale = 1.0 if dense else -(spec.lr or 0.01)
+    fresh = dense and not spec.accumulate
+
+    def call():
+        return tables.backward(grad_output, spec.grad_dtype, indices, offsets, B, psw, out,
+                               scale=scale, zero_first=fresh)
+
+    st = call()
+    torch.cuda.synchronize()
+    if st != "OK":
+        return {"status": st}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(calls):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / calls
+    return {"mode": mode, "accumulate": bool(not fresh) if dense else None, "calls": calls,
+            "ms_per_call": ms, "lookups_per_s": inp.N / (ms * 1e-3),
+            "float_atomics_per_call": int(np.diff(inp.D_offsets).astype(np.int64)[
+                np.repeat(np.arange(inp.T), np.diff(inp.offsets[::inp.B]))
+                if inp.offsets is not None else np.zeros(inp.N, np.int64)].sum()),
+            "slowdown_vs_path": ms / ms_path, "status": st}
 
 
 def plan_npasses(inp: synth.Inputs) -> int:

@@ -16,6 +16,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsgb.so")
 SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "api.cpp")]
+# the atomic scatter-add backward, a comparison baseline kept in its own library
+ATOMIC_LIB = os.path.join(HERE, "libsgb_atomic.so")
+ATOMIC_SOURCES = [os.path.join(CSRC, "atomic_scatter.hip")]
 ARCH = os.environ.get("SGB_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
@@ -33,11 +36,11 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False, out: str = LIB, defines: tuple = ()) -> str:
+def build(verbose: bool = False, out: str = LIB, defines: tuple = (), sources=None) -> str:
     """Compile every source into libsgb.so (always recompiles).  `defines`
     (e.g. ("SGB_SHORT_UNR=2",)) override the tuning knobs of internal.h."""
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *FLAGS, *[f"-D{d}" for d in defines], *SOURCES, "-o", tmp]
+    cmd = [hipcc(), *FLAGS, *[f"-D{d}" for d in defines], *(sources or SOURCES), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -52,6 +55,11 @@ def build(verbose: bool = False, out: str = LIB, defines: tuple = ()) -> str:
     return out
 
 
+def build_atomic(verbose: bool = False) -> str:
+    """Compile the atomic scatter-add baseline into libsgb_atomic.so."""
+    return build(verbose=verbose, out=ATOMIC_LIB, sources=ATOMIC_SOURCES)
+
+
 if __name__ == "__main__":
     import argparse
     ap = argparse.ArgumentParser()
@@ -59,3 +67,5 @@ if __name__ == "__main__":
     ap.add_argument("-D", dest="defines", action="append", default=[])
     a = ap.parse_args()
     print(build(verbose=True, out=a.out, defines=tuple(a.defines)))
+    if a.out == LIB:
+        print(build_atomic(verbose=True))

@@ -28,6 +28,26 @@ def test_every_declared_function_is_exported():
         assert f" T {name}" in out, f"{name} not a defined dynamic symbol"
 
 
+def test_atomic_library_exports_its_header():
+    """libsgb_atomic.so (the atomic scatter-add baseline) exports what
+    include/sgb_atomic.h declares, and rejects bad arguments on the host."""
+    import sparse_gradient_backward_amd.atomic as atomic
+    declared = atomic.header_functions()
+    assert declared == ["sgb_atomic_backward"]
+    out = subprocess.run(["nm", "-D", "--defined-only", atomic.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    for name in declared:
+        assert f" T {name}" in out, f"{name} not a defined dynamic symbol"
+    f = atomic._lib.sgb_atomic_backward
+    # argument errors return before any device call
+    assert f(0, None, None, None, 8, 0, 0, None, 0, None, 0, None, 1, None, None, 1.0, 0,
+             None) == 1
+    p = ctypes.c_void_p(16)
+    assert f(1, p, p, p, 6, 0, 0, p, 0, p, 0, p, 1, None, p, 1.0, 0, None) == 1   # D % 4
+    assert f(2, p, p, p, 8, 0, 2, p, 0, p, 0, None, 0, None, p, 1.0, 0, None) == 2  # nobag, T>1
+    assert f(1, p, p, p, 8, 0, 0, p, 0, p, 0, None, 1, None, p, 1.0, 0, None) == 1  # no offsets
+
+
 def test_struct_layout_matches_header():
     src = r"""
 #include <stdio.h>
