@@ -66,8 +66,16 @@ def _lib(path: Optional[str] = None):
         lib.orc_row_grads.argtypes = [P, i64, vp, i32, vp, vp]
         lib.orc_update_rows.argtypes = [i32, i32, i64, vp, i32, vp, f32, f32, vp, vp]
         lib.orc_forward.argtypes = [P, vp, vp]
+        u32, u64 = ctypes.c_uint32, ctypes.c_uint64
+        lib.orc_philox4x32_10.argtypes = [vp, vp, vp]
+        lib.orc_philox4x32_10.restype = None
+        lib.orc_bf16_round_array.argtypes = [vp, vp, vp, i64]
+        lib.orc_bf16_round_array.restype = None
+        lib.orc_update_rows_bf16.argtypes = [i32, i64, vp, i32, vp, f32, f32, vp, vp, vp, i32,
+                                             u64, u32]
         for f in (lib.orc_validate, lib.orc_linearize, lib.orc_runs,
-                  lib.orc_row_grads, lib.orc_update_rows, lib.orc_forward):
+                  lib.orc_row_grads, lib.orc_update_rows, lib.orc_forward,
+                  lib.orc_update_rows_bf16):
             f.restype = ctypes.c_int
         _libs[path] = lib
     return _libs[path]
@@ -188,6 +196,45 @@ def update_rows(mode: str, G: np.ndarray, D: np.ndarray, rows0: Optional[np.ndar
     D = np.ascontiguousarray(D, np.int32)
     _check(_lib(lib).orc_update_rows(MODE[mode], 1 if accumulate else 0, n, _ptr(D), ldg, _ptr(G),
                                      float(lr), float(eps), _ptr(rows), _ptr(mom)), "update_rows")
+    return rows, mom
+
+
+def philox4x32_10(counter, key, lib: Optional[str] = None) -> np.ndarray:
+    """One Philox4x32-10 block: four uint32 words from a 4-word counter and 2-word key."""
+    c = np.ascontiguousarray(counter, np.uint32)
+    k = np.ascontiguousarray(key, np.uint32)
+    out = np.zeros(4, np.uint32)
+    _lib(lib).orc_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def bf16_round(x: np.ndarray, rnd: Optional[np.ndarray] = None,
+               lib: Optional[str] = None) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16): nearest even, or stochastic with one
+    uint32 random word per element."""
+    x = np.ascontiguousarray(x, np.float32).ravel()
+    r = None if rnd is None else np.ascontiguousarray(rnd, np.uint32).ravel()
+    out = np.zeros(x.size, np.uint16)
+    _lib(lib).orc_bf16_round_array(_ptr(x), _ptr(r), _ptr(out), x.size)
+    return out
+
+
+def update_rows_bf16(mode: str, G: np.ndarray, D: np.ndarray, rows0: np.ndarray,
+                     mom0: Optional[np.ndarray], row_ids: np.ndarray, lr: float = 0.0,
+                     eps: float = 0.0, stochastic: bool = True, seed: int = 0, offset: int = 0,
+                     lib: Optional[str] = None):
+    """SGD / row-wise Adagrad on bf16 rows (uint16 bit patterns [n, ldg]);
+    returns (rows uint16 [n, ldg], mom fp32 [n])."""
+    G = np.ascontiguousarray(G, np.float64)
+    n, ldg = G.shape
+    rows = np.ascontiguousarray(rows0, np.uint16).copy()
+    mom = np.zeros(n, np.float32) if mom0 is None else np.ascontiguousarray(mom0, np.float32).copy()
+    D = np.ascontiguousarray(D, np.int32)
+    ids = np.ascontiguousarray(row_ids, np.int64)
+    _check(_lib(lib).orc_update_rows_bf16(MODE[mode], n, _ptr(D), ldg, _ptr(G), float(lr),
+                                          float(eps), _ptr(rows), _ptr(mom), _ptr(ids),
+                                          1 if stochastic else 0, int(seed) & (2**64 - 1),
+                                          int(offset) & 0xFFFFFFFF), "update_rows_bf16")
     return rows, mom
 
 

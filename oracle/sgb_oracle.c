@@ -28,7 +28,9 @@
  * Every function here is pinned by the CPU test suite against something other
  * than itself: hand-worked cases, a dense one-hot matrix product, the mass
  * invariant, closed forms of the optimizer steps and brute-force run
- * structure.  No function is "parity unpinned".
+ * structure; the bf16 weight rows by the generator's published known-answer
+ * vectors, torch's fp32 -> bf16 conversion, exhaustive rounding counts and
+ * binomial bounds.  No function is "parity unpinned".
  */
 #include <math.h>
 #include <stdint.h>
@@ -452,3 +454,122 @@ int orc_forward(const orc_problem* p, const float* W, float* out) {
   return ORC_OK;
 }
 
+
+/* ------------------------------------------------------------------------ */
+/* bf16 weight rows: round to nearest even, or stochastic rounding          */
+/* ------------------------------------------------------------------------ */
+
+/* The FBGEMM page stores an updated row into 16-bit weights with stochastic
+ * rounding when asked for it, drawing from a Philox generator seeded per
+ * call [P1, the split-kernel weight store: `stochastic_rounding_init`, the
+ * row's `set_stoc_state`]; the bodies of the rounding and of the state are
+ * not printed.  Readings:
+ *  - the generator is Philox4x32-10 as published (Salmon, Moraes, Dror and
+ *    Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11): 10 rounds,
+ *    multipliers 0xD2511F53 / 0xCD9E8D57, key increments 0x9E3779B9 /
+ *    0xBB67AE85, the key bumped before every round after the first;
+ *  - the element (linear row id r, column d) takes word d % 4 of the block
+ *    with counter (d / 4, r mod 2^32, r / 2^32, offset) and key
+ *    (seed mod 2^32, seed / 2^32): one block per 4 columns of a row, so the
+ *    bits depend on the row and column and not on any launch shape;
+ *  - the fp32 result of the update (computed as for fp32 rows, rounded once
+ *    to fp32) is rounded to bf16 stochastically by adding the word's high 16
+ *    bits to the fp32 bit pattern and keeping the high half: the magnitude
+ *    rounds up with probability (dropped bits) / 2^16, so the rounding is
+ *    unbiased; without stochastic rounding it is round-to-nearest-even;
+ *  - infinities keep their high half, NaNs stay (quiet) NaNs. */
+
+static uint32_t orc_mulhi32(uint32_t a, uint32_t b) {
+  return (uint32_t)(((uint64_t)a * (uint64_t)b) >> 32);
+}
+
+void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+  uint32_t k0 = key[0], k1 = key[1];
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = orc_mulhi32(0xD2511F53u, c0);
+    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = orc_mulhi32(0xCD9E8D57u, c2);
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n1 = lo1, n2 = hi0 ^ c3 ^ k1, n3 = lo0;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+static uint32_t orc_f32_bits(float x) {
+  uint32_t u;
+  memcpy(&u, &x, 4);
+  return u;
+}
+
+/* non-finite: keep the high half; a NaN keeps its quiet bit set */
+static int orc_bf16_special(uint32_t u, uint16_t* h) {
+  if ((u & 0x7F800000u) != 0x7F800000u) return 0;
+  *h = (uint16_t)((u >> 16) | ((u & 0x007FFFFFu) ? 0x0040u : 0u));
+  return 1;
+}
+
+uint16_t orc_bf16_rne(float x) {
+  const uint32_t u = orc_f32_bits(x);
+  uint16_t h;
+  if (orc_bf16_special(u, &h)) return h;
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+uint16_t orc_bf16_sr(float x, uint32_t rnd) {
+  const uint32_t u = orc_f32_bits(x);
+  uint16_t h;
+  if (orc_bf16_special(u, &h)) return h;
+  return (uint16_t)((u + (rnd >> 16)) >> 16);
+}
+
+/* Rounds n fp32 values; rnd == NULL: nearest even, else stochastic with rnd[i]. */
+void orc_bf16_round_array(const float* x, const uint32_t* rnd, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = rnd ? orc_bf16_sr(x[i], rnd[i]) : orc_bf16_rne(x[i]);
+}
+
+/* The Philox word of element (row, col), as read above. */
+static uint32_t orc_sr_word(uint64_t seed, uint32_t offset, int64_t row, int col) {
+  const uint32_t ctr[4] = {(uint32_t)(col >> 2), (uint32_t)(uint64_t)row,
+                           (uint32_t)((uint64_t)row >> 32), offset};
+  const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t out[4];
+  orc_philox4x32_10(ctr, key, out);
+  return out[col & 3];
+}
+
+/* SGD or row-wise Adagrad on bf16 rows: each row is widened exactly to fp32,
+ * updated as orc_update_rows does (fp64, rounded once to fp32), and rounded
+ * to bf16.  rows: [nrows][ldg] bf16 bit patterns, updated in place; row_ids:
+ * the rows' linear ids (the stochastic-rounding counter). */
+int orc_update_rows_bf16(int32_t mode, int64_t nrows, const int32_t* D, int32_t ldg,
+                         const double* G, float lr, float eps, uint16_t* rows, float* mom,
+                         const int64_t* row_ids, int32_t stochastic, uint64_t seed,
+                         uint32_t offset) {
+  if (mode != ORC_SGD && mode != ORC_ROWWISE_ADAGRAD) return ORC_INVALID_ARGUMENT;
+  float* tmp = (float*)malloc(sizeof(float) * (size_t)(ldg > 0 ? ldg : 1));
+  if (tmp == NULL) return ORC_INVALID_ARGUMENT;
+  int st = ORC_OK;
+  for (int64_t k = 0; k < nrows && st == ORC_OK; ++k) {
+    uint16_t* h = rows + k * (int64_t)ldg;
+    const int Dk = D[k];
+    if (Dk <= 0 || Dk > ldg) {
+      st = ORC_INVALID_ARGUMENT;
+      break;
+    }
+    for (int d = 0; d < Dk; ++d) {
+      const uint32_t u = ((uint32_t)h[d]) << 16;
+      memcpy(&tmp[d], &u, 4);
+    }
+    st = orc_update_rows(mode, 0, 1, &D[k], ldg, G + k * (int64_t)ldg, lr, eps, tmp,
+                         mom ? &mom[k] : NULL);
+    for (int d = 0; d < Dk && st == ORC_OK; ++d)
+      h[d] = stochastic ? orc_bf16_sr(tmp[d], orc_sr_word(seed, offset, row_ids[k], d))
+                        : orc_bf16_rne(tmp[d]);
+  }
+  free(tmp);
+  return st;
+}
