@@ -294,6 +294,8 @@ def main():
     del flush
     status = plan.device_status(ws)
     fwd = forward_measure(plan, inp, spec, indices, offsets, psw, out, ws, args.steps)
+    bf16w = bf16_weights_measure(plan, spec, grad_output, indices, offsets, B, psw, out, mom, ws,
+                                 args.steps, ms_per_step)
     atomic = atomic_measure(inp, spec, grad_output, indices, offsets, psw, out,
                             min(args.steps, 20), ms_per_step)
 
@@ -361,6 +363,7 @@ def main():
                      "traffic": measured_traffic(spec.name, kernel_names[dom]), "bytes_per_launch": int(per_launch_bytes),
                      "launch_ms": per_launch_ms},
         "forward": fwd,
+        "bf16_weights": bf16w,
         "atomic_scatter": atomic,
         "cpu_baseline": cpu,
         "device_status": status,
@@ -410,6 +413,38 @@ def forward_measure(plan, inp, spec, indices, offsets, psw, table, ws, steps) ->
             "device_status": status,
             "roofline": {"bound": "hbm", "kernel": "k_forward", "achieved": gbps,
                          "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS}}
+
+
+def bf16_weights_measure(plan, spec, grad_output, indices, offsets, B, psw, out, mom, ws, steps,
+                         ms_path):
+    """The same step with the weights held in bf16 and stochastic rounding
+    in the fused update (SGD and row-wise Adagrad workloads only): a bf16
+    copy of the weights (nearest-even of the fp32 ones), `steps` plain calls
+    timed by HIP events, each with its own Philox offset."""
+    if spec.mode == "dense":
+        return None
+    w = out.to(torch.bfloat16)
+    m = None if mom is None else mom.clone()
+
+    def call(k):
+        plan.backward(grad_output, indices, offsets, B, psw, spec.mode, weights=w, momentum=m,
+                      lr=spec.lr, eps=spec.eps, workspace=ws, stochastic_rounding=True,
+                      sr_seed=spec.seed, sr_offset=k)
+
+    for k in range(3):
+        call(k)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k in range(steps):
+        call(3 + k)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    status = plan.device_status(ws)
+    del w, m
+    return {"ms_per_step": ms, "stochastic_rounding": True, "vs_fp32_weights": ms / ms_path,
+            "device_status": status}
 
 
 def atomic_measure(inp, spec, grad_output, indices, offsets, psw, out, calls, ms_path) -> dict:

@@ -134,8 +134,9 @@ typedef struct {
 /* Where and how the result is written; device pointers, caller-owned. */
 typedef struct {
   int32_t mode;      /* an sgb_mode value                                        */
-  float* weights;    /* SGD / Adagrad: flat fp32 rows, table t row i at element
-                        woff[t] + i * D_t with woff[t] = sum_{t'<t} E_t' * D_t'  */
+  void* weights;     /* SGD / Adagrad: flat rows of weights_dtype elements, table
+                        t row i at element woff[t] + i * D_t with
+                        woff[t] = sum_{t'<t} E_t' * D_t'                         */
   float* momentum;   /* Adagrad: fp32[sum_t E_t], one value per row, indexed by
                         linear id hsc[t] + i                                      */
   float* grad;       /* DENSE: fp32, same layout as weights                       */
@@ -144,6 +145,22 @@ typedef struct {
                         get grad[row] += G_row, all others untouched             */
   float lr;          /* SGD / Adagrad learning rate                               */
   float eps;         /* Adagrad epsilon (added outside the square root)          */
+  /* 16-bit weights (FBGEMM page, split-kernel weight store: a 16-bit row is
+     stored with stochastic rounding from a Philox state seeded per call).
+     A zero-initialised tail keeps fp32 weights.                               */
+  int32_t weights_dtype;       /* SGB_F32, or SGB_BF16 (SGD / Adagrad only;
+                                  DENSE with SGB_BF16 is SGB_ERR_UNSUPPORTED)  */
+  int32_t stochastic_rounding; /* bf16: 1 = stochastic, 0 = nearest even.  The
+                                  updated value is formed in fp32 as for fp32
+                                  rows, then element (linear id r, column d)
+                                  adds the high 16 bits of word d % 4 of
+                                  Philox4x32-10(counter = (d / 4, r mod 2^32,
+                                  r / 2^32, sr_offset mod 2^32), key = (sr_seed
+                                  mod 2^32, sr_seed / 2^32)) to its fp32 bit
+                                  pattern and keeps the high half              */
+  uint64_t sr_seed;            /* Philox key                                   */
+  uint64_t sr_offset;          /* its low 32 bits: counter word 3 (e.g. the
+                                  step), so steps draw different bits         */
 } sgb_update;
 
 /*

@@ -68,7 +68,9 @@ class _Lookups(ctypes.Structure):
 class _Update(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("weights", ctypes.c_void_p),
                 ("momentum", ctypes.c_void_p), ("grad", ctypes.c_void_p),
-                ("accumulate", ctypes.c_int32), ("lr", ctypes.c_float), ("eps", ctypes.c_float)]
+                ("accumulate", ctypes.c_int32), ("lr", ctypes.c_float), ("eps", ctypes.c_float),
+                ("weights_dtype", ctypes.c_int32), ("stochastic_rounding", ctypes.c_int32),
+                ("sr_seed", ctypes.c_uint64), ("sr_offset", ctypes.c_uint64)]
 
 
 class _RunsView(ctypes.Structure):
@@ -168,9 +170,13 @@ STAGES = ("linearize", "sort_count", "sort_offsets", "sort_scatter", "sort", "rl
 def sgb_backward(plan: int, grad_output, indices, offsets, B: int, per_sample_weights,
                  mode: str, weights=None, momentum=None, grad=None, accumulate: bool = False,
                  lr: float = 0.0, eps: float = 0.0, workspace=None, stream=None,
-                 events=None) -> None:
+                 events=None, stochastic_rounding: bool = False, sr_seed: int = 0,
+                 sr_offset: int = 0) -> None:
     """Enqueue one backward pass.  Tensors are device tensors; grad_output is
-    float32 or bfloat16, indices/offsets int64, per_sample_weights float32.
+    float32 or bfloat16, indices/offsets int64, per_sample_weights float32;
+    weights float32, or bfloat16 (SGD / row-wise Adagrad) rounded to nearest
+    even or, with stochastic_rounding, stochastically from (sr_seed,
+    sr_offset).
     `events`, if given, is a list of 2 * len(STAGES) recorded-once
     torch.cuda.Event(enable_timing=True) objects (or None entries) that the
     library records around each stage (sgb_backward_timed)."""
@@ -178,7 +184,9 @@ def sgb_backward(plan: int, grad_output, indices, offsets, B: int, per_sample_we
     gd = {torch.float32: "f32", torch.bfloat16: "bf16"}[grad_output.dtype]
     for name, t, dt in (("indices", indices, torch.int64), ("offsets", offsets, torch.int64),
                         ("per_sample_weights", per_sample_weights, torch.float32),
-                        ("weights", weights, torch.float32), ("momentum", momentum, torch.float32),
+                        ("weights", weights, weights.dtype if weights is not None and
+                         weights.dtype == torch.bfloat16 else torch.float32),
+                        ("momentum", momentum, torch.float32),
                         ("grad", grad, torch.float32)):
         if t is not None and (t.dtype != dt or not t.is_contiguous()):
             raise SgbError(SGB_ERR_INVALID_ARGUMENT, f"sgb_backward: {name} must be contiguous {dt}")
@@ -186,8 +194,11 @@ def sgb_backward(plan: int, grad_output, indices, offsets, B: int, per_sample_we
         raise SgbError(SGB_ERR_INVALID_ARGUMENT, "sgb_backward: grad_output must be contiguous")
     batch = _Batch(_ptr(grad_output), DTYPE[gd], _ptr(indices), int(indices.numel()),
                    _ptr(offsets), int(B), _ptr(per_sample_weights))
+    w_bf16 = weights is not None and weights.dtype == torch.bfloat16
     upd = _Update(MODE[mode], _ptr(weights), _ptr(momentum), _ptr(grad), 1 if accumulate else 0,
-                  float(lr), float(eps))
+                  float(lr), float(eps), DTYPE["bf16"] if w_bf16 else DTYPE["f32"],
+                  1 if stochastic_rounding else 0, int(sr_seed) & (2**64 - 1),
+                  int(sr_offset) & (2**64 - 1))
     ws_ptr = _ptr(workspace)
     ws_bytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
     if events is None:

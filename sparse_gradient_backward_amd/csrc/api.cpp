@@ -335,8 +335,12 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   if (u->mode == SGB_ROWWISE_ADAGRAD && (!u->weights || !u->momentum))
     return SGB_ERR_INVALID_ARGUMENT;
   if (u->mode == SGB_ROWWISE_ADAGRAD && p->Dmax > kMaxCb * kColBlock) return SGB_ERR_UNSUPPORTED;
-  float* out = u->mode == SGB_DENSE_GRAD ? u->grad : u->weights;
-  if (!aligned(out, 16)) return SGB_ERR_INVALID_ARGUMENT;
+  if (u->weights_dtype != SGB_F32 && u->weights_dtype != SGB_BF16) return SGB_ERR_INVALID_ARGUMENT;
+  const bool w_bf16 = u->mode != SGB_DENSE_GRAD && u->weights_dtype == SGB_BF16;
+  if (u->mode == SGB_DENSE_GRAD && u->weights_dtype == SGB_BF16) return SGB_ERR_UNSUPPORTED;
+  void* outv = u->mode == SGB_DENSE_GRAD ? static_cast<void*>(u->grad) : u->weights;
+  if (!aligned(outv, 16)) return SGB_ERR_INVALID_ARGUMENT;
+  float* out = w_bf16 ? nullptr : static_cast<float*>(outv);
   const bool fresh = u->mode == SGB_DENSE_GRAD && !u->accumulate;
   DeviceGuard guard(p->device);
   if (!guard.ok) return SGB_ERR_HIP;
@@ -504,6 +508,12 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   q.run_ticket = at<uint32_t>(ws, L.runtk);
   q.partials = at<double>(ws, L.part);
   q.out = out;
+  q.out_h = w_bf16 ? static_cast<uint16_t*>(outv) : nullptr;
+  q.w_bf16 = w_bf16 ? 1 : 0;
+  q.sr = (w_bf16 && u->stochastic_rounding) ? 1 : 0;
+  q.sr_key0 = (uint32_t)u->sr_seed;
+  q.sr_key1 = (uint32_t)(u->sr_seed >> 32);
+  q.sr_ctr3 = (uint32_t)u->sr_offset;
   q.mom = u->mode == SGB_ROWWISE_ADAGRAD ? u->momentum : nullptr;
   q.status = status;
   q.N = N;

@@ -58,9 +58,6 @@ constexpr int kMaxD = 8192;
 #ifndef SGB_WIDE_UNR16
 #define SGB_WIDE_UNR16 4
 #endif
-#ifndef SGB_WIDE_NT
-#define SGB_WIDE_NT 0
-#endif
 #ifndef SGB_WIDE_WAVES
 #define SGB_WIDE_WAVES 8
 #endif
@@ -304,7 +301,8 @@ struct RedParams {
   uint32_t* sc_ticket;
   uint32_t* run_ticket;
   double* partials;         // fp64 partial sums of long-run work items
-  float* out;               // weights (SGD/Adagrad) or dense grad
+  float* out;               // fp32 weights (SGD/Adagrad) or dense grad
+  uint16_t* out_h;          // bf16 weights (SGD/Adagrad), when w_bf16
   float* mom;               // Adagrad state
   uint32_t* status;
   int64_t N;
@@ -321,6 +319,9 @@ struct RedParams {
   int32_t accumulate;
   float lr;
   float eps;
+  int32_t w_bf16;           // weights are bf16 (out_h), else fp32 (out)
+  int32_t sr;               // bf16: stochastic rounding, else nearest even
+  uint32_t sr_key0, sr_key1, sr_ctr3;  // Philox key (seed) and counter word 3 (offset)
 };
 
 struct FwdParams {

@@ -1081,19 +1081,124 @@ __device__ __forceinline__ int grad_row_of(const RedParams& p, uint32_t info, in
   return (int)(b < 0 ? 0 : (b < p.B ? b : p.B - 1));
 }
 
+__device__ __forceinline__ float4 ld4(const float* q) { return *reinterpret_cast<const float4*>(q); }
+__device__ __forceinline__ void st4(float* q, float4 v) { *reinterpret_cast<float4*>(q) = v; }
+
 struct RowDst {
-  float* out;  // first element of the output row
-  float* mom;  // its Adagrad state
+  void* out;    // the row's first element: fp32, or bf16 weights
+  float* mom;   // its Adagrad state
+  int64_t lin;  // its linear id (the stochastic-rounding counter)
 };
 
+// The output row of element offset e (WB: bf16 weights).
+template <bool WB>
+__device__ __forceinline__ void* row_ptr(const RedParams& p, int64_t e) {
+  if constexpr (WB)
+    return p.out_h + e;
+  else
+    return p.out + e;
+}
+
+template <bool WB>
 __device__ __forceinline__ RowDst row_dest(const RedParams& p, int t, int D, int64_t lin) {
   const int64_t h0 = p.hsc[t], E = p.hsc[t + 1] - h0;
   int64_t row = lin - h0;
   row = row < 0 ? 0 : (row < E ? row : E - 1);
   RowDst d;
-  d.out = p.out + p.woff[t] + row * (int64_t)D;
+  d.out = row_ptr<WB>(p, p.woff[t] + row * (int64_t)D);
   d.mom = p.mom ? p.mom + h0 + row : nullptr;
+  d.lin = h0 + row;
   return d;
+}
+
+// ---- bf16 weight rows
+//
+// SGD and row-wise Adagrad may keep their rows in bf16.  A row is widened
+// exactly to fp32, updated as an fp32 row is (fp64, rounded once to fp32),
+// and rounded to bf16: to nearest even, or stochastically as the FBGEMM
+// page's 16-bit weight store does with a Philox state seeded per call (the
+// bodies are not printed; the generator here is the published
+// Philox4x32-10 of Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers:
+// As Easy as 1, 2, 3", SC'11).  Element (linear id r, column d) takes word
+// d % 4 of the block with counter (d / 4, r mod 2^32, r / 2^32, offset) and
+// key (seed mod 2^32, seed / 2^32), so the bits depend on the row and the
+// column, never on which wave writes them.  Stochastic rounding adds the
+// word's high 16 bits to the fp32 pattern and keeps the high half (the
+// magnitude rounds up with probability dropped bits / 2^16); infinities keep
+// their high half and NaNs stay quiet NaNs.
+
+struct U4 {
+  uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ U4 philox4x32_10(U4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
+    const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+    c = U4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+  }
+  return c;
+}
+
+__device__ __forceinline__ uint32_t bf16_nonfinite(uint32_t u) {
+  return (u >> 16) | ((u & 0x007FFFFFu) ? 0x0040u : 0u);
+}
+
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7F800000u) == 0x7F800000u) return bf16_nonfinite(u);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t bf16_sr(float x, uint32_t rnd) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7F800000u) == 0x7F800000u) return bf16_nonfinite(u);
+  return (u + (rnd >> 16)) >> 16;
+}
+
+// The row's old values at columns [col + off, col + off + 4): fp32, or bf16
+// widened exactly.  The address is formed as (row + col) + off: the
+// short-run reducer keeps row + col across its pieces, and forming
+// row + (col + off) instead costs it a register (and a spill).
+template <bool WB>
+__device__ __forceinline__ float4 ldw4(const RedParams& p, const RowDst& d, int col, int off = 0) {
+  if constexpr (!WB) return ld4(static_cast<const float*>(d.out) + col + off);
+  const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(d.out) + col + off);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+
+// Stores the row's new values at columns [col, col+4) (col % 4 == 0).
+template <bool WB>
+__device__ __forceinline__ void stw4(const RedParams& p, const RowDst& d, int col, float4 v,
+                                     int off = 0) {
+  if constexpr (!WB) {
+    st4(static_cast<float*>(d.out) + col + off, v);
+    return;
+  }
+  col += off;
+  uint32_t h0, h1, h2, h3;
+  if (p.sr) {
+    const U4 r = philox4x32_10(
+        U4{(uint32_t)col >> 2, (uint32_t)d.lin, (uint32_t)((uint64_t)d.lin >> 32), p.sr_ctr3},
+        p.sr_key0, p.sr_key1);
+    h0 = bf16_sr(v.x, r.x);
+    h1 = bf16_sr(v.y, r.y);
+    h2 = bf16_sr(v.z, r.z);
+    h3 = bf16_sr(v.w, r.w);
+  } else {
+    h0 = bf16_rne(v.x);
+    h1 = bf16_rne(v.y);
+    h2 = bf16_rne(v.z);
+    h3 = bf16_rne(v.w);
+  }
+  *reinterpret_cast<uint2*>(static_cast<uint16_t*>(d.out) + col) =
+      make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
 }
 
 // Lane groups of a long-run item: lpl lanes per group (the power of two
@@ -1214,8 +1319,6 @@ __device__ __forceinline__ double group_sum(double x, int lpl) {
   return x;
 }
 
-__device__ __forceinline__ float4 ld4(const float* q) { return *reinterpret_cast<const float4*>(q); }
-__device__ __forceinline__ void st4(float* q, float4 v) { *reinterpret_cast<float4*>(q) = v; }
 
 // One fp32 result from an fp64 value, rounded once.
 __device__ __forceinline__ float4 round4(double x, double y, double z, double w) {
@@ -1232,13 +1335,13 @@ __device__ __forceinline__ float4 round4(double x, double y, double z, double w)
 // `cache_backward_sgd_kernel`).  Dense: store, or add for an accumulating
 // grad_weight (tinygrad `_embedding_bwd_kernel`).  The old row value is read
 // before getG so that the read overlaps the gather.
-template <class F>
+template <bool WB, class F>
 __device__ __forceinline__ void finish_row(const RedParams& p, const Groups& G, const RowDst& dst,
                                            int D, bool write, int cb_lo, int cb_hi, F&& getG) {
   const int lig = G.lig;
   if (p.mode == kModeAdagrad) {
     const bool w0ok = write && 4 * lig < D;
-    const float4 w0 = w0ok ? ld4(dst.out + 4 * lig) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 w0 = w0ok ? ldw4<WB>(p, dst, 4 * lig) : make_float4(0.f, 0.f, 0.f, 0.f);
     const float m0 = write ? *dst.mom : 0.f;
     const int ncb = col_blocks(D);
     const d4 g0 = getG(0);
@@ -1253,15 +1356,15 @@ __device__ __forceinline__ void finish_row(const RedParams& p, const Groups& G, 
     const double m = (double)m0 + ss / (double)D;
     const double mult = (double)p.lr / (sqrt(m) + (double)p.eps);
     if (w0ok)
-      st4(dst.out + 4 * lig, round4((double)w0.x - g0.x * mult, (double)w0.y - g0.y * mult,
+      stw4<WB>(p, dst, 4 * lig, round4((double)w0.x - g0.x * mult, (double)w0.y - g0.y * mult,
                                     (double)w0.z - g0.z * mult, (double)w0.w - g0.w * mult));
 #pragma unroll 1
     for (int cb = 1; cb < ncb; ++cb) {
       const d4 g = getG(cb);
       const int col = cb * kColBlock + 4 * lig;
       if (write && col < D) {
-        const float4 wv = ld4(dst.out + col);
-        st4(dst.out + col, round4((double)wv.x - g.x * mult, (double)wv.y - g.y * mult,
+        const float4 wv = ldw4<WB>(p, dst, col);
+        stw4<WB>(p, dst, col, round4((double)wv.x - g.x * mult, (double)wv.y - g.y * mult,
                                   (double)wv.z - g.z * mult, (double)wv.w - g.w * mult));
       }
     }
@@ -1274,7 +1377,7 @@ __device__ __forceinline__ void finish_row(const RedParams& p, const Groups& G, 
   for (int cb = cb_lo; cb < cb_hi; ++cb) {
     const int col = cb * kColBlock + 4 * lig;
     const bool ok = write && col < D;
-    const float4 old = (ok && needs_old) ? ld4(dst.out + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 old = (ok && needs_old) ? ldw4<WB>(p, dst, col) : make_float4(0.f, 0.f, 0.f, 0.f);
     const d4 g = getG(cb);
     if (!ok) continue;
     float4 wv;
@@ -1286,7 +1389,7 @@ __device__ __forceinline__ void finish_row(const RedParams& p, const Groups& G, 
                   (double)old.w + g.w);
     else
       wv = round4(g.x, g.y, g.z, g.w);
-    st4(dst.out + col, wv);
+    stw4<WB>(p, dst, col, wv);
   }
 }
 
@@ -1294,6 +1397,7 @@ __device__ __forceinline__ void finish_row(const RedParams& p, const Groups& G, 
 // columns, fp64) is complete, from the old values `old` (and Adagrad state
 // m0) read before g was gathered.  Row-wise Adagrad here covers a row of one
 // block; wider rows take finish_row.
+template <bool WB>
 __device__ __forceinline__ void update_block(const RedParams& p, const Groups& G, const RowDst& dst,
                                              int D, bool write, int cb, const float4& old, float m0,
                                              const d4& g) {
@@ -1305,7 +1409,7 @@ __device__ __forceinline__ void update_block(const RedParams& p, const Groups& G
     const double m = (double)m0 + ss / (double)D;
     const double mult = (double)p.lr / (sqrt(m) + (double)p.eps);
     if (ok)
-      st4(dst.out + col, round4((double)old.x - g.x * mult, (double)old.y - g.y * mult,
+      stw4<WB>(p, dst, col, round4((double)old.x - g.x * mult, (double)old.y - g.y * mult,
                                 (double)old.z - g.z * mult, (double)old.w - g.w * mult));
     if (write && lig == 0) *dst.mom = (float)m;
     return;
@@ -1321,7 +1425,7 @@ __device__ __forceinline__ void update_block(const RedParams& p, const Groups& G
   } else {
     wv = round4(g.x, g.y, g.z, g.w);
   }
-  st4(dst.out + col, wv);
+  stw4<WB>(p, dst, col, wv);
 }
 // Partials travel between waves on different XCDs.  They are written and read
 // with device-scope (agent) atomic accesses, which the hardware keeps coherent
@@ -1401,7 +1505,7 @@ __device__ __forceinline__ d4 sum_slots(const RedParams& p, const Groups& G, uin
   return fold_groups(acc, G.lpl);
 }
 
-template <bool BF16>
+template <bool BF16, bool WB>
 __device__ __forceinline__ void long_item(const RedParams& p, const LongRun& rec, int c, int cb) {
   const int t = rec.t, start = rec.start, len = rec.len, D = rec.D;
   const Groups G = groups_of(lanes_per_row(D));
@@ -1416,7 +1520,7 @@ __device__ __forceinline__ void long_item(const RedParams& p, const LongRun& rec
   const int cb_lo = adagrad ? 0 : cb;
   const int cb_hi = adagrad ? ncb : cb + 1;
   const int64_t gcol = rec.gcol;
-  const RowDst dst{p.out + rec.out, p.mom ? p.mom + rec.mom : nullptr};
+  const RowDst dst{row_ptr<WB>(p, rec.out), p.mom ? p.mom + rec.mom : nullptr, rec.mom};
   // each lane group takes a contiguous share of the chunk, so that the
   // adjacent lookups of one bag stay together for merging
   const int per = (hi - lo + ng - 1) / ng;
@@ -1437,12 +1541,12 @@ __device__ __forceinline__ void long_item(const RedParams& p, const LongRun& rec
     const bool col_ok = col < D;
     // the old row (and state) is read before the gather so the two overlap
     const bool rd = direct && g == 0 && col_ok && needs_old;
-    const float4 old = rd ? ld4(dst.out + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 old = rd ? ldw4<WB>(p, dst, col) : make_float4(0.f, 0.f, 0.f, 0.f);
     const float mom0 = (direct && adagrad && g == 0) ? *dst.mom : 0.f;
     const d4 a = fold_groups(
         gather_merged<SGB_LONG_UNR, BF16>(p, G, glo, ghi, slices, t, gcol + col, col_ok, q), G.lpl);
     if (direct)
-      update_block(p, G, dst, D, g == 0, cbx, old, mom0, a);
+      update_block<WB>(p, G, dst, D, g == 0, cbx, old, mom0, a);
     else if (g == 0 && col_ok)
       store_partial(slot_of(p, cbeg, c, ncb, cbx) + 4 * lig, a);
   }
@@ -1452,7 +1556,7 @@ __device__ __forceinline__ void long_item(const RedParams& p, const LongRun& rec
   if (!ticket_last(p.sc_ticket + cbeg + (int64_t)m0 * ncb + cb_lo, (uint32_t)members)) return;
   const int nsc = (nch + kSuperChunk - 1) / kSuperChunk;
   if (nsc == 1) {
-    finish_row(p, G, dst, D, g == 0, cb_lo, cb_hi, [&](int cbx) {
+    finish_row<WB>(p, G, dst, D, g == 0, cb_lo, cb_hi, [&](int cbx) {
       return sum_slots(p, G, cbeg, ncb, 0, nch, 1, cbx, D);
     });
     return;
@@ -1464,7 +1568,7 @@ __device__ __forceinline__ void long_item(const RedParams& p, const LongRun& rec
       store_partial(slot_of(p, cbeg, m0, ncb, cbx) + 4 * lig, a);
   }
   if (!ticket_last(p.run_ticket + cbeg + cb_lo, (uint32_t)nsc)) return;
-  finish_row(p, G, dst, D, g == 0, cb_lo, cb_hi, [&](int cbx) {
+  finish_row<WB>(p, G, dst, D, g == 0, cb_lo, cb_hi, [&](int cbx) {
     return sum_slots(p, G, cbeg, ncb, 0, nsc, kSuperChunk, cbx, D);
   });
 }
@@ -1512,7 +1616,7 @@ __device__ __forceinline__ LongRun uniform_rec(const LongRun& r) {
   return u;
 }
 
-template <bool BF16>
+template <bool BF16, bool WB>
 __global__ __launch_bounds__(256) void k_reduce_long(RedParams p) {
   const uint32_t n_items = *p.total_items;
   const int nlong = (int)*p.num_long;
@@ -1526,7 +1630,7 @@ __global__ __launch_bounds__(256) void k_reduce_long(RedParams p) {
     const int local = (int)(w - rec.cbeg);
     const int c = local / rec.ncb, cb = local % rec.ncb;
     if (p.mode == kModeAdagrad && cb != 0) continue;
-    long_item<BF16>(p, rec, c, cb);
+    long_item<BF16, WB>(p, rec, c, cb);
   }
 }
 
@@ -1551,7 +1655,7 @@ __device__ __forceinline__ int short_lpl(int D) {
 // xor tree, and the first of them writes the row.  Called with the whole wave
 // active.  The row's old value and Adagrad state are read before the gather
 // so that the reads overlap.
-template <int CPL, bool BF16>
+template <int CPL, bool BF16, bool WB>
 __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, int lpl, int64_t base,
                                             int len, uint64_t key, int rowi, float cf, int t,
                                             int D, int cb) {
@@ -1583,14 +1687,14 @@ __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, in
   for (int i = 0; i < NP; ++i)
     if (active && col + 4 * lpl * i < D) vmask |= 1 << i;
   const int wmask = lead ? vmask : 0;
-  RowDst dst{nullptr, nullptr};
-  if (lead) dst = row_dest(p, t, D, (int64_t)id);
+  RowDst dst{nullptr, nullptr, 0};
+  if (lead) dst = row_dest<WB>(p, t, D, (int64_t)id);
   const bool needs_old = p.mode != kModeDense || p.accumulate;
   float4 old[NP];
   d4 acc[NP];
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
-    old[i] = (needs_old && ((wmask >> i) & 1)) ? ld4(dst.out + col + 4 * lpl * i)
+    old[i] = (needs_old && ((wmask >> i) & 1)) ? ldw4<WB>(p, dst, col, 4 * lpl * i)
                                               : make_float4(0.f, 0.f, 0.f, 0.f);
     acc[i] = d4_zero();
   }
@@ -1661,9 +1765,10 @@ __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, in
 #pragma unroll
     for (int i = 0; i < NP; ++i)
       if ((wmask >> i) & 1)
-        st4(dst.out + col + 4 * lpl * i,
+        stw4<WB>(p, dst, col,
             round4((double)old[i].x - acc[i].x * mult, (double)old[i].y - acc[i].y * mult,
-                   (double)old[i].z - acc[i].z * mult, (double)old[i].w - acc[i].w * mult));
+                   (double)old[i].z - acc[i].z * mult, (double)old[i].w - acc[i].w * mult),
+            4 * lpl * i);
     if (lead && lig == 0) *dst.mom = (float)mm;
     return;
   }
@@ -1681,7 +1786,7 @@ __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, in
                  (double)old[i].w + a.w);
     else
       w = round4(a.x, a.y, a.z, a.w);
-    st4(dst.out + col + 4 * lpl * i, w);
+    stw4<WB>(p, dst, col, w, 4 * lpl * i);
   }
 }
 
@@ -1692,7 +1797,7 @@ __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, in
 // runs (length < thr) that start in its 64 >> sub_log positions, in batches
 // of at most 64/lpl runs of one table.  Rows wider than 512 columns are
 // skipped here (k_reduce_wide serves them).
-template <int CPL, bool BF16>
+template <int CPL, bool BF16, bool WB>
 __device__ __forceinline__ void reduce_short(const RedParams& p) {
   const int lane = lane_id();
   const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -1741,16 +1846,18 @@ __device__ __forceinline__ void reduce_short(const RedParams& p) {
     }
     pending &= ~sel;
     if (D > 512 || cb * 64 * CPL >= D) continue;  // wider rows: k_reduce_wide
-    short_batch<CPL, BF16>(p, sel, lpl, base, len, key, rowi, cf, t0, D, cb);
+    short_batch<CPL, BF16, WB>(p, sel, lpl, base, len, key, rowi, cf, t0, D, cb);
   }
 }
 
 // 8 columns per lane with fp64 sums fits about 80 VGPRs: 6 waves per SIMD overlap
-// the runs' dependent memory steps.
-template <bool BF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SGB_SHORT8_WAVES, SGB_SHORT8_WAVES)))
+// the runs' dependent memory steps.  The bf16-weight instances take one wave
+// less: their rounding code needs the registers (at 80 they spill).
+template <bool BF16, bool WB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
+    WB ? SGB_SHORT8_WAVES - 1 : SGB_SHORT8_WAVES, WB ? SGB_SHORT8_WAVES - 1 : SGB_SHORT8_WAVES)))
 void k_reduce_short8(RedParams p) {
-  reduce_short<8, BF16>(p);
+  reduce_short<8, BF16, WB>(p);
 }
 
 
@@ -1812,18 +1919,7 @@ __device__ __forceinline__ uint64_t rl64(uint64_t x, int l) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-__device__ __forceinline__ void wide_st4(float* q, float4 v) {
-#if SGB_WIDE_NT
-  __builtin_nontemporal_store(v.x, q);
-  __builtin_nontemporal_store(v.y, q + 1);
-  __builtin_nontemporal_store(v.z, q + 2);
-  __builtin_nontemporal_store(v.w, q + 3);
-#else
-  st4(q, v);
-#endif
-}
-
-template <int CPL, int UNR, bool BF16>
+template <int CPL, int UNR, bool BF16, bool WB>
 __device__ __forceinline__ void wide_item(const RedParams& p, const WideRun& m, const WideLane& d0,
                                           int cb) {
   constexpr int NP = CPL / 4;
@@ -1839,13 +1935,13 @@ __device__ __forceinline__ void wide_item(const RedParams& p, const WideRun& m, 
 #pragma unroll
   for (int i = 0; i < NP; ++i)
     if (col + 256 * i < D) vmask |= 1 << i;
-  const RowDst dst = row_dest(p, t, D, (int64_t)(kv0 >> p.info_bits));
+  const RowDst dst = row_dest<WB>(p, t, D, (int64_t)(kv0 >> p.info_bits));
   const bool needs_old = p.mode != kModeDense || p.accumulate;
   float4 old[NP];
   d4 acc[NP];
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
-    old[i] = (needs_old && ((vmask >> i) & 1)) ? ld4(dst.out + col + 256 * i)
+    old[i] = (needs_old && ((vmask >> i) & 1)) ? ldw4<WB>(p, dst, col + 256 * i)
                                               : make_float4(0.f, 0.f, 0.f, 0.f);
     acc[i] = d4_zero();
   }
@@ -1887,7 +1983,7 @@ __device__ __forceinline__ void wide_item(const RedParams& p, const WideRun& m, 
 #pragma unroll
     for (int i = 0; i < NP; ++i)
       if ((vmask >> i) & 1)
-        st4(dst.out + col + 256 * i,
+        stw4<WB>(p, dst, col + 256 * i,
             round4((double)old[i].x - acc[i].x * mult, (double)old[i].y - acc[i].y * mult,
                    (double)old[i].z - acc[i].z * mult, (double)old[i].w - acc[i].w * mult));
     if (lane_id() == 0) *dst.mom = (float)mm;
@@ -1907,11 +2003,11 @@ __device__ __forceinline__ void wide_item(const RedParams& p, const WideRun& m, 
                  (double)old[i].w + a.w);
     else
       w = round4(a.x, a.y, a.z, a.w);
-    wide_st4(dst.out + col + 256 * i, w);
+    stw4<WB>(p, dst, col + 256 * i, w);
   }
 }
 
-template <int CPL, int UNR, bool BF16>
+template <int CPL, int UNR, bool BF16, bool WB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, SGB_WIDE_WAVES)))
 void k_reduce_wide(RedParams p) {
   const int64_t nw = (int64_t)gridDim.x * 4;
@@ -1925,7 +2021,7 @@ void k_reduce_wide(RedParams p) {
   for (; item < items; item += nw) {
     const WideRun m2 = wide_run(p, item + 2 * nw, items, ncb);
     const WideLane d1 = wide_lane(p, m1, 0);
-    wide_item<CPL, UNR, BF16>(p, m0, d0, (int)(item % ncb));
+    wide_item<CPL, UNR, BF16, WB>(p, m0, d0, (int)(item % ncb));
     m0 = m1;
     d0 = d1;
     m1 = m2;
@@ -2126,49 +2222,68 @@ hipError_t launch_fill(const FillParams& p, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Each reducer has an instance per (grad_output dtype, weight dtype): the
+// fp32-weight instances carry no bf16 rounding code (nor its registers).
+template <bool BF16, bool WB>
+void launch_long_t(const RedParams& p, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((k_reduce_long<BF16, WB>), dim3(grid), dim3(256), 0, s, p);
+}
+
 hipError_t launch_reduce_long(const RedParams& p, bool bf16, int grid, hipStream_t s) {
+  const bool wb = p.w_bf16 != 0;
   if (bf16)
-    hipLaunchKernelGGL(k_reduce_long<true>, dim3(grid), dim3(256), 0, s, p);
+    wb ? launch_long_t<true, true>(p, grid, s) : launch_long_t<true, false>(p, grid, s);
   else
-    hipLaunchKernelGGL(k_reduce_long<false>, dim3(grid), dim3(256), 0, s, p);
+    wb ? launch_long_t<false, true>(p, grid, s) : launch_long_t<false, false>(p, grid, s);
   return hipGetLastError();
 }
 
 // Row-wise Adagrad needs a whole row in one item: 16 columns per lane (rows
 // up to 1024); dense and SGD rows take SGB_WIDE_CPL columns per lane.
-template <bool BF16>
+template <bool BF16, bool WB>
 void launch_wide_t(RedParams q, bool adagrad, int dmax, const int* grid, hipStream_t s) {
   if (adagrad) {
     q.wide_ncb = (dmax + 1023) / 1024;
-    hipLaunchKernelGGL((k_reduce_wide<16, kWideUnr16, BF16>), dim3(grid[0]), dim3(256), 0, s, q);
+    hipLaunchKernelGGL((k_reduce_wide<16, kWideUnr16, BF16, WB>), dim3(grid[0]), dim3(256), 0, s,
+                       q);
   } else {
     q.wide_ncb = (dmax + 64 * kWideCpl - 1) / (64 * kWideCpl);
-    hipLaunchKernelGGL((k_reduce_wide<kWideCpl, kWideUnr, BF16>), dim3(grid[1]), dim3(256), 0, s,
-                       q);
+    hipLaunchKernelGGL((k_reduce_wide<kWideCpl, kWideUnr, BF16, WB>), dim3(grid[1]), dim3(256),
+                       0, s, q);
   }
 }
 
 void launch_reduce_wide(const RedParams& p, bool bf16, int dmax, const int* grid, hipStream_t s) {
   const bool adagrad = p.mode == kModeAdagrad;
+  const bool wb = p.w_bf16 != 0;
   if (bf16)
-    launch_wide_t<true>(p, adagrad, dmax, grid + 2, s);
+    wb ? launch_wide_t<true, true>(p, adagrad, dmax, grid + 2, s)
+       : launch_wide_t<true, false>(p, adagrad, dmax, grid + 2, s);
   else
-    launch_wide_t<false>(p, adagrad, dmax, grid, s);
+    wb ? launch_wide_t<false, true>(p, adagrad, dmax, grid, s)
+       : launch_wide_t<false, false>(p, adagrad, dmax, grid, s);
 }
 
-// Blocks per CU of the wide-row reducer instances, in the order
-// {fp32 Adagrad, fp32 other, bf16 Adagrad, bf16 other}.
+// Blocks per CU of the wide-row reducer instances (fp32 weights; the persistent
+// grid of the bf16-weight instances is the same), in the order
+// {fp32 Adagrad, fp32 other, bf16 Adagrad, bf16 other} of grad_output dtypes.
 void reduce_wide_blocks_per_cu(int out[4]) {
-  const void* k[4] = {reinterpret_cast<const void*>(k_reduce_wide<16, kWideUnr16, false>),
-                      reinterpret_cast<const void*>(k_reduce_wide<kWideCpl, kWideUnr, false>),
-                      reinterpret_cast<const void*>(k_reduce_wide<16, kWideUnr16, true>),
-                      reinterpret_cast<const void*>(k_reduce_wide<kWideCpl, kWideUnr, true>)};
+  const void* k[4] = {
+      reinterpret_cast<const void*>(k_reduce_wide<16, kWideUnr16, false, false>),
+      reinterpret_cast<const void*>(k_reduce_wide<kWideCpl, kWideUnr, false, false>),
+      reinterpret_cast<const void*>(k_reduce_wide<16, kWideUnr16, true, false>),
+      reinterpret_cast<const void*>(k_reduce_wide<kWideCpl, kWideUnr, true, false>)};
   for (int i = 0; i < 4; ++i) {
     int n = 0;
     out[i] = (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k[i], 256, 0) == hipSuccess && n > 0)
                  ? n
                  : 2;
   }
+}
+
+template <bool BF16, bool WB>
+void launch_short8_t(const RedParams& q, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((k_reduce_short8<BF16, WB>), grid, dim3(256), 0, s, q);
 }
 
 hipError_t launch_reduce_short(const RedParams& p, bool bf16, int dmin, int dmax,
@@ -2185,10 +2300,11 @@ hipError_t launch_reduce_short(const RedParams& p, bool bf16, int dmin, int dmax
     RedParams q = p;
     q.sub_log = sub_for(kShortSub8);
     const dim3 grid((unsigned)(((windows << q.sub_log) + 3) / 4), 1);
+    const bool wb = p.w_bf16 != 0;
     if (bf16)
-      hipLaunchKernelGGL(k_reduce_short8<true>, grid, dim3(256), 0, s, q);
+      wb ? launch_short8_t<true, true>(q, grid, s) : launch_short8_t<true, false>(q, grid, s);
     else
-      hipLaunchKernelGGL(k_reduce_short8<false>, grid, dim3(256), 0, s, q);
+      wb ? launch_short8_t<false, true>(q, grid, s) : launch_short8_t<false, false>(q, grid, s);
   }
   if (dmax > 512) launch_reduce_wide(p, bf16, dmax, wide_grid, s);
   return hipGetLastError();
@@ -2210,8 +2326,8 @@ hipError_t launch_forward(const FwdParams& p, hipStream_t s) {
 
 int reduce_long_blocks_per_cu(bool bf16) {
   int n = 0;
-  hipError_t e = bf16 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_reduce_long<true>, 256, 0)
-                      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_reduce_long<false>, 256, 0);
+  hipError_t e = bf16 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_reduce_long<true, false>, 256, 0)
+                      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_reduce_long<false, false>, 256, 0);
   return (e == hipSuccess && n > 0) ? n : 2;
 }
 

@@ -62,6 +62,8 @@ int main(void) {
   printf("sgb_update %zu\n", sizeof(sgb_update));
   F(sgb_update, mode); F(sgb_update, weights); F(sgb_update, momentum); F(sgb_update, grad);
   F(sgb_update, accumulate); F(sgb_update, lr); F(sgb_update, eps);
+  F(sgb_update, weights_dtype); F(sgb_update, stochastic_rounding); F(sgb_update, sr_seed);
+  F(sgb_update, sr_offset);
   printf("sgb_runs_view %zu\n", sizeof(sgb_runs_view));
   F(sgb_runs_view, sorted_packed); F(sgb_runs_view, info_bits); F(sgb_runs_view, unique_ids);
   F(sgb_runs_view, run_lengths); F(sgb_runs_view, cumulative); F(sgb_runs_view, num_runs);
