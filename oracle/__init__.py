@@ -73,9 +73,14 @@ def _lib(path: Optional[str] = None):
         lib.orc_bf16_round_array.restype = None
         lib.orc_update_rows_bf16.argtypes = [i32, i64, vp, i32, vp, f32, f32, vp, vp, vp, i32,
                                              u64, u32]
+        lib.orc_i8_quantize.argtypes = [vp, i64, i32, vp]
+        lib.orc_i8_quantize.restype = None
+        lib.orc_i8_dequantize.argtypes = [vp, i64, i32, vp]
+        lib.orc_i8_dequantize.restype = None
+        lib.orc_update_rows_int8.argtypes = [i32, i64, vp, i32, vp, f32, f32, vp, i32, vp]
         for f in (lib.orc_validate, lib.orc_linearize, lib.orc_runs,
                   lib.orc_row_grads, lib.orc_update_rows, lib.orc_forward,
-                  lib.orc_update_rows_bf16):
+                  lib.orc_update_rows_bf16, lib.orc_update_rows_int8):
             f.restype = ctypes.c_int
         _libs[path] = lib
     return _libs[path]
@@ -235,6 +240,41 @@ def update_rows_bf16(mode: str, G: np.ndarray, D: np.ndarray, rows0: np.ndarray,
                                           float(eps), _ptr(rows), _ptr(mom), _ptr(ids),
                                           1 if stochastic else 0, int(seed) & (2**64 - 1),
                                           int(offset) & 0xFFFFFFFF), "update_rows_bf16")
+    return rows, mom
+
+
+def i8_quantize(w: np.ndarray, lib: Optional[str] = None) -> np.ndarray:
+    """fp32 rows [n, D] -> INT8 rows [n, D + 8] (codes, then fp32 scale and bias)."""
+    w = np.ascontiguousarray(w, np.float32)
+    n, D = w.shape
+    rows = np.zeros((n, D + 8), np.uint8)
+    _lib(lib).orc_i8_quantize(_ptr(w), n, D, _ptr(rows))
+    return rows
+
+
+def i8_dequantize(rows: np.ndarray, lib: Optional[str] = None) -> np.ndarray:
+    """INT8 rows [n, D + 8] -> fp32 [n, D]."""
+    rows = np.ascontiguousarray(rows, np.uint8)
+    n, W = rows.shape
+    w = np.zeros((n, W - 8), np.float32)
+    _lib(lib).orc_i8_dequantize(_ptr(rows), n, W - 8, _ptr(w))
+    return w
+
+
+def update_rows_int8(mode: str, G: np.ndarray, D: np.ndarray, rows0: np.ndarray,
+                     mom0: Optional[np.ndarray], lr: float = 0.0, eps: float = 0.0,
+                     lib: Optional[str] = None):
+    """SGD / row-wise Adagrad on INT8 rows (uint8 [n, ldr], row k's D[k] codes
+    then its scale and bias); returns (rows uint8 [n, ldr], mom fp32 [n])."""
+    G = np.ascontiguousarray(G, np.float64)
+    n, ldg = G.shape
+    rows = np.ascontiguousarray(rows0, np.uint8).copy()
+    ldr = rows.shape[1]
+    mom = np.zeros(n, np.float32) if mom0 is None else np.ascontiguousarray(mom0, np.float32).copy()
+    D = np.ascontiguousarray(D, np.int32)
+    _check(_lib(lib).orc_update_rows_int8(MODE[mode], n, _ptr(D), ldg, _ptr(G), float(lr),
+                                          float(eps), _ptr(rows), ldr, _ptr(mom)),
+           "update_rows_int8")
     return rows, mom
 
 

@@ -573,3 +573,87 @@ int orc_update_rows_bf16(int32_t mode, int64_t nrows, const int32_t* D, int32_t 
   free(tmp);
   return st;
 }
+
+/* ------------------------------------------------------------------------ */
+/* INT8 row-wise quantized weight rows                                       */
+/* ------------------------------------------------------------------------ */
+
+/* The FBGEMM page keeps 8-bit rows with per-row quantization parameters
+ * stored in the row (row width D + kINT8QparamsBytes), loads the row with
+ * its parameters, and after the update computes new parameters from the
+ * updated row (`thrust_find_qparams`) before storing it [P1, split-kernel
+ * weight store]; the bodies are not printed.  Readings:
+ *  - a row is D uint8 codes followed by two fp32 values, scale then bias
+ *    (D + 8 bytes; D % 4 == 0, so the pair is 4-byte aligned);
+ *  - a code c stands for fmaf(c, scale, bias) (fp32, fused);
+ *  - the update is the fp32-row update (fp64, rounded once to fp32);
+ *  - new parameters: bias = min of the updated row, scale = (max - min) / 255
+ *    in fp32;
+ *  - code = rint((w - bias) / scale) (fp32 subtraction and division, round
+ *    half to even), clamped to [0, 255]; a constant row (scale 0) gets
+ *    code 0. */
+
+static float orc_i8_value(uint8_t c, float scale, float bias) {
+  return fmaf((float)c, scale, bias);
+}
+
+static void orc_i8_quantize_row(const float* w, int D, uint8_t* row) {
+  float mn = w[0], mx = w[0];
+  for (int d = 1; d < D; ++d) {
+    if (w[d] < mn) mn = w[d];
+    if (w[d] > mx) mx = w[d];
+  }
+  const float scale = (mx - mn) / 255.0f;
+  const float bias = mn;
+  for (int d = 0; d < D; ++d) {
+    float q = scale > 0.0f ? rintf((w[d] - bias) / scale) : 0.0f;
+    if (q < 0.0f) q = 0.0f;
+    if (q > 255.0f) q = 255.0f;
+    row[d] = (uint8_t)q;
+  }
+  memcpy(row + D, &scale, 4);
+  memcpy(row + D + 4, &bias, 4);
+}
+
+/* Quantizes n rows of D fp32 values into rows of D + 8 bytes. */
+void orc_i8_quantize(const float* w, int64_t n, int32_t D, uint8_t* rows) {
+  for (int64_t k = 0; k < n; ++k)
+    orc_i8_quantize_row(w + k * (int64_t)D, D, rows + k * (int64_t)(D + 8));
+}
+
+/* Dequantizes n rows of D + 8 bytes into D fp32 values each. */
+void orc_i8_dequantize(const uint8_t* rows, int64_t n, int32_t D, float* w) {
+  for (int64_t k = 0; k < n; ++k) {
+    const uint8_t* r = rows + k * (int64_t)(D + 8);
+    float scale, bias;
+    memcpy(&scale, r + D, 4);
+    memcpy(&bias, r + D + 4, 4);
+    for (int d = 0; d < D; ++d) w[k * (int64_t)D + d] = orc_i8_value(r[d], scale, bias);
+  }
+}
+
+/* SGD or row-wise Adagrad on INT8 rows: rows[k] holds row k's D[k] codes and
+ * its parameters at byte offset k * ldr (ldr >= D[k] + 8); the row is
+ * dequantized, updated as orc_update_rows does, and quantized again. */
+int orc_update_rows_int8(int32_t mode, int64_t nrows, const int32_t* D, int32_t ldg,
+                         const double* G, float lr, float eps, uint8_t* rows, int32_t ldr,
+                         float* mom) {
+  if (mode != ORC_SGD && mode != ORC_ROWWISE_ADAGRAD) return ORC_INVALID_ARGUMENT;
+  float* tmp = (float*)malloc(sizeof(float) * (size_t)(ldg > 0 ? ldg : 1));
+  if (tmp == NULL) return ORC_INVALID_ARGUMENT;
+  int st = ORC_OK;
+  for (int64_t k = 0; k < nrows && st == ORC_OK; ++k) {
+    const int Dk = D[k];
+    if (Dk <= 0 || Dk > ldg || Dk + 8 > ldr) {
+      st = ORC_INVALID_ARGUMENT;
+      break;
+    }
+    uint8_t* r = rows + k * (int64_t)ldr;
+    orc_i8_dequantize(r, 1, Dk, tmp);
+    st = orc_update_rows(mode, 0, 1, &D[k], ldg, G + k * (int64_t)ldg, lr, eps, tmp,
+                         mom ? &mom[k] : NULL);
+    if (st == ORC_OK) orc_i8_quantize_row(tmp, Dk, r);
+  }
+  free(tmp);
+  return st;
+}

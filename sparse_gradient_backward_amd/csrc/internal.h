@@ -67,6 +67,9 @@ constexpr int kMaxD = 8192;
 #ifndef SGB_FILL_CUS_PER_WG
 #define SGB_FILL_CUS_PER_WG 1
 #endif
+#ifndef SGB_FILL_THREADS
+#define SGB_FILL_THREADS 256
+#endif
 
 // sort pass tiling: items per thread of a tile, fewer for small batches
 // (more, shorter tiles fill the GPU and finish sooner) than for large ones
@@ -77,6 +80,9 @@ static_assert(kSortItemsSmall <= kSortItemsLarge, "small batches take the smalle
 __host__ __device__ inline int sort_items_for(int64_t N) {
   return N <= (int64_t)SGB_SORT_SMALL_N ? kSortItemsSmall : kSortItemsLarge;
 }
+
+// zero fill: threads of each (looping) workgroup
+constexpr int kFillThreads = SGB_FILL_THREADS;
 
 // run-length encoding / run post-processing tiling
 constexpr int kScanThreads = 256;

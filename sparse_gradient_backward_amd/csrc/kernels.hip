@@ -947,7 +947,7 @@ __global__ __launch_bounds__(kScanThreads) void k_post(PostParams p) {
 // while the ids are linearised and sorted; the reducers write the touched
 // rows after it.
 
-__global__ __launch_bounds__(256) void k_fill(FillParams p) {
+__global__ __launch_bounds__(kFillThreads) void k_fill(FillParams p) {
   // few workgroups, each looping over fill blocks: the fill saturates HBM
   // without holding the CU slots that the concurrent latency-bound kernels need
   for (int b = blockIdx.x; b < p.nblocks; b += gridDim.x) {
@@ -2218,7 +2218,7 @@ hipError_t launch_post(const PostParams& p, int grid, hipStream_t s) {
 }
 
 hipError_t launch_fill(const FillParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(k_fill, dim3(grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(k_fill, dim3(grid), dim3(kFillThreads), 0, s, p);
   return hipGetLastError();
 }
 
