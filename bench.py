@@ -296,6 +296,8 @@ def main():
     fwd = forward_measure(plan, inp, spec, indices, offsets, psw, out, ws, args.steps)
     bf16w = bf16_weights_measure(plan, spec, grad_output, indices, offsets, B, psw, out, mom, ws,
                                  args.steps, ms_per_step)
+    int8w = int8_weights_measure(plan, inp, spec, grad_output, indices, offsets, B, psw, mom, ws,
+                                 args.steps, ms_per_step)
     atomic = atomic_measure(inp, spec, grad_output, indices, offsets, psw, out,
                             min(args.steps, 20), ms_per_step)
 
@@ -364,6 +366,7 @@ def main():
                      "launch_ms": per_launch_ms},
         "forward": fwd,
         "bf16_weights": bf16w,
+        "int8_weights": int8w,
         "atomic_scatter": atomic,
         "cpu_baseline": cpu,
         "device_status": status,
@@ -445,6 +448,47 @@ def bf16_weights_measure(plan, spec, grad_output, indices, offsets, B, psw, out,
     del w, m
     return {"ms_per_step": ms, "stochastic_rounding": True, "vs_fp32_weights": ms / ms_path,
             "device_status": status}
+
+
+def int8_weights_measure(plan, inp, spec, grad_output, indices, offsets, B, psw, mom, ws, steps,
+                         ms_path):
+    """The same step with INT8 row-wise quantized weight rows (SGD and
+    row-wise Adagrad workloads with rows up to 1024 wide): synthetic rows
+    made on the device (codes uniform in [0, 255], scale 0.02 / 255, bias
+    -0.01, so values span [-0.01, 0.01]), `steps` plain calls timed by HIP
+    events."""
+    D = np.diff(inp.D_offsets).astype(np.int64)
+    if spec.mode == "dense" or int(D.max()) > 1024:
+        return None
+    E = np.diff(inp.hash_size_cumsum).astype(np.int64)
+    woff8 = np.concatenate([[0], np.cumsum(E * (D + 8))])
+    dev = grad_output.device
+    g = torch.Generator(device=dev)
+    g.manual_seed(spec.seed + 8)
+    w = torch.randint(0, 256, (int(woff8[-1]),), dtype=torch.uint8, device=dev, generator=g)
+    qp = torch.tensor([0.02 / 255.0, -0.01], dtype=torch.float32, device=dev).view(torch.uint8)
+    for t in range(inp.T):
+        rows = w[int(woff8[t]):int(woff8[t + 1])].view(int(E[t]), int(D[t]) + 8)
+        rows[:, int(D[t]):] = qp
+    m = None if mom is None else mom.clone()
+
+    def call():
+        plan.backward(grad_output, indices, offsets, B, psw, spec.mode, weights=w, momentum=m,
+                      lr=spec.lr, eps=spec.eps, workspace=ws)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    status = plan.device_status(ws)
+    del w, m
+    return {"ms_per_step": ms, "vs_fp32_weights": ms / ms_path, "device_status": status}
 
 
 def atomic_measure(inp, spec, grad_output, indices, offsets, psw, out, calls, ms_path) -> dict:

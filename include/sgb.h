@@ -71,8 +71,9 @@ typedef enum {
  * nobag variant.  SGB_POOL_NONE is the nobag (per-token) case. */
 typedef enum { SGB_POOL_SUM = 0, SGB_POOL_MEAN = 1, SGB_POOL_NONE = 2 } sgb_pooling;
 
-/* Element type of grad_output. */
-typedef enum { SGB_F32 = 0, SGB_BF16 = 1 } sgb_dtype;
+/* Element type of grad_output (F32, BF16) and of weight rows (F32, BF16,
+ * INT8: row-wise quantized rows, weights only). */
+typedef enum { SGB_F32 = 0, SGB_BF16 = 1, SGB_INT8 = 2 } sgb_dtype;
 
 /* Output mode, FBTT page OPTIM_{SGD, ADAGRAD, DENSE} (Adagrad is row-wise). */
 typedef enum { SGB_DENSE_GRAD = 0, SGB_SGD = 1, SGB_ROWWISE_ADAGRAD = 2 } sgb_mode;
@@ -136,7 +137,10 @@ typedef struct {
   int32_t mode;      /* an sgb_mode value                                        */
   void* weights;     /* SGD / Adagrad: flat rows of weights_dtype elements, table
                         t row i at element woff[t] + i * D_t with
-                        woff[t] = sum_{t'<t} E_t' * D_t'                         */
+                        woff[t] = sum_{t'<t} E_t' * D_t'; INT8: table t row i
+                        at byte woff8[t] + i * (D_t + 8) with woff8[t] =
+                        sum_{t'<t} E_t' * (D_t' + 8), the row's D_t uint8
+                        codes followed by its fp32 scale and fp32 bias       */
   float* momentum;   /* Adagrad: fp32[sum_t E_t], one value per row, indexed by
                         linear id hsc[t] + i                                      */
   float* grad;       /* DENSE: fp32, same layout as weights                       */
@@ -148,8 +152,18 @@ typedef struct {
   /* 16-bit weights (FBGEMM page, split-kernel weight store: a 16-bit row is
      stored with stochastic rounding from a Philox state seeded per call).
      A zero-initialised tail keeps fp32 weights.                               */
-  int32_t weights_dtype;       /* SGB_F32, or SGB_BF16 (SGD / Adagrad only;
-                                  DENSE with SGB_BF16 is SGB_ERR_UNSUPPORTED)  */
+  int32_t weights_dtype;       /* SGB_F32, SGB_BF16 or SGB_INT8 (the last two
+                                  SGD / Adagrad only: with DENSE they are
+                                  SGB_ERR_UNSUPPORTED).  INT8 rows (FBGEMM
+                                  page: 8-bit rows carry their quantization
+                                  parameters, recomputed from the updated row)
+                                  need every D_t <= 1024 (else
+                                  SGB_ERR_UNSUPPORTED): code c stands for
+                                  fmaf(c, scale, bias); after the fp32-row
+                                  update, bias = row min, scale = (max - min)
+                                  / 255, code = rint((w - bias) / scale)
+                                  clamped to [0, 255] (0 if scale is 0), fp32
+                                  arithmetic with correctly rounded division */
   int32_t stochastic_rounding; /* bf16: 1 = stochastic, 0 = nearest even.  The
                                   updated value is formed in fp32 as for fp32
                                   rows, then element (linear id r, column d)

@@ -48,7 +48,7 @@ if len(_hip_runtimes()) > 1:
 SGB_OK, SGB_ERR_INVALID_ARGUMENT, SGB_ERR_UNSUPPORTED, SGB_ERR_WORKSPACE_TOO_SMALL, \
     SGB_ERR_INDEX_OUT_OF_RANGE, SGB_ERR_BAD_OFFSETS, SGB_ERR_HIP, SGB_ERR_INTERNAL = range(8)
 POOLING = {"sum": 0, "mean": 1, "none": 2}
-DTYPE = {"f32": 0, "bf16": 1}
+DTYPE = {"f32": 0, "bf16": 1, "int8": 2}
 MODE = {"dense": 0, "sgd": 1, "rowwise_adagrad": 2}
 
 
@@ -176,7 +176,8 @@ def sgb_backward(plan: int, grad_output, indices, offsets, B: int, per_sample_we
     float32 or bfloat16, indices/offsets int64, per_sample_weights float32;
     weights float32, or bfloat16 (SGD / row-wise Adagrad) rounded to nearest
     even or, with stochastic_rounding, stochastically from (sr_seed,
-    sr_offset).
+    sr_offset), or uint8 INT8 rows (SGD / row-wise Adagrad: each row its D
+    codes then fp32 scale and bias, tables back to back).
     `events`, if given, is a list of 2 * len(STAGES) recorded-once
     torch.cuda.Event(enable_timing=True) objects (or None entries) that the
     library records around each stage (sgb_backward_timed)."""
@@ -185,7 +186,7 @@ def sgb_backward(plan: int, grad_output, indices, offsets, B: int, per_sample_we
     for name, t, dt in (("indices", indices, torch.int64), ("offsets", offsets, torch.int64),
                         ("per_sample_weights", per_sample_weights, torch.float32),
                         ("weights", weights, weights.dtype if weights is not None and
-                         weights.dtype == torch.bfloat16 else torch.float32),
+                         weights.dtype in (torch.bfloat16, torch.uint8) else torch.float32),
                         ("momentum", momentum, torch.float32),
                         ("grad", grad, torch.float32)):
         if t is not None and (t.dtype != dt or not t.is_contiguous()):
@@ -194,9 +195,10 @@ def sgb_backward(plan: int, grad_output, indices, offsets, B: int, per_sample_we
         raise SgbError(SGB_ERR_INVALID_ARGUMENT, "sgb_backward: grad_output must be contiguous")
     batch = _Batch(_ptr(grad_output), DTYPE[gd], _ptr(indices), int(indices.numel()),
                    _ptr(offsets), int(B), _ptr(per_sample_weights))
-    w_bf16 = weights is not None and weights.dtype == torch.bfloat16
+    wdt = {torch.bfloat16: "bf16", torch.uint8: "int8"}.get(
+        weights.dtype if weights is not None else None, "f32")
     upd = _Update(MODE[mode], _ptr(weights), _ptr(momentum), _ptr(grad), 1 if accumulate else 0,
-                  float(lr), float(eps), DTYPE["bf16"] if w_bf16 else DTYPE["f32"],
+                  float(lr), float(eps), DTYPE[wdt],
                   1 if stochastic_rounding else 0, int(sr_seed) & (2**64 - 1),
                   int(sr_offset) & (2**64 - 1))
     ws_ptr = _ptr(workspace)

@@ -35,11 +35,12 @@ struct sgb_plan_s {
   int64_t total_rows = 0;   // sum of E_t
   int64_t total_elems = 0;  // sum of E_t * D_t
   int key_bits = 0;
-  std::vector<int64_t> hsc, woff;
+  std::vector<int64_t> hsc, woff, woff8;
   std::vector<int32_t> doff;
   int64_t* d_hsc = nullptr;
   int32_t* d_doff = nullptr;
   int64_t* d_woff = nullptr;
+  int64_t* d_woff8 = nullptr;  // byte offsets of INT8 weight tables
   FillBlock* d_fill = nullptr;
   int32_t n_fill = 0;
   int num_cus = 1;
@@ -232,6 +233,7 @@ sgb_status sgb_plan_create(sgb_plan* out, int32_t T, const int64_t* hsc, const i
   p->hsc.assign(hsc, hsc + T + 1);
   p->doff.assign(doff, doff + T + 1);
   p->woff.assign(T + 1, 0);
+  p->woff8.assign(T + 1, 0);
   std::vector<FillBlock> fill;
   for (int32_t t = 0; t < T; ++t) {
     const int64_t E = hsc[t + 1] - hsc[t];
@@ -244,6 +246,7 @@ sgb_status sgb_plan_create(sgb_plan* out, int32_t T, const int64_t* hsc, const i
       p->items_den = den;
     }
     p->woff[t + 1] = p->woff[t] + E * D;
+    p->woff8[t + 1] = p->woff8[t] + E * (D + 8);
     const int64_t rows_per = std::max<int64_t>(1, 16384 / D);
     for (int64_t r0 = 0; r0 < E; r0 += rows_per)
       fill.push_back(FillBlock{t, (int32_t)std::min<int64_t>(rows_per, E - r0), r0});
@@ -270,12 +273,15 @@ sgb_status sgb_plan_create(sgb_plan* out, int32_t T, const int64_t* hsc, const i
   ok = ok && hipMalloc(&p->d_hsc, sizeof(int64_t) * (T + 1)) == hipSuccess &&
             hipMalloc(&p->d_doff, sizeof(int32_t) * (T + 1)) == hipSuccess &&
             hipMalloc(&p->d_woff, sizeof(int64_t) * (T + 1)) == hipSuccess &&
+            hipMalloc(&p->d_woff8, sizeof(int64_t) * (T + 1)) == hipSuccess &&
             hipMalloc(&p->d_fill, sizeof(FillBlock) * fill.size()) == hipSuccess;
   ok = ok && hipMemcpy(p->d_hsc, p->hsc.data(), sizeof(int64_t) * (T + 1),
                        hipMemcpyHostToDevice) == hipSuccess;
   ok = ok && hipMemcpy(p->d_doff, p->doff.data(), sizeof(int32_t) * (T + 1),
                        hipMemcpyHostToDevice) == hipSuccess;
   ok = ok && hipMemcpy(p->d_woff, p->woff.data(), sizeof(int64_t) * (T + 1),
+                       hipMemcpyHostToDevice) == hipSuccess;
+  ok = ok && hipMemcpy(p->d_woff8, p->woff8.data(), sizeof(int64_t) * (T + 1),
                        hipMemcpyHostToDevice) == hipSuccess;
   ok = ok && hipMemcpy(p->d_fill, fill.data(), sizeof(FillBlock) * fill.size(),
                        hipMemcpyHostToDevice) == hipSuccess;
@@ -293,6 +299,7 @@ void sgb_plan_destroy(sgb_plan p) {
   if (p->d_hsc) (void)hipFree(p->d_hsc);
   if (p->d_doff) (void)hipFree(p->d_doff);
   if (p->d_woff) (void)hipFree(p->d_woff);
+  if (p->d_woff8) (void)hipFree(p->d_woff8);
   if (p->d_fill) (void)hipFree(p->d_fill);
   for (hipEvent_t e : p->ev)
     if (e) (void)hipEventDestroy(e);
@@ -335,12 +342,15 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   if (u->mode == SGB_ROWWISE_ADAGRAD && (!u->weights || !u->momentum))
     return SGB_ERR_INVALID_ARGUMENT;
   if (u->mode == SGB_ROWWISE_ADAGRAD && p->Dmax > kMaxCb * kColBlock) return SGB_ERR_UNSUPPORTED;
-  if (u->weights_dtype != SGB_F32 && u->weights_dtype != SGB_BF16) return SGB_ERR_INVALID_ARGUMENT;
+  if (u->weights_dtype != SGB_F32 && u->weights_dtype != SGB_BF16 && u->weights_dtype != SGB_INT8)
+    return SGB_ERR_INVALID_ARGUMENT;
+  if (u->mode == SGB_DENSE_GRAD && u->weights_dtype != SGB_F32) return SGB_ERR_UNSUPPORTED;
   const bool w_bf16 = u->mode != SGB_DENSE_GRAD && u->weights_dtype == SGB_BF16;
-  if (u->mode == SGB_DENSE_GRAD && u->weights_dtype == SGB_BF16) return SGB_ERR_UNSUPPORTED;
+  const bool w_int8 = u->mode != SGB_DENSE_GRAD && u->weights_dtype == SGB_INT8;
+  if (w_int8 && p->Dmax > kMaxCb * kColBlock) return SGB_ERR_UNSUPPORTED;
   void* outv = u->mode == SGB_DENSE_GRAD ? static_cast<void*>(u->grad) : u->weights;
   if (!aligned(outv, 16)) return SGB_ERR_INVALID_ARGUMENT;
-  float* out = w_bf16 ? nullptr : static_cast<float*>(outv);
+  float* out = (w_bf16 || w_int8) ? nullptr : static_cast<float*>(outv);
   const bool fresh = u->mode == SGB_DENSE_GRAD && !u->accumulate;
   DeviceGuard guard(p->device);
   if (!guard.ok) return SGB_ERR_HIP;
@@ -509,7 +519,9 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   q.partials = at<double>(ws, L.part);
   q.out = out;
   q.out_h = w_bf16 ? static_cast<uint16_t*>(outv) : nullptr;
-  q.w_bf16 = w_bf16 ? 1 : 0;
+  q.out_q = w_int8 ? static_cast<uint8_t*>(outv) : nullptr;
+  q.woff8 = p->d_woff8;
+  q.w_kind = w_int8 ? 2 : (w_bf16 ? 1 : 0);
   q.sr = (w_bf16 && u->stochastic_rounding) ? 1 : 0;
   q.sr_key0 = (uint32_t)u->sr_seed;
   q.sr_key1 = (uint32_t)(u->sr_seed >> 32);

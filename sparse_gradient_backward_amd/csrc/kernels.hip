@@ -1084,30 +1084,32 @@ __device__ __forceinline__ int grad_row_of(const RedParams& p, uint32_t info, in
 __device__ __forceinline__ float4 ld4(const float* q) { return *reinterpret_cast<const float4*>(q); }
 __device__ __forceinline__ void st4(float* q, float4 v) { *reinterpret_cast<float4*>(q) = v; }
 
+// Weight kinds of the reducer instances: fp32 rows (or a dense gradient),
+// bf16 rows, INT8 rows (codes then the row's fp32 scale and bias).
+constexpr int kWF32 = 0, kWBF16 = 1, kWINT8 = 2;
+
 struct RowDst {
-  void* out;    // the row's first element: fp32, or bf16 weights
+  void* out;    // the row's first element (fp32 / bf16) or first byte (INT8)
   float* mom;   // its Adagrad state
   int64_t lin;  // its linear id (the stochastic-rounding counter)
+  int32_t D;    // its width (INT8: the parameters follow the D codes)
 };
 
-// The output row of element offset e (WB: bf16 weights).
-template <bool WB>
-__device__ __forceinline__ void* row_ptr(const RedParams& p, int64_t e) {
-  if constexpr (WB)
-    return p.out_h + e;
-  else
-    return p.out + e;
-}
-
-template <bool WB>
+template <int WK>
 __device__ __forceinline__ RowDst row_dest(const RedParams& p, int t, int D, int64_t lin) {
   const int64_t h0 = p.hsc[t], E = p.hsc[t + 1] - h0;
   int64_t row = lin - h0;
   row = row < 0 ? 0 : (row < E ? row : E - 1);
   RowDst d;
-  d.out = row_ptr<WB>(p, p.woff[t] + row * (int64_t)D);
+  if constexpr (WK == kWINT8)
+    d.out = p.out_q + p.woff8[t] + row * (int64_t)(D + 8);
+  else if constexpr (WK == kWBF16)
+    d.out = p.out_h + p.woff[t] + row * (int64_t)D;
+  else
+    d.out = p.out + p.woff[t] + row * (int64_t)D;
   d.mom = p.mom ? p.mom + h0 + row : nullptr;
   d.lin = h0 + row;
+  d.D = D;
   return d;
 }
 
@@ -1165,22 +1167,38 @@ __device__ __forceinline__ uint32_t bf16_sr(float x, uint32_t rnd) {
 // widened exactly.  The address is formed as (row + col) + off: the
 // short-run reducer keeps row + col across its pieces, and forming
 // row + (col + off) instead costs it a register (and a spill).
-template <bool WB>
+template <int WK>
 __device__ __forceinline__ float4 ldw4(const RedParams& p, const RowDst& d, int col, int off = 0) {
-  if constexpr (!WB) return ld4(static_cast<const float*>(d.out) + col + off);
-  const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(d.out) + col + off);
-  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+  if constexpr (WK == kWF32) {
+    return ld4(static_cast<const float*>(d.out) + col + off);
+  } else if constexpr (WK == kWBF16) {
+    const uint2 u =
+        *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(d.out) + col + off);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+  } else {
+    // code c stands for fmaf(c, scale, bias)
+    const uint8_t* r = static_cast<const uint8_t*>(d.out);
+    const uint32_t c = *reinterpret_cast<const uint32_t*>(r + col + off);
+    const float scale = *reinterpret_cast<const float*>(r + d.D);
+    const float bias = *reinterpret_cast<const float*>(r + d.D + 4);
+    return make_float4(fmaf((float)(c & 0xffu), scale, bias),
+                       fmaf((float)((c >> 8) & 0xffu), scale, bias),
+                       fmaf((float)((c >> 16) & 0xffu), scale, bias),
+                       fmaf((float)(c >> 24), scale, bias));
+  }
 }
 
 // Stores the row's new values at columns [col, col+4) (col % 4 == 0).
-template <bool WB>
+template <int WK>
 __device__ __forceinline__ void stw4(const RedParams& p, const RowDst& d, int col, float4 v,
                                      int off = 0) {
-  if constexpr (!WB) {
+  if constexpr (WK == kWINT8) {
+    return;  // never reached: INT8 rows are requantized whole (store_codes4)
+  } else if constexpr (WK == kWF32) {
     st4(static_cast<float*>(d.out) + col + off, v);
     return;
-  }
+  } else {
   col += off;
   uint32_t h0, h1, h2, h3;
   if (p.sr) {
@@ -1199,6 +1217,64 @@ __device__ __forceinline__ void stw4(const RedParams& p, const RowDst& d, int co
   }
   *reinterpret_cast<uint2*>(static_cast<uint16_t*>(d.out) + col) =
       make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+  }
+}
+
+// ---- INT8 weight rows
+//
+// The FBGEMM page keeps 8-bit rows with their quantization parameters in the
+// row, loads a row with its parameters and, after the update, finds new
+// parameters from the updated row before storing it (bodies not printed).
+// Here a row is its D codes followed by fp32 scale and bias; code c stands
+// for fmaf(c, scale, bias).  After the update (fp64, rounded once to fp32,
+// as for fp32 rows) the new bias is the row's minimum, the new scale
+// (max - min) / 255, and each code rint((w - bias) / scale) clamped to
+// [0, 255] (0 for a constant row), all in fp32 with correctly rounded
+// division.  A row is served whole by one lane group, so the minimum and
+// maximum are a group reduction.
+
+__device__ __forceinline__ float group_min(float x, int lpl) {
+  for (int off = lpl / 2; off > 0; off >>= 1) x = fminf(x, __shfl_xor(x, off, 64));
+  return x;
+}
+
+__device__ __forceinline__ float group_max(float x, int lpl) {
+  for (int off = lpl / 2; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+  return x;
+}
+
+__device__ __forceinline__ void minmax4(const float4& v, float& mn, float& mx) {
+  mn = fminf(fminf(mn, v.x), fminf(fminf(v.y, v.z), v.w));
+  mx = fmaxf(fmaxf(mx, v.x), fmaxf(fmaxf(v.y, v.z), v.w));
+}
+
+__device__ __forceinline__ uint32_t code_of(float w, float scale, float bias) {
+  if (!(scale > 0.f)) return 0u;
+  const float q = __builtin_rintf(__fdiv_rn(w - bias, scale));
+  return (uint32_t)fminf(fmaxf(q, 0.f), 255.f);
+}
+
+// Codes of 4 values, packed little-endian (column col + k in byte k).
+__device__ __forceinline__ uint32_t codes4(const float4& v, float scale, float bias) {
+  return code_of(v.x, scale, bias) | (code_of(v.y, scale, bias) << 8) |
+         (code_of(v.z, scale, bias) << 16) | (code_of(v.w, scale, bias) << 24);
+}
+
+// New parameters of a row from its lanes' partial minimum and maximum.
+__device__ __forceinline__ float2 qparams_of(float mn, float mx, int lpl) {
+  mn = group_min(mn, lpl);
+  mx = group_max(mx, lpl);
+  return make_float2(__fdiv_rn(mx - mn, 255.0f), mn);
+}
+
+__device__ __forceinline__ void store_codes4(const RowDst& d, int col, const float4& v, float2 qp) {
+  *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(d.out) + col) = codes4(v, qp.x, qp.y);
+}
+
+__device__ __forceinline__ void store_qparams(const RowDst& d, float2 qp) {
+  uint8_t* r = static_cast<uint8_t*>(d.out);
+  *reinterpret_cast<float*>(r + d.D) = qp.x;
+  *reinterpret_cast<float*>(r + d.D + 4) = qp.y;
 }
 
 // Lane groups of a long-run item: lpl lanes per group (the power of two
@@ -1335,13 +1411,59 @@ __device__ __forceinline__ float4 round4(double x, double y, double z, double w)
 // `cache_backward_sgd_kernel`).  Dense: store, or add for an accumulating
 // grad_weight (tinygrad `_embedding_bwd_kernel`).  The old row value is read
 // before getG so that the read overlaps the gather.
-template <bool WB, class F>
+template <int WK, class F>
 __device__ __forceinline__ void finish_row(const RedParams& p, const Groups& G, const RowDst& dst,
                                            int D, bool write, int cb_lo, int cb_hi, F&& getG) {
   const int lig = G.lig;
+  if constexpr (WK == kWINT8) {
+    // the whole row: the step (Adagrad: the mean square over every block
+    // first), the new values' range, then the codes
+    const int ncb = col_blocks(D);
+    const bool adagrad = p.mode == kModeAdagrad;
+    const float m0 = (write && adagrad) ? *dst.mom : 0.f;
+    double mult = (double)p.lr, m = 0.0;
+    if (adagrad) {
+      double ss = 0.0;
+#pragma unroll 1
+      for (int cb = 0; cb < ncb; ++cb) {
+        const d4 g = getG(cb);
+        if (cb * kColBlock + 4 * lig < D) ss += d4_sumsq(g);
+      }
+      ss = group_sum(ss, G.lpl);
+      m = (double)m0 + ss / (double)D;
+      mult = (double)p.lr / (sqrt(m) + (double)p.eps);
+    }
+    float mn = INFINITY, mx = -INFINITY;
+#pragma unroll 1
+    for (int cb = 0; cb < ncb; ++cb) {
+      const int col = cb * kColBlock + 4 * lig;
+      const d4 g = getG(cb);
+      if (col < D) {
+        const float4 o = write ? ldw4<WK>(p, dst, col) : make_float4(0.f, 0.f, 0.f, 0.f);
+        minmax4(round4((double)o.x - g.x * mult, (double)o.y - g.y * mult,
+                       (double)o.z - g.z * mult, (double)o.w - g.w * mult), mn, mx);
+      }
+    }
+    const float2 qp = qparams_of(mn, mx, G.lpl);
+#pragma unroll 1
+    for (int cb = 0; cb < ncb; ++cb) {
+      const int col = cb * kColBlock + 4 * lig;
+      const d4 g = getG(cb);
+      if (write && col < D) {
+        const float4 o = ldw4<WK>(p, dst, col);
+        store_codes4(dst, col, round4((double)o.x - g.x * mult, (double)o.y - g.y * mult,
+                                      (double)o.z - g.z * mult, (double)o.w - g.w * mult), qp);
+      }
+    }
+    if (write && lig == 0) {
+      store_qparams(dst, qp);
+      if (adagrad) *dst.mom = (float)m;
+    }
+    return;
+  } else {
   if (p.mode == kModeAdagrad) {
     const bool w0ok = write && 4 * lig < D;
-    const float4 w0 = w0ok ? ldw4<WB>(p, dst, 4 * lig) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 w0 = w0ok ? ldw4<WK>(p, dst, 4 * lig) : make_float4(0.f, 0.f, 0.f, 0.f);
     const float m0 = write ? *dst.mom : 0.f;
     const int ncb = col_blocks(D);
     const d4 g0 = getG(0);
@@ -1356,15 +1478,15 @@ __device__ __forceinline__ void finish_row(const RedParams& p, const Groups& G, 
     const double m = (double)m0 + ss / (double)D;
     const double mult = (double)p.lr / (sqrt(m) + (double)p.eps);
     if (w0ok)
-      stw4<WB>(p, dst, 4 * lig, round4((double)w0.x - g0.x * mult, (double)w0.y - g0.y * mult,
+      stw4<WK>(p, dst, 4 * lig, round4((double)w0.x - g0.x * mult, (double)w0.y - g0.y * mult,
                                     (double)w0.z - g0.z * mult, (double)w0.w - g0.w * mult));
 #pragma unroll 1
     for (int cb = 1; cb < ncb; ++cb) {
       const d4 g = getG(cb);
       const int col = cb * kColBlock + 4 * lig;
       if (write && col < D) {
-        const float4 wv = ldw4<WB>(p, dst, col);
-        stw4<WB>(p, dst, col, round4((double)wv.x - g.x * mult, (double)wv.y - g.y * mult,
+        const float4 wv = ldw4<WK>(p, dst, col);
+        stw4<WK>(p, dst, col, round4((double)wv.x - g.x * mult, (double)wv.y - g.y * mult,
                                   (double)wv.z - g.z * mult, (double)wv.w - g.w * mult));
       }
     }
@@ -1377,7 +1499,7 @@ __device__ __forceinline__ void finish_row(const RedParams& p, const Groups& G, 
   for (int cb = cb_lo; cb < cb_hi; ++cb) {
     const int col = cb * kColBlock + 4 * lig;
     const bool ok = write && col < D;
-    const float4 old = (ok && needs_old) ? ldw4<WB>(p, dst, col) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 old = (ok && needs_old) ? ldw4<WK>(p, dst, col) : make_float4(0.f, 0.f, 0.f, 0.f);
     const d4 g = getG(cb);
     if (!ok) continue;
     float4 wv;
@@ -1389,7 +1511,8 @@ __device__ __forceinline__ void finish_row(const RedParams& p, const Groups& G, 
                   (double)old.w + g.w);
     else
       wv = round4(g.x, g.y, g.z, g.w);
-    stw4<WB>(p, dst, col, wv);
+    stw4<WK>(p, dst, col, wv);
+  }
   }
 }
 
@@ -1397,19 +1520,40 @@ __device__ __forceinline__ void finish_row(const RedParams& p, const Groups& G, 
 // columns, fp64) is complete, from the old values `old` (and Adagrad state
 // m0) read before g was gathered.  Row-wise Adagrad here covers a row of one
 // block; wider rows take finish_row.
-template <bool WB>
+template <int WK>
 __device__ __forceinline__ void update_block(const RedParams& p, const Groups& G, const RowDst& dst,
                                              int D, bool write, int cb, const float4& old, float m0,
                                              const d4& g) {
   const int lig = G.lig;
   const int col = cb * kColBlock + 4 * lig;
   const bool ok = write && col < D;
+  if constexpr (WK == kWINT8) {
+    // a row of one block: the step, the range over the group, the codes
+    const bool adagrad = p.mode == kModeAdagrad;
+    double mult = (double)p.lr, m = 0.0;
+    if (adagrad) {
+      const double ss = group_sum(col < D ? d4_sumsq(g) : 0.0, G.lpl);
+      m = (double)m0 + ss / (double)D;
+      mult = (double)p.lr / (sqrt(m) + (double)p.eps);
+    }
+    const float4 nw = round4((double)old.x - g.x * mult, (double)old.y - g.y * mult,
+                             (double)old.z - g.z * mult, (double)old.w - g.w * mult);
+    float mn = INFINITY, mx = -INFINITY;
+    if (col < D) minmax4(nw, mn, mx);
+    const float2 qp = qparams_of(mn, mx, G.lpl);
+    if (ok) store_codes4(dst, col, nw, qp);
+    if (write && lig == 0) {
+      store_qparams(dst, qp);
+      if (adagrad) *dst.mom = (float)m;
+    }
+    return;
+  }
   if (p.mode == kModeAdagrad) {
     const double ss = group_sum(col < D ? d4_sumsq(g) : 0.0, G.lpl);
     const double m = (double)m0 + ss / (double)D;
     const double mult = (double)p.lr / (sqrt(m) + (double)p.eps);
     if (ok)
-      stw4<WB>(p, dst, col, round4((double)old.x - g.x * mult, (double)old.y - g.y * mult,
+      stw4<WK>(p, dst, col, round4((double)old.x - g.x * mult, (double)old.y - g.y * mult,
                                 (double)old.z - g.z * mult, (double)old.w - g.w * mult));
     if (write && lig == 0) *dst.mom = (float)m;
     return;
@@ -1425,7 +1569,7 @@ __device__ __forceinline__ void update_block(const RedParams& p, const Groups& G
   } else {
     wv = round4(g.x, g.y, g.z, g.w);
   }
-  stw4<WB>(p, dst, col, wv);
+  stw4<WK>(p, dst, col, wv);
 }
 // Partials travel between waves on different XCDs.  They are written and read
 // with device-scope (agent) atomic accesses, which the hardware keeps coherent
@@ -1505,7 +1649,23 @@ __device__ __forceinline__ d4 sum_slots(const RedParams& p, const Groups& G, uin
   return fold_groups(acc, G.lpl);
 }
 
-template <bool BF16, bool WB>
+// The output row of a long run.
+template <int WK>
+__device__ __forceinline__ RowDst long_row(const RedParams& p, const LongRun& rec) {
+  RowDst d;
+  if constexpr (WK == kWINT8)
+    d.out = p.out_q + p.woff8[rec.t] + (rec.mom - p.hsc[rec.t]) * (int64_t)(rec.D + 8);
+  else if constexpr (WK == kWBF16)
+    d.out = p.out_h + rec.out;
+  else
+    d.out = p.out + rec.out;
+  d.mom = p.mom ? p.mom + rec.mom : nullptr;
+  d.lin = rec.mom;
+  d.D = rec.D;
+  return d;
+}
+
+template <bool BF16, int WK>
 __device__ __forceinline__ void long_item(const RedParams& p, const LongRun& rec, int c, int cb) {
   const int t = rec.t, start = rec.start, len = rec.len, D = rec.D;
   const Groups G = groups_of(lanes_per_row(D));
@@ -1517,10 +1677,11 @@ __device__ __forceinline__ void long_item(const RedParams& p, const LongRun& rec
   const int hi = min(lo + chl, start + len);
   // Adagrad needs the whole row in one wave: item cb 0 covers every block
   const bool adagrad = p.mode == kModeAdagrad;
-  const int cb_lo = adagrad ? 0 : cb;
-  const int cb_hi = adagrad ? ncb : cb + 1;
+  const bool whole = adagrad || WK == kWINT8;  // INT8 rows are requantized whole
+  const int cb_lo = whole ? 0 : cb;
+  const int cb_hi = whole ? ncb : cb + 1;
   const int64_t gcol = rec.gcol;
-  const RowDst dst{row_ptr<WB>(p, rec.out), p.mom ? p.mom + rec.mom : nullptr, rec.mom};
+  const RowDst dst = long_row<WK>(p, rec);
   // each lane group takes a contiguous share of the chunk, so that the
   // adjacent lookups of one bag stay together for merging
   const int per = (hi - lo + ng - 1) / ng;
@@ -1532,7 +1693,7 @@ __device__ __forceinline__ void long_item(const RedParams& p, const LongRun& rec
   // row of one block) updates the row itself; otherwise each block's sum is
   // this item's partial.  One gather site keeps the register budget that of
   // a single gather loop.
-  const bool direct = nch == 1 && (!adagrad || ncb == 1);
+  const bool direct = nch == 1 && (!whole || ncb == 1);
   const bool needs_old = p.mode != kModeDense || p.accumulate;
   const uint32_t cbeg = rec.cbeg;
 #pragma unroll 1
@@ -1541,12 +1702,12 @@ __device__ __forceinline__ void long_item(const RedParams& p, const LongRun& rec
     const bool col_ok = col < D;
     // the old row (and state) is read before the gather so the two overlap
     const bool rd = direct && g == 0 && col_ok && needs_old;
-    const float4 old = rd ? ldw4<WB>(p, dst, col) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 old = rd ? ldw4<WK>(p, dst, col) : make_float4(0.f, 0.f, 0.f, 0.f);
     const float mom0 = (direct && adagrad && g == 0) ? *dst.mom : 0.f;
     const d4 a = fold_groups(
         gather_merged<SGB_LONG_UNR, BF16>(p, G, glo, ghi, slices, t, gcol + col, col_ok, q), G.lpl);
     if (direct)
-      update_block<WB>(p, G, dst, D, g == 0, cbx, old, mom0, a);
+      update_block<WK>(p, G, dst, D, g == 0, cbx, old, mom0, a);
     else if (g == 0 && col_ok)
       store_partial(slot_of(p, cbeg, c, ncb, cbx) + 4 * lig, a);
   }
@@ -1556,7 +1717,7 @@ __device__ __forceinline__ void long_item(const RedParams& p, const LongRun& rec
   if (!ticket_last(p.sc_ticket + cbeg + (int64_t)m0 * ncb + cb_lo, (uint32_t)members)) return;
   const int nsc = (nch + kSuperChunk - 1) / kSuperChunk;
   if (nsc == 1) {
-    finish_row<WB>(p, G, dst, D, g == 0, cb_lo, cb_hi, [&](int cbx) {
+    finish_row<WK>(p, G, dst, D, g == 0, cb_lo, cb_hi, [&](int cbx) {
       return sum_slots(p, G, cbeg, ncb, 0, nch, 1, cbx, D);
     });
     return;
@@ -1568,7 +1729,7 @@ __device__ __forceinline__ void long_item(const RedParams& p, const LongRun& rec
       store_partial(slot_of(p, cbeg, m0, ncb, cbx) + 4 * lig, a);
   }
   if (!ticket_last(p.run_ticket + cbeg + cb_lo, (uint32_t)nsc)) return;
-  finish_row<WB>(p, G, dst, D, g == 0, cb_lo, cb_hi, [&](int cbx) {
+  finish_row<WK>(p, G, dst, D, g == 0, cb_lo, cb_hi, [&](int cbx) {
     return sum_slots(p, G, cbeg, ncb, 0, nsc, kSuperChunk, cbx, D);
   });
 }
@@ -1616,7 +1777,7 @@ __device__ __forceinline__ LongRun uniform_rec(const LongRun& r) {
   return u;
 }
 
-template <bool BF16, bool WB>
+template <bool BF16, int WK>
 __global__ __launch_bounds__(256) void k_reduce_long(RedParams p) {
   const uint32_t n_items = *p.total_items;
   const int nlong = (int)*p.num_long;
@@ -1629,8 +1790,8 @@ __global__ __launch_bounds__(256) void k_reduce_long(RedParams p) {
     const LongRun rec = uniform_rec(p.long_recs[k]);
     const int local = (int)(w - rec.cbeg);
     const int c = local / rec.ncb, cb = local % rec.ncb;
-    if (p.mode == kModeAdagrad && cb != 0) continue;
-    long_item<BF16, WB>(p, rec, c, cb);
+    if ((p.mode == kModeAdagrad || WK == kWINT8) && cb != 0) continue;
+    long_item<BF16, WK>(p, rec, c, cb);
   }
 }
 
@@ -1655,7 +1816,7 @@ __device__ __forceinline__ int short_lpl(int D) {
 // xor tree, and the first of them writes the row.  Called with the whole wave
 // active.  The row's old value and Adagrad state are read before the gather
 // so that the reads overlap.
-template <int CPL, bool BF16, bool WB>
+template <int CPL, bool BF16, int WK>
 __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, int lpl, int64_t base,
                                             int len, uint64_t key, int rowi, float cf, int t,
                                             int D, int cb) {
@@ -1687,14 +1848,14 @@ __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, in
   for (int i = 0; i < NP; ++i)
     if (active && col + 4 * lpl * i < D) vmask |= 1 << i;
   const int wmask = lead ? vmask : 0;
-  RowDst dst{nullptr, nullptr, 0};
-  if (lead) dst = row_dest<WB>(p, t, D, (int64_t)id);
+  RowDst dst{nullptr, nullptr, 0, 0};
+  if (lead) dst = row_dest<WK>(p, t, D, (int64_t)id);
   const bool needs_old = p.mode != kModeDense || p.accumulate;
   float4 old[NP];
   d4 acc[NP];
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
-    old[i] = (needs_old && ((wmask >> i) & 1)) ? ldw4<WB>(p, dst, col, 4 * lpl * i)
+    old[i] = (needs_old && ((wmask >> i) & 1)) ? ldw4<WK>(p, dst, col, 4 * lpl * i)
                                               : make_float4(0.f, 0.f, 0.f, 0.f);
     acc[i] = d4_zero();
   }
@@ -1754,6 +1915,36 @@ __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, in
 #pragma unroll
     for (int i = 0; i < NP; ++i) d4_add(acc[i], d4_xor(acc[i], off));
   }
+  if constexpr (WK == kWINT8) {
+    // the whole row sits in this lane group: step, range, codes
+    double mult = (double)p.lr, mm = 0.0;
+    if (p.mode == kModeAdagrad) {
+      double ss = 0.0;
+#pragma unroll
+      for (int i = 0; i < NP; ++i)
+        if ((vmask >> i) & 1) ss += d4_sumsq(acc[i]);
+      for (int off = lpl >> 1; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+      mm = (double)m0 + ss / (double)D;
+      mult = (double)p.lr / (sqrt(mm) + (double)p.eps);
+    }
+    float4 nw[NP];
+    float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      nw[i] = round4((double)old[i].x - acc[i].x * mult, (double)old[i].y - acc[i].y * mult,
+                     (double)old[i].z - acc[i].z * mult, (double)old[i].w - acc[i].w * mult);
+      if ((vmask >> i) & 1) minmax4(nw[i], mn, mx);
+    }
+    const float2 qp = qparams_of(mn, mx, lpl);
+#pragma unroll
+    for (int i = 0; i < NP; ++i)
+      if ((wmask >> i) & 1) store_codes4(dst, col + 4 * lpl * i, nw[i], qp);
+    if (lead && lig == 0) {
+      store_qparams(dst, qp);
+      if (p.mode == kModeAdagrad) *dst.mom = (float)mm;
+    }
+    return;
+  }
   if (p.mode == kModeAdagrad) {
     double ss = 0.0;
 #pragma unroll
@@ -1765,7 +1956,7 @@ __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, in
 #pragma unroll
     for (int i = 0; i < NP; ++i)
       if ((wmask >> i) & 1)
-        stw4<WB>(p, dst, col,
+        stw4<WK>(p, dst, col,
             round4((double)old[i].x - acc[i].x * mult, (double)old[i].y - acc[i].y * mult,
                    (double)old[i].z - acc[i].z * mult, (double)old[i].w - acc[i].w * mult),
             4 * lpl * i);
@@ -1786,7 +1977,7 @@ __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, in
                  (double)old[i].w + a.w);
     else
       w = round4(a.x, a.y, a.z, a.w);
-    stw4<WB>(p, dst, col, w, 4 * lpl * i);
+    stw4<WK>(p, dst, col, w, 4 * lpl * i);
   }
 }
 
@@ -1797,7 +1988,7 @@ __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, in
 // runs (length < thr) that start in its 64 >> sub_log positions, in batches
 // of at most 64/lpl runs of one table.  Rows wider than 512 columns are
 // skipped here (k_reduce_wide serves them).
-template <int CPL, bool BF16, bool WB>
+template <int CPL, bool BF16, int WK>
 __device__ __forceinline__ void reduce_short(const RedParams& p) {
   const int lane = lane_id();
   const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -1846,18 +2037,19 @@ __device__ __forceinline__ void reduce_short(const RedParams& p) {
     }
     pending &= ~sel;
     if (D > 512 || cb * 64 * CPL >= D) continue;  // wider rows: k_reduce_wide
-    short_batch<CPL, BF16, WB>(p, sel, lpl, base, len, key, rowi, cf, t0, D, cb);
+    short_batch<CPL, BF16, WK>(p, sel, lpl, base, len, key, rowi, cf, t0, D, cb);
   }
 }
 
 // 8 columns per lane with fp64 sums fits about 80 VGPRs: 6 waves per SIMD overlap
 // the runs' dependent memory steps.  The bf16-weight instances take one wave
 // less: their rounding code needs the registers (at 80 they spill).
-template <bool BF16, bool WB>
+template <bool BF16, int WK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
-    WB ? SGB_SHORT8_WAVES - 1 : SGB_SHORT8_WAVES, WB ? SGB_SHORT8_WAVES - 1 : SGB_SHORT8_WAVES)))
+    WK != kWF32 ? SGB_SHORT8_WAVES - 1 : SGB_SHORT8_WAVES,
+    WK != kWF32 ? SGB_SHORT8_WAVES - 1 : SGB_SHORT8_WAVES)))
 void k_reduce_short8(RedParams p) {
-  reduce_short<8, BF16, WB>(p);
+  reduce_short<8, BF16, WK>(p);
 }
 
 
@@ -1919,7 +2111,7 @@ __device__ __forceinline__ uint64_t rl64(uint64_t x, int l) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-template <int CPL, int UNR, bool BF16, bool WB>
+template <int CPL, int UNR, bool BF16, int WK>
 __device__ __forceinline__ void wide_item(const RedParams& p, const WideRun& m, const WideLane& d0,
                                           int cb) {
   constexpr int NP = CPL / 4;
@@ -1935,13 +2127,13 @@ __device__ __forceinline__ void wide_item(const RedParams& p, const WideRun& m, 
 #pragma unroll
   for (int i = 0; i < NP; ++i)
     if (col + 256 * i < D) vmask |= 1 << i;
-  const RowDst dst = row_dest<WB>(p, t, D, (int64_t)(kv0 >> p.info_bits));
+  const RowDst dst = row_dest<WK>(p, t, D, (int64_t)(kv0 >> p.info_bits));
   const bool needs_old = p.mode != kModeDense || p.accumulate;
   float4 old[NP];
   d4 acc[NP];
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
-    old[i] = (needs_old && ((vmask >> i) & 1)) ? ldw4<WB>(p, dst, col + 256 * i)
+    old[i] = (needs_old && ((vmask >> i) & 1)) ? ldw4<WK>(p, dst, col + 256 * i)
                                               : make_float4(0.f, 0.f, 0.f, 0.f);
     acc[i] = d4_zero();
   }
@@ -1971,6 +2163,36 @@ __device__ __forceinline__ void wide_item(const RedParams& p, const WideRun& m, 
         for (int i = 0; i < NP; ++i) d4_fma(acc[i], c[u], widen4<BF16>(r[u][i]));
     }
   }
+  if constexpr (WK == kWINT8) {
+    // one item holds the whole row (INT8 rows are at most 1024 wide)
+    double mult = (double)p.lr, mm = 0.0;
+    if (p.mode == kModeAdagrad) {
+      double ss = 0.0;
+#pragma unroll
+      for (int i = 0; i < NP; ++i)
+        if ((vmask >> i) & 1) ss += d4_sumsq(acc[i]);
+      ss = group_sum(ss, 64);
+      mm = (double)m0 + ss / (double)D;
+      mult = (double)p.lr / (sqrt(mm) + (double)p.eps);
+    }
+    float4 nw[NP];
+    float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      nw[i] = round4((double)old[i].x - acc[i].x * mult, (double)old[i].y - acc[i].y * mult,
+                     (double)old[i].z - acc[i].z * mult, (double)old[i].w - acc[i].w * mult);
+      if ((vmask >> i) & 1) minmax4(nw[i], mn, mx);
+    }
+    const float2 qp = qparams_of(mn, mx, 64);
+#pragma unroll
+    for (int i = 0; i < NP; ++i)
+      if ((vmask >> i) & 1) store_codes4(dst, col + 256 * i, nw[i], qp);
+    if (lane_id() == 0) {
+      store_qparams(dst, qp);
+      if (p.mode == kModeAdagrad) *dst.mom = (float)mm;
+    }
+    return;
+  }
   if (p.mode == kModeAdagrad) {
     // one item holds the whole row (row-wise Adagrad rows are at most 1024 wide)
     double ss = 0.0;
@@ -1983,7 +2205,7 @@ __device__ __forceinline__ void wide_item(const RedParams& p, const WideRun& m, 
 #pragma unroll
     for (int i = 0; i < NP; ++i)
       if ((vmask >> i) & 1)
-        stw4<WB>(p, dst, col + 256 * i,
+        stw4<WK>(p, dst, col + 256 * i,
             round4((double)old[i].x - acc[i].x * mult, (double)old[i].y - acc[i].y * mult,
                    (double)old[i].z - acc[i].z * mult, (double)old[i].w - acc[i].w * mult));
     if (lane_id() == 0) *dst.mom = (float)mm;
@@ -2003,11 +2225,11 @@ __device__ __forceinline__ void wide_item(const RedParams& p, const WideRun& m, 
                  (double)old[i].w + a.w);
     else
       w = round4(a.x, a.y, a.z, a.w);
-    stw4<WB>(p, dst, col + 256 * i, w);
+    stw4<WK>(p, dst, col + 256 * i, w);
   }
 }
 
-template <int CPL, int UNR, bool BF16, bool WB>
+template <int CPL, int UNR, bool BF16, int WK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, SGB_WIDE_WAVES)))
 void k_reduce_wide(RedParams p) {
   const int64_t nw = (int64_t)gridDim.x * 4;
@@ -2021,7 +2243,7 @@ void k_reduce_wide(RedParams p) {
   for (; item < items; item += nw) {
     const WideRun m2 = wide_run(p, item + 2 * nw, items, ncb);
     const WideLane d1 = wide_lane(p, m1, 0);
-    wide_item<CPL, UNR, BF16, WB>(p, m0, d0, (int)(item % ncb));
+    wide_item<CPL, UNR, BF16, WK>(p, m0, d0, (int)(item % ncb));
     m0 = m1;
     d0 = d1;
     m1 = m2;
@@ -2222,57 +2444,64 @@ hipError_t launch_fill(const FillParams& p, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Each reducer has an instance per (grad_output dtype, weight dtype): the
-// fp32-weight instances carry no bf16 rounding code (nor its registers).
-template <bool BF16, bool WB>
-void launch_long_t(const RedParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_reduce_long<BF16, WB>), dim3(grid), dim3(256), 0, s, p);
-}
-
-hipError_t launch_reduce_long(const RedParams& p, bool bf16, int grid, hipStream_t s) {
-  const bool wb = p.w_bf16 != 0;
-  if (bf16)
-    wb ? launch_long_t<true, true>(p, grid, s) : launch_long_t<true, false>(p, grid, s);
-  else
-    wb ? launch_long_t<false, true>(p, grid, s) : launch_long_t<false, false>(p, grid, s);
-  return hipGetLastError();
-}
-
-// Row-wise Adagrad needs a whole row in one item: 16 columns per lane (rows
-// up to 1024); dense and SGD rows take SGB_WIDE_CPL columns per lane.
-template <bool BF16, bool WB>
-void launch_wide_t(RedParams q, bool adagrad, int dmax, const int* grid, hipStream_t s) {
-  if (adagrad) {
-    q.wide_ncb = (dmax + 1023) / 1024;
-    hipLaunchKernelGGL((k_reduce_wide<16, kWideUnr16, BF16, WB>), dim3(grid[0]), dim3(256), 0, s,
-                       q);
+// Each reducer has an instance per (grad_output dtype, weight kind): the
+// fp32-weight instances carry no bf16 or INT8 code (nor its registers).
+template <template <bool, int> class L, class... A>
+void by_kind(bool bf16, int wk, A&&... a) {
+  if (bf16) {
+    if (wk == kWINT8) L<true, kWINT8>::go(a...);
+    else if (wk == kWBF16) L<true, kWBF16>::go(a...);
+    else L<true, kWF32>::go(a...);
   } else {
-    q.wide_ncb = (dmax + 64 * kWideCpl - 1) / (64 * kWideCpl);
-    hipLaunchKernelGGL((k_reduce_wide<kWideCpl, kWideUnr, BF16, WB>), dim3(grid[1]), dim3(256),
-                       0, s, q);
+    if (wk == kWINT8) L<false, kWINT8>::go(a...);
+    else if (wk == kWBF16) L<false, kWBF16>::go(a...);
+    else L<false, kWF32>::go(a...);
   }
 }
 
+template <bool BF16, int WK>
+struct LongLaunch {
+  static void go(const RedParams& p, int grid, hipStream_t s) {
+    hipLaunchKernelGGL((k_reduce_long<BF16, WK>), dim3(grid), dim3(256), 0, s, p);
+  }
+};
+
+hipError_t launch_reduce_long(const RedParams& p, bool bf16, int grid, hipStream_t s) {
+  by_kind<LongLaunch>(bf16, p.w_kind, p, grid, s);
+  return hipGetLastError();
+}
+
+// Row-wise Adagrad and INT8 rows need a whole row in one item: 16 columns
+// per lane (rows up to 1024); dense and SGD rows take SGB_WIDE_CPL columns
+// per lane.
+template <bool BF16, int WK>
+struct WideLaunch {
+  static void go(RedParams q, int dmax, const int* grid, hipStream_t s) {
+    if (q.mode == kModeAdagrad || WK == kWINT8) {
+      q.wide_ncb = (dmax + 1023) / 1024;
+      hipLaunchKernelGGL((k_reduce_wide<16, kWideUnr16, BF16, WK>), dim3(grid[0]), dim3(256), 0,
+                         s, q);
+    } else {
+      q.wide_ncb = (dmax + 64 * kWideCpl - 1) / (64 * kWideCpl);
+      hipLaunchKernelGGL((k_reduce_wide<kWideCpl, kWideUnr, BF16, WK>), dim3(grid[1]), dim3(256),
+                         0, s, q);
+    }
+  }
+};
+
 void launch_reduce_wide(const RedParams& p, bool bf16, int dmax, const int* grid, hipStream_t s) {
-  const bool adagrad = p.mode == kModeAdagrad;
-  const bool wb = p.w_bf16 != 0;
-  if (bf16)
-    wb ? launch_wide_t<true, true>(p, adagrad, dmax, grid + 2, s)
-       : launch_wide_t<true, false>(p, adagrad, dmax, grid + 2, s);
-  else
-    wb ? launch_wide_t<false, true>(p, adagrad, dmax, grid, s)
-       : launch_wide_t<false, false>(p, adagrad, dmax, grid, s);
+  by_kind<WideLaunch>(bf16, p.w_kind, p, dmax, bf16 ? grid + 2 : grid, s);
 }
 
 // Blocks per CU of the wide-row reducer instances (fp32 weights; the persistent
-// grid of the bf16-weight instances is the same), in the order
-// {fp32 Adagrad, fp32 other, bf16 Adagrad, bf16 other} of grad_output dtypes.
+// grid of the other weight kinds is the same), in the order
+// {fp32 whole-row, fp32 other, bf16 whole-row, bf16 other} of grad_output dtypes.
 void reduce_wide_blocks_per_cu(int out[4]) {
   const void* k[4] = {
-      reinterpret_cast<const void*>(k_reduce_wide<16, kWideUnr16, false, false>),
-      reinterpret_cast<const void*>(k_reduce_wide<kWideCpl, kWideUnr, false, false>),
-      reinterpret_cast<const void*>(k_reduce_wide<16, kWideUnr16, true, false>),
-      reinterpret_cast<const void*>(k_reduce_wide<kWideCpl, kWideUnr, true, false>)};
+      reinterpret_cast<const void*>(k_reduce_wide<16, kWideUnr16, false, kWF32>),
+      reinterpret_cast<const void*>(k_reduce_wide<kWideCpl, kWideUnr, false, kWF32>),
+      reinterpret_cast<const void*>(k_reduce_wide<16, kWideUnr16, true, kWF32>),
+      reinterpret_cast<const void*>(k_reduce_wide<kWideCpl, kWideUnr, true, kWF32>)};
   for (int i = 0; i < 4; ++i) {
     int n = 0;
     out[i] = (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k[i], 256, 0) == hipSuccess && n > 0)
@@ -2281,10 +2510,12 @@ void reduce_wide_blocks_per_cu(int out[4]) {
   }
 }
 
-template <bool BF16, bool WB>
-void launch_short8_t(const RedParams& q, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_reduce_short8<BF16, WB>), grid, dim3(256), 0, s, q);
-}
+template <bool BF16, int WK>
+struct Short8Launch {
+  static void go(const RedParams& q, dim3 grid, hipStream_t s) {
+    hipLaunchKernelGGL((k_reduce_short8<BF16, WK>), grid, dim3(256), 0, s, q);
+  }
+};
 
 hipError_t launch_reduce_short(const RedParams& p, bool bf16, int dmin, int dmax,
                                const int* wide_grid, hipStream_t s) {
@@ -2300,11 +2531,7 @@ hipError_t launch_reduce_short(const RedParams& p, bool bf16, int dmin, int dmax
     RedParams q = p;
     q.sub_log = sub_for(kShortSub8);
     const dim3 grid((unsigned)(((windows << q.sub_log) + 3) / 4), 1);
-    const bool wb = p.w_bf16 != 0;
-    if (bf16)
-      wb ? launch_short8_t<true, true>(q, grid, s) : launch_short8_t<true, false>(q, grid, s);
-    else
-      wb ? launch_short8_t<false, true>(q, grid, s) : launch_short8_t<false, false>(q, grid, s);
+    by_kind<Short8Launch>(bf16, p.w_kind, q, grid, s);
   }
   if (dmax > 512) launch_reduce_wide(p, bf16, dmax, wide_grid, s);
   return hipGetLastError();
@@ -2326,8 +2553,8 @@ hipError_t launch_forward(const FwdParams& p, hipStream_t s) {
 
 int reduce_long_blocks_per_cu(bool bf16) {
   int n = 0;
-  hipError_t e = bf16 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_reduce_long<true, false>, 256, 0)
-                      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_reduce_long<false, false>, 256, 0);
+  hipError_t e = bf16 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_reduce_long<true, kWF32>, 256, 0)
+                      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_reduce_long<false, kWF32>, 256, 0);
   return (e == hipSuccess && n > 0) ? n : 2;
 }
 
