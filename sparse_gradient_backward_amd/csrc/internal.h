@@ -84,6 +84,13 @@ __host__ __device__ inline int sort_items_for(int64_t N) {
 // zero fill: threads of each (looping) workgroup
 constexpr int kFillThreads = SGB_FILL_THREADS;
 
+// up to this many tiles, a sort pass and the run-length encoding skip their
+// scan kernel: each tile sums the raw counts of the tiles before it
+#ifndef SGB_FUSE_TILES
+#define SGB_FUSE_TILES 32
+#endif
+constexpr int kFuseTiles = SGB_FUSE_TILES;
+
 // run-length encoding / run post-processing tiling
 constexpr int kScanThreads = 256;
 constexpr int kScanItems = 16;
@@ -240,6 +247,7 @@ struct SortParams {
   uint32_t* bases;          // [radix]: digit totals
   uint32_t* status;
   uint32_t epoch;
+  int32_t fuse_offsets;     // tiles <= kFuseTiles: the scatter derives its offsets itself
 };
 
 struct RleParams {
@@ -252,6 +260,7 @@ struct RleParams {
   int32_t* head_run;        // [N]: run index at each run's first position
   int32_t* num_runs;
   uint32_t* tile_runs;      // [tiles]: runs starting in each tile, then the first run index
+  int32_t fuse_scan;        // tiles <= kFuseTiles: the write kernel scans the counts itself
 };
 
 struct PostParams {

@@ -478,8 +478,23 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(SortParams p) {
   for (int h = 0; h < kDigitsPerThread; ++h) {
     const int d = kDigitsPerThread * tid + h;
     const int dc = d < radix ? d : 0;  // unconditional loads: none waits behind a branch
-    goff[h] = p.counts[(size_t)dc * p.tiles + tile];
-    dtot[h] = p.bases[dc];
+    if (p.fuse_offsets) {
+      // few tiles: this tile's offset and the digit's total straight from
+      // the raw tile counts (k_sort_offsets is not launched)
+      const uint32_t* row = p.counts + (size_t)dc * p.tiles;
+      uint32_t before = 0, all = 0;
+#pragma unroll 8
+      for (int64_t j = 0; j < p.tiles; ++j) {
+        const uint32_t c = row[j];
+        all += c;
+        before += j < (int64_t)tile ? c : 0u;
+      }
+      goff[h] = before;
+      dtot[h] = all;
+    } else {
+      goff[h] = p.counts[(size_t)dc * p.tiles + tile];
+      dtot[h] = p.bases[dc];
+    }
     if (d >= radix) dtot[h] = 0u;
   }
 #pragma unroll
@@ -696,7 +711,25 @@ __global__ __launch_bounds__(kScanThreads) void k_rle_write(RleParams p) {
   const int n = (int)min((int64_t)kScanTile, p.N - base);
   uint64_t key[kScanItems];
   const uint32_t heads = rle_heads(p, base, n, key, s_edge);
-  const uint32_t first = p.tile_runs[blockIdx.x];
+  uint32_t first;
+  if (p.fuse_scan) {
+    // few tiles: this tile's first run index from the raw tile counts
+    // (k_rle_scan is not launched); the last tile closes the run starts
+    uint32_t before = 0, all = 0;
+#pragma unroll 8
+    for (int64_t j = 0; j < p.tiles; ++j) {
+      const uint32_t c = p.tile_runs[j];
+      all += c;
+      before += j < (int64_t)blockIdx.x ? c : 0u;
+    }
+    first = before;
+    if (blockIdx.x == p.tiles - 1 && tid == 0) {
+      p.cum[all] = (int32_t)p.N;
+      *p.num_runs = (int32_t)all;
+    }
+  } else {
+    first = p.tile_runs[blockIdx.x];
+  }
   // heads of every (item round, wave) in tile order, then their exclusive scan
   uint64_t bal[kScanItems];
 #pragma unroll
@@ -2409,7 +2442,8 @@ hipError_t launch_sort_pass(const SortParams& p, hipStream_t s,
     hipLaunchKernelGGL(k_sort_count<kSortItemsLarge>, dim3(tiles), dim3(kSortThreads), 0, s, p);
   m(SGB_STAGE_SORT_COUNT, 1);
   m(SGB_STAGE_SORT_OFFSETS, 0);
-  hipLaunchKernelGGL(k_sort_offsets, dim3(1u << p.bits), dim3(kScanThreads), 0, s, p);
+  if (!p.fuse_offsets)
+    hipLaunchKernelGGL(k_sort_offsets, dim3(1u << p.bits), dim3(kScanThreads), 0, s, p);
   m(SGB_STAGE_SORT_OFFSETS, 1);
   m(SGB_STAGE_SORT_SCATTER, 0);
   if (p.items == kSortItemsSmall)
@@ -2426,7 +2460,7 @@ hipError_t launch_rle(const RleParams& p, hipStream_t s, const std::function<voi
   hipLaunchKernelGGL(k_rle_count, dim3(tiles), dim3(kScanThreads), 0, s, p);
   mark(SGB_STAGE_RLE_COUNT, 1);
   mark(SGB_STAGE_RLE_SCAN, 0);
-  hipLaunchKernelGGL(k_rle_scan, dim3(1), dim3(kScanThreads), 0, s, p);
+  if (!p.fuse_scan) hipLaunchKernelGGL(k_rle_scan, dim3(1), dim3(kScanThreads), 0, s, p);
   mark(SGB_STAGE_RLE_SCAN, 1);
   mark(SGB_STAGE_RLE_WRITE, 0);
   hipLaunchKernelGGL(k_rle_write, dim3(tiles), dim3(kScanThreads), 0, s, p);
