@@ -2166,7 +2166,7 @@ __device__ __forceinline__ void wide_item(const RedParams& p, const WideRun& m, 
   d4 acc[NP];
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
-    old[i] = (needs_old && ((vmask >> i) & 1)) ? ldw4<WK>(p, dst, col + 256 * i)
+    old[i] = (needs_old && ((vmask >> i) & 1)) ? ldw4<WK>(p, dst, col, 256 * i)
                                               : make_float4(0.f, 0.f, 0.f, 0.f);
     acc[i] = d4_zero();
   }
@@ -2238,9 +2238,10 @@ __device__ __forceinline__ void wide_item(const RedParams& p, const WideRun& m, 
 #pragma unroll
     for (int i = 0; i < NP; ++i)
       if ((vmask >> i) & 1)
-        stw4<WK>(p, dst, col + 256 * i,
+        stw4<WK>(p, dst, col,
             round4((double)old[i].x - acc[i].x * mult, (double)old[i].y - acc[i].y * mult,
-                   (double)old[i].z - acc[i].z * mult, (double)old[i].w - acc[i].w * mult));
+                   (double)old[i].z - acc[i].z * mult, (double)old[i].w - acc[i].w * mult),
+            256 * i);
     if (lane_id() == 0) *dst.mom = (float)mm;
     return;
   }
@@ -2258,7 +2259,7 @@ __device__ __forceinline__ void wide_item(const RedParams& p, const WideRun& m, 
                  (double)old[i].w + a.w);
     else
       w = round4(a.x, a.y, a.z, a.w);
-    stw4<WK>(p, dst, col + 256 * i, w);
+    stw4<WK>(p, dst, col, w, 256 * i);
   }
 }
 
