@@ -351,15 +351,19 @@ constexpr int kCountCopies = (kSortThreads / 64) * kCopiesPerWave;
 // digits of the radix per thread in the scatter's per-digit steps
 constexpr int kDigitsPerThread = kRadixMax / kSortThreads;
 
+// The histograms take kCountCopies * radix words of dynamic LDS: sized to the
+// pass's digit width, so passes of 8 or 9 bits leave room for more resident
+// workgroups than the widest (10-bit) pass.
 template <int kSortItems>
 __global__ __launch_bounds__(kSortThreads) void k_sort_count(SortParams p) {
   constexpr int kSortTile = kSortThreads * kSortItems;
-  __shared__ uint32_t s_h[kCountCopies][kRadixMax];
+  extern __shared__ uint32_t s_hist[];
   const int tid = threadIdx.x, w = (tid >> 6) * kCopiesPerWave + (tid & (kCopiesPerWave - 1));
   const uint32_t tile = blockIdx.x;
   const int radix = 1 << p.bits;
   const uint32_t dmask = (uint32_t)radix - 1u;
-  for (int d = tid; d < kCountCopies * kRadixMax; d += kSortThreads) (&s_h[0][0])[d] = 0u;
+  auto s_h = [&](int copy) { return s_hist + copy * radix; };
+  for (int d = tid; d < kCountCopies * radix; d += kSortThreads) s_hist[d] = 0u;
   const int64_t base = (int64_t)tile * kSortTile;
   const int n = (int)min((int64_t)kSortTile, p.N - base);
   uint64_t kv[kSortItems];
@@ -380,16 +384,16 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_count(SortParams p) {
     const uint32_t d0 = __builtin_amdgcn_readfirstlane(d);
     const uint64_t same = __ballot(valid && d == d0);
     if (valid && d == d0) {
-      if (lane == __builtin_ctzll(same)) atomicAdd(&s_h[w][d0], (uint32_t)__popcll(same));
+      if (lane == __builtin_ctzll(same)) atomicAdd(&s_h(w)[d0], (uint32_t)__popcll(same));
     } else if (valid) {
-      atomicAdd(&s_h[w][d], 1u);
+      atomicAdd(&s_h(w)[d], 1u);
     }
   }
   __syncthreads();
   for (int d = tid; d < radix; d += kSortThreads) {
     uint32_t c = 0;
 #pragma unroll
-    for (int ww = 0; ww < kCountCopies; ++ww) c += s_h[ww][d];
+    for (int ww = 0; ww < kCountCopies; ++ww) c += s_h(ww)[d];
     p.counts[(size_t)d * p.tiles + tile] = c;
   }
 }
@@ -445,19 +449,22 @@ template <int kSortItems>
 __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(SortParams p) {
   constexpr int kSortTile = kSortThreads * kSortItems;
   __shared__ uint64_t s_kv[kSortTile];  // keys, then coefficients, in tile order by digit
-  __shared__ uint32_t s_wcnt[kSortThreads / 64][kRadixMax];
-  __shared__ uint32_t s_local[kRadixMax];
-  __shared__ int32_t s_gbase[kRadixMax];
   __shared__ uint32_t s_tmp[4];
+  // per-digit tables sized to the pass's radix (dynamic LDS): each wave's
+  // running digit counts, the tile's digit offsets, the global bases
+  extern __shared__ uint32_t s_digit[];
+  const int radix = 1 << p.bits;
+  auto s_wcnt = [&](int wave) { return s_digit + wave * radix; };
+  uint32_t* s_local = s_digit + (kSortThreads / 64) * radix;
+  int32_t* s_gbase = reinterpret_cast<int32_t*>(s_local + radix);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int radix = 1 << p.bits;
   const uint32_t dmask = (uint32_t)radix - 1u;
   const bool has_coef = p.coef_in != nullptr;
   const uint32_t tile = blockIdx.x;
   const int64_t base = (int64_t)tile * kSortTile;
   const int tile_n = (int)min((int64_t)kSortTile, p.N - base);
-  for (int d = lane; d < radix; d += 64) s_wcnt[w][d] = 0u;
+  for (int d = lane; d < radix; d += 64) s_wcnt(w)[d] = 0u;
 
   uint64_t kv[kSortItems];
   float cf[kSortItems];
@@ -504,9 +511,9 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(SortParams p) {
     const uint32_t d = digit_of(kv[k], p.shift, dmask);
     const uint64_t peers = digit_peers(d, p.bits, valid);
     const uint32_t below = bits_below(peers);
-    const uint32_t before = valid ? s_wcnt[w][d] : 0u;
+    const uint32_t before = valid ? s_wcnt(w)[d] : 0u;
     rank[k] = before + below;
-    if (valid && below == 0) s_wcnt[w][d] = before + (uint32_t)__popcll(peers);
+    if (valid && below == 0) s_wcnt(w)[d] = before + (uint32_t)__popcll(peers);
   }
   __syncthreads();
 
@@ -519,8 +526,8 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(SortParams p) {
     if (d < radix) {
 #pragma unroll
       for (int ww = 0; ww < kSortThreads / 64; ++ww) {
-        const uint32_t c = s_wcnt[ww][d];
-        s_wcnt[ww][d] = acc;
+        const uint32_t c = s_wcnt(ww)[d];
+        s_wcnt(ww)[d] = acc;
         acc += c;
       }
     }
@@ -553,7 +560,7 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(SortParams p) {
     const int e = w * 64 * kSortItems + k * 64 + lane;
     if (e < tile_n) {
       const uint32_t d = digit_of(kv[k], p.shift, dmask);
-      rank[k] += s_local[d] + s_wcnt[w][d];
+      rank[k] += s_local[d] + s_wcnt(w)[d];
       s_kv[rank[k]] = kv[k];
     }
   }
@@ -2437,20 +2444,26 @@ hipError_t launch_sort_pass(const SortParams& p, hipStream_t s,
     if (mark) mark(stage, end);
   };
   m(SGB_STAGE_SORT_COUNT, 0);
+  const size_t hist_bytes = sizeof(uint32_t) * (size_t)kCountCopies << p.bits;
   if (p.items == kSortItemsSmall)
-    hipLaunchKernelGGL(k_sort_count<kSortItemsSmall>, dim3(tiles), dim3(kSortThreads), 0, s, p);
+    hipLaunchKernelGGL(k_sort_count<kSortItemsSmall>, dim3(tiles), dim3(kSortThreads), hist_bytes,
+                       s, p);
   else
-    hipLaunchKernelGGL(k_sort_count<kSortItemsLarge>, dim3(tiles), dim3(kSortThreads), 0, s, p);
+    hipLaunchKernelGGL(k_sort_count<kSortItemsLarge>, dim3(tiles), dim3(kSortThreads), hist_bytes,
+                       s, p);
   m(SGB_STAGE_SORT_COUNT, 1);
   m(SGB_STAGE_SORT_OFFSETS, 0);
   if (!p.fuse_offsets)
     hipLaunchKernelGGL(k_sort_offsets, dim3(1u << p.bits), dim3(kScanThreads), 0, s, p);
   m(SGB_STAGE_SORT_OFFSETS, 1);
   m(SGB_STAGE_SORT_SCATTER, 0);
+  const size_t digit_bytes = sizeof(uint32_t) * (size_t)(kSortThreads / 64 + 2) << p.bits;
   if (p.items == kSortItemsSmall)
-    hipLaunchKernelGGL(k_sort_scatter<kSortItemsSmall>, dim3(tiles), dim3(kSortThreads), 0, s, p);
+    hipLaunchKernelGGL(k_sort_scatter<kSortItemsSmall>, dim3(tiles), dim3(kSortThreads),
+                       digit_bytes, s, p);
   else
-    hipLaunchKernelGGL(k_sort_scatter<kSortItemsLarge>, dim3(tiles), dim3(kSortThreads), 0, s, p);
+    hipLaunchKernelGGL(k_sort_scatter<kSortItemsLarge>, dim3(tiles), dim3(kSortThreads),
+                       digit_bytes, s, p);
   m(SGB_STAGE_SORT_SCATTER, 1);
   return hipGetLastError();
 }
