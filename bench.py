@@ -196,7 +196,7 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the backward pass here runs on one GPU; --gpus must be 1 (no multi-GPU path)"}))
         sys.exit(2)
 
     import sparse_gradient_backward_amd as sgb
