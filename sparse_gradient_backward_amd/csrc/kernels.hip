@@ -8,18 +8,24 @@
 //   k_sort_count / k_sort_offsets / k_sort_scatter
 //                  one stable LSD radix pass (<= 10-bit digits) as
 //                  reduce-then-scan: tile digit counts, their scan per digit,
-//                  ballot-ranked LDS-staged scatter
+//                  ballot-ranked LDS-staged scatter (with at most kFuseTiles
+//                  tiles the scatter scans the counts itself and
+//                  k_sort_offsets is not launched)
 //   k_rle_count / k_rle_scan / k_rle_write
 //                  run heads of the sorted ids -> unique ids, run starts, count
+//                  (k_rle_scan likewise folded into k_rle_write on few tiles)
 //   k_post         run lengths, ascending long-run list and records
 //   k_fill         zeros of a fresh dense gradient (side stream, from the start)
-//   k_reduce_short short runs (side stream, after run-length encoding): the
-//                  runs starting in a part of a 64-position window, one per
-//                  lane group
+//   k_reduce_short8 short runs of rows up to 512 columns (side stream, after
+//                  run-length encoding): the runs starting in a part of a
+//                  64-position window, one per lane group
+//   k_reduce_wide  short runs of wider rows (same stream): (run, column
+//                  block) items dealt to persistent waves
 //   k_reduce_long  (chunk, column block) items of long runs, fp64 partials
 //                  combined in a fixed order by the last-arriving workgroup
-//   Both reducers finish each row with the fused dense / SGD / row-wise
-//   Adagrad step.
+//   Every reducer finishes each row with the fused dense / SGD / row-wise
+//   Adagrad step, on fp32, bf16 (nearest-even or stochastic rounding) or
+//   INT8 row-wise quantized weight rows (one instance per weight kind).
 //
 // Method: "fbgemm_gpu/codegen/embedding_backward_split_template.cu" (FBGEMM),
 // host entry `..._exact_cuda` (linearise, sort, run-length encode, long
@@ -1007,7 +1013,7 @@ __global__ __launch_bounds__(kFillThreads) void k_fill(FillParams p) {
 // power of two covering D/4, capped at one wave); a row wider than 256
 // columns is covered in column blocks of 256.
 //
-// k_reduce_short: one wave per 64 consecutive sorted positions.  The wave
+// k_reduce_short8: one wave per 64 consecutive sorted positions.  The wave
 //   reads the packed words of its window once, finds the run heads in it
 //   (id differs from the previous position), takes each run's length from the
 //   run starts, and serves the short runs (length < thr) that start in the
