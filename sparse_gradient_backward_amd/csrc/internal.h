@@ -35,7 +35,7 @@ constexpr int kMaxD = 8192;
 #define SGB_LONG_UNR 8
 #endif
 #ifndef SGB_MAX_CHUNKS
-#define SGB_MAX_CHUNKS 2048
+#define SGB_MAX_CHUNKS 1024
 #endif
 #ifndef SGB_CHUNK_DIV
 #define SGB_CHUNK_DIV 8192
