@@ -61,6 +61,9 @@ constexpr int kMaxD = 8192;
 #ifndef SGB_WIDE_WAVES
 #define SGB_WIDE_WAVES 8
 #endif
+#ifndef SGB_WIDE_GRID_MULT
+#define SGB_WIDE_GRID_MULT 8
+#endif
 #ifndef SGB_SHORT8_WAVES
 #define SGB_SHORT8_WAVES 6
 #endif
@@ -118,6 +121,8 @@ static_assert(kShortSub8 >= 0 && kShortSub8 <= 6 && kShortSub16 >= 0 && kShortSu
 constexpr int kWideCpl = SGB_WIDE_CPL;
 constexpr int kWideUnr = SGB_WIDE_UNR;
 constexpr int kWideUnr16 = SGB_WIDE_UNR16;
+// workgroups of the wide-row reducer: this many times those resident at once
+constexpr int kWideGridMult = SGB_WIDE_GRID_MULT;
 static_assert(kWideCpl == 4 || kWideCpl == 8 || kWideCpl == 16, "pieces of 4 columns, 256 apart");
 
 // long runs: chunk sizing and two-level combine

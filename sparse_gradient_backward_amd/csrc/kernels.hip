@@ -20,7 +20,8 @@
 //                  run-length encoding): the runs starting in a part of a
 //                  64-position window, one per lane group
 //   k_reduce_wide  short runs of wider rows (same stream): (run, column
-//                  block) items dealt to persistent waves
+//                  block) items dealt round-robin to waves, several times
+//                  more workgroups than fit at once
 //   k_reduce_long  (chunk, column block) items of long runs, fp64 partials
 //                  combined in a fixed order by the last-arriving workgroup
 //   Every reducer finishes each row with the fused dense / SGD / row-wise
@@ -2105,11 +2106,15 @@ void k_reduce_short8(RedParams p) {
 // (read and write of the old row, 8 bytes per column) outweighs the gather of
 // its few lookups, and a wave that served every run of a 64-position window
 // in turn paid two memory round trips per run.  Here the work is dealt by
-// run: items (run, column block of 64*CPL columns) go round-robin to
-// persistent waves, the whole wave serves one item (each lane CPL columns,
-// pieces of 4 columns 256 apart), and before a wave gathers its current item
-// it has issued the loads of the next item's first sorted words and of the
-// run starts of the item after that, so an item costs about one round trip.
+// run: items (run, column block of 64*CPL columns) go round-robin to the
+// waves, the whole wave serves one item (each lane CPL columns, pieces of 4
+// columns 256 apart), and before a wave gathers its current item it has
+// issued the loads of the next item's first sorted words and of the run
+// starts of the item after that, so an item costs about one round trip.
+// Items differ in cost (runs of 1 to thr - 1 lookups), so the grid holds
+// several times the workgroups that fit at once: a wave takes few items, and
+// the hardware starts new waves where short items finished, instead of
+// leaving a fixed set of waves to wait for the one that drew a long run.
 // Lookups are gathered UNR at a time from wave-uniform row offsets (readlane),
 // accumulated with fp64 FMAs.  Runs of length >= thr belong to the long-run
 // reducer, rows of 512 columns or fewer to k_reduce_short8.
@@ -2528,17 +2533,23 @@ hipError_t launch_reduce_long(const RedParams& p, bool bf16, int grid, hipStream
 // Row-wise Adagrad and INT8 rows need a whole row in one item: 16 columns
 // per lane (rows up to 1024); dense and SGD rows take SGB_WIDE_CPL columns
 // per lane.
+// The grid is kWideGridMult times the resident workgroups, capped at one
+// wave per item of the largest run count the batch allows (N runs).
 template <bool BF16, int WK>
 struct WideLaunch {
+  static unsigned blocks(const RedParams& q, int resident) {
+    const int64_t cap = (q.N * q.wide_ncb + 3) / 4;
+    return (unsigned)std::max<int64_t>(1, std::min<int64_t>((int64_t)resident * kWideGridMult, cap));
+  }
   static void go(RedParams q, int dmax, const int* grid, hipStream_t s) {
     if (q.mode == kModeAdagrad || WK == kWINT8) {
       q.wide_ncb = (dmax + 1023) / 1024;
-      hipLaunchKernelGGL((k_reduce_wide<16, kWideUnr16, BF16, WK>), dim3(grid[0]), dim3(256), 0,
-                         s, q);
+      hipLaunchKernelGGL((k_reduce_wide<16, kWideUnr16, BF16, WK>), dim3(blocks(q, grid[0])),
+                         dim3(256), 0, s, q);
     } else {
       q.wide_ncb = (dmax + 64 * kWideCpl - 1) / (64 * kWideCpl);
-      hipLaunchKernelGGL((k_reduce_wide<kWideCpl, kWideUnr, BF16, WK>), dim3(grid[1]), dim3(256),
-                         0, s, q);
+      hipLaunchKernelGGL((k_reduce_wide<kWideCpl, kWideUnr, BF16, WK>), dim3(blocks(q, grid[1])),
+                         dim3(256), 0, s, q);
     }
   }
 };
@@ -2547,7 +2558,7 @@ void launch_reduce_wide(const RedParams& p, bool bf16, int dmax, const int* grid
   by_kind<WideLaunch>(bf16, p.w_kind, p, dmax, bf16 ? grid + 2 : grid, s);
 }
 
-// Blocks per CU of the wide-row reducer instances (fp32 weights; the persistent
+// Resident blocks per CU of the wide-row reducer instances (fp32 weights; the
 // grid of the other weight kinds is the same), in the order
 // {fp32 whole-row, fp32 other, bf16 whole-row, bf16 other} of grad_output dtypes.
 void reduce_wide_blocks_per_cu(int out[4]) {
