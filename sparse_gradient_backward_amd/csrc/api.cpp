@@ -471,7 +471,7 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   rp.head_run = at<int32_t>(ws, L.headrun);
   rp.num_runs = &hdr->num_runs;
   rp.tiles = L.scan_tiles;
-  rp.fuse_scan = L.scan_tiles <= kFuseTiles ? 1 : 0;
+  rp.fuse_scan = L.scan_tiles <= kFuseScanTiles ? 1 : 0;
   rp.tile_runs = at<uint32_t>(ws, L.tile_runs);
   if (launch_rle(rp, stream, mark) != hipSuccess) return SGB_ERR_HIP;
 

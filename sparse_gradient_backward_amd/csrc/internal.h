@@ -93,6 +93,11 @@ constexpr int kFillThreads = SGB_FILL_THREADS;
 #define SGB_FUSE_TILES 32
 #endif
 constexpr int kFuseTiles = SGB_FUSE_TILES;
+// run-length tiles up to which k_rle_write scans the tile counts itself
+#ifndef SGB_FUSE_SCAN_TILES
+#define SGB_FUSE_SCAN_TILES 1024
+#endif
+constexpr int kFuseScanTiles = SGB_FUSE_SCAN_TILES;
 
 // run-length encoding / run post-processing tiling
 constexpr int kScanThreads = 256;
@@ -265,7 +270,7 @@ struct RleParams {
   int32_t* head_run;        // [N]: run index at each run's first position
   int32_t* num_runs;
   uint32_t* tile_runs;      // [tiles]: runs starting in each tile, then the first run index
-  int32_t fuse_scan;        // tiles <= kFuseTiles: the write kernel scans the counts itself
+  int32_t fuse_scan;        // tiles <= kFuseScanTiles: the write kernel scans the counts itself
 };
 
 struct PostParams {

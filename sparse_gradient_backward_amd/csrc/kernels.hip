@@ -13,7 +13,8 @@
 //                  k_sort_offsets is not launched)
 //   k_rle_count / k_rle_scan / k_rle_write
 //                  run heads of the sorted ids -> unique ids, run starts, count
-//                  (k_rle_scan likewise folded into k_rle_write on few tiles)
+//                  (k_rle_scan folded into k_rle_write up to kFuseScanTiles
+//                  tiles, the counts summed by the whole workgroup)
 //   k_post         run lengths, ascending long-run list and records
 //   k_fill         zeros of a fresh dense gradient (side stream, from the start)
 //   k_reduce_short8 short runs of rows up to 512 columns (side stream, after
@@ -727,14 +728,30 @@ __global__ __launch_bounds__(kScanThreads) void k_rle_write(RleParams p) {
   const uint32_t heads = rle_heads(p, base, n, key, s_edge);
   uint32_t first;
   if (p.fuse_scan) {
-    // few tiles: this tile's first run index from the raw tile counts
-    // (k_rle_scan is not launched); the last tile closes the run starts
+    // up to kFuseScanTiles tiles: this tile's first run index from the raw
+    // tile counts (k_rle_scan is not launched), each thread summing every
+    // 256th count, then a block sum; the last tile closes the run starts
+    __shared__ uint32_t s_sum[2][kScanThreads / 64];
     uint32_t before = 0, all = 0;
-#pragma unroll 8
-    for (int64_t j = 0; j < p.tiles; ++j) {
+#pragma unroll 4
+    for (int64_t j = tid; j < p.tiles; j += kScanThreads) {
       const uint32_t c = p.tile_runs[j];
       all += c;
       before += j < (int64_t)blockIdx.x ? c : 0u;
+    }
+    before = wave_sum(before);
+    all = wave_sum(all);
+    if (lane == 0) {
+      s_sum[0][w] = before;
+      s_sum[1][w] = all;
+    }
+    __syncthreads();
+    before = 0;
+    all = 0;
+#pragma unroll
+    for (int i = 0; i < kScanThreads / 64; ++i) {
+      before += s_sum[0][i];
+      all += s_sum[1][i];
     }
     first = before;
     if (blockIdx.x == p.tiles - 1 && tid == 0) {
