@@ -195,6 +195,19 @@ def test_huge_run_two_level_combine(sgb):
     check_case(sgb, inp, "rowwise_adagrad", 64, lr=0.01, eps=1e-8)
 
 
+@pytest.mark.parametrize("tokens", [300_000, 1024 * 4096, 1024 * 4096 + 1])
+def test_many_run_tiles(sgb, tokens):
+    """Run-length tiles of 4096 sorted positions: up to 1024 tiles the run
+    write scans the tile counts itself, one more and the scan kernel runs;
+    300 000 lookups also take the sort's separate offset scan (over 32 sort
+    tiles).  Runs are compared bit-exact, rows to the usual tolerance."""
+    s = synth.Spec("tiles", 1, (60000,), (4,), 0, ("fixed", 1), ("zipf", 1.05), "none", False,
+                   "f32", "dense", accumulate=True, nobag_tokens=tokens, seed=41)
+    inp = synth.generate(s)
+    _say(f"[parity] many run tiles N={inp.N}")
+    check_case(sgb, inp, "dense", 64, accumulate=True)
+
+
 # ------------------------------------------------------------------ properties
 
 def test_deterministic(sgb):
