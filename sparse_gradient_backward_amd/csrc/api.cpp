@@ -45,7 +45,7 @@ struct sgb_plan_s {
   int32_t n_fill = 0;
   int num_cus = 1;
   int red_grid[2] = {1, 1};  // persistent grid of the long-run reducer (f32, bf16)
-  int wide_grid[4] = {1, 1, 1, 1};  // persistent grid of the wide-row reducer (see launch_reduce_short)
+  int wide_grid[4] = {1, 1, 1, 1};  // resident workgroups of the wide-row reducer (see launch_reduce_short)
   // side streams (default priority): [0] clears a fresh dense gradient while
   // the ids are sorted, [1] reduces the short runs while the long-run list is
   // built and the long runs are reduced; the events fork and join them.  The
