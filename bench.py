@@ -34,6 +34,10 @@ HBM_PEAK_GBPS = 8000.0
 STAGES = ("linearize", "sort_count", "sort_offsets", "sort_scatter", "sort", "rle_count",
           "rle_scan", "rle_write", "runs", "fill", "reduce_long", "reduce_short")
 SORT_KERNELS = ("sort_count", "sort_offsets", "sort_scatter")  # timed on the first pass
+# run-length tiles of 4096 sorted positions up to which the library encodes
+# runs in one kernel (k_rle_write alone; the count and scan stages then time
+# no kernel)
+RLE_ONE_PASS_TILES = 128
 KERNEL_SOURCES = ("sparse_gradient_backward_amd/csrc/kernels.hip",
                   "sparse_gradient_backward_amd/csrc/internal.h",
                   "sparse_gradient_backward_amd/csrc/api.cpp")
@@ -62,6 +66,7 @@ def stage_bytes(inp: synth.Inputs, spec: synth.Spec, U: int, run_D: np.ndarray,
     sort_tile = 256 * (8 if N <= (1 << 20) else 12)
     tiles = (N + sort_tile - 1) // sort_tile
     scan_tiles = (N + 4095) // 4096
+    one_pass = scan_tiles <= RLE_ONE_PASS_TILES
 
     def update(D):
         if spec.mode == "dense":
@@ -78,9 +83,9 @@ def stage_bytes(inp: synth.Inputs, spec: synth.Spec, U: int, run_D: np.ndarray,
         "sort_count": N * 8 + tiles * radix0 * 4,
         "sort_offsets": tiles * radix0 * 4 * 2 + radix0 * 4,
         "sort_scatter": N * rec * 2 + tiles * radix0 * 4 + radix0 * 4,
-        "rle_count": N * 8 + scan_tiles * 4,
-        "rle_scan": scan_tiles * 4 * 2 + 8,
-        "rle_write": N * 8 + scan_tiles * 4 + U * (8 + 4 + 4),
+        "rle_count": 0 if one_pass else N * 8 + scan_tiles * 4,
+        "rle_scan": 0 if one_pass else scan_tiles * 4 * 2 + 8,
+        "rle_write": N * 8 + scan_tiles * 4 * (2 if one_pass else 1) + U * (8 + 4 + 4),
         "runs": U * (4 + 4) + int(lg.sum()) * (48 + 4 + 4),
         "fill": int((Es * Ds).sum()) * 4 if fresh else 0,
         "reduce_long": gather_long + int(run_len[lg].sum()) * rec + int(lg.sum()) * 48
@@ -311,9 +316,17 @@ def main():
     npasses = plan_npasses(inp)
     radix0 = 1 << pass_bits0(inp)
     sb, b_path, b_comp = stage_bytes(inp, spec, U, run_D, lens, thr, npasses, radix0)
+    # the stage that each kernel times ("sort" spans the passes; on few tiles
+    # the run-head count and scan stages are done inside k_rle_write)
+    kernel_names = {"reduce_long": "k_reduce_long", "fill": "k_fill", "linearize": "k_linearize",
+                    "sort_count": "k_sort_count", "sort_offsets": "k_sort_offsets",
+                    "sort_scatter": "k_sort_scatter", "rle_write": "k_rle_write", "runs": "k_post",
+                    "reduce_short": short_kernels(np.diff(inp.D_offsets))}
+    if (inp.N + 4095) // 4096 > RLE_ONE_PASS_TILES:
+        kernel_names.update(rle_count="k_rle_count", rle_scan="k_rle_scan")
     # dominant kernel: the largest time per step (a sort kernel runs once per pass)
     per_step = {k: v * (npasses if k in SORT_KERNELS else 1)
-                for k, v in stage_ms.items() if k != "sort"}
+                for k, v in stage_ms.items() if k in kernel_names}
     dom = max(per_step, key=lambda k: per_step[k])
     per_launch_bytes = sb[dom]
     per_launch_ms = stage_ms[dom]
@@ -327,11 +340,6 @@ def main():
         log("timing the CPU oracle")
         cpu = cpu_baseline(inp, spec, thr, args.cpu_min_s, args.cpu_max_reps)
 
-    kernel_names = {"reduce_long": "k_reduce_long", "fill": "k_fill", "linearize": "k_linearize",
-                    "sort_count": "k_sort_count", "sort_offsets": "k_sort_offsets",
-                    "sort_scatter": "k_sort_scatter", "rle_count": "k_rle_count",
-                    "rle_scan": "k_rle_scan", "rle_write": "k_rle_write", "runs": "k_post",
-                    "reduce_short": short_kernels(np.diff(inp.D_offsets))}
     res = {
         "metric": METRIC,
         "value": inp.N / (ms_per_step * 1e-3),

@@ -213,11 +213,11 @@ typedef enum {
   SGB_STAGE_SORT_OFFSETS = 2,  /* radix pass: digit offsets of every tile         */
   SGB_STAGE_SORT_SCATTER = 3,  /* radix pass: stable rank and scatter             */
   SGB_STAGE_SORT = 4,          /* all radix passes                                */
-  SGB_STAGE_RLE_COUNT = 5,     /* run heads of every tile                         */
-  SGB_STAGE_RLE_SCAN = 6,      /* first run index of every tile, run count        */
-  SGB_STAGE_RLE_WRITE = 7,     /* unique ids, run starts                          */
+  SGB_STAGE_RLE_COUNT = 5,     /* run heads of every tile (inside stage 7: empty) */
+  SGB_STAGE_RLE_SCAN = 6,      /* first run index of every tile (inside 7: empty) */
+  SGB_STAGE_RLE_WRITE = 7,     /* run heads, tile scan, unique ids, run starts    */
   SGB_STAGE_RUNS = 8,          /* run lengths, long-run list, chunk prefix        */
-  SGB_STAGE_FILL = 9,          /* zeros of untouched rows (fresh dense grad only) */
+  SGB_STAGE_FILL = 9,          /* zeros of the whole gradient (fresh dense only)  */
   SGB_STAGE_REDUCE_LONG = 10,  /* long runs: chunked reduction + fused row write  */
   SGB_STAGE_REDUCE_SHORT = 11, /* short runs: reduction + fused row write         */
   SGB_NUM_STAGES = 12

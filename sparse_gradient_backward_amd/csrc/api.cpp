@@ -99,7 +99,8 @@ struct Layout {
   int64_t sort_tiles = 0, scan_tiles = 0;
   int64_t max_long = 0;   // bound on the number of long runs
   int64_t max_items = 0;  // bound on the (chunk, column block) items over all long runs
-  size_t hdr = 0, hist = 0, counts = 0, zero_begin = 0, tile_runs = 0, post_lb = 0, zero_end = 0;
+  size_t hdr = 0, hist = 0, counts = 0, zero_begin = 0, rle_lb = 0, post_lb = 0, zero_end = 0,
+         tile_runs = 0;
   size_t kvA = 0, kvB = 0, coefA = 0, coefB = 0, uniq = 0, cum = 0, headrun = 0, lens = 0, longs = 0,
          chunkb = 0, longrec = 0, runtk = 0, sctk = 0, part = 0, total = 0;
 };
@@ -150,6 +151,7 @@ sgb_status make_layout(const sgb_plan_s* p, int64_t N, int32_t B, bool has_offse
   L->hdr = take(sizeof(Header));
   L->hist = take(sizeof(uint32_t) * kMaxPasses * kRadixMax);  // digit bases of each pass
   L->zero_begin = align_up(o, 256);
+  L->rle_lb = take(sizeof(uint32_t) * (size_t)L->scan_tiles);  // one pass only
   L->post_lb = take(sizeof(uint64_t) * (size_t)L->scan_tiles);
   L->runtk = take(sizeof(uint32_t) * (size_t)L->max_items);
   L->sctk = take(sizeof(uint32_t) * (size_t)L->max_items);
@@ -471,8 +473,13 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   rp.head_run = at<int32_t>(ws, L.headrun);
   rp.num_runs = &hdr->num_runs;
   rp.tiles = L.scan_tiles;
+  rp.one_pass = L.scan_tiles <= kOnePassTiles ? 1 : 0;
   rp.fuse_scan = L.scan_tiles <= kFuseScanTiles ? 1 : 0;
   rp.tile_runs = at<uint32_t>(ws, L.tile_runs);
+  rp.lookback = at<uint32_t>(ws, L.rle_lb);
+  rp.tile_ctr = &hdr->rle_tile_ctr;
+  rp.status = status;
+  rp.epoch = epoch;
   if (launch_rle(rp, stream, mark) != hipSuccess) return SGB_ERR_HIP;
 
   PostParams pp{};

@@ -93,10 +93,16 @@ constexpr int kFillThreads = SGB_FILL_THREADS;
 #define SGB_FUSE_TILES 32
 #endif
 constexpr int kFuseTiles = SGB_FUSE_TILES;
-// run-length tiles up to which k_rle_write scans the tile counts itself
+// run-length tiles: up to kOnePassTiles k_rle_write alone (look-back over the
+// tile counts); up to kFuseScanTiles k_rle_count then k_rle_write summing the
+// counts itself; beyond, k_rle_count, k_rle_scan, k_rle_write
+#ifndef SGB_ONE_PASS_TILES
+#define SGB_ONE_PASS_TILES 128
+#endif
 #ifndef SGB_FUSE_SCAN_TILES
 #define SGB_FUSE_SCAN_TILES 1024
 #endif
+constexpr int kOnePassTiles = SGB_ONE_PASS_TILES;
 constexpr int kFuseScanTiles = SGB_FUSE_SCAN_TILES;
 
 // run-length encoding / run post-processing tiling
@@ -192,7 +198,7 @@ struct Header {
   uint32_t status;                    // epoch << 8 | first device-detected error of that call
   uint32_t epoch;                     // epoch of the last call (set while linearising)
   uint32_t post_tile_ctr;             // dynamic tile ids of the run post-processing
-  uint32_t unused;
+  uint32_t rle_tile_ctr;              // dynamic tile ids of the run-length encoding
   int32_t num_runs;                   // U
   uint32_t total_items;               // chunks over all long runs
   int64_t num_long;                   // number of long runs
@@ -270,7 +276,12 @@ struct RleParams {
   int32_t* head_run;        // [N]: run index at each run's first position
   int32_t* num_runs;
   uint32_t* tile_runs;      // [tiles]: runs starting in each tile, then the first run index
-  int32_t fuse_scan;        // tiles <= kFuseScanTiles: the write kernel scans the counts itself
+  int32_t fuse_scan;        // tiles <= kFuseScanTiles: the write kernel sums the counts itself
+  int32_t one_pass;         // tiles <= kOnePassTiles: the write kernel alone, by look-back
+  uint32_t* lookback;       // [tiles], zeroed per call: look-back words of the tile run counts
+  uint32_t* tile_ctr;       // dynamic tile ids of the one-pass write (zeroed per call)
+  uint32_t* status;
+  uint32_t epoch;
 };
 
 struct PostParams {

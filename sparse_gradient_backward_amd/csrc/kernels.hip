@@ -13,8 +13,9 @@
 //                  k_sort_offsets is not launched)
 //   k_rle_count / k_rle_scan / k_rle_write
 //                  run heads of the sorted ids -> unique ids, run starts, count
-//                  (k_rle_scan folded into k_rle_write up to kFuseScanTiles
-//                  tiles, the counts summed by the whole workgroup)
+//                  (few tiles: k_rle_write alone, by look-back over the tile
+//                  counts; more: the counts summed in k_rle_write; many: all
+//                  three kernels)
 //   k_post         run lengths, ascending long-run list and records
 //   k_fill         zeros of a fresh dense gradient (side stream, from the start)
 //   k_reduce_short8 short runs of rows up to 512 columns (side stream, after
@@ -208,6 +209,7 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
   if (blockIdx.x == 0 && tid == 0) {
     p.header->epoch = p.epoch;
     p.header->post_tile_ctr = 0u;
+    p.header->rle_tile_ctr = 0u;
   }
 
   for (int64_t q = blockIdx.x * (int64_t)kLinThreads + tid; q < p.zero_vec4;
@@ -621,7 +623,7 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(SortParams p) {
 // ------------------------------------------------------------------ run-length encoding
 //
 // Run-length encoding of the sorted ids: position i starts a run when its id
-// differs from position i-1.  Reduce-then-scan in three kernels:
+// differs from position i-1.  Reduce-then-scan:
 //   k_rle_count  run heads of every tile
 //   k_rle_scan   one workgroup: exclusive scan of the tile counts (each
 //                tile's first run index), the run count U and the closing
@@ -630,6 +632,7 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(SortParams p) {
 //                scan of run lengths, FBGEMM
 //                `sorted_linear_indices_cumulative_run_lengths`), and its run
 //                index at its position
+// with the first two folded into k_rle_write on fewer tiles (below).
 // Items are read coalesced (item k of thread t is position k*256 + t); a
 // position's predecessor is the previous lane, or for lane 0 the last lane of
 // the wave before it in that order (through LDS).
@@ -718,48 +721,65 @@ __global__ __launch_bounds__(kScanThreads) void k_rle_scan(RleParams p) {
   }
 }
 
+// k_rle_write takes its tile's first run index one of three ways: on at most
+// kOnePassTiles tiles (one pass, no other kernel) the workgroup takes the next
+// tile from an atomic counter, counts its heads and sums the counts of the
+// tiles before it by decoupled look-back (Merrill & Garland's single-pass
+// scan); on more tiles k_rle_count has counted every tile's heads, and on at
+// most kFuseScanTiles the workgroup sums the counts of the tiles before it,
+// beyond that k_rle_scan has scanned them.  The last tile closes the run
+// starts with N and stores U.  (A look-back chain over thousands of tiles
+// costs more than the count kernel saves.)
 __global__ __launch_bounds__(kScanThreads) void k_rle_write(RleParams p) {
   __shared__ uint64_t s_edge[kScanItems][kScanThreads / 64];
   __shared__ uint32_t s_off[kScanItems * (kScanThreads / 64)];
+  __shared__ uint32_t s_tile, s_first;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t base = (int64_t)blockIdx.x * kScanTile;
+  uint32_t tile = blockIdx.x;
+  if (p.one_pass) {
+    if (tid == 0)
+      s_tile = __hip_atomic_fetch_add(p.tile_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    tile = s_tile;
+  }
+  const int64_t base = (int64_t)tile * kScanTile;
   const int n = (int)min((int64_t)kScanTile, p.N - base);
   uint64_t key[kScanItems];
   const uint32_t heads = rle_heads(p, base, n, key, s_edge);
-  uint32_t first;
-  if (p.fuse_scan) {
-    // up to kFuseScanTiles tiles: this tile's first run index from the raw
-    // tile counts (k_rle_scan is not launched), each thread summing every
-    // 256th count, then a block sum; the last tile closes the run starts
-    __shared__ uint32_t s_sum[2][kScanThreads / 64];
-    uint32_t before = 0, all = 0;
+  uint32_t first = 0;
+  if (!p.one_pass) {
+    if (p.fuse_scan) {
+      // each thread sums every 256th tile count, then a block sum
+      __shared__ uint32_t s_sum[2][kScanThreads / 64];
+      uint32_t before = 0, all = 0;
 #pragma unroll 4
-    for (int64_t j = tid; j < p.tiles; j += kScanThreads) {
-      const uint32_t c = p.tile_runs[j];
-      all += c;
-      before += j < (int64_t)blockIdx.x ? c : 0u;
-    }
-    before = wave_sum(before);
-    all = wave_sum(all);
-    if (lane == 0) {
-      s_sum[0][w] = before;
-      s_sum[1][w] = all;
-    }
-    __syncthreads();
-    before = 0;
-    all = 0;
+      for (int64_t j = tid; j < p.tiles; j += kScanThreads) {
+        const uint32_t c = p.tile_runs[j];
+        all += c;
+        before += j < (int64_t)tile ? c : 0u;
+      }
+      before = wave_sum(before);
+      all = wave_sum(all);
+      if (lane == 0) {
+        s_sum[0][w] = before;
+        s_sum[1][w] = all;
+      }
+      __syncthreads();
+      before = 0;
+      all = 0;
 #pragma unroll
-    for (int i = 0; i < kScanThreads / 64; ++i) {
-      before += s_sum[0][i];
-      all += s_sum[1][i];
+      for (int i = 0; i < kScanThreads / 64; ++i) {
+        before += s_sum[0][i];
+        all += s_sum[1][i];
+      }
+      first = before;
+      if ((int64_t)tile == p.tiles - 1 && tid == 0) {
+        p.cum[all] = (int32_t)p.N;
+        *p.num_runs = (int32_t)all;
+      }
+    } else {
+      first = p.tile_runs[tile];
     }
-    first = before;
-    if (blockIdx.x == p.tiles - 1 && tid == 0) {
-      p.cum[all] = (int32_t)p.N;
-      *p.num_runs = (int32_t)all;
-    }
-  } else {
-    first = p.tile_runs[blockIdx.x];
   }
   // heads of every (item round, wave) in tile order, then their exclusive scan
   uint64_t bal[kScanItems];
@@ -779,8 +799,20 @@ __global__ __launch_bounds__(kScanThreads) void k_rle_write(RleParams p) {
       if (lane >= off) incl += o;
     }
     s_off[lane] = incl - c;
+    if (p.one_pass) {
+      const uint32_t total = __shfl(incl, 63, 64);
+      const uint32_t f = wave_lookback<uint32_t>(p.lookback, tile, total, p.status, p.epoch);
+      if (lane == 0) {
+        s_first = f;
+        if ((int64_t)tile == p.tiles - 1) {
+          p.cum[f + total] = (int32_t)p.N;
+          *p.num_runs = (int32_t)(f + total);
+        }
+      }
+    }
   }
   __syncthreads();
+  if (p.one_pass) first = s_first;
 #pragma unroll
   for (int k = 0; k < kScanItems; ++k) {
     if (!((heads >> k) & 1u)) continue;
@@ -2498,11 +2530,15 @@ hipError_t launch_sort_pass(const SortParams& p, hipStream_t s,
 
 hipError_t launch_rle(const RleParams& p, hipStream_t s, const std::function<void(int, int)>& mark) {
   const unsigned tiles = (unsigned)p.tiles;
+  // in one pass the count and scan stages are done inside k_rle_write: their
+  // marks then bracket no kernel, so that every stage's pair of events is
+  // still recorded
   mark(SGB_STAGE_RLE_COUNT, 0);
-  hipLaunchKernelGGL(k_rle_count, dim3(tiles), dim3(kScanThreads), 0, s, p);
+  if (!p.one_pass) hipLaunchKernelGGL(k_rle_count, dim3(tiles), dim3(kScanThreads), 0, s, p);
   mark(SGB_STAGE_RLE_COUNT, 1);
   mark(SGB_STAGE_RLE_SCAN, 0);
-  if (!p.fuse_scan) hipLaunchKernelGGL(k_rle_scan, dim3(1), dim3(kScanThreads), 0, s, p);
+  if (!p.one_pass && !p.fuse_scan)
+    hipLaunchKernelGGL(k_rle_scan, dim3(1), dim3(kScanThreads), 0, s, p);
   mark(SGB_STAGE_RLE_SCAN, 1);
   mark(SGB_STAGE_RLE_WRITE, 0);
   hipLaunchKernelGGL(k_rle_write, dim3(tiles), dim3(kScanThreads), 0, s, p);

@@ -195,12 +195,15 @@ def test_huge_run_two_level_combine(sgb):
     check_case(sgb, inp, "rowwise_adagrad", 64, lr=0.01, eps=1e-8)
 
 
-@pytest.mark.parametrize("tokens", [300_000, 1024 * 4096, 1024 * 4096 + 1])
+@pytest.mark.parametrize("tokens", [300_000, 128 * 4096, 128 * 4096 + 1, 1024 * 4096,
+                                    1024 * 4096 + 1])
 def test_many_run_tiles(sgb, tokens):
-    """Run-length tiles of 4096 sorted positions: up to 1024 tiles the run
-    write scans the tile counts itself, one more and the scan kernel runs;
-    300 000 lookups also take the sort's separate offset scan (over 32 sort
-    tiles).  Runs are compared bit-exact, rows to the usual tolerance."""
+    """Run-length tiles of 4096 sorted positions: up to 128 tiles the run
+    write alone (look-back over the tile counts), up to 1024 the count kernel
+    and a run write that sums the counts itself, beyond that the scan kernel
+    too; each limit and one more.  300 000 lookups also take the sort's
+    separate offset scan (over 32 sort tiles).  Runs are compared bit-exact,
+    rows to the usual tolerance."""
     s = synth.Spec("tiles", 1, (60000,), (4,), 0, ("fixed", 1), ("zipf", 1.05), "none", False,
                    "f32", "dense", accumulate=True, nobag_tokens=tokens, seed=41)
     inp = synth.generate(s)
