@@ -4,14 +4,19 @@
 One step = one sgb_backward() call -- the whole path: linearise, radix sort,
 run-length encode, long-run split, segmented reduce and the fused row write
 -- over one synthetic batch already resident in HBM.  Default workload: the
-T=8 x E=100k x D=128 dense-gradient configuration (mean pooling with
-per-sample weights, Zipf 1.05, B=2048); --config selects another one.
+largest one that fits one GPU, T=32 tables x E=1M rows with D = 64/128/256
+cycling (18.7 GB of weights), B=16384 bags of Poisson(20) lookups drawn
+Zipf(1.2), sum pooling, fused row-wise Adagrad; --config selects another one.
 
 Prints ONE JSON line on stdout (progress goes to stderr):
   value        lookups/s of the whole step (wall clock, synchronised)
+  achieved_GBps_path   the whole path's algorithmic bytes / step time
+  counter_GBps_path    HBM bytes the FETCH_SIZE / WRITE_SIZE counters measured
+               for every kernel of the step (profiles/pmc_traffic.txt, when
+               taken on the current kernel sources) / step time
   roofline     the dominant kernel (largest time per step): algorithmic bytes
                per launch / its mean launch duration from HIP events around it
-  cpu_baseline the CPU oracle (plain C, one thread) on the same batch
+  cpu_baseline the CPU oracle (plain C, one thread) on a bounded sample
 """
 from __future__ import annotations
 
@@ -31,9 +36,9 @@ import synth  # noqa: E402
 
 METRIC = "embedding-bwd lookups/sec + achieved HBM GB/s (% of MI355X peak), 1 GPU"
 HBM_PEAK_GBPS = 8000.0
-STAGES = ("linearize", "sort_count", "sort_offsets", "sort_scatter", "sort", "rle_count",
+STAGES = ("linearize", "sort_pass", "sort", "rle_count",
           "rle_scan", "rle_write", "runs", "fill", "reduce_long", "reduce_short")
-SORT_KERNELS = ("sort_count", "sort_offsets", "sort_scatter")  # timed on the first pass
+SORT_KERNELS = ("sort_pass",)  # one launch per radix pass, timed on the first pass
 # run-length tiles of 4096 sorted positions up to which the library encodes
 # runs in one kernel (k_rle_write alone; the count and scan stages then time
 # no kernel)
@@ -49,10 +54,15 @@ def log(*a):
 
 
 def stage_bytes(inp: synth.Inputs, spec: synth.Spec, U: int, run_D: np.ndarray,
-                run_len: np.ndarray, thr: int, npasses: int, radix0: int):
+                run_len: np.ndarray, thr: int, npasses: int, radix0: int,
+                long_rows_D: int | None = None):
     """Algorithmic bytes of one launch of each kernel: every input read once,
     every output written once; a radix pass reads and writes the packed words
-    (and coefficients) once; each run's gather and row update once."""
+    (and coefficients) once; each run's gather and row update once.
+    `long_rows_D` (if given) is the sum of D over the grad_output rows the
+    long-run reducer reads: it reads a bag's row once for all of the bag's
+    lookups of one chunk (see long_gather_elems), so the long runs' gather is
+    counted by rows read, not by lookups."""
     N = inp.N
     c = 1 if (spec.pooling == "mean" or spec.weighted) else 0
     sg = 2 if spec.grad_dtype == "bf16" else 4
@@ -62,8 +72,10 @@ def stage_bytes(inp: synth.Inputs, spec: synth.Spec, U: int, run_D: np.ndarray,
     Ds = np.diff(inp.D_offsets).astype(np.int64)
     Es = np.diff(inp.hash_size_cumsum).astype(np.int64)
     touched_elems = int(run_D.sum())
-    # sort tiles: 256 threads x 8 items for batches up to 2^20 lookups, x 12 above
-    sort_tile = 256 * (8 if N <= (1 << 20) else 12)
+    # tiles of the first radix pass: 1024 x 12 items above 2^20 lookups (digits
+    # of up to 9 bits), 512 x 8 above 2^16, else 256 x 8
+    sort_tile = 1024 * 12 if (N > (1 << 20) and radix0 <= 512) else (
+        512 * 8 if N > (1 << 16) else 256 * 8)
     tiles = (N + sort_tile - 1) // sort_tile
     scan_tiles = (N + 4095) // 4096
     one_pass = scan_tiles <= RLE_ONE_PASS_TILES
@@ -77,23 +89,24 @@ def stage_bytes(inp: synth.Inputs, spec: synth.Spec, U: int, run_D: np.ndarray,
 
     lg = run_len >= thr
     gather_long = int((run_len[lg] * run_D[lg]).sum()) * sg
+    gather_long_read = gather_long if long_rows_D is None else int(long_rows_D) * sg
     gather_short = int((run_len[~lg] * run_D[~lg]).sum()) * sg
     b = {
         "linearize": N * (8 + 8 + 4 * c + (4 if spec.weighted else 0)) + (BT + 1) * 8 * (BT > 0),
-        "sort_count": N * 8 + tiles * radix0 * 4,
-        "sort_offsets": tiles * radix0 * 4 * 2 + radix0 * 4,
-        "sort_scatter": N * rec * 2 + tiles * radix0 * 4 + radix0 * 4,
+        # a pass reads and writes every packed word (and coefficient) once,
+        # its digit totals, and publishes two look-back words per tile and digit
+        "sort_pass": N * rec * 2 + tiles * radix0 * 4 * 2 + 8 * radix0 * 4,
         "rle_count": 0 if one_pass else N * 8 + scan_tiles * 4,
         "rle_scan": 0 if one_pass else scan_tiles * 4 * 2 + 8,
         "rle_write": N * 8 + scan_tiles * 4 * (2 if one_pass else 1) + U * (8 + 4 + 4),
         "runs": U * (4 + 4) + int(lg.sum()) * (48 + 4 + 4),
         "fill": int((Es * Ds).sum()) * 4 if fresh else 0,
-        "reduce_long": gather_long + int(run_len[lg].sum()) * rec + int(lg.sum()) * 48
+        "reduce_long": gather_long_read + int(run_len[lg].sum()) * rec + int(lg.sum()) * 48
         + update(run_D[lg]),
         "reduce_short": gather_short + N * 8 + int(run_len[~lg].sum()) * 4 * c
         + int((~lg).sum()) * 8 + update(run_D[~lg]),
     }
-    b["sort"] = npasses * (b["sort_count"] + b["sort_offsets"] + b["sort_scatter"])
+    b["sort"] = npasses * b["sort_pass"]
     # whole path, counted as the contract's byte model: indices read, the
     # sorted stream (8-byte id + 4-byte info + coefficient) written and read
     # once, the gather, offsets, 24 bytes per run, the row update
@@ -107,6 +120,54 @@ def stage_bytes(inp: synth.Inputs, spec: synth.Spec, U: int, run_D: np.ndarray,
         + (N * 4 if spec.weighted else 0) \
         + (int((Es * Ds).sum()) * 4 if fresh else update(run_D))
     return b, b_path, b_comp
+
+
+def chunk_len(run_len: np.ndarray, D: np.ndarray, N: int) -> np.ndarray:
+    """Lookups per chunk of each long run, as the library cuts them: a base of
+    128..512 lookups grown with the batch (one doubling per 2 * 8192 lookups
+    above 128 * 8192), divided by the row's 256-column blocks with a floor of
+    128, and never more than 1024 chunks per run."""
+    base = 128
+    while base < 512 and base * 2 * 8192 <= N:
+        base *= 2
+    cmin = np.maximum(base // ((D + 255) // 256), 128)
+    return np.maximum((run_len + 1023) // 1024, cmin)
+
+
+def lanes_per_row(D: int) -> int:
+    """Lanes of a lane group serving a row of D columns at 4 columns per lane:
+    the power of two covering D / 4, from 4 to 64."""
+    need, lpl = (D + 3) // 4, 4
+    while lpl < need and lpl < 64:
+        lpl *= 2
+    return lpl
+
+
+def long_gather_elems(sorted_info: np.ndarray, cum: np.ndarray, run_len: np.ndarray,
+                      run_D: np.ndarray, thr: int, N: int) -> int:
+    """Sum of D over the grad_output rows the long-run reducer reads.  A chunk
+    is shared by the 64 / lpl lane groups of a wave in contiguous parts, and
+    each group takes its part lpl lookups at a time; within such a slice,
+    adjacent lookups of one bag share their grad_output row, which is read
+    once (their coefficients are summed first)."""
+    lg = np.nonzero(run_len >= thr)[0]
+    total = 0
+    for r in lg:
+        s0, L, D = int(cum[r]), int(run_len[r]), int(run_D[r])
+        cl = int(chunk_len(np.array([L]), np.array([D]), N)[0])
+        lpl = lanes_per_row(D)
+        ng = 64 // lpl
+        pos = np.arange(L, dtype=np.int64)
+        lo = (pos // cl) * cl
+        n = np.minimum(cl, L - lo)
+        per = (n + ng - 1) // ng
+        off = pos - lo
+        within = off - (off // per) * per
+        inf = sorted_info[s0:s0 + L]
+        new = within % lpl == 0
+        new[1:] |= inf[1:] != inf[:-1]
+        total += int(new.sum()) * D
+    return total
 
 
 def short_kernels(dims) -> str:
@@ -131,30 +192,54 @@ def kernel_digest() -> str:
     return h.hexdigest()[:12]
 
 
-def measured_traffic(workload: str, kernel: str):
-    """HBM bytes per launch of one kernel, from the FETCH_SIZE and WRITE_SIZE
-    counter runs recorded in profiles/pmc_traffic.txt (already scaled by the
-    copy-kernel calibration), or None when no figure exists for the current
-    kernel sources."""
+def traffic_table(workload: str) -> dict:
+    """HBM bytes per launch of every kernel of one workload, {kernel: (fetch,
+    write)}, from the FETCH_SIZE and WRITE_SIZE counter runs recorded in
+    profiles/pmc_traffic.txt (already scaled by the copy-kernel calibration);
+    empty when no figures exist for the current kernel sources."""
     if not os.path.exists(TRAFFIC_FILE):
-        return None
+        return {}
     src = kernel_digest()
+    out = {}
     for line in open(TRAFFIC_FILE):
         f = line.split()
-        if len(f) < 4 or f[0] != "kernel" or f[1] != workload or f[2] != kernel:
+        if len(f) < 4 or f[0] != "kernel" or f[1] != workload:
             continue
-        kv = dict(x.split("=", 1) for x in f[3:])
-        if kv.get("src") == src:
-            return float(kv["fetch_bytes"]) + float(kv["write_bytes"])
-    return None
+        # the kernel name may hold spaces ("k_reduce_long[bf16 rows]"): it runs
+        # up to the first key=value field
+        k = next(i for i, x in enumerate(f) if "=" in x or i == len(f) - 1)
+        name = " ".join(f[2:k])
+        kv = dict(x.split("=", 1) for x in f[k:] if "=" in x)
+        if kv.get("src") == src and "fetch_bytes" in kv and "write_bytes" in kv:
+            out[name] = (float(kv["fetch_bytes"]), float(kv["write_bytes"]))
+    return out
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of one kernel ('a+b' names sum their kernels), or
+    None when the counters were not taken on the current kernel sources."""
+    tab = traffic_table(workload)
+    parts = kernel.split("+")
+    if not all(k in tab for k in parts):
+        return None
+    return float(sum(sum(tab[k]) for k in parts))
+
+
+def counter_path_bytes(workload: str, launches: dict):
+    """HBM bytes of one whole step by the counters: each path kernel's
+    measured bytes per launch times its launches per step (`launches`:
+    {kernel: count}); None unless every kernel has a figure for the current
+    sources."""
+    tab = traffic_table(workload)
+    if not launches or not all(k in tab for k in launches):
+        return None
+    return float(sum(sum(tab[k]) * n for k, n in launches.items()))
 
 
 def cpu_baseline(inp: synth.Inputs, spec: synth.Spec, thr: int, min_s: float, max_reps: int):
     """The CPU oracle as it stands (plain C, single thread) on the same batch."""
     import oracle
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from harness import oracle_problem
-    prob = oracle_problem(inp)
+    prob = oracle.problem_from_inputs(inp)
     reps, total = 0, 0.0
     while reps < max_reps and (reps == 0 or total < min_s):
         t0 = time.perf_counter()
@@ -181,7 +266,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--thr", type=int, default=None,
                     help="max_segment_length_per_warp (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -298,7 +383,10 @@ def main():
     cold_ms = float(np.median([c0.elapsed_time(c1) for c0, c1 in cold_ev]))
     del flush
     status = plan.device_status(ws)
-    fwd = forward_measure(plan, inp, spec, indices, offsets, psw, out, ws, args.steps)
+    uniq_v = view["unique_ids"].cpu().numpy()
+    rows_D = int(np.diff(inp.D_offsets).astype(np.int64)[
+        np.searchsorted(inp.hash_size_cumsum, uniq_v, side="right") - 1].sum())
+    fwd = forward_measure(plan, inp, spec, indices, offsets, psw, out, ws, args.steps, rows_D)
     bf16w = bf16_weights_measure(plan, spec, grad_output, indices, offsets, B, psw, out, mom, ws,
                                  args.steps, ms_per_step)
     int8w = int8_weights_measure(plan, inp, spec, grad_output, indices, offsets, B, psw, mom, ws,
@@ -315,12 +403,17 @@ def main():
     nlong = view["num_long"]
     npasses = plan_npasses(inp)
     radix0 = 1 << pass_bits0(inp)
-    sb, b_path, b_comp = stage_bytes(inp, spec, U, run_D, lens, thr, npasses, radix0)
+    packed = view["sorted_packed"].cpu().numpy().view(np.uint64)
+    infos = (packed & np.uint64((1 << view["info_bits"]) - 1)).astype(np.int64)
+    cum = view["cumulative"].cpu().numpy().astype(np.int64)
+    long_D = long_gather_elems(infos, cum, lens, run_D, thr, inp.N) \
+        if spec.pooling != "none" else None
+    del packed, infos
+    sb, b_path, b_comp = stage_bytes(inp, spec, U, run_D, lens, thr, npasses, radix0, long_D)
     # the stage that each kernel times ("sort" spans the passes; on few tiles
     # the run-head count and scan stages are done inside k_rle_write)
     kernel_names = {"reduce_long": "k_reduce_long", "fill": "k_fill", "linearize": "k_linearize",
-                    "sort_count": "k_sort_count", "sort_offsets": "k_sort_offsets",
-                    "sort_scatter": "k_sort_scatter", "rle_write": "k_rle_write", "runs": "k_post",
+                    "sort_pass": "k_sort_pass", "rle_write": "k_rle_write", "runs": "k_post",
                     "reduce_short": short_kernels(np.diff(inp.D_offsets))}
     if (inp.N + 4095) // 4096 > RLE_ONE_PASS_TILES:
         kernel_names.update(rle_count="k_rle_count", rle_scan="k_rle_scan")
@@ -332,6 +425,16 @@ def main():
     per_launch_ms = stage_ms[dom]
     achieved = per_launch_bytes / (per_launch_ms * 1e-3) / 1e9
     gbps_path = b_path / (ms_per_step * 1e-3) / 1e9
+    # the whole step by the counters: every kernel of the step, times its
+    # launches per step
+    launches = {}
+    for k, name in kernel_names.items():
+        if k not in stage_ms:
+            continue
+        for kn in name.split("+"):
+            launches[kn] = npasses if k in SORT_KERNELS else 1
+    cnt_bytes = counter_path_bytes(spec.name, launches)
+    cnt_gbps = None if cnt_bytes is None else cnt_bytes / (ms_per_step * 1e-3) / 1e9
     log(f"stages (ms): " + ", ".join(f"{k}={v:.4f}" for k, v in stage_ms.items()))
     log(f"step {ms_per_step:.4f} ms (instrumented {ms_timed:.4f} ms); path {gbps_path:.0f} GB/s")
 
@@ -361,6 +464,9 @@ def main():
         "achieved_GBps_path": gbps_path,
         "hbm_pct_path": 100.0 * gbps_path / HBM_PEAK_GBPS,
         "bytes_alg_path": int(b_path),
+        "counter_bytes_path": cnt_bytes,
+        "counter_GBps_path": cnt_gbps,
+        "hbm_pct_path_counters": None if cnt_gbps is None else 100.0 * cnt_gbps / HBM_PEAK_GBPS,
         "bytes_compulsory": int(b_comp),
         "achieved_GBps_compulsory": b_comp / (ms_per_step * 1e-3) / 1e9,
         "cold": {"ms_per_call_median": cold_ms, "value": inp.N / (cold_ms * 1e-3),
@@ -383,12 +489,16 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-def forward_measure(plan, inp, spec, indices, offsets, psw, table, ws, steps) -> dict:
+def forward_measure(plan, inp, spec, indices, offsets, psw, table, ws, steps,
+                    rows_D: int) -> dict:
     """The pooled forward (sgb_forward) on the same lookups, reading `table`
     (the workload's weights, or for a dense-gradient workload its gradient
     buffer, which has the weights' shape), timed by HIP events around
-    `steps` back-to-back calls.  Algorithmic bytes per call: each lookup's
-    weight row, index (and weight), the offsets, and the output written."""
+    `steps` back-to-back calls.  Its rate is given by compulsory bytes: each
+    distinct weight row read once (`rows_D` = the sum of D over the distinct
+    rows looked up), the indices (and weights) and offsets read once, the
+    output written once; rows looked up again are served by the caches, so
+    counting a row per lookup would overstate the HBM rate."""
     B = inp.B if inp.offsets is not None else 0
     doff = inp.D_offsets
     Ds = np.diff(doff).astype(np.int64)
@@ -397,12 +507,7 @@ def forward_measure(plan, inp, spec, indices, offsets, psw, table, ws, steps) ->
     else:
         shape = (inp.B, int(doff[-1]))
     res = torch.empty(shape, dtype=torch.float32, device=table.device)
-    if inp.offsets is not None:
-        per_table = np.diff(inp.offsets[::inp.B]) if inp.B > 0 else np.zeros(inp.T, np.int64)
-        gather = int((per_table * Ds).sum()) * 4
-    else:
-        gather = inp.N * int(Ds[0]) * 4
-    bytes_alg = gather + inp.N * (8 + (4 if inp.per_sample_weights is not None else 0)) \
+    bytes_comp = int(rows_D) * 4 + inp.N * (8 + (4 if inp.per_sample_weights is not None else 0)) \
         + ((B * inp.T + 1) * 8 if inp.offsets is not None else 0) + int(np.prod(shape)) * 4
 
     def call():
@@ -419,11 +524,13 @@ def forward_measure(plan, inp, spec, indices, offsets, psw, table, ws, steps) ->
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     status = plan.device_status(ws)
-    gbps = bytes_alg / (ms * 1e-3) / 1e9
-    return {"ms_per_call": ms, "lookups_per_s": inp.N / (ms * 1e-3), "bytes_alg": int(bytes_alg),
-            "device_status": status,
+    gbps = bytes_comp / (ms * 1e-3) / 1e9
+    return {"ms_per_call": ms, "lookups_per_s": inp.N / (ms * 1e-3),
+            "bytes_compulsory": int(bytes_comp), "device_status": status,
             "roofline": {"bound": "hbm", "kernel": "k_forward", "achieved": gbps,
-                         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS}}
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
+                         "bytes": "compulsory",
+                         "traffic": measured_traffic(spec.name, "k_forward")}}
 
 
 def bf16_weights_measure(plan, spec, grad_output, indices, offsets, B, psw, out, mom, ws, steps,

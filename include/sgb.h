@@ -205,22 +205,20 @@ sgb_status sgb_backward(sgb_plan plan, const sgb_batch* batch, const sgb_update*
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* Timed regions of sgb_backward() (see sgb_backward_timed): one per kernel,
- * in launch order, plus SGB_STAGE_SORT spanning every radix pass.  The three
- * sort-pass kernels are timed on the first pass. */
+ * in launch order, plus SGB_STAGE_SORT spanning every radix pass. */
 typedef enum {
-  SGB_STAGE_LINEARIZE = 0,     /* bags -> packed (linear id, info) words         */
-  SGB_STAGE_SORT_COUNT = 1,    /* radix pass: digit counts of every tile          */
-  SGB_STAGE_SORT_OFFSETS = 2,  /* radix pass: digit offsets of every tile         */
-  SGB_STAGE_SORT_SCATTER = 3,  /* radix pass: stable rank and scatter             */
-  SGB_STAGE_SORT = 4,          /* all radix passes                                */
-  SGB_STAGE_RLE_COUNT = 5,     /* run heads of every tile (inside stage 7: empty) */
-  SGB_STAGE_RLE_SCAN = 6,      /* first run index of every tile (inside 7: empty) */
-  SGB_STAGE_RLE_WRITE = 7,     /* run heads, tile scan, unique ids, run starts    */
-  SGB_STAGE_RUNS = 8,          /* run lengths, long-run list, chunk prefix        */
-  SGB_STAGE_FILL = 9,          /* zeros of the whole gradient (fresh dense only)  */
-  SGB_STAGE_REDUCE_LONG = 10,  /* long runs: chunked reduction + fused row write  */
-  SGB_STAGE_REDUCE_SHORT = 11, /* short runs: reduction + fused row write         */
-  SGB_NUM_STAGES = 12
+  SGB_STAGE_LINEARIZE = 0,     /* bags -> packed (linear id, info) words, and the
+                                  first radix pass's digit histogram             */
+  SGB_STAGE_SORT_PASS = 1,     /* the first radix pass alone                     */
+  SGB_STAGE_SORT = 2,          /* all radix passes                               */
+  SGB_STAGE_RLE_COUNT = 3,     /* run heads of every tile (inside stage 5: empty) */
+  SGB_STAGE_RLE_SCAN = 4,      /* first run index of every tile (inside 5: empty) */
+  SGB_STAGE_RLE_WRITE = 5,     /* run heads, tile scan, unique ids, run starts    */
+  SGB_STAGE_RUNS = 6,          /* run lengths, long-run list, chunk prefix        */
+  SGB_STAGE_FILL = 7,          /* zeros of the whole gradient (fresh dense only)  */
+  SGB_STAGE_REDUCE_LONG = 8,   /* long runs: chunked reduction + fused row write  */
+  SGB_STAGE_REDUCE_SHORT = 9,  /* short runs: reduction + fused row write         */
+  SGB_NUM_STAGES = 10
 } sgb_stage;
 
 /*

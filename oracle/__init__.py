@@ -127,6 +127,16 @@ class Problem:
                         1 if g is not None and g.dtype == np.uint16 else 0)
 
 
+def problem_from_inputs(inp) -> Problem:
+    """The Problem of a generated batch (any object with the fields of
+    ``synth.Inputs``: T, B, hash_size_cumsum, D_offsets, offsets, indices,
+    per_sample_weights, grad_output and ``spec.pooling``)."""
+    return Problem(T=inp.T, B=inp.B, hash_size_cumsum=inp.hash_size_cumsum,
+                   D_offsets=inp.D_offsets, offsets=inp.offsets, indices=inp.indices,
+                   per_sample_weights=inp.per_sample_weights, pooling=inp.spec.pooling,
+                   grad_output=inp.grad_output)
+
+
 def _check(st: int, what: str):
     if st != 0:
         raise OracleError(STATUS.get(st, str(st)), what)

@@ -163,7 +163,7 @@ def _stream(stream) -> Optional[int]:
     return int(s.cuda_stream)
 
 
-STAGES = ("linearize", "sort_count", "sort_offsets", "sort_scatter", "sort", "rle_count",
+STAGES = ("linearize", "sort_pass", "sort", "rle_count",
           "rle_scan", "rle_write", "runs", "fill", "reduce_long", "reduce_short")
 
 

@@ -96,11 +96,13 @@ struct Layout {
   int npasses = 0;
   int pass_bits[kMaxPasses] = {};
   int pass_key_shift[kMaxPasses] = {};
-  int64_t sort_tiles = 0, scan_tiles = 0;
+  int pass_shape[kMaxPasses] = {};
+  int64_t pass_tiles[kMaxPasses] = {};
+  int64_t scan_tiles = 0;
   int64_t max_long = 0;   // bound on the number of long runs
   int64_t max_items = 0;  // bound on the (chunk, column block) items over all long runs
-  size_t hdr = 0, hist = 0, counts = 0, zero_begin = 0, rle_lb = 0, post_lb = 0, zero_end = 0,
-         tile_runs = 0;
+  size_t hdr = 0, hist0 = 0, zero_begin = 0, hist[kMaxPasses] = {}, sort_lb[kMaxPasses] = {},
+         rle_lb = 0, post_lb = 0, zero_end = 0, tile_runs = 0;
   size_t kvA = 0, kvB = 0, coefA = 0, coefB = 0, uniq = 0, cum = 0, headrun = 0, lens = 0, longs = 0,
          chunkb = 0, longrec = 0, runtk = 0, sctk = 0, part = 0, total = 0;
 };
@@ -124,15 +126,15 @@ sgb_status make_layout(const sgb_plan_s* p, int64_t N, int32_t B, bool has_offse
   if (L->npasses > kMaxPasses) return SGB_ERR_UNSUPPORTED;  // linear ids >= 2^40
   int at = 0;
   for (int i = 0; i < L->npasses; ++i) {
+    // the wider digits first: every later pass's digits fit the tables of
+    // the pass before it
     L->pass_bits[i] = p->key_bits / L->npasses + (i < p->key_bits % L->npasses ? 1 : 0);
     L->pass_key_shift[i] = at;
     at += L->pass_bits[i];
+    L->pass_shape[i] = sort_shape_for(N, L->pass_bits[i]);
+    const int64_t tile = sort_tile_items(L->pass_shape[i]);
+    L->pass_tiles[i] = (N + tile - 1) / tile;
   }
-  const int64_t sort_tile = (int64_t)kSortThreads * sort_items_for(N);
-  L->sort_tiles = (N + sort_tile - 1) / sort_tile;
-  // the tile counts are sized for the smallest tiles, so a workspace sized
-  // for N also fits every smaller batch
-  const int64_t max_sort_tiles = (N + kSortThreads * kSortItemsSmall - 1) / (kSortThreads * kSortItemsSmall);
   L->scan_tiles = (N + kScanTile - 1) / kScanTile;
   L->max_long = N / p->thr + 1;
   // a long run of len lookups in a table of width D has ceil(len / chunk_len)
@@ -149,14 +151,34 @@ sgb_status make_layout(const sgb_plan_s* p, int64_t N, int32_t B, bool has_offse
     return at_;
   };
   L->hdr = take(sizeof(Header));
-  L->hist = take(sizeof(uint32_t) * kMaxPasses * kRadixMax);  // digit bases of each pass
+  // the first pass's digit histogram (cleared by k_linearize's first workgroup)
+  L->hist0 = take(sizeof(uint32_t) * kHistSlices * kRadixMax);
+  // cleared by k_linearize for the kernels after it: the later passes'
+  // histograms, the look-back words of each radix pass, of the run-length
+  // encoding and of the run post-processing, the long-run combine tickets
   L->zero_begin = align_up(o, 256);
+  L->hist[0] = L->hist0;
+  for (int i = 1; i < L->npasses; ++i) L->hist[i] = take(sizeof(uint32_t) * kHistSlices << L->pass_bits[i]);
   L->rle_lb = take(sizeof(uint32_t) * (size_t)L->scan_tiles);  // one pass only
   L->post_lb = take(sizeof(uint64_t) * (size_t)L->scan_tiles);
   L->runtk = take(sizeof(uint32_t) * (size_t)L->max_items);
   L->sctk = take(sizeof(uint32_t) * (size_t)L->max_items);
-  L->zero_end = align_up(o, 256);
-  L->counts = take(sizeof(uint32_t) * (size_t)max_sort_tiles * kRadixMax);
+  // the radix passes' look-back words, packed by this batch's tile shapes
+  // (only they are cleared), in room for the most tiles any shape gives, so
+  // that a workspace sized for N fits every smaller batch
+  const size_t lb0 = align_up(o, 256);
+  size_t used = 0, room = 0;
+  auto lb_words = [](int64_t tiles) {  // tile words and group words
+    return (size_t)(tiles + (tiles + kSortLbGroup - 1) / kSortLbGroup);
+  };
+  for (int i = 0; i < L->npasses; ++i) {
+    L->sort_lb[i] = lb0 + used;
+    used += align_up(sizeof(uint32_t) * lb_words(L->pass_tiles[i]) << L->pass_bits[i], 256);
+    room += align_up(sizeof(uint32_t) * lb_words((N + kSortTileMin - 1) / kSortTileMin)
+                         << L->pass_bits[i], 256);
+  }
+  L->zero_end = lb0 + used;
+  o = lb0 + room;
   L->tile_runs = take(sizeof(uint32_t) * (size_t)L->scan_tiles);
   L->kvA = take(sizeof(uint64_t) * (size_t)N);
   L->kvB = take(sizeof(uint64_t) * (size_t)N);
@@ -424,9 +446,13 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   lp.header = hdr;
   lp.zero_begin = at<uint4>(ws, L.zero_begin);
   lp.zero_vec4 = (int64_t)((L.zero_end - L.zero_begin) / 16);
+  lp.hist = L.npasses > 0 ? at<uint32_t>(ws, L.hist0) : nullptr;
+  lp.hist_bits = L.npasses > 0 ? L.pass_bits[0] : 0;
+  lp.hist_ready = &hdr->hist_ready;
   const int64_t lin_tiles = b->offsets ? ((int64_t)b->B * p->T + kLinBags - 1) / kLinBags
                                        : (N + kLinLookups - 1) / kLinLookups;
-  const int lin_grid = (int)std::max<int64_t>(1, std::min<int64_t>(lin_tiles, 16ll * p->num_cus));
+  const int lin_grid =
+      (int)std::max<int64_t>(1, std::min<int64_t>(lin_tiles, (int64_t)SGB_LIN_WG_PER_CU * p->num_cus));
   mark(SGB_STAGE_LINEARIZE, 0);
   if (launch_linearize(lp, lin_grid, stream) != hipSuccess) return SGB_ERR_HIP;
   mark(SGB_STAGE_LINEARIZE, 1);
@@ -444,19 +470,22 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
     sp.kv_out = kv_out;
     sp.coef_out = cf_out;
     sp.N = N;
-    sp.tiles = L.sort_tiles;
-    sp.items = sort_items_for(N);
-    sp.fuse_offsets = L.sort_tiles <= kFuseTiles ? 1 : 0;
+    sp.tiles = (int32_t)L.pass_tiles[ps];
+    sp.shape = L.pass_shape[ps];
     sp.shift = L.info_bits + L.pass_key_shift[ps];
     sp.bits = L.pass_bits[ps];
-    sp.counts = at<uint32_t>(ws, L.counts);
-    sp.bases = at<uint32_t>(ws, L.hist) + ps * kRadixMax;
+    sp.hist = at<uint32_t>(ws, L.hist[ps]);
+    const bool last = ps + 1 == L.npasses;
+    sp.hist_next = last ? nullptr : at<uint32_t>(ws, L.hist[ps + 1]);
+    sp.shift_next = last ? 0 : L.info_bits + L.pass_key_shift[ps + 1];
+    sp.bits_next = last ? 0 : L.pass_bits[ps + 1];
+    sp.lookback = at<uint32_t>(ws, L.sort_lb[ps]);
+    sp.tile_ctr = &hdr->sort_tile_ctr[ps];
     sp.status = status;
     sp.epoch = epoch;
-    // the kernels of the first pass are timed one by one
-    const std::function<void(int, int)> pass_mark =
-        ps == 0 ? std::function<void(int, int)>(mark) : std::function<void(int, int)>();
-    if (launch_sort_pass(sp, stream, pass_mark) != hipSuccess) return SGB_ERR_HIP;
+    if (ps == 0) mark(SGB_STAGE_SORT_PASS, 0);
+    if (launch_sort_pass(sp, stream) != hipSuccess) return SGB_ERR_HIP;
+    if (ps == 0) mark(SGB_STAGE_SORT_PASS, 1);
     std::swap(kv_in, kv_out);
     std::swap(cf_in, cf_out);
   }

@@ -19,15 +19,6 @@ constexpr int kColBlock = 256;        // columns one wave covers per pass (64 la
 constexpr int kMaxD = 8192;
 
 // Tuning knobs (compile-time; the defaults are the measured best).
-#ifndef SGB_SORT_ITEMS_SMALL
-#define SGB_SORT_ITEMS_SMALL 8
-#endif
-#ifndef SGB_SORT_ITEMS_LARGE
-#define SGB_SORT_ITEMS_LARGE 12
-#endif
-#ifndef SGB_SORT_SMALL_N
-#define SGB_SORT_SMALL_N (1 << 20)
-#endif
 #ifndef SGB_SHORT_UNR
 #define SGB_SHORT_UNR 2
 #endif
@@ -73,26 +64,46 @@ constexpr int kMaxD = 8192;
 #ifndef SGB_FILL_THREADS
 #define SGB_FILL_THREADS 256
 #endif
+#ifndef SGB_LIN_WG_PER_CU
+#define SGB_LIN_WG_PER_CU 16
+#endif
+#ifndef SGB_LOOKBACK
+#define SGB_LOOKBACK 16
+#endif
+constexpr int kSortLbGroup = 16;  // tiles per look-back group of a radix pass
 
-// sort pass tiling: items per thread of a tile, fewer for small batches
-// (more, shorter tiles fill the GPU and finish sooner) than for large ones
-constexpr int kSortThreads = 256;
-constexpr int kSortItemsSmall = SGB_SORT_ITEMS_SMALL;
-constexpr int kSortItemsLarge = SGB_SORT_ITEMS_LARGE;
-static_assert(kSortItemsSmall <= kSortItemsLarge, "small batches take the smaller tiles");
-__host__ __device__ inline int sort_items_for(int64_t N) {
-  return N <= (int64_t)SGB_SORT_SMALL_N ? kSortItemsSmall : kSortItemsLarge;
+// Radix pass tiling.  A pass is one kernel (k_sort_pass) whose workgroups
+// each sort one tile of TPB threads x ITEMS items; the shape depends on the
+// batch and on the pass's digit width (its LDS holds the tile and one digit
+// table per wave, so 10-bit digits take the smaller tiles):
+//   large  1024 x 12 (12288 items), digits up to 9 bits, N > kSortLargeN
+//   medium  512 x 8  ( 4096 items), N > kSortMediumN
+//   small   256 x 8  ( 2048 items)
+#ifndef SGB_SORT_LARGE_N
+#define SGB_SORT_LARGE_N (1 << 20)
+#endif
+#ifndef SGB_SORT_MEDIUM_N
+#define SGB_SORT_MEDIUM_N (1 << 16)
+#endif
+enum SortShape { kSortSmall = 0, kSortMedium = 1, kSortLarge = 2 };
+__host__ __device__ inline int sort_shape_for(int64_t N, int bits) {
+  if (N > (int64_t)SGB_SORT_LARGE_N && bits <= 9) return kSortLarge;
+  if (N > (int64_t)SGB_SORT_MEDIUM_N) return kSortMedium;
+  return kSortSmall;
 }
+__host__ __device__ inline int sort_tile_items(int shape) {
+  return shape == kSortLarge ? 1024 * 12 : (shape == kSortMedium ? 512 * 8 : 256 * 8);
+}
+// fewest items of any tile shape: bounds the tiles of a batch
+constexpr int kSortTileMin = 256 * 8;
+// copies of each pass's global digit histogram: workgroups add their counts
+// into copy (workgroup id mod kHistSlices), spreading same-address atomics;
+// readers sum the copies
+constexpr int kHistSlices = 8;
 
 // zero fill: threads of each (looping) workgroup
 constexpr int kFillThreads = SGB_FILL_THREADS;
 
-// up to this many tiles, a sort pass and the run-length encoding skip their
-// scan kernel: each tile sums the raw counts of the tiles before it
-#ifndef SGB_FUSE_TILES
-#define SGB_FUSE_TILES 32
-#endif
-constexpr int kFuseTiles = SGB_FUSE_TILES;
 // run-length tiles: up to kOnePassTiles k_rle_write alone (look-back over the
 // tile counts); up to kFuseScanTiles k_rle_count then k_rle_write summing the
 // counts itself; beyond, k_rle_count, k_rle_scan, k_rle_write
@@ -202,7 +213,9 @@ struct Header {
   int32_t num_runs;                   // U
   uint32_t total_items;               // chunks over all long runs
   int64_t num_long;                   // number of long runs
-  uint32_t pad[24];
+  uint32_t hist_ready;                // epoch once the first pass's histogram is zeroed
+  uint32_t sort_tile_ctr[4];          // dynamic tile ids of each radix pass
+  uint32_t pad[19];
 };
 static_assert(sizeof(Header) <= 128, "header too large");
 
@@ -247,6 +260,13 @@ struct LinParams {
   Header* header;           // epoch and counters reset by the first workgroup
   uint4* zero_begin;        // region zeroed for the later kernels
   int64_t zero_vec4;
+  // digit histogram of the first radix pass ([kHistSlices][1 << hist_bits]),
+  // NULL when the ids need no sorting: zeroed by workgroup 0, which then
+  // publishes the call's epoch in hist_ready; every workgroup adds its counts
+  // once it sees that epoch
+  uint32_t* hist;
+  int32_t hist_bits;        // the first pass's digit: the low hist_bits bits of the id
+  uint32_t* hist_ready;
 };
 
 struct SortParams {
@@ -255,15 +275,21 @@ struct SortParams {
   uint64_t* kv_out;
   float* coef_out;
   int64_t N;
-  int64_t tiles;            // tiles of kSortThreads * items lookups
-  int32_t items;            // sort_items_for(N)
+  int32_t tiles;            // tiles of sort_tile_items(shape) lookups
+  int32_t shape;            // sort_shape_for(N, bits)
   int32_t shift;
   int32_t bits;
-  uint32_t* counts;         // [radix][tiles]: tile digit counts, then their offsets
-  uint32_t* bases;          // [radix]: digit totals
+  const uint32_t* hist;     // [kHistSlices][1 << bits]: this pass's digit totals
+  uint32_t* hist_next;      // [kHistSlices][1 << bits_next] (zeroed), or NULL on the last pass
+  int32_t shift_next;
+  int32_t bits_next;
+  uint32_t* lookback;       // (zeroed) [tiles][1 << bits]: each tile's digit counts, then
+                            // its inclusive prefix over the tiles; then
+                            // [ceil(tiles / 16)][1 << bits]: per group of 16 tiles, its
+                            // total, then the inclusive prefix at its end
+  uint32_t* tile_ctr;       // (zeroed) tile ids in start order
   uint32_t* status;
   uint32_t epoch;
-  int32_t fuse_offsets;     // tiles <= kFuseTiles: the scatter derives its offsets itself
 };
 
 struct RleParams {
@@ -391,8 +417,7 @@ hipError_t launch_init(void* header_and_hist, size_t bytes, hipStream_t s);
 hipError_t launch_linearize(const LinParams& p, int grid, hipStream_t s);
 // `mark(stage, end)` (if set) records the timing events of a kernel's
 // timed region just before (end = 0) and after (end = 1) its launch.
-hipError_t launch_sort_pass(const SortParams& p, hipStream_t s,
-                            const std::function<void(int, int)>& mark);
+hipError_t launch_sort_pass(const SortParams& p, hipStream_t s);
 hipError_t launch_rle(const RleParams& p, hipStream_t s, const std::function<void(int, int)>& mark);
 hipError_t launch_post(const PostParams& p, int grid, hipStream_t s);
 hipError_t launch_fill(const FillParams& p, int grid, hipStream_t s);

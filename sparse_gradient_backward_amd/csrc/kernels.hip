@@ -80,6 +80,22 @@ __device__ __forceinline__ void set_status_wave(uint32_t* st, uint32_t epoch, ui
   if (m && lane_id() == __builtin_ctzll(m)) set_status(st, epoch, code);
 }
 
+// Adds 1 for this lane's digit d into the LDS histogram h: the lanes that
+// share the first valid lane's digit (on skewed ids usually the hot one) are
+// added by one atomic of their first lane.  Wave-uniform call.
+__device__ __forceinline__ void hist_add(uint32_t* h, uint32_t d, bool valid) {
+  const uint64_t live = __ballot(valid);
+  if (!live) return;
+  const int first = __builtin_ctzll(live);
+  const uint32_t d0 = (uint32_t)__shfl(d, first, 64);
+  const uint64_t same = __ballot(valid && d == d0);
+  if (valid && d == d0) {
+    if (lane_id() == first) atomicAdd(&h[d0], (uint32_t)__popcll(same));
+  } else if (valid) {
+    atomicAdd(&h[d], 1u);
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_incl_scan(T x) {
   const int lane = lane_id();
@@ -98,9 +114,9 @@ __device__ __forceinline__ T wave_sum(T x) {
   return x;
 }
 
-// Exclusive scan over the 256 threads of a block (one value each).  `tmp`
-// holds 4 values of LDS.  Contains two barriers.
-template <typename T>
+// Exclusive scan over the W waves of a block (one value per thread).  `tmp`
+// holds W values of LDS.  Contains two barriers.
+template <typename T, int W = 4>
 __device__ __forceinline__ T block_excl_scan(T x, T* tmp, T& total) {
   const int lane = lane_id(), w = threadIdx.x >> 6;
   const T inc = wave_incl_scan(x);
@@ -108,7 +124,7 @@ __device__ __forceinline__ T block_excl_scan(T x, T* tmp, T& total) {
   __syncthreads();
   T before = 0, all = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < W; ++i) {
     const T v = tmp[i];
     if (i < w) before += v;
     all += v;
@@ -204,13 +220,32 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
   __shared__ int64_t s_E[kLinBags];
   __shared__ int32_t s_t[kLinBags];
   __shared__ float s_scale[kLinBags];
+  __shared__ uint32_t s_dig[kRadixMax];  // this workgroup's first-pass digit counts
   __shared__ int s_bad;
   const int tid = threadIdx.x;
-  if (blockIdx.x == 0 && tid == 0) {
-    p.header->epoch = p.epoch;
-    p.header->post_tile_ctr = 0u;
-    p.header->rle_tile_ctr = 0u;
+  const int radix0 = p.hist ? (1 << p.hist_bits) : 0;
+  const uint32_t dmask0 = (uint32_t)radix0 - 1u;
+  if (blockIdx.x == 0) {
+    if (tid == 0) {
+      p.header->epoch = p.epoch;
+      p.header->post_tile_ctr = 0u;
+      p.header->rle_tile_ctr = 0u;
+#pragma unroll
+      for (int i = 0; i < kMaxPasses; ++i) p.header->sort_tile_ctr[i] = 0u;
+    }
+    // the first pass's histogram starts from zero: cleared here, before the
+    // epoch is published in hist_ready (the other workgroups add their counts
+    // only after they have seen it)
+    for (int i = tid; i < kHistSlices * radix0; i += kLinThreads)
+      __hip_atomic_store(&p.hist[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (tid == 0 && radix0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __hip_atomic_store(p.hist_ready, p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
+  for (int d = tid; d < radix0; d += kLinThreads) s_dig[d] = 0u;
+  // (s_dig is first written after the barrier of the first tile below)
 
   for (int64_t q = blockIdx.x * (int64_t)kLinThreads + tid; q < p.zero_vec4;
        q += (int64_t)gridDim.x * kLinThreads)
@@ -236,6 +271,7 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
           p.kv_out[i] = (key << p.info_bits) | (uint64_t)i;
         }
         set_status_wave(p.status, p.epoch, kStIndex, bad);
+        if (radix0) hist_add(s_dig, (uint32_t)key & dmask0, valid);
       }
     }
   } else {
@@ -323,119 +359,64 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
             if (p.coef_out) p.coef_out[i] = s_scale[lo] * w[k];
           }
           set_status_wave(p.status, p.epoch, kStIndex, bad);
+          if (radix0) hist_add(s_dig, (uint32_t)key & dmask0, valid);
         }
       }
       __syncthreads();
     }
+  }
+  if (!radix0) return;
+  // add this workgroup's counts into one copy of the first pass's histogram,
+  // once workgroup 0 has cleared it (it does so first, waiting for nothing)
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t spins = 0;
+    while (__hip_atomic_load(p.hist_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != p.epoch) {
+      if (++spins > kSpinLimit) {
+        set_status(p.status, p.epoch, kStInternal);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  }
+  __syncthreads();
+  uint32_t* h = p.hist + (size_t)(blockIdx.x % kHistSlices) * radix0;
+  for (int d = tid; d < radix0; d += kLinThreads) {
+    const uint32_t c = s_dig[d];
+    if (c) __hip_atomic_fetch_add(&h[d], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 // ------------------------------------------------------------------ radix sort
 //
 // One stable LSD pass over `bits` (<= 10) digit bits at `shift` of the packed
-// word, as reduce-then-scan in three kernels (no workgroup waits for another):
-//   k_sort_count    digit counts of every tile, stored digit-major
-//   k_sort_offsets  one workgroup per digit: exclusive scan of its counts over
-//                   the tiles, and the digit's total (each scatter workgroup
-//                   scans the totals into the digits' first positions)
-//   k_sort_scatter  ranks each tile's items by digit, stably, and writes each
-//                   digit group to its offset
-// Ranking (the multisplit of Adinets & Merrill, "Onesweep", 2022, done per
-// wave64): the lanes of one item round find their same-digit peers with one
-// ballot per digit bit -- a lane's peers are the lanes that agree with it on
-// every bit.  Its cost does not depend on the data; LDS atomics would
-// serialise on the hot digits of skewed keys.  Rank = per-wave running count
-// of the digit + peers in lower lanes.  Items are loaded wave-striped, so
-// (wave, item, lane) order is input order and the pass is stable.  The tile
-// is reordered by digit in LDS so the global writes of each digit group are
+// word is ONE kernel (a single sweep over the keys; the decoupled look-back of
+// Merrill & Garland, "Single-pass Parallel Prefix Scan with Decoupled
+// Look-back", 2016, kept per digit as in Adinets & Merrill, "Onesweep", 2022):
+//   - each workgroup takes the next tile id from a counter, so ids follow the
+//     order in which workgroups start and every earlier tile is running or
+//     done;
+//   - it ranks its items by digit, stably: the lanes of one item round find
+//     their same-digit peers with one ballot per digit bit (a lane's peers
+//     agree with it on every bit); rank = the wave's running count of the
+//     digit + peers in lower lanes.  Items are loaded wave-striped, so
+//     (wave, item, lane) order is input order.  The cost does not depend on
+//     the data (LDS atomics would serialise on the hot digits of skewed ids);
+//   - it publishes its per-digit counts, then, per digit, sums the counts of
+//     earlier tiles back to the nearest tile that has published its
+//     inclusive prefix (64 digits per wave, kLookback tiles per load round),
+//     and publishes its own inclusive prefix;
+//   - an item goes to base[digit] + items of its digit in earlier tiles +
+//     its rank in the tile, base being the exclusive scan of the pass's
+//     global digit histogram.  The histogram is counted before the pass: the
+//     first pass's by k_linearize, each later pass's by the pass before it
+//     (digit totals do not depend on the order of the keys).
+// The tile is reordered by digit in LDS so that each digit's writes are
 // contiguous; keys, then coefficients, pass through the same LDS buffer.
 
 __device__ __forceinline__ uint32_t digit_of(uint64_t kv, int shift, uint32_t dmask) {
   return (uint32_t)(kv >> shift) & dmask;
-}
-
-// Lanes of a wave that share a sub-histogram in k_sort_count: 2 copies per
-// wave halve same-address conflicts of skewed keys.
-constexpr int kCopiesPerWave = 2;
-constexpr int kCountCopies = (kSortThreads / 64) * kCopiesPerWave;
-// digits of the radix per thread in the scatter's per-digit steps
-constexpr int kDigitsPerThread = kRadixMax / kSortThreads;
-
-// The histograms take kCountCopies * radix words of dynamic LDS: sized to the
-// pass's digit width, so passes of 8 or 9 bits leave room for more resident
-// workgroups than the widest (10-bit) pass.
-template <int kSortItems>
-__global__ __launch_bounds__(kSortThreads) void k_sort_count(SortParams p) {
-  constexpr int kSortTile = kSortThreads * kSortItems;
-  extern __shared__ uint32_t s_hist[];
-  const int tid = threadIdx.x, w = (tid >> 6) * kCopiesPerWave + (tid & (kCopiesPerWave - 1));
-  const uint32_t tile = blockIdx.x;
-  const int radix = 1 << p.bits;
-  const uint32_t dmask = (uint32_t)radix - 1u;
-  auto s_h = [&](int copy) { return s_hist + copy * radix; };
-  for (int d = tid; d < kCountCopies * radix; d += kSortThreads) s_hist[d] = 0u;
-  const int64_t base = (int64_t)tile * kSortTile;
-  const int n = (int)min((int64_t)kSortTile, p.N - base);
-  uint64_t kv[kSortItems];
-#pragma unroll
-  for (int k = 0; k < kSortItems; ++k) {
-    const int q = k * kSortThreads + tid;
-    kv[k] = q < n ? p.kv_in[base + q] : 0ull;
-  }
-  __syncthreads();
-  // the lanes that share the first lane's digit (on skewed keys usually the
-  // hot one) are counted with one atomic by their first lane; the others
-  // add one each into their lane group's copy
-  const int lane = tid & 63;
-#pragma unroll
-  for (int k = 0; k < kSortItems; ++k) {
-    const bool valid = k * kSortThreads + tid < n;
-    const uint32_t d = digit_of(kv[k], p.shift, dmask);
-    const uint32_t d0 = __builtin_amdgcn_readfirstlane(d);
-    const uint64_t same = __ballot(valid && d == d0);
-    if (valid && d == d0) {
-      if (lane == __builtin_ctzll(same)) atomicAdd(&s_h(w)[d0], (uint32_t)__popcll(same));
-    } else if (valid) {
-      atomicAdd(&s_h(w)[d], 1u);
-    }
-  }
-  __syncthreads();
-  for (int d = tid; d < radix; d += kSortThreads) {
-    uint32_t c = 0;
-#pragma unroll
-    for (int ww = 0; ww < kCountCopies; ++ww) c += s_h(ww)[d];
-    p.counts[(size_t)d * p.tiles + tile] = c;
-  }
-}
-
-// Workgroup d: offsets[d][j] = items of digit d in tiles < j, in place over
-// the counts, and the row total of digit d.
-__global__ __launch_bounds__(kScanThreads) void k_sort_offsets(SortParams p) {
-  __shared__ uint32_t s_tmp[4];
-  const int tid = threadIdx.x;
-  const int d = blockIdx.x;
-  uint32_t* row = p.counts + (size_t)d * p.tiles;
-  uint32_t carry = 0;
-  for (int64_t c0 = 0; c0 < p.tiles; c0 += (int64_t)kScanThreads * kScanItems) {
-    uint32_t v[kScanItems];
-    uint32_t sum = 0;
-#pragma unroll
-    for (int k = 0; k < kScanItems; ++k) {
-      const int64_t j = c0 + (int64_t)tid * kScanItems + k;
-      v[k] = j < p.tiles ? row[j] : 0u;
-      sum += v[k];
-    }
-    uint32_t total;
-    uint32_t run = carry + block_excl_scan<uint32_t>(sum, s_tmp, total);
-#pragma unroll
-    for (int k = 0; k < kScanItems; ++k) {
-      const int64_t j = c0 + (int64_t)tid * kScanItems + k;
-      if (j < p.tiles) row[j] = run;
-      run += v[k];
-    }
-    carry += total;
-  }
-  if (tid == 0) p.bases[d] = carry;
 }
 
 // Same-digit peers of this lane among the valid lanes: the lanes that agree
@@ -455,145 +436,283 @@ __device__ __forceinline__ uint64_t digit_peers(uint32_t d, int bits, bool valid
   return valid ? (~(((uint64_t)mhi << 32) | mlo) & live) : 0ull;
 }
 
-template <int kSortItems>
-__global__ __launch_bounds__(kSortThreads) void k_sort_scatter(SortParams p) {
-  constexpr int kSortTile = kSortThreads * kSortItems;
-  __shared__ uint64_t s_kv[kSortTile];  // keys, then coefficients, in tile order by digit
-  __shared__ uint32_t s_tmp[4];
-  // per-digit tables sized to the pass's radix (dynamic LDS): each wave's
-  // running digit counts, the tile's digit offsets, the global bases
-  extern __shared__ uint32_t s_digit[];
-  const int radix = 1 << p.bits;
-  auto s_wcnt = [&](int wave) { return s_digit + wave * radix; };
-  uint32_t* s_local = s_digit + (kSortThreads / 64) * radix;
-  int32_t* s_gbase = reinterpret_cast<int32_t*>(s_local + radix);
+// Look-back rounds: tiles whose published words one lane loads at once.
+constexpr int kLookback = SGB_LOOKBACK;
+// Tiles per look-back group (the first level of the look-back).
+constexpr int kLbGroup = kSortLbGroup;
+
+template <int TPB, int ITEMS, int RMAX>
+__global__ __launch_bounds__(TPB) void k_sort_pass(SortParams p) {
+  constexpr int W = TPB / 64;
+  constexpr int TILE = TPB * ITEMS;
+  constexpr int DPT = (RMAX + TPB - 1) / TPB;  // consecutive digits owned by a thread
+  constexpr int CPW = (RMAX / 64 + W - 1) / W;  // 64-digit columns a wave looks back for
+  // copies of the next pass's digit counts: lane l adds into copy l % NC, so
+  // that the lanes of a hot digit (skewed ids) do not all hit one address
+  constexpr int NC = RMAX <= 512 ? 8 : 4;
+  static_assert(TILE < 65536, "16-bit wave offsets");
+  __shared__ uint64_t s_kv[TILE];               // keys, then coefficients, in tile order by digit
+  __shared__ uint16_t s_wcnt[W][RMAX];          // each wave's digit counts, then its offsets
+  __shared__ uint32_t s_cnt[RMAX];              // the tile's count of each digit
+  __shared__ uint32_t s_local[RMAX];            // the tile's exclusive offset of each digit
+  __shared__ int32_t s_gbase[RMAX];             // destination of the digit's slot 0 minus s_local
+  __shared__ uint32_t s_next[NC][RMAX];         // the tile's counts of the next pass's digits
+  __shared__ uint32_t s_tmp[W];
+  __shared__ uint32_t s_tile;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int radix = 1 << p.bits;
   const uint32_t dmask = (uint32_t)radix - 1u;
+  const int radix_n = p.hist_next ? (1 << p.bits_next) : 0;
+  const uint32_t nmask = (uint32_t)radix_n - 1u;
   const bool has_coef = p.coef_in != nullptr;
-  const uint32_t tile = blockIdx.x;
-  const int64_t base = (int64_t)tile * kSortTile;
-  const int tile_n = (int)min((int64_t)kSortTile, p.N - base);
-  for (int d = lane; d < radix; d += 64) s_wcnt(w)[d] = 0u;
+  if (tid == 0) s_tile = atomicAdd(p.tile_ctr, 1u);
+  for (int i = tid; i < W * RMAX; i += TPB) (&s_wcnt[0][0])[i] = 0u;
+  for (int i = tid; i < NC * RMAX; i += TPB) (&s_next[0][0])[i] = 0u;
+  __syncthreads();
+  const uint32_t tile = s_tile;
+  if (tile >= (uint32_t)p.tiles) {  // a stale tile counter: never proceed out of range
+    if (tid == 0) set_status(p.status, p.epoch, kStInternal);
+    return;
+  }
+  const int64_t base = (int64_t)tile * TILE;
+  const int tile_n = (int)min((int64_t)TILE, p.N - base);
 
-  uint64_t kv[kSortItems];
-  float cf[kSortItems];
-  uint32_t rank[kSortItems];
+  uint64_t kv[ITEMS];
+  float cf[ITEMS];
+  uint32_t rank[ITEMS];
 #pragma unroll
-  for (int k = 0; k < kSortItems; ++k) {
-    const int e = w * 64 * kSortItems + k * 64 + lane;
+  for (int k = 0; k < ITEMS; ++k) {
+    const int e = w * 64 * ITEMS + k * 64 + lane;
     const bool valid = e < tile_n;
     kv[k] = valid ? p.kv_in[base + e] : 0ull;
     cf[k] = (valid && has_coef) ? p.coef_in[base + e] : 0.0f;
   }
-  // global offsets of this tile's digit groups (independent of the ranking):
-  // the digit's base (exclusive scan of the digit totals, done below) plus
-  // the tile's offset within the digit
-  // (thread tid owns digits kDigitsPerThread * tid + h, h < kDigitsPerThread)
-  uint32_t goff[kDigitsPerThread], dtot[kDigitsPerThread];
+  // digit totals of the pass (sum of the histogram copies), owned digits
+  uint32_t tot[DPT];
 #pragma unroll
-  for (int h = 0; h < kDigitsPerThread; ++h) {
-    const int d = kDigitsPerThread * tid + h;
-    const int dc = d < radix ? d : 0;  // unconditional loads: none waits behind a branch
-    if (p.fuse_offsets) {
-      // few tiles: this tile's offset and the digit's total straight from
-      // the raw tile counts (k_sort_offsets is not launched)
-      const uint32_t* row = p.counts + (size_t)dc * p.tiles;
-      uint32_t before = 0, all = 0;
-#pragma unroll 8
-      for (int64_t j = 0; j < p.tiles; ++j) {
-        const uint32_t c = row[j];
-        all += c;
-        before += j < (int64_t)tile ? c : 0u;
-      }
-      goff[h] = before;
-      dtot[h] = all;
-    } else {
-      goff[h] = p.counts[(size_t)dc * p.tiles + tile];
-      dtot[h] = p.bases[dc];
+  for (int h = 0; h < DPT; ++h) {
+    const int d = tid * DPT + h;
+    uint32_t t = 0;
+    if (d < radix) {
+#pragma unroll
+      for (int sl = 0; sl < kHistSlices; ++sl) t += p.hist[sl * radix + d];
     }
-    if (d >= radix) dtot[h] = 0u;
+    tot[h] = t;
+  }
+  // rank within the wave.  First every item's same-digit peers (bit-major,
+  // so that the ballots of the ITEMS items are independent work for the
+  // scheduler), then the short chain through the wave's LDS counts; the
+  // next pass's digits are counted on the way.
+  uint32_t dg[ITEMS];
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) dg[k] = digit_of(kv[k], p.shift, dmask);
+  uint32_t mlo[ITEMS], mhi[ITEMS];  // lanes that differ from this one on some digit bit
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) mlo[k] = mhi[k] = 0u;
+#pragma unroll
+  for (int b = 0; b < kMaxDigitBits; ++b) {
+    if (b < p.bits) {  // uniform
+#pragma unroll
+      for (int k = 0; k < ITEMS; ++k) {
+        // bit b of the digit as 0 or all ones (one sign-extending bit-field
+        // extract), its ballot, and the lanes that disagree on it
+        const int32_t t = (int32_t)(dg[k] << (31 - b));  // bit b in the sign
+        const uint64_t m = __ballot(t < 0);
+        const uint32_t sx = (uint32_t)(t >> 31);         // 0 or all ones
+        mlo[k] |= (uint32_t)m ^ sx;
+        mhi[k] |= (uint32_t)(m >> 32) ^ sx;
+      }
+    }
   }
 #pragma unroll
-  for (int k = 0; k < kSortItems; ++k) {
-    const int e = w * 64 * kSortItems + k * 64 + lane;
+  for (int k = 0; k < ITEMS; ++k) {
+    const int e = w * 64 * ITEMS + k * 64 + lane;
     const bool valid = e < tile_n;
-    const uint32_t d = digit_of(kv[k], p.shift, dmask);
-    const uint64_t peers = digit_peers(d, p.bits, valid);
+    const uint64_t live = __ballot(valid);
+    const uint64_t peers = valid ? (~(((uint64_t)mhi[k] << 32) | mlo[k]) & live) : 0ull;
+    const uint32_t d = dg[k];
     const uint32_t below = bits_below(peers);
-    const uint32_t before = valid ? s_wcnt(w)[d] : 0u;
+    const uint32_t before = valid ? (uint32_t)s_wcnt[w][d] : 0u;
     rank[k] = before + below;
-    if (valid && below == 0) s_wcnt(w)[d] = before + (uint32_t)__popcll(peers);
+    if (valid && below == 0) s_wcnt[w][d] = (uint16_t)(before + (uint32_t)__popcll(peers));
+    if (radix_n && valid) atomicAdd(&s_next[lane % NC][digit_of(kv[k], p.shift_next, nmask)], 1u);
   }
   __syncthreads();
 
-  // per digit: exclusive offsets of the waves and the tile's count
-  uint32_t cnt[kDigitsPerThread];
+  // per digit: exclusive offsets of the waves and the tile's count, published
+  // at once for the look-back of later tiles (tile 0's count is already its
+  // inclusive prefix)
+  uint32_t cnt[DPT];
 #pragma unroll
-  for (int h = 0; h < kDigitsPerThread; ++h) {
-    const int d = kDigitsPerThread * tid + h;
+  for (int h = 0; h < DPT; ++h) {
+    const int d = tid * DPT + h;
     uint32_t acc = 0;
     if (d < radix) {
 #pragma unroll
-      for (int ww = 0; ww < kSortThreads / 64; ++ww) {
-        const uint32_t c = s_wcnt(ww)[d];
-        s_wcnt(ww)[d] = acc;
+      for (int ww = 0; ww < W; ++ww) {
+        const uint32_t c = s_wcnt[ww][d];
+        s_wcnt[ww][d] = (uint16_t)acc;
         acc += c;
       }
+      s_cnt[d] = acc;
+      __hip_atomic_store(&p.lookback[(size_t)tile * radix + d], (tile == 0 ? kFlagP32 : kFlagA32) | acc,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     cnt[h] = acc;
   }
   {
-    uint32_t tot, dsum = 0, csum = 0;
+    uint32_t tot_all, dsum = 0, csum = 0;
 #pragma unroll
-    for (int h = 0; h < kDigitsPerThread; ++h) {
-      dsum += dtot[h];
+    for (int h = 0; h < DPT; ++h) {
+      dsum += tot[h];
       csum += cnt[h];
     }
-    uint32_t g = block_excl_scan<uint32_t>(dsum, s_tmp, tot);
-    uint32_t ex = block_excl_scan<uint32_t>(csum, s_tmp, tot);
+    uint32_t g = block_excl_scan<uint32_t, W>(dsum, s_tmp, tot_all);
+    uint32_t ex = block_excl_scan<uint32_t, W>(csum, s_tmp, tot_all);
 #pragma unroll
-    for (int h = 0; h < kDigitsPerThread; ++h) {
-      const int d = kDigitsPerThread * tid + h;
+    for (int h = 0; h < DPT; ++h) {
+      const int d = tid * DPT + h;
       if (d < radix) {
         s_local[d] = ex;
-        s_gbase[d] = (int32_t)(goff[h] + g) - (int32_t)ex;
+        s_gbase[d] = (int32_t)g;
       }
-      g += dtot[h];
+      g += tot[h];
       ex += cnt[h];
     }
   }
   __syncthreads();
-  // tile position of every item, then keys through LDS to their groups
+  // tile position of every item: keys through LDS to their digit groups
 #pragma unroll
-  for (int k = 0; k < kSortItems; ++k) {
-    const int e = w * 64 * kSortItems + k * 64 + lane;
+  for (int k = 0; k < ITEMS; ++k) {
+    const int e = w * 64 * ITEMS + k * 64 + lane;
     if (e < tile_n) {
       const uint32_t d = digit_of(kv[k], p.shift, dmask);
-      rank[k] += s_local[d] + s_wcnt(w)[d];
+      rank[k] += s_local[d] + (uint32_t)s_wcnt[w][d];
       s_kv[rank[k]] = kv[k];
+    }
+  }
+  // look-back in two levels: wave w serves the digit columns w, w + W, ...
+  // (lane = digit).  First the earlier tiles of this tile's group of
+  // kLbGroup; unless one of them already holds an inclusive prefix, the
+  // group's last tile then publishes the group's total at once, and the walk
+  // continues over the words of earlier groups (a group total, or the
+  // inclusive prefix at the group's end).  Tiles that start together thus
+  // need a few load rounds, not one per kLookback tiles before them.
+  const uint32_t grp = tile / kLbGroup, gfirst = grp * kLbGroup;
+  const bool glast = tile % kLbGroup == kLbGroup - 1;
+  const int nin = (int)(tile - gfirst);  // earlier tiles of the group
+  uint32_t* lbt = p.lookback;                              // [tiles][radix]
+  uint32_t* lbg = p.lookback + (size_t)p.tiles * radix;    // [groups][radix]
+#pragma unroll 1
+  for (int ci = 0; ci < CPW; ++ci) {
+    const int col = w + ci * W;
+    if (col * 64 >= radix) break;  // uniform
+    const int d = col * 64 + lane;
+    const bool live = d < radix;  // fewer than 64 digits: the other lanes idle
+    uint32_t excl = 0, spins = 0;
+    bool done = tile == 0 || !live;
+    bool in_done = done || nin == 0;
+    while (__ballot(!in_done)) {
+      uint32_t v[kLbGroup - 1];
+#pragma unroll
+      for (int j = 0; j < kLbGroup - 1; ++j)
+        v[j] = (!in_done && j < nin)
+                   ? __hip_atomic_load(&lbt[(size_t)(tile - 1 - j) * radix + d], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT)
+                   : 0u;
+      bool wait = false;
+      if (!in_done) {
+        uint32_t sum = 0;
+        bool found = false, ready = true;
+#pragma unroll
+        for (int j = 0; j < kLbGroup - 1; ++j) {
+          if (j < nin && !found) {
+            const uint32_t f = v[j] >> 30;
+            ready = ready && f != 0u;
+            sum += v[j] & kVal32;
+            found = f == 2u;
+          }
+        }
+        if (ready) {
+          excl = sum;
+          in_done = true;
+          done = found;
+        } else if (++spins > kSpinLimit) {
+          set_status(p.status, p.epoch, kStInternal);
+          in_done = done = true;
+        } else {
+          wait = true;
+        }
+      }
+      if (__ballot(wait)) __builtin_amdgcn_s_sleep(1);
+    }
+    if (glast && live && !done)
+      __hip_atomic_store(&lbg[(size_t)grp * radix + d], kFlagA32 | (excl + s_cnt[d]),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int64_t top = (int64_t)grp - 1;
+    while (__ballot(!done)) {
+      uint32_t v[kLookback];
+#pragma unroll
+      for (int j = 0; j < kLookback; ++j) {
+        const int64_t gi = top - j;
+        v[j] = (!done && gi >= 0) ? __hip_atomic_load(&lbg[(size_t)gi * radix + d],
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                  : kFlagP32;  // before group 0: prefix 0
+      }
+      bool wait = false;
+      if (!done) {
+        uint32_t sum = 0;
+        bool found = false, ready = true;
+#pragma unroll
+        for (int j = 0; j < kLookback; ++j) {
+          if (!found) {
+            const uint32_t f = v[j] >> 30;
+            ready = ready && f != 0u;
+            sum += v[j] & kVal32;
+            found = f == 2u;
+          }
+        }
+        if (ready) {
+          excl += sum;
+          done = found;
+          top -= kLookback;
+        } else if (++spins > kSpinLimit) {
+          set_status(p.status, p.epoch, kStInternal);
+          done = true;
+        } else {
+          wait = true;
+        }
+      }
+      if (__ballot(wait)) __builtin_amdgcn_s_sleep(1);
+    }
+    if (live) {
+      const uint32_t incl = kFlagP32 | (excl + s_cnt[d]);
+      __hip_atomic_store(&lbt[(size_t)tile * radix + d], incl, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      if (glast)
+        __hip_atomic_store(&lbg[(size_t)grp * radix + d], incl, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      s_gbase[d] += (int32_t)excl - (int32_t)s_local[d];
     }
   }
   __syncthreads();
   // every slot's key and destination first (all LDS reads in flight), then
   // the stores; slot q of the tile goes to s_gbase[its digit] + q
-  uint64_t v[kSortItems];
-  int64_t pos[kSortItems];
+  uint64_t v[ITEMS];
+  int32_t pos[ITEMS];
 #pragma unroll
-  for (int k = 0; k < kSortItems; ++k) {
-    const int q = k * kSortThreads + tid;
+  for (int k = 0; k < ITEMS; ++k) {
+    const int q = k * TPB + tid;
     v[k] = s_kv[q < tile_n ? q : 0];
   }
 #pragma unroll
-  for (int k = 0; k < kSortItems; ++k) {
-    const int q = k * kSortThreads + tid;
-    pos[k] = (int64_t)s_gbase[digit_of(v[k], p.shift, dmask)] + q;
-  }
+  for (int k = 0; k < ITEMS; ++k) pos[k] = s_gbase[digit_of(v[k], p.shift, dmask)] + k * TPB + tid;
   bool bad = false;
 #pragma unroll
-  for (int k = 0; k < kSortItems; ++k) {
-    const int q = k * kSortThreads + tid;
-    const bool okp = pos[k] >= 0 && pos[k] < p.N;
+  for (int k = 0; k < ITEMS; ++k) {
+    const int q = k * TPB + tid;
+    const bool okp = pos[k] >= 0 && (int64_t)pos[k] < p.N;
     if (q < tile_n) {
       if (okp)
         p.kv_out[pos[k]] = v[k];
@@ -602,21 +721,32 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(SortParams p) {
     }
   }
   set_status_wave(p.status, p.epoch, kStInternal, bad);
-  if (!has_coef) return;
-  // coefficients the same way, through the same buffer once every key has
-  // been read from it
-  __syncthreads();
-  float* s_cf = reinterpret_cast<float*>(s_kv);
+  if (has_coef) {
+    // coefficients the same way, through the same buffer once every key has
+    // been read from it
+    __syncthreads();
+    float* s_cf = reinterpret_cast<float*>(s_kv);
 #pragma unroll
-  for (int k = 0; k < kSortItems; ++k) {
-    const int e = w * 64 * kSortItems + k * 64 + lane;
-    if (e < tile_n) s_cf[rank[k]] = cf[k];
+    for (int k = 0; k < ITEMS; ++k) {
+      const int e = w * 64 * ITEMS + k * 64 + lane;
+      if (e < tile_n) s_cf[rank[k]] = cf[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+      const int q = k * TPB + tid;
+      if (q < tile_n && pos[k] >= 0 && (int64_t)pos[k] < p.N) p.coef_out[pos[k]] = s_cf[q];
+    }
   }
-  __syncthreads();
+  // the next pass's digit counts of this tile, into one copy of its histogram
+  if (radix_n) {
+    uint32_t* hn = p.hist_next + (size_t)(tile % kHistSlices) * radix_n;
+    for (int d = tid; d < radix_n; d += TPB) {
+      uint32_t c = 0;
 #pragma unroll
-  for (int k = 0; k < kSortItems; ++k) {
-    const int q = k * kSortThreads + tid;
-    if (q < tile_n && pos[k] >= 0 && pos[k] < p.N) p.coef_out[pos[k]] = s_cf[q];
+      for (int i = 0; i < NC; ++i) c += s_next[i][d];
+      if (c) __hip_atomic_fetch_add(&hn[d], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -2496,35 +2626,30 @@ hipError_t launch_linearize(const LinParams& p, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_sort_pass(const SortParams& p, hipStream_t s,
-                            const std::function<void(int, int)>& mark) {
-  if (p.items != kSortItemsSmall && p.items != kSortItemsLarge) return hipErrorInvalidValue;
-  const unsigned tiles = (unsigned)p.tiles;
-  auto m = [&](int stage, int end) {
-    if (mark) mark(stage, end);
-  };
-  m(SGB_STAGE_SORT_COUNT, 0);
-  const size_t hist_bytes = sizeof(uint32_t) * (size_t)kCountCopies << p.bits;
-  if (p.items == kSortItemsSmall)
-    hipLaunchKernelGGL(k_sort_count<kSortItemsSmall>, dim3(tiles), dim3(kSortThreads), hist_bytes,
-                       s, p);
-  else
-    hipLaunchKernelGGL(k_sort_count<kSortItemsLarge>, dim3(tiles), dim3(kSortThreads), hist_bytes,
-                       s, p);
-  m(SGB_STAGE_SORT_COUNT, 1);
-  m(SGB_STAGE_SORT_OFFSETS, 0);
-  if (!p.fuse_offsets)
-    hipLaunchKernelGGL(k_sort_offsets, dim3(1u << p.bits), dim3(kScanThreads), 0, s, p);
-  m(SGB_STAGE_SORT_OFFSETS, 1);
-  m(SGB_STAGE_SORT_SCATTER, 0);
-  const size_t digit_bytes = sizeof(uint32_t) * (size_t)(kSortThreads / 64 + 2) << p.bits;
-  if (p.items == kSortItemsSmall)
-    hipLaunchKernelGGL(k_sort_scatter<kSortItemsSmall>, dim3(tiles), dim3(kSortThreads),
-                       digit_bytes, s, p);
-  else
-    hipLaunchKernelGGL(k_sort_scatter<kSortItemsLarge>, dim3(tiles), dim3(kSortThreads),
-                       digit_bytes, s, p);
-  m(SGB_STAGE_SORT_SCATTER, 1);
+hipError_t launch_sort_pass(const SortParams& p, hipStream_t s) {
+  if (p.bits < 1 || p.bits > kMaxDigitBits || (p.hist_next && p.bits_next > p.bits) ||
+      p.tiles < 1)
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)p.tiles);
+  const int64_t tile = sort_tile_items(p.shape);
+  if ((int64_t)p.tiles != (p.N + tile - 1) / tile) return hipErrorInvalidValue;
+  switch (p.shape) {
+    case kSortLarge:
+      if (p.bits > 9) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((k_sort_pass<1024, 12, 512>), grid, dim3(1024), 0, s, p);
+      break;
+    case kSortMedium:
+      if (p.bits <= 9)
+        hipLaunchKernelGGL((k_sort_pass<512, 8, 512>), grid, dim3(512), 0, s, p);
+      else
+        hipLaunchKernelGGL((k_sort_pass<512, 8, 1024>), grid, dim3(512), 0, s, p);
+      break;
+    default:
+      if (p.bits <= 9)
+        hipLaunchKernelGGL((k_sort_pass<256, 8, 512>), grid, dim3(256), 0, s, p);
+      else
+        hipLaunchKernelGGL((k_sort_pass<256, 8, 1024>), grid, dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -18,10 +18,7 @@ ATOL, RTOL = 1e-4, 1e-5   # |gpu - oracle| <= 1e-4 + 1e-5 * |oracle|
 
 
 def oracle_problem(inp: synth.Inputs) -> oracle.Problem:
-    return oracle.Problem(T=inp.T, B=inp.B, hash_size_cumsum=inp.hash_size_cumsum,
-                          D_offsets=inp.D_offsets, offsets=inp.offsets, indices=inp.indices,
-                          per_sample_weights=inp.per_sample_weights, pooling=inp.spec.pooling,
-                          grad_output=inp.grad_output)
+    return oracle.problem_from_inputs(inp)
 
 
 def row_elements(inp: synth.Inputs, rows: np.ndarray):

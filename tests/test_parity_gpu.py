@@ -213,13 +213,39 @@ def test_many_run_tiles(sgb, tokens):
     """Run-length tiles of 4096 sorted positions: up to 128 tiles the run
     write alone (look-back over the tile counts), up to 1024 the count kernel
     and a run write that sums the counts itself, beyond that the scan kernel
-    too; each limit and one more.  300 000 lookups also take the sort's
-    separate offset scan (over 32 sort tiles).  Runs are compared bit-exact,
-    rows to the usual tolerance."""
+    too; each limit and one more.  Runs are compared bit-exact, rows to the
+    usual tolerance."""
     s = synth.Spec("tiles", 1, (60000,), (4,), 0, ("fixed", 1), ("zipf", 1.05), "none", False,
                    "f32", "dense", accumulate=True, nobag_tokens=tokens, seed=41)
     inp = synth.generate(s)
     _say(f"[parity] many run tiles N={inp.N}")
+    check_case(sgb, inp, "dense", 64, accumulate=True)
+
+
+SORT_SHAPES = [
+    # (rows, lookups, index distribution): id bits -> digits per radix pass; tile shape
+    (1, 3000, ("uniform",)),            # 0 bits: nothing to sort
+    (2, 5000, ("uniform",)),            # 1 bit, radix 2 (most look-back lanes idle); small tiles
+    (6, 5000, ("zipf", 1.5)),           # 3 bits, radix 8
+    (60000, 65536, ("zipf", 1.05)),     # 16 bits -> 8/8; small tiles, the largest such batch
+    (60000, 65537, ("zipf", 1.05)),     # medium tiles from here
+    (1 << 20, 300_000, ("uniform",)),   # 20 bits -> 10/10: medium tiles with 1024 digits
+    (1 << 20, 1_200_000, ("zipf", 1.1)),  # 10-bit digits keep medium tiles above 2^20 lookups
+    (1 << 22, 1_200_000, ("zipf", 1.2)),  # 22 bits -> 8/7/7: large tiles, skewed ids
+    ((1 << 25) - 1, 1_500_000, ("uniform",)),  # 25 bits -> 9/8/8: large tiles, 123 of them
+]
+
+
+@pytest.mark.parametrize("rows,tokens,dist", SORT_SHAPES)
+def test_sort_shapes(sgb, rows, tokens, dist):
+    """Every radix tile shape and digit width of the single-sweep passes
+    (look-back over up to several hundred tiles, histograms counted by the
+    linearisation and by each pass for the next): the run structure is
+    compared bit-exact, rows to the usual tolerance."""
+    s = synth.Spec("sortshape", 1, (rows,), (4,), 0, ("fixed", 1), dist, "none", False,
+                   "f32", "dense", accumulate=True, nobag_tokens=tokens, seed=61 + rows % 89)
+    inp = synth.generate(s)
+    _say(f"[parity] sort shape rows={rows} N={inp.N} dist={dist}")
     check_case(sgb, inp, "dense", 64, accumulate=True)
 
 
