@@ -193,8 +193,12 @@ typedef struct {
  *  Each touched row is read and written once; untouched rows and state are
  *  not written (a fresh dense gradient is zeroed whole first, then its
  *  touched rows are written).  A row's sum is accumulated in fp64 in a fixed
- *  order and rounded once to fp32.  num_indices == 0 is a no-op (a fresh
- *  dense grad is still zero-filled).  Allocates nothing.
+ *  order and rounded once to fp32; each term is a product coef * grad
+ *  element, except in the short-run reducer, which first adds the fp32
+ *  products of two consecutive lookups in fp32 (so a row's result is not the
+ *  fp64 sum rounded once, but stays within 1e-4 + 1e-5 |G| of the exact sum
+ *  on the tested workloads).  num_indices == 0 is a no-op (a fresh dense
+ *  grad is still zero-filled).  Allocates nothing.
  *  Part of the work runs on two side streams the plan owns (the zero fill of
  *  a fresh dense gradient, and the short-run reduction); they start after
  *  everything enqueued on `stream` before the call, and `stream` waits for
@@ -250,6 +254,10 @@ sgb_status sgb_device_status(sgb_plan plan, const void* workspace, void* stream,
  * (linear_id << info_bits) | info, info = t*B + b (bag) or i*T + t (nobag),
  * in stable sorted order (FBGEMM `transpose_embedding_input` outputs, with the
  * id and info carried in one word).  Counts live on the device.
+ * sgb_runs_view_get needs the num_indices and B of that last call (they fix
+ * the workspace layout); the call recorded them in the workspace, and a
+ * mismatch returns SGB_ERR_INVALID_ARGUMENT.  It reads them back with a
+ * synchronous copy (it waits for the device).
  */
 typedef struct {
   const uint64_t* sorted_packed;    /* [N]                                     */

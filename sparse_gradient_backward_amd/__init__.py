@@ -181,26 +181,9 @@ def sgb_backward(plan: int, grad_output, indices, offsets, B: int, per_sample_we
     `events`, if given, is a list of 2 * len(STAGES) recorded-once
     torch.cuda.Event(enable_timing=True) objects (or None entries) that the
     library records around each stage (sgb_backward_timed)."""
-    import torch
-    gd = {torch.float32: "f32", torch.bfloat16: "bf16"}[grad_output.dtype]
-    for name, t, dt in (("indices", indices, torch.int64), ("offsets", offsets, torch.int64),
-                        ("per_sample_weights", per_sample_weights, torch.float32),
-                        ("weights", weights, weights.dtype if weights is not None and
-                         weights.dtype in (torch.bfloat16, torch.uint8) else torch.float32),
-                        ("momentum", momentum, torch.float32),
-                        ("grad", grad, torch.float32)):
-        if t is not None and (t.dtype != dt or not t.is_contiguous()):
-            raise SgbError(SGB_ERR_INVALID_ARGUMENT, f"sgb_backward: {name} must be contiguous {dt}")
-    if not grad_output.is_contiguous():
-        raise SgbError(SGB_ERR_INVALID_ARGUMENT, "sgb_backward: grad_output must be contiguous")
-    batch = _Batch(_ptr(grad_output), DTYPE[gd], _ptr(indices), int(indices.numel()),
-                   _ptr(offsets), int(B), _ptr(per_sample_weights))
-    wdt = {torch.bfloat16: "bf16", torch.uint8: "int8"}.get(
-        weights.dtype if weights is not None else None, "f32")
-    upd = _Update(MODE[mode], _ptr(weights), _ptr(momentum), _ptr(grad), 1 if accumulate else 0,
-                  float(lr), float(eps), DTYPE[wdt],
-                  1 if stochastic_rounding else 0, int(sr_seed) & (2**64 - 1),
-                  int(sr_offset) & (2**64 - 1))
+    batch, upd = _marshal(grad_output, indices, offsets, B, per_sample_weights, mode, weights,
+                          momentum, grad, accumulate, lr, eps, stochastic_rounding, sr_seed,
+                          sr_offset, "sgb_backward")
     ws_ptr = _ptr(workspace)
     ws_bytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
     if events is None:
@@ -211,6 +194,31 @@ def sgb_backward(plan: int, grad_output, indices, offsets, B: int, per_sample_we
                                           for e in events])
         _check(_lib.sgb_backward_timed(plan, ctypes.byref(batch), ctypes.byref(upd), ws_ptr,
                                        ws_bytes, _stream(stream), arr), "sgb_backward_timed")
+
+
+def _marshal(grad_output, indices, offsets, B, per_sample_weights, mode, weights, momentum, grad,
+             accumulate, lr, eps, stochastic_rounding, sr_seed, sr_offset, where):
+    import torch
+    gd = {torch.float32: "f32", torch.bfloat16: "bf16"}[grad_output.dtype]
+    for name, t, dt in (("indices", indices, torch.int64), ("offsets", offsets, torch.int64),
+                        ("per_sample_weights", per_sample_weights, torch.float32),
+                        ("weights", weights, weights.dtype if weights is not None and
+                         weights.dtype in (torch.bfloat16, torch.uint8) else torch.float32),
+                        ("momentum", momentum, torch.float32),
+                        ("grad", grad, torch.float32)):
+        if t is not None and (t.dtype != dt or not t.is_contiguous()):
+            raise SgbError(SGB_ERR_INVALID_ARGUMENT, f"{where}: {name} must be contiguous {dt}")
+    if not grad_output.is_contiguous():
+        raise SgbError(SGB_ERR_INVALID_ARGUMENT, f"{where}: grad_output must be contiguous")
+    batch = _Batch(_ptr(grad_output), DTYPE[gd], _ptr(indices), int(indices.numel()),
+                   _ptr(offsets), int(B), _ptr(per_sample_weights))
+    wdt = {torch.bfloat16: "bf16", torch.uint8: "int8"}.get(
+        weights.dtype if weights is not None else None, "f32")
+    upd = _Update(MODE[mode], _ptr(weights), _ptr(momentum), _ptr(grad), 1 if accumulate else 0,
+                  float(lr), float(eps), DTYPE[wdt],
+                  1 if stochastic_rounding else 0, int(sr_seed) & (2**64 - 1),
+                  int(sr_offset) & (2**64 - 1))
+    return batch, upd
 
 
 def sgb_forward(plan: int, indices, offsets, B: int, per_sample_weights, weights, output,

@@ -12,7 +12,6 @@
 
 #include <algorithm>
 #include <atomic>
-#include <functional>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -383,6 +382,16 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
     if (ev) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev), s);
   };
   auto mark = [&](int stage, int end) { mark_on(stream, stage, end); };
+  // the same marks for kernels launched from kernels.hip
+  struct MarkCtx {
+    void* const* events;
+    hipStream_t stream;
+  } mark_ctx{events, stream};
+  const StageMark mark_fn = [](void* c, int stage, int end) {
+    const MarkCtx* m = static_cast<const MarkCtx*>(c);
+    void* ev = m->events ? m->events[2 * stage + end] : nullptr;
+    if (ev) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev), m->stream);
+  };
 
   if (N == 0) {  // FBGEMM host entry: no indices -> nothing to do (dense grad stays zero)
     // clear the status word so sgb_device_status() reports this call
@@ -509,7 +518,7 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   rp.tile_ctr = &hdr->rle_tile_ctr;
   rp.status = status;
   rp.epoch = epoch;
-  if (launch_rle(rp, stream, mark) != hipSuccess) return SGB_ERR_HIP;
+  if (launch_rle(rp, stream, mark_fn, &mark_ctx) != hipSuccess) return SGB_ERR_HIP;
 
   PostParams pp{};
   pp.cum = rp.cum;
@@ -668,6 +677,16 @@ sgb_status sgb_runs_view_get(sgb_plan p, const void* ws, int64_t N, int32_t B,
   const bool nobag_no_off = p->pooling == SGB_POOL_NONE && B == 0;
   sgb_status st = make_layout(p, N, B, !nobag_no_off, &L);
   if (st != SGB_OK) return st;
+  // the layout must be the one the last call on this workspace used: it
+  // recorded its N and B in the header
+  {
+    DeviceGuard guard(p->device);
+    if (!guard.ok) return SGB_ERR_HIP;
+    Header h;
+    if (hipMemcpy(&h, ws, sizeof(Header), hipMemcpyDeviceToHost) != hipSuccess) return SGB_ERR_HIP;
+    if (h.num_indices != N || (N > 0 && h.B != (nobag_no_off ? 0 : B)))
+      return SGB_ERR_INVALID_ARGUMENT;
+  }
   void* w = const_cast<void*>(ws);
   Header* hdr = at<Header>(w, L.hdr);
   out->sorted_packed = at<uint64_t>(w, (L.npasses % 2 == 0) ? L.kvA : L.kvB);

@@ -6,7 +6,6 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include <functional>
 
 namespace sgb {
 
@@ -213,11 +212,14 @@ struct Header {
   int32_t num_runs;                   // U
   uint32_t total_items;               // chunks over all long runs
   int64_t num_long;                   // number of long runs
+  int64_t num_indices;                // N of the last call (its run structure's layout)
+  int32_t B;                          // B of the last call (0: nobag without offsets)
   uint32_t hist_ready;                // epoch once the first pass's histogram is zeroed
   uint32_t sort_tile_ctr[4];          // dynamic tile ids of each radix pass
-  uint32_t pad[19];
+  uint32_t pad[16];
 };
 static_assert(sizeof(Header) <= 128, "header too large");
+static_assert(offsetof(Header, num_indices) % 8 == 0, "aligned counts");
 
 // A long run as the long-run reducer needs it (written by k_post).
 struct LongRun {
@@ -415,10 +417,11 @@ struct FwdParams {
 
 hipError_t launch_init(void* header_and_hist, size_t bytes, hipStream_t s);
 hipError_t launch_linearize(const LinParams& p, int grid, hipStream_t s);
-// `mark(stage, end)` (if set) records the timing events of a kernel's
-// timed region just before (end = 0) and after (end = 1) its launch.
 hipError_t launch_sort_pass(const SortParams& p, hipStream_t s);
-hipError_t launch_rle(const RleParams& p, hipStream_t s, const std::function<void(int, int)>& mark);
+// `mark(ctx, stage, end)` (if set) records the timing events of a stage just
+// before (end = 0) and after (end = 1) its kernel.
+using StageMark = void (*)(void* ctx, int stage, int end);
+hipError_t launch_rle(const RleParams& p, hipStream_t s, StageMark mark, void* ctx);
 hipError_t launch_post(const PostParams& p, int grid, hipStream_t s);
 hipError_t launch_fill(const FillParams& p, int grid, hipStream_t s);
 hipError_t launch_reduce_long(const RedParams& p, bool bf16, int grid, hipStream_t s);

@@ -228,6 +228,8 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
   if (blockIdx.x == 0) {
     if (tid == 0) {
       p.header->epoch = p.epoch;
+      p.header->num_indices = p.N;
+      p.header->B = p.B;
       p.header->post_tile_ctr = 0u;
       p.header->rle_tile_ctr = 0u;
 #pragma unroll
@@ -2653,8 +2655,11 @@ hipError_t launch_sort_pass(const SortParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_rle(const RleParams& p, hipStream_t s, const std::function<void(int, int)>& mark) {
+hipError_t launch_rle(const RleParams& p, hipStream_t s, StageMark mark_fn, void* ctx) {
   const unsigned tiles = (unsigned)p.tiles;
+  auto mark = [&](int stage, int end) {
+    if (mark_fn) mark_fn(ctx, stage, end);
+  };
   // in one pass the count and scan stages are done inside k_rle_write: their
   // marks then bracket no kernel, so that every stage's pair of events is
   // still recorded

@@ -249,6 +249,23 @@ def test_sort_shapes(sgb, rows, tokens, dist):
     check_case(sgb, inp, "dense", 64, accumulate=True)
 
 
+def test_runs_view_rejects_another_layout(sgb):
+    """The run view needs the N and B of the last call on the workspace
+    (they fix its layout); the call records them, and a view asked with
+    other sizes is refused instead of pointing into the wrong regions."""
+    s = synth.spec(1)
+    inp = synth.generate(s)
+    out0, _ = initial_buffers(inp, s.mode, False)
+    run = run_gpu(sgb, inp, s.mode, 4, torch.from_numpy(out0).cuda(), None, lr=s.lr)
+    assert run.status == "SGB_OK"
+    v = run.plan.runs_view(run.ws, inp.N, inp.B)
+    assert v["num_runs"] > 0
+    for N, B in ((inp.N - 1, inp.B), (inp.N, inp.B + 1)):
+        with pytest.raises(sgb.SgbError) as e:
+            run.plan.runs_view(run.ws, N, B)
+        assert e.value.name == "SGB_ERR_INVALID_ARGUMENT"
+
+
 # ------------------------------------------------------------------ properties
 
 def test_deterministic(sgb):
