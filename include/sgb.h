@@ -208,6 +208,26 @@ typedef struct {
 sgb_status sgb_backward(sgb_plan plan, const sgb_batch* batch, const sgb_update* update,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * sgb_backward_noalloc -- sgb_backward() for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the workspace is a fixed scratch array
+ * the library holds on every GPU it runs on (one copy per GPU, kept until the
+ * process ends), so the caller passes only inputs and outputs.
+ *  Limit: batches whose sgb_workspace_bytes() exceeds 64 MiB (about a
+ *  million lookups of rows up to 256 wide) return SGB_ERR_WORKSPACE_TOO_SMALL
+ *  before anything is enqueued.
+ *  Same kernels, results and errors as sgb_backward(); it calls no hipMalloc,
+ *  hipFree or other allocating routine.  Every call on one GPU uses that
+ *  GPU's single scratch copy, which keeps the last call's contents: calls that
+ *  overlap on one GPU (other streams, other host threads, other plans) race
+ *  and must be serialised by the caller.  sgb_device_status() and
+ *  sgb_runs_view_get() read this scratch when given a NULL workspace.
+ *  SGB_ERR_HIP if the scratch's address could not be found at plan creation.
+ */
+sgb_status sgb_backward_noalloc(sgb_plan plan, const sgb_batch* batch, const sgb_update* update,
+                                void* stream);
+
 /* Timed regions of sgb_backward() (see sgb_backward_timed): one per kernel,
  * in launch order, plus SGB_STAGE_SORT spanning every radix pass. */
 typedef enum {
@@ -243,7 +263,8 @@ sgb_status sgb_backward_timed(sgb_plan plan, const sgb_batch* batch, const sgb_u
  * sgb_device_status -- synchronises `stream`, then stores in *out the first
  * error the kernels recorded in `workspace` during the last sgb_backward()
  * that used it (SGB_OK if none).  The return value reports failures of this
- * call itself (SGB_ERR_HIP).
+ * call itself (SGB_ERR_HIP).  workspace NULL: the scratch of
+ * sgb_backward_noalloc() on the plan's GPU.
  */
 sgb_status sgb_device_status(sgb_plan plan, const void* workspace, void* stream, int32_t* out);
 
@@ -257,7 +278,8 @@ sgb_status sgb_device_status(sgb_plan plan, const void* workspace, void* stream,
  * sgb_runs_view_get needs the num_indices and B of that last call (they fix
  * the workspace layout); the call recorded them in the workspace, and a
  * mismatch returns SGB_ERR_INVALID_ARGUMENT.  It reads them back with a
- * synchronous copy (it waits for the device).
+ * synchronous copy (it waits for the device).  workspace NULL: the scratch of
+ * sgb_backward_noalloc() on the plan's GPU.
  */
 typedef struct {
   const uint64_t* sorted_packed;    /* [N]                                     */

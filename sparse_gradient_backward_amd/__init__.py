@@ -89,13 +89,14 @@ _lib.sgb_backward.argtypes = [_vp, ctypes.POINTER(_Batch), ctypes.POINTER(_Updat
                               ctypes.c_size_t, _vp]
 _lib.sgb_backward_timed.argtypes = [_vp, ctypes.POINTER(_Batch), ctypes.POINTER(_Update), _vp,
                                     ctypes.c_size_t, _vp, ctypes.POINTER(_vp)]
+_lib.sgb_backward_noalloc.argtypes = [_vp, ctypes.POINTER(_Batch), ctypes.POINTER(_Update), _vp]
 _lib.sgb_device_status.argtypes = [_vp, _vp, _vp, ctypes.POINTER(_i32)]
 _lib.sgb_forward.argtypes = [_vp, ctypes.POINTER(_Lookups), _vp, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.sgb_runs_view_get.argtypes = [_vp, _vp, _i64, _i32, ctypes.POINTER(_RunsView)]
 _lib.sgb_status_string.argtypes = [_i32]
 _lib.sgb_status_string.restype = ctypes.c_char_p
 for _f in ("sgb_plan_create", "sgb_workspace_bytes", "sgb_backward", "sgb_backward_timed",
-           "sgb_device_status", "sgb_runs_view_get", "sgb_forward"):
+           "sgb_backward_noalloc", "sgb_device_status", "sgb_runs_view_get", "sgb_forward"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -196,6 +197,22 @@ def sgb_backward(plan: int, grad_output, indices, offsets, B: int, per_sample_we
                                        ws_bytes, _stream(stream), arr), "sgb_backward_timed")
 
 
+def sgb_backward_noalloc(plan: int, grad_output, indices, offsets, B: int, per_sample_weights,
+                         mode: str, weights=None, momentum=None, grad=None,
+                         accumulate: bool = False, lr: float = 0.0, eps: float = 0.0,
+                         stream=None, stochastic_rounding: bool = False, sr_seed: int = 0,
+                         sr_offset: int = 0) -> None:
+    """sgb_backward without a workspace: the library's fixed per-GPU scratch
+    (64 MiB) serves as one, and nothing is allocated.  Calls that overlap on
+    one GPU race; device_status / runs_view read this scratch when given
+    workspace=None."""
+    batch, upd = _marshal(grad_output, indices, offsets, B, per_sample_weights, mode, weights,
+                          momentum, grad, accumulate, lr, eps, stochastic_rounding, sr_seed,
+                          sr_offset, "sgb_backward_noalloc")
+    _check(_lib.sgb_backward_noalloc(plan, ctypes.byref(batch), ctypes.byref(upd),
+                                     _stream(stream)), "sgb_backward_noalloc")
+
+
 def _marshal(grad_output, indices, offsets, B, per_sample_weights, mode, weights, momentum, grad,
              accumulate, lr, eps, stochastic_rounding, sr_seed, sr_offset, where):
     import torch
@@ -290,6 +307,9 @@ class Plan:
 
     def backward(self, *args, **kw):
         return sgb_backward(self.handle, *args, **kw)
+
+    def backward_noalloc(self, *args, **kw):
+        return sgb_backward_noalloc(self.handle, *args, **kw)
 
     def forward(self, *args, **kw):
         return sgb_forward(self.handle, *args, **kw)

@@ -52,6 +52,9 @@ struct sgb_plan_s {
   hipStream_t aux[2] = {nullptr, nullptr};
   hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};  // fork, fill done, rle done, short done
   std::mutex mu;
+  // this device's copy of the fixed scratch of sgb_backward_noalloc (NULL if
+  // its lookup failed)
+  void* scratch = nullptr;
 };
 
 namespace {
@@ -312,6 +315,7 @@ sgb_status sgb_plan_create(sgb_plan* out, int32_t T, const int64_t* hsc, const i
     sgb_plan_destroy(p);
     return SGB_ERR_HIP;
   }
+  if (scratch_address(&p->scratch) != hipSuccess) p->scratch = nullptr;
   *out = p;
   return SGB_OK;
 }
@@ -345,6 +349,21 @@ sgb_status sgb_workspace_bytes(sgb_plan p, int64_t N, int32_t B, size_t* bytes) 
 sgb_status sgb_backward(sgb_plan p, const sgb_batch* b, const sgb_update* u, void* ws,
                         size_t ws_bytes, void* stream_) {
   return sgb_backward_timed(p, b, u, ws, ws_bytes, stream_, nullptr);
+}
+
+sgb_status sgb_backward_noalloc(sgb_plan p, const sgb_batch* b, const sgb_update* u,
+                                void* stream_) {
+  if (!p || !b || !u) return SGB_ERR_INVALID_ARGUMENT;
+  if (!p->scratch) return SGB_ERR_HIP;
+  // the batch must fit the fixed scratch (the workspace sgb_backward would need)
+  Layout L;
+  const bool with_offsets = b->offsets != nullptr;
+  if (b->num_indices > 0) {
+    const sgb_status st = make_layout(p, b->num_indices, with_offsets ? b->B : 0, with_offsets, &L);
+    if (st != SGB_OK) return st;
+    if (L.total > kScratchBytes) return SGB_ERR_WORKSPACE_TOO_SMALL;
+  }
+  return sgb_backward_timed(p, b, u, p->scratch, kScratchBytes, stream_, nullptr);
 }
 
 sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* u, void* ws,
@@ -657,6 +676,7 @@ sgb_status sgb_forward(sgb_plan p, const sgb_lookups* lk, const float* weights, 
 }
 
 sgb_status sgb_device_status(sgb_plan p, const void* ws, void* stream_, int32_t* out) {
+  if (p && !ws) ws = p->scratch;  // the no-allocation entry point's scratch
   if (!p || !ws || !out) return SGB_ERR_INVALID_ARGUMENT;
   DeviceGuard guard(p->device);
   if (!guard.ok) return SGB_ERR_HIP;
@@ -672,6 +692,7 @@ sgb_status sgb_device_status(sgb_plan p, const void* ws, void* stream_, int32_t*
 
 sgb_status sgb_runs_view_get(sgb_plan p, const void* ws, int64_t N, int32_t B,
                              sgb_runs_view* out) {
+  if (p && !ws) ws = p->scratch;  // the no-allocation entry point's scratch
   if (!p || !ws || !out) return SGB_ERR_INVALID_ARGUMENT;
   Layout L;
   const bool nobag_no_off = p->pooling == SGB_POOL_NONE && B == 0;

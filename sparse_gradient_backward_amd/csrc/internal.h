@@ -415,6 +415,11 @@ struct FwdParams {
 
 // ---------------------------------------------------------------- launchers (kernels.hip)
 
+// Fixed device scratch of sgb_backward_noalloc: bytes of the per-GPU array,
+// and its address on the current device (looked up once per device).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+hipError_t scratch_address(void** out);
+
 hipError_t launch_init(void* header_and_hist, size_t bytes, hipStream_t s);
 hipError_t launch_linearize(const LinParams& p, int grid, hipStream_t s);
 hipError_t launch_sort_pass(const SortParams& p, hipStream_t s);

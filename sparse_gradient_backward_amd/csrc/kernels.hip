@@ -36,6 +36,8 @@
 // "tt_embeddings_cuda.cu" (FBTT-Embedding) for the SGD / row-wise Adagrad
 // formulas.  The kernels here are designed for wave64 CDNA4; see the notes at
 // each kernel for where they depart from the pages' CUDA design.
+#include <mutex>
+
 #include "internal.h"
 #include "sgb.h"
 
@@ -2611,6 +2613,35 @@ __global__ __launch_bounds__(256) void k_forward(FwdParams p) {
 }
 
 }  // namespace
+
+// ------------------------------------------------------------------ no-allocation scratch
+//
+// The workspace of sgb_backward_noalloc, for callers that cannot allocate
+// device memory: a file-scope device array, one copy on every GPU the library
+// runs on, held until the process ends.  In host code its name is only a
+// stand-in for the symbol; the device address of the current GPU's copy is
+// looked up once per device and kept.
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 // ------------------------------------------------------------------ launchers
 

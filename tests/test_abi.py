@@ -17,7 +17,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def test_every_declared_function_is_exported():
     declared = sgb.header_functions()
     assert set(declared) == {"sgb_plan_create", "sgb_plan_destroy", "sgb_workspace_bytes",
-                             "sgb_backward", "sgb_backward_timed", "sgb_device_status",
+                             "sgb_backward", "sgb_backward_timed", "sgb_backward_noalloc",
+                             "sgb_device_status",
                              "sgb_runs_view_get", "sgb_status_string", "sgb_forward"}
     lib = ctypes.CDLL(sgb.LIB_PATH)
     for name in declared:
