@@ -568,12 +568,12 @@ def bf16_weights_measure(plan, spec, grad_output, indices, offsets, B, psw, out,
 def int8_weights_measure(plan, inp, spec, grad_output, indices, offsets, B, psw, mom, ws, steps,
                          ms_path):
     """The same step with INT8 row-wise quantized weight rows (SGD and
-    row-wise Adagrad workloads with rows up to 1024 wide): synthetic rows
+    row-wise Adagrad workloads): synthetic rows
     made on the device (codes uniform in [0, 255], scale 0.02 / 255, bias
     -0.01, so values span [-0.01, 0.01]), `steps` plain calls timed by HIP
     events."""
     D = np.diff(inp.D_offsets).astype(np.int64)
-    if spec.mode == "dense" or int(D.max()) > 1024:
+    if spec.mode == "dense":
         return None
     E = np.diff(inp.hash_size_cumsum).astype(np.int64)
     woff8 = np.concatenate([[0], np.cumsum(E * (D + 8))])

@@ -383,13 +383,11 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   if (u->mode == SGB_SGD && !u->weights) return SGB_ERR_INVALID_ARGUMENT;
   if (u->mode == SGB_ROWWISE_ADAGRAD && (!u->weights || !u->momentum))
     return SGB_ERR_INVALID_ARGUMENT;
-  if (u->mode == SGB_ROWWISE_ADAGRAD && p->Dmax > kMaxCb * kColBlock) return SGB_ERR_UNSUPPORTED;
   if (u->weights_dtype != SGB_F32 && u->weights_dtype != SGB_BF16 && u->weights_dtype != SGB_INT8)
     return SGB_ERR_INVALID_ARGUMENT;
   if (u->mode == SGB_DENSE_GRAD && u->weights_dtype != SGB_F32) return SGB_ERR_UNSUPPORTED;
   const bool w_bf16 = u->mode != SGB_DENSE_GRAD && u->weights_dtype == SGB_BF16;
   const bool w_int8 = u->mode != SGB_DENSE_GRAD && u->weights_dtype == SGB_INT8;
-  if (w_int8 && p->Dmax > kMaxCb * kColBlock) return SGB_ERR_UNSUPPORTED;
   void* outv = u->mode == SGB_DENSE_GRAD ? static_cast<void*>(u->grad) : u->weights;
   if (!aligned(outv, 16)) return SGB_ERR_INVALID_ARGUMENT;
   float* out = (w_bf16 || w_int8) ? nullptr : static_cast<float*>(outv);

@@ -13,7 +13,6 @@ namespace sgb {
 constexpr int kMaxDigitBits = 10;     // LSD digits of <= 10 bits
 constexpr int kMaxPasses = 4;         // linear ids below 2^40
 constexpr int kRadixMax = 1 << kMaxDigitBits;
-constexpr int kMaxCb = 4;             // Adagrad rows held in registers: D <= 4 * 256
 constexpr int kColBlock = 256;        // columns one wave covers per pass (64 lanes x 4)
 constexpr int kMaxD = 8192;
 

@@ -1832,16 +1832,22 @@ __device__ __forceinline__ d4 load_partial(const double* q) {
 
 // Last-arrival ticket: waits until this wave's partial stores have completed
 // (s_waitcnt vmcnt(0): on this architecture the vector-memory counter also
-// covers stores), counts the arrival with a device-scope atomic, and reports
-// whether this wave completes the group.  The caller reads the members'
-// partials only after this returns true, i.e. after the atomic's result came
-// back, with device-scope loads.
+// covers stores, and agent-scope atomic stores complete at the level where
+// every XCD sees them), counts the arrival with a device-scope atomic, and
+// reports whether this wave completes the group.  The caller reads the
+// members' partials only after this returns true, i.e. after the atomic's
+// result came back, with device-scope loads.  The signal fences keep the
+// compiler from moving the partial stores below the wait or the partial
+// loads above the ticket (they emit no instruction).
 __device__ __forceinline__ bool ticket_last(uint32_t* ctr, uint32_t members) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) expcnt(7) lgkmcnt(15)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   uint32_t old = 0;
   if (lane_id() == 0)
     old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   old = __shfl(old, 0, 64);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   return old + 1 == members;
 }
 
@@ -2345,6 +2351,49 @@ __device__ __forceinline__ uint64_t rl64(uint64_t x, int l) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// A short run of a row-wise Adagrad or INT8 row wider than one item holds
+// (1024 columns): the whole wave serves the run, and finish_row takes the
+// row's 256-column blocks from a gather of the run's lookups, repeated on
+// each of its passes (mean square, then the update; INT8 rows also their
+// range), so nothing beyond 4 columns per lane is held at a time.
+template <bool BF16, int WK>
+__device__ __forceinline__ void wide_run_multi(const RedParams& p, const WideRun& m,
+                                            const WideLane& d0, int t, int D, int64_t lin) {
+  constexpr int UNR = 4;
+  const Groups G = groups_of(64);
+  const RowDst dst = row_dest<WK>(p, t, D, lin);
+  const uint64_t imask = info_mask(p);
+  const int len = m.e - m.s;
+  const int64_t gbase = p.nobag ? 0 : p.doff[t];
+  auto getG = [&](int cb) -> d4 {
+    const int col = cb * kColBlock + 4 * lane_id();
+    const bool ok = col < D;
+    const int64_t gcol = gbase + col;
+    d4 acc = d4_zero();
+    for (int j0 = 0; j0 < len; j0 += 64) {
+      const WideLane dl = j0 == 0 ? d0 : wide_lane(p, m, j0);
+      const int rowi = grad_row_of(p, (uint32_t)(dl.kv & imask), t);
+      const int cnt = min(64, len - j0);
+      for (int u0 = 0; u0 < cnt; u0 += UNR) {
+        Raw4<BF16> r[UNR];
+        float c[UNR];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+          const bool in = u0 + u < cnt;
+          const int src = in ? u0 + u : cnt - 1;
+          c[u] = in ? rlf(dl.cf, src) : 0.f;
+          r[u] = (in && ok) ? load_raw4<BF16>(p.grad, (int64_t)rl32(rowi, src) * p.row_stride + gcol)
+                            : zero_raw4<BF16>();
+        }
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) d4_fma(acc, c[u], widen4<BF16>(r[u]));
+      }
+    }
+    return acc;
+  };
+  finish_row<WK>(p, G, dst, D, true, 0, col_blocks(D), getG);
+}
+
 template <int CPL, int UNR, bool BF16, int WK>
 __device__ __forceinline__ void wide_item(const RedParams& p, const WideRun& m, const WideLane& d0,
                                           int cb) {
@@ -2355,6 +2404,8 @@ __device__ __forceinline__ void wide_item(const RedParams& p, const WideRun& m, 
   const uint64_t kv0 = rl64(d0.kv, 0);
   const int t = uni32(table_of(p, (uint32_t)(kv0 & imask)));
   const int D = uni32(p.doff[t + 1] - p.doff[t]);
+  // whole rows wider than one item are served by k_reduce_wide_multi
+  if ((p.mode == kModeAdagrad || WK == kWINT8) && D > 64 * CPL) return;
   if (D <= 512 || cb * 64 * CPL >= D) return;
   const int col = cb * 64 * CPL + 4 * lane_id();
   int vmask = 0;
@@ -2398,7 +2449,7 @@ __device__ __forceinline__ void wide_item(const RedParams& p, const WideRun& m, 
     }
   }
   if constexpr (WK == kWINT8) {
-    // one item holds the whole row (INT8 rows are at most 1024 wide)
+    // one item holds the whole row (up to 1024 columns)
     double mult = (double)p.lr, mm = 0.0;
     if (p.mode == kModeAdagrad) {
       double ss = 0.0;
@@ -2428,7 +2479,7 @@ __device__ __forceinline__ void wide_item(const RedParams& p, const WideRun& m, 
     return;
   }
   if (p.mode == kModeAdagrad) {
-    // one item holds the whole row (row-wise Adagrad rows are at most 1024 wide)
+    // one item holds the whole row (up to 1024 columns)
     double ss = 0.0;
 #pragma unroll
     for (int i = 0; i < NP; ++i)
@@ -2485,6 +2536,29 @@ void k_reduce_wide(RedParams p) {
   }
 }
 
+
+// Short runs of row-wise Adagrad / INT8 rows wider than 1024 columns: one
+// wave per run (grid-stride over the runs), launched only when a table is
+// that wide.
+template <bool BF16, int WK>
+__global__ __launch_bounds__(256) void k_reduce_wide_multi(RedParams p) {
+  const int64_t runs = *p.num_runs;
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  const uint64_t imask = info_mask(p);
+  for (int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); r < runs; r += nw) {
+    WideRun m;
+    m.s = uni32(p.cum[r]);
+    m.e = uni32(p.cum[r + 1]);
+    const int len = m.e - m.s;
+    if (len <= 0 || len >= p.thr) continue;
+    const WideLane d0 = wide_lane(p, m, 0);
+    const uint64_t kv0 = rl64(d0.kv, 0);
+    const int t = uni32(table_of(p, (uint32_t)(kv0 & imask)));
+    const int D = uni32(p.doff[t + 1] - p.doff[t]);
+    if (D <= 1024) continue;
+    wide_run_multi<BF16, WK>(p, m, d0, t, D, (int64_t)(kv0 >> p.info_bits));
+  }
+}
 
 // ------------------------------------------------------------------ k_forward
 //
@@ -2757,9 +2831,15 @@ struct WideLaunch {
   }
   static void go(RedParams q, int dmax, const int* grid, hipStream_t s) {
     if (q.mode == kModeAdagrad || WK == kWINT8) {
-      q.wide_ncb = (dmax + 1023) / 1024;
+      q.wide_ncb = 1;  // one item per run: a whole row of up to 1024 columns
       hipLaunchKernelGGL((k_reduce_wide<16, kWideUnr16, BF16, WK>), dim3(blocks(q, grid[0])),
                          dim3(256), 0, s, q);
+      if (dmax > 1024) {
+        // wider rows: one wave per run, as many workgroups as the runs allow
+        // up to the wide reducer's grid
+        hipLaunchKernelGGL((k_reduce_wide_multi<BF16, WK>), dim3(blocks(q, grid[0])), dim3(256), 0,
+                           s, q);
+      }
     } else {
       q.wide_ncb = (dmax + 64 * kWideCpl - 1) / (64 * kWideCpl);
       hipLaunchKernelGGL((k_reduce_wide<kWideCpl, kWideUnr, BF16, WK>), dim3(blocks(q, grid[1])),

@@ -348,13 +348,6 @@ def test_host_detected_errors(sgb):
     with pytest.raises(sgb.SgbError) as e:
         plan.backward(g, idx, None, 0, None, "sgd", workspace=ws)   # no weights
     assert e.value.name == "SGB_ERR_INVALID_ARGUMENT"
-    wide = sgb.Plan(np.array([0, 10]), np.array([0, 2048]), "sum", 4)
-    with pytest.raises(sgb.SgbError) as e:
-        wide.backward(torch.zeros(1, 2048, device="cuda"), idx[:1], torch.tensor([0, 1],
-                      device="cuda"), 1, None, "rowwise_adagrad", weights=torch.zeros(20480,
-                      device="cuda"), momentum=torch.zeros(10, device="cuda"),
-                      workspace=wide.workspace(1, 1))
-    assert e.value.name == "SGB_ERR_UNSUPPORTED"
 
 
 @pytest.mark.parametrize("cfg", [2, 5])
