@@ -73,6 +73,12 @@ def _lib(path: Optional[str] = None):
         lib.orc_bf16_round_array.restype = None
         lib.orc_update_rows_bf16.argtypes = [i32, i64, vp, i32, vp, f32, f32, vp, vp, vp, i32,
                                              u64, u32]
+        lib.orc_f16_round_array.argtypes = [vp, vp, vp, i64]
+        lib.orc_f16_round_array.restype = None
+        lib.orc_f16_widen_array.argtypes = [vp, vp, i64]
+        lib.orc_f16_widen_array.restype = None
+        lib.orc_update_rows_f16.argtypes = [i32, i64, vp, i32, vp, f32, f32, vp, vp, vp, i32,
+                                            u64, u32]
         lib.orc_i8_quantize.argtypes = [vp, i64, i32, vp]
         lib.orc_i8_quantize.restype = None
         lib.orc_i8_dequantize.argtypes = [vp, i64, i32, vp]
@@ -80,7 +86,7 @@ def _lib(path: Optional[str] = None):
         lib.orc_update_rows_int8.argtypes = [i32, i64, vp, i32, vp, f32, f32, vp, i32, vp]
         for f in (lib.orc_validate, lib.orc_linearize, lib.orc_runs,
                   lib.orc_row_grads, lib.orc_update_rows, lib.orc_forward,
-                  lib.orc_update_rows_bf16, lib.orc_update_rows_int8):
+                  lib.orc_update_rows_bf16, lib.orc_update_rows_int8, lib.orc_update_rows_f16):
             f.restype = ctypes.c_int
         _libs[path] = lib
     return _libs[path]
@@ -250,6 +256,44 @@ def update_rows_bf16(mode: str, G: np.ndarray, D: np.ndarray, rows0: np.ndarray,
                                           float(eps), _ptr(rows), _ptr(mom), _ptr(ids),
                                           1 if stochastic else 0, int(seed) & (2**64 - 1),
                                           int(offset) & 0xFFFFFFFF), "update_rows_bf16")
+    return rows, mom
+
+
+def f16_round(x: np.ndarray, rnd: Optional[np.ndarray] = None,
+              lib: Optional[str] = None) -> np.ndarray:
+    """fp32 -> binary16 bit patterns (uint16): nearest even, or stochastic
+    with one uint32 random word per element."""
+    x = np.ascontiguousarray(x, np.float32).ravel()
+    r = None if rnd is None else np.ascontiguousarray(rnd, np.uint32).ravel()
+    out = np.zeros(x.size, np.uint16)
+    _lib(lib).orc_f16_round_array(_ptr(x), _ptr(r), _ptr(out), x.size)
+    return out
+
+
+def f16_widen(h: np.ndarray, lib: Optional[str] = None) -> np.ndarray:
+    """binary16 bit patterns -> fp32 (exact)."""
+    h = np.ascontiguousarray(h, np.uint16).ravel()
+    out = np.zeros(h.size, np.float32)
+    _lib(lib).orc_f16_widen_array(_ptr(h), _ptr(out), h.size)
+    return out
+
+
+def update_rows_f16(mode: str, G: np.ndarray, D: np.ndarray, rows0: np.ndarray,
+                    mom0: Optional[np.ndarray], row_ids: np.ndarray, lr: float = 0.0,
+                    eps: float = 0.0, stochastic: bool = True, seed: int = 0, offset: int = 0,
+                    lib: Optional[str] = None):
+    """SGD / row-wise Adagrad on fp16 rows (uint16 bit patterns [n, ldg]);
+    returns (rows uint16 [n, ldg], mom fp32 [n])."""
+    G = np.ascontiguousarray(G, np.float64)
+    n, ldg = G.shape
+    rows = np.ascontiguousarray(rows0, np.uint16).copy()
+    mom = np.zeros(n, np.float32) if mom0 is None else np.ascontiguousarray(mom0, np.float32).copy()
+    D = np.ascontiguousarray(D, np.int32)
+    ids = np.ascontiguousarray(row_ids, np.int64)
+    _check(_lib(lib).orc_update_rows_f16(MODE[mode], n, _ptr(D), ldg, _ptr(G), float(lr),
+                                         float(eps), _ptr(rows), _ptr(mom), _ptr(ids),
+                                         1 if stochastic else 0, int(seed) & (2**64 - 1),
+                                         int(offset) & 0xFFFFFFFF), "update_rows_f16")
     return rows, mom
 
 

@@ -30,7 +30,8 @@
  * invariant, closed forms of the optimizer steps and brute-force run
  * structure; the bf16 weight rows by the generator's published known-answer
  * vectors, torch's fp32 -> bf16 conversion, exhaustive rounding counts and
- * binomial bounds.  No function is "parity unpinned".
+ * binomial bounds; the fp16 rows by numpy's and torch's IEEE fp32 -> fp16
+ * conversion, exhaustive rounding counts and closed forms.  No function is "parity unpinned".
  */
 #include <math.h>
 #include <stdint.h>
@@ -569,6 +570,135 @@ int orc_update_rows_bf16(int32_t mode, int64_t nrows, const int32_t* D, int32_t 
     for (int d = 0; d < Dk && st == ORC_OK; ++d)
       h[d] = stochastic ? orc_bf16_sr(tmp[d], orc_sr_word(seed, offset, row_ids[k], d))
                         : orc_bf16_rne(tmp[d]);
+  }
+  free(tmp);
+  return st;
+}
+
+/* ------------------------------------------------------------------------ */
+/* fp16 weight rows: round to nearest even, or stochastic rounding          */
+/* ------------------------------------------------------------------------ */
+
+/* The page's 16-bit weight rows may also be IEEE binary16 (fp16).  Readings
+ * (the rounding bodies are not printed; the generator and the element's
+ * random word are those read above for bf16 rows):
+ *  - the grid: binary16 values, spacing u = 2^(e - 10) in binade
+ *    [2^e, 2^(e+1)) for e >= -14 and u = 2^-24 below 2^-14 (gradual
+ *    underflow), continued without an upper bound; a magnitude above the
+ *    largest finite value 65504 becomes infinity;
+ *  - nearest even: IEEE 754 rounding to that grid (so 65520, the midpoint
+ *    above 65504, and anything larger become infinity);
+ *  - stochastic: with lo the grid point at or below |x| and f = (|x| - lo)
+ *    / u, the magnitude rounds up to lo + u iff the element's full 32-bit
+ *    word w satisfies w < f * 2^32 (probability f, so the rounding is
+ *    unbiased where no overflow occurs);
+ *  - infinities keep their sign; a NaN becomes the quiet NaN 0x7E00 with its
+ *    sign. */
+
+/* Grid point at or below a >= 0 (as a count q of spacings u) and the
+ * fraction of a spacing above it; all exact in double for an fp32 a. */
+static double orc_f16_grid(double a, double* u, double* frac) {
+  if (a < ldexp(1.0, -14)) {
+    *u = ldexp(1.0, -24);
+  } else {
+    int k;
+    (void)frexp(a, &k);  /* a = m * 2^k, m in [0.5, 1): binade e = k - 1 */
+    *u = ldexp(1.0, k - 1 - 10);
+  }
+  const double q = floor(a / *u);
+  *frac = a / *u - q;
+  return q;
+}
+
+/* binary16 bits of sign and magnitude v (a grid point, or beyond 65504) */
+static uint16_t orc_f16_encode(int neg, double v) {
+  const uint16_t s = neg ? 0x8000u : 0u;
+  if (v > 65504.0) return (uint16_t)(s | 0x7C00u);
+  if (v < ldexp(1.0, -14)) return (uint16_t)(s | (uint16_t)(v * ldexp(1.0, 24)));
+  int k;
+  (void)frexp(v, &k);
+  const int e = k - 1;
+  const uint16_t mant = (uint16_t)((v / ldexp(1.0, e) - 1.0) * 1024.0);
+  return (uint16_t)(s | (uint16_t)((e + 15) << 10) | mant);
+}
+
+/* non-finite inputs; returns 1 when x was one */
+static int orc_f16_special(float x, uint16_t* h) {
+  if (isnan(x)) {
+    *h = (uint16_t)((signbit(x) ? 0x8000u : 0u) | 0x7E00u);
+    return 1;
+  }
+  if (isinf(x)) {
+    *h = (uint16_t)((x < 0 ? 0x8000u : 0u) | 0x7C00u);
+    return 1;
+  }
+  return 0;
+}
+
+uint16_t orc_f16_rne(float x) {
+  uint16_t h;
+  if (orc_f16_special(x, &h)) return h;
+  double u, f;
+  const double a = fabs((double)x);
+  double q = orc_f16_grid(a, &u, &f);
+  if (f > 0.5 || (f == 0.5 && fmod(q, 2.0) == 1.0)) q += 1.0;
+  return orc_f16_encode(signbit(x) != 0, q * u);
+}
+
+uint16_t orc_f16_sr(float x, uint32_t rnd) {
+  uint16_t h;
+  if (orc_f16_special(x, &h)) return h;
+  double u, f;
+  const double a = fabs((double)x);
+  double q = orc_f16_grid(a, &u, &f);
+  if ((double)rnd < f * 4294967296.0) q += 1.0;
+  return orc_f16_encode(signbit(x) != 0, q * u);
+}
+
+/* binary16 -> fp32, exact */
+static float orc_f16_to_f32(uint16_t h) {
+  const int neg = (h >> 15) & 1, ex = (h >> 10) & 31, man = h & 1023;
+  double v;
+  if (ex == 31) v = man ? NAN : INFINITY;
+  else if (ex == 0) v = ldexp((double)man, -24);
+  else v = ldexp(1.0 + man / 1024.0, ex - 15);
+  return (float)(neg ? -v : v);
+}
+
+/* Rounds n fp32 values; rnd == NULL: nearest even, else stochastic with rnd[i]. */
+void orc_f16_round_array(const float* x, const uint32_t* rnd, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = rnd ? orc_f16_sr(x[i], rnd[i]) : orc_f16_rne(x[i]);
+}
+
+void orc_f16_widen_array(const uint16_t* h, float* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_f16_to_f32(h[i]);
+}
+
+/* SGD or row-wise Adagrad on fp16 rows: widened exactly to fp32, updated as
+ * orc_update_rows does (fp64, rounded once to fp32), rounded to fp16.  rows:
+ * [nrows][ldg] binary16 bit patterns, updated in place; row_ids: the rows'
+ * linear ids (the stochastic-rounding counter). */
+int orc_update_rows_f16(int32_t mode, int64_t nrows, const int32_t* D, int32_t ldg,
+                        const double* G, float lr, float eps, uint16_t* rows, float* mom,
+                        const int64_t* row_ids, int32_t stochastic, uint64_t seed,
+                        uint32_t offset) {
+  if (mode != ORC_SGD && mode != ORC_ROWWISE_ADAGRAD) return ORC_INVALID_ARGUMENT;
+  float* tmp = (float*)malloc(sizeof(float) * (size_t)(ldg > 0 ? ldg : 1));
+  if (tmp == NULL) return ORC_INVALID_ARGUMENT;
+  int st = ORC_OK;
+  for (int64_t k = 0; k < nrows && st == ORC_OK; ++k) {
+    uint16_t* h = rows + k * (int64_t)ldg;
+    const int Dk = D[k];
+    if (Dk <= 0 || Dk > ldg) {
+      st = ORC_INVALID_ARGUMENT;
+      break;
+    }
+    for (int d = 0; d < Dk; ++d) tmp[d] = orc_f16_to_f32(h[d]);
+    st = orc_update_rows(mode, 0, 1, &D[k], ldg, G + k * (int64_t)ldg, lr, eps, tmp,
+                         mom ? &mom[k] : NULL);
+    for (int d = 0; d < Dk && st == ORC_OK; ++d)
+      h[d] = stochastic ? orc_f16_sr(tmp[d], orc_sr_word(seed, offset, row_ids[k], d))
+                        : orc_f16_rne(tmp[d]);
   }
   free(tmp);
   return st;
