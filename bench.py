@@ -389,6 +389,8 @@ def main():
     fwd = forward_measure(plan, inp, spec, indices, offsets, psw, out, ws, args.steps, rows_D)
     bf16w = bf16_weights_measure(plan, spec, grad_output, indices, offsets, B, psw, out, mom, ws,
                                  args.steps, ms_per_step)
+    f16w = bf16_weights_measure(plan, spec, grad_output, indices, offsets, B, psw, out, mom, ws,
+                                args.steps, ms_per_step, dtype=torch.float16)
     int8w = int8_weights_measure(plan, inp, spec, grad_output, indices, offsets, B, psw, mom, ws,
                                  args.steps, ms_per_step)
     atomic = atomic_measure(inp, spec, grad_output, indices, offsets, psw, out,
@@ -480,6 +482,7 @@ def main():
                      "launch_ms": per_launch_ms},
         "forward": fwd,
         "bf16_weights": bf16w,
+        "f16_weights": f16w,
         "int8_weights": int8w,
         "atomic_scatter": atomic,
         "cpu_baseline": cpu,
@@ -534,14 +537,15 @@ def forward_measure(plan, inp, spec, indices, offsets, psw, table, ws, steps,
 
 
 def bf16_weights_measure(plan, spec, grad_output, indices, offsets, B, psw, out, mom, ws, steps,
-                         ms_path):
-    """The same step with the weights held in bf16 and stochastic rounding
-    in the fused update (SGD and row-wise Adagrad workloads only): a bf16
-    copy of the weights (nearest-even of the fp32 ones), `steps` plain calls
-    timed by HIP events, each with its own Philox offset."""
+                         ms_path, dtype=torch.bfloat16):
+    """The same step with the weights held in a 16-bit type (bf16, or fp16
+    with dtype=torch.float16) and stochastic rounding in the fused update
+    (SGD and row-wise Adagrad workloads only): a 16-bit copy of the weights
+    (nearest-even of the fp32 ones), `steps` plain calls timed by HIP
+    events, each with its own Philox offset."""
     if spec.mode == "dense":
         return None
-    w = out.to(torch.bfloat16)
+    w = out.to(dtype)
     m = None if mom is None else mom.clone()
 
     def call(k):

@@ -72,8 +72,9 @@ typedef enum {
 typedef enum { SGB_POOL_SUM = 0, SGB_POOL_MEAN = 1, SGB_POOL_NONE = 2 } sgb_pooling;
 
 /* Element type of grad_output (F32, BF16) and of weight rows (F32, BF16,
- * INT8: row-wise quantized rows, weights only). */
-typedef enum { SGB_F32 = 0, SGB_BF16 = 1, SGB_INT8 = 2 } sgb_dtype;
+ * F16: IEEE binary16, INT8: row-wise quantized rows; the last two weights
+ * only). */
+typedef enum { SGB_F32 = 0, SGB_BF16 = 1, SGB_INT8 = 2, SGB_F16 = 3 } sgb_dtype;
 
 /* Output mode, FBTT page OPTIM_{SGD, ADAGRAD, DENSE} (Adagrad is row-wise). */
 typedef enum { SGB_DENSE_GRAD = 0, SGB_SGD = 1, SGB_ROWWISE_ADAGRAD = 2 } sgb_mode;
@@ -152,26 +153,32 @@ typedef struct {
   /* 16-bit weights (FBGEMM page, split-kernel weight store: a 16-bit row is
      stored with stochastic rounding from a Philox state seeded per call).
      A zero-initialised tail keeps fp32 weights.                               */
-  int32_t weights_dtype;       /* SGB_F32, SGB_BF16 or SGB_INT8 (the last two
-                                  SGD / Adagrad only: with DENSE they are
-                                  SGB_ERR_UNSUPPORTED).  INT8 rows (FBGEMM
-                                  page: 8-bit rows carry their quantization
-                                  parameters, recomputed from the updated row)
-                                  need every D_t <= 1024 (else
-                                  SGB_ERR_UNSUPPORTED): code c stands for
+  int32_t weights_dtype;       /* SGB_F32, SGB_BF16, SGB_F16 or SGB_INT8 (the
+                                  last three SGD / Adagrad only: with DENSE
+                                  they are SGB_ERR_UNSUPPORTED).  INT8 rows
+                                  (FBGEMM page: 8-bit rows carry their
+                                  quantization parameters, recomputed from
+                                  the updated row): code c stands for
                                   fmaf(c, scale, bias); after the fp32-row
                                   update, bias = row min, scale = (max - min)
                                   / 255, code = rint((w - bias) / scale)
                                   clamped to [0, 255] (0 if scale is 0), fp32
                                   arithmetic with correctly rounded division */
-  int32_t stochastic_rounding; /* bf16: 1 = stochastic, 0 = nearest even.  The
-                                  updated value is formed in fp32 as for fp32
-                                  rows, then element (linear id r, column d)
-                                  adds the high 16 bits of word d % 4 of
+  int32_t stochastic_rounding; /* 16-bit rows: 1 = stochastic, 0 = nearest
+                                  even.  The updated value is formed in fp32
+                                  as for fp32 rows; element (linear id r,
+                                  column d) draws word w = word d % 4 of
                                   Philox4x32-10(counter = (d / 4, r mod 2^32,
                                   r / 2^32, sr_offset mod 2^32), key = (sr_seed
-                                  mod 2^32, sr_seed / 2^32)) to its fp32 bit
-                                  pattern and keeps the high half              */
+                                  mod 2^32, sr_seed / 2^32)).  bf16: adds the
+                                  high 16 bits of w to the fp32 bit pattern
+                                  and keeps the high half.  fp16: with f the
+                                  fraction of the binary16 spacing (2^-24
+                                  below 2^-14) by which the magnitude exceeds
+                                  the grid point below it, rounds the
+                                  magnitude up iff w < f * 2^32; beyond 65504
+                                  the result is infinity.  Nearest even is
+                                  IEEE rounding to either format.              */
   uint64_t sr_seed;            /* Philox key                                   */
   uint64_t sr_offset;          /* its low 32 bits: counter word 3 (e.g. the
                                   step), so steps draw different bits         */

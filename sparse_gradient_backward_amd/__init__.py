@@ -48,7 +48,7 @@ if len(_hip_runtimes()) > 1:
 SGB_OK, SGB_ERR_INVALID_ARGUMENT, SGB_ERR_UNSUPPORTED, SGB_ERR_WORKSPACE_TOO_SMALL, \
     SGB_ERR_INDEX_OUT_OF_RANGE, SGB_ERR_BAD_OFFSETS, SGB_ERR_HIP, SGB_ERR_INTERNAL = range(8)
 POOLING = {"sum": 0, "mean": 1, "none": 2}
-DTYPE = {"f32": 0, "bf16": 1, "int8": 2}
+DTYPE = {"f32": 0, "bf16": 1, "int8": 2, "f16": 3}
 MODE = {"dense": 0, "sgd": 1, "rowwise_adagrad": 2}
 
 
@@ -175,9 +175,9 @@ def sgb_backward(plan: int, grad_output, indices, offsets, B: int, per_sample_we
                  sr_offset: int = 0) -> None:
     """Enqueue one backward pass.  Tensors are device tensors; grad_output is
     float32 or bfloat16, indices/offsets int64, per_sample_weights float32;
-    weights float32, or bfloat16 (SGD / row-wise Adagrad) rounded to nearest
-    even or, with stochastic_rounding, stochastically from (sr_seed,
-    sr_offset), or uint8 INT8 rows (SGD / row-wise Adagrad: each row its D
+    weights float32, or bfloat16 / float16 (SGD / row-wise Adagrad) rounded
+    to nearest even or, with stochastic_rounding, stochastically from
+    (sr_seed, sr_offset), or uint8 INT8 rows (SGD / row-wise Adagrad: each row its D
     codes then fp32 scale and bias, tables back to back).
     `events`, if given, is a list of 2 * len(STAGES) recorded-once
     torch.cuda.Event(enable_timing=True) objects (or None entries) that the
@@ -220,7 +220,8 @@ def _marshal(grad_output, indices, offsets, B, per_sample_weights, mode, weights
     for name, t, dt in (("indices", indices, torch.int64), ("offsets", offsets, torch.int64),
                         ("per_sample_weights", per_sample_weights, torch.float32),
                         ("weights", weights, weights.dtype if weights is not None and
-                         weights.dtype in (torch.bfloat16, torch.uint8) else torch.float32),
+                         weights.dtype in (torch.bfloat16, torch.float16, torch.uint8)
+                         else torch.float32),
                         ("momentum", momentum, torch.float32),
                         ("grad", grad, torch.float32)):
         if t is not None and (t.dtype != dt or not t.is_contiguous()):
@@ -229,7 +230,7 @@ def _marshal(grad_output, indices, offsets, B, per_sample_weights, mode, weights
         raise SgbError(SGB_ERR_INVALID_ARGUMENT, f"{where}: grad_output must be contiguous")
     batch = _Batch(_ptr(grad_output), DTYPE[gd], _ptr(indices), int(indices.numel()),
                    _ptr(offsets), int(B), _ptr(per_sample_weights))
-    wdt = {torch.bfloat16: "bf16", torch.uint8: "int8"}.get(
+    wdt = {torch.bfloat16: "bf16", torch.float16: "f16", torch.uint8: "int8"}.get(
         weights.dtype if weights is not None else None, "f32")
     upd = _Update(MODE[mode], _ptr(weights), _ptr(momentum), _ptr(grad), 1 if accumulate else 0,
                   float(lr), float(eps), DTYPE[wdt],

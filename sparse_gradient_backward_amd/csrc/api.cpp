@@ -383,10 +383,12 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   if (u->mode == SGB_SGD && !u->weights) return SGB_ERR_INVALID_ARGUMENT;
   if (u->mode == SGB_ROWWISE_ADAGRAD && (!u->weights || !u->momentum))
     return SGB_ERR_INVALID_ARGUMENT;
-  if (u->weights_dtype != SGB_F32 && u->weights_dtype != SGB_BF16 && u->weights_dtype != SGB_INT8)
+  if (u->weights_dtype != SGB_F32 && u->weights_dtype != SGB_BF16 && u->weights_dtype != SGB_INT8 &&
+      u->weights_dtype != SGB_F16)
     return SGB_ERR_INVALID_ARGUMENT;
   if (u->mode == SGB_DENSE_GRAD && u->weights_dtype != SGB_F32) return SGB_ERR_UNSUPPORTED;
-  const bool w_bf16 = u->mode != SGB_DENSE_GRAD && u->weights_dtype == SGB_BF16;
+  const bool w_f16 = u->mode != SGB_DENSE_GRAD && u->weights_dtype == SGB_F16;
+  const bool w_bf16 = u->mode != SGB_DENSE_GRAD && (u->weights_dtype == SGB_BF16 || w_f16);
   const bool w_int8 = u->mode != SGB_DENSE_GRAD && u->weights_dtype == SGB_INT8;
   void* outv = u->mode == SGB_DENSE_GRAD ? static_cast<void*>(u->grad) : u->weights;
   if (!aligned(outv, 16)) return SGB_ERR_INVALID_ARGUMENT;
@@ -586,6 +588,7 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   q.out_q = w_int8 ? static_cast<uint8_t*>(outv) : nullptr;
   q.woff8 = p->d_woff8;
   q.w_kind = w_int8 ? 2 : (w_bf16 ? 1 : 0);
+  q.w_f16 = w_f16 ? 1 : 0;
   q.sr = (w_bf16 && u->stochastic_rounding) ? 1 : 0;
   q.sr_key0 = (uint32_t)u->sr_seed;
   q.sr_key1 = (uint32_t)(u->sr_seed >> 32);

@@ -1393,8 +1393,62 @@ __device__ __forceinline__ uint32_t bf16_sr(float x, uint32_t rnd) {
   return (u + (rnd >> 16)) >> 16;
 }
 
-// The row's old values at columns [col + off, col + off + 4): fp32, or bf16
-// widened exactly.  The address is formed as (row + col) + off: the
+// ---- fp16 weight rows
+//
+// The 16-bit rows may also be IEEE binary16 (the same instances as bf16 rows,
+// switched by p.w_f16).  Widening is exact.  Rounding works on the fp32 bit
+// pattern: the significand m (implicit bit included) is cut at the binary16
+// grid of its binade (spacing 2^(max(E, -14) - 10) for fp32 exponent E, so
+// values below 2^-14 land on the subnormal grid of 2^-24); the sh dropped
+// bits decide the rounding, and a carry out of the kept bits moves to the
+// next binade, to infinity past 65504.  Nearest even rounds up past half a
+// spacing and on ties to an odd count; stochastic rounding rounds the
+// magnitude up iff the element's 32-bit word w satisfies w < f * 2^32, f the
+// dropped fraction (w an integer, so against the ceiling of f * 2^32).
+// Infinities keep their sign; a NaN becomes the quiet NaN 0x7E00 with its
+// sign.
+
+__device__ __forceinline__ float f16_widen(uint32_t h) {
+  const uint32_t s = (h & 0x8000u) << 16, ex = (h >> 10) & 31u, man = h & 1023u;
+  if (ex == 31u) return __uint_as_float(s | 0x7F800000u | (man << 13));
+  if (ex != 0u) return __uint_as_float(s | ((ex + 112u) << 23) | (man << 13));
+  // subnormal or zero: man * 2^-24, exact in fp32
+  const float v = (float)man * 5.9604644775390625e-08f;
+  return s ? -v : v;
+}
+
+__device__ __forceinline__ uint32_t f16_round(float x, uint32_t rnd, bool sr) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t s = (u >> 16) & 0x8000u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a >= 0x7F800000u) return s | (a > 0x7F800000u ? 0x7E00u : 0x7C00u);
+  if (a >= 0x47800000u) return s | 0x7C00u;  // |x| >= 65536
+  const int e = (int)(a >> 23);
+  const uint32_t m = (a & 0x7FFFFFu) | (e ? 0x800000u : 0u);
+  const int E = e ? e - 127 : -126;
+  const int Eg = E > -14 ? E : -14;
+  const int sh = 13 + (Eg - E);  // dropped bits, >= 13
+  const uint32_t q = sh >= 24 ? 0u : m >> sh;
+  const uint32_t rem = sh >= 24 ? m : (m & ((1u << sh) - 1u));
+  bool up;
+  if (!sr) {
+    const uint32_t half = 1u << (sh - 1 < 31 ? sh - 1 : 31);
+    up = sh <= 24 && (rem > half || (rem == half && (q & 1u)));
+  } else {
+    uint64_t thr;
+    if (sh <= 32) {
+      thr = (uint64_t)rem << (32 - sh);
+    } else {
+      const int k = sh - 32;
+      thr = k >= 32 ? (uint64_t)(rem != 0u) : (((uint64_t)rem + (1ull << k) - 1ull) >> k);
+    }
+    up = (uint64_t)rnd < thr;
+  }
+  return s | ((((uint32_t)(Eg + 14)) << 10) + q + (up ? 1u : 0u));
+}
+
+// The row's old values at columns [col + off, col + off + 4): fp32, or bf16 /
+// fp16 widened exactly.  The address is formed as (row + col) + off: the
 // short-run reducer keeps row + col across its pieces, and forming
 // row + (col + off) instead costs it a register (and a spill).
 template <int WK>
@@ -1404,6 +1458,9 @@ __device__ __forceinline__ float4 ldw4(const RedParams& p, const RowDst& d, int 
   } else if constexpr (WK == kWBF16) {
     const uint2 u =
         *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(d.out) + col + off);
+    if (p.w_f16)
+      return make_float4(f16_widen(u.x & 0xffffu), f16_widen(u.x >> 16), f16_widen(u.y & 0xffffu),
+                         f16_widen(u.y >> 16));
     return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
                        __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
   } else {
@@ -1435,10 +1492,22 @@ __device__ __forceinline__ void stw4(const RedParams& p, const RowDst& d, int co
     const U4 r = philox4x32_10(
         U4{(uint32_t)col >> 2, (uint32_t)d.lin, (uint32_t)((uint64_t)d.lin >> 32), p.sr_ctr3},
         p.sr_key0, p.sr_key1);
-    h0 = bf16_sr(v.x, r.x);
-    h1 = bf16_sr(v.y, r.y);
-    h2 = bf16_sr(v.z, r.z);
-    h3 = bf16_sr(v.w, r.w);
+    if (p.w_f16) {
+      h0 = f16_round(v.x, r.x, true);
+      h1 = f16_round(v.y, r.y, true);
+      h2 = f16_round(v.z, r.z, true);
+      h3 = f16_round(v.w, r.w, true);
+    } else {
+      h0 = bf16_sr(v.x, r.x);
+      h1 = bf16_sr(v.y, r.y);
+      h2 = bf16_sr(v.z, r.z);
+      h3 = bf16_sr(v.w, r.w);
+    }
+  } else if (p.w_f16) {
+    h0 = f16_round(v.x, 0u, false);
+    h1 = f16_round(v.y, 0u, false);
+    h2 = f16_round(v.z, 0u, false);
+    h3 = f16_round(v.w, 0u, false);
   } else {
     h0 = bf16_rne(v.x);
     h1 = bf16_rne(v.y);

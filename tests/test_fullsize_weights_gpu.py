@@ -1,5 +1,6 @@
-"""GPU parity of bf16 and INT8 weight rows at the full sizes of the SGD and
-row-wise Adagrad workloads (configs 1, 3, 5), drawn as bench.py draws them.
+"""GPU parity of bf16, fp16 and INT8 weight rows at the full sizes of the
+SGD and row-wise Adagrad workloads (configs 1, 3, 5), drawn as bench.py draws
+them.
 
 Sampled rows -- the 32 longest runs and 200 random others -- are compared
 with the oracle from each row's initial value read back before the call,
@@ -155,3 +156,48 @@ def test_full_size_int8_rows(sgb, cfg):
     _check_mom(mom, m0s, m0u, sample, untouched, emom, f"config {cfg}")
     assert np.array_equal(get(uidx)[uvalid], u0[uvalid])
     print(f"[fullsize-int8] config {cfg}: ok ({bad} codes off by one of {ncode})", flush=True)
+
+
+@pytest.mark.parametrize("cfg", [1, 3, 5])
+def test_full_size_f16_rows(sgb, cfg):
+    """fp16 (IEEE binary16) rows with stochastic rounding, as the bf16 case:
+    elements within two fp16 spacings plus the fp32 tolerance, at most 1 in
+    10^3 differing."""
+    spec = synth.spec(cfg)
+    print(f"[fullsize-f16] config {cfg} {spec.name}: generating", flush=True)
+    inp = synth.generate(spec)
+    n = int(inp.weights_offsets[-1])
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(spec.seed)
+    w = torch.empty(n, dtype=torch.float32, device="cuda").normal_(0.0, spec.weights_std,
+                                                                     generator=gen)
+    w = w.to(torch.float16)
+    mom = _momentum(inp, spec)
+    sample, untouched = _draw(inp, spec, cfg)
+    elems, valid, D = row_elements(inp, sample)
+    uel, uvalid, _ = row_elements(inp, untouched)
+    bits = lambda idx: w[torch.from_numpy(idx.reshape(-1)).cuda()].cpu().view(torch.int16) \
+        .numpy().view(np.uint16).reshape(idx.shape)
+    w0, u0 = bits(elems), bits(uel)
+    m0s = None if mom is None else mom[torch.from_numpy(sample).cuda()].cpu().numpy()
+    m0u = None if mom is None else mom[torch.from_numpy(untouched).cuda()].cpu().numpy()
+    print(f"[fullsize-f16] config {cfg}: N={inp.N}: run", flush=True)
+    _run(sgb, inp, spec, w, mom, stochastic_rounding=True, sr_seed=78, sr_offset=4)
+    G, _ = oracle.row_grads(oracle_problem(inp), sample)
+    exp, emom = oracle.update_rows_f16(spec.mode, G, D, np.where(valid, w0, 0), m0s, sample,
+                                       lr=spec.lr, eps=spec.eps, stochastic=True, seed=78,
+                                       offset=4)
+    got = bits(elems)
+    diff = (got != exp) & valid
+    if diff.any():
+        g = got[diff].view(np.float16).astype(np.float64)
+        e = exp[diff].view(np.float16).astype(np.float64)
+        mag = np.maximum(np.abs(g), np.abs(e))
+        spacing = np.where(mag < 2.0 ** -14, 2.0 ** -24,
+                           np.ldexp(1.0, np.frexp(np.maximum(mag, 2.0 ** -14))[1] - 11))
+        assert np.all(np.abs(g - e) <= 2 * spacing + 1e-4 + 1e-5 * np.abs(e))
+        assert diff.sum() <= max(2, int(valid.sum()) // 1000), f"{int(diff.sum())} differ"
+    _check_mom(mom, m0s, m0u, sample, untouched, emom, f"config {cfg}")
+    assert np.array_equal(bits(uel)[uvalid], u0[uvalid])
+    print(f"[fullsize-f16] config {cfg}: ok ({int(diff.sum())} one-spacing differences of "
+          f"{int(valid.sum())})", flush=True)
