@@ -4,10 +4,12 @@ Each workload is drawn exactly as bench.py draws it (same seeds, same plan
 and max_segment_length_per_warp) and run once.  Checked against the oracle:
   * the run structure over all N lookups, bit-exact (sorted ids and infos,
     unique ids, run lengths, starts, long runs);
-  * sampled touched rows -- the 32 longest runs (the chunked, multi-workgroup
-    ones) and 200 random others -- within |gpu - oracle| <= 1e-4 + 1e-5 |oracle|,
-    from each row's initial value read back before the call;
-  * 2000 sampled untouched rows bit-unchanged (zero for a fresh dense grad).
+  * every touched row (and, for row-wise Adagrad, every touched momentum
+    value) within |gpu - oracle| <= 1e-4 + 1e-5 |oracle|, from the rows'
+    initial values read back before the call;
+  * every other element of the weights / dense gradient and of the momentum
+    bit-unchanged (zero for a fresh dense gradient), compared on the device
+    against a copy taken before the call.
 """
 import sys
 
@@ -59,20 +61,15 @@ def test_full_size(sgb, cfg):
     if spec.mode == "rowwise_adagrad":
         mom = torch.rand(inp.total_rows, dtype=torch.float32, device="cuda", generator=gen)
 
-    # oracle run structure (all N lookups) and the rows to sample
+    # oracle run structure (all N lookups); every touched row is compared
     keys, infos, _ = oracle.linearize(oracle_problem(inp))
     ref = oracle.runs(keys, infos, spec.thr)
     uniq, lens = ref["unique_ids"], ref["run_lengths"]
-    rng = np.random.default_rng(cfg)
-    top = uniq[np.argsort(-lens, kind="stable")[:32]]
-    rnd = rng.choice(uniq, size=min(200, uniq.shape[0]), replace=False)
-    sample = np.unique(np.concatenate([top, rnd]))
-    untouched = np.setdiff1d(rng.integers(0, inp.total_rows, 4000), uniq)[:2000]
-    w0, valid = _rows_view(out, inp, sample)
-    u0, uvalid = _rows_view(out, inp, untouched)
-    m0 = None if mom is None else mom[torch.from_numpy(sample).cuda()].cpu().numpy()
-    mu0 = None if mom is None else mom[torch.from_numpy(untouched).cuda()].cpu().numpy()
-
+    w0, valid = _rows_view(out, inp, uniq)
+    m0 = None if mom is None else mom[torch.from_numpy(uniq).cuda()].cpu().numpy()
+    # copies for the untouched check (on the device)
+    out0 = out.clone()
+    mom_0 = None if mom is None else mom.clone()
     plan = sgb.Plan(inp.hash_size_cumsum, inp.D_offsets, spec.pooling, spec.thr)
     ws = plan.workspace(inp.N, B)
     kw = dict(grad=out) if spec.mode == "dense" else dict(weights=out, momentum=mom)
@@ -93,22 +90,33 @@ def test_full_size(sgb, cfg):
     assert np.array_equal(view["cumulative"].cpu().numpy(), ref["cumulative"])
     assert np.array_equal(view["long_run_ids"].cpu().numpy(), ref["long_run_ids"])
 
-    G, _ = oracle.row_grads(oracle_problem(inp), sample)
-    D = np.diff(inp.D_offsets)[np.searchsorted(inp.hash_size_cumsum, sample, side="right") - 1]
+    G, _ = oracle.row_grads(oracle_problem(inp), uniq)
+    D = np.diff(inp.D_offsets)[np.searchsorted(inp.hash_size_cumsum, uniq, side="right") - 1]
     exp, emom = oracle.update_rows(spec.mode, G, D, None if fresh else w0, m0, lr=spec.lr,
                                    eps=spec.eps, accumulate=spec.accumulate)
-    got, _ = _rows_view(out, inp, sample)
-    assert_close(got, exp, valid, f"config {cfg} sampled rows")
+    del G
+    got, _ = _rows_view(out, inp, uniq)
+    assert_close(got, exp, valid, f"config {cfg} touched rows")
+    del got, exp
     if mom is not None:
-        gm = mom[torch.from_numpy(sample).cuda()].cpu().numpy()
-        assert_close(gm, emom, None, f"config {cfg} sampled momentum")
-        gmu = mom[torch.from_numpy(untouched).cuda()].cpu().numpy()
-        assert np.array_equal(gmu.view(np.uint32), mu0.view(np.uint32))
-    gu, _ = _rows_view(out, inp, untouched)
+        gm = mom[torch.from_numpy(uniq).cuda()].cpu().numpy()
+        assert_close(gm, emom, None, f"config {cfg} momentum")
+    # every element outside the touched rows: unchanged (zero for a fresh
+    # dense gradient), on the device
+    elems, _, _ = row_elements(inp, uniq)
+    touched_idx = torch.from_numpy(elems[valid]).cuda()
+    del elems
     if fresh:
-        assert np.all(gu[uvalid] == 0)
+        changed = out.view(torch.int32) != 0
     else:
-        assert np.array_equal(gu[uvalid].view(np.uint32), u0[uvalid].view(np.uint32))
-    print(f"[fullsize] config {cfg}: ok ({sample.shape[0]} rows, {untouched.shape[0]} untouched)",
-          flush=True)
+        changed = out.view(torch.int32) != out0.view(torch.int32)
+    changed[touched_idx] = False
+    assert not bool(changed.any()), f"config {cfg}: {int(changed.sum())} untouched elements changed"
+    del changed, touched_idx, out0
+    if mom is not None:
+        mchanged = mom.view(torch.int32) != mom_0.view(torch.int32)
+        mchanged[torch.from_numpy(uniq).cuda()] = False
+        assert not bool(mchanged.any()), "untouched momentum changed"
+    print(f"[fullsize] config {cfg}: ok ({uniq.shape[0]} touched rows, {int(valid.sum())} "
+          f"elements; all others unchanged)", flush=True)
     sys.stdout.flush()
