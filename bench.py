@@ -36,13 +36,9 @@ import synth  # noqa: E402
 
 METRIC = "embedding-bwd lookups/sec + achieved HBM GB/s (% of MI355X peak), 1 GPU"
 HBM_PEAK_GBPS = 8000.0
-STAGES = ("linearize", "sort_pass", "sort", "rle_count",
-          "rle_scan", "rle_write", "runs", "fill", "reduce_long", "reduce_short")
+STAGES = ("linearize", "sort_pass", "sort", "rle", "runs", "fill", "reduce_long",
+          "reduce_short")
 SORT_KERNELS = ("sort_pass",)  # one launch per radix pass, timed on the first pass
-# run-length tiles of 4096 sorted positions up to which the library encodes
-# runs in one kernel (k_rle_write alone; the count and scan stages then time
-# no kernel)
-RLE_ONE_PASS_TILES = 128
 KERNEL_SOURCES = ("sparse_gradient_backward_amd/csrc/kernels.hip",
                   "sparse_gradient_backward_amd/csrc/internal.h",
                   "sparse_gradient_backward_amd/csrc/api.cpp")
@@ -78,7 +74,6 @@ def stage_bytes(inp: synth.Inputs, spec: synth.Spec, U: int, run_D: np.ndarray,
         512 * 8 if N > (1 << 16) else 256 * 8)
     tiles = (N + sort_tile - 1) // sort_tile
     scan_tiles = (N + 4095) // 4096
-    one_pass = scan_tiles <= RLE_ONE_PASS_TILES
 
     def update(D):
         if spec.mode == "dense":
@@ -96,9 +91,10 @@ def stage_bytes(inp: synth.Inputs, spec: synth.Spec, U: int, run_D: np.ndarray,
         # a pass reads and writes every packed word (and coefficient) once,
         # its digit totals, and publishes two look-back words per tile and digit
         "sort_pass": N * rec * 2 + tiles * radix0 * 4 * 2 + 8 * radix0 * 4,
-        "rle_count": 0 if one_pass else N * 8 + scan_tiles * 4,
-        "rle_scan": 0 if one_pass else scan_tiles * 4 * 2 + 8,
-        "rle_write": N * 8 + scan_tiles * 4 * (2 if one_pass else 1) + U * (8 + 4 + 4),
+        # the sorted words read once (compulsory: beyond 128 tiles the count
+        # kernel reads them a second time), two look-back words per tile,
+        # each run's unique id, start and run index written
+        "rle": N * 8 + scan_tiles * 4 * 2 + U * (8 + 4 + 4),
         "runs": U * (4 + 4) + int(lg.sum()) * (48 + 4 + 4),
         "fill": int((Es * Ds).sum()) * 4 if fresh else 0,
         "reduce_long": gather_long_read + int(run_len[lg].sum()) * rec + int(lg.sum()) * 48
@@ -168,6 +164,18 @@ def long_gather_elems(sorted_info: np.ndarray, cum: np.ndarray, run_len: np.ndar
         new[1:] |= inf[1:] != inf[:-1]
         total += int(new.sum()) * D
     return total
+
+
+def rle_kernels(N: int) -> str:
+    """Kernels of the run-length stage for N sorted positions (tiles of 4096):
+    up to 128 tiles the run write alone, up to 4096 the count kernel first,
+    beyond that the one-workgroup scan of the counts too."""
+    tiles = (N + 4095) // 4096
+    if tiles <= 128:
+        return "k_rle_write"
+    if tiles <= 4096:
+        return "k_rle_count+k_rle_write"
+    return "k_rle_count+k_rle_scan+k_rle_write"
 
 
 def short_kernels(dims) -> str:
@@ -412,13 +420,10 @@ def main():
         if spec.pooling != "none" else None
     del packed, infos
     sb, b_path, b_comp = stage_bytes(inp, spec, U, run_D, lens, thr, npasses, radix0, long_D)
-    # the stage that each kernel times ("sort" spans the passes; on few tiles
-    # the run-head count and scan stages are done inside k_rle_write)
+    # the kernel that each stage times ("sort" spans the passes)
     kernel_names = {"reduce_long": "k_reduce_long", "fill": "k_fill", "linearize": "k_linearize",
-                    "sort_pass": "k_sort_pass", "rle_write": "k_rle_write", "runs": "k_post",
+                    "sort_pass": "k_sort_pass", "rle": rle_kernels(inp.N), "runs": "k_post",
                     "reduce_short": short_kernels(np.diff(inp.D_offsets))}
-    if (inp.N + 4095) // 4096 > RLE_ONE_PASS_TILES:
-        kernel_names.update(rle_count="k_rle_count", rle_scan="k_rle_scan")
     # dominant kernel: the largest time per step (a sort kernel runs once per pass)
     per_step = {k: v * (npasses if k in SORT_KERNELS else 1)
                 for k, v in stage_ms.items() if k in kernel_names}

@@ -242,14 +242,13 @@ typedef enum {
                                   first radix pass's digit histogram             */
   SGB_STAGE_SORT_PASS = 1,     /* the first radix pass alone                     */
   SGB_STAGE_SORT = 2,          /* all radix passes                               */
-  SGB_STAGE_RLE_COUNT = 3,     /* run heads of every tile (inside stage 5: empty) */
-  SGB_STAGE_RLE_SCAN = 4,      /* first run index of every tile (inside 5: empty) */
-  SGB_STAGE_RLE_WRITE = 5,     /* run heads, tile scan, unique ids, run starts    */
-  SGB_STAGE_RUNS = 6,          /* run lengths, long-run list, chunk prefix        */
-  SGB_STAGE_FILL = 7,          /* zeros of the whole gradient (fresh dense only)  */
-  SGB_STAGE_REDUCE_LONG = 8,   /* long runs: chunked reduction + fused row write  */
-  SGB_STAGE_REDUCE_SHORT = 9,  /* short runs: reduction + fused row write         */
-  SGB_NUM_STAGES = 10
+  SGB_STAGE_RLE = 3,           /* run heads, first run index of every tile,
+                                  unique ids, run starts                          */
+  SGB_STAGE_RUNS = 4,          /* run lengths, long-run list, chunk prefix        */
+  SGB_STAGE_FILL = 5,          /* zeros of the whole gradient (fresh dense only)  */
+  SGB_STAGE_REDUCE_LONG = 6,   /* long runs: chunked reduction + fused row write  */
+  SGB_STAGE_REDUCE_SHORT = 7,  /* short runs: reduction + fused row write         */
+  SGB_NUM_STAGES = 8
 } sgb_stage;
 
 /*

@@ -164,8 +164,8 @@ def _stream(stream) -> Optional[int]:
     return int(s.cuda_stream)
 
 
-STAGES = ("linearize", "sort_pass", "sort", "rle_count",
-          "rle_scan", "rle_write", "runs", "fill", "reduce_long", "reduce_short")
+STAGES = ("linearize", "sort_pass", "sort", "rle", "runs", "fill", "reduce_long",
+          "reduce_short")
 
 
 def sgb_backward(plan: int, grad_output, indices, offsets, B: int, per_sample_weights,

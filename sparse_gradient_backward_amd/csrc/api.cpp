@@ -104,9 +104,9 @@ struct Layout {
   int64_t max_long = 0;   // bound on the number of long runs
   int64_t max_items = 0;  // bound on the (chunk, column block) items over all long runs
   size_t hdr = 0, hist0 = 0, zero_begin = 0, hist[kMaxPasses] = {}, sort_lb[kMaxPasses] = {},
-         rle_lb = 0, post_lb = 0, zero_end = 0, tile_runs = 0;
+         rle_lb = 0, post_lb = 0, zero_end = 0;
   size_t kvA = 0, kvB = 0, coefA = 0, coefB = 0, uniq = 0, cum = 0, headrun = 0, lens = 0, longs = 0,
-         chunkb = 0, longrec = 0, runtk = 0, sctk = 0, part = 0, total = 0;
+         chunkb = 0, longrec = 0, runtk = 0, sctk = 0, tile_runs = 0, part = 0, total = 0;
 };
 
 sgb_status make_layout(const sgb_plan_s* p, int64_t N, int32_t B, bool has_offsets, Layout* L) {
@@ -161,8 +161,10 @@ sgb_status make_layout(const sgb_plan_s* p, int64_t N, int32_t B, bool has_offse
   L->zero_begin = align_up(o, 256);
   L->hist[0] = L->hist0;
   for (int i = 1; i < L->npasses; ++i) L->hist[i] = take(sizeof(uint32_t) * kHistSlices << L->pass_bits[i]);
-  L->rle_lb = take(sizeof(uint32_t) * (size_t)L->scan_tiles);  // one pass only
-  L->post_lb = take(sizeof(uint64_t) * (size_t)L->scan_tiles);
+  const size_t scan_words =
+      (size_t)(L->scan_tiles + (L->scan_tiles + kLbScalarGroupTiles - 1) / kLbScalarGroupTiles);
+  L->rle_lb = take(sizeof(uint32_t) * scan_words);
+  L->post_lb = take(sizeof(uint64_t) * scan_words);
   L->runtk = take(sizeof(uint32_t) * (size_t)L->max_items);
   L->sctk = take(sizeof(uint32_t) * (size_t)L->max_items);
   // the radix passes' look-back words, packed by this batch's tile shapes
@@ -181,7 +183,6 @@ sgb_status make_layout(const sgb_plan_s* p, int64_t N, int32_t B, bool has_offse
   }
   L->zero_end = lb0 + used;
   o = lb0 + room;
-  L->tile_runs = take(sizeof(uint32_t) * (size_t)L->scan_tiles);
   L->kvA = take(sizeof(uint64_t) * (size_t)N);
   L->kvB = take(sizeof(uint64_t) * (size_t)N);
   L->coefA = take(sizeof(float) * (size_t)N);
@@ -189,6 +190,7 @@ sgb_status make_layout(const sgb_plan_s* p, int64_t N, int32_t B, bool has_offse
   L->uniq = take(sizeof(int64_t) * (size_t)N);
   L->cum = take(sizeof(int32_t) * (size_t)(N + 1));
   L->headrun = take(sizeof(int32_t) * (size_t)N);
+  L->tile_runs = take(sizeof(uint32_t) * (size_t)L->scan_tiles);
   L->lens = take(sizeof(int32_t) * (size_t)N);
   L->longs = take(sizeof(int32_t) * (size_t)L->max_long);
   L->longrec = take(sizeof(LongRun) * (size_t)L->max_long);
@@ -295,7 +297,13 @@ sgb_status sgb_plan_create(sgb_plan* out, int32_t T, const int64_t* hsc, const i
   bool ok = hipStreamCreateWithFlags(&p->aux[0], hipStreamNonBlocking) == hipSuccess &&
             hipStreamCreateWithFlags(&p->aux[1], hipStreamNonBlocking) == hipSuccess;
   for (int i = 0; i < 4 && ok; ++i)
-    ok = hipEventCreateWithFlags(&p->ev[i], hipEventDisableTiming) == hipSuccess;
+    // the fork events order work between the plan's streams on this device
+    // only and need no system-scope release at their records; the join event
+    // keeps it, so that a host waiting on the caller's stream sees the side
+    // stream's writes
+    ok = hipEventCreateWithFlags(&p->ev[i], hipEventDisableTiming |
+                                                (i < 3 ? hipEventDisableSystemFence : 0)) ==
+         hipSuccess;
   ok = ok && hipMalloc(&p->d_hsc, sizeof(int64_t) * (T + 1)) == hipSuccess &&
             hipMalloc(&p->d_doff, sizeof(int32_t) * (T + 1)) == hipSuccess &&
             hipMalloc(&p->d_woff, sizeof(int64_t) * (T + 1)) == hipSuccess &&
@@ -401,16 +409,6 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
     if (ev) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev), s);
   };
   auto mark = [&](int stage, int end) { mark_on(stream, stage, end); };
-  // the same marks for kernels launched from kernels.hip
-  struct MarkCtx {
-    void* const* events;
-    hipStream_t stream;
-  } mark_ctx{events, stream};
-  const StageMark mark_fn = [](void* c, int stage, int end) {
-    const MarkCtx* m = static_cast<const MarkCtx*>(c);
-    void* ev = m->events ? m->events[2 * stage + end] : nullptr;
-    if (ev) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev), m->stream);
-  };
 
   if (N == 0) {  // FBGEMM host entry: no indices -> nothing to do (dense grad stays zero)
     // clear the status word so sgb_device_status() reports this call
@@ -530,14 +528,16 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   rp.head_run = at<int32_t>(ws, L.headrun);
   rp.num_runs = &hdr->num_runs;
   rp.tiles = L.scan_tiles;
-  rp.one_pass = L.scan_tiles <= kOnePassTiles ? 1 : 0;
-  rp.fuse_scan = L.scan_tiles <= kFuseScanTiles ? 1 : 0;
-  rp.tile_runs = at<uint32_t>(ws, L.tile_runs);
   rp.lookback = at<uint32_t>(ws, L.rle_lb);
   rp.tile_ctr = &hdr->rle_tile_ctr;
+  rp.tile_runs = at<uint32_t>(ws, L.tile_runs);
+  rp.one_pass = L.scan_tiles <= kOnePassTiles ? 1 : 0;
+  rp.fuse_scan = L.scan_tiles <= kFuseScanTiles ? 1 : 0;
   rp.status = status;
   rp.epoch = epoch;
-  if (launch_rle(rp, stream, mark_fn, &mark_ctx) != hipSuccess) return SGB_ERR_HIP;
+  mark(SGB_STAGE_RLE, 0);
+  if (launch_rle(rp, stream) != hipSuccess) return SGB_ERR_HIP;
+  mark(SGB_STAGE_RLE, 1);
 
   PostParams pp{};
   pp.cum = rp.cum;
@@ -559,6 +559,7 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   pp.long_recs = at<LongRun>(ws, L.longrec);
   pp.num_long = &hdr->num_long;
   pp.total_items = &hdr->total_items;
+  pp.tiles = L.scan_tiles;
   pp.lookback = at<uint64_t>(ws, L.post_lb);
   pp.tile_ctr = &hdr->post_tile_ctr;
   pp.status = status;

@@ -68,6 +68,12 @@ constexpr int kMaxD = 8192;
 #ifndef SGB_LOOKBACK
 #define SGB_LOOKBACK 16
 #endif
+#ifndef SGB_ONE_PASS_TILES
+#define SGB_ONE_PASS_TILES 128
+#endif
+#ifndef SGB_FUSE_SCAN_TILES
+#define SGB_FUSE_SCAN_TILES 4096
+#endif
 constexpr int kSortLbGroup = 16;  // tiles per look-back group of a radix pass
 
 // Radix pass tiling.  A pass is one kernel (k_sort_pass) whose workgroups
@@ -102,15 +108,14 @@ constexpr int kHistSlices = 8;
 // zero fill: threads of each (looping) workgroup
 constexpr int kFillThreads = SGB_FILL_THREADS;
 
-// run-length tiles: up to kOnePassTiles k_rle_write alone (look-back over the
-// tile counts); up to kFuseScanTiles k_rle_count then k_rle_write summing the
-// counts itself; beyond, k_rle_count, k_rle_scan, k_rle_write
-#ifndef SGB_ONE_PASS_TILES
-#define SGB_ONE_PASS_TILES 128
-#endif
-#ifndef SGB_FUSE_SCAN_TILES
-#define SGB_FUSE_SCAN_TILES 1024
-#endif
+// groups of tiles of the scalar look-backs (run-length encoding, run
+// post-processing): their look-back words are [tiles] then [groups]
+constexpr int kLbScalarGroupTiles = 32;
+
+// run-length encoding: up to kOnePassTiles tiles k_rle_write alone (each
+// tile's first run index by look-back over the tiles' head counts); up to
+// kFuseScanTiles k_rle_count, then k_rle_write summing the counts before its
+// tile; beyond that k_rle_count, k_rle_scan and k_rle_write
 constexpr int kOnePassTiles = SGB_ONE_PASS_TILES;
 constexpr int kFuseScanTiles = SGB_FUSE_SCAN_TILES;
 
@@ -124,6 +129,7 @@ constexpr int kLinThreads = 256;
 constexpr int kLinBags = 64;
 constexpr int kLinLookups = 4 * kLinThreads;
 constexpr int kLinPer = 8;            // lookups per thread whose loads are issued together
+constexpr int kLinHistCopies = 4;     // copies of the first-pass digit histogram in LDS
 static_assert(kLinBags < kLinThreads, "one thread per bag offset of a tile");
 
 // short runs: sorted positions of one window of the short-run reducer, and
@@ -302,11 +308,11 @@ struct RleParams {
   int32_t* cum;
   int32_t* head_run;        // [N]: run index at each run's first position
   int32_t* num_runs;
+  uint32_t* lookback;       // zeroed per call: [tiles] then [groups of 32 tiles] look-back words
+  uint32_t* tile_ctr;       // dynamic tile ids (zeroed per call)
   uint32_t* tile_runs;      // [tiles]: runs starting in each tile, then the first run index
-  int32_t fuse_scan;        // tiles <= kFuseScanTiles: the write kernel sums the counts itself
-  int32_t one_pass;         // tiles <= kOnePassTiles: the write kernel alone, by look-back
-  uint32_t* lookback;       // [tiles], zeroed per call: look-back words of the tile run counts
-  uint32_t* tile_ctr;       // dynamic tile ids of the one-pass write (zeroed per call)
+  int32_t one_pass;         // tiles <= kOnePassTiles: k_rle_write alone, by look-back
+  int32_t fuse_scan;        // tiles <= kFuseScanTiles: k_rle_write sums the counts itself
   uint32_t* status;
   uint32_t epoch;
 };
@@ -331,7 +337,8 @@ struct PostParams {
   LongRun* long_recs;       // [num_long]
   int64_t* num_long;
   uint32_t* total_items;
-  uint64_t* lookback;       // [tiles]
+  int64_t tiles;            // tiles of kScanTile runs the grid covers at most
+  uint64_t* lookback;       // zeroed per call: [tiles] then [groups of 32 tiles]
   uint32_t* tile_ctr;
   uint32_t* status;
   uint32_t epoch;
@@ -423,10 +430,7 @@ hipError_t scratch_address(void** out);
 hipError_t launch_init(void* header_and_hist, size_t bytes, hipStream_t s);
 hipError_t launch_linearize(const LinParams& p, int grid, hipStream_t s);
 hipError_t launch_sort_pass(const SortParams& p, hipStream_t s);
-// `mark(ctx, stage, end)` (if set) records the timing events of a stage just
-// before (end = 0) and after (end = 1) its kernel.
-using StageMark = void (*)(void* ctx, int stage, int end);
-hipError_t launch_rle(const RleParams& p, hipStream_t s, StageMark mark, void* ctx);
+hipError_t launch_rle(const RleParams& p, hipStream_t s);
 hipError_t launch_post(const PostParams& p, int grid, hipStream_t s);
 hipError_t launch_fill(const FillParams& p, int grid, hipStream_t s);
 hipError_t launch_reduce_long(const RedParams& p, bool bf16, int grid, hipStream_t s);

@@ -13,9 +13,9 @@
 //                  k_sort_offsets is not launched)
 //   k_rle_count / k_rle_scan / k_rle_write
 //                  run heads of the sorted ids -> unique ids, run starts, count
-//                  (few tiles: k_rle_write alone, by look-back over the tile
-//                  counts; more: the counts summed in k_rle_write; many: all
-//                  three kernels)
+//                  (few tiles: k_rle_write alone, each tile's first run index
+//                  by a two-level look-back over the tiles' head counts; more:
+//                  the counts first, summed in k_rle_write; many: all three)
 //   k_post         run lengths, ascending long-run list and records
 //   k_fill         zeros of a fresh dense gradient (side stream, from the start)
 //   k_reduce_short8 short runs of rows up to 512 columns (side stream, after
@@ -82,22 +82,6 @@ __device__ __forceinline__ void set_status_wave(uint32_t* st, uint32_t epoch, ui
   if (m && lane_id() == __builtin_ctzll(m)) set_status(st, epoch, code);
 }
 
-// Adds 1 for this lane's digit d into the LDS histogram h: the lanes that
-// share the first valid lane's digit (on skewed ids usually the hot one) are
-// added by one atomic of their first lane.  Wave-uniform call.
-__device__ __forceinline__ void hist_add(uint32_t* h, uint32_t d, bool valid) {
-  const uint64_t live = __ballot(valid);
-  if (!live) return;
-  const int first = __builtin_ctzll(live);
-  const uint32_t d0 = (uint32_t)__shfl(d, first, 64);
-  const uint64_t same = __ballot(valid && d == d0);
-  if (valid && d == d0) {
-    if (lane_id() == first) atomicAdd(&h[d0], (uint32_t)__popcll(same));
-  } else if (valid) {
-    atomicAdd(&h[d], 1u);
-  }
-}
-
 template <typename T>
 __device__ __forceinline__ T wave_incl_scan(T x) {
   const int lane = lane_id();
@@ -138,11 +122,12 @@ __device__ __forceinline__ T block_excl_scan(T x, T* tmp, T& total) {
 
 // Decoupled look-back over scalar per-tile values for one whole wave
 // (Merrill & Garland, "Single-pass Parallel Prefix Scan with Decoupled
-// Look-back", 2016): publish this tile's aggregate, inspect the 64 preceding
-// tiles at once, sum back to the nearest inclusive prefix, publish ours.
-// Tile ids come from an atomic counter, so every tile waited on belongs to a
-// workgroup that started earlier and is resident; the wait is still bounded
-// and records kStInternal if it ever expires.
+// Look-back", 2016): publish this tile's aggregate, sum the earlier tiles'
+// words back to the nearest inclusive prefix, publish ours.  Tile ids come
+// from an atomic counter, so every tile waited on belongs to a workgroup that
+// started earlier and is resident; the wait is still bounded and records
+// kStInternal if it ever expires.  The word's top two bits flag an aggregate
+// (A) or an inclusive prefix (P).
 template <typename W>
 struct LB;
 template <>
@@ -156,20 +141,60 @@ struct LB<uint64_t> {
   static constexpr int S = 62;
 };
 
+// Two levels, for any number of tiles: the earlier tiles of this
+// tile's group of kLbScalarGroup (one load per lane), then whole groups --
+// each group's last tile publishes the group's total as soon as it has it,
+// then the inclusive prefix at the group's end -- 64 groups per load round.
+// Tiles that start together need a few rounds, not one per 64 tiles before
+// them.  lbg has a word per group.  Wave-uniform call.
+constexpr int kLbScalarGroup = kLbScalarGroupTiles;
+
 template <typename W>
-__device__ W wave_lookback(W* lb, uint32_t tile, W agg, uint32_t* status, uint32_t epoch) {
+__device__ W wave_lookback2(W* lbt, W* lbg, uint32_t tile, W agg, uint32_t* status,
+                            uint32_t epoch) {
   const int lane = lane_id();
   if (lane == 0)
-    __hip_atomic_store(&lb[tile], (tile == 0 ? LB<W>::P : LB<W>::A) | agg, __ATOMIC_RELAXED,
+    __hip_atomic_store(&lbt[tile], (tile == 0 ? LB<W>::P : LB<W>::A) | agg, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t grp = tile / kLbScalarGroup;
+  const int nin = (int)(tile - grp * kLbScalarGroup);
+  const bool glast = tile % kLbScalarGroup == kLbScalarGroup - 1;
   W excl = 0;
-  if (tile == 0) return excl;
-  int64_t top = (int64_t)tile - 1;
+  bool done = tile == 0;
   uint32_t spins = 0;
-  for (;;) {
+  if (!done && nin > 0) {
+    for (;;) {
+      const bool in = lane < nin;
+      const W v = in ? __hip_atomic_load(&lbt[tile - 1 - lane], __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT)
+                     : (W)0;
+      const uint32_t flag = (uint32_t)(v >> LB<W>::S);
+      const uint64_t pref = __ballot(in && flag == 2);
+      const uint64_t notready = __ballot(in && flag == 0);
+      const int first = pref ? __builtin_ctzll(pref) : nin - 1;
+      const uint64_t upto = (2ull << first) - 1ull;
+      if (notready & upto) {
+        if (++spins > kSpinLimit) {
+          if (lane == 0) set_status(status, epoch, kStInternal);
+          done = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        continue;
+      }
+      excl = wave_sum<W>(lane <= first ? (v & LB<W>::V) : (W)0);
+      done = pref != 0;
+      break;
+    }
+  }
+  if (!done && glast && lane == 0)
+    __hip_atomic_store(&lbg[grp], LB<W>::A | (excl + agg), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  int64_t top = (int64_t)grp - 1;
+  while (!done) {
     const int64_t idx = top - lane;
-    const W v = idx >= 0 ? __hip_atomic_load(&lb[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                         : LB<W>::P;  // before tile 0: prefix 0
+    const W v = idx >= 0 ? __hip_atomic_load(&lbg[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : LB<W>::P;  // before group 0: prefix 0
     const uint32_t flag = (uint32_t)(v >> LB<W>::S);
     const uint64_t pref = __ballot(flag == 2);
     const uint64_t notready = __ballot(flag == 0);
@@ -180,16 +205,18 @@ __device__ W wave_lookback(W* lb, uint32_t tile, W agg, uint32_t* status, uint32
         if (lane == 0) set_status(status, epoch, kStInternal);
         break;
       }
-      __builtin_amdgcn_s_sleep(2);
+      __builtin_amdgcn_s_sleep(1);
       continue;
     }
     excl += wave_sum<W>(lane <= first ? (v & LB<W>::V) : (W)0);
     if (first < 64) break;
     top -= 64;
   }
-  if (lane == 0)
-    __hip_atomic_store(&lb[tile], LB<W>::P | (excl + agg), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0) {
+    const W incl = LB<W>::P | (excl + agg);
+    __hip_atomic_store(&lbt[tile], incl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (glast) __hip_atomic_store(&lbg[grp], incl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   return excl;
 }
 
@@ -222,7 +249,10 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
   __shared__ int64_t s_E[kLinBags];
   __shared__ int32_t s_t[kLinBags];
   __shared__ float s_scale[kLinBags];
-  __shared__ uint32_t s_dig[kRadixMax];  // this workgroup's first-pass digit counts
+  // this workgroup's first-pass digit counts, in kLinHistCopies copies: lane
+  // l adds into copy l % kLinHistCopies, so that the lanes of a hot digit
+  // (skewed ids) do not all add to one address
+  __shared__ uint32_t s_dig[kLinHistCopies][kRadixMax];
   __shared__ int s_bad;
   const int tid = threadIdx.x;
   const int radix0 = p.hist ? (1 << p.hist_bits) : 0;
@@ -248,8 +278,9 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
       __hip_atomic_store(p.hist_ready, p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  for (int d = tid; d < radix0; d += kLinThreads) s_dig[d] = 0u;
-  // (s_dig is first written after the barrier of the first tile below)
+  for (int i = tid; i < kLinHistCopies * radix0; i += kLinThreads)
+    s_dig[i / radix0][i % radix0] = 0u;
+  __syncthreads();
 
   for (int64_t q = blockIdx.x * (int64_t)kLinThreads + tid; q < p.zero_vec4;
        q += (int64_t)gridDim.x * kLinThreads)
@@ -275,7 +306,7 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
           p.kv_out[i] = (key << p.info_bits) | (uint64_t)i;
         }
         set_status_wave(p.status, p.epoch, kStIndex, bad);
-        if (radix0) hist_add(s_dig, (uint32_t)key & dmask0, valid);
+        if (radix0 && valid) atomicAdd(&s_dig[tid % kLinHistCopies][(uint32_t)key & dmask0], 1u);
       }
     }
   } else {
@@ -363,7 +394,8 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
             if (p.coef_out) p.coef_out[i] = s_scale[lo] * w[k];
           }
           set_status_wave(p.status, p.epoch, kStIndex, bad);
-          if (radix0) hist_add(s_dig, (uint32_t)key & dmask0, valid);
+          if (radix0 && valid)
+            atomicAdd(&s_dig[tid % kLinHistCopies][(uint32_t)key & dmask0], 1u);
         }
       }
       __syncthreads();
@@ -387,7 +419,9 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
   __syncthreads();
   uint32_t* h = p.hist + (size_t)(blockIdx.x % kHistSlices) * radix0;
   for (int d = tid; d < radix0; d += kLinThreads) {
-    const uint32_t c = s_dig[d];
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < kLinHistCopies; ++i) c += s_dig[i][d];
     if (c) __hip_atomic_fetch_add(&h[d], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -757,19 +791,24 @@ __global__ __launch_bounds__(TPB) void k_sort_pass(SortParams p) {
 // ------------------------------------------------------------------ run-length encoding
 //
 // Run-length encoding of the sorted ids: position i starts a run when its id
-// differs from position i-1.  Reduce-then-scan:
-//   k_rle_count  run heads of every tile
-//   k_rle_scan   one workgroup: exclusive scan of the tile counts (each
-//                tile's first run index), the run count U and the closing
-//                run start N
-//   k_rle_write  each head writes its unique id and its start (the exclusive
-//                scan of run lengths, FBGEMM
-//                `sorted_linear_indices_cumulative_run_lengths`), and its run
-//                index at its position
-// with the first two folded into k_rle_write on fewer tiles (below).
-// Items are read coalesced (item k of thread t is position k*256 + t); a
-// position's predecessor is the previous lane, or for lane 0 the last lane of
-// the wave before it in that order (through LDS).
+// differs from position i-1.  Each tile counts its heads and needs the number
+// of heads before it (its first run index); every head then writes its unique
+// id and its start (the exclusive scan of run lengths, FBGEMM
+// `sorted_linear_indices_cumulative_run_lengths`) and its run index at its
+// position, and the last tile writes the run count U and the closing start N.
+// The first run index comes one of three ways, by tile count:
+//   <= kOnePassTiles   k_rle_write alone: tiles taken in order from an atomic
+//                      counter, two-level decoupled look-back over the tiles'
+//                      head counts (one read of the ids)
+//   <= kFuseScanTiles  k_rle_count stores every tile's count, k_rle_write
+//                      sums the counts before its tile
+//   more               k_rle_count, k_rle_scan (one workgroup scans the
+//                      counts), k_rle_write
+// Beyond about a hundred tiles the one-pass look-back waits cost more than a
+// second read of the ids (measured: 2561 tiles 56 us in one pass, 43 us with
+// the counts first; 800 tiles 19 us and 15 us).  Items are read coalesced (item k of thread t is
+// position k*256 + t); a position's predecessor is the previous lane, or for
+// lane 0 the last lane of the wave before it in that order (through LDS).
 
 // Ids of this thread's kScanItems positions and which of them start a run.
 // Returns the head bits; ids land in key[].
@@ -826,8 +865,10 @@ __global__ __launch_bounds__(kScanThreads) void k_rle_count(RleParams p) {
   }
 }
 
+// one workgroup: tile counts -> first run index of every tile, U and the
+// closing start N
 __global__ __launch_bounds__(kScanThreads) void k_rle_scan(RleParams p) {
-  __shared__ uint32_t s_tmp[4];
+  __shared__ uint32_t s_tmp[kScanThreads / 64];
   const int tid = threadIdx.x;
   uint32_t carry = 0;
   for (int64_t c0 = 0; c0 < p.tiles; c0 += (int64_t)kScanThreads * kScanItems) {
@@ -855,15 +896,6 @@ __global__ __launch_bounds__(kScanThreads) void k_rle_scan(RleParams p) {
   }
 }
 
-// k_rle_write takes its tile's first run index one of three ways: on at most
-// kOnePassTiles tiles (one pass, no other kernel) the workgroup takes the next
-// tile from an atomic counter, counts its heads and sums the counts of the
-// tiles before it by decoupled look-back (Merrill & Garland's single-pass
-// scan); on more tiles k_rle_count has counted every tile's heads, and on at
-// most kFuseScanTiles the workgroup sums the counts of the tiles before it,
-// beyond that k_rle_scan has scanned them.  The last tile closes the run
-// starts with N and stores U.  (A look-back chain over thousands of tiles
-// costs more than the count kernel saves.)
 __global__ __launch_bounds__(kScanThreads) void k_rle_write(RleParams p) {
   __shared__ uint64_t s_edge[kScanItems][kScanThreads / 64];
   __shared__ uint32_t s_off[kScanItems * (kScanThreads / 64)];
@@ -880,7 +912,6 @@ __global__ __launch_bounds__(kScanThreads) void k_rle_write(RleParams p) {
   const int n = (int)min((int64_t)kScanTile, p.N - base);
   uint64_t key[kScanItems];
   const uint32_t heads = rle_heads(p, base, n, key, s_edge);
-  uint32_t first = 0;
   if (!p.one_pass) {
     if (p.fuse_scan) {
       // each thread sums every 256th tile count, then a block sum
@@ -899,23 +930,26 @@ __global__ __launch_bounds__(kScanThreads) void k_rle_write(RleParams p) {
         s_sum[1][w] = all;
       }
       __syncthreads();
-      before = 0;
-      all = 0;
+      if (tid == 0) {
+        before = 0;
+        all = 0;
 #pragma unroll
-      for (int i = 0; i < kScanThreads / 64; ++i) {
-        before += s_sum[0][i];
-        all += s_sum[1][i];
+        for (int i = 0; i < kScanThreads / 64; ++i) {
+          before += s_sum[0][i];
+          all += s_sum[1][i];
+        }
+        s_first = before;
+        if ((int64_t)tile == p.tiles - 1) {
+          p.cum[all] = (int32_t)p.N;
+          *p.num_runs = (int32_t)all;
+        }
       }
-      first = before;
-      if ((int64_t)tile == p.tiles - 1 && tid == 0) {
-        p.cum[all] = (int32_t)p.N;
-        *p.num_runs = (int32_t)all;
-      }
-    } else {
-      first = p.tile_runs[tile];
+    } else if (tid == 0) {
+      s_first = p.tile_runs[tile];
     }
   }
-  // heads of every (item round, wave) in tile order, then their exclusive scan
+  // heads of every (item round, wave) in tile order, then their exclusive
+  // scan; in one pass also the tile's first run index by look-back
   uint64_t bal[kScanItems];
 #pragma unroll
   for (int k = 0; k < kScanItems; ++k) {
@@ -935,7 +969,8 @@ __global__ __launch_bounds__(kScanThreads) void k_rle_write(RleParams p) {
     s_off[lane] = incl - c;
     if (p.one_pass) {
       const uint32_t total = __shfl(incl, 63, 64);
-      const uint32_t f = wave_lookback<uint32_t>(p.lookback, tile, total, p.status, p.epoch);
+      const uint32_t f = wave_lookback2<uint32_t>(p.lookback, p.lookback + p.tiles, tile, total,
+                                                  p.status, p.epoch);
       if (lane == 0) {
         s_first = f;
         if ((int64_t)tile == p.tiles - 1) {
@@ -946,7 +981,7 @@ __global__ __launch_bounds__(kScanThreads) void k_rle_write(RleParams p) {
     }
   }
   __syncthreads();
-  if (p.one_pass) first = s_first;
+  const uint32_t first = s_first;
 #pragma unroll
   for (int k = 0; k < kScanItems; ++k) {
     if (!((heads >> k) & 1u)) continue;
@@ -1103,7 +1138,8 @@ __global__ __launch_bounds__(kScanThreads) void k_post(PostParams p) {
   uint64_t total;
   const uint64_t before = block_excl_scan<uint64_t>(sum, s_tmp, total);
   if (tid < 64) {
-    const uint64_t ex = wave_lookback<uint64_t>(p.lookback, tile, total, p.status, p.epoch);
+    const uint64_t ex = wave_lookback2<uint64_t>(p.lookback, p.lookback + p.tiles, tile, total,
+                                                 p.status, p.epoch);
     if (tid == 0) s_excl = ex;
   }
   // run lengths, coalesced
@@ -2829,24 +2865,12 @@ hipError_t launch_sort_pass(const SortParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_rle(const RleParams& p, hipStream_t s, StageMark mark_fn, void* ctx) {
+hipError_t launch_rle(const RleParams& p, hipStream_t s) {
   const unsigned tiles = (unsigned)p.tiles;
-  auto mark = [&](int stage, int end) {
-    if (mark_fn) mark_fn(ctx, stage, end);
-  };
-  // in one pass the count and scan stages are done inside k_rle_write: their
-  // marks then bracket no kernel, so that every stage's pair of events is
-  // still recorded
-  mark(SGB_STAGE_RLE_COUNT, 0);
   if (!p.one_pass) hipLaunchKernelGGL(k_rle_count, dim3(tiles), dim3(kScanThreads), 0, s, p);
-  mark(SGB_STAGE_RLE_COUNT, 1);
-  mark(SGB_STAGE_RLE_SCAN, 0);
   if (!p.one_pass && !p.fuse_scan)
     hipLaunchKernelGGL(k_rle_scan, dim3(1), dim3(kScanThreads), 0, s, p);
-  mark(SGB_STAGE_RLE_SCAN, 1);
-  mark(SGB_STAGE_RLE_WRITE, 0);
   hipLaunchKernelGGL(k_rle_write, dim3(tiles), dim3(kScanThreads), 0, s, p);
-  mark(SGB_STAGE_RLE_WRITE, 1);
   return hipGetLastError();
 }
 

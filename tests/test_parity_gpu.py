@@ -207,11 +207,11 @@ def test_huge_run_two_level_combine(sgb):
     check_case(sgb, inp, "rowwise_adagrad", 64, lr=0.01, eps=1e-8)
 
 
-@pytest.mark.parametrize("tokens", [300_000, 128 * 4096, 128 * 4096 + 1, 1024 * 4096,
-                                    1024 * 4096 + 1])
+@pytest.mark.parametrize("tokens", [300_000, 128 * 4096, 128 * 4096 + 1, 4096 * 4096,
+                                    4096 * 4096 + 1])
 def test_many_run_tiles(sgb, tokens):
     """Run-length tiles of 4096 sorted positions: up to 128 tiles the run
-    write alone (look-back over the tile counts), up to 1024 the count kernel
+    write alone (look-back over the tile counts), up to 4096 the count kernel
     and a run write that sums the counts itself, beyond that the scan kernel
     too; each limit and one more.  Runs are compared bit-exact, rows to the
     usual tolerance."""
