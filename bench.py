@@ -68,10 +68,14 @@ def stage_bytes(inp: synth.Inputs, spec: synth.Spec, U: int, run_D: np.ndarray,
     Ds = np.diff(inp.D_offsets).astype(np.int64)
     Es = np.diff(inp.hash_size_cumsum).astype(np.int64)
     touched_elems = int(run_D.sum())
-    # tiles of the first radix pass: 1024 x 12 items above 2^20 lookups (digits
-    # of up to 9 bits), 512 x 8 above 2^16, else 256 x 8
-    sort_tile = 1024 * 12 if (N > (1 << 20) and radix0 <= 512) else (
-        512 * 8 if N > (1 << 16) else 256 * 8)
+    # tiles of the first radix pass (digits of up to 9 bits: 512 x 12 items
+    # above 2^22 lookups, 1024 x 12 above 2^20), 512 x 8 above 2^16, else 256 x 8
+    if N > (1 << 22) and radix0 <= 512:
+        sort_tile = 512 * 12
+    elif N > (1 << 20) and radix0 <= 512:
+        sort_tile = 1024 * 12
+    else:
+        sort_tile = 512 * 8 if N > (1 << 16) else 256 * 8
     tiles = (N + sort_tile - 1) // sort_tile
     scan_tiles = (N + 4095) // 4096
 

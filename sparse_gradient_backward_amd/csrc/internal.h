@@ -80,23 +80,32 @@ constexpr int kSortLbGroup = 16;  // tiles per look-back group of a radix pass
 // each sort one tile of TPB threads x ITEMS items; the shape depends on the
 // batch and on the pass's digit width (its LDS holds the tile and one digit
 // table per wave, so 10-bit digits take the smaller tiles):
+//   huge    512 x 12 ( 6144 items), digits up to 9 bits, N > kSortHugeN
 //   large  1024 x 12 (12288 items), digits up to 9 bits, N > kSortLargeN
 //   medium  512 x 8  ( 4096 items), N > kSortMediumN
 //   small   256 x 8  ( 2048 items)
+// (Up to a few hundred large tiles are all resident at once, one per CU; on
+// more, two half-size tiles per CU overlap one's loads with the other's
+// ranking.)
+#ifndef SGB_SORT_HUGE_N
+#define SGB_SORT_HUGE_N (1 << 22)
+#endif
 #ifndef SGB_SORT_LARGE_N
 #define SGB_SORT_LARGE_N (1 << 20)
 #endif
 #ifndef SGB_SORT_MEDIUM_N
 #define SGB_SORT_MEDIUM_N (1 << 16)
 #endif
-enum SortShape { kSortSmall = 0, kSortMedium = 1, kSortLarge = 2 };
+enum SortShape { kSortSmall = 0, kSortMedium = 1, kSortLarge = 2, kSortHuge = 3 };
 __host__ __device__ inline int sort_shape_for(int64_t N, int bits) {
+  if (N > (int64_t)SGB_SORT_HUGE_N && bits <= 9) return kSortHuge;
   if (N > (int64_t)SGB_SORT_LARGE_N && bits <= 9) return kSortLarge;
   if (N > (int64_t)SGB_SORT_MEDIUM_N) return kSortMedium;
   return kSortSmall;
 }
 __host__ __device__ inline int sort_tile_items(int shape) {
-  return shape == kSortLarge ? 1024 * 12 : (shape == kSortMedium ? 512 * 8 : 256 * 8);
+  return shape == kSortHuge ? 512 * 12
+       : shape == kSortLarge ? 1024 * 12 : (shape == kSortMedium ? 512 * 8 : 256 * 8);
 }
 // fewest items of any tile shape: bounds the tiles of a batch
 constexpr int kSortTileMin = 256 * 8;

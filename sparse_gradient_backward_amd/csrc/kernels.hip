@@ -614,6 +614,10 @@ __global__ __launch_bounds__(TPB) void k_sort_pass(SortParams p) {
       if (d < radix) {
         s_local[d] = ex;
         s_gbase[d] = (int32_t)g;
+        // each wave's offset becomes its tile offset: one table read per
+        // item below (the sum stays below TILE < 2^16)
+#pragma unroll
+        for (int ww = 0; ww < W; ++ww) s_wcnt[ww][d] = (uint16_t)(s_wcnt[ww][d] + ex);
       }
       g += tot[h];
       ex += cnt[h];
@@ -625,8 +629,7 @@ __global__ __launch_bounds__(TPB) void k_sort_pass(SortParams p) {
   for (int k = 0; k < ITEMS; ++k) {
     const int e = w * 64 * ITEMS + k * 64 + lane;
     if (e < tile_n) {
-      const uint32_t d = digit_of(kv[k], p.shift, dmask);
-      rank[k] += s_local[d] + (uint32_t)s_wcnt[w][d];
+      rank[k] += (uint32_t)s_wcnt[w][dg[k]];
       s_kv[rank[k]] = kv[k];
     }
   }
@@ -2846,6 +2849,10 @@ hipError_t launch_sort_pass(const SortParams& p, hipStream_t s) {
   const int64_t tile = sort_tile_items(p.shape);
   if ((int64_t)p.tiles != (p.N + tile - 1) / tile) return hipErrorInvalidValue;
   switch (p.shape) {
+    case kSortHuge:
+      if (p.bits > 9) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((k_sort_pass<512, 12, 512>), grid, dim3(512), 0, s, p);
+      break;
     case kSortLarge:
       if (p.bits > 9) return hipErrorInvalidValue;
       hipLaunchKernelGGL((k_sort_pass<1024, 12, 512>), grid, dim3(1024), 0, s, p);

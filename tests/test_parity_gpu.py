@@ -124,6 +124,32 @@ def test_wide_and_narrow_tables_all_short(sgb):
     check_case(sgb, inp, "dense", 40, accumulate=True)
 
 
+@pytest.mark.parametrize("mode,acc", [("dense", True), ("dense", False), ("sgd", False),
+                                      ("rowwise_adagrad", False)])
+def test_medium_runs_of_wide_rows(sgb, mode, acc):
+    """Medium runs of wide rows: runs of 1 to 257 lookups (63/64/65 and
+    255/256/257 among them) in tables of 512, 2048 and 4096 columns, thr =
+    256.  The runs below 256 lookups of the two wider tables are each gathered
+    by the wave of one (run, column block) item of the wide-row reducer, those
+    of the 512-column table by the window reducer; from 256 on the chunked
+    long-run reducer serves them, and they form the long-run list."""
+    lens = np.array([1, 63, 64, 65, 200, 255, 256, 257, 2, 31])
+    B = int(lens.sum())
+    s = synth.Spec("medium", 3, (64, 64, 64), (512, 2048, 4096), B, ("fixed", 1), ("uniform",),
+                   "sum", False, "bf16", mode, accumulate=acc, seed=53)
+    inp = synth.generate(s)
+    rng = np.random.default_rng(54)
+    parts = []
+    for _ in range(3):
+        ids = rng.choice(64, size=lens.shape[0], replace=False)
+        v = np.repeat(ids, lens)
+        rng.shuffle(v)
+        parts.append(v)
+    inp.indices = np.concatenate(parts).astype(np.int64)
+    _say(f"[parity] medium runs of wide rows {mode} acc={acc} N={inp.N}")
+    check_case(sgb, inp, mode, 256, accumulate=acc, lr=0.05, eps=1e-6)
+
+
 def test_wide_rows_more_items_than_waves(sgb):
     """~25 000 runs of 2048-column rows: ~100 000 (run, column block) items,
     more than the wide-row reducer's waves (eight times the resident
@@ -233,6 +259,9 @@ SORT_SHAPES = [
     (1 << 20, 1_200_000, ("zipf", 1.1)),  # 10-bit digits keep medium tiles above 2^20 lookups
     (1 << 22, 1_200_000, ("zipf", 1.2)),  # 22 bits -> 8/7/7: large tiles, skewed ids
     ((1 << 25) - 1, 1_500_000, ("uniform",)),  # 25 bits -> 9/8/8: large tiles, 123 of them
+    ((1 << 25) - 1, 1 << 22, ("uniform",)),    # the largest batch of large tiles (342)
+    ((1 << 25) - 1, (1 << 22) + 1, ("zipf", 1.2)),  # huge tiles (683) from here
+    (1 << 20, (1 << 22) + 1, ("uniform",)),    # 10-bit digits keep medium tiles
 ]
 
 
