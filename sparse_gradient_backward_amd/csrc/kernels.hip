@@ -414,7 +414,9 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
       }
       __builtin_amdgcn_s_sleep(2);
     }
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    // pairs with the clearing workgroup's release fence: its zero stores are
+    // visible to the adds below (ordered after this by the barrier)
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
   uint32_t* h = p.hist + (size_t)(blockIdx.x % kHistSlices) * radix0;
