@@ -63,7 +63,7 @@ constexpr int kMaxD = 8192;
 #define SGB_FILL_THREADS 256
 #endif
 #ifndef SGB_LIN_WG_PER_CU
-#define SGB_LIN_WG_PER_CU 16
+#define SGB_LIN_WG_PER_CU 4
 #endif
 #ifndef SGB_LOOKBACK
 #define SGB_LOOKBACK 16
@@ -140,6 +140,7 @@ constexpr int kLinLookups = 4 * kLinThreads;
 constexpr int kLinPer = 8;            // lookups per thread whose loads are issued together
 constexpr int kLinHistCopies = 4;     // copies of the first-pass digit histogram in LDS
 static_assert(kLinBags < kLinThreads, "one thread per bag offset of a tile");
+static_assert((kLinBags & (kLinBags - 1)) == 0, "the bag search halves a power of two");
 
 // short runs: sorted positions of one window of the short-run reducer, and
 // log2 of the waves sharing a window (each serves the runs starting in its

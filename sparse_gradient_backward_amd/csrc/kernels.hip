@@ -312,21 +312,32 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
   } else {
     const int64_t nbags = (int64_t)p.B * p.T;
     const int64_t tiles = (nbags + kLinBags - 1) / kLinBags;
+    // offsets of a tile's bags and the row range of each bag's table (the
+    // table of bag t*B+b is known without offsets), loaded together; the next
+    // tile's are loaded while this tile's lookups are in flight
+    int64_t nov = 0, nh0 = 0, nh1 = 0;
+    auto load_tile_meta = [&](int64_t tl) {
+      const int64_t b = tl * kLinBags;
+      const int n = (int)min((int64_t)kLinBags, nbags - b);
+      if (tid <= n) nov = p.offsets[b + tid];
+      if (tid < n) {
+        int t = (int)((b + tid) / p.B);
+        t = t < p.T ? t : p.T - 1;
+        nh0 = p.hsc[t];
+        nh1 = p.hsc[t + 1];
+      }
+    };
+    if ((int64_t)blockIdx.x < tiles) load_tile_meta(blockIdx.x);
     for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
       const int64_t b0 = tile * kLinBags;
       const int nb = (int)min((int64_t)kLinBags, nbags - b0);
       if (tid == 0) s_bad = 0;
-      // offsets of the tile's bags and the row range of each bag's table,
-      // loaded together (the table of bag t*B+b is known without offsets)
-      int64_t ov = 0, h0 = 0, h1 = 0;
-      if (tid <= nb) ov = p.offsets[b0 + tid];
+      const int64_t ov = nov, h0 = nh0, h1 = nh1;
       if (tid < nb) {
-        int t = (int)((b0 + tid) / p.B);
-        t = t < p.T ? t : p.T - 1;
-        s_t[tid] = t;
-        h0 = p.hsc[t];
-        h1 = p.hsc[t + 1];
+        const int t = (int)((b0 + tid) / p.B);
+        s_t[tid] = t < p.T ? t : p.T - 1;
       }
+      if (tile + gridDim.x < tiles) load_tile_meta(tile + gridDim.x);
       __syncthreads();
       if (tid <= nb) {
         const bool bad = ov < 0 || ov > p.N || (b0 + tid == 0 && ov != 0) ||
@@ -372,14 +383,13 @@ __global__ __launch_bounds__(kLinThreads) void k_linearize(LinParams p) {
           uint64_t key = 0;
           bool bad = false;
           if (valid) {
-            int lo = 0, hi = nb;  // s_off[lo] <= i < s_off[hi]
-            while (hi - lo > 1) {
-              const int mid = (lo + hi) >> 1;
-              if (s_off[mid] <= i)
-                lo = mid;
-              else
-                hi = mid;
-            }
+            // the bag of lookup i: the last lo < nb with s_off[lo] <= i (empty
+            // bags are passed over).  A fixed number of steps, so that the
+            // searches of the kLinPer lookups overlap their LDS reads.
+            int lo = 0;
+#pragma unroll
+            for (int step = kLinBags / 2; step >= 1; step >>= 1)
+              if (lo + step < nb && s_off[lo + step] <= i) lo += step;
             const int t = s_t[lo];
             const int64_t E = s_E[lo];
             int64_t x = idx[k];
