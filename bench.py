@@ -49,6 +49,16 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def num_cus() -> int:
+    """Compute units of the GPU (256 on MI355X when none is visible)."""
+    try:
+        if torch.cuda.is_available():
+            return int(torch.cuda.get_device_properties(0).multi_processor_count)
+    except Exception:
+        pass
+    return 256
+
+
 def stage_bytes(inp: synth.Inputs, spec: synth.Spec, U: int, run_D: np.ndarray,
                 run_len: np.ndarray, thr: int, npasses: int, radix0: int,
                 long_rows_D: int | None = None):
@@ -69,11 +79,15 @@ def stage_bytes(inp: synth.Inputs, spec: synth.Spec, U: int, run_D: np.ndarray,
     Es = np.diff(inp.hash_size_cumsum).astype(np.int64)
     touched_elems = int(run_D.sum())
     # tiles of the first radix pass (digits of up to 9 bits: 512 x 12 items
-    # above 2^22 lookups, 1024 x 12 above 2^20), 512 x 8 above 2^16, else 256 x 8
+    # above 2^22 lookups; above 2^20, 1024 x I with the fewest I in 8..12 that
+    # keeps the tiles within the CUs), 512 x 8 above 2^16, else 256 x 8
     if N > (1 << 22) and radix0 <= 512:
         sort_tile = 512 * 12
     elif N > (1 << 20) and radix0 <= 512:
-        sort_tile = 1024 * 12
+        items = 8
+        while items < 12 and (N + 1024 * items - 1) // (1024 * items) > num_cus():
+            items += 1
+        sort_tile = 1024 * items
     else:
         sort_tile = 512 * 8 if N > (1 << 16) else 256 * 8
     tiles = (N + sort_tile - 1) // sort_tile

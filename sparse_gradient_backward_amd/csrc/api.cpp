@@ -133,7 +133,7 @@ sgb_status make_layout(const sgb_plan_s* p, int64_t N, int32_t B, bool has_offse
     L->pass_bits[i] = p->key_bits / L->npasses + (i < p->key_bits % L->npasses ? 1 : 0);
     L->pass_key_shift[i] = at;
     at += L->pass_bits[i];
-    L->pass_shape[i] = sort_shape_for(N, L->pass_bits[i]);
+    L->pass_shape[i] = sort_shape_for(N, L->pass_bits[i], p->num_cus);
     const int64_t tile = sort_tile_items(L->pass_shape[i]);
     L->pass_tiles[i] = (N + tile - 1) / tile;
   }

@@ -80,13 +80,16 @@ constexpr int kSortLbGroup = 16;  // tiles per look-back group of a radix pass
 // each sort one tile of TPB threads x ITEMS items; the shape depends on the
 // batch and on the pass's digit width (its LDS holds the tile and one digit
 // table per wave, so 10-bit digits take the smaller tiles):
-//   huge    512 x 12 ( 6144 items), digits up to 9 bits, N > kSortHugeN
-//   large  1024 x 12 (12288 items), digits up to 9 bits, N > kSortLargeN
-//   medium  512 x 8  ( 4096 items), N > kSortMediumN
-//   small   256 x 8  ( 2048 items)
-// (Up to a few hundred large tiles are all resident at once, one per CU; on
-// more, two half-size tiles per CU overlap one's loads with the other's
-// ranking.)
+//   huge     512 x 12 ( 6144 items), digits up to 9 bits, N > kSortHugeN
+//   large   1024 x I  (I = 8..12), digits up to 9 bits, N > kSortLargeN: the
+//           fewest items per thread that keep the tiles within the CUs, so
+//           that every tile is resident at once and the pass is one round
+//           (more than 12 would exceed the LDS)
+//   medium   512 x 8  ( 4096 items), N > kSortMediumN
+//   small    256 x 8  ( 2048 items)
+// (A large tile fills one CU.  Beyond 12 x 1024 items per CU the pass takes
+// several rounds, and two half-size tiles per CU overlap one's loads with
+// the other's ranking.)
 #ifndef SGB_SORT_HUGE_N
 #define SGB_SORT_HUGE_N (1 << 22)
 #endif
@@ -96,16 +99,27 @@ constexpr int kSortLbGroup = 16;  // tiles per look-back group of a radix pass
 #ifndef SGB_SORT_MEDIUM_N
 #define SGB_SORT_MEDIUM_N (1 << 16)
 #endif
-enum SortShape { kSortSmall = 0, kSortMedium = 1, kSortLarge = 2, kSortHuge = 3 };
-__host__ __device__ inline int sort_shape_for(int64_t N, int bits) {
+// shape codes: kSortLarge8 + (I - 8) is the large shape with I items
+enum SortShape {
+  kSortSmall = 0,
+  kSortMedium = 1,
+  kSortHuge = 2,
+  kSortLarge8 = 3,
+  kSortLarge12 = kSortLarge8 + 4
+};
+__host__ __device__ inline int sort_shape_for(int64_t N, int bits, int cus) {
   if (N > (int64_t)SGB_SORT_HUGE_N && bits <= 9) return kSortHuge;
-  if (N > (int64_t)SGB_SORT_LARGE_N && bits <= 9) return kSortLarge;
+  if (N > (int64_t)SGB_SORT_LARGE_N && bits <= 9) {
+    int items = 8;
+    while (items < 12 && (N + 1024 * items - 1) / (1024 * items) > (int64_t)cus) ++items;
+    return kSortLarge8 + (items - 8);
+  }
   if (N > (int64_t)SGB_SORT_MEDIUM_N) return kSortMedium;
   return kSortSmall;
 }
 __host__ __device__ inline int sort_tile_items(int shape) {
-  return shape == kSortHuge ? 512 * 12
-       : shape == kSortLarge ? 1024 * 12 : (shape == kSortMedium ? 512 * 8 : 256 * 8);
+  if (shape >= kSortLarge8 && shape <= kSortLarge12) return 1024 * (8 + shape - kSortLarge8);
+  return shape == kSortHuge ? 512 * 12 : (shape == kSortMedium ? 512 * 8 : 256 * 8);
 }
 // fewest items of any tile shape: bounds the tiles of a batch
 constexpr int kSortTileMin = 256 * 8;
@@ -293,7 +307,7 @@ struct SortParams {
   float* coef_out;
   int64_t N;
   int32_t tiles;            // tiles of sort_tile_items(shape) lookups
-  int32_t shape;            // sort_shape_for(N, bits)
+  int32_t shape;            // sort_shape_for(N, bits, CUs)
   int32_t shift;
   int32_t bits;
   const uint32_t* hist;     // [kHistSlices][1 << bits]: this pass's digit totals

@@ -2865,9 +2865,19 @@ hipError_t launch_sort_pass(const SortParams& p, hipStream_t s) {
       if (p.bits > 9) return hipErrorInvalidValue;
       hipLaunchKernelGGL((k_sort_pass<512, 12, 512>), grid, dim3(512), 0, s, p);
       break;
-    case kSortLarge:
+    case kSortLarge8:
+    case kSortLarge8 + 1:
+    case kSortLarge8 + 2:
+    case kSortLarge8 + 3:
+    case kSortLarge12:
       if (p.bits > 9) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((k_sort_pass<1024, 12, 512>), grid, dim3(1024), 0, s, p);
+      switch (p.shape - kSortLarge8) {
+        case 0: hipLaunchKernelGGL((k_sort_pass<1024, 8, 512>), grid, dim3(1024), 0, s, p); break;
+        case 1: hipLaunchKernelGGL((k_sort_pass<1024, 9, 512>), grid, dim3(1024), 0, s, p); break;
+        case 2: hipLaunchKernelGGL((k_sort_pass<1024, 10, 512>), grid, dim3(1024), 0, s, p); break;
+        case 3: hipLaunchKernelGGL((k_sort_pass<1024, 11, 512>), grid, dim3(1024), 0, s, p); break;
+        default: hipLaunchKernelGGL((k_sort_pass<1024, 12, 512>), grid, dim3(1024), 0, s, p);
+      }
       break;
     case kSortMedium:
       if (p.bits <= 9)

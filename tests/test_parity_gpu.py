@@ -257,9 +257,15 @@ SORT_SHAPES = [
     (60000, 65537, ("zipf", 1.05)),     # medium tiles from here
     (1 << 20, 300_000, ("uniform",)),   # 20 bits -> 10/10: medium tiles with 1024 digits
     (1 << 20, 1_200_000, ("zipf", 1.1)),  # 10-bit digits keep medium tiles above 2^20 lookups
-    (1 << 22, 1_200_000, ("zipf", 1.2)),  # 22 bits -> 8/7/7: large tiles, skewed ids
-    ((1 << 25) - 1, 1_500_000, ("uniform",)),  # 25 bits -> 9/8/8: large tiles, 123 of them
-    ((1 << 25) - 1, 1 << 22, ("uniform",)),    # the largest batch of large tiles (342)
+    # large tiles of 1024 x I items, I the fewest of 8..12 that keeps the
+    # tiles within the CUs (on a 256-CU GPU: I = 8 up to 2^21 lookups, 9 up
+    # to 2.36 M, 10 up to 2.62 M, 11 up to 2.88 M, then 12)
+    (1 << 22, 1_200_000, ("zipf", 1.2)),  # 22 bits -> 8/7/7: 1024 x 8, skewed ids
+    ((1 << 25) - 1, 1_500_000, ("uniform",)),  # 25 bits -> 9/8/8: 1024 x 8
+    ((1 << 25) - 1, (1 << 21) + 1, ("zipf", 1.2)),  # 1024 x 9
+    ((1 << 25) - 1, 2_500_000, ("uniform",)),  # 1024 x 10
+    ((1 << 25) - 1, 2_800_000, ("zipf", 1.1)),  # 1024 x 11
+    ((1 << 25) - 1, 1 << 22, ("uniform",)),    # 1024 x 12, the largest batch of large tiles
     ((1 << 25) - 1, (1 << 22) + 1, ("zipf", 1.2)),  # huge tiles (683) from here
     (1 << 20, (1 << 22) + 1, ("uniform",)),    # 10-bit digits keep medium tiles
 ]
