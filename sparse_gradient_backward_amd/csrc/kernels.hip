@@ -1394,6 +1394,53 @@ __device__ __forceinline__ RowDst row_dest(const RedParams& p, int t, int D, int
   return d;
 }
 
+// Table metadata a reducer wave reads for every run it serves (row width,
+// first row id, first element of the table), through generic pointers:
+// to a copy in the workgroup's LDS, staged at the start for up to kMetaT
+// tables, or to the plan's global arrays beyond that.  A wave whose items are
+// one or two runs would otherwise wait two more memory round trips per item.
+struct MetaView {
+  const int32_t* doff;
+  const int64_t* hsc;
+  const int64_t* woff;  // woff8 for INT8 rows
+};
+
+template <int WK>
+__device__ __forceinline__ RowDst row_dest_m(const RedParams& p, const MetaView& mv, int t, int D,
+                                             int64_t lin) {
+  const int64_t h0 = mv.hsc[t], E = mv.hsc[t + 1] - h0;
+  int64_t row = lin - h0;
+  row = row < 0 ? 0 : (row < E ? row : E - 1);
+  RowDst d;
+  if constexpr (WK == kWINT8)
+    d.out = p.out_q + mv.woff[t] + row * (int64_t)(D + 8);
+  else if constexpr (WK == kWBF16)
+    d.out = p.out_h + mv.woff[t] + row * (int64_t)D;
+  else
+    d.out = p.out + mv.woff[t] + row * (int64_t)D;
+  d.mom = p.mom ? p.mom + h0 + row : nullptr;
+  d.lin = h0 + row;
+  d.D = D;
+  return d;
+}
+
+// Copies the plan's table metadata into `s` (all threads of the workgroup
+// take part; a barrier ends it) and returns the view the reducer reads.
+template <int WK, class P>
+__device__ __forceinline__ MetaView stage_meta(const P& p, MetaLds& s) {
+  const int64_t* wo = WK == kWINT8 ? p.woff8 : p.woff;
+  const bool staged = p.T <= kMetaT;
+  if (staged) {
+    for (int j = threadIdx.x; j <= p.T; j += blockDim.x) {
+      s.doff[j] = p.doff[j];
+      s.hsc[j] = p.hsc[j];
+      s.woff[j] = wo[j];
+    }
+  }
+  __syncthreads();
+  return staged ? MetaView{s.doff, s.hsc, s.woff} : MetaView{p.doff, p.hsc, wo};
+}
+
 // ---- bf16 weight rows
 //
 // SGD and row-wise Adagrad may keep their rows in bf16.  A row is widened
@@ -2515,15 +2562,15 @@ __device__ __forceinline__ void wide_run_multi(const RedParams& p, const WideRun
 }
 
 template <int CPL, int UNR, bool BF16, int WK>
-__device__ __forceinline__ void wide_item(const RedParams& p, const WideRun& m, const WideLane& d0,
-                                          int cb) {
+__device__ __forceinline__ void wide_item(const RedParams& p, const MetaView& mv, const WideRun& m,
+                                          const WideLane& d0, int cb) {
   constexpr int NP = CPL / 4;
   const int len = m.e - m.s;
   if (len <= 0 || len >= p.thr) return;
   const uint64_t imask = info_mask(p);
   const uint64_t kv0 = rl64(d0.kv, 0);
   const int t = uni32(table_of(p, (uint32_t)(kv0 & imask)));
-  const int D = uni32(p.doff[t + 1] - p.doff[t]);
+  const int D = uni32(mv.doff[t + 1] - mv.doff[t]);
   // whole rows wider than one item are served by k_reduce_wide_multi
   if ((p.mode == kModeAdagrad || WK == kWINT8) && D > 64 * CPL) return;
   if (D <= 512 || cb * 64 * CPL >= D) return;
@@ -2532,7 +2579,7 @@ __device__ __forceinline__ void wide_item(const RedParams& p, const WideRun& m, 
 #pragma unroll
   for (int i = 0; i < NP; ++i)
     if (col + 256 * i < D) vmask |= 1 << i;
-  const RowDst dst = row_dest<WK>(p, t, D, (int64_t)(kv0 >> p.info_bits));
+  const RowDst dst = row_dest_m<WK>(p, mv, t, D, (int64_t)(kv0 >> p.info_bits));
   const bool needs_old = p.mode != kModeDense || p.accumulate;
   float4 old[NP];
   d4 acc[NP];
@@ -2543,7 +2590,7 @@ __device__ __forceinline__ void wide_item(const RedParams& p, const WideRun& m, 
     acc[i] = d4_zero();
   }
   const float m0 = p.mode == kModeAdagrad ? *dst.mom : 0.f;
-  const int64_t gcol = (p.nobag ? 0 : p.doff[t]) + col;
+  const int64_t gcol = (p.nobag ? 0 : mv.doff[t]) + col;
   for (int j0 = 0; j0 < len; j0 += 64) {
     const WideLane dl = j0 == 0 ? d0 : wide_lane(p, m, j0);
     const int rowi = grad_row_of(p, (uint32_t)(dl.kv & imask), t);
@@ -2638,18 +2685,21 @@ __device__ __forceinline__ void wide_item(const RedParams& p, const WideRun& m, 
 template <int CPL, int UNR, bool BF16, int WK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, SGB_WIDE_WAVES)))
 void k_reduce_wide(RedParams p) {
+  __shared__ MetaLds s_meta;
   const int64_t nw = (int64_t)gridDim.x * 4;
   int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int ncb = p.wide_ncb;
   const int64_t items = (int64_t)(*p.num_runs) * ncb;
-  if (item >= items) return;
+  // the first item's run starts are loaded with the metadata
   WideRun m0 = wide_run(p, item, items, ncb);
+  const MetaView mv = stage_meta<WK>(p, s_meta);
+  if (item >= items) return;
   WideLane d0 = wide_lane(p, m0, 0);
   WideRun m1 = wide_run(p, item + nw, items, ncb);
   for (; item < items; item += nw) {
     const WideRun m2 = wide_run(p, item + 2 * nw, items, ncb);
     const WideLane d1 = wide_lane(p, m1, 0);
-    wide_item<CPL, UNR, BF16, WK>(p, m0, d0, (int)(item % ncb));
+    wide_item<CPL, UNR, BF16, WK>(p, mv, m0, d0, (int)(item % ncb));
     m0 = m1;
     d0 = d1;
     m1 = m2;
