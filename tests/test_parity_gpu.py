@@ -150,6 +150,21 @@ def test_medium_runs_of_wide_rows(sgb, mode, acc):
     check_case(sgb, inp, mode, 256, accumulate=acc, lr=0.05, eps=1e-6)
 
 
+@pytest.mark.parametrize("T", [512, 600])
+@pytest.mark.parametrize("mode", ["dense", "sgd", "rowwise_adagrad"])
+def test_many_tables(sgb, T, mode):
+    """Table metadata is staged in LDS for up to 512 tables (run
+    post-processing, wide-row reducer) and read from memory beyond that: 512
+    and 600 tables of 8, 64, 520 and 1028 columns, Zipf ids so that some runs
+    are long (thr = 4)."""
+    dims = tuple((8, 64, 520, 1028)[t % 4] for t in range(T))
+    s = synth.Spec("manytables", T, (40,) * T, dims, 24, ("uniform", 0, 5), ("zipf", 1.3),
+                   "sum", False, "f32", mode, seed=83)
+    inp = synth.generate(s)
+    _say(f"[parity] {T} tables {mode} N={inp.N}")
+    check_case(sgb, inp, mode, 4, lr=0.02, eps=1e-6)
+
+
 def test_wide_rows_more_items_than_waves(sgb):
     """~25 000 runs of 2048-column rows: ~100 000 (run, column block) items,
     more than the wide-row reducer's waves (eight times the resident
