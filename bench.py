@@ -413,6 +413,8 @@ def main():
     rows_D = int(np.diff(inp.D_offsets).astype(np.int64)[
         np.searchsorted(inp.hash_size_cumsum, uniq_v, side="right") - 1].sum())
     fwd = forward_measure(plan, inp, spec, indices, offsets, psw, out, ws, args.steps, rows_D)
+    piped = pipelined_measure(plan, inp, spec, grad_output, indices, offsets, B, psw, out, mom,
+                              args.steps, ms_per_step)
     bf16w = bf16_weights_measure(plan, spec, grad_output, indices, offsets, B, psw, out, mom, ws,
                                  args.steps, ms_per_step)
     f16w = bf16_weights_measure(plan, spec, grad_output, indices, offsets, B, psw, out, mom, ws,
@@ -504,6 +506,7 @@ def main():
                      "traffic": measured_traffic(spec.name, kernel_names[dom]), "bytes_per_launch": int(per_launch_bytes),
                      "launch_ms": per_launch_ms},
         "forward": fwd,
+        "pipelined": piped,
         "bf16_weights": bf16w,
         "f16_weights": f16w,
         "int8_weights": int8w,
@@ -513,6 +516,52 @@ def main():
         "kernel_src": kernel_digest(),
     }
     print(json.dumps(res), flush=True)
+
+
+def pipelined_measure(plan, inp, spec, grad_output, indices, offsets, B, psw, out, mom, steps,
+                      ms_path) -> dict:
+    """The same steps through sgb_prepare / sgb_apply, pipelined: the lookups
+    of step i+1 are prepared (linearise, sort, runs) into a second workspace
+    on one stream while step i is applied (reductions, row updates) on
+    another; the applies stay ordered, as updates of one model must. All K
+    prepares and K applies are in the timed region (wall clock between two
+    synchronisations)."""
+    wss = [plan.workspace(inp.N, B), plan.workspace(inp.N, B)]
+    # the applies on the current stream, the prepares on one more: with the
+    # plan's two side streams that is four, one hardware queue each (more
+    # streams than queues would share queues and serialise)
+    sf, sm = torch.cuda.Stream(), torch.cuda.current_stream()
+    kw = dict(grad=out) if spec.mode == "dense" else dict(weights=out, momentum=mom)
+    prepared = [torch.cuda.Event(), torch.cuda.Event()]
+    applied = [torch.cuda.Event(), torch.cuda.Event()]
+
+    def run(k):
+        sf.wait_stream(sm)
+        for e in applied:
+            e.record(sm)
+        plan.prepare(indices, offsets, B, psw, wss[0], stream=sf)
+        prepared[0].record(sf)
+        for i in range(k):
+            if i + 1 < k:  # the next step's lookups, once its workspace is free
+                sf.wait_event(applied[(i + 1) % 2])
+                plan.prepare(indices, offsets, B, psw, wss[(i + 1) % 2], stream=sf)
+                prepared[(i + 1) % 2].record(sf)
+            sm.wait_event(prepared[i % 2])
+            plan.apply(grad_output, indices, offsets, B, psw, spec.mode, accumulate=spec.accumulate,
+                       lr=spec.lr, eps=spec.eps, workspace=wss[i % 2], stream=sm, **kw)
+            applied[i % 2].record(sm)
+
+    run(3)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(steps)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    status = [plan.device_status(w) for w in wss]
+    del wss
+    return {"ms_per_step": ms, "value": inp.N / (ms * 1e-3), "steps": steps,
+            "vs_plain_step": ms / ms_path,
+            "device_status": "SGB_OK" if all(x == "SGB_OK" for x in status) else status}
 
 
 def forward_measure(plan, inp, spec, indices, offsets, psw, table, ws, steps,

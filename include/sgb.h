@@ -64,7 +64,9 @@ typedef enum {
   SGB_ERR_INDEX_OUT_OF_RANGE = 4, /* device-detected: index outside [0, E_t)   */
   SGB_ERR_BAD_OFFSETS = 5,        /* device-detected: offsets malformed        */
   SGB_ERR_HIP = 6,                /* a HIP runtime call failed                 */
-  SGB_ERR_INTERNAL = 7            /* device-detected: a bounded wait expired   */
+  SGB_ERR_INTERNAL = 7            /* device-detected: a bounded wait expired,
+                                     or sgb_apply() on a workspace prepared for
+                                     other lookups (its N or B differ)        */
 } sgb_status;
 
 /* Pooling of the forward pass, FBGEMM page host entry `pooling_mode` and the
@@ -214,6 +216,36 @@ typedef struct {
  */
 sgb_status sgb_backward(sgb_plan plan, const sgb_batch* batch, const sgb_update* update,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sgb_prepare / sgb_apply -- sgb_backward() in two parts, so that the part
+ * that reads only the lookups can run ahead (FBGEMM host entry: the sort and
+ * run-length steps depend on indices and offsets alone, the reduction on
+ * grad_output and the rows).
+ *  sgb_prepare enqueues on `stream` the linearisation, radix sort, run-length
+ *  encoding and long-run list of `batch` into `workspace` (it reads
+ *  indices, offsets, per_sample_weights and num_indices/B; grad_output may
+ *  be NULL).  sgb_apply enqueues the rest -- the zero fill of a fresh dense
+ *  gradient, the reductions and the row updates -- reading the run
+ *  structure from `workspace`.
+ *  Contract: an sgb_apply() call must see, in stream order, a completed
+ *  sgb_prepare() of the same plan with the same lookups (indices, offsets,
+ *  per_sample_weights, num_indices, B) into the same workspace, and no later
+ *  sgb_prepare() or sgb_backward() into that workspace may start before the
+ *  sgb_apply() has finished; the host cannot check this (the run structure
+ *  lives on the device).  Results, errors and determinism are those of
+ *  sgb_backward(): sgb_prepare() followed by sgb_apply() on one stream is the
+ *  same computation.  With two workspaces a caller can prepare batch i+1 on
+ *  one stream while batch i is applied on another; applies that update the
+ *  same rows must still be ordered.  sgb_apply() uses the plan's side streams
+ *  as sgb_backward() does (one apply of a plan at a time).  Arguments and
+ *  host-detected errors as for sgb_backward(); sgb_prepare() checks no
+ *  update, sgb_apply() repeats the batch checks.
+ */
+sgb_status sgb_prepare(sgb_plan plan, const sgb_batch* batch, void* workspace,
+                       size_t workspace_bytes, void* stream);
+sgb_status sgb_apply(sgb_plan plan, const sgb_batch* batch, const sgb_update* update,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * sgb_backward_noalloc -- sgb_backward() for callers that cannot allocate

@@ -90,13 +90,17 @@ _lib.sgb_backward.argtypes = [_vp, ctypes.POINTER(_Batch), ctypes.POINTER(_Updat
 _lib.sgb_backward_timed.argtypes = [_vp, ctypes.POINTER(_Batch), ctypes.POINTER(_Update), _vp,
                                     ctypes.c_size_t, _vp, ctypes.POINTER(_vp)]
 _lib.sgb_backward_noalloc.argtypes = [_vp, ctypes.POINTER(_Batch), ctypes.POINTER(_Update), _vp]
+_lib.sgb_prepare.argtypes = [_vp, ctypes.POINTER(_Batch), _vp, ctypes.c_size_t, _vp]
+_lib.sgb_apply.argtypes = [_vp, ctypes.POINTER(_Batch), ctypes.POINTER(_Update), _vp,
+                           ctypes.c_size_t, _vp]
 _lib.sgb_device_status.argtypes = [_vp, _vp, _vp, ctypes.POINTER(_i32)]
 _lib.sgb_forward.argtypes = [_vp, ctypes.POINTER(_Lookups), _vp, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.sgb_runs_view_get.argtypes = [_vp, _vp, _i64, _i32, ctypes.POINTER(_RunsView)]
 _lib.sgb_status_string.argtypes = [_i32]
 _lib.sgb_status_string.restype = ctypes.c_char_p
 for _f in ("sgb_plan_create", "sgb_workspace_bytes", "sgb_backward", "sgb_backward_timed",
-           "sgb_backward_noalloc", "sgb_device_status", "sgb_runs_view_get", "sgb_forward"):
+           "sgb_backward_noalloc", "sgb_prepare", "sgb_apply", "sgb_device_status",
+           "sgb_runs_view_get", "sgb_forward"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -213,6 +217,37 @@ def sgb_backward_noalloc(plan: int, grad_output, indices, offsets, B: int, per_s
                                      _stream(stream)), "sgb_backward_noalloc")
 
 
+def sgb_prepare(plan: int, indices, offsets, B: int, per_sample_weights, workspace,
+                stream=None, grad_output=None) -> None:
+    """Enqueue the part of the backward that reads only the lookups
+    (linearisation, sort, run-length encoding, long-run list) into
+    `workspace`; sgb_apply with the same lookups and workspace finishes it."""
+    import torch
+    go = grad_output if grad_output is not None else torch.empty(0, dtype=torch.float32)
+    batch, _ = _marshal(go, indices, offsets, B, per_sample_weights, "dense", None, None, None,
+                        False, 0.0, 0.0, False, 0, 0, "sgb_prepare")
+    if grad_output is None:
+        batch.grad_output = None
+    ws_bytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
+    _check(_lib.sgb_prepare(plan, ctypes.byref(batch), _ptr(workspace), ws_bytes,
+                            _stream(stream)), "sgb_prepare")
+
+
+def sgb_apply(plan: int, grad_output, indices, offsets, B: int, per_sample_weights, mode: str,
+              weights=None, momentum=None, grad=None, accumulate: bool = False, lr: float = 0.0,
+              eps: float = 0.0, workspace=None, stream=None, stochastic_rounding: bool = False,
+              sr_seed: int = 0, sr_offset: int = 0) -> None:
+    """Enqueue the reductions and row updates of a batch whose lookups
+    sgb_prepare has already processed into `workspace` (same arguments as
+    sgb_backward)."""
+    batch, upd = _marshal(grad_output, indices, offsets, B, per_sample_weights, mode, weights,
+                          momentum, grad, accumulate, lr, eps, stochastic_rounding, sr_seed,
+                          sr_offset, "sgb_apply")
+    ws_bytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
+    _check(_lib.sgb_apply(plan, ctypes.byref(batch), ctypes.byref(upd), _ptr(workspace),
+                          ws_bytes, _stream(stream)), "sgb_apply")
+
+
 def _marshal(grad_output, indices, offsets, B, per_sample_weights, mode, weights, momentum, grad,
              accumulate, lr, eps, stochastic_rounding, sr_seed, sr_offset, where):
     import torch
@@ -311,6 +346,12 @@ class Plan:
 
     def backward_noalloc(self, *args, **kw):
         return sgb_backward_noalloc(self.handle, *args, **kw)
+
+    def prepare(self, *args, **kw):
+        return sgb_prepare(self.handle, *args, **kw)
+
+    def apply(self, *args, **kw):
+        return sgb_apply(self.handle, *args, **kw)
 
     def forward(self, *args, **kw):
         return sgb_forward(self.handle, *args, **kw)

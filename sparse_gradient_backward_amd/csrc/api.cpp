@@ -215,6 +215,11 @@ T* at(void* ws, size_t off) {
 
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
+// which part of the path an enqueue call runs (see enqueue)
+enum Part { kPartAll, kPartFront, kPartReduce };
+sgb_status enqueue(sgb_plan p, const sgb_batch* b, const sgb_update* u, void* ws,
+                   size_t ws_bytes, void* stream_, void* const* events, Part part);
+
 }  // namespace
 
 extern "C" {
@@ -356,7 +361,16 @@ sgb_status sgb_workspace_bytes(sgb_plan p, int64_t N, int32_t B, size_t* bytes) 
 
 sgb_status sgb_backward(sgb_plan p, const sgb_batch* b, const sgb_update* u, void* ws,
                         size_t ws_bytes, void* stream_) {
-  return sgb_backward_timed(p, b, u, ws, ws_bytes, stream_, nullptr);
+  return enqueue(p, b, u, ws, ws_bytes, stream_, nullptr, kPartAll);
+}
+
+sgb_status sgb_prepare(sgb_plan p, const sgb_batch* b, void* ws, size_t ws_bytes, void* stream_) {
+  return enqueue(p, b, nullptr, ws, ws_bytes, stream_, nullptr, kPartFront);
+}
+
+sgb_status sgb_apply(sgb_plan p, const sgb_batch* b, const sgb_update* u, void* ws,
+                     size_t ws_bytes, void* stream_) {
+  return enqueue(p, b, u, ws, ws_bytes, stream_, nullptr, kPartReduce);
 }
 
 sgb_status sgb_backward_noalloc(sgb_plan p, const sgb_batch* b, const sgb_update* u,
@@ -371,12 +385,29 @@ sgb_status sgb_backward_noalloc(sgb_plan p, const sgb_batch* b, const sgb_update
     if (st != SGB_OK) return st;
     if (L.total > kScratchBytes) return SGB_ERR_WORKSPACE_TOO_SMALL;
   }
-  return sgb_backward_timed(p, b, u, p->scratch, kScratchBytes, stream_, nullptr);
+  return enqueue(p, b, u, p->scratch, kScratchBytes, stream_, nullptr, kPartAll);
 }
 
 sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* u, void* ws,
                               size_t ws_bytes, void* stream_, void* const* events) {
-  if (!p || !b || !u) return SGB_ERR_INVALID_ARGUMENT;
+  return enqueue(p, b, u, ws, ws_bytes, stream_, events, kPartAll);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The whole path (kPartAll), or the part of it that reads only the lookups
+// (kPartFront: linearise, sort, run-length encoding, run post-processing),
+// or the rest (kPartReduce: zero fill, reducers, row updates), which needs
+// the run structure a kPartFront call with the same lookups left in `ws`.
+sgb_status enqueue(sgb_plan p, const sgb_batch* b, const sgb_update* u, void* ws,
+                   size_t ws_bytes, void* stream_, void* const* events, Part part) {
+  const bool do_front = part != kPartReduce, do_reduce = part != kPartFront;
+  if (!p || !b || (do_reduce && !u)) return SGB_ERR_INVALID_ARGUMENT;
+  // the front never reads the update; a neutral one keeps the shared checks simple
+  const sgb_update front_only{};
+  if (!do_reduce) u = &front_only;
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
   const int64_t N = b->num_indices;
   const bool nobag = p->pooling == SGB_POOL_NONE;
@@ -385,23 +416,25 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   if (nobag && b->per_sample_weights) return SGB_ERR_UNSUPPORTED;
   if (!b->offsets && !(nobag && p->T == 1)) return SGB_ERR_INVALID_ARGUMENT;
   if (b->offsets && b->B <= 0) return SGB_ERR_INVALID_ARGUMENT;
-  if (u->mode != SGB_DENSE_GRAD && u->mode != SGB_SGD && u->mode != SGB_ROWWISE_ADAGRAD)
-    return SGB_ERR_INVALID_ARGUMENT;
-  if (u->mode == SGB_DENSE_GRAD && !u->grad) return SGB_ERR_INVALID_ARGUMENT;
-  if (u->mode == SGB_SGD && !u->weights) return SGB_ERR_INVALID_ARGUMENT;
-  if (u->mode == SGB_ROWWISE_ADAGRAD && (!u->weights || !u->momentum))
-    return SGB_ERR_INVALID_ARGUMENT;
-  if (u->weights_dtype != SGB_F32 && u->weights_dtype != SGB_BF16 && u->weights_dtype != SGB_INT8 &&
-      u->weights_dtype != SGB_F16)
-    return SGB_ERR_INVALID_ARGUMENT;
-  if (u->mode == SGB_DENSE_GRAD && u->weights_dtype != SGB_F32) return SGB_ERR_UNSUPPORTED;
+  if (do_reduce) {
+    if (u->mode != SGB_DENSE_GRAD && u->mode != SGB_SGD && u->mode != SGB_ROWWISE_ADAGRAD)
+      return SGB_ERR_INVALID_ARGUMENT;
+    if (u->mode == SGB_DENSE_GRAD && !u->grad) return SGB_ERR_INVALID_ARGUMENT;
+    if (u->mode == SGB_SGD && !u->weights) return SGB_ERR_INVALID_ARGUMENT;
+    if (u->mode == SGB_ROWWISE_ADAGRAD && (!u->weights || !u->momentum))
+      return SGB_ERR_INVALID_ARGUMENT;
+    if (u->weights_dtype != SGB_F32 && u->weights_dtype != SGB_BF16 &&
+        u->weights_dtype != SGB_INT8 && u->weights_dtype != SGB_F16)
+      return SGB_ERR_INVALID_ARGUMENT;
+    if (u->mode == SGB_DENSE_GRAD && u->weights_dtype != SGB_F32) return SGB_ERR_UNSUPPORTED;
+  }
   const bool w_f16 = u->mode != SGB_DENSE_GRAD && u->weights_dtype == SGB_F16;
   const bool w_bf16 = u->mode != SGB_DENSE_GRAD && (u->weights_dtype == SGB_BF16 || w_f16);
   const bool w_int8 = u->mode != SGB_DENSE_GRAD && u->weights_dtype == SGB_INT8;
   void* outv = u->mode == SGB_DENSE_GRAD ? static_cast<void*>(u->grad) : u->weights;
-  if (!aligned(outv, 16)) return SGB_ERR_INVALID_ARGUMENT;
+  if (do_reduce && !aligned(outv, 16)) return SGB_ERR_INVALID_ARGUMENT;
   float* out = (w_bf16 || w_int8) ? nullptr : static_cast<float*>(outv);
-  const bool fresh = u->mode == SGB_DENSE_GRAD && !u->accumulate;
+  const bool fresh = do_reduce && u->mode == SGB_DENSE_GRAD && !u->accumulate;
   DeviceGuard guard(p->device);
   if (!guard.ok) return SGB_ERR_HIP;
   auto mark_on = [&](hipStream_t s, int stage, int end) {
@@ -412,7 +445,7 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
 
   if (N == 0) {  // FBGEMM host entry: no indices -> nothing to do (dense grad stays zero)
     // clear the status word so sgb_device_status() reports this call
-    if (ws && aligned(ws, 256) && ws_bytes >= sizeof(Header) &&
+    if (do_front && ws && aligned(ws, 256) && ws_bytes >= sizeof(Header) &&
         launch_init(ws, sizeof(Header), stream) != hipSuccess)
       return SGB_ERR_HIP;
     if (fresh && p->n_fill > 0) {
@@ -421,8 +454,9 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
     }
     return SGB_OK;
   }
-  if (!b->indices || !b->grad_output) return SGB_ERR_INVALID_ARGUMENT;
-  if (!aligned(b->grad_output, b->grad_dtype == SGB_F32 ? 16 : 8)) return SGB_ERR_INVALID_ARGUMENT;
+  if (!b->indices || (do_reduce && !b->grad_output)) return SGB_ERR_INVALID_ARGUMENT;
+  if (do_reduce && !aligned(b->grad_output, b->grad_dtype == SGB_F32 ? 16 : 8))
+    return SGB_ERR_INVALID_ARGUMENT;
   if (!ws || !aligned(ws, 256)) return SGB_ERR_INVALID_ARGUMENT;
   Layout L;
   sgb_status st = make_layout(p, N, b->offsets ? b->B : 0, b->offsets != nullptr, &L);
@@ -480,7 +514,7 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   const int lin_grid =
       (int)std::max<int64_t>(1, std::min<int64_t>(lin_tiles, (int64_t)SGB_LIN_WG_PER_CU * p->num_cus));
   mark(SGB_STAGE_LINEARIZE, 0);
-  if (launch_linearize(lp, lin_grid, stream) != hipSuccess) return SGB_ERR_HIP;
+  if (do_front && launch_linearize(lp, lin_grid, stream) != hipSuccess) return SGB_ERR_HIP;
   mark(SGB_STAGE_LINEARIZE, 1);
 
   // LSD radix passes, ping-pong between A and B
@@ -510,7 +544,7 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
     sp.status = status;
     sp.epoch = epoch;
     if (ps == 0) mark(SGB_STAGE_SORT_PASS, 0);
-    if (launch_sort_pass(sp, stream) != hipSuccess) return SGB_ERR_HIP;
+    if (do_front && launch_sort_pass(sp, stream) != hipSuccess) return SGB_ERR_HIP;
     if (ps == 0) mark(SGB_STAGE_SORT_PASS, 1);
     std::swap(kv_in, kv_out);
     std::swap(cf_in, cf_out);
@@ -536,7 +570,7 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   rp.status = status;
   rp.epoch = epoch;
   mark(SGB_STAGE_RLE, 0);
-  if (launch_rle(rp, stream) != hipSuccess) return SGB_ERR_HIP;
+  if (do_front && launch_rle(rp, stream) != hipSuccess) return SGB_ERR_HIP;
   mark(SGB_STAGE_RLE, 1);
 
   PostParams pp{};
@@ -581,6 +615,7 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   q.num_runs = rp.num_runs;
   q.total_items = pp.total_items;
   q.num_long = &hdr->num_long;
+  q.header = hdr;
   q.sc_ticket = at<uint32_t>(ws, L.sctk);
   q.run_ticket = at<uint32_t>(ws, L.runtk);
   q.partials = at<double>(ws, L.part);
@@ -612,17 +647,23 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   // short runs need only the sorted words and run starts: side stream from
   // here on (after the zero fill), while the long-run list is built and the
   // long runs are reduced here; the two write disjoint rows
-  if (hipEventRecord(p->ev[2], stream) != hipSuccess ||
-      hipStreamWaitEvent(short_s, p->ev[2], 0) != hipSuccess ||
-      (fresh && hipStreamWaitEvent(short_s, p->ev[1], 0) != hipSuccess))
-    return SGB_ERR_HIP;
-  mark_on(short_s, SGB_STAGE_REDUCE_SHORT, 0);
-  if (launch_reduce_short(q, bf16, p->Dmin, p->Dmax, p->wide_grid, short_s) != hipSuccess) return SGB_ERR_HIP;
-  mark_on(short_s, SGB_STAGE_REDUCE_SHORT, 1);
-  if (hipEventRecord(p->ev[3], short_s) != hipSuccess) return SGB_ERR_HIP;
-  mark(SGB_STAGE_RUNS, 0);
-  if (launch_post(pp, (int)L.scan_tiles, stream) != hipSuccess) return SGB_ERR_HIP;
-  mark(SGB_STAGE_RUNS, 1);
+  if (do_reduce) {
+    if (hipEventRecord(p->ev[2], stream) != hipSuccess ||
+        hipStreamWaitEvent(short_s, p->ev[2], 0) != hipSuccess ||
+        (fresh && hipStreamWaitEvent(short_s, p->ev[1], 0) != hipSuccess))
+      return SGB_ERR_HIP;
+    mark_on(short_s, SGB_STAGE_REDUCE_SHORT, 0);
+    if (launch_reduce_short(q, bf16, p->Dmin, p->Dmax, p->wide_grid, short_s) != hipSuccess)
+      return SGB_ERR_HIP;
+    mark_on(short_s, SGB_STAGE_REDUCE_SHORT, 1);
+    if (hipEventRecord(p->ev[3], short_s) != hipSuccess) return SGB_ERR_HIP;
+  }
+  if (do_front) {
+    mark(SGB_STAGE_RUNS, 0);
+    if (launch_post(pp, (int)L.scan_tiles, stream) != hipSuccess) return SGB_ERR_HIP;
+    mark(SGB_STAGE_RUNS, 1);
+  }
+  if (!do_reduce) return SGB_OK;
   if (fresh && hipStreamWaitEvent(stream, p->ev[1], 0) != hipSuccess) return SGB_ERR_HIP;
   mark(SGB_STAGE_REDUCE_LONG, 0);
   if (launch_reduce_long(q, bf16, p->red_grid[bf16 ? 1 : 0], stream) != hipSuccess)
@@ -632,6 +673,10 @@ sgb_status sgb_backward_timed(sgb_plan p, const sgb_batch* b, const sgb_update* 
   if (hipStreamWaitEvent(stream, p->ev[3], 0) != hipSuccess) return SGB_ERR_HIP;
   return SGB_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 sgb_status sgb_forward(sgb_plan p, const sgb_lookups* lk, const float* weights, float* output,
                        void* ws, size_t ws_bytes, void* stream_) {

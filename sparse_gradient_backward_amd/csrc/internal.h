@@ -392,6 +392,7 @@ struct RedParams {
   const int32_t* num_runs;
   const uint32_t* total_items;
   const int64_t* num_long;
+  const Header* header;     // the workspace's header: N and B of the run structure
   uint32_t* sc_ticket;
   uint32_t* run_ticket;
   double* partials;         // fp64 partial sums of long-run work items

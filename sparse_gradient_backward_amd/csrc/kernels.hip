@@ -1352,6 +1352,19 @@ __device__ __forceinline__ int table_of(const RedParams& p, uint32_t info) {
   return t < p.T ? t : p.T - 1;
 }
 
+// The run structure a reducer reads must be the one the linearisation of
+// this call's lookups wrote (sgb_apply after sgb_prepare into the same
+// workspace): the header records that call's N and B.  On a mismatch the
+// reducer records an internal error and does nothing, instead of walking
+// another batch's runs.  (The header is one value for the whole grid, so
+// every wave takes the same branch.)
+__device__ __forceinline__ bool runs_match(const RedParams& p) {
+  const Header* h = p.header;
+  const bool ok = h->num_indices == p.N && h->B == p.B;
+  if (!ok && blockIdx.x == 0 && threadIdx.x == 0) set_status(p.status, h->epoch, kStInternal);
+  return ok;
+}
+
 // Row of grad_output that a lookup of table t reads.
 __device__ __forceinline__ int grad_row_of(const RedParams& p, uint32_t info, int t) {
   if (p.nobag) {
@@ -2182,6 +2195,7 @@ __device__ __forceinline__ LongRun uniform_rec(const LongRun& r) {
 
 template <bool BF16, int WK>
 __global__ __launch_bounds__(256) void k_reduce_long(RedParams p) {
+  if (!runs_match(p)) return;
   const uint32_t n_items = *p.total_items;
   const int nlong = (int)*p.num_long;
   // items are dealt round-robin: consecutive chunks of a hot run go to
@@ -2452,6 +2466,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     WK != kWF32 ? SGB_SHORT8_WAVES - 1 : SGB_SHORT8_WAVES,
     WK != kWF32 ? SGB_SHORT8_WAVES - 1 : SGB_SHORT8_WAVES)))
 void k_reduce_short8(RedParams p) {
+  if (!runs_match(p)) return;
   reduce_short<8, BF16, WK>(p);
 }
 
@@ -2686,6 +2701,7 @@ template <int CPL, int UNR, bool BF16, int WK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, SGB_WIDE_WAVES)))
 void k_reduce_wide(RedParams p) {
   __shared__ MetaLds s_meta;
+  if (!runs_match(p)) return;
   const int64_t nw = (int64_t)gridDim.x * 4;
   int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int ncb = p.wide_ncb;
@@ -2712,6 +2728,7 @@ void k_reduce_wide(RedParams p) {
 // that wide.
 template <bool BF16, int WK>
 __global__ __launch_bounds__(256) void k_reduce_wide_multi(RedParams p) {
+  if (!runs_match(p)) return;
   const int64_t runs = *p.num_runs;
   const int64_t nw = (int64_t)gridDim.x * 4;
   const uint64_t imask = info_mask(p);

@@ -18,7 +18,7 @@ def test_every_declared_function_is_exported():
     declared = sgb.header_functions()
     assert set(declared) == {"sgb_plan_create", "sgb_plan_destroy", "sgb_workspace_bytes",
                              "sgb_backward", "sgb_backward_timed", "sgb_backward_noalloc",
-                             "sgb_device_status",
+                             "sgb_prepare", "sgb_apply", "sgb_device_status",
                              "sgb_runs_view_get", "sgb_status_string", "sgb_forward"}
     lib = ctypes.CDLL(sgb.LIB_PATH)
     for name in declared:
@@ -117,5 +117,11 @@ def test_null_arguments():
     assert lib.sgb_backward(None, None, None, None, ctypes.c_size_t(0), None) == \
         sgb.SGB_ERR_INVALID_ARGUMENT
     assert lib.sgb_workspace_bytes(None, ctypes.c_int64(10), 1, None) == \
+        sgb.SGB_ERR_INVALID_ARGUMENT
+    lib.sgb_prepare.restype = ctypes.c_int
+    lib.sgb_apply.restype = ctypes.c_int
+    assert lib.sgb_prepare(None, None, None, ctypes.c_size_t(0), None) == \
+        sgb.SGB_ERR_INVALID_ARGUMENT
+    assert lib.sgb_apply(None, None, None, None, ctypes.c_size_t(0), None) == \
         sgb.SGB_ERR_INVALID_ARGUMENT
     lib.sgb_plan_destroy(None)
