@@ -213,6 +213,7 @@ typedef struct {
  *  everything enqueued on `stream` before the call, and `stream` waits for
  *  them before any work enqueued after the call, so the call behaves as if
  *  it ran on `stream` alone.  Calls with one plan share its side streams.
+ *  Batches of at most 16384 lookups run on `stream` alone.
  */
 sgb_status sgb_backward(sgb_plan plan, const sgb_batch* batch, const sgb_update* update,
                         void* workspace, size_t workspace_bytes, void* stream);

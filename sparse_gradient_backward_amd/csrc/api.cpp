@@ -472,8 +472,8 @@ sgb_status enqueue(sgb_plan p, const sgb_batch* b, const sgb_update* u, void* ws
   // the plan's side streams and fork/join events: one call's sequence at a time
   std::lock_guard<std::mutex> lock(p->mu);
   // the timed variant runs every kernel in order on `stream`, so that each
-  // kernel's events bracket that kernel alone
-  const bool overlap = events == nullptr;
+  // kernel's events bracket that kernel alone; so do small batches
+  const bool overlap = events == nullptr && N > kSerialMaxN;
   hipStream_t fill_s = overlap ? p->aux[0] : stream, short_s = overlap ? p->aux[1] : stream;
   if (fresh) {
     // fork: the fresh gradient is cleared on a side stream, overlapping the

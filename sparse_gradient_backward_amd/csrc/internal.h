@@ -68,6 +68,9 @@ constexpr int kMaxD = 8192;
 #ifndef SGB_LOOKBACK
 #define SGB_LOOKBACK 16
 #endif
+#ifndef SGB_SERIAL_MAX_N
+#define SGB_SERIAL_MAX_N 16384
+#endif
 #ifndef SGB_ONE_PASS_TILES
 #define SGB_ONE_PASS_TILES 128
 #endif
@@ -139,6 +142,10 @@ constexpr int kLbScalarGroupTiles = 32;
 // tile's first run index by look-back over the tiles' head counts); up to
 // kFuseScanTiles k_rle_count, then k_rle_write summing the counts before its
 // tile; beyond that k_rle_count, k_rle_scan and k_rle_write
+// Batches of at most kSerialMaxN lookups run every kernel on the caller's
+// stream: their kernels are a few microseconds each, and the fork to the
+// plan's side streams and the join cost more than the overlap returns.
+constexpr int64_t kSerialMaxN = SGB_SERIAL_MAX_N;
 constexpr int kOnePassTiles = SGB_ONE_PASS_TILES;
 constexpr int kFuseScanTiles = SGB_FUSE_SCAN_TILES;
 
