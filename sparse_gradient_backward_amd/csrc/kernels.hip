@@ -1437,6 +1437,49 @@ __device__ __forceinline__ RowDst row_dest_m(const RedParams& p, const MetaView&
   return d;
 }
 
+// A table's metadata for a wave-uniform table index, through scalar loads:
+// the plan's arrays are read-only while a kernel runs, so they are read as
+// constant memory (the scalar data cache) instead of through the vector
+// memory path, where each lookup would wait behind the wave's gathers.
+template <typename T>
+__device__ __forceinline__ T ld_const(const T* a, int64_t i) {
+  typedef const __attribute__((address_space(4))) T* cptr;
+  return ((cptr)a)[i];
+}
+
+struct TabMeta {
+  int32_t D;     // row width
+  int32_t dcol;  // first column of the table in a grad_output row
+  int64_t h0;    // first linear id
+  int64_t E;     // rows
+  int64_t wo;    // first element (INT8: byte) of the table's rows
+};
+
+template <int WK>
+__device__ __forceinline__ TabMeta tab_meta(const RedParams& p, int t) {
+  const int32_t d0 = ld_const(p.doff, t), d1 = ld_const(p.doff, t + 1);
+  const int64_t h0 = ld_const(p.hsc, t), h1 = ld_const(p.hsc, t + 1);
+  const int64_t wo = ld_const(WK == kWINT8 ? p.woff8 : p.woff, t);
+  return TabMeta{d1 - d0, d0, h0, h1 - h0, wo};
+}
+
+template <int WK>
+__device__ __forceinline__ RowDst row_dest_t(const RedParams& p, const TabMeta& tm, int64_t lin) {
+  int64_t row = lin - tm.h0;
+  row = row < 0 ? 0 : (row < tm.E ? row : tm.E - 1);
+  RowDst d;
+  if constexpr (WK == kWINT8)
+    d.out = p.out_q + tm.wo + row * (int64_t)(tm.D + 8);
+  else if constexpr (WK == kWBF16)
+    d.out = p.out_h + tm.wo + row * (int64_t)tm.D;
+  else
+    d.out = p.out + tm.wo + row * (int64_t)tm.D;
+  d.mom = p.mom ? p.mom + tm.h0 + row : nullptr;
+  d.lin = tm.h0 + row;
+  d.D = tm.D;
+  return d;
+}
+
 // Copies the plan's table metadata into `s` (all threads of the workgroup
 // take part; a barrier ends it) and returns the view the reducer reads.
 template <int WK, class P>
@@ -2236,7 +2279,8 @@ __device__ __forceinline__ int short_lpl(int D) {
 template <int CPL, bool BF16, int WK>
 __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, int lpl, int64_t base,
                                             int len, uint64_t key, int rowi, float cf, int t,
-                                            int D, int cb) {
+                                            const TabMeta& tm, int cb) {
+  const int D = tm.D;
   constexpr int NP = CPL / 4;
   const int lg = __builtin_ctz(lpl);
   const int lane = lane_id(), g = lane >> lg, lig = lane & (lpl - 1), gb = g << lg;
@@ -2266,65 +2310,98 @@ __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, in
     if (active && col + 4 * lpl * i < D) vmask |= 1 << i;
   const int wmask = lead ? vmask : 0;
   RowDst dst{nullptr, nullptr, 0, 0};
-  if (lead) dst = row_dest<WK>(p, t, D, (int64_t)id);
+  if (lead) dst = row_dest_t<WK>(p, tm, (int64_t)id);
   const bool needs_old = p.mode != kModeDense || p.accumulate;
-  float4 old[NP];
-  d4 acc[NP];
-#pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    old[i] = (needs_old && ((wmask >> i) & 1)) ? ldw4<WK>(p, dst, col, 4 * lpl * i)
-                                              : make_float4(0.f, 0.f, 0.f, 0.f);
-    acc[i] = d4_zero();
-  }
-  const float m0 = (p.mode == kModeAdagrad && lead) ? *dst.mom : 0.f;
-  const int64_t gcol = (p.nobag ? 0 : p.doff[t]) + col;
+  const int64_t gcol = (p.nobag ? 0 : tm.dcol) + col;
   const uint64_t imask = info_mask(p);
   const bool has_coef = p.coef != nullptr;
-  // slices of lpl lookups of this group's run, every (1 << glg)-th one; the
-  // first slice's metadata comes from the window when it lies inside it
-  bool firstb = true;
-  for (int j0 = s + (q << lg); j0 < s + n; j0 += lpl << glg) {
+  d4 acc[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) acc[i] = d4_zero();
+  // one round: the group's lookups jj .. jj + UNR - 1 of its current slice
+  // (lane gb + j holds lookup j's grad_output row and coefficient)
+  auto gather = [&](Raw4<BF16> (&r)[SGB_SHORT_UNR][NP], float (&c)[SGB_SHORT_UNR], int ri, float ci,
+                    int jj, int cnt) {
+    // every shuffle first (unconditional), then the loads: no wait for a
+    // coefficient sits between two of the round's gathers
+    int ro[SGB_SHORT_UNR];
+#pragma unroll
+    for (int u = 0; u < SGB_SHORT_UNR; ++u) {
+      const int srcl = gb + min(jj + u, lpl - 1);
+      ro[u] = __shfl(ri, srcl, 64);
+      c[u] = __shfl(ci, srcl, 64);
+    }
+#pragma unroll
+    for (int u = 0; u < SGB_SHORT_UNR; ++u) {
+      const bool ok = jj + u < cnt;
+      c[u] = ok ? c[u] : 0.f;
+      const int64_t e = (int64_t)ro[u] * p.row_stride + gcol;
+#pragma unroll
+      for (int i = 0; i < NP; ++i)
+        r[u][i] = (ok && ((vmask >> i) & 1)) ? load_raw4<BF16>(p.grad, e + 4 * lpl * i)
+                                             : zero_raw4<BF16>();
+    }
+  };
+  // the round's few products are summed in fp32, the run's sum in fp64
+  auto accumulate = [&](const Raw4<BF16> (&r)[SGB_SHORT_UNR][NP], const float (&c)[SGB_SHORT_UNR]) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int u = 0; u < SGB_SHORT_UNR; ++u) {
+        const float4 v = widen4<BF16>(r[u][i]);
+        t.x = fmaf(c[u], v.x, t.x);
+        t.y = fmaf(c[u], v.y, t.y);
+        t.z = fmaf(c[u], v.z, t.z);
+        t.w = fmaf(c[u], v.w, t.w);
+      }
+      d4_add(acc[i], d4{(double)t.x, (double)t.y, (double)t.z, (double)t.w});
+    }
+  };
+  // The group takes slices of lpl lookups of its run, every (1 << glg)-th
+  // one.  The first round of its first slice (whose metadata comes from the
+  // window when it lies inside it) is loaded together with the old row and
+  // its Adagrad state, with nothing waited for in between: a run of at most
+  // SGB_SHORT_UNR lookups costs one memory round trip.
+  const int j0f = s + (q << lg);
+  int ri = 0;
+  float ci = 0.f;
+  if (wl < 64) {
+    ri = prow;
+    ci = pcf;
+  } else if (j0f + lig < s + n) {
+    ri = grad_row_of(p, (uint32_t)(p.kv[j0f + lig] & imask), t);
+    ci = has_coef ? p.coef[j0f + lig] : 1.0f;
+  }
+  const int cnt0 = min(lpl, s + n - j0f);  // <= 0 for a group with nothing to gather
+  Raw4<BF16> r[SGB_SHORT_UNR][NP];
+  float c[SGB_SHORT_UNR];
+  gather(r, c, ri, ci, 0, cnt0);
+  float4 old[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i)
+    old[i] = (needs_old && ((wmask >> i) & 1)) ? ldw4<WK>(p, dst, col, 4 * lpl * i)
+                                              : make_float4(0.f, 0.f, 0.f, 0.f);
+  // every lane loads (the others the first state word), so that the load sits
+  // outside a branch and nothing waits for it before the sums need it
+  const float m0 = p.mode == kModeAdagrad ? *(lead ? dst.mom : p.mom) : 0.f;
+  accumulate(r, c);
+  for (int jj = SGB_SHORT_UNR; jj < cnt0; jj += SGB_SHORT_UNR) {
+    gather(r, c, ri, ci, jj, cnt0);
+    accumulate(r, c);
+  }
+  for (int j0 = j0f + (lpl << glg); j0 < s + n; j0 += lpl << glg) {
     const int jm = j0 + lig;
-    int ri = 0;
-    float ci = 0.f;
-    if (firstb && wl < 64) {
-      ri = prow;
-      ci = pcf;
-    } else if (jm < s + n) {
+    ri = 0;
+    ci = 0.f;
+    if (jm < s + n) {
       ri = grad_row_of(p, (uint32_t)(p.kv[jm] & imask), t);
       ci = has_coef ? p.coef[jm] : 1.0f;
     }
-    firstb = false;
     const int cnt = min(lpl, s + n - j0);
     for (int jj = 0; jj < cnt; jj += SGB_SHORT_UNR) {
-      Raw4<BF16> r[SGB_SHORT_UNR][NP];
-      float c[SGB_SHORT_UNR];
-#pragma unroll
-      for (int u = 0; u < SGB_SHORT_UNR; ++u) {
-        const int srcl = gb + min(jj + u, lpl - 1);
-        const bool ok = jj + u < cnt;
-        const int ro = __shfl(ri, srcl, 64);
-        c[u] = ok ? __shfl(ci, srcl, 64) : 0.f;
-        const int64_t e = (int64_t)ro * p.row_stride + gcol;
-#pragma unroll
-        for (int i = 0; i < NP; ++i)
-          r[u][i] = (ok && ((vmask >> i) & 1)) ? load_raw4<BF16>(p.grad, e + 4 * lpl * i)
-                                               : zero_raw4<BF16>();
-      }
-#pragma unroll
-      for (int i = 0; i < NP; ++i) {
-        // the round's few products are summed in fp32, the run's sum in fp64
-        float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int u = 0; u < SGB_SHORT_UNR; ++u) {
-          const float4 v = widen4<BF16>(r[u][i]);
-          t.x = fmaf(c[u], v.x, t.x);
-          t.y = fmaf(c[u], v.y, t.y);
-          t.z = fmaf(c[u], v.z, t.z);
-          t.w = fmaf(c[u], v.w, t.w);
-        }
-        d4_add(acc[i], d4{(double)t.x, (double)t.y, (double)t.z, (double)t.w});
-      }
+      gather(r, c, ri, ci, jj, cnt);
+      accumulate(r, c);
     }
   }
   // fold the groups of each run (uniform trip count: the whole wave takes part)
@@ -2444,7 +2521,8 @@ __device__ __forceinline__ void reduce_short(const RedParams& p) {
     const int lead = __builtin_ctzll(pending);
     const int t0 = __builtin_amdgcn_readfirstlane(__shfl(t, lead, 64));
     const uint64_t same = __ballot(todo && t == t0) & pending;
-    const int D = p.doff[t0 + 1] - p.doff[t0];
+    const TabMeta tm = tab_meta<WK>(p, t0);
+    const int D = tm.D;
     const int lpl = short_lpl<CPL>(D);
     uint64_t sel = 0, rest = same;
     for (int i = 0; i < 64 / lpl && rest; ++i) {
@@ -2454,7 +2532,7 @@ __device__ __forceinline__ void reduce_short(const RedParams& p) {
     }
     pending &= ~sel;
     if (D > 512 || cb * 64 * CPL >= D) continue;  // wider rows: k_reduce_wide
-    short_batch<CPL, BF16, WK>(p, sel, lpl, base, len, key, rowi, cf, t0, D, cb);
+    short_batch<CPL, BF16, WK>(p, sel, lpl, base, len, key, rowi, cf, t0, tm, cb);
   }
 }
 
