@@ -80,7 +80,7 @@ def stage_bytes(inp: synth.Inputs, spec: synth.Spec, U: int, run_D: np.ndarray,
     touched_elems = int(run_D.sum())
     # tiles of the first radix pass (digits of up to 9 bits: 512 x 12 items
     # above 2^22 lookups; above 2^20, 1024 x I with the fewest I in 8..12 that
-    # keeps the tiles within the CUs), 512 x 8 above 2^16, else 256 x 8
+    # keeps the tiles within the CUs), 512 x 8 above 2^12, else 256 x 8
     if N > (1 << 22) and radix0 <= 512:
         sort_tile = 512 * 12
     elif N > (1 << 20) and radix0 <= 512:
@@ -89,7 +89,7 @@ def stage_bytes(inp: synth.Inputs, spec: synth.Spec, U: int, run_D: np.ndarray,
             items += 1
         sort_tile = 1024 * items
     else:
-        sort_tile = 512 * 8 if N > (1 << 16) else 256 * 8
+        sort_tile = 512 * 8 if N > (1 << 12) else 256 * 8
     tiles = (N + sort_tile - 1) // sort_tile
     scan_tiles = (N + 4095) // 4096
 

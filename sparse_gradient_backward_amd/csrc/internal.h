@@ -90,6 +90,9 @@ constexpr int kSortLbGroup = 16;  // tiles per look-back group of a radix pass
 //           (more than 12 would exceed the LDS)
 //   medium   512 x 8  ( 4096 items), N > kSortMediumN
 //   small    256 x 8  ( 2048 items)
+// (A batch of a few thousand lookups sorts in a handful of tiles, each one
+// latency chain: medium tiles, with twice the waves ranking, take the chain
+// in half the rounds.)
 // (A large tile fills one CU.  Beyond 12 x 1024 items per CU the pass takes
 // several rounds, and two half-size tiles per CU overlap one's loads with
 // the other's ranking.)
@@ -100,7 +103,7 @@ constexpr int kSortLbGroup = 16;  // tiles per look-back group of a radix pass
 #define SGB_SORT_LARGE_N (1 << 20)
 #endif
 #ifndef SGB_SORT_MEDIUM_N
-#define SGB_SORT_MEDIUM_N (1 << 16)
+#define SGB_SORT_MEDIUM_N (1 << 12)
 #endif
 // shape codes: kSortLarge8 + (I - 8) is the large shape with I items
 enum SortShape {

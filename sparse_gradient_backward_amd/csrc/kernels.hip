@@ -1389,54 +1389,6 @@ struct RowDst {
   int32_t D;    // its width (INT8: the parameters follow the D codes)
 };
 
-template <int WK>
-__device__ __forceinline__ RowDst row_dest(const RedParams& p, int t, int D, int64_t lin) {
-  const int64_t h0 = p.hsc[t], E = p.hsc[t + 1] - h0;
-  int64_t row = lin - h0;
-  row = row < 0 ? 0 : (row < E ? row : E - 1);
-  RowDst d;
-  if constexpr (WK == kWINT8)
-    d.out = p.out_q + p.woff8[t] + row * (int64_t)(D + 8);
-  else if constexpr (WK == kWBF16)
-    d.out = p.out_h + p.woff[t] + row * (int64_t)D;
-  else
-    d.out = p.out + p.woff[t] + row * (int64_t)D;
-  d.mom = p.mom ? p.mom + h0 + row : nullptr;
-  d.lin = h0 + row;
-  d.D = D;
-  return d;
-}
-
-// Table metadata a reducer wave reads for every run it serves (row width,
-// first row id, first element of the table), through generic pointers:
-// to a copy in the workgroup's LDS, staged at the start for up to kMetaT
-// tables, or to the plan's global arrays beyond that.  A wave whose items are
-// one or two runs would otherwise wait two more memory round trips per item.
-struct MetaView {
-  const int32_t* doff;
-  const int64_t* hsc;
-  const int64_t* woff;  // woff8 for INT8 rows
-};
-
-template <int WK>
-__device__ __forceinline__ RowDst row_dest_m(const RedParams& p, const MetaView& mv, int t, int D,
-                                             int64_t lin) {
-  const int64_t h0 = mv.hsc[t], E = mv.hsc[t + 1] - h0;
-  int64_t row = lin - h0;
-  row = row < 0 ? 0 : (row < E ? row : E - 1);
-  RowDst d;
-  if constexpr (WK == kWINT8)
-    d.out = p.out_q + mv.woff[t] + row * (int64_t)(D + 8);
-  else if constexpr (WK == kWBF16)
-    d.out = p.out_h + mv.woff[t] + row * (int64_t)D;
-  else
-    d.out = p.out + mv.woff[t] + row * (int64_t)D;
-  d.mom = p.mom ? p.mom + h0 + row : nullptr;
-  d.lin = h0 + row;
-  d.D = D;
-  return d;
-}
-
 // A table's metadata for a wave-uniform table index, through scalar loads:
 // the plan's arrays are read-only while a kernel runs, so they are read as
 // constant memory (the scalar data cache) instead of through the vector
@@ -1464,7 +1416,7 @@ __device__ __forceinline__ TabMeta tab_meta(const RedParams& p, int t) {
 }
 
 template <int WK>
-__device__ __forceinline__ RowDst row_dest_t(const RedParams& p, const TabMeta& tm, int64_t lin) {
+__device__ __forceinline__ RowDst row_dest(const RedParams& p, const TabMeta& tm, int64_t lin) {
   int64_t row = lin - tm.h0;
   row = row < 0 ? 0 : (row < tm.E ? row : tm.E - 1);
   RowDst d;
@@ -1478,23 +1430,6 @@ __device__ __forceinline__ RowDst row_dest_t(const RedParams& p, const TabMeta& 
   d.lin = tm.h0 + row;
   d.D = tm.D;
   return d;
-}
-
-// Copies the plan's table metadata into `s` (all threads of the workgroup
-// take part; a barrier ends it) and returns the view the reducer reads.
-template <int WK, class P>
-__device__ __forceinline__ MetaView stage_meta(const P& p, MetaLds& s) {
-  const int64_t* wo = WK == kWINT8 ? p.woff8 : p.woff;
-  const bool staged = p.T <= kMetaT;
-  if (staged) {
-    for (int j = threadIdx.x; j <= p.T; j += blockDim.x) {
-      s.doff[j] = p.doff[j];
-      s.hsc[j] = p.hsc[j];
-      s.woff[j] = wo[j];
-    }
-  }
-  __syncthreads();
-  return staged ? MetaView{s.doff, s.hsc, s.woff} : MetaView{p.doff, p.hsc, wo};
 }
 
 // ---- bf16 weight rows
@@ -2310,7 +2245,7 @@ __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, in
     if (active && col + 4 * lpl * i < D) vmask |= 1 << i;
   const int wmask = lead ? vmask : 0;
   RowDst dst{nullptr, nullptr, 0, 0};
-  if (lead) dst = row_dest_t<WK>(p, tm, (int64_t)id);
+  if (lead) dst = row_dest<WK>(p, tm, (int64_t)id);
   const bool needs_old = p.mode != kModeDense || p.accumulate;
   const int64_t gcol = (p.nobag ? 0 : tm.dcol) + col;
   const uint64_t imask = info_mask(p);
@@ -2579,8 +2514,8 @@ __device__ __forceinline__ WideRun wide_run(const RedParams& p, int64_t item, in
   WideRun m{0, 0};
   if (item < items) {
     const int r = (int)(item / ncb);
-    m.s = uni32(p.cum[r]);
-    m.e = uni32(p.cum[r + 1]);
+    m.s = p.cum[r];  // the same word in every lane: made wave-uniform where used
+    m.e = p.cum[r + 1];
   }
   return m;
 }
@@ -2592,9 +2527,9 @@ struct WideLane {
 };
 
 __device__ __forceinline__ WideLane wide_lane(const RedParams& p, const WideRun& m, int j0) {
-  const int j = m.s + j0 + lane_id();
+  const int j = uni32(m.s) + j0 + lane_id();
   WideLane d{0ull, 1.0f};
-  if (j < m.e) {
+  if (j < uni32(m.e)) {
     d.kv = p.kv[j];
     if (p.coef) d.cf = p.coef[j];
   }
@@ -2618,13 +2553,15 @@ __device__ __forceinline__ uint64_t rl64(uint64_t x, int l) {
 // range), so nothing beyond 4 columns per lane is held at a time.
 template <bool BF16, int WK>
 __device__ __forceinline__ void wide_run_multi(const RedParams& p, const WideRun& m,
-                                            const WideLane& d0, int t, int D, int64_t lin) {
+                                            const WideLane& d0, int t, const TabMeta& tm,
+                                            int64_t lin) {
   constexpr int UNR = 4;
+  const int D = tm.D;
   const Groups G = groups_of(64);
-  const RowDst dst = row_dest<WK>(p, t, D, lin);
+  const RowDst dst = row_dest<WK>(p, tm, lin);
   const uint64_t imask = info_mask(p);
   const int len = m.e - m.s;
-  const int64_t gbase = p.nobag ? 0 : p.doff[t];
+  const int64_t gbase = p.nobag ? 0 : tm.dcol;
   auto getG = [&](int cb) -> d4 {
     const int col = cb * kColBlock + 4 * lane_id();
     const bool ok = col < D;
@@ -2655,15 +2592,16 @@ __device__ __forceinline__ void wide_run_multi(const RedParams& p, const WideRun
 }
 
 template <int CPL, int UNR, bool BF16, int WK>
-__device__ __forceinline__ void wide_item(const RedParams& p, const MetaView& mv, const WideRun& m,
+__device__ __forceinline__ void wide_item(const RedParams& p, const WideRun& m,
                                           const WideLane& d0, int cb) {
   constexpr int NP = CPL / 4;
-  const int len = m.e - m.s;
+  const int len = uni32(m.e) - uni32(m.s);
   if (len <= 0 || len >= p.thr) return;
   const uint64_t imask = info_mask(p);
   const uint64_t kv0 = rl64(d0.kv, 0);
   const int t = uni32(table_of(p, (uint32_t)(kv0 & imask)));
-  const int D = uni32(mv.doff[t + 1] - mv.doff[t]);
+  const TabMeta tm = tab_meta<WK>(p, t);
+  const int D = tm.D;
   // whole rows wider than one item are served by k_reduce_wide_multi
   if ((p.mode == kModeAdagrad || WK == kWINT8) && D > 64 * CPL) return;
   if (D <= 512 || cb * 64 * CPL >= D) return;
@@ -2672,7 +2610,7 @@ __device__ __forceinline__ void wide_item(const RedParams& p, const MetaView& mv
 #pragma unroll
   for (int i = 0; i < NP; ++i)
     if (col + 256 * i < D) vmask |= 1 << i;
-  const RowDst dst = row_dest_m<WK>(p, mv, t, D, (int64_t)(kv0 >> p.info_bits));
+  const RowDst dst = row_dest<WK>(p, tm, (int64_t)(kv0 >> p.info_bits));
   const bool needs_old = p.mode != kModeDense || p.accumulate;
   float4 old[NP];
   d4 acc[NP];
@@ -2682,8 +2620,11 @@ __device__ __forceinline__ void wide_item(const RedParams& p, const MetaView& mv
                                               : make_float4(0.f, 0.f, 0.f, 0.f);
     acc[i] = d4_zero();
   }
-  const float m0 = p.mode == kModeAdagrad ? *dst.mom : 0.f;
-  const int64_t gcol = (p.nobag ? 0 : mv.doff[t]) + col;
+  // (outside a branch: the state is waited for only where the sums need it;
+  // without Adagrad state the first sorted word stands in)
+  const float mv0 = *(p.mode == kModeAdagrad ? dst.mom : reinterpret_cast<const float*>(p.kv));
+  const float m0 = p.mode == kModeAdagrad ? mv0 : 0.f;
+  const int64_t gcol = (p.nobag ? 0 : tm.dcol) + col;
   for (int j0 = 0; j0 < len; j0 += 64) {
     const WideLane dl = j0 == 0 ? d0 : wide_lane(p, m, j0);
     const int rowi = grad_row_of(p, (uint32_t)(dl.kv & imask), t);
@@ -2778,22 +2719,19 @@ __device__ __forceinline__ void wide_item(const RedParams& p, const MetaView& mv
 template <int CPL, int UNR, bool BF16, int WK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, SGB_WIDE_WAVES)))
 void k_reduce_wide(RedParams p) {
-  __shared__ MetaLds s_meta;
   if (!runs_match(p)) return;
   const int64_t nw = (int64_t)gridDim.x * 4;
   int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int ncb = p.wide_ncb;
   const int64_t items = (int64_t)(*p.num_runs) * ncb;
-  // the first item's run starts are loaded with the metadata
-  WideRun m0 = wide_run(p, item, items, ncb);
-  const MetaView mv = stage_meta<WK>(p, s_meta);
   if (item >= items) return;
+  WideRun m0 = wide_run(p, item, items, ncb);
   WideLane d0 = wide_lane(p, m0, 0);
   WideRun m1 = wide_run(p, item + nw, items, ncb);
   for (; item < items; item += nw) {
     const WideRun m2 = wide_run(p, item + 2 * nw, items, ncb);
     const WideLane d1 = wide_lane(p, m1, 0);
-    wide_item<CPL, UNR, BF16, WK>(p, mv, m0, d0, (int)(item % ncb));
+    wide_item<CPL, UNR, BF16, WK>(p, m0, d0, (int)(item % ncb));
     m0 = m1;
     d0 = d1;
     m1 = m2;
@@ -2819,9 +2757,9 @@ __global__ __launch_bounds__(256) void k_reduce_wide_multi(RedParams p) {
     const WideLane d0 = wide_lane(p, m, 0);
     const uint64_t kv0 = rl64(d0.kv, 0);
     const int t = uni32(table_of(p, (uint32_t)(kv0 & imask)));
-    const int D = uni32(p.doff[t + 1] - p.doff[t]);
-    if (D <= 1024) continue;
-    wide_run_multi<BF16, WK>(p, m, d0, t, D, (int64_t)(kv0 >> p.info_bits));
+    const TabMeta tm = tab_meta<WK>(p, t);
+    if (tm.D <= 1024) continue;
+    wide_run_multi<BF16, WK>(p, m, d0, t, tm, (int64_t)(kv0 >> p.info_bits));
   }
 }
 

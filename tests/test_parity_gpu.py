@@ -266,10 +266,10 @@ def test_many_run_tiles(sgb, tokens):
 SORT_SHAPES = [
     # (rows, lookups, index distribution): id bits -> digits per radix pass; tile shape
     (1, 3000, ("uniform",)),            # 0 bits: nothing to sort
-    (2, 5000, ("uniform",)),            # 1 bit, radix 2 (most look-back lanes idle); small tiles
-    (6, 5000, ("zipf", 1.5)),           # 3 bits, radix 8
-    (60000, 65536, ("zipf", 1.05)),     # 16 bits -> 8/8; small tiles, the largest such batch
-    (60000, 65537, ("zipf", 1.05)),     # medium tiles from here
+    (2, 4000, ("uniform",)),            # 1 bit, radix 2 (most look-back lanes idle); small tiles
+    (6, 4096, ("zipf", 1.5)),           # 3 bits, radix 8; small tiles, the largest such batch
+    (60000, 4097, ("zipf", 1.05)),      # 16 bits -> 8/8; medium tiles from here
+    (60000, 65537, ("zipf", 1.05)),     # 17 medium tiles
     (1 << 20, 300_000, ("uniform",)),   # 20 bits -> 10/10: medium tiles with 1024 digits
     (1 << 20, 1_200_000, ("zipf", 1.1)),  # 10-bit digits keep medium tiles above 2^20 lookups
     # large tiles of 1024 x I items, I the fewest of 8..12 that keeps the
