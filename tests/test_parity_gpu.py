@@ -153,10 +153,10 @@ def test_medium_runs_of_wide_rows(sgb, mode, acc):
 @pytest.mark.parametrize("T", [512, 600])
 @pytest.mark.parametrize("mode", ["dense", "sgd", "rowwise_adagrad"])
 def test_many_tables(sgb, T, mode):
-    """Table metadata is staged in LDS for up to 512 tables (run
-    post-processing, wide-row reducer) and read from memory beyond that: 512
-    and 600 tables of 8, 64, 520 and 1028 columns, Zipf ids so that some runs
-    are long (thr = 4)."""
+    """Run post-processing stages the table metadata in LDS for up to 512
+    tables and reads it from memory beyond that; the reducers read it through
+    scalar loads indexed by table: 512 and 600 tables of 8, 64, 520 and 1028
+    columns, Zipf ids so that some runs are long (thr = 4)."""
     dims = tuple((8, 64, 520, 1028)[t % 4] for t in range(T))
     s = synth.Spec("manytables", T, (40,) * T, dims, 24, ("uniform", 0, 5), ("zipf", 1.3),
                    "sum", False, "f32", mode, seed=83)
