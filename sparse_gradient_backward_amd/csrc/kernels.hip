@@ -4,13 +4,13 @@
 //   k_init         zero the workspace header (empty batches only)
 //   k_linearize    bags -> per-lookup packed word (linear id << info_bits | info)
 //                  and coefficient; range and offset checks; zeroes the
-//                  region the later kernels count in
-//   k_sort_count / k_sort_offsets / k_sort_scatter
-//                  one stable LSD radix pass (<= 10-bit digits) as
-//                  reduce-then-scan: tile digit counts, their scan per digit,
-//                  ballot-ranked LDS-staged scatter (with at most kFuseTiles
-//                  tiles the scatter scans the counts itself and
-//                  k_sort_offsets is not launched)
+//                  region the later kernels count in; counts the first radix
+//                  pass's digits
+//   k_sort_pass    one stable LSD radix pass (<= 10-bit digits) in a single
+//                  sweep: each tile ranks its items by ballots, finds the
+//                  items of each digit in earlier tiles by a decoupled
+//                  look-back, and scatters through LDS; it counts the next
+//                  pass's digits on the way
 //   k_rle_count / k_rle_scan / k_rle_write
 //                  run heads of the sorted ids -> unique ids, run starts, count
 //                  (few tiles: k_rle_write alone, each tile's first run index
@@ -27,8 +27,10 @@
 //   k_reduce_long  (chunk, column block) items of long runs, fp64 partials
 //                  combined in a fixed order by the last-arriving workgroup
 //   Every reducer finishes each row with the fused dense / SGD / row-wise
-//   Adagrad step, on fp32, bf16 (nearest-even or stochastic rounding) or
-//   INT8 row-wise quantized weight rows (one instance per weight kind).
+//   Adagrad step, on fp32, bf16 or fp16 (nearest-even or stochastic
+//   rounding) or INT8 row-wise quantized weight rows (one instance per weight
+//   kind), reading the table metadata through scalar loads and the weight
+//   rows non-temporally.
 //
 // Method: "fbgemm_gpu/codegen/embedding_backward_split_template.cu" (FBGEMM),
 // host entry `..._exact_cuda` (linearise, sort, run-length encode, long
