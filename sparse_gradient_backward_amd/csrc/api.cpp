@@ -623,8 +623,7 @@ sgb_status enqueue(sgb_plan p, const sgb_batch* b, const sgb_update* u, void* ws
   q.out_h = w_bf16 ? static_cast<uint16_t*>(outv) : nullptr;
   q.out_q = w_int8 ? static_cast<uint8_t*>(outv) : nullptr;
   q.woff8 = p->d_woff8;
-  q.w_kind = w_int8 ? 2 : (w_bf16 ? 1 : 0);
-  q.w_f16 = w_f16 ? 1 : 0;
+  q.w_kind = w_int8 ? 2 : (w_f16 ? 3 : (w_bf16 ? 1 : 0));
   q.sr = (w_bf16 && u->stochastic_rounding) ? 1 : 0;
   q.sr_key0 = (uint32_t)u->sr_seed;
   q.sr_key1 = (uint32_t)(u->sr_seed >> 32);

@@ -407,7 +407,7 @@ struct RedParams {
   uint32_t* run_ticket;
   double* partials;         // fp64 partial sums of long-run work items
   float* out;               // fp32 weights (SGD/Adagrad) or dense grad
-  uint16_t* out_h;          // bf16 or fp16 weights (SGD/Adagrad), w_kind 1
+  uint16_t* out_h;          // bf16 or fp16 weights (SGD/Adagrad), w_kind 1 or 3
   uint8_t* out_q;           // INT8 weight rows (D codes, fp32 scale, fp32 bias), w_kind 2
   const int64_t* woff8;     // [T+1] byte offset of table t's INT8 rows
   float* mom;               // Adagrad state
@@ -426,8 +426,8 @@ struct RedParams {
   int32_t accumulate;
   float lr;
   float eps;
-  int32_t w_kind;           // weights: 0 fp32 (out), 1 bf16 (out_h), 2 INT8 rows (out_q)
-  int32_t w_f16;            // w_kind 1: the 16-bit rows are IEEE binary16, not bf16
+  int32_t w_kind;           // weights: 0 fp32 (out), 1 bf16 (out_h), 2 INT8 rows (out_q),
+                            // 3 fp16 (out_h)
   int32_t sr;               // 16-bit rows: stochastic rounding, else nearest even
   uint32_t sr_key0, sr_key1, sr_ctr3;  // Philox key (seed) and counter word 3 (offset)
 };

@@ -471,23 +471,6 @@ __device__ __forceinline__ uint32_t digit_of(uint64_t kv, int shift, uint32_t dm
   return (uint32_t)(kv >> shift) & dmask;
 }
 
-// Same-digit peers of this lane among the valid lanes: the lanes that agree
-// with it on each of the `bits` low bits of d.  Wave-uniform call.
-__device__ __forceinline__ uint64_t digit_peers(uint32_t d, int bits, bool valid) {
-  uint32_t mlo = 0, mhi = 0;  // lanes that differ from this one on some bit
-#pragma unroll
-  for (int b = 0; b < kMaxDigitBits; ++b) {
-    if (b < bits) {  // uniform
-      const int32_t sx = -(int32_t)((d >> b) & 1u);  // 0 or all ones
-      const uint64_t m = __ballot(sx != 0);
-      mlo |= (uint32_t)m ^ (uint32_t)sx;
-      mhi |= (uint32_t)(m >> 32) ^ (uint32_t)sx;
-    }
-  }
-  const uint64_t live = __ballot(valid);
-  return valid ? (~(((uint64_t)mhi << 32) | mlo) & live) : 0ull;
-}
-
 // Look-back rounds: tiles whose published words one lane loads at once.
 constexpr int kLookback = SGB_LOOKBACK;
 // Tiles per look-back group (the first level of the look-back).
@@ -1404,8 +1387,12 @@ __device__ __forceinline__ void st2_nt(void* q, uint2 v) {
 }
 
 // Weight kinds of the reducer instances: fp32 rows (or a dense gradient),
-// bf16 rows, INT8 rows (codes then the row's fp32 scale and bias).
-constexpr int kWF32 = 0, kWBF16 = 1, kWINT8 = 2;
+// bf16 rows, INT8 rows (codes then the row's fp32 scale and bias), fp16 rows.
+// Each kind has instances of its own, so that no instance carries another
+// kind's rounding code (or its registers).
+constexpr int kWF32 = 0, kWBF16 = 1, kWINT8 = 2, kWF16 = 3;
+// the 16-bit kinds share their row layout and loads
+constexpr bool is16(int wk) { return wk == kWBF16 || wk == kWF16; }
 
 struct RowDst {
   void* out;    // the row's first element (fp32 / bf16) or first byte (INT8)
@@ -1447,7 +1434,7 @@ __device__ __forceinline__ RowDst row_dest(const RedParams& p, const TabMeta& tm
   RowDst d;
   if constexpr (WK == kWINT8)
     d.out = p.out_q + tm.wo + row * (int64_t)(tm.D + 8);
-  else if constexpr (WK == kWBF16)
+  else if constexpr (is16(WK))
     d.out = p.out_h + tm.wo + row * (int64_t)tm.D;
   else
     d.out = p.out + tm.wo + row * (int64_t)tm.D;
@@ -1509,8 +1496,8 @@ __device__ __forceinline__ uint32_t bf16_sr(float x, uint32_t rnd) {
 
 // ---- fp16 weight rows
 //
-// The 16-bit rows may also be IEEE binary16 (the same instances as bf16 rows,
-// switched by p.w_f16).  Widening is exact.  Rounding works on the fp32 bit
+// The 16-bit rows may also be IEEE binary16 (weight kind kWF16, with the
+// layout and loads of bf16 rows).  Widening is exact.  Rounding works on the fp32 bit
 // pattern: the significand m (implicit bit included) is cut at the binary16
 // grid of its binade (spacing 2^(max(E, -14) - 10) for fp32 exponent E, so
 // values below 2^-14 land on the subnormal grid of 2^-24); the sh dropped
@@ -1569,9 +1556,9 @@ template <int WK>
 __device__ __forceinline__ float4 ldw4(const RedParams& p, const RowDst& d, int col, int off = 0) {
   if constexpr (WK == kWF32) {
     return ld4_nt(static_cast<const float*>(d.out) + col + off);
-  } else if constexpr (WK == kWBF16) {
+  } else if constexpr (is16(WK)) {
     const uint2 u = ld2_nt(static_cast<const uint16_t*>(d.out) + col + off);
-    if (p.w_f16)
+    if constexpr (WK == kWF16)
       return make_float4(f16_widen(u.x & 0xffffu), f16_widen(u.x >> 16), f16_widen(u.y & 0xffffu),
                          f16_widen(u.y >> 16));
     return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
@@ -1605,7 +1592,7 @@ __device__ __forceinline__ void stw4(const RedParams& p, const RowDst& d, int co
     const U4 r = philox4x32_10(
         U4{(uint32_t)col >> 2, (uint32_t)d.lin, (uint32_t)((uint64_t)d.lin >> 32), p.sr_ctr3},
         p.sr_key0, p.sr_key1);
-    if (p.w_f16) {
+    if constexpr (WK == kWF16) {
       h0 = f16_round(v.x, r.x, true);
       h1 = f16_round(v.y, r.y, true);
       h2 = f16_round(v.z, r.z, true);
@@ -1616,7 +1603,7 @@ __device__ __forceinline__ void stw4(const RedParams& p, const RowDst& d, int co
       h2 = bf16_sr(v.z, r.z);
       h3 = bf16_sr(v.w, r.w);
     }
-  } else if (p.w_f16) {
+  } else if constexpr (WK == kWF16) {
     h0 = f16_round(v.x, 0u, false);
     h1 = f16_round(v.y, 0u, false);
     h2 = f16_round(v.z, 0u, false);
@@ -2072,7 +2059,7 @@ __device__ __forceinline__ RowDst long_row(const RedParams& p, const LongRun& re
   RowDst d;
   if constexpr (WK == kWINT8)
     d.out = p.out_q + p.woff8[rec.t] + (rec.mom - p.hsc[rec.t]) * (int64_t)(rec.D + 8);
-  else if constexpr (WK == kWBF16)
+  else if constexpr (is16(WK))
     d.out = p.out_h + rec.out;
   else
     d.out = p.out + rec.out;
@@ -3026,10 +3013,12 @@ void by_kind(bool bf16, int wk, A&&... a) {
   if (bf16) {
     if (wk == kWINT8) L<true, kWINT8>::go(a...);
     else if (wk == kWBF16) L<true, kWBF16>::go(a...);
+    else if (wk == kWF16) L<true, kWF16>::go(a...);
     else L<true, kWF32>::go(a...);
   } else {
     if (wk == kWINT8) L<false, kWINT8>::go(a...);
     else if (wk == kWBF16) L<false, kWBF16>::go(a...);
+    else if (wk == kWF16) L<false, kWF16>::go(a...);
     else L<false, kWF32>::go(a...);
   }
 }
