@@ -1510,6 +1510,10 @@ __device__ __forceinline__ uint32_t bf16_sr(float x, uint32_t rnd) {
 // sign.
 
 __device__ __forceinline__ float f16_widen(uint32_t h) {
+  // a normal binary16 value: its exponent rebased by 112 and its significand
+  // moved up 13 bits (equal to the general path below for every input)
+  if (((h >> 10) & 31u) - 1u < 30u)
+    return __uint_as_float(((h & 0x8000u) << 16) | (((h & 0x7FFFu) + (112u << 10)) << 13));
   const uint32_t s = (h & 0x8000u) << 16, ex = (h >> 10) & 31u, man = h & 1023u;
   if (ex == 31u) return __uint_as_float(s | 0x7F800000u | (man << 13));
   if (ex != 0u) return __uint_as_float(s | ((ex + 112u) << 23) | (man << 13));
@@ -1522,6 +1526,17 @@ __device__ __forceinline__ uint32_t f16_round(float x, uint32_t rnd, bool sr) {
   const uint32_t u = __float_as_uint(x);
   const uint32_t s = (u >> 16) & 0x8000u;
   const uint32_t a = u & 0x7FFFFFFFu;
+  if (a - 0x38800000u < 0x0F000000u) {
+    // 2^-14 <= |x| < 2^16, a normal binary16 binade: the dropped bits are the
+    // low 13 of the fp32 pattern and the kept ones its exponent (rebased by
+    // 112) and top 10 significand bits, so a carry from the rounding moves
+    // into the exponent, and to infinity past 65504, by itself.  (Equal to
+    // the general path below for every fp32 input.)
+    const uint32_t rem = a & 0x1FFFu;
+    const bool up = sr ? rnd < (rem << 19)
+                       : (rem > 0x1000u || (rem == 0x1000u && ((a >> 13) & 1u)));
+    return s | (((a >> 13) - 0x1C000u) + (up ? 1u : 0u));
+  }
   if (a >= 0x7F800000u) return s | (a > 0x7F800000u ? 0x7E00u : 0x7C00u);
   if (a >= 0x47800000u) return s | 0x7C00u;  // |x| >= 65536
   const int e = (int)(a >> 23);
