@@ -1497,13 +1497,13 @@ __device__ __forceinline__ uint32_t bf16_sr(float x, uint32_t rnd) {
 // ---- fp16 weight rows
 //
 // The 16-bit rows may also be IEEE binary16 (weight kind kWF16, with the
-// layout and loads of bf16 rows).  Widening is exact.  Rounding works on the fp32 bit
-// pattern: the significand m (implicit bit included) is cut at the binary16
-// grid of its binade (spacing 2^(max(E, -14) - 10) for fp32 exponent E, so
-// values below 2^-14 land on the subnormal grid of 2^-24); the sh dropped
-// bits decide the rounding, and a carry out of the kept bits moves to the
-// next binade, to infinity past 65504.  Nearest even rounds up past half a
-// spacing and on ties to an odd count; stochastic rounding rounds the
+// layout and loads of bf16 rows).  Widening is exact.  Rounding works on the
+// fp32 bit pattern: the significand m (implicit bit included) is cut at the
+// binary16 grid of its binade (spacing 2^(max(E, -14) - 10) for fp32 exponent
+// E, so values below 2^-14 land on the subnormal grid of 2^-24); the sh
+// dropped bits decide the rounding, and a carry out of the kept bits moves to
+// the next binade, to infinity past 65504.  Nearest even rounds up past half
+// a spacing and on ties to an odd count; stochastic rounding rounds the
 // magnitude up iff the element's 32-bit word w satisfies w < f * 2^32, f the
 // dropped fraction (w an integer, so against the ceiling of f * 2^32).
 // Infinities keep their sign; a NaN becomes the quiet NaN 0x7E00 with its
@@ -2234,8 +2234,8 @@ __device__ __forceinline__ int short_lpl(int D) {
 // groups, each run gets the largest power-of-two number of groups that fits:
 // its groups take interleaved slices of lpl lookups and are folded by a fixed
 // xor tree, and the first of them writes the row.  Called with the whole wave
-// active.  The row's old value and Adagrad state are read before the gather
-// so that the reads overlap.
+// active.  The row's old value and Adagrad state are loaded together with the
+// first gather round.
 template <int CPL, bool BF16, int WK>
 __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, int lpl, int64_t base,
                                             int len, uint64_t key, int rowi, float cf, int t,
