@@ -50,7 +50,8 @@ struct sgb_plan_s {
   // built and the long runs are reduced; the events fork and join them.  The
   // mutex keeps one call's fork/join sequence from interleaving with another's.
   hipStream_t aux[2] = {nullptr, nullptr};
-  hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};  // fork, fill done, rle done, short done
+  // fork, fill done, sorted (or rle done), short done (the join), rle done
+  hipEvent_t ev[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
   std::mutex mu;
   // this device's copy of the fixed scratch of sgb_backward_noalloc (NULL if
   // its lookup failed)
@@ -301,13 +302,13 @@ sgb_status sgb_plan_create(sgb_plan* out, int32_t T, const int64_t* hsc, const i
 
   bool ok = hipStreamCreateWithFlags(&p->aux[0], hipStreamNonBlocking) == hipSuccess &&
             hipStreamCreateWithFlags(&p->aux[1], hipStreamNonBlocking) == hipSuccess;
-  for (int i = 0; i < 4 && ok; ++i)
+  for (int i = 0; i < 5 && ok; ++i)
     // the fork events order work between the plan's streams on this device
     // only and need no system-scope release at their records; the join event
-    // keeps it, so that a host waiting on the caller's stream sees the side
-    // stream's writes
+    // (ev[3]) keeps it, so that a host waiting on the caller's stream sees the
+    // side stream's writes
     ok = hipEventCreateWithFlags(&p->ev[i], hipEventDisableTiming |
-                                                (i < 3 ? hipEventDisableSystemFence : 0)) ==
+                                                (i != 3 ? hipEventDisableSystemFence : 0)) ==
          hipSuccess;
   ok = ok && hipMalloc(&p->d_hsc, sizeof(int64_t) * (T + 1)) == hipSuccess &&
             hipMalloc(&p->d_doff, sizeof(int32_t) * (T + 1)) == hipSuccess &&
@@ -552,6 +553,14 @@ sgb_status enqueue(sgb_plan p, const sgb_batch* b, const sgb_update* u, void* ws
   if (L.npasses > 0) mark(SGB_STAGE_SORT, 1);
   const uint64_t* kv_sorted = kv_in;
   const float* cf_sorted = cf_in;
+  // early fork: with the ids sorted, the reducer of short runs of rows up to
+  // 512 columns finds the run lengths itself (scan_runs) and starts on the
+  // side stream here, overlapping run-length encoding and the long-run list
+  const bool early = overlap && N <= kEarlyForkMaxN && do_front && do_reduce &&
+                     p->thr <= kScanRunsMaxThr && p->Dmin <= 512;
+  if (early && (hipEventRecord(p->ev[2], stream) != hipSuccess ||
+                hipStreamWaitEvent(short_s, p->ev[2], 0) != hipSuccess))
+    return SGB_ERR_HIP;
 
   RleParams rp{};
   rp.kv = kv_sorted;
@@ -572,6 +581,8 @@ sgb_status enqueue(sgb_plan p, const sgb_batch* b, const sgb_update* u, void* ws
   mark(SGB_STAGE_RLE, 0);
   if (do_front && launch_rle(rp, stream) != hipSuccess) return SGB_ERR_HIP;
   mark(SGB_STAGE_RLE, 1);
+  if (early && p->Dmax > 512 && hipEventRecord(p->ev[4], stream) != hipSuccess)
+    return SGB_ERR_HIP;
 
   PostParams pp{};
   pp.cum = rp.cum;
@@ -642,19 +653,35 @@ sgb_status enqueue(sgb_plan p, const sgb_batch* b, const sgb_update* u, void* ws
   q.accumulate = u->accumulate ? 1 : 0;
   q.lr = u->lr;
   q.eps = u->eps;
+  q.scan_runs = early ? 1 : 0;
   const bool bf16 = b->grad_dtype == SGB_BF16;
   // short runs need only the sorted words and run starts: side stream from
   // here on (after the zero fill), while the long-run list is built and the
   // long runs are reduced here; the two write disjoint rows
   if (do_reduce) {
-    if (hipEventRecord(p->ev[2], stream) != hipSuccess ||
-        hipStreamWaitEvent(short_s, p->ev[2], 0) != hipSuccess ||
-        (fresh && hipStreamWaitEvent(short_s, p->ev[1], 0) != hipSuccess))
-      return SGB_ERR_HIP;
-    mark_on(short_s, SGB_STAGE_REDUCE_SHORT, 0);
-    if (launch_reduce_short(q, bf16, p->Dmin, p->Dmax, p->wide_grid, short_s) != hipSuccess)
-      return SGB_ERR_HIP;
-    mark_on(short_s, SGB_STAGE_REDUCE_SHORT, 1);
+    if (early) {
+      // the side stream already waits for the sort; the wider rows' reducer
+      // reads the run starts, so it waits for run-length encoding too
+      if (fresh && hipStreamWaitEvent(short_s, p->ev[1], 0) != hipSuccess) return SGB_ERR_HIP;
+      if (launch_reduce_short(q, bf16, p->Dmin, p->Dmax, p->wide_grid, kShortRows, short_s) !=
+          hipSuccess)
+        return SGB_ERR_HIP;
+      if (p->Dmax > 512 &&
+          (hipStreamWaitEvent(short_s, p->ev[4], 0) != hipSuccess ||
+           launch_reduce_short(q, bf16, p->Dmin, p->Dmax, p->wide_grid, kWideRows, short_s) !=
+               hipSuccess))
+        return SGB_ERR_HIP;
+    } else {
+      if (hipEventRecord(p->ev[2], stream) != hipSuccess ||
+          hipStreamWaitEvent(short_s, p->ev[2], 0) != hipSuccess ||
+          (fresh && hipStreamWaitEvent(short_s, p->ev[1], 0) != hipSuccess))
+        return SGB_ERR_HIP;
+      mark_on(short_s, SGB_STAGE_REDUCE_SHORT, 0);
+      if (launch_reduce_short(q, bf16, p->Dmin, p->Dmax, p->wide_grid, kShortRows | kWideRows,
+                              short_s) != hipSuccess)
+        return SGB_ERR_HIP;
+      mark_on(short_s, SGB_STAGE_REDUCE_SHORT, 1);
+    }
     if (hipEventRecord(p->ev[3], short_s) != hipSuccess) return SGB_ERR_HIP;
   }
   if (do_front) {

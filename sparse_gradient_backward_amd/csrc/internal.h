@@ -71,6 +71,9 @@ constexpr int kMaxD = 8192;
 #ifndef SGB_SERIAL_MAX_N
 #define SGB_SERIAL_MAX_N 16384
 #endif
+#ifndef SGB_EARLY_FORK_MAX_N
+#define SGB_EARLY_FORK_MAX_N (1 << 22)
+#endif
 #ifndef SGB_ONE_PASS_TILES
 #define SGB_ONE_PASS_TILES 128
 #endif
@@ -145,12 +148,23 @@ constexpr int kLbScalarGroupTiles = 32;
 // tile's first run index by look-back over the tiles' head counts); up to
 // kFuseScanTiles k_rle_count, then k_rle_write summing the counts before its
 // tile; beyond that k_rle_count, k_rle_scan and k_rle_write
+constexpr int kOnePassTiles = SGB_ONE_PASS_TILES;
+constexpr int kFuseScanTiles = SGB_FUSE_SCAN_TILES;
 // Batches of at most kSerialMaxN lookups run every kernel on the caller's
 // stream: their kernels are a few microseconds each, and the fork to the
 // plan's side streams and the join cost more than the overlap returns.
 constexpr int64_t kSerialMaxN = SGB_SERIAL_MAX_N;
-constexpr int kOnePassTiles = SGB_ONE_PASS_TILES;
-constexpr int kFuseScanTiles = SGB_FUSE_SCAN_TILES;
+// Batches of kSerialMaxN to kEarlyForkMaxN lookups start the reducer of short
+// runs (rows up to 512 columns) as soon as the ids are sorted: it finds the
+// length of each window's last run by scanning the sorted words after the
+// window, and runs beside run-length encoding and the long-run list instead
+// of after them.  That needs a long-run threshold that bounds the scan to a
+// few reads (kScanRunsMaxThr words).  Larger batches fork after run-length
+// encoding: their short-run reducer fills the chip for hundreds of
+// microseconds, and sharing it with the scans delays the long-run reducer by
+// more than the early start returns.
+constexpr int64_t kEarlyForkMaxN = SGB_EARLY_FORK_MAX_N;
+constexpr int kScanRunsMaxThr = 4096;
 
 // run-length encoding / run post-processing tiling
 constexpr int kScanThreads = 256;
@@ -421,6 +435,8 @@ struct RedParams {
   int32_t thr;
   int32_t chunk_base;       // chunk_base_for(N)
   int32_t sub_log;          // short-run reducer: log2 of the waves per window
+  int32_t scan_runs;        // short-run reducer: find the length of a window's last run
+                            // from the sorted words after it, not from the run starts
   int32_t wide_ncb;         // wide-row reducer: column blocks per run
   int32_t mode;
   int32_t accumulate;
@@ -469,9 +485,11 @@ hipError_t launch_rle(const RleParams& p, hipStream_t s);
 hipError_t launch_post(const PostParams& p, int grid, hipStream_t s);
 hipError_t launch_fill(const FillParams& p, int grid, hipStream_t s);
 hipError_t launch_reduce_long(const RedParams& p, bool bf16, int grid, hipStream_t s);
-// wide_grid: blocks of the wide-row reducer, {fp32 Adagrad, fp32 other, bf16 Adagrad, bf16 other}
+// wide_grid: blocks of the wide-row reducer, {fp32 Adagrad, fp32 other, bf16 Adagrad, bf16 other};
+// parts: kShortRows (rows up to 512 columns) and/or kWideRows (wider rows)
+constexpr int kShortRows = 1, kWideRows = 2;
 hipError_t launch_reduce_short(const RedParams& p, bool bf16, int dmin, int dmax,
-                               const int* wide_grid, hipStream_t s);
+                               const int* wide_grid, int parts, hipStream_t s);
 void reduce_wide_blocks_per_cu(int out[4]);
 int reduce_long_blocks_per_cu(bool bf16);
 hipError_t launch_forward(const FwdParams& p, hipStream_t s);

@@ -2437,11 +2437,15 @@ __device__ __forceinline__ void short_batch(const RedParams& p, uint64_t sel, in
 
 // Windows of 64 sorted positions, each shared by 2^sub_log waves.  Run heads
 // are where the id changes; a run's length is the distance to the next head
-// in the window, and only a run that reaches the window's end looks its
-// length up (run index at the head, run starts).  A wave serves the short
-// runs (length < thr) that start in its 64 >> sub_log positions, in batches
-// of at most 64/lpl runs of one table.  Rows wider than 512 columns are
-// skipped here (k_reduce_wide serves them).
+// in the window, and only a run that reaches the window's end needs more: its
+// run index at the head and the run starts, or, with p.scan_runs, the sorted
+// words after the window, read 64 at a time (the first 64 with the window's
+// own) until a different id shows where the run ends or thr positions past
+// its head are passed.  The scan makes the reducer independent of run-length
+// encoding, so that it can start as soon as the ids are sorted.  A wave
+// serves the short runs (length < thr) that start in its 64 >> sub_log
+// positions, in batches of at most 64/lpl runs of one table.  Rows wider than
+// 512 columns are skipped here (k_reduce_wide serves them).
 template <int CPL, bool BF16, int WK>
 __device__ __forceinline__ void reduce_short(const RedParams& p) {
   const int lane = lane_id();
@@ -2454,6 +2458,8 @@ __device__ __forceinline__ void reduce_short(const RedParams& p) {
   const int64_t pos = base + lane;
   const bool in = pos < p.N;
   const uint64_t kv = in ? p.kv[pos] : 0ull;
+  const bool in_next = p.scan_runs && pos + 64 < p.N;
+  const uint64_t key_next = in_next ? (p.kv[pos + 64] >> p.info_bits) : 0ull;
   const uint64_t key = kv >> p.info_bits;
   uint64_t prev = __shfl_up(key, 1, 64);
   if (lane == 0) prev = base > 0 ? (p.kv[base - 1] >> p.info_bits) : ~0ull;
@@ -2466,10 +2472,38 @@ __device__ __forceinline__ void reduce_short(const RedParams& p) {
   const float cf = (in && p.coef) ? p.coef[pos] : 1.0f;
   // length to the next head in the window; the run of the last head may go on
   const uint64_t after = lane < 63 ? (heads & (~0ull << (lane + 1))) : 0ull;
+  int last_len = 0;  // with p.scan_runs: the length of the last head's run, or >= thr
+  if (p.scan_runs) {
+    const int hl = 63 - __builtin_clzll(heads);
+    const int64_t hpos = base + hl;
+    const int vl = (int)min((int64_t)63, p.N - 1 - base);   // the window's last position
+    const uint64_t klast = __shfl(key, vl, 64);               // the last run's id
+    int64_t end = -1;
+    if (base + 64 >= p.N) {
+      end = p.N;
+    } else {
+      const uint64_t m = __ballot(in_next && key_next != klast);
+      if (m) end = base + 64 + __builtin_ctzll(m);
+      else if (base + 128 >= p.N) end = p.N;
+    }
+    // (rare) the run goes on past the next window: further words, until its
+    // end or until it is known to be long
+    for (int64_t b2 = base + 128; end < 0 && b2 < hpos + p.thr; b2 += 64) {
+      const int64_t q = b2 + lane;
+      const bool v = q < p.N;
+      const uint64_t k2 = v ? (p.kv[q] >> p.info_bits) : 0ull;
+      const uint64_t m = __ballot(v && k2 != klast);
+      if (m) end = b2 + __builtin_ctzll(m);
+      else if (b2 + 64 >= p.N) end = p.N;
+    }
+    last_len = end < 0 ? p.thr : (int)min(end - hpos, (int64_t)p.thr);
+  }
   int len = 0;
   if (head) {
     if (after) {
       len = __builtin_ctzll(after) - lane;
+    } else if (p.scan_runs) {
+      len = last_len;
     } else {
       const int r = p.head_run[pos];
       len = p.cum[r + 1] - (int)pos;
@@ -3109,7 +3143,7 @@ struct Short8Launch {
 };
 
 hipError_t launch_reduce_short(const RedParams& p, bool bf16, int dmin, int dmax,
-                               const int* wide_grid, hipStream_t s) {
+                               const int* wide_grid, int parts, hipStream_t s) {
   const int64_t windows = (p.N + kShortSpan - 1) / kShortSpan;
   // waves per window, reduced when the grid would pass 2^32 threads
   auto sub_for = [&](int want) {
@@ -3117,14 +3151,14 @@ hipError_t launch_reduce_short(const RedParams& p, bool bf16, int dmin, int dmax
     while (sub > 0 && (windows << sub) > (1ll << 25)) --sub;
     return sub;
   };
-  if (dmin <= 512) {
+  if ((parts & kShortRows) && dmin <= 512) {
     // rows up to 512 columns: 8 columns per lane, one wave per row at most
     RedParams q = p;
     q.sub_log = sub_for(kShortSub8);
     const dim3 grid((unsigned)(((windows << q.sub_log) + 3) / 4), 1);
     by_kind<Short8Launch>(bf16, p.w_kind, q, grid, s);
   }
-  if (dmax > 512) launch_reduce_wide(p, bf16, dmax, wide_grid, s);
+  if ((parts & kWideRows) && dmax > 512) launch_reduce_wide(p, bf16, dmax, wide_grid, s);
   return hipGetLastError();
 }
 

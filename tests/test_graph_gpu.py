@@ -4,10 +4,11 @@ The path enqueues no memsets and allocates nothing, and its fork to the
 plan's side streams and the join go through events, which a capture turns
 into graph edges.  A captured call is replayed several times, with eager
 work and synchronisations between the replays; after every replay the rows
-(and momentum) must be bit-equal to the same number of eager calls.  Both
-schedules are covered: a small batch runs on the caller's stream alone, a
-larger one forks the short-run reduction (and a fresh gradient's zero fill)
-to the side streams.
+(and momentum) must be bit-equal to the same number of eager calls.  Every
+schedule is covered: a small batch runs on the caller's stream alone, larger
+ones fork the short-run reduction (and a fresh gradient's zero fill) to the
+side streams, right after the sort for rows up to 512 columns, after
+run-length encoding for the 1024-column rows.
 """
 import sys
 

@@ -165,6 +165,58 @@ def test_many_tables(sgb, T, mode):
     check_case(sgb, inp, mode, 4, lr=0.02, eps=1e-6)
 
 
+def _early_fork_case(seed):
+    """Three tables of 64, 256 and 1024 columns, 9001 one-lookup bags each
+    (27 003 lookups: above the single-stream limit, a ragged last window).
+    Each table's runs have lengths that sit around the 64-position windows
+    and the thresholds below (1 .. 4097 lookups, the largest id of each
+    table 100), the rest of its bags runs of 1 to 5 lookups, ids shuffled so
+    that the runs fall at every offset of a window."""
+    B = 9001
+    s = synth.Spec("earlyfork", 3, (20000, 20000, 20000), (64, 256, 1024), B, ("fixed", 1),
+                   ("uniform",), "sum", False, "f32", "sgd", seed=seed)
+    inp = synth.generate(s)
+    rng = np.random.default_rng(seed)
+    fixed = [1, 2, 63, 64, 65, 127, 128, 129, 130, 200, 1000]
+    cols = []
+    for t in range(3):
+        lens = [4095 + t] + (list(fixed) if t == 0 else list(rng.choice(fixed, 6, replace=False)))
+        while B - 100 - sum(lens) > 5:
+            lens.append(int(rng.integers(1, 6)))
+        if B - 100 - sum(lens) > 0:
+            lens.append(B - 100 - sum(lens))
+        ids = rng.choice(19999, size=len(lens), replace=False)
+        v = np.concatenate([np.repeat(ids, lens), np.full(100, 19999)])
+        assert v.size == B
+        rng.shuffle(v)
+        cols.append(v)
+    inp.indices = np.concatenate(cols).astype(np.int64)
+    return inp
+
+
+@pytest.mark.parametrize("thr", [1, 64, 129, 4096, 4097])
+def test_early_fork_run_scan(sgb, thr):
+    """Batches between the single-stream limit and 2^22 lookups, with a
+    long-run threshold of at most 4096, start the short-run reducer of rows
+    up to 512 columns right after the sort: it finds the length of each
+    window's last run by scanning the sorted words after the window (up to
+    thr words past the run's head), while run-length encoding and the
+    long-run list run beside it; the 1024-column rows' reducer waits for the
+    run starts.  thr = 4097 takes the fork after run-length encoding."""
+    inp = _early_fork_case(61)
+    _say(f"[parity] early fork thr={thr} N={inp.N}")
+    check_case(sgb, inp, "sgd", thr, lr=0.05)
+
+
+@pytest.mark.parametrize("mode,acc", [("dense", False), ("dense", True), ("rowwise_adagrad", False)])
+def test_early_fork_modes(sgb, mode, acc):
+    """The early fork with a fresh dense gradient (the side stream also waits
+    for the zero fill), an accumulated one, and row-wise Adagrad."""
+    inp = _early_fork_case(62)
+    _say(f"[parity] early fork {mode} acc={acc} N={inp.N}")
+    check_case(sgb, inp, mode, 129, accumulate=acc, lr=0.05, eps=1e-6)
+
+
 def test_wide_rows_more_items_than_waves(sgb):
     """~25 000 runs of 2048-column rows: ~100 000 (run, column block) items,
     more than the wide-row reducer's waves (eight times the resident
