@@ -35,6 +35,9 @@ CASES = [
     (dict(cfg=3, T=4, E=(20000,) * 4, B=300), "rowwise_adagrad", False),   # ~24 k: forked
     (dict(cfg=2, T=3, E=(4000, 2500, 3000), B=1500), "dense", False),    # fresh: fill forked too
     (dict(cfg=4, E=(9000,), D=(1024,), nobag_tokens=20000), "dense", True),
+    # ~40 k lookups of 64- and 1024-column rows: the early fork, then the
+    # wide-row reducer after run-length encoding, on the same side stream
+    (dict(cfg=3, T=2, E=(3000, 2000), D=(64, 1024), B=1000), "sgd", False),
 ]
 
 
