@@ -19,8 +19,10 @@
 //   k_post         run lengths, ascending long-run list and records
 //   k_fill         zeros of a fresh dense gradient (side stream, from the start)
 //   k_reduce_short8 short runs of rows up to 512 columns (side stream, after
-//                  run-length encoding): the runs starting in a part of a
-//                  64-position window, one per lane group
+//                  run-length encoding; for mid-sized batches right after the
+//                  sort, the length of a window's last run then read from the
+//                  sorted ids after the window): the runs starting in a part
+//                  of a 64-position window, one per lane group
 //   k_reduce_wide  short runs of wider rows (same stream): (run, column
 //                  block) items dealt round-robin to waves, several times
 //                  more workgroups than fit at once
