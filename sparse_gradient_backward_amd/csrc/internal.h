@@ -51,7 +51,7 @@ constexpr int kMaxD = 8192;
 #define SGB_WIDE_WAVES 8
 #endif
 #ifndef SGB_WIDE_GRID_MULT
-#define SGB_WIDE_GRID_MULT 8
+#define SGB_WIDE_GRID_MULT 16
 #endif
 #ifndef SGB_SHORT8_WAVES
 #define SGB_SHORT8_WAVES 6

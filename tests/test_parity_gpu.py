@@ -218,11 +218,11 @@ def test_early_fork_modes(sgb, mode, acc):
 
 
 def test_wide_rows_more_items_than_waves(sgb):
-    """~25 000 runs of 2048-column rows: ~100 000 (run, column block) items,
-    more than the wide-row reducer's waves (eight times the resident
+    """~50 000 runs of 2048-column rows: ~200 000 (run, column block) items,
+    more than the wide-row reducer's waves (sixteen times the resident
     workgroups), so waves take a second item after their first."""
-    s = synth.Spec("wideloop", 1, (40000,), (2048,), 0, ("fixed", 1), ("uniform",), "none", False,
-                   "bf16", "dense", accumulate=True, nobag_tokens=40000, seed=43)
+    s = synth.Spec("wideloop", 1, (80000,), (2048,), 0, ("fixed", 1), ("uniform",), "none", False,
+                   "bf16", "dense", accumulate=True, nobag_tokens=80000, seed=43)
     inp = synth.generate(s)
     _say(f"[parity] wide rows, many items N={inp.N}")
     check_case(sgb, inp, "dense", 64, accumulate=True)
