@@ -63,10 +63,10 @@ constexpr int kMaxD = 8192;
 #define SGB_FILL_THREADS 256
 #endif
 #ifndef SGB_LIN_WG_PER_CU
-#define SGB_LIN_WG_PER_CU 4
+#define SGB_LIN_WG_PER_CU 6
 #endif
 #ifndef SGB_LOOKBACK
-#define SGB_LOOKBACK 16
+#define SGB_LOOKBACK 4
 #endif
 #ifndef SGB_SERIAL_MAX_N
 #define SGB_SERIAL_MAX_N 16384
