@@ -456,9 +456,12 @@ def test_host_detected_errors(sgb):
 def test_own_stream_and_timed(sgb, cfg):
     """The call on a stream of the caller's own, completed by synchronising that
     stream alone (the side streams are joined back into it), matches the
-    oracle; the timed entry point (events around every kernel) gives
-    bit-identical outputs."""
-    s = synth.spec(2, T=2, E=(4000, 3000), B=300) if cfg == 2 else \
+    oracle; the timed entry point (events around every kernel, every kernel
+    on the one stream, run lengths from the run starts) gives bit-identical
+    outputs to the plain call (here, for both workloads, with the short-run
+    reducer forked right after the sort and, for the dense one, the zero
+    fill forked at the start)."""
+    s = synth.spec(2, T=2, E=(4000, 3000), B=700) if cfg == 2 else \
         synth.spec(5, E=(60000,), B=2000)
     inp = synth.generate(s)
     _say(f"[parity] own stream config {cfg} N={inp.N}")
