@@ -217,6 +217,37 @@ def test_early_fork_modes(sgb, mode, acc):
     check_case(sgb, inp, mode, 129, accumulate=acc, lr=0.05, eps=1e-6)
 
 
+@pytest.mark.parametrize("mode,acc,thr", [("sgd", False, 129), ("dense", False, 64),
+                                          ("dense", True, 4096)])
+def test_early_fork_equals_serial_schedule(sgb, mode, acc, thr):
+    """The early fork (run lengths from the sorted ids after each window,
+    rows up to 512 columns reduced beside run-length encoding, the
+    1024-column rows after it) gives bit-identical rows to the timed entry
+    point, which runs every kernel in order on one stream and takes the run
+    lengths from the run starts."""
+    inp = _early_fork_case(63)
+    _say(f"[parity] early fork vs serial {mode} acc={acc} thr={thr} N={inp.N}")
+    dev = to_dev(inp)
+    plan = sgb.Plan(inp.hash_size_cumsum, inp.D_offsets, inp.spec.pooling, thr)
+    ws = plan.workspace(inp.N, inp.B)
+    o0, m0 = initial_buffers(inp, mode, acc)
+    outs = []
+    for timed in (False, True):
+        out = torch.from_numpy(o0).cuda()
+        kw = dict(grad=out) if mode == "dense" else dict(weights=out, momentum=None)
+        events = None
+        if timed:
+            events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(sgb.STAGES))]
+            for e in events:
+                e.record()
+        plan.backward(dev["grad"], dev["indices"], dev["offsets"], inp.B, dev["psw"], mode,
+                      accumulate=acc, lr=0.05, eps=1e-6, workspace=ws, events=events, **kw)
+        torch.cuda.synchronize()
+        assert plan.device_status(ws) == "SGB_OK"
+        outs.append(out.cpu().numpy())
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
 def test_wide_rows_more_items_than_waves(sgb):
     """~50 000 runs of 2048-column rows: ~200 000 (run, column block) items,
     more than the wide-row reducer's waves (sixteen times the resident
