@@ -2533,14 +2533,12 @@ __device__ __forceinline__ void reduce_short(const RedParams& p) {
 }
 
 // 8 columns per lane with fp64 sums fits about 80 VGPRs: 6 waves per SIMD overlap
-// the runs' dependent memory steps.  The 16-bit row instances are held to the
-// same budget (the fp16 one spills a few registers, which costs less than a
-// wave less per SIMD); the INT8 instance, whose requantisation needs the
-// registers, takes one wave less.
+// the runs' dependent memory steps.  The 16-bit and INT8 row instances are
+// held to the same budget: the bf16 and fp16 ones spill a few registers,
+// which costs less than a wave less per SIMD.
 template <bool BF16, int WK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
-    WK == kWINT8 ? SGB_SHORT8_WAVES - 1 : SGB_SHORT8_WAVES,
-    WK == kWINT8 ? SGB_SHORT8_WAVES - 1 : SGB_SHORT8_WAVES)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SGB_SHORT8_WAVES,
+                                                                     SGB_SHORT8_WAVES)))
 void k_reduce_short8(RedParams p) {
   if (!runs_match(p)) return;
   reduce_short<8, BF16, WK>(p);
